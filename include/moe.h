@@ -1,0 +1,247 @@
+/*
+ * moe.h — C ABI of libmoe: one MoE layer's routed-expert computation on an
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer computes, for T tokens x[t] of width H:
+ *   router logits -> top-k experts and renormalised softmax weights,
+ *   grouping of the (token, slot) rows by expert through a resident slot table,
+ *   block-FP4 expert FFNs  down( SiLU(gate x) * (up x) ),
+ *   combine  y[t] = sum_j w[t,j] * E_{id[t,j]}(x[t]) + sigma(x[t].w_sg) * E_shared(x[t]).
+ *
+ * Sources (cited by page and section throughout this library):
+ *   [Strata]    "strata-expert-paths", hanayo.cn, 2026-10-13 — an engine's MoE
+ *               layer walk-through: router, grouping, expert paths, combine,
+ *               staging ring, tail-skip.
+ *   [FreeToken] "FreeToken 阅读笔记" (FreeToken reading notes), zhongzhuzhou.org,
+ *               2026-08-23 — (layer, expert) slot pool, device-resident control
+ *               flow, full-layer double buffering.
+ *   [PLE]       "02-PLE 如何从 NVMe 送到 GPU" (how PLE rows travel from NVMe to
+ *               the GPU), mengman.github.io, 2026-09-10 — the NVFP4 block-FP4
+ *               encoding and its packed-row byte count.
+ *
+ * Conventions for every entry point:
+ *   - Ownership: the caller owns every device buffer, pinned host buffer and
+ *     stream.  The library never allocates device memory.  It owns only a
+ *     ring's opaque struct and its four hipEvent_t.
+ *   - Asynchrony: device work is enqueued on the given stream; no entry point
+ *     synchronises, and all enqueued work is capturable into a HIP graph.  Grid
+ *     shapes depend only on moe_dims, never on data: device-side counts mask
+ *     unused blocks.
+ *   - Errors: every entry point validates synchronously and returns a
+ *     negative MOE_ERR_* code having enqueued nothing; moe_last_error() gives a
+ *     human-readable detail for the calling thread.  Anomalies that only the
+ *     device can see are OR-ed into the caller's int32 dev_status word
+ *     (MOE_DEV_* bits), which the caller reads after its own synchronisation.
+ *   - Pointers marked "device" must be device (or managed) memory; all device
+ *     pointers must be 16-byte aligned (MOE_ERR_ALIGN otherwise).
+ *   - Thread safety: re-entrant; a ring is driven from one host thread.
+ *
+ * Shapes: 1 <= T, 1 <= k <= E <= 1024, H % 32 == 0, I % 32 == 0, 32 <= H, I <= 16384.
+ * The shared expert has the same intermediate size I as a routed expert.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A HIP stream handle (hipStream_t); NULL means the legacy default stream. */
+struct ihipStream_t;
+typedef struct ihipStream_t* moe_stream_t;
+
+/* ---- status codes ------------------------------------------------------- */
+#define MOE_OK 0
+#define MOE_ERR_ARG (-1)        /* NULL pointer where one is required, bad enum/flag */
+#define MOE_ERR_SHAPE (-2)      /* dims outside the supported shapes listed above */
+#define MOE_ERR_ALIGN (-3)      /* a device pointer is not 16-byte aligned */
+#define MOE_ERR_NOT_PINNED (-4) /* host source of a staged copy is not page-locked */
+#define MOE_ERR_WORKSPACE (-5)  /* workspace missing or smaller than moe_workspace_bytes */
+#define MOE_ERR_HIP (-6)        /* a HIP runtime call or kernel launch failed */
+#define MOE_ERR_STATE (-7)      /* ring protocol violated (see moe_stage_h2d) */
+
+/* ---- device status bits (OR-ed into *dev_status by kernels) ------------- */
+#define MOE_DEV_BAD_EXPERT_ID 1   /* a topk id outside [0, E): its row is dropped */
+#define MOE_DEV_NOT_RESIDENT 2    /* a non-empty group's slot is -1: rows are zero */
+#define MOE_DEV_BAD_SLOT 4        /* a slot index >= n_slots: rows are zero */
+
+const char* moe_status_string(int status);
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* moe_last_error(void);
+/* Library version string. */
+const char* moe_version(void);
+
+/* ---- dimensions --------------------------------------------------------- */
+typedef struct moe_dims {
+  int32_t T; /* tokens in this call (one chunk / one verification window) */
+  int32_t H; /* hidden width */
+  int32_t I; /* expert intermediate width (routed and shared) */
+  int32_t E; /* routed experts per layer; the shared expert is index E */
+  int32_t k; /* experts picked per token */
+  int32_t L; /* layers addressed by the slot table (rows of slot_table) */
+} moe_dims;
+
+/* ---- expert blob format ([PLE] "NVFP4 code 和 scale 如何反量化" and
+ *      "一个 160 维向量在 packed 文件中占 90 字节") --------------------------
+ *
+ * One blob holds every tensor of one (layer, expert) ([FreeToken] 3, one cache
+ * slot per (layer, expert)).  Its three matrices are
+ *     m = 0  gate  [I rows][H columns]
+ *     m = 1  up    [I rows][H columns]
+ *     m = 2  down  [H rows][I columns]
+ * (rows are output units; columns are the reduction axis K).
+ * Each matrix is stored NVFP4-style:
+ *   codes  [rows][K/2] bytes, row-major.  Byte c of a row holds column 2c in
+ *          its low nibble and column 2c+1 in its high nibble.  A nibble is an
+ *          E2M1 code: bit 3 is the sign, bits 0..2 index the magnitudes
+ *          {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+ *   scales [rows][K/16] bytes, row-major, OCP FP8 E4M3FN (bias 7, no infinity,
+ *          0x7F/0xFF NaN).  Scale b of a row applies to columns 16b..16b+15.
+ *   global one fp32 per matrix.
+ * value(r, c) = e2m1(code(r, c)) * e4m3(scale(r, c/16)) * global.
+ * Section order inside a blob: gate codes, up codes, down codes, gate scales,
+ * up scales, down scales, then the three fp32 globals (gate, up, down).
+ * Every section starts on a 256-byte boundary.  Blobs sit in a pool at
+ * pool + slot * slot_stride, slot_stride = blob_bytes rounded up to 4096.
+ * Gate codes and up codes are adjacent, so rows 0..2I-1 of the gate codes
+ * section read as one [2I][H/2] matrix (likewise the gate+up scales).
+ */
+typedef struct moe_blob_layout {
+  uint64_t blob_bytes;    /* bytes up to the end of the globals */
+  uint64_t slot_stride;   /* blob_bytes rounded up to a multiple of 4096 */
+  uint64_t off_codes[3];  /* byte offsets of gate, up, down codes */
+  uint64_t off_scales[3]; /* byte offsets of gate, up, down scales */
+  uint64_t off_globals;   /* byte offset of float[3] {G_gate, G_up, G_down} */
+} moe_blob_layout;
+
+/* Host, pure.  Fills *out for widths (H, I).  MOE_ERR_SHAPE unless H and I are
+ * multiples of 32 within [32, 16384]. */
+int moe_blob_layout_init(int32_t H, int32_t I, moe_blob_layout* out);
+
+/* Host, pure.  Bytes of device workspace that moe_group and moe_expert_ffn
+ * need for dims d (the same buffer is passed to both, group first). */
+int moe_workspace_bytes(const moe_dims* d, uint64_t* out_bytes);
+
+/* ---- S1 + S2: router ---------------------------------------------------
+ * [Strata] "显存里缓存的是什么？" (the router picks the experts and their merge
+ * weights) and "还有一条会改变输出的路径" (experts are ranked per token).
+ *
+ * Logits: exactly one of w_router / logits_in is non-NULL.
+ *   w_router  device fp32 [H][E] row-major: l[t,e] = sum_h x[t,h] * W[h,e],
+ *             accumulated in fp32 (rounding point R0: fp32 logits).
+ *   logits_in device fp32 [T][E]: used as given.
+ * x            device bf16 bits [T][H] row-major (required: the shared gate reads it).
+ * w_shared_gate device fp32 [H]: sigma[t] = 1 / (1 + exp(-sum_h x[t,h] w_sg[h])).
+ * logits_out   device fp32 [T][E] or NULL: receives the logits used.
+ * topk_ids     device int32 [T][k]: slot j holds the j-th largest logit; ties
+ *              go to the lower expert index.
+ * topk_w       device fp32 [T][k]: w_j = exp(l_j - l_0) / sum_{j'<k} exp(l_j' - l_0),
+ *              i.e. the softmax over all E renormalised to the chosen k.
+ * shared_sigma device fp32 [T].
+ * Logits must be finite (NaN/inf inputs give unspecified ids).
+ */
+int moe_route(const moe_dims* d, const uint16_t* x, const float* w_router,
+              const float* logits_in, const float* w_shared_gate,
+              float* logits_out, int32_t* topk_ids, float* topk_w,
+              float* shared_sigma, moe_stream_t stream);
+
+/* ---- S3: grouping ------------------------------------------------------
+ * [Strata] "路由以后，专家怎样分工？" (tokens of one layer and window that picked
+ * the same expert form one group recording their inputs and output positions)
+ * and "哪些专家能长期留在显存？" (the residency table maps (layer, expert) to a
+ * slot or to a special not-resident value); [FreeToken] 4 (logical -> physical
+ * slot rewrite on the device, no host synchronisation).
+ *
+ * Row space p: [0, T*k) routed rows grouped by expert (ascending expert, then
+ * ascending token inside a group); [T*k, T*k+T) shared-expert rows in token
+ * order.  f = t*k + j is the flat (token, slot) index.
+ * topk_ids   device int32 [T][k].  Ids outside [0,E) set MOE_DEV_BAD_EXPERT_ID
+ *            and are placed in no group (inv_perm -1, no row).
+ * slot_table device int32 [L][E+1]; column E is the shared expert; -1 = not
+ *            resident.  layer in [0, L).  n_slots bounds valid slot indices.
+ * offsets    device int32 [E+2]: routed group e < E is rows
+ *            [offsets[e], offsets[e+1]); offsets[E] = number of routed rows
+ *            with a valid id (T*k when all are valid); offsets[E+1] = T*k + T.
+ *            The shared group is always rows [T*k, T*k+T); rows
+ *            [offsets[E], T*k) exist only when ids were dropped and are unused.
+ * perm       device int32 [T*k]: p -> f (routed rows only).
+ * inv_perm   device int32 [T*k]: f -> p (-1 for a dropped bad id).
+ * group_slot device int32 [E+1]: slot_table[layer][e].
+ * dev_status device int32 [1]: MOE_DEV_* bits are OR-ed in.
+ * ws         device workspace of >= moe_workspace_bytes(d) bytes; it also
+ *            carries the work list that moe_expert_ffn reads.
+ */
+int moe_group(const moe_dims* d, int32_t layer, const int32_t* topk_ids,
+              const int32_t* slot_table, int32_t n_slots, int32_t* offsets,
+              int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
+              int32_t* dev_status, void* ws, uint64_t ws_bytes,
+              moe_stream_t stream);
+
+/* ---- S4: expert FFNs ---------------------------------------------------
+ * [Strata] "路由以后，专家怎样分工？" and "CPU 怎样把剩下的专家算完？" (gate/up,
+ * activation, the intermediate re-encoded for the next kernel, down).
+ * For every row p of group e (routed or shared) with token t:
+ *   g = G_gate * sum_c x[t,c] Wg[i,c],  u = G_up * sum_c x[t,c] Wu[i,c]
+ *   h[p,i] = bf16_rne( g / (1 + exp(-g)) * u )                 (rounding point R1)
+ *   Y[p,n] = bf16_rne( G_down * sum_i h[p,i] Wd[n,i] )          (rounding point R3)
+ * with the matrices decoded from the blob at pool + group_slot[e]*slot_stride.
+ * Weight codes and scales multiply exactly; sums are fp32.
+ * x          device bf16 [T][H].
+ * pool       device, pool_bytes long; every slot used must lie inside it.
+ * h          device bf16 [T*k+T][I] (intermediate, also an output).
+ * y_rows     device bf16 [T*k+T][H]: unweighted expert outputs per row.
+ * Rows of a group whose slot is -1 or >= pool_bytes/slot_stride are written
+ * as zeros and flagged in dev_status.
+ * offsets/perm/group_slot/ws: exactly as written by moe_group on the same stream.
+ */
+int moe_expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool,
+                   uint64_t pool_bytes, const moe_blob_layout* layout,
+                   const int32_t* offsets, const int32_t* perm,
+                   const int32_t* group_slot, uint16_t* h, uint16_t* y_rows,
+                   int32_t* dev_status, void* ws, uint64_t ws_bytes,
+                   moe_stream_t stream);
+
+/* ---- S5: combine -------------------------------------------------------
+ * [Strata] "路由以后，专家怎样分工？" (each expert output times its router weight,
+ * summed, plus the gated shared-expert contribution) and "少算这些专家，会付出
+ * 什么代价？" (the output is linear in the weighted expert terms).
+ *   y[t] = bf16_rne( sum_{j<k} w[t,j] * Y[inv_perm[t*k+j]] + sigma[t] * Y[T*k+t] )
+ * accumulated in fp32 in exactly this order (rounding point R2); no
+ * renormalisation.  A slot whose inv_perm is -1 contributes nothing.
+ */
+int moe_combine(const moe_dims* d, const uint16_t* y_rows,
+                const int32_t* inv_perm, const float* topk_w,
+                const float* shared_sigma, uint16_t* y, moe_stream_t stream);
+
+/* ---- S6: two-slot staging ring ([Strata] "PCIe 搬运怎样与计算重叠？";
+ *      [FreeToken] 3.1 full-layer double buffering) --------------------------
+ * Two device slots of slot_bytes each, written by a copy stream and read by a
+ * compute stream.  Per slot s the ring holds events copied[s] and used[s]:
+ *   moe_stage_h2d: on copy_stream wait used[s] (the last release of s), then
+ *     hipMemcpyAsync(slot s <- pinned host src), then record copied[s].
+ *     Slots are used alternately 0,1,0,1...; *out_slot receives s.  The source
+ *     must be page-locked (MOE_ERR_NOT_PINNED otherwise) and bytes <= slot_bytes.
+ *     MOE_ERR_STATE if slot s was staged but not yet released.
+ *   moe_ring_acquire: compute stream waits copied[s]; s must be staged.
+ *   moe_ring_release: records used[s] on the compute stream after the reads of
+ *     s; s must be acquired.  A later stage into s waits for it.
+ * A slot's data is valid for reads enqueued on the compute stream between its
+ * acquire and its release.
+ */
+typedef struct moe_ring moe_ring;
+int moe_ring_create(void* slot0, void* slot1, uint64_t slot_bytes,
+                    moe_stream_t copy_stream, moe_ring** out);
+int moe_stage_h2d(moe_ring* ring, const void* pinned_host_src, uint64_t bytes,
+                  int32_t* out_slot);
+int moe_ring_acquire(moe_ring* ring, int32_t slot, moe_stream_t compute);
+int moe_ring_release(moe_ring* ring, int32_t slot, moe_stream_t compute);
+int moe_ring_slot_ptr(moe_ring* ring, int32_t slot, void** out);
+int moe_ring_destroy(moe_ring* ring);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,363 @@
+"""Plain CPU oracle for one MoE layer's routed-expert computation (fp64).
+
+TEST INFRASTRUCTURE.  Only the tests (tests/), the smoke check in
+__graft_entry__.smoke() and the cpu_baseline leg of bench.py may import or call
+this module.  The product path (the HIP library and its Python binding) never
+does, and this module imports nothing from it.
+
+What it computes, step by step, and where each step is defined:
+
+  Pages cited (title, site, date):
+    [Strata]    "strata-expert-paths", hanayo.cn, 2026-10-13.
+    [FreeToken] "FreeToken 阅读笔记" (FreeToken reading notes), zhongzhuzhou.org,
+                2026-08-23.
+    [PLE]       "【Qwen3.8-Flash-Next 端侧部署】02-PLE 如何从 NVMe 送到 GPU",
+                mengman.github.io, 2026-09-10.
+
+  1. Weight decode — [PLE] section "NVFP4 code 和 scale 如何反量化": the low and
+     high nibble of a byte are two codes; a code's low 3 bits pick a magnitude
+     from {0, .5, 1, 1.5, 2, 3, 4, 6} and its top bit is the sign; each run of
+     16 values is multiplied by its FP8 E4M3 block scale and then by one FP32
+     global scale.  E4M3 here is the OCP E4M3FN encoding (bias 7, subnormals,
+     no infinity, S.1111.111 is NaN).  The product is exact in fp64.
+  2. Router logits — [Strata] "显存里缓存的是什么？": the router decides which
+     experts a token uses and the merge weight of each output.  When the router
+     matrix is given, logits are x . W_r summed in fp64 and stored as fp32
+     (rounding point R0); otherwise the logits are an input.
+  3. Top-k — experts ordered by (logit descending, expert index ascending); the
+     first k are slots 0..k-1 ([Strata] "还有一条会改变输出的路径" ranks a token's
+     experts; ties to the lower index is the reading adopted).
+  4. Weights — the softmax over all E logits renormalised to the k chosen:
+     w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0), in fp64.
+  5. Shared gate — sigma_t = 1 / (1 + exp(-x_t . w_sg)) in fp64 ([Strata]
+     "路由以后，专家怎样分工？": the gated shared-expert contribution).
+  6. Groups — [Strata] "路由以后，专家怎样分工？": the tokens of a layer that picked
+     the same expert form one group recording their inputs and output
+     positions.  Groups in ascending expert index, rows inside a group in
+     ascending token order; the shared expert's group is every token, last.
+  7. Expert FFN per row — [Strata] "CPU 怎样把剩下的专家算完？": gate/up, the
+     activation, the intermediate re-encoded for the next kernel, then down.
+     g = Wg x, u = Wu x (fp64); h = bf16(g / (1 + e^-g) * u) (rounding point R1);
+     Y = bf16(Wd h) (rounding point R3).
+  8. Combine — [Strata] "路由以后，专家怎样分工？" and "少算这些专家，会付出什么代价？":
+     y_t = bf16( sum_j w_j Y[row(t, j)] + sigma_t Y_shared[t] ) (rounding point
+     R2), with no renormalisation.
+
+bf16 rounding is round-to-nearest-even from the exact fp64 value (no detour
+through fp32).  Parity pins for every function live in tests/test_oracle_*.py.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Callable, Dict, List, Optional, Sequence
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# 1. Formats
+# ---------------------------------------------------------------------------
+
+#: E2M1 magnitudes indexed by the low three bits of a code ([PLE], NVFP4 dequant).
+E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """E2M1 nibble codes (0..15) -> fp64 values.  Bit 3 is the sign."""
+    c = np.asarray(codes, dtype=np.int64)
+    mag = np.asarray(E2M1_MAGNITUDES, dtype=np.float64)[c & 7]
+    return np.where((c & 8) != 0, -mag, mag)
+
+
+def e4m3fn_decode(b) -> np.ndarray:
+    """OCP FP8 E4M3FN bytes -> fp64.
+
+    sign = bit 7, exponent = bits 3..6 (bias 7), mantissa = bits 0..2.
+    exponent 0: subnormal m/8 * 2^-6; exponent 1..15: (1 + m/8) * 2^(e-7);
+    exponent 15 with mantissa 7 is NaN; there is no infinity.
+    """
+    b = np.asarray(b, dtype=np.int64)
+    s = np.where((b >> 7) & 1, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = b & 7
+    sub = m / 8.0 * 2.0 ** -6
+    norm = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    v = s * np.where(e == 0, sub, norm)
+    return np.where((e == 15) & (m == 7), np.nan, v)
+
+
+@dataclass(frozen=True)
+class BlobLayout:
+    """Byte layout of one (layer, expert) blob, as specified in include/moe.h.
+
+    Sections, each starting on a 256-byte boundary: gate codes [I][H/2], up codes
+    [I][H/2], down codes [H][I/2], gate scales [I][H/16], up scales [I][H/16],
+    down scales [H][I/16], then 3 fp32 globals (gate, up, down).
+    """
+
+    H: int
+    I: int
+    off_codes: tuple
+    off_scales: tuple
+    off_globals: int
+    blob_bytes: int
+    slot_stride: int
+
+    def matrix_shape(self, m: int):
+        """(rows, K) of matrix m: 0 gate [I,H], 1 up [I,H], 2 down [H,I]."""
+        return (self.I, self.H) if m < 2 else (self.H, self.I)
+
+
+def _align(v: int, a: int) -> int:
+    return (v + a - 1) // a * a
+
+
+def matrix_bytes(rows: int, K: int):
+    """(code bytes, scale bytes) of one NVFP4 matrix: two codes per byte, one
+    E4M3 scale per 16 values ([PLE] "一个 160 维向量在 packed 文件中占 90 字节")."""
+    assert K % 16 == 0
+    return rows * K // 2, rows * K // 16
+
+
+def blob_layout(H: int, I: int) -> BlobLayout:
+    shapes = [(I, H), (I, H), (H, I)]
+    off = 0
+    oc, os_ = [], []
+    for r, K in shapes:
+        oc.append(off)
+        off = _align(off + matrix_bytes(r, K)[0], 256)
+    for r, K in shapes:
+        os_.append(off)
+        off = _align(off + matrix_bytes(r, K)[1], 256)
+    og = off
+    blob = og + 12
+    return BlobLayout(H, I, tuple(oc), tuple(os_), og, blob, _align(blob, 4096))
+
+
+def dequant(blob, lay: BlobLayout, m: int) -> np.ndarray:
+    """Matrix m of a blob as exact fp64 [rows, K]:
+    value(r, c) = e2m1(code(r, c)) * e4m3(scale(r, c // 16)) * global."""
+    buf = np.frombuffer(blob, dtype=np.uint8) if not isinstance(blob, np.ndarray) else blob.view(np.uint8)
+    rows, K = lay.matrix_shape(m)
+    ncode, nscale = matrix_bytes(rows, K)
+    codes = buf[lay.off_codes[m]: lay.off_codes[m] + ncode].reshape(rows, K // 2)
+    scales = buf[lay.off_scales[m]: lay.off_scales[m] + nscale].reshape(rows, K // 16)
+    g = float(np.frombuffer(buf[lay.off_globals + 4 * m: lay.off_globals + 4 * m + 4].tobytes(), dtype="<f4")[0])
+    q = np.empty((rows, K), dtype=np.float64)
+    q[:, 0::2] = e2m1_decode(codes & 0xF)          # even column: low nibble
+    q[:, 1::2] = e2m1_decode(codes >> 4)           # odd column: high nibble
+    s = e4m3fn_decode(scales)                      # [rows, K/16]
+    return q * np.repeat(s, 16, axis=1) * g
+
+
+# ---------------------------------------------------------------------------
+# Rounding points
+# ---------------------------------------------------------------------------
+
+_BF16_OVERFLOW = 2.0 ** 128
+
+
+def bf16_round(v) -> np.ndarray:
+    """Round fp64 values to the nearest bfloat16 value, ties to even, directly
+    from the fp64 value.  Returns fp64 holding bf16-representable values."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.array(v, copy=True)
+    fin = np.isfinite(v) & (v != 0)
+    _, e = np.frexp(v[fin])                        # v = m * 2^e, 0.5 <= |m| < 1
+    q = np.maximum(e - 8, -133)                    # 8 significant bits; subnormal quantum 2^-133
+    r = np.ldexp(np.rint(np.ldexp(v[fin], -q)), q)  # np.rint: round half to even
+    r = np.where(np.abs(r) >= _BF16_OVERFLOW, np.copysign(np.inf, r), r)
+    out[fin] = r
+    return out
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(v) -> np.ndarray:
+    """fp64 -> bf16 bit patterns, rounding to nearest even."""
+    r = bf16_round(v).astype(np.float32)            # exact: r is on the bf16 grid
+    return (r.view(np.uint32) >> 16).astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# 2-5. Router
+# ---------------------------------------------------------------------------
+
+def router_logits(x: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    """logits[t, e] = fp32( sum_h x[t, h] * W_r[h, e] ), summed in fp64 (R0)."""
+    return (np.asarray(x, np.float64) @ np.asarray(w_router, np.float64)).astype(np.float32)
+
+
+def topk(logits: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest logits per row; ties go to the lower index.
+    Slot j holds the j-th in order (logit descending, index ascending)."""
+    lg = np.asarray(logits, dtype=np.float64)
+    assert np.all(np.isfinite(lg)), "logits must be finite"
+    order = np.argsort(-lg, axis=1, kind="stable")  # stable: equal keys keep index order
+    return order[:, :k].astype(np.int32)
+
+
+def topk_weights(logits: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0) over the chosen k (fp64)."""
+    lg = np.asarray(logits, dtype=np.float64)
+    sel = np.take_along_axis(lg, np.asarray(ids, np.int64), axis=1)
+    ex = np.exp(sel - sel[:, :1])
+    return ex / ex.sum(axis=1, keepdims=True)
+
+
+def shared_gate(x: np.ndarray, w_shared_gate: np.ndarray) -> np.ndarray:
+    """sigma_t = 1 / (1 + exp(-x_t . w_sg)) in fp64."""
+    z = np.asarray(x, np.float64) @ np.asarray(w_shared_gate, np.float64)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+# ---------------------------------------------------------------------------
+# 6. Grouping
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Groups:
+    offsets: np.ndarray   # int32 [E+2]
+    perm: np.ndarray      # int32 [T*k]: row p -> flat index f = t*k + j
+    inv_perm: np.ndarray  # int32 [T*k]: f -> p
+
+
+def group(ids: np.ndarray, E: int) -> Groups:
+    """For e = 0..E-1 in order, append the flat rows f = t*k + j with
+    ids[t, j] == e, t ascending.  The shared group (index E) is rows
+    [T*k, T*k + T) in token order."""
+    T, k = ids.shape
+    flat = np.asarray(ids, np.int64).reshape(-1)
+    perm: List[int] = []
+    offsets = np.zeros(E + 2, dtype=np.int32)
+    for e in range(E):
+        offsets[e] = len(perm)
+        perm.extend(np.nonzero(flat == e)[0].tolist())   # ascending f == ascending t
+    offsets[E] = len(perm)
+    offsets[E + 1] = T * k + T
+    assert len(perm) == T * k, "every id must lie in [0, E)"
+    perm_a = np.asarray(perm, dtype=np.int32)
+    inv = np.empty(T * k, dtype=np.int32)
+    inv[perm_a] = np.arange(T * k, dtype=np.int32)
+    return Groups(offsets, perm_a, inv)
+
+
+# ---------------------------------------------------------------------------
+# 7. Expert FFN
+# ---------------------------------------------------------------------------
+
+@dataclass
+class FfnRows:
+    h_pre: np.ndarray   # fp64 [n, I], before R1
+    h: np.ndarray       # fp64 [n, I], bf16 values (R1)
+    y_pre: np.ndarray   # fp64 [n, H], before R3
+    y: np.ndarray       # fp64 [n, H], bf16 values (R3)
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    return g / (1.0 + np.exp(-g))
+
+
+def expert_ffn(x_rows: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> FfnRows:
+    """Rows of one expert: h = bf16(silu(Wg x) * (Wu x)); Y = bf16(Wd h)."""
+    xr = np.asarray(x_rows, np.float64)
+    g = xr @ wg.T
+    u = xr @ wu.T
+    h_pre = silu(g) * u
+    h = bf16_round(h_pre)
+    y_pre = h @ wd.T
+    return FfnRows(h_pre, h, y_pre, bf16_round(y_pre))
+
+
+# ---------------------------------------------------------------------------
+# 8. Combine
+# ---------------------------------------------------------------------------
+
+def combine(y_routed: np.ndarray, w: np.ndarray, sigma: np.ndarray, y_shared: np.ndarray):
+    """y_t = bf16( sum_j w[t,j] * y_routed[t,j,:] + sigma_t * y_shared[t,:] ).
+
+    y_routed: fp64 [n, k, H], the bf16 expert rows of each token's slots in slot
+    order; y_shared: fp64 [n, H].  Returns (fp64 sum before R2, bf16-rounded)."""
+    acc = np.zeros(y_shared.shape, dtype=np.float64)
+    for j in range(y_routed.shape[1]):
+        acc = acc + w[:, j:j + 1] * y_routed[:, j, :]
+    acc = acc + sigma[:, None] * y_shared
+    return acc, bf16_round(acc)
+
+
+# ---------------------------------------------------------------------------
+# Whole layer
+# ---------------------------------------------------------------------------
+
+@dataclass
+class LayerResult:
+    logits: np.ndarray          # fp32 [T, E]
+    ids: np.ndarray             # int32 [T, k]
+    w: np.ndarray               # fp64 [T, k]
+    sigma: np.ndarray           # fp64 [T]
+    groups: Groups
+    tokens: np.ndarray          # int64 [n]: tokens whose rows/outputs were computed
+    h: Dict[int, np.ndarray] = field(default_factory=dict)      # row p -> fp64 [I] (bf16 values)
+    h_pre: Dict[int, np.ndarray] = field(default_factory=dict)
+    y_rows: Dict[int, np.ndarray] = field(default_factory=dict)  # row p -> fp64 [H] (bf16 values)
+    y_rows_pre: Dict[int, np.ndarray] = field(default_factory=dict)
+    y_pre: Optional[np.ndarray] = None   # fp64 [n, H] before R2
+    y: Optional[np.ndarray] = None       # fp64 [n, H] bf16 values
+
+
+def moe_layer(x_bits: np.ndarray, blob_of: Callable[[int], bytes], H: int, I: int, E: int, k: int,
+              w_shared_gate: np.ndarray, w_router: Optional[np.ndarray] = None,
+              logits: Optional[np.ndarray] = None, tokens: Optional[Sequence[int]] = None,
+              dense_weights: Optional[Dict[int, tuple]] = None) -> LayerResult:
+    """One MoE layer.
+
+    x_bits: uint16 bf16 bits [T, H].  blob_of(e) returns the blob bytes of
+    expert e (e == E is the shared expert).  Exactly one of w_router / logits.
+    Routing and grouping cover every token; the FFN rows and the combine are
+    computed for `tokens` (default: all), since a token's output depends only
+    on its own row, its routing and the expert bytes.
+    """
+    assert (w_router is None) != (logits is None)
+    T = x_bits.shape[0]
+    x = bf16_bits_to_f64(x_bits)
+    lg = router_logits(x, w_router) if w_router is not None else np.asarray(logits, np.float32)
+    ids = topk(lg, k)
+    w = topk_weights(lg, ids)
+    sigma = shared_gate(x, w_shared_gate)
+    groups = group(ids, E)
+    tok = np.arange(T) if tokens is None else np.asarray(sorted(set(int(t) for t in tokens)), np.int64)
+    res = LayerResult(lg, ids, w, sigma, groups, tok)
+
+    lay = blob_layout(H, I)
+    cache = {} if dense_weights is None else dense_weights
+
+    def weights(e):
+        if e not in cache:
+            b = blob_of(e)
+            cache[e] = tuple(dequant(b, lay, m) for m in range(3))
+        return cache[e]
+
+    # rows needed, grouped by expert: (expert, row p, token t)
+    need: Dict[int, List[tuple]] = {}
+    for t in tok:
+        for j in range(k):
+            f = int(t) * k + j
+            need.setdefault(int(ids[t, j]), []).append((int(groups.inv_perm[f]), int(t)))
+        need.setdefault(E, []).append((T * k + int(t), int(t)))
+    for e in sorted(need):
+        rows = need[e]
+        wg, wu, wd = weights(e)
+        out = expert_ffn(x[[t for _, t in rows]], wg, wu, wd)
+        for i, (p, _) in enumerate(rows):
+            res.h_pre[p], res.h[p] = out.h_pre[i], out.h[i]
+            res.y_rows_pre[p], res.y_rows[p] = out.y_pre[i], out.y[i]
+        if dense_weights is None:
+            cache.pop(e, None)   # keep memory bounded for large experts
+
+    yr = np.stack([np.stack([res.y_rows[int(groups.inv_perm[int(t) * k + j])] for j in range(k)]) for t in tok])
+    ysh = np.stack([res.y_rows[T * k + int(t)] for t in tok])
+    res.y_pre, res.y = combine(yr, w[tok], sigma[tok], ysh)
+    return res
