@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE layer's routed-expert hot path on one MI355X.
+
+Prints ONE JSON line.  A "step" is one pass of the whole path (route, group,
+expert FFN, combine) over one batch of synthetic input, for every layer of the
+workload.  Default workload: the 48-layer decode step (T = 4 tokens, H = 2048,
+I = 512, E = 512 + 1 shared, top-10, Zipf s = 1.0 routing, block-FP4 experts,
+every (layer, expert) resident in an HBM slot pool).  Inputs for every timed
+step are generated on the device before timing starts.
+
+Extra objects on the line:
+  roofline      the expert-FFN launch (dominant stage): algorithmic bytes (decode,
+                HBM-bound) or flops (prefill, MFMA-bound) per launch divided by
+                its mean duration from HIP events on its stream, against the
+                MI355X spec peak (HBM 8.0 TB/s; dense bf16 MFMA 2.5 PFLOP/s).
+  cpu_baseline  the CPU oracle (oracle/, fp64 numpy, 1 thread) on a bounded
+                sample of the same workload, scaled to tokens/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; decode expert-weight GB/s & prefill TFLOP/s vs peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="decode48",
+                    help="tiny | decode48 | decode43x64 | prefill8192 (default decode48)")
+    ap.add_argument("--eager", action="store_true", help="launch every call eagerly instead of HIP graphs")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Workload:
+    """Device-resident inputs of every step to be run, plus one set of layer buffers."""
+
+    def __init__(self, cfg, n_steps, B, DevGen):
+        import torch
+        from moe_expert_ffn_top_amd.layer import LayerBuffers
+        from synth import zipf_logits
+
+        self.cfg = cfg
+        self.dims = B.Dims(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.L)
+        self.layout = B.moe_blob_layout_init(cfg.H, cfg.I)
+        dev = DevGen()
+        E1, L = cfg.E1, cfg.L
+        self.n_slots = L * E1
+        self.slot_table = torch.arange(self.n_slots, dtype=torch.int32, device="cuda").view(L, E1).contiguous()
+        self.pool_bytes = self.n_slots * self.layout.slot_stride
+        log("allocating %.2f GB expert pool (%d slots x %d B)" % (self.pool_bytes / 1e9, self.n_slots,
+                                                                 self.layout.slot_stride))
+        self.pool = torch.zeros(self.pool_bytes, dtype=torch.uint8, device="cuda")
+        t0 = time.time()
+        dev.pool(cfg, 0, L, self.slot_table.data_ptr(), self.n_slots, self.layout, self.pool.data_ptr())
+        torch.cuda.synchronize()
+        log("pool generated on device in %.1f s" % (time.time() - t0))
+        # per-step inputs: steps cycle through the workload's own steps
+        self.n_inputs = min(n_steps, max(cfg.steps, 1)) if cfg.router == "zipf" else min(n_steps, 4)
+        self.x = torch.empty((self.n_inputs, L, cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+        for s in range(self.n_inputs):
+            for l in range(L):
+                dev.x(cfg, l, s, self.x[s, l].data_ptr())
+        self.wsg = torch.empty((L, cfg.H), dtype=torch.float32, device="cuda")
+        for l in range(L):
+            dev.w_shared_gate(cfg, l, self.wsg[l].data_ptr())
+        if cfg.router == "matrix":
+            self.wr = torch.empty((L, cfg.H, cfg.E), dtype=torch.float32, device="cuda")
+            for l in range(L):
+                dev.w_router(cfg, l, self.wr[l].data_ptr())
+            self.logits = None
+        else:
+            self.wr = None
+            lg = np.stack([np.stack([zipf_logits(cfg, l, s) for l in range(L)]) for s in range(self.n_inputs)])
+            self.logits = torch.from_numpy(lg).cuda()
+        torch.cuda.synchronize()
+        self.buf = LayerBuffers.allocate(self.dims)
+
+    def input_index(self, step):
+        return step % self.n_inputs
+
+    def run_step(self, step, stream=None, ffn_events=None):
+        """Enqueue every layer of one step.  ffn_events: list to which
+        (start, end) event pairs around each expert-FFN launch are appended."""
+        import torch
+        from moe_expert_ffn_top_amd import binding as B
+
+        s = self.input_index(step)
+        d, buf = self.dims, self.buf
+        for l in range(self.cfg.L):
+            x = self.x[s, l]
+            if self.wr is not None:
+                B.moe_route(d, x, self.wr[l], None, self.wsg[l], buf.logits, buf.ids, buf.w, buf.sigma, stream)
+            else:
+                B.moe_route(d, x, None, self.logits[s, l], self.wsg[l], None, buf.ids, buf.w, buf.sigma, stream)
+            B.moe_group(d, l, buf.ids, self.slot_table, self.n_slots, buf.offsets, buf.perm, buf.inv_perm,
+                        buf.group_slot, buf.status, buf.ws, stream=stream)
+            if ffn_events is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+            B.moe_expert_ffn(d, x, self.pool, self.pool_bytes, self.layout, buf.offsets, buf.perm, buf.group_slot,
+                             buf.h, buf.y_rows, buf.status, buf.ws, stream=stream)
+            if ffn_events is not None:
+                e1.record()
+                ffn_events.append((e0, e1, buf.offsets.clone()))
+            B.moe_combine(d, buf.y_rows, buf.inv_perm, buf.w, buf.sigma, buf.y, stream)
+
+
+def expert_work(cfg, offsets_list, blob_bytes):
+    """Algorithmic work of the FFN launches: bytes of the distinct expert blobs
+    touched (routed groups with rows, plus the shared expert) and flops
+    (6 H I per row)."""
+    nbytes, flops = [], []
+    for off in offsets_list:
+        o = off.cpu().numpy()
+        active = int(np.count_nonzero(np.diff(o[:cfg.E + 1]))) + 1
+        rows = int(o[cfg.E]) + cfg.T
+        nbytes.append(active * blob_bytes)
+        flops.append(6.0 * cfg.H * cfg.I * rows)
+    return np.array(nbytes, dtype=np.float64), np.array(flops, dtype=np.float64)
+
+
+def cpu_baseline(cfg, seconds):
+    """Time the oracle (fp64 numpy, one thread) on a bounded sample of the
+    workload: whole layers of step 0 for decode (all T tokens), a token sample
+    for prefill; scaled to tokens/s of the full step."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import moe_oracle as O
+    from synth import HostGen, zipf_logits
+
+    gen = HostGen()
+    olay = O.blob_layout(cfg.H, cfg.I)
+    done_layers, t_oracle = 0, 0.0
+    sample = ""
+    with threadpool_limits(limits=1):
+        if cfg.T <= 64:
+            for l in range(cfg.L):
+                x = gen.x(cfg, l, 0)
+                wsg = gen.w_shared_gate(cfg, l)
+                kw = dict(w_router=gen.w_router(cfg, l)) if cfg.router == "matrix" else dict(
+                    logits=zipf_logits(cfg, l, 0))
+                lg = O.router_logits(O.bf16_bits_to_f64(x), kw["w_router"]) if "w_router" in kw else kw["logits"]
+                need = set(O.topk(lg, cfg.k).reshape(-1).tolist()) | {cfg.E}
+                blobs = {e: gen.expert_blob(cfg, l, e, olay) for e in need}   # generation is not timed
+                t0 = time.perf_counter()
+                O.moe_layer(x, lambda e: blobs[e], cfg.H, cfg.I, cfg.E, cfg.k, wsg, **kw)
+                t_oracle += time.perf_counter() - t0
+                done_layers += 1
+                if t_oracle >= seconds:
+                    break
+            value = cfg.T / (t_oracle / done_layers * cfg.L)
+            sample = "%d of %d layers of decode step 0 (all %d tokens each), oracle time %.1f s, scaled to the " \
+                     "full %d-layer step" % (done_layers, cfg.L, cfg.T, t_oracle, cfg.L)
+        else:
+            l = 0
+            x = gen.x(cfg, l, 0)
+            wsg = gen.w_shared_gate(cfg, l)
+            wr = gen.w_router(cfg, l) if cfg.router == "matrix" else None
+            lgz = None if wr is not None else zipf_logits(cfg, l, 0)
+            ntok = 16
+            blob_cache = {}
+
+            def blob(e):
+                if e not in blob_cache:
+                    blob_cache[e] = gen.expert_blob(cfg, l, e, olay)
+                return blob_cache[e]
+            lg = O.router_logits(O.bf16_bits_to_f64(x), wr) if wr is not None else lgz
+            toks = list(range(ntok))
+            for e in set(O.topk(lg[toks], cfg.k).reshape(-1).tolist()) | {cfg.E}:
+                blob(e)
+            t0 = time.perf_counter()
+            O.moe_layer(x, blob, cfg.H, cfg.I, cfg.E, cfg.k, wsg, w_router=wr, logits=lgz, tokens=toks)
+            t_oracle = time.perf_counter() - t0
+            value = ntok / t_oracle
+            sample = "layer 0, routing and grouping of all %d tokens plus expert FFN and combine of %d sampled " \
+                     "tokens; oracle time %.1f s; rate = sampled tokens / time" % (cfg.T, ntok, t_oracle)
+    return {"value": value, "unit": "tokens/s", "cores": 1, "kind": "oracle", "sample": sample}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build runs the MoE layer on a single MI355X and has no "
+              "multi-GPU path (requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from moe_expert_ffn_top_amd import binding as B
+    from synth import DevGen, config_by_name
+
+    cfg = config_by_name(args.config)
+    if cfg.staged:
+        print("workload %s (staged ring) is not wired into bench.py yet" % cfg.name, file=sys.stderr)
+        sys.exit(2)
+    K, W = args.steps, args.warmup
+    wl = Workload(cfg, W + K, B, DevGen)
+    stream = torch.cuda.current_stream()
+
+    graphs = []
+    if not args.eager:
+        log("capturing %d step graphs" % min(W + K, wl.n_inputs))
+        for s in range(min(W + K, wl.n_inputs)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                wl.run_step(s)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def step(i):
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            wl.run_step(i)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    status = int(wl.buf.status.item())
+    assert status == 0, "device status %d after warmup" % status
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(K):
+        step(W + i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / K
+    tokens_per_s = cfg.T / (ms_per_step / 1e3)
+    log("%.4f ms/step, %.1f tokens/s" % (ms_per_step, tokens_per_s))
+
+    # roofline of the expert-FFN launch: events around each launch on its stream
+    events = []
+    for i in range(min(K, 8)):
+        wl.run_step(W + i, ffn_events=events)
+    torch.cuda.synchronize()
+    dur_ms = np.array([a.elapsed_time(b) for a, b, _ in events])
+    nbytes, flops = expert_work(cfg, [o for _, _, o in events], wl.layout.blob_bytes)
+    decode = cfg.T <= 64
+    if decode:
+        achieved = float(nbytes.mean() / (dur_ms.mean() * 1e-3) / 1e9)
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "kernel": "moe_expert_ffn launch (gate/up + down)", "launch_us": float(dur_ms.mean() * 1e3),
+                "bytes_per_launch": float(nbytes.mean())}
+    else:
+        achieved = float(flops.mean() / (dur_ms.mean() * 1e-3) / 1e12)
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                "kernel": "moe_expert_ffn launch (gate/up + down)", "launch_us": float(dur_ms.mean() * 1e3),
+                "flops_per_launch": float(flops.mean())}
+    log("expert FFN launch: %.1f us, %s" % (dur_ms.mean() * 1e3, roof))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(cfg, args.cpu_baseline_seconds)
+
+    line = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded; random block-FP4 weights, bf16 activations)",
+        "config": {"workload": cfg.name, "T": cfg.T, "layers": cfg.L, "H": cfg.H, "I": cfg.I, "E": cfg.E,
+                   "k": cfg.k, "shared_experts": 1,
+                   "routing": ("zipf s=%g" % cfg.zipf_s) if cfg.router == "zipf" else "router matrix",
+                   "graphs": not args.eager, "parallelism": "single GPU"},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+"""Thin ctypes binding of libmoe (include/moe.h).
+
+Argument marshalling only: every function forwards to the C entry point of the
+same name, passing device pointers (torch tensors or ints) and a HIP stream
+handle.  Nothing here computes any part of the MoE layer, and there is no
+fallback: if libmoe.so is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libmoe.so is not built at %s; run `python -m moe_expert_ffn_top_amd.build` "
+                      "or __graft_entry__.build()" % LIB_PATH)
+_lib = ctypes.CDLL(LIB_PATH)
+
+MOE_OK = 0
+MOE_ERR_ARG = -1
+MOE_ERR_SHAPE = -2
+MOE_ERR_ALIGN = -3
+MOE_ERR_NOT_PINNED = -4
+MOE_ERR_WORKSPACE = -5
+MOE_ERR_HIP = -6
+MOE_ERR_STATE = -7
+MOE_DEV_BAD_EXPERT_ID = 1
+MOE_DEV_NOT_RESIDENT = 2
+MOE_DEV_BAD_SLOT = 4
+
+#: every symbol include/moe.h declares
+EXPORTED = ("moe_status_string", "moe_last_error", "moe_version", "moe_blob_layout_init", "moe_workspace_bytes",
+            "moe_route", "moe_group", "moe_expert_ffn", "moe_combine", "moe_ring_create", "moe_stage_h2d",
+            "moe_ring_acquire", "moe_ring_release", "moe_ring_slot_ptr", "moe_ring_destroy")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("L", ctypes.c_int32)]
+
+    def __init__(self, T, H, I, E, k, L=1):
+        super().__init__(T, H, I, E, k, L)
+
+
+class BlobLayout(ctypes.Structure):
+    _fields_ = [("blob_bytes", ctypes.c_uint64), ("slot_stride", ctypes.c_uint64),
+                ("off_codes", ctypes.c_uint64 * 3), ("off_scales", ctypes.c_uint64 * 3),
+                ("off_globals", ctypes.c_uint64)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (where, _lib.moe_status_string(status).decode(),
+                                                 _lib.moe_last_error().decode()))
+
+
+_vp, _i32, _u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64
+_DP = ctypes.POINTER(Dims)
+_lib.moe_status_string.restype = ctypes.c_char_p
+_lib.moe_status_string.argtypes = [ctypes.c_int]
+_lib.moe_last_error.restype = ctypes.c_char_p
+_lib.moe_version.restype = ctypes.c_char_p
+_lib.moe_blob_layout_init.argtypes = [_i32, _i32, ctypes.POINTER(BlobLayout)]
+_lib.moe_workspace_bytes.argtypes = [_DP, ctypes.POINTER(_u64)]
+_lib.moe_route.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.moe_group.argtypes = [_DP, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _u64, _vp]
+_lib.moe_expert_ffn.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _u64, _vp]
+_lib.moe_combine.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.moe_ring_create.argtypes = [_vp, _vp, _u64, _vp, ctypes.POINTER(_vp)]
+_lib.moe_stage_h2d.argtypes = [_vp, _vp, _u64, ctypes.POINTER(_i32)]
+_lib.moe_ring_acquire.argtypes = [_vp, _i32, _vp]
+_lib.moe_ring_release.argtypes = [_vp, _i32, _vp]
+_lib.moe_ring_slot_ptr.argtypes = [_vp, _i32, ctypes.POINTER(_vp)]
+_lib.moe_ring_destroy.argtypes = [_vp]
+
+
+def _p(t) -> Optional[int]:
+    """Device/host address of a torch tensor, an int, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _s(stream) -> Optional[int]:
+    """HIP stream handle: None -> torch's current stream; int; torch stream."""
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != MOE_OK:
+        raise MoeError(rc, where)
+
+
+def moe_version() -> str:
+    return _lib.moe_version().decode()
+
+
+def moe_status_string(status: int) -> str:
+    return _lib.moe_status_string(status).decode()
+
+
+def moe_blob_layout_init(H: int, I: int) -> BlobLayout:
+    out = BlobLayout()
+    _check(_lib.moe_blob_layout_init(H, I, ctypes.byref(out)), "moe_blob_layout_init")
+    return out
+
+
+def moe_workspace_bytes(dims: Dims) -> int:
+    out = _u64()
+    _check(_lib.moe_workspace_bytes(ctypes.byref(dims), ctypes.byref(out)), "moe_workspace_bytes")
+    return out.value
+
+
+def moe_route(dims, x, w_router, logits_in, w_shared_gate, logits_out, topk_ids, topk_w, shared_sigma,
+              stream=None) -> None:
+    _check(_lib.moe_route(ctypes.byref(dims), _p(x), _p(w_router), _p(logits_in), _p(w_shared_gate), _p(logits_out),
+                          _p(topk_ids), _p(topk_w), _p(shared_sigma), _s(stream)), "moe_route")
+
+
+def moe_group(dims, layer, topk_ids, slot_table, n_slots, offsets, perm, inv_perm, group_slot, dev_status, ws,
+              ws_bytes: Optional[int] = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.moe_group(ctypes.byref(dims), layer, _p(topk_ids), _p(slot_table), n_slots, _p(offsets), _p(perm),
+                          _p(inv_perm), _p(group_slot), _p(dev_status), _p(ws), ws_bytes, _s(stream)), "moe_group")
+
+
+def moe_expert_ffn(dims, x, pool, pool_bytes, layout: BlobLayout, offsets, perm, group_slot, h, y_rows, dev_status,
+                   ws, ws_bytes: Optional[int] = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.moe_expert_ffn(ctypes.byref(dims), _p(x), _p(pool), pool_bytes, ctypes.byref(layout), _p(offsets),
+                               _p(perm), _p(group_slot), _p(h), _p(y_rows), _p(dev_status), _p(ws), ws_bytes,
+                               _s(stream)), "moe_expert_ffn")
+
+
+def moe_combine(dims, y_rows, inv_perm, topk_w, shared_sigma, y, stream=None) -> None:
+    _check(_lib.moe_combine(ctypes.byref(dims), _p(y_rows), _p(inv_perm), _p(topk_w), _p(shared_sigma), _p(y),
+                            _s(stream)), "moe_combine")
+
+
+def moe_ring_create(slot0, slot1, slot_bytes: int, copy_stream) -> int:
+    out = _vp()
+    _check(_lib.moe_ring_create(_p(slot0), _p(slot1), slot_bytes, _s(copy_stream), ctypes.byref(out)),
+           "moe_ring_create")
+    return out.value
+
+
+def moe_stage_h2d(ring: int, pinned_host_src, nbytes: int) -> int:
+    slot = _i32()
+    _check(_lib.moe_stage_h2d(ring, _p(pinned_host_src), nbytes, ctypes.byref(slot)), "moe_stage_h2d")
+    return slot.value
+
+
+def moe_ring_acquire(ring: int, slot: int, compute_stream=None) -> None:
+    _check(_lib.moe_ring_acquire(ring, slot, _s(compute_stream)), "moe_ring_acquire")
+
+
+def moe_ring_release(ring: int, slot: int, compute_stream=None) -> None:
+    _check(_lib.moe_ring_release(ring, slot, _s(compute_stream)), "moe_ring_release")
+
+
+def moe_ring_slot_ptr(ring: int, slot: int) -> int:
+    out = _vp()
+    _check(_lib.moe_ring_slot_ptr(ring, slot, ctypes.byref(out)), "moe_ring_slot_ptr")
+    return out.value
+
+
+def moe_ring_destroy(ring: int) -> None:
+    _check(_lib.moe_ring_destroy(ring), "moe_ring_destroy")
+
+
+def raw_status(fn_name: str, *args) -> int:
+    """Call a C entry point and return its status without raising (for tests of
+    the argument validation)."""
+    return getattr(_lib, fn_name)(*args)

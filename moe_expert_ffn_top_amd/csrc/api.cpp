@@ -1,0 +1,229 @@
+// libmoe C ABI: argument validation, status codes, launches on the caller's stream.
+// Semantics of every entry point are documented in include/moe.h.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "moe_common.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_width(int32_t v, const char* name) {
+  if (v < 32 || v > 16384 || v % 32 != 0)
+    return fail(MOE_ERR_SHAPE, "%s = %d: must be a multiple of 32 in [32, 16384]", name, v);
+  return MOE_OK;
+}
+
+int check_dims(const moe_dims* d) {
+  if (!d) return fail(MOE_ERR_ARG, "dims is NULL");
+  if (d->T < 1) return fail(MOE_ERR_SHAPE, "T = %d: must be >= 1", d->T);
+  if (d->T > (1 << 20)) return fail(MOE_ERR_SHAPE, "T = %d: must be <= 2^20", d->T);
+  int r = check_width(d->H, "H");
+  if (r) return r;
+  if ((r = check_width(d->I, "I"))) return r;
+  if (d->E < 1 || d->E > 1024) return fail(MOE_ERR_SHAPE, "E = %d: must be in [1, 1024]", d->E);
+  if (d->k < 1 || d->k > d->E) return fail(MOE_ERR_SHAPE, "k = %d: must be in [1, E = %d]", d->k, d->E);
+  if (d->L < 1) return fail(MOE_ERR_SHAPE, "L = %d: must be >= 1", d->L);
+  if ((int64_t)d->T * (d->k + 1) > INT32_MAX / 2) return fail(MOE_ERR_SHAPE, "T * (k + 1) too large");
+  return MOE_OK;
+}
+
+#define REQUIRE(p, align, name)                                                                   \
+  do {                                                                                            \
+    if (!(p)) return fail(MOE_ERR_ARG, "%s is NULL", name);                                       \
+    if (!aligned((p), (align))) return fail(MOE_ERR_ALIGN, "%s is not %d-byte aligned", name, (int)(align)); \
+  } while (0)
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+namespace moe {
+int record_error(int code, const char* msg) {
+  g_last_error = msg;
+  return code;
+}
+}  // namespace moe
+
+extern "C" {
+
+const char* moe_status_string(int s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_ARG: return "MOE_ERR_ARG";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN";
+    case MOE_ERR_NOT_PINNED: return "MOE_ERR_NOT_PINNED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    case MOE_ERR_STATE: return "MOE_ERR_STATE";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+const char* moe_version(void) { return "libmoe 0.1 (gfx950)"; }
+
+int moe_blob_layout_init(int32_t H, int32_t I, moe_blob_layout* out) {
+  if (!out) return fail(MOE_ERR_ARG, "out is NULL");
+  int r = check_width(H, "H");
+  if (r) return r;
+  if ((r = check_width(I, "I"))) return r;
+  const uint64_t rows[3] = {(uint64_t)I, (uint64_t)I, (uint64_t)H};
+  const uint64_t kk[3] = {(uint64_t)H, (uint64_t)H, (uint64_t)I};
+  uint64_t off = 0;
+  for (int m = 0; m < 3; m++) {
+    out->off_codes[m] = off;
+    off = moe::align256(off + rows[m] * kk[m] / 2);
+  }
+  for (int m = 0; m < 3; m++) {
+    out->off_scales[m] = off;
+    off = moe::align256(off + rows[m] * kk[m] / 16);
+  }
+  out->off_globals = off;
+  out->blob_bytes = off + 12;
+  out->slot_stride = (out->blob_bytes + 4095) & ~uint64_t(4095);
+  return ok();
+}
+
+int moe_workspace_bytes(const moe_dims* d, uint64_t* out_bytes) {
+  int r = check_dims(d);
+  if (r) return r;
+  if (!out_bytes) return fail(MOE_ERR_ARG, "out_bytes is NULL");
+  *out_bytes = moe::ws_layout(*d).total;
+  return ok();
+}
+
+int moe_route(const moe_dims* d, const uint16_t* x, const float* w_router, const float* logits_in,
+              const float* w_shared_gate, float* logits_out, int32_t* topk_ids, float* topk_w, float* shared_sigma,
+              moe_stream_t stream) {
+  int r = check_dims(d);
+  if (r) return r;
+  if ((w_router == nullptr) == (logits_in == nullptr))
+    return fail(MOE_ERR_ARG, "exactly one of w_router and logits_in must be given");
+  if (w_router && !logits_out) return fail(MOE_ERR_ARG, "logits_out is required when w_router is given");
+  REQUIRE(x, 16, "x");
+  REQUIRE(w_shared_gate, 4, "w_shared_gate");
+  REQUIRE(topk_ids, 4, "topk_ids");
+  REQUIRE(topk_w, 4, "topk_w");
+  REQUIRE(shared_sigma, 4, "shared_sigma");
+  if (w_router) REQUIRE(w_router, 16, "w_router");
+  if (logits_in) REQUIRE(logits_in, 4, "logits_in");
+  if (logits_out) REQUIRE(logits_out, 4, "logits_out");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const float* lg = logits_in;
+  if (w_router) {
+    hipError_t e = moe::launch_router_matrix(*d, x, w_router, logits_out, s);
+    if (e != hipSuccess) return hip_status(e, "router logits launch");
+    lg = logits_out;
+  } else if (logits_out && logits_out != logits_in) {
+    hipError_t e = hipMemcpyAsync(logits_out, logits_in, (size_t)d->T * d->E * sizeof(float),
+                                  hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_status(e, "logits copy");
+  }
+  return hip_status(moe::launch_topk(*d, lg, x, w_shared_gate, topk_ids, topk_w, shared_sigma, s), "top-k launch");
+}
+
+int moe_group(const moe_dims* d, int32_t layer, const int32_t* topk_ids, const int32_t* slot_table, int32_t n_slots,
+              int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* group_slot, int32_t* dev_status, void* ws,
+              uint64_t ws_bytes, moe_stream_t stream) {
+  int r = check_dims(d);
+  if (r) return r;
+  if (layer < 0 || layer >= d->L) return fail(MOE_ERR_ARG, "layer = %d outside [0, L = %d)", layer, d->L);
+  if (n_slots < 0) return fail(MOE_ERR_ARG, "n_slots = %d < 0", n_slots);
+  REQUIRE(topk_ids, 4, "topk_ids");
+  REQUIRE(slot_table, 4, "slot_table");
+  REQUIRE(offsets, 4, "offsets");
+  REQUIRE(perm, 4, "perm");
+  REQUIRE(inv_perm, 4, "inv_perm");
+  REQUIRE(group_slot, 4, "group_slot");
+  REQUIRE(dev_status, 4, "dev_status");
+  REQUIRE(ws, 16, "ws");
+  const uint64_t need = moe::ws_layout(*d).total;
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace %llu bytes < required %llu", (unsigned long long)ws_bytes,
+                (unsigned long long)need);
+  return hip_status(moe::launch_group(*d, layer, topk_ids, slot_table, n_slots, offsets, perm, inv_perm, group_slot,
+                                      dev_status, ws, reinterpret_cast<hipStream_t>(stream)),
+                    "group launch");
+}
+
+int moe_expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
+                   const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm,
+                   const int32_t* group_slot, uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws,
+                   uint64_t ws_bytes, moe_stream_t stream) {
+  int r = check_dims(d);
+  if (r) return r;
+  if (!layout) return fail(MOE_ERR_ARG, "layout is NULL");
+  moe_blob_layout want;
+  if ((r = moe_blob_layout_init(d->H, d->I, &want))) return r;
+  if (memcmp(&want, layout, sizeof want) != 0)
+    return fail(MOE_ERR_ARG, "layout does not match moe_blob_layout_init(H = %d, I = %d)", d->H, d->I);
+  REQUIRE(x, 16, "x");
+  REQUIRE(pool, 16, "pool");
+  REQUIRE(offsets, 4, "offsets");
+  REQUIRE(perm, 4, "perm");
+  REQUIRE(group_slot, 4, "group_slot");
+  REQUIRE(h, 16, "h");
+  REQUIRE(y_rows, 16, "y_rows");
+  REQUIRE(dev_status, 4, "dev_status");
+  REQUIRE(ws, 16, "ws");
+  const uint64_t need = moe::ws_layout(*d).total;
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace %llu bytes < required %llu", (unsigned long long)ws_bytes,
+                (unsigned long long)need);
+  moe::FfnGeom g;
+  g.pool = static_cast<const uint8_t*>(pool);
+  g.slot_stride = layout->slot_stride;
+  g.n_slots = (int64_t)(pool_bytes / layout->slot_stride);
+  for (int m = 0; m < 3; m++) {
+    g.off_codes[m] = layout->off_codes[m];
+    g.off_scales[m] = layout->off_scales[m];
+  }
+  g.off_globals = layout->off_globals;
+  return hip_status(moe::launch_ffn(*d, x, g, perm, h, y_rows, dev_status, ws, reinterpret_cast<hipStream_t>(stream)),
+                    "expert FFN launch");
+}
+
+int moe_combine(const moe_dims* d, const uint16_t* y_rows, const int32_t* inv_perm, const float* topk_w,
+                const float* shared_sigma, uint16_t* y, moe_stream_t stream) {
+  int r = check_dims(d);
+  if (r) return r;
+  REQUIRE(y_rows, 16, "y_rows");
+  REQUIRE(inv_perm, 4, "inv_perm");
+  REQUIRE(topk_w, 4, "topk_w");
+  REQUIRE(shared_sigma, 4, "shared_sigma");
+  REQUIRE(y, 16, "y");
+  return hip_status(moe::launch_combine(*d, y_rows, inv_perm, topk_w, shared_sigma, y,
+                                        reinterpret_cast<hipStream_t>(stream)),
+                    "combine launch");
+}
+
+}  // extern "C"

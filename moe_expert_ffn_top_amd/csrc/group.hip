@@ -1,0 +1,167 @@
+// S3: grouping of (token, slot) rows by expert through the slot table.
+//
+// [Strata] "路由以后，专家怎样分工？": within one layer and window, the tokens that
+// picked the same expert form one group that records their inputs and output
+// positions, so the expert's weights are read once for the whole group.
+// [Strata] "哪些专家能长期留在显存？": the residency table maps (layer, expert) to a
+// slot, or to a special not-resident value.  [FreeToken] 4: the logical ->
+// physical rewrite stays on the device, with fixed launch shapes and
+// device-side counts, so no host synchronisation is needed.
+//
+// A stable counting sort in three fixed-shape kernels:
+//   count   per 256-entry block, LDS histogram of expert ids (order-free atomics)
+//   scan    one block: per-expert prefix over blocks, exclusive scan over experts,
+//           slot rewrite, and the FFN tile list
+//   scatter per block, one wavefront walks its 4 chunks of 64 entries in order;
+//           inside a chunk, ballots give each entry its rank among equal ids,
+//           so a row's position depends only on the ids (deterministic).
+#include "moe_common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kBlk = 256;
+
+__global__ __launch_bounds__(256) void k_count(const int32_t* __restrict__ ids, int64_t F, int E,
+                                               int32_t* __restrict__ cnt, int32_t* __restrict__ status) {
+  __shared__ int32_t hist[1024];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int64_t f = (int64_t)blockIdx.x * kBlk + threadIdx.x;
+  if (f < F) {
+    const int e = ids[f];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    else atomicOr(status, MOE_DEV_BAD_EXPERT_ID);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// Block-wide exclusive scan for blockDim.x == 1024 (16 wavefronts).
+__device__ int block_exclusive_scan(int v, int* lds16, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) lds16[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    int wv = lane < 16 ? lds16[lane] : 0;
+    int winc = wv;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int o = __shfl_up(winc, off);
+      if (lane >= off) winc += o;
+    }
+    if (lane < 16) lds16[lane] = winc - wv;  // exclusive wave offsets
+    if (lane == 15) lds16[16] = winc;
+  }
+  __syncthreads();
+  const int r = lds16[wave] + inc - v;
+  *total = lds16[16];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(1024) void k_scan(int64_t nb, int T, int k, int E, int layer,
+                                               const int32_t* __restrict__ slot_table, int32_t n_slots,
+                                               int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
+                                               int32_t* __restrict__ group_slot, int32_t* __restrict__ status,
+                                               int32_t* __restrict__ meta, int4* __restrict__ tiles) {
+  __shared__ int lds[17];
+  const int e = threadIdx.x;
+  int count = 0;
+  if (e < E) {
+    for (int64_t b = 0; b < nb; b++) {
+      const int c = cnt[b * E + e];
+      cnt[b * E + e] = count;  // exclusive prefix of expert e over blocks
+      count += c;
+    }
+  }
+  int total = 0;
+  const int off = block_exclusive_scan(count, lds, &total);
+  const int64_t Tk = (int64_t)T * k;
+  int slot = -1;
+  if (e < E) {
+    offsets[e] = off;
+    slot = slot_table[(int64_t)layer * (E + 1) + e];
+    group_slot[e] = slot;
+    if (count > 0 && slot < 0) atomicOr(status, MOE_DEV_NOT_RESIDENT);
+    if (count > 0 && slot >= n_slots) atomicOr(status, MOE_DEV_BAD_SLOT);
+  }
+  if (e == 0) {
+    offsets[E] = total;
+    offsets[E + 1] = (int32_t)(Tk + T);
+    const int ss = slot_table[(int64_t)layer * (E + 1) + E];
+    group_slot[E] = ss;
+    if (ss < 0) atomicOr(status, MOE_DEV_NOT_RESIDENT);
+    if (ss >= n_slots) atomicOr(status, MOE_DEV_BAD_SLOT);
+  }
+  // FFN tiles of kTileRows rows: routed groups in expert order, then the shared group
+  const int nt = (count + kTileRows - 1) / kTileRows;
+  int nt_total = 0;
+  const int tbase = block_exclusive_scan(nt, lds, &nt_total);
+  for (int i = 0; i < nt; i++) {
+    const int n = min(kTileRows, count - i * kTileRows);
+    tiles[tbase + i] = make_int4(e, off + i * kTileRows, n, slot);
+  }
+  const int nts = (T + kTileRows - 1) / kTileRows;
+  const int ss = slot_table[(int64_t)layer * (E + 1) + E];
+  for (int i = threadIdx.x; i < nts; i += blockDim.x)
+    tiles[nt_total + i] = make_int4(E, (int32_t)(Tk + (int64_t)i * kTileRows), min(kTileRows, T - i * kTileRows), ss);
+  if (threadIdx.x == 0) meta[0] = nt_total + nts;
+}
+
+__global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ ids, int64_t F, int E,
+                                                const int32_t* __restrict__ cnt, const int32_t* __restrict__ offsets,
+                                                int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+  __shared__ int32_t run[1024];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) run[e] = offsets[e] + cnt[(int64_t)blockIdx.x * E + e];
+  __syncthreads();
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int c = 0; c < kBlk / 64; c++) {
+    const int64_t f = (int64_t)blockIdx.x * kBlk + c * 64 + lane;
+    const bool in = f < F;
+    const int e = in ? ids[f] : -1;
+    const bool ok = in && e >= 0 && e < E;
+    if (in && !ok) inv_perm[f] = -1;
+    unsigned long long todo = __ballot(ok);
+    while (todo) {
+      const int leader = __ffsll((long long)todo) - 1;
+      const int le = __shfl(e, leader);
+      const unsigned long long mask = __ballot(ok && e == le);
+      const int base = run[le];
+      if (ok && e == le) {
+        const int p = base + __popcll(mask & lt);
+        perm[p] = (int32_t)f;
+        inv_perm[f] = p;
+      }
+      if (lane == leader) run[le] = base + __popcll(mask);
+      todo &= ~mask;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, const int32_t* slot_table,
+                        int32_t n_slots, int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
+                        int32_t* dev_status, void* ws, hipStream_t s) {
+  const WsLayout wl = ws_layout(d);
+  const int64_t F = (int64_t)d.T * d.k;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  int32_t* cnt = reinterpret_cast<int32_t*>(base + wl.off_cnt);
+  int32_t* meta = reinterpret_cast<int32_t*>(base + wl.off_meta);
+  int4* tiles = reinterpret_cast<int4*>(base + wl.off_tiles);
+  hipLaunchKernelGGL(k_count, dim3((unsigned)wl.nb), dim3(256), 0, s, ids, F, d.E, cnt, dev_status);
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, wl.nb, d.T, d.k, d.E, layer, slot_table, n_slots, cnt,
+                     offsets, group_slot, dev_status, meta, tiles);
+  hipLaunchKernelGGL(k_scatter, dim3((unsigned)wl.nb), dim3(64), 0, s, ids, F, d.E, cnt, offsets, perm, inv_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe

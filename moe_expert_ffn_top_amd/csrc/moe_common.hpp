@@ -1,0 +1,115 @@
+// Internal declarations of libmoe: device helpers, workspace layout, launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Rows per FFN tile: the M extent of one v_mfma_f32_16x16x32_bf16.
+constexpr int kTileRows = 16;
+
+// ---- workspace layout (shared by moe_group and moe_expert_ffn) --------------
+// cnt    int32 [nb][E]   per-256-row-block expert counts, then block prefixes
+// meta   int32 [64]      meta[0] = number of FFN tiles
+// tiles  int4  [max_tiles] {group, first row p0, rows n (<= 16), slot}
+struct WsLayout {
+  int64_t nb;         // blocks of 256 flat (token, slot) entries
+  int64_t max_tiles;  // upper bound on FFN tiles
+  uint64_t off_cnt, off_meta, off_tiles, total;
+};
+
+inline uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
+
+inline WsLayout ws_layout(const moe_dims& d) {
+  WsLayout w;
+  const int64_t F = (int64_t)d.T * d.k;
+  w.nb = (F + 255) / 256;
+  const int64_t routed_groups = F < d.E ? F : d.E;
+  w.max_tiles = (F + kTileRows - 1) / kTileRows + routed_groups + (d.T + kTileRows - 1) / kTileRows + 1;
+  w.off_cnt = 0;
+  w.off_meta = align256((uint64_t)w.nb * d.E * 4);
+  w.off_tiles = w.off_meta + 256;
+  w.total = align256(w.off_tiles + (uint64_t)w.max_tiles * 16);
+  return w;
+}
+
+// ---- small device helpers --------------------------------------------------
+__device__ inline float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// E4M3FN byte `sel` (0..3) of w -> fp32 (gfx950 converts the OCP encoding).
+template <int SEL>
+__device__ inline float e4m3_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
+}
+
+// Eight E2M1 codes (one 32-bit word, low nibble first) times the block scale s,
+// as bf16.  code * s has at most 6 significant bits, so the bf16 values are exact.
+__device__ inline bf16x8 dequant8(uint32_t w, float s) {
+  f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  bf16x8 r;
+  r[0] = (__bf16)(p0[0] * s);
+  r[1] = (__bf16)(p0[1] * s);
+  r[2] = (__bf16)(p1[0] * s);
+  r[3] = (__bf16)(p1[1] * s);
+  r[4] = (__bf16)(p2[0] * s);
+  r[5] = (__bf16)(p2[1] * s);
+  r[6] = (__bf16)(p3[0] * s);
+  r[7] = (__bf16)(p3[1] * s);
+  return r;
+}
+
+__device__ inline bf16x8 as_bf16x8(uint4 v) {
+  union {
+    uint4 u;
+    bf16x8 b;
+  } c;
+  c.u = v;
+  return c.b;
+}
+
+__device__ inline f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Sets the calling thread's moe_last_error() text; returns code.
+int record_error(int code, const char* msg);
+
+// ---- launchers (return hipSuccess or the launch error) ---------------------
+struct FfnGeom {
+  const uint8_t* pool;
+  uint64_t slot_stride;
+  int64_t n_slots;
+  uint64_t off_codes[3];
+  uint64_t off_scales[3];
+  uint64_t off_globals;
+};
+
+hipError_t launch_router_matrix(const moe_dims& d, const uint16_t* x, const float* w_router, float* logits,
+                                hipStream_t s);
+hipError_t launch_topk(const moe_dims& d, const float* logits, const uint16_t* x, const float* w_sg,
+                       int32_t* ids, float* w, float* sigma, hipStream_t s);
+hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, const int32_t* slot_table,
+                        int32_t n_slots, int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
+                        int32_t* dev_status, void* ws, hipStream_t s);
+hipError_t launch_ffn(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm,
+                      uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws, hipStream_t s);
+hipError_t launch_combine(const moe_dims& d, const uint16_t* y_rows, const int32_t* inv_perm, const float* w,
+                          const float* sigma, uint16_t* y, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,140 @@
+"""libmoe's C ABI on the CPU: it loads, exports what include/moe.h declares, its
+host-pure functions agree with the format spec, and argument validation
+returns the documented codes without enqueueing anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+from oracle import moe_oracle as O
+
+
+@pytest.fixture(scope="module")
+def B():
+    from moe_expert_ffn_top_amd import binding
+    return binding
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(B):
+    declared = _declared_functions()
+    assert len(declared) >= 15
+    assert sorted(B.EXPORTED) == declared
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(B):
+    assert "gfx950" in B.moe_version()
+    assert B.moe_status_string(0) == "MOE_OK"
+    for code in range(-7, 0):
+        assert B.moe_status_string(code).startswith("MOE_ERR_")
+
+
+@pytest.mark.parametrize("H,I", [(32, 32), (512, 256), (2048, 512), (4096, 2048), (96, 160), (16384, 32)])
+def test_blob_layout_matches_format_spec(B, H, I):
+    lay = B.moe_blob_layout_init(H, I)
+    ref = O.blob_layout(H, I)
+    assert tuple(lay.off_codes) == ref.off_codes
+    assert tuple(lay.off_scales) == ref.off_scales
+    assert lay.off_globals == ref.off_globals
+    assert lay.blob_bytes == ref.blob_bytes and lay.slot_stride == ref.slot_stride
+
+
+@pytest.mark.parametrize("H,I", [(0, 32), (48, 32), (32, 16400), (32, -32)])
+def test_blob_layout_rejects_bad_widths(B, H, I):
+    with pytest.raises(B.MoeError) as e:
+        B.moe_blob_layout_init(H, I)
+    assert e.value.status == B.MOE_ERR_SHAPE
+
+
+@pytest.mark.parametrize("dims,code", [
+    ((0, 512, 256, 32, 4, 1), "MOE_ERR_SHAPE"),      # empty input: T = 0
+    ((8, 500, 256, 32, 4, 1), "MOE_ERR_SHAPE"),      # H % 32 != 0
+    ((8, 512, 256, 32, 33, 1), "MOE_ERR_SHAPE"),     # k > E
+    ((8, 512, 256, 1025, 4, 1), "MOE_ERR_SHAPE"),    # E > 1024
+    ((8, 512, 256, 32, 0, 1), "MOE_ERR_SHAPE"),      # k = 0
+    ((8, 512, 256, 32, 4, 0), "MOE_ERR_SHAPE"),      # L = 0
+])
+def test_workspace_rejects_bad_dims(B, dims, code):
+    with pytest.raises(B.MoeError) as e:
+        B.moe_workspace_bytes(B.Dims(*dims))
+    assert B.moe_status_string(e.value.status) == code
+
+
+def test_workspace_grows_with_tokens(B):
+    a = B.moe_workspace_bytes(B.Dims(4, 2048, 512, 512, 10, 48))
+    b = B.moe_workspace_bytes(B.Dims(8192, 2048, 512, 512, 10, 1))
+    assert 0 < a < b and a % 256 == 0 and b % 256 == 0
+
+
+def _d(B):
+    return B.Dims(8, 512, 256, 32, 4, 1)
+
+
+def test_route_validation(B):
+    d = ctypes.byref(_d(B))
+    fake = 1 << 20  # an aligned non-null address; never dereferenced on these paths
+    # neither router matrix nor logits
+    assert B.raw_status("moe_route", d, fake, None, None, fake, None, fake, fake, fake, None) == B.MOE_ERR_ARG
+    # both
+    assert B.raw_status("moe_route", d, fake, fake, fake, fake, fake, fake, fake, fake, None) == B.MOE_ERR_ARG
+    # router matrix without logits_out
+    assert B.raw_status("moe_route", d, fake, fake, None, fake, None, fake, fake, fake, None) == B.MOE_ERR_ARG
+    # NULL x
+    assert B.raw_status("moe_route", d, None, None, fake, fake, None, fake, fake, fake, None) == B.MOE_ERR_ARG
+    # misaligned x
+    assert B.raw_status("moe_route", d, fake + 2, None, fake, fake, None, fake, fake, fake, None) == B.MOE_ERR_ALIGN
+
+
+def test_group_validation(B):
+    dims = _d(B)
+    d = ctypes.byref(dims)
+    fake = 1 << 20
+    need = B.moe_workspace_bytes(dims)
+    args = [fake, fake, 4, fake, fake, fake, fake, fake, fake]
+    assert B.raw_status("moe_group", d, 0, *args, need - 1, None) == B.MOE_ERR_WORKSPACE
+    assert B.raw_status("moe_group", d, 1, *args, need, None) == B.MOE_ERR_ARG        # layer >= L
+    assert B.raw_status("moe_group", d, -1, *args, need, None) == B.MOE_ERR_ARG
+    bad = list(args)
+    bad[0] = None
+    assert B.raw_status("moe_group", d, 0, *bad, need, None) == B.MOE_ERR_ARG
+
+
+def test_ffn_validation(B):
+    dims = _d(B)
+    d = ctypes.byref(dims)
+    fake = 1 << 20
+    lay = B.moe_blob_layout_init(512, 256)
+    need = B.moe_workspace_bytes(dims)
+    ok_args = (fake, fake, 1 << 30, ctypes.byref(lay), fake, fake, fake, fake, fake, fake, fake, need, None)
+    wrong = B.moe_blob_layout_init(512, 512)
+    bad_layout = list(ok_args)
+    bad_layout[3] = ctypes.byref(wrong)
+    assert B.raw_status("moe_expert_ffn", d, *bad_layout) == B.MOE_ERR_ARG
+    short_ws = list(ok_args)
+    short_ws[11] = need - 256
+    assert B.raw_status("moe_expert_ffn", d, *short_ws) == B.MOE_ERR_WORKSPACE
+    unaligned_pool = list(ok_args)
+    unaligned_pool[1] = fake + 8
+    assert B.raw_status("moe_expert_ffn", d, *unaligned_pool) == B.MOE_ERR_ALIGN
+
+
+def test_combine_and_ring_validation(B):
+    d = ctypes.byref(_d(B))
+    fake = 1 << 20
+    assert B.raw_status("moe_combine", d, None, fake, fake, fake, fake, None) == B.MOE_ERR_ARG
+    assert B.raw_status("moe_combine", d, fake, fake, fake, fake, fake + 4, None) == B.MOE_ERR_ALIGN
+    out = ctypes.c_void_p()
+    assert B.raw_status("moe_ring_create", None, fake, 4096, None, ctypes.byref(out)) == B.MOE_ERR_ARG
+    assert B.raw_status("moe_ring_create", fake, fake + 1, 4096, None, ctypes.byref(out)) == B.MOE_ERR_ALIGN
+    assert B.raw_status("moe_ring_destroy", None) == B.MOE_ERR_ARG
+    assert B.raw_status("moe_ring_acquire", None, 0, None) == B.MOE_ERR_ARG

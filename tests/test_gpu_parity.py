@@ -1,0 +1,177 @@
+"""GPU parity at sizes the oracle finishes in seconds (every output compared).
+
+Covers the tiny workload, several FFN tiles with ragged tails, a reduction
+axis that is not a multiple of the 128-value step, degenerate shapes (T = 1,
+E = k = 1, k = E, E = 1024), a non-resident slot, an out-of-range expert id,
+token-permutation invariance and run-to-run determinism."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import assert_close, bf16_to_f64, compare_layer, say
+from oracle import moe_oracle as O
+from synth import CONFIGS, Config, HostGen, zipf_logits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from moe_expert_ffn_top_amd import binding
+    return binding
+
+
+class Case:
+    """Host-generated inputs of one layer (layer 0), uploaded to the GPU."""
+
+    def __init__(self, B, cfg: Config, gen: HostGen, slot_override=None):
+        from moe_expert_ffn_top_amd.layer import LayerBuffers
+        self.cfg = cfg
+        self.dims = B.Dims(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, 1)
+        self.layout = B.moe_blob_layout_init(cfg.H, cfg.I)
+        olay = O.blob_layout(cfg.H, cfg.I)
+        E1 = cfg.E + 1
+        self.blobs = {e: gen.expert_blob(cfg, 0, e, olay) for e in range(E1)}
+        pool = np.concatenate([self.blobs[e] for e in range(E1)])
+        self.pool = torch.from_numpy(pool).cuda()
+        self.pool_bytes = pool.nbytes
+        st = np.arange(E1, dtype=np.int32)[None, :].copy()
+        if slot_override:
+            for e, s in slot_override.items():
+                st[0, e] = s
+        self.slot_table = torch.from_numpy(st).cuda()
+        self.x_bits = gen.x(cfg, 0, 0)
+        self.x = torch.from_numpy(self.x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+        self.wsg = gen.w_shared_gate(cfg, 0)
+        self.wsg_t = torch.from_numpy(self.wsg).cuda()
+        if cfg.router == "matrix":
+            self.wr = gen.w_router(cfg, 0)
+            self.wr_t = torch.from_numpy(self.wr).cuda()
+            self.logits = None
+        else:
+            self.wr = None
+            self.wr_t = None
+            self.logits = zipf_logits(cfg, 0, 0)
+            self.logits_t = torch.from_numpy(self.logits).cuda()
+        self.buf = LayerBuffers.allocate(self.dims)
+
+    def run(self, B):
+        from moe_expert_ffn_top_amd.layer import run_layer
+        run_layer(self.buf, 0, self.x, self.pool, self.pool_bytes, self.layout, self.slot_table, self.cfg.E1,
+                  self.wsg_t, w_router=self.wr_t, logits=None if self.logits is None else self.logits_t)
+        torch.cuda.synchronize()
+
+    def oracle(self, **kw):
+        c = self.cfg
+        return O.moe_layer(self.x_bits, lambda e: self.blobs[e], c.H, c.I, c.E, c.k, self.wsg,
+                           w_router=self.wr, logits=self.logits, **kw)
+
+    def compare(self, ora, **kw):
+        return compare_layer(self.buf, ora, self.cfg.T, self.cfg.k, self.cfg.E, drawn_logits=self.logits is not None,
+                             x64=O.bf16_bits_to_f64(self.x_bits), w_router=self.wr, **kw)
+
+
+SMALL = {
+    "tiny": CONFIGS[1],
+    "multitile_ragged": Config(31, "mt", T=100, H=512, I=256, E=8, k=2, L=1, router="matrix"),
+    "ragged_K_zipf": Config(32, "rk", T=37, H=96, I=160, E=6, k=3, L=1, router="zipf", zipf_s=1.0),
+    "degenerate_T1_E1": Config(33, "deg", T=1, H=64, I=32, E=1, k=1, L=1, router="matrix"),
+    "k_equals_E": Config(34, "kE", T=5, H=128, I=64, E=6, k=6, L=1, router="zipf", zipf_s=0.5),
+    "E1024_max": Config(35, "E1024", T=3, H=64, I=64, E=1024, k=8, L=1, router="zipf", zipf_s=1.0),
+    "big_k_wide": Config(36, "bk", T=19, H=1024, I=512, E=64, k=16, L=1, router="matrix"),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_parity_small(B, hostgen, name):
+    cfg = SMALL[name]
+    say("[gpu] parity case %s T=%d H=%d I=%d E=%d k=%d" % (name, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k))
+    case = Case(B, cfg, hostgen)
+    case.run(B)
+    assert int(case.buf.status.item()) == 0
+    stats = case.compare(case.oracle())
+    say("[gpu]   %s ok: %s" % (name, stats))
+
+
+def test_non_resident_slot_gives_zero_rows_and_status(B, hostgen):
+    cfg = CONFIGS[1]
+    say("[gpu] non-resident slot case")
+    probe = Case(B, cfg, hostgen)
+    probe.run(B)
+    ids = probe.buf.ids.cpu().numpy()
+    missing = int(ids[0, 0])            # an expert that token 0 picks
+    case = Case(B, cfg, hostgen, slot_override={missing: -1})
+    case.run(B)
+    assert int(case.buf.status.item()) & B.MOE_DEV_NOT_RESIDENT
+    ora = case.oracle()
+    inv = case.buf.inv_perm.cpu().numpy()
+    T, k = cfg.T, cfg.k
+    yr = np.zeros((T, k, cfg.H))
+    for t in range(T):
+        for j in range(k):
+            if ora.ids[t, j] != missing:
+                yr[t, j] = ora.y_rows[int(ora.groups.inv_perm[t * k + j])]
+    ysh = np.stack([ora.y_rows[T * k + t] for t in range(T)])
+    y_ref, _ = O.combine(yr, ora.w, ora.sigma, ysh)
+    rows = [int(inv[t * k + j]) for t in range(T) for j in range(k) if ids[t, j] == missing]
+    assert rows and np.all(bf16_to_f64(case.buf.y_rows[rows]) == 0)
+    assert np.all(bf16_to_f64(case.buf.h[rows]) == 0)
+    assert_close(bf16_to_f64(case.buf.y), y_ref, "y with a non-resident expert")
+
+
+def test_bad_expert_id_is_dropped_and_flagged(B, hostgen):
+    cfg = CONFIGS[1]
+    say("[gpu] bad expert id case")
+    case = Case(B, cfg, hostgen)
+    case.run(B)
+    ora = case.oracle()
+    d, buf = case.dims, case.buf
+    ids = buf.ids.clone()
+    ids[2, 1] = cfg.E            # out of range
+    buf.status.zero_()
+    B.moe_group(d, 0, ids, case.slot_table, cfg.E1, buf.offsets, buf.perm, buf.inv_perm, buf.group_slot,
+                buf.status, buf.ws)
+    B.moe_expert_ffn(d, case.x, case.pool, case.pool_bytes, case.layout, buf.offsets, buf.perm, buf.group_slot,
+                     buf.h, buf.y_rows, buf.status, buf.ws)
+    B.moe_combine(d, buf.y_rows, buf.inv_perm, buf.w, buf.sigma, buf.y)
+    torch.cuda.synchronize()
+    assert int(buf.status.item()) & B.MOE_DEV_BAD_EXPERT_ID
+    assert int(buf.inv_perm[2 * cfg.k + 1].item()) == -1
+    off = buf.offsets.cpu().numpy()
+    assert off[cfg.E] == cfg.T * cfg.k - 1 and off[cfg.E + 1] == cfg.T * cfg.k + cfg.T
+    T, k = cfg.T, cfg.k
+    yr = np.stack([np.stack([ora.y_rows[int(ora.groups.inv_perm[t * k + j])] for j in range(k)]) for t in range(T)])
+    yr[2, 1] = 0.0
+    ysh = np.stack([ora.y_rows[T * k + t] for t in range(T)])
+    y_ref, _ = O.combine(yr, ora.w, ora.sigma, ysh)
+    assert_close(bf16_to_f64(buf.y), y_ref, "y with a dropped id")
+
+
+def test_token_permutation_bit_exact_on_gpu(B, hostgen):
+    cfg = SMALL["multitile_ragged"]
+    say("[gpu] token permutation case")
+    a = Case(B, cfg, hostgen)
+    a.run(B)
+    pi = np.random.default_rng(7).permutation(cfg.T)
+    b = Case(B, cfg, hostgen)
+    b.x_bits = a.x_bits[pi]
+    b.x = torch.from_numpy(b.x_bits.view(np.int16).copy()).cuda().view(torch.bfloat16)
+    b.run(B)
+    pi_t = torch.as_tensor(pi, device="cuda")
+    assert torch.equal(b.buf.ids, a.buf.ids[pi_t])
+    assert torch.equal(b.buf.y.view(torch.int16), a.buf.y.view(torch.int16)[pi_t])
+
+
+def test_run_to_run_determinism(B, hostgen):
+    cfg = SMALL["multitile_ragged"]
+    say("[gpu] determinism case")
+    a = Case(B, cfg, hostgen)
+    a.run(B)
+    first = [t.clone() for t in (a.buf.ids, a.buf.perm, a.buf.h.view(torch.int16), a.buf.y.view(torch.int16))]
+    for _ in range(3):
+        a.run(B)
+        again = (a.buf.ids, a.buf.perm, a.buf.h.view(torch.int16), a.buf.y.view(torch.int16))
+        for u, v in zip(first, again):
+            assert torch.equal(u, v)
