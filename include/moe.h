@@ -134,7 +134,8 @@ int moe_workspace_bytes(const moe_dims* d, uint64_t* out_bytes);
  *             accumulated in fp32 (rounding point R0: fp32 logits).
  *   logits_in device fp32 [T][E]: used as given.
  * x            device bf16 bits [T][H] row-major (required: the shared gate reads it).
- * w_shared_gate device fp32 [H]: sigma[t] = 1 / (1 + exp(-sum_h x[t,h] w_sg[h])).
+ * w_shared_gate device fp32 [H], 16-byte aligned:
+ *              sigma[t] = 1 / (1 + exp(-sum_h x[t,h] w_sg[h])).
  * logits_out   device fp32 [T][E] or NULL: receives the logits used.
  * topk_ids     device int32 [T][k]: slot j holds the j-th largest logit; ties
  *              go to the lower expert index.

@@ -60,23 +60,38 @@ class MoeError(RuntimeError):
 
 _vp, _i32, _u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64
 _DP = ctypes.POINTER(Dims)
-_lib.moe_status_string.restype = ctypes.c_char_p
-_lib.moe_status_string.argtypes = [ctypes.c_int]
-_lib.moe_last_error.restype = ctypes.c_char_p
-_lib.moe_version.restype = ctypes.c_char_p
-_lib.moe_blob_layout_init.argtypes = [_i32, _i32, ctypes.POINTER(BlobLayout)]
-_lib.moe_workspace_bytes.argtypes = [_DP, ctypes.POINTER(_u64)]
-_lib.moe_route.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
-_lib.moe_group.argtypes = [_DP, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _u64, _vp]
-_lib.moe_expert_ffn.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                _u64, _vp]
-_lib.moe_combine.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp]
-_lib.moe_ring_create.argtypes = [_vp, _vp, _u64, _vp, ctypes.POINTER(_vp)]
-_lib.moe_stage_h2d.argtypes = [_vp, _vp, _u64, ctypes.POINTER(_i32)]
-_lib.moe_ring_acquire.argtypes = [_vp, _i32, _vp]
-_lib.moe_ring_release.argtypes = [_vp, _i32, _vp]
-_lib.moe_ring_slot_ptr.argtypes = [_vp, _i32, ctypes.POINTER(_vp)]
-_lib.moe_ring_destroy.argtypes = [_vp]
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Declare the C signatures of include/moe.h on a loaded library."""
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_last_error.restype = ctypes.c_char_p
+    lib.moe_version.restype = ctypes.c_char_p
+    lib.moe_blob_layout_init.argtypes = [_i32, _i32, ctypes.POINTER(BlobLayout)]
+    lib.moe_workspace_bytes.argtypes = [_DP, ctypes.POINTER(_u64)]
+    lib.moe_route.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.moe_group.argtypes = [_DP, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _u64, _vp]
+    lib.moe_expert_ffn.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _vp, _vp,
+                                   _vp, _u64, _vp]
+    lib.moe_combine.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.moe_ring_create.argtypes = [_vp, _vp, _u64, _vp, ctypes.POINTER(_vp)]
+    lib.moe_stage_h2d.argtypes = [_vp, _vp, _u64, ctypes.POINTER(_i32)]
+    lib.moe_ring_acquire.argtypes = [_vp, _i32, _vp]
+    lib.moe_ring_release.argtypes = [_vp, _i32, _vp]
+    lib.moe_ring_slot_ptr.argtypes = [_vp, _i32, ctypes.POINTER(_vp)]
+    lib.moe_ring_destroy.argtypes = [_vp]
+    return lib
+
+
+_bind(_lib)
+
+
+def use_library(path: str) -> None:
+    """Route every call of this module to another build of libmoe (e.g. a
+    build with different kernel tuning constants)."""
+    global _lib
+    _lib = _bind(ctypes.CDLL(path))
 
 
 def _p(t) -> Optional[int]:

@@ -130,7 +130,7 @@ int moe_route(const moe_dims* d, const uint16_t* x, const float* w_router, const
     return fail(MOE_ERR_ARG, "exactly one of w_router and logits_in must be given");
   if (w_router && !logits_out) return fail(MOE_ERR_ARG, "logits_out is required when w_router is given");
   REQUIRE(x, 16, "x");
-  REQUIRE(w_shared_gate, 4, "w_shared_gate");
+  REQUIRE(w_shared_gate, 16, "w_shared_gate");
   REQUIRE(topk_ids, 4, "topk_ids");
   REQUIRE(topk_w, 4, "topk_w");
   REQUIRE(shared_sigma, 4, "shared_sigma");

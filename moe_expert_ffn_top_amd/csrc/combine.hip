@@ -20,16 +20,28 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ yr
   const int col = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (col >= H) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; j++) {
-    const int p = inv[(int64_t)t * k + j];
-    if (p < 0) continue;
-    const float wj = w[(int64_t)t * k + j];
-    const uint4 v = *reinterpret_cast<const uint4*>(yr + (int64_t)p * H + col);
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  // batches of 8 slots: indices and weights, then the rows, then the math in slot order
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int p[8];
+    float wj[8];
+    uint4 v[8];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      acc[2 * i] = fmaf(wj, bf16_bits_to_f32(u[i] & 0xFFFFu), acc[2 * i]);
-      acc[2 * i + 1] = fmaf(wj, bf16_bits_to_f32(u[i] >> 16), acc[2 * i + 1]);
+    for (int u = 0; u < 8; u++) {
+      p[u] = (j0 + u < k) ? inv[(int64_t)t * k + j0 + u] : -1;
+      wj[u] = (j0 + u < k) ? w[(int64_t)t * k + j0 + u] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; u++)
+      v[u] = (p[u] >= 0) ? *reinterpret_cast<const uint4*>(yr + (int64_t)p[u] * H + col) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      if (p[u] < 0) continue;
+      const uint32_t uu[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        acc[2 * i] = fmaf(wj[u], bf16_bits_to_f32(uu[i] & 0xFFFFu), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(wj[u], bf16_bits_to_f32(uu[i] >> 16), acc[2 * i + 1]);
+      }
     }
   }
   const float st = sigma[t];

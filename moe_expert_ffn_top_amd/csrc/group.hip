@@ -8,7 +8,8 @@
 // physical rewrite stays on the device, with fixed launch shapes and
 // device-side counts, so no host synchronisation is needed.
 //
-// A stable counting sort in three fixed-shape kernels:
+// Up to 256 (token, slot) entries (decode): one fused single-block kernel.
+// Otherwise a stable counting sort in three fixed-shape kernels:
 //   count   per 256-entry block, LDS histogram of expert ids (order-free atomics)
 //   scan    one block: per-expert prefix over blocks, exclusive scan over experts,
 //           slot rewrite, and the FFN tile list
@@ -66,6 +67,47 @@ __device__ int block_exclusive_scan(int v, int* lds16, int* total) {
   return r;
 }
 
+// Thread e (< E) holds count = rows of expert e.  Writes offsets, group_slot,
+// residency status and the FFN tile list; returns this expert's first row.
+__device__ int scan_and_tiles(int count, int T, int k, int E, int layer, const int32_t* __restrict__ slot_table,
+                              int32_t n_slots, int32_t* __restrict__ offsets, int32_t* __restrict__ group_slot,
+                              int32_t* __restrict__ status, int32_t* __restrict__ meta, int4* __restrict__ tiles,
+                              int* lds17) {
+  const int e = threadIdx.x;
+  int total = 0;
+  const int off = block_exclusive_scan(count, lds17, &total);
+  const int64_t Tk = (int64_t)T * k;
+  int slot = -1;
+  if (e < E) {
+    offsets[e] = off;
+    slot = slot_table[(int64_t)layer * (E + 1) + e];
+    group_slot[e] = slot;
+    if (count > 0 && slot < 0) atomicOr(status, MOE_DEV_NOT_RESIDENT);
+    if (count > 0 && slot >= n_slots) atomicOr(status, MOE_DEV_BAD_SLOT);
+  }
+  const int ss = slot_table[(int64_t)layer * (E + 1) + E];
+  if (e == 0) {
+    offsets[E] = total;
+    offsets[E + 1] = (int32_t)(Tk + T);
+    group_slot[E] = ss;
+    if (ss < 0) atomicOr(status, MOE_DEV_NOT_RESIDENT);
+    if (ss >= n_slots) atomicOr(status, MOE_DEV_BAD_SLOT);
+  }
+  // FFN tiles of kTileRows rows: routed groups in expert order, then the shared group
+  const int nt = (count + kTileRows - 1) / kTileRows;
+  int nt_total = 0;
+  const int tbase = block_exclusive_scan(nt, lds17, &nt_total);
+  for (int i = 0; i < nt; i++) {
+    const int n = min(kTileRows, count - i * kTileRows);
+    tiles[tbase + i] = make_int4(e, off + i * kTileRows, n, slot);
+  }
+  const int nts = (T + kTileRows - 1) / kTileRows;
+  for (int i = threadIdx.x; i < nts; i += blockDim.x)
+    tiles[nt_total + i] = make_int4(E, (int32_t)(Tk + (int64_t)i * kTileRows), min(kTileRows, T - i * kTileRows), ss);
+  if (threadIdx.x == 0) meta[0] = nt_total + nts;
+  return off;
+}
+
 __global__ __launch_bounds__(1024) void k_scan(int64_t nb, int T, int k, int E, int layer,
                                                const int32_t* __restrict__ slot_table, int32_t n_slots,
                                                int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
@@ -81,38 +123,53 @@ __global__ __launch_bounds__(1024) void k_scan(int64_t nb, int T, int k, int E, 
       count += c;
     }
   }
-  int total = 0;
-  const int off = block_exclusive_scan(count, lds, &total);
-  const int64_t Tk = (int64_t)T * k;
-  int slot = -1;
-  if (e < E) {
-    offsets[e] = off;
-    slot = slot_table[(int64_t)layer * (E + 1) + e];
-    group_slot[e] = slot;
-    if (count > 0 && slot < 0) atomicOr(status, MOE_DEV_NOT_RESIDENT);
-    if (count > 0 && slot >= n_slots) atomicOr(status, MOE_DEV_BAD_SLOT);
+  scan_and_tiles(count, T, k, E, layer, slot_table, n_slots, offsets, group_slot, status, meta, tiles, lds);
+}
+
+// Whole grouping in one 1024-thread block for F = T*k <= kSmallF entries: the
+// rank of an entry is the number of earlier entries with the same expert,
+// counted directly over the ids staged in LDS.
+constexpr int kSmallF = 256;
+
+__global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict__ ids, int F, int T, int k, int E,
+                                                      int layer, const int32_t* __restrict__ slot_table,
+                                                      int32_t n_slots, int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+                                                      int32_t* __restrict__ group_slot, int32_t* __restrict__ status,
+                                                      int32_t* __restrict__ meta, int4* __restrict__ tiles) {
+  __shared__ int32_t hist[1024];
+  __shared__ int32_t sid[kSmallF];
+  __shared__ int lds[17];
+  const int tid = threadIdx.x;
+  if (tid < E) hist[tid] = 0;
+  int e_mine = -1;
+  if (tid < F) {
+    e_mine = ids[tid];
+    if (e_mine < 0 || e_mine >= E) {
+      atomicOr(status, MOE_DEV_BAD_EXPERT_ID);
+      e_mine = -1;
+    }
+    sid[tid] = e_mine;
   }
-  if (e == 0) {
-    offsets[E] = total;
-    offsets[E + 1] = (int32_t)(Tk + T);
-    const int ss = slot_table[(int64_t)layer * (E + 1) + E];
-    group_slot[E] = ss;
-    if (ss < 0) atomicOr(status, MOE_DEV_NOT_RESIDENT);
-    if (ss >= n_slots) atomicOr(status, MOE_DEV_BAD_SLOT);
+  __syncthreads();
+  if (e_mine >= 0) atomicAdd(&hist[e_mine], 1);
+  __syncthreads();
+  const int count = tid < E ? hist[tid] : 0;
+  const int off = scan_and_tiles(count, T, k, E, layer, slot_table, n_slots, offsets, group_slot, status, meta, tiles,
+                                 lds);
+  if (tid < E) hist[tid] = off;  // hist now holds each expert's first row
+  __syncthreads();
+  if (tid < F) {
+    if (e_mine < 0) {
+      inv_perm[tid] = -1;
+    } else {
+      int rank = 0;
+      for (int f = 0; f < F; f++) rank += (f < tid && sid[f] == e_mine) ? 1 : 0;
+      const int p = hist[e_mine] + rank;
+      perm[p] = tid;
+      inv_perm[tid] = p;
+    }
   }
-  // FFN tiles of kTileRows rows: routed groups in expert order, then the shared group
-  const int nt = (count + kTileRows - 1) / kTileRows;
-  int nt_total = 0;
-  const int tbase = block_exclusive_scan(nt, lds, &nt_total);
-  for (int i = 0; i < nt; i++) {
-    const int n = min(kTileRows, count - i * kTileRows);
-    tiles[tbase + i] = make_int4(e, off + i * kTileRows, n, slot);
-  }
-  const int nts = (T + kTileRows - 1) / kTileRows;
-  const int ss = slot_table[(int64_t)layer * (E + 1) + E];
-  for (int i = threadIdx.x; i < nts; i += blockDim.x)
-    tiles[nt_total + i] = make_int4(E, (int32_t)(Tk + (int64_t)i * kTileRows), min(kTileRows, T - i * kTileRows), ss);
-  if (threadIdx.x == 0) meta[0] = nt_total + nts;
 }
 
 __global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ ids, int64_t F, int E,
@@ -157,6 +214,11 @@ hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, co
   int32_t* cnt = reinterpret_cast<int32_t*>(base + wl.off_cnt);
   int32_t* meta = reinterpret_cast<int32_t*>(base + wl.off_meta);
   int4* tiles = reinterpret_cast<int4*>(base + wl.off_tiles);
+  if (F <= kSmallF) {
+    hipLaunchKernelGGL(k_group_small, dim3(1), dim3(1024), 0, s, ids, (int)F, d.T, d.k, d.E, layer, slot_table,
+                       n_slots, offsets, perm, inv_perm, group_slot, dev_status, meta, tiles);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_count, dim3((unsigned)wl.nb), dim3(256), 0, s, ids, F, d.E, cnt, dev_status);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, wl.nb, d.T, d.k, d.E, layer, slot_table, n_slots, cnt,
                      offsets, group_slot, dev_status, meta, tiles);

@@ -117,9 +117,37 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
       win_i[j] = bi;
     }
   }
-  // shared gate: z = x[t] . w_sg, fixed lane-stride order then a fixed tree
+  // shared gate: z = x[t] . w_sg.  Lane l takes 8-value chunks l, l+64, ...;
+  // loads of 4 chunks are issued before their math; then a fixed xor tree.
   float z = 0.0f;
-  for (int h = lane; h < H; h += 64) z = fmaf(bf16_bits_to_f32(x[(int64_t)t * H + h]), w_sg[h], z);
+  const int nch = H / 8;
+  const uint16_t* xr = x + (int64_t)t * H;
+  for (int c0 = 0; c0 < nch; c0 += 4 * 64) {
+    uint4 xv[4];
+    float4 wv[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int c = c0 + u * 64 + lane;
+      xv[u] = make_uint4(0, 0, 0, 0);
+      wv[u][0] = wv[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c < nch) {
+        xv[u] = *reinterpret_cast<const uint4*>(xr + 8 * c);
+        wv[u][0] = *reinterpret_cast<const float4*>(w_sg + 8 * c);
+        wv[u][1] = *reinterpret_cast<const float4*>(w_sg + 8 * c + 4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const uint32_t xs[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+      const float ws[8] = {wv[u][0].x, wv[u][0].y, wv[u][0].z, wv[u][0].w,
+                           wv[u][1].x, wv[u][1].y, wv[u][1].z, wv[u][1].w};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        z = fmaf(bf16_bits_to_f32(xs[i] & 0xFFFFu), ws[2 * i], z);
+        z = fmaf(bf16_bits_to_f32(xs[i] >> 16), ws[2 * i + 1], z);
+      }
+    }
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
   // lane 0 wrote the winners above and is the only reader: no barrier needed
