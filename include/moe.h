@@ -191,7 +191,8 @@ int moe_group(const moe_dims* d, int32_t layer, const int32_t* topk_ids,
  * with the matrices decoded from the blob at pool + group_slot[e]*slot_stride.
  * Weight codes and scales multiply exactly; sums are fp32.
  * x          device bf16 [T][H].
- * pool       device, pool_bytes long; every slot used must lie inside it.
+ * pool       device, pool_bytes long (at least one slot_stride, MOE_ERR_ARG
+ *            otherwise); every slot used must lie inside it.
  * h          device bf16 [T*k+T][I] (intermediate, also an output).
  * y_rows     device bf16 [T*k+T][H]: unweighted expert outputs per row.
  * Rows of a group whose slot is -1 or >= pool_bytes/slot_stride are written

@@ -199,6 +199,13 @@ int moe_expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool, uint6
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace %llu bytes < required %llu", (unsigned long long)ws_bytes,
                 (unsigned long long)need);
+  if (pool_bytes < layout->slot_stride)
+    return fail(MOE_ERR_ARG, "pool_bytes %llu is smaller than one slot (%llu)", (unsigned long long)pool_bytes,
+                (unsigned long long)layout->slot_stride);
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || n_cu <= 0)
+    return fail(MOE_ERR_HIP, "cannot query the device's compute-unit count");
   moe::FfnGeom g;
   g.pool = static_cast<const uint8_t*>(pool);
   g.slot_stride = layout->slot_stride;
@@ -208,7 +215,7 @@ int moe_expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool, uint6
     g.off_scales[m] = layout->off_scales[m];
   }
   g.off_globals = layout->off_globals;
-  return hip_status(moe::launch_ffn(*d, x, g, perm, h, y_rows, dev_status, ws, reinterpret_cast<hipStream_t>(stream)),
+  return hip_status(moe::launch_ffn_dec(*d, x, g, perm, h, y_rows, ws, n_cu, reinterpret_cast<hipStream_t>(stream)),
                     "expert FFN launch");
 }
 

@@ -72,7 +72,8 @@ __device__ int block_exclusive_scan(int v, int* lds16, int* total) {
 __device__ int scan_and_tiles(int count, int T, int k, int E, int layer, const int32_t* __restrict__ slot_table,
                               int32_t n_slots, int32_t* __restrict__ offsets, int32_t* __restrict__ group_slot,
                               int32_t* __restrict__ status, int32_t* __restrict__ meta, int4* __restrict__ tiles,
-                              int* lds17) {
+                              int32_t* __restrict__ tile_tok, int32_t* __restrict__ tile_base, int* lds17,
+                              int* tbase_out = nullptr) {
   const int e = threadIdx.x;
   int total = 0;
   const int off = block_exclusive_scan(count, lds17, &total);
@@ -97,6 +98,8 @@ __device__ int scan_and_tiles(int count, int T, int k, int E, int layer, const i
   const int nt = (count + kTileRows - 1) / kTileRows;
   int nt_total = 0;
   const int tbase = block_exclusive_scan(nt, lds17, &nt_total);
+  if (e < E) tile_base[e] = tbase;
+  if (tbase_out) *tbase_out = tbase;
   for (int i = 0; i < nt; i++) {
     const int n = min(kTileRows, count - i * kTileRows);
     tiles[tbase + i] = make_int4(e, off + i * kTileRows, n, slot);
@@ -104,6 +107,11 @@ __device__ int scan_and_tiles(int count, int T, int k, int E, int layer, const i
   const int nts = (T + kTileRows - 1) / kTileRows;
   for (int i = threadIdx.x; i < nts; i += blockDim.x)
     tiles[nt_total + i] = make_int4(E, (int32_t)(Tk + (int64_t)i * kTileRows), min(kTileRows, T - i * kTileRows), ss);
+  for (int i = threadIdx.x; i < nts * kTileRows; i += blockDim.x) {  // shared rows: token = row - T*k
+    const int tl = i / kTileRows, r = i % kTileRows;
+    const int n = min(kTileRows, T - tl * kTileRows);
+    tile_tok[(int64_t)(nt_total + tl) * kTileRows + r] = tl * kTileRows + (r < n ? r : 0);
+  }
   if (threadIdx.x == 0) meta[0] = nt_total + nts;
   return off;
 }
@@ -112,7 +120,8 @@ __global__ __launch_bounds__(1024) void k_scan(int64_t nb, int T, int k, int E, 
                                                const int32_t* __restrict__ slot_table, int32_t n_slots,
                                                int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
                                                int32_t* __restrict__ group_slot, int32_t* __restrict__ status,
-                                               int32_t* __restrict__ meta, int4* __restrict__ tiles) {
+                                               int32_t* __restrict__ meta, int4* __restrict__ tiles,
+                                               int32_t* __restrict__ tile_tok, int32_t* __restrict__ tile_base) {
   __shared__ int lds[17];
   const int e = threadIdx.x;
   int count = 0;
@@ -123,7 +132,23 @@ __global__ __launch_bounds__(1024) void k_scan(int64_t nb, int T, int k, int E, 
       count += c;
     }
   }
-  scan_and_tiles(count, T, k, E, layer, slot_table, n_slots, offsets, group_slot, status, meta, tiles, lds);
+  scan_and_tiles(count, T, k, E, layer, slot_table, n_slots, offsets, group_slot, status, meta, tiles, tile_tok,
+                 tile_base, lds);
+}
+
+// Token of routed row p (flat index f) into its tile's row table; the first
+// row of a tile also fills the padding rows of a partial tile.
+// tile_base and offsets may be LDS or global copies.
+__device__ inline void note_tile_row(int32_t* __restrict__ tile_tok, const int32_t* tile_base,
+                                     const int32_t* offsets, int e, int p, int f, int k, int count) {
+  const int rel = p - offsets[e];
+  const int tl = tile_base[e] + rel / kTileRows, r = rel % kTileRows;
+  const int t = f / k;
+  tile_tok[(int64_t)tl * kTileRows + r] = t;
+  if (r == 0) {
+    const int n = min(kTileRows, count - rel);
+    for (int rr = n; rr < kTileRows; rr++) tile_tok[(int64_t)tl * kTileRows + rr] = t;
+  }
 }
 
 // Whole grouping in one 1024-thread block for F = T*k <= kSmallF entries: the
@@ -136,8 +161,12 @@ __global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict_
                                                       int32_t n_slots, int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
                                                       int32_t* __restrict__ group_slot, int32_t* __restrict__ status,
-                                                      int32_t* __restrict__ meta, int4* __restrict__ tiles) {
+                                                      int32_t* __restrict__ meta, int4* __restrict__ tiles,
+                                                      int32_t* __restrict__ tile_tok,
+                                                      int32_t* __restrict__ tile_base) {
   __shared__ int32_t hist[1024];
+  __shared__ int32_t cntl[1024];
+  __shared__ int32_t tbl[1024];
   __shared__ int32_t sid[kSmallF];
   __shared__ int lds[17];
   const int tid = threadIdx.x;
@@ -155,9 +184,14 @@ __global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict_
   if (e_mine >= 0) atomicAdd(&hist[e_mine], 1);
   __syncthreads();
   const int count = tid < E ? hist[tid] : 0;
+  if (tid < E) cntl[tid] = count;
+  int tb = 0;
   const int off = scan_and_tiles(count, T, k, E, layer, slot_table, n_slots, offsets, group_slot, status, meta, tiles,
-                                 lds);
-  if (tid < E) hist[tid] = off;  // hist now holds each expert's first row
+                                 tile_tok, tile_base, lds, &tb);
+  if (tid < E) {
+    hist[tid] = off;  // hist now holds each expert's first row
+    tbl[tid] = tb;
+  }
   __syncthreads();
   if (tid < F) {
     if (e_mine < 0) {
@@ -168,13 +202,16 @@ __global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict_
       const int p = hist[e_mine] + rank;
       perm[p] = tid;
       inv_perm[tid] = p;
+      note_tile_row(tile_tok, tbl, hist, e_mine, p, tid, k, cntl[e_mine]);
     }
   }
 }
 
-__global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ ids, int64_t F, int E,
+__global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ ids, int64_t F, int E, int k,
                                                 const int32_t* __restrict__ cnt, const int32_t* __restrict__ offsets,
-                                                int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+                                                int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+                                                int32_t* __restrict__ tile_tok,
+                                                const int32_t* __restrict__ tile_base) {
   __shared__ int32_t run[1024];
   const int lane = threadIdx.x;
   for (int e = lane; e < E; e += 64) run[e] = offsets[e] + cnt[(int64_t)blockIdx.x * E + e];
@@ -196,6 +233,7 @@ __global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ ids,
         const int p = base + __popcll(mask & lt);
         perm[p] = (int32_t)f;
         inv_perm[f] = p;
+        note_tile_row(tile_tok, tile_base, offsets, e, p, (int)f, k, offsets[e + 1] - offsets[e]);
       }
       if (lane == leader) run[le] = base + __popcll(mask);
       todo &= ~mask;
@@ -214,15 +252,18 @@ hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, co
   int32_t* cnt = reinterpret_cast<int32_t*>(base + wl.off_cnt);
   int32_t* meta = reinterpret_cast<int32_t*>(base + wl.off_meta);
   int4* tiles = reinterpret_cast<int4*>(base + wl.off_tiles);
+  int32_t* tile_tok = reinterpret_cast<int32_t*>(base + wl.off_tile_tok);
+  int32_t* tile_base = reinterpret_cast<int32_t*>(base + wl.off_tile_base);
   if (F <= kSmallF) {
     hipLaunchKernelGGL(k_group_small, dim3(1), dim3(1024), 0, s, ids, (int)F, d.T, d.k, d.E, layer, slot_table,
-                       n_slots, offsets, perm, inv_perm, group_slot, dev_status, meta, tiles);
+                       n_slots, offsets, perm, inv_perm, group_slot, dev_status, meta, tiles, tile_tok, tile_base);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_count, dim3((unsigned)wl.nb), dim3(256), 0, s, ids, F, d.E, cnt, dev_status);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, wl.nb, d.T, d.k, d.E, layer, slot_table, n_slots, cnt,
-                     offsets, group_slot, dev_status, meta, tiles);
-  hipLaunchKernelGGL(k_scatter, dim3((unsigned)wl.nb), dim3(64), 0, s, ids, F, d.E, cnt, offsets, perm, inv_perm);
+                     offsets, group_slot, dev_status, meta, tiles, tile_tok, tile_base);
+  hipLaunchKernelGGL(k_scatter, dim3((unsigned)wl.nb), dim3(64), 0, s, ids, F, d.E, d.k, cnt, offsets, perm, inv_perm,
+                     tile_tok, tile_base);
   return hipGetLastError();
 }
 

@@ -16,13 +16,15 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kTileRows = 16;
 
 // ---- workspace layout (shared by moe_group and moe_expert_ffn) --------------
-// cnt    int32 [nb][E]   per-256-row-block expert counts, then block prefixes
-// meta   int32 [64]      meta[0] = number of FFN tiles
-// tiles  int4  [max_tiles] {group, first row p0, rows n (<= 16), slot}
+// cnt       int32 [nb][E]       per-256-row-block expert counts, then block prefixes
+// meta      int32 [64]          meta[0] = number of FFN tiles
+// tiles     int4  [max_tiles]   {group, first row p0, rows n (<= 16), slot}
+// tile_tok  int32 [max_tiles][16] token of each tile row (rows >= n repeat row 0)
+// tile_base int32 [E]           first tile of each routed group
 struct WsLayout {
   int64_t nb;         // blocks of 256 flat (token, slot) entries
   int64_t max_tiles;  // upper bound on FFN tiles
-  uint64_t off_cnt, off_meta, off_tiles, total;
+  uint64_t off_cnt, off_meta, off_tiles, off_tile_tok, off_tile_base, total;
 };
 
 inline uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
@@ -36,7 +38,9 @@ inline WsLayout ws_layout(const moe_dims& d) {
   w.off_cnt = 0;
   w.off_meta = align256((uint64_t)w.nb * d.E * 4);
   w.off_tiles = w.off_meta + 256;
-  w.total = align256(w.off_tiles + (uint64_t)w.max_tiles * 16);
+  w.off_tile_tok = align256(w.off_tiles + (uint64_t)w.max_tiles * 16);
+  w.off_tile_base = align256(w.off_tile_tok + (uint64_t)w.max_tiles * 64);
+  w.total = align256(w.off_tile_base + (uint64_t)d.E * 4);
   return w;
 }
 
@@ -109,6 +113,8 @@ hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, co
                         int32_t* dev_status, void* ws, hipStream_t s);
 hipError_t launch_ffn(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm,
                       uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws, hipStream_t s);
+hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm,
+                          uint16_t* h, uint16_t* y_rows, void* ws, int n_cu, hipStream_t s);
 hipError_t launch_combine(const moe_dims& d, const uint16_t* y_rows, const int32_t* inv_perm, const float* w,
                           const float* sigma, uint16_t* y, hipStream_t s);
 
