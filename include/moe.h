@@ -36,7 +36,9 @@
  *     pointers must be 16-byte aligned (MOE_ERR_ALIGN otherwise).
  *   - Thread safety: re-entrant; a ring is driven from one host thread.
  *
- * Shapes: 1 <= T, 1 <= k <= E <= 1024, H % 32 == 0, I % 32 == 0, 32 <= H, I <= 16384.
+ * Shapes: 1 <= T <= 2^20, 1 <= k <= E <= 1024, H % 32 == 0, I % 32 == 0,
+ * 32 <= H, I <= 16384, T * H * 2 < 2^31 (x addressable with 32-bit byte
+ * offsets) and T * (k + 1) < 2^30.
  * The shared expert has the same intermediate size I as a routed expert.
  */
 #ifndef MOE_H_

@@ -48,6 +48,8 @@ int check_dims(const moe_dims* d) {
   if (d->k < 1 || d->k > d->E) return fail(MOE_ERR_SHAPE, "k = %d: must be in [1, E = %d]", d->k, d->E);
   if (d->L < 1) return fail(MOE_ERR_SHAPE, "L = %d: must be >= 1", d->L);
   if ((int64_t)d->T * (d->k + 1) > INT32_MAX / 2) return fail(MOE_ERR_SHAPE, "T * (k + 1) too large");
+  if ((int64_t)d->T * d->H * 2 > INT32_MAX) return fail(MOE_ERR_SHAPE, "T * H * 2 = %lld bytes of x: must be < 2^31",
+                                                       (long long)d->T * d->H * 2);
   return MOE_OK;
 }
 

@@ -10,32 +10,42 @@
 #include "moe_common.hpp"
 
 namespace moe {
+#ifdef MOE_STAGE_TIMING
+STAGE_TIMES_DEFINE(moe_debug_stage_times_combine)
+#endif
 namespace {
 
-// grid (T, ceil(H / 2048)); 256 threads x 8 consecutive columns.
+// grid (T, ceil(H / 2048)); 256 threads x 8 consecutive columns.  Two dependent
+// rounds of loads: the slot indices, weights, sigma and the shared row first,
+// then every routed row of the token at once (kCombineSlots per pass).
+constexpr int kCombineSlots = 16;
+
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ yr, const int32_t* __restrict__ inv,
                                                  const float* __restrict__ w, const float* __restrict__ sigma,
                                                  int T, int H, int k, uint16_t* __restrict__ y) {
+  STAGE_STAMP(2, 0);
   const int t = blockIdx.x;
   const int col = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (col >= H) return;
+  const float st = sigma[t];
+  const uint4 vs = *reinterpret_cast<const uint4*>(yr + ((int64_t)T * k + t) * H + col);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  // batches of 8 slots: indices and weights, then the rows, then the math in slot order
-  for (int j0 = 0; j0 < k; j0 += 8) {
-    int p[8];
-    float wj[8];
-    uint4 v[8];
+  for (int j0 = 0; j0 < k; j0 += kCombineSlots) {
+    int p[kCombineSlots];
+    float wj[kCombineSlots];
 #pragma unroll
-    for (int u = 0; u < 8; u++) {
-      p[u] = (j0 + u < k) ? inv[(int64_t)t * k + j0 + u] : -1;
-      wj[u] = (j0 + u < k) ? w[(int64_t)t * k + j0 + u] : 0.0f;
+    for (int u = 0; u < kCombineSlots; u++) {
+      const int j = min(j0 + u, k - 1);
+      p[u] = inv[(int64_t)t * k + j];
+      wj[u] = (j0 + u < k) ? w[(int64_t)t * k + j] : 0.0f;
     }
+    uint4 v[kCombineSlots];
 #pragma unroll
-    for (int u = 0; u < 8; u++)
-      v[u] = (p[u] >= 0) ? *reinterpret_cast<const uint4*>(yr + (int64_t)p[u] * H + col) : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < kCombineSlots; u++)
+      v[u] = *reinterpret_cast<const uint4*>(yr + (int64_t)max(p[u], 0) * H + col);
 #pragma unroll
-    for (int u = 0; u < 8; u++) {
-      if (p[u] < 0) continue;
+    for (int u = 0; u < kCombineSlots; u++) {
+      if (j0 + u >= k || p[u] < 0) continue;
       const uint32_t uu[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
       for (int i = 0; i < 4; i++) {
@@ -44,9 +54,8 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ yr
       }
     }
   }
-  const float st = sigma[t];
-  const uint4 v = *reinterpret_cast<const uint4*>(yr + ((int64_t)T * k + t) * H + col);
-  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  STAGE_STAMP(2, 1);
+  const uint32_t u[4] = {vs.x, vs.y, vs.z, vs.w};
   uint32_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -55,6 +64,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ yr
     o[i] = (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
   }
   *reinterpret_cast<uint4*>(y + (int64_t)t * H + col) = make_uint4(o[0], o[1], o[2], o[3]);
+  STAGE_STAMP(2, 2);
 }
 
 }  // namespace

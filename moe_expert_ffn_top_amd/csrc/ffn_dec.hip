@@ -38,6 +38,30 @@ __device__ inline cptr<T> as_const(const T* p) {
   return (cptr<T>)p;
 }
 
+#ifdef MOE_DEC_TIMING
+// Tuning builds only: per-wavefront wall-clock stamps (start, first item's
+// descriptor ready, first weights arrived, end of items 1..4, end).
+__device__ unsigned long long g_dec_times[1 << 17][8];
+#define DEC_STAMP(i)                                                                              \
+  do {                                                                                            \
+    if ((threadIdx.x & 63) == 0) {                                                                \
+      const unsigned w = (((blockIdx.x * 4u + (threadIdx.x >> 6)) & ((1u << 16) - 1)) | (GATEUP ? 0u : (1u << 16))); \
+      g_dec_times[w][i] = wall_clock64();                                                         \
+    }                                                                                             \
+  } while (0)
+#else
+#define DEC_STAMP(i) \
+  do {               \
+  } while (0)
+#endif
+
+#ifndef MOE_DEC_CONTIG
+#define MOE_DEC_CONTIG 0
+#endif
+#ifndef MOE_DEC_ABUF
+#define MOE_DEC_ABUF 1
+#endif
+
 struct DecArgs {
   uint64_t slot_stride;
   int64_t n_slots;
@@ -45,7 +69,8 @@ struct DecArgs {
   uint64_t off_scales[3];
   uint64_t off_globals;
   int32_t H, I;
-  int32_t n_ug;  // unit-block groups (workgroup items) per tile
+  int32_t n_ug;     // unit-block groups (workgroup items) per tile
+  int32_t a_bytes;  // bytes of x (T * H * 2), the gate/up A buffer
 };
 
 // One lane's loads for one 128-value K step.
@@ -62,6 +87,8 @@ struct Item {
   const uint8_t* scales[NMAT];
   int sodd[NMAT];
   const uint16_t* arow;  // this lane's input row (padding rows repeat row 0)
+  __amdgpu_buffer_rsrc_t arsrc;  // A rows as a buffer: padding lanes read out of range (zeros, no traffic)
+  uint32_t aoff;                 // this lane's row start in arsrc (bytes)
   float g0, g1;          // fp32 global scales (gate, up) or (down, -)
   int p0, n, unit;
   bool live;      // an item exists
@@ -84,6 +111,8 @@ __device__ inline Item<GATEUP ? 2 : 1> make_item(const DecArgs& a, int item, int
   it.live = false;
   it.resident = false;
   it.arow = ain;
+  it.arsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(ain), (short)0, 0, 0x00020000);
+  it.aoff = 0x80000000u;
   it.g0 = it.g1 = 0.f;
   it.p0 = it.n = it.unit = 0;
 #pragma unroll
@@ -113,8 +142,14 @@ __device__ inline Item<GATEUP ? 2 : 1> make_item(const DecArgs& a, int item, int
 #pragma unroll
     for (int j = 0; j < 16; j++) t = (c == j) ? tok[j] : t;
     it.arow = ain + (int64_t)t * a.H;
+    it.arsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(ain), (short)0, a.a_bytes, 0x00020000);
+    it.aoff = c < it.n ? (uint32_t)t * (uint32_t)a.H * 2u : 0x80000000u;
   } else {
     it.arow = ain + (int64_t)(it.p0 + min(c, it.n - 1)) * a.I;
+    // the buffer holds exactly the tile's rows, so lanes c >= n fall outside it
+    it.arsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(ain + (int64_t)it.p0 * a.I), (short)0,
+                                                 it.n * a.I * 2, 0x00020000);
+    it.aoff = (uint32_t)c * (uint32_t)a.I * 2u;
   }
   it.resident = td.w >= 0 && td.w < a.n_slots;
   if (!it.resident) return it;
@@ -145,10 +180,20 @@ __device__ inline void load_step(Step<NMAT>& s, const Item<NMAT>& it, int ch) {
   }
 }
 
-__device__ inline void load_a(uint4* xa, const uint16_t* arow, int ch) {
-  const uint4* p = reinterpret_cast<const uint4*>(arow + (int64_t)ch * 32);
+template <int NMAT>
+__device__ inline void load_a(uint4* xa, const Item<NMAT>& it, int ch) {
+#if MOE_DEC_ABUF
+  using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(it.arsrc, it.aoff + (uint32_t)ch * 64u + 16u * i, 0, 0);
+    xa[i] = uint4{v.x, v.y, v.z, v.w};
+  }
+#else
+  const uint4* p = reinterpret_cast<const uint4*>(it.arow + (int64_t)ch * 32);
 #pragma unroll
   for (int i = 0; i < 4; i++) xa[i] = p[i];
+#endif
 }
 
 template <int NMAT>
@@ -186,15 +231,31 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
   const bool kempty = kpart * wc >= nc;
 
   __shared__ f32x4 red[4][NMAT][64];
+  // chunk of step s for this lane
+#if MOE_DEC_CONTIG
+#define DEC_CH(s) (c0 + q * S + (s))
+#else
+#define DEC_CH(s) (c0 + 4 * (s) + q)
+#endif
 
+  DEC_STAMP(0);
   int item = blockIdx.x;
   Item<NMAT> cur = make_item<GATEUP>(a, item, n_items, ub, c, tiles, tile_tok, pool, ain);
   if (!cur.live) return;
+  DEC_STAMP(1);
+#ifdef MOE_DEC_TIMING
+  int n_done = 0;
+#endif
+  // A fragments of every step of the current item stay in registers.  Once
+  // step s is computed, its registers (weights and A) are refilled with the
+  // next item's step s, so both stream one item ahead and every wait is on
+  // loads issued a whole item earlier.
+  uint4 xa[S][4];
+#pragma unroll
+  for (int s = 0; s < S; s++) load_a(xa[s], cur, min(DEC_CH(s), c1 - 1));
   Step<NMAT> fb[S];
 #pragma unroll
-  for (int s = 0; s < S; s++) load_step<NMAT>(fb[s], cur, min(c0 + 4 * s + q, c1 - 1));
-  uint4 xa[4];
-  load_a(xa, cur.arow, min(c0 + q, c1 - 1));
+  for (int s = 0; s < S; s++) load_step<NMAT>(fb[s], cur, min(DEC_CH(s), c1 - 1));
 
   while (cur.live) {
     const int nitem = item + gridDim.x;
@@ -204,17 +265,18 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
     for (int m = 0; m < NMAT; m++) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < S; s++) {
-      const int chr = c0 + 4 * s + q;
+      const int chr = DEC_CH(s);
       const int chc = min(chr, c1 - 1);
-      uint4 xn[4];
-      // next A fragment: this item's next step, or the next item's first step
-      if (s + 1 < S) load_a(xn, cur.arow, min(c0 + 4 * (s + 1) + q, c1 - 1));
-      else load_a(xn, nxt.arow, min(c0 + q, c1 - 1));
-      mma_step<NMAT>(fb[s], xa, cur, chc, !kempty && chr < c1 && cur.resident, acc);
+      mma_step<NMAT>(fb[s], xa[s], cur, chc, !kempty && chr < c1 && cur.resident, acc);
+#ifdef MOE_DEC_TIMING
+      if (s == 0 && n_done == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        DEC_STAMP(2);
+      }
+#endif
       // this step's registers now carry the next item's step s
-      load_step<NMAT>(fb[s], nxt, min(c0 + 4 * s + q, c1 - 1));
-#pragma unroll
-      for (int i = 0; i < 4; i++) xa[i] = xn[i];
+      load_step<NMAT>(fb[s], nxt, min(DEC_CH(s), c1 - 1));
+      load_a(xa[s], nxt, min(DEC_CH(s), c1 - 1));
       __builtin_amdgcn_sched_barrier(0);
     }
     // split-K partials meet in LDS; kpart 0 finishes the unit block
@@ -254,7 +316,12 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
     }
     item = nitem;
     cur = nxt;
+#ifdef MOE_DEC_TIMING
+    n_done++;
+    if (n_done <= 4) DEC_STAMP(2 + n_done);
+#endif
   }
+  DEC_STAMP(7);
 }
 
 // steps per wave = ceil(K / 128 / SPLITK) <= 4 for K <= 2048 with SPLITK 4;
@@ -306,6 +373,7 @@ hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g
   a.off_globals = g.off_globals;
   a.H = d.H;
   a.I = d.I;
+  a.a_bytes = (int32_t)((int64_t)d.T * d.H * 2);
   DecPtrs ptrs;
   ptrs.tiles = reinterpret_cast<const int4*>(base + wl.off_tiles);
   ptrs.tile_tok = reinterpret_cast<const int32_t*>(base + wl.off_tile_tok);
@@ -337,5 +405,13 @@ hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g
   }
   return hipSuccess;
 }
+
+#ifdef MOE_DEC_TIMING
+extern "C" void* moe_debug_dec_times(void) {
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_dec_times)) != hipSuccess) return nullptr;
+  return p;
+}
+#endif
 
 }  // namespace moe

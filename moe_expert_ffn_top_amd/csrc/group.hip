@@ -19,6 +19,9 @@
 #include "moe_common.hpp"
 
 namespace moe {
+#ifdef MOE_STAGE_TIMING
+STAGE_TIMES_DEFINE(moe_debug_stage_times_group)
+#endif
 namespace {
 
 constexpr int kBlk = 256;
@@ -69,8 +72,10 @@ __device__ int block_exclusive_scan(int v, int* lds16, int* total) {
 
 // Thread e (< E) holds count = rows of expert e.  Writes offsets, group_slot,
 // residency status and the FFN tile list; returns this expert's first row.
-__device__ int scan_and_tiles(int count, int T, int k, int E, int layer, const int32_t* __restrict__ slot_table,
-                              int32_t n_slots, int32_t* __restrict__ offsets, int32_t* __restrict__ group_slot,
+// `slot` is slot_table[layer][e] for thread e < E and `ss` the shared expert's
+// slot; the caller loads both at its start, so their latency overlaps its own.
+__device__ int scan_and_tiles(int count, int T, int k, int E, int slot, int ss, int32_t n_slots,
+                              int32_t* __restrict__ offsets, int32_t* __restrict__ group_slot,
                               int32_t* __restrict__ status, int32_t* __restrict__ meta, int4* __restrict__ tiles,
                               int32_t* __restrict__ tile_tok, int32_t* __restrict__ tile_base, int* lds17,
                               int* tbase_out = nullptr) {
@@ -78,15 +83,12 @@ __device__ int scan_and_tiles(int count, int T, int k, int E, int layer, const i
   int total = 0;
   const int off = block_exclusive_scan(count, lds17, &total);
   const int64_t Tk = (int64_t)T * k;
-  int slot = -1;
   if (e < E) {
     offsets[e] = off;
-    slot = slot_table[(int64_t)layer * (E + 1) + e];
     group_slot[e] = slot;
     if (count > 0 && slot < 0) atomicOr(status, MOE_DEV_NOT_RESIDENT);
     if (count > 0 && slot >= n_slots) atomicOr(status, MOE_DEV_BAD_SLOT);
   }
-  const int ss = slot_table[(int64_t)layer * (E + 1) + E];
   if (e == 0) {
     offsets[E] = total;
     offsets[E + 1] = (int32_t)(Tk + T);
@@ -124,6 +126,8 @@ __global__ __launch_bounds__(1024) void k_scan(int64_t nb, int T, int k, int E, 
                                                int32_t* __restrict__ tile_tok, int32_t* __restrict__ tile_base) {
   __shared__ int lds[17];
   const int e = threadIdx.x;
+  const int slot = e < E ? slot_table[(int64_t)layer * (E + 1) + e] : -1;
+  const int ss = slot_table[(int64_t)layer * (E + 1) + E];
   int count = 0;
   if (e < E) {
     for (int64_t b = 0; b < nb; b++) {
@@ -132,8 +136,8 @@ __global__ __launch_bounds__(1024) void k_scan(int64_t nb, int T, int k, int E, 
       count += c;
     }
   }
-  scan_and_tiles(count, T, k, E, layer, slot_table, n_slots, offsets, group_slot, status, meta, tiles, tile_tok,
-                 tile_base, lds);
+  scan_and_tiles(count, T, k, E, slot, ss, n_slots, offsets, group_slot, status, meta, tiles, tile_tok, tile_base,
+                 lds);
 }
 
 // Token of routed row p (flat index f) into its tile's row table; the first
@@ -167,9 +171,12 @@ __global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict_
   __shared__ int32_t hist[1024];
   __shared__ int32_t cntl[1024];
   __shared__ int32_t tbl[1024];
-  __shared__ int32_t sid[kSmallF];
+  __shared__ __align__(16) int32_t sid[kSmallF];
   __shared__ int lds[17];
   const int tid = threadIdx.x;
+  STAGE_STAMP(1, 0);
+  const int slot = tid < E ? slot_table[(int64_t)layer * (E + 1) + tid] : -1;
+  const int ss = slot_table[(int64_t)layer * (E + 1) + E];
   if (tid < E) hist[tid] = 0;
   int e_mine = -1;
   if (tid < F) {
@@ -178,33 +185,47 @@ __global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict_
       atomicOr(status, MOE_DEV_BAD_EXPERT_ID);
       e_mine = -1;
     }
-    sid[tid] = e_mine;
   }
+  if (tid < kSmallF) sid[tid] = e_mine;  // -1 beyond F and for bad ids
   __syncthreads();
+  STAGE_STAMP(1, 1);
   if (e_mine >= 0) atomicAdd(&hist[e_mine], 1);
   __syncthreads();
   const int count = tid < E ? hist[tid] : 0;
   if (tid < E) cntl[tid] = count;
   int tb = 0;
-  const int off = scan_and_tiles(count, T, k, E, layer, slot_table, n_slots, offsets, group_slot, status, meta, tiles,
+  STAGE_STAMP(1, 2);
+  const int off = scan_and_tiles(count, T, k, E, slot, ss, n_slots, offsets, group_slot, status, meta, tiles,
                                  tile_tok, tile_base, lds, &tb);
+  STAGE_STAMP(1, 3);
   if (tid < E) {
     hist[tid] = off;  // hist now holds each expert's first row
     tbl[tid] = tb;
   }
   __syncthreads();
+  STAGE_STAMP(1, 4);
   if (tid < F) {
     if (e_mine < 0) {
       inv_perm[tid] = -1;
     } else {
+      // rank = earlier entries with the same expert; 4 staged ids per LDS read,
+      // over the wavefront's uniform range of earlier entries
+      const int fend = min(F, (tid | 63) + 1);
       int rank = 0;
-      for (int f = 0; f < F; f++) rank += (f < tid && sid[f] == e_mine) ? 1 : 0;
+      const int4* sid4 = reinterpret_cast<const int4*>(sid);
+#pragma unroll 4
+      for (int f0 = 0; f0 < fend; f0 += 4) {
+        const int4 q = sid4[f0 >> 2];
+        rank += (f0 + 0 < tid && q.x == e_mine) + (f0 + 1 < tid && q.y == e_mine) +
+                (f0 + 2 < tid && q.z == e_mine) + (f0 + 3 < tid && q.w == e_mine);
+      }
       const int p = hist[e_mine] + rank;
       perm[p] = tid;
       inv_perm[tid] = p;
       note_tile_row(tile_tok, tbl, hist, e_mine, p, tid, k, cntl[e_mine]);
     }
   }
+  STAGE_STAMP(1, 5);
 }
 
 __global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ ids, int64_t F, int E, int k,

@@ -44,6 +44,28 @@ inline WsLayout ws_layout(const moe_dims& d) {
   return w;
 }
 
+// ---- tuning builds only: wall-clock stamps of the small kernels' phases ----
+#ifdef MOE_STAGE_TIMING
+// [kernel][phase], written by thread 0 of block 0 (100 MHz wall clock); each
+// source file that stamps defines its own g_stage_times and getter
+#define STAGE_TIMES_DEFINE(getter)                                                   \
+  __device__ unsigned long long g_stage_times[8][8];                                 \
+  extern "C" void* getter(void) {                                                    \
+    void* p = nullptr;                                                               \
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_stage_times)) != hipSuccess) return nullptr; \
+    return p;                                                                        \
+  }
+#define STAGE_STAMP(kern, i)                                                         \
+  do {                                                                               \
+    if (threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0)                      \
+      g_stage_times[kern][i] = wall_clock64();                                       \
+  } while (0)
+#else
+#define STAGE_STAMP(kern, i) \
+  do {                       \
+  } while (0)
+#endif
+
 // ---- small device helpers --------------------------------------------------
 __device__ inline float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
