@@ -4,43 +4,53 @@
 // group has few rows and the expert's weight bytes dominate; the time goes
 // into reading them ([FreeToken] 2.2: decode is a stream of small, latency-
 // sensitive expert reads).  This kernel is built for that regime:
-//  - A persistent grid (sized to stay resident) walks a list of work items
-//    (tile of <= 16 rows, block of output units); each workgroup requests the
-//    weights of its next item before it computes the current one, so the
-//    dependent-load chains of an item (tile descriptor -> slot -> weights)
-//    overlap the previous item's math.
-//  - A operand: bf16 rows read straight from x (through perm) or h, exact.
-//  - B operand: lane (c = lane % 16, q = lane / 16) owns output unit c and per
-//    128-value K step loads 16 code bytes (32 E2M1 values, chunk q) and their
-//    two E4M3 scales; codes are decoded with v_cvt_scalef32_pk_f32_fp4 and
-//    multiplied by the scale in fp32 (exact: <= 6 significant bits), then
-//    packed to bf16 (exact).  v_mfma_f32_16x16x32_bf16 sums exact products in
-//    fp32.
-//  - SPLITK wavefronts of a unit block split K; partials meet in LDS.
-// MFMA rows beyond a tile's n read a real row and their outputs are discarded.
+//  - A persistent grid (sized to stay resident) walks a list of work units
+//    (tile of <= 16 rows, block of output units, K round); each workgroup
+//    requests the weights of its next unit before it computes the current one,
+//    so the dependent-load chains of a unit (tile descriptor -> slot ->
+//    weights) overlap the previous unit's math.
+//  - A operand: bf16 rows of x (gathered through the tile's token table) or of
+//    h, read exactly, through buffer loads: lanes of the MFMA rows beyond the
+//    tile's n rows address past the end of the buffer and get zeros without
+//    any memory traffic.
+//  - B operand: lane (c = lane % 16, q = lane / 16) owns output unit c of each
+//    of its unit blocks and per 128-value K step loads 16 code bytes (32 E2M1
+//    values) and their two E4M3 scales; codes are decoded with
+//    v_cvt_scalef32_pk_f32_fp4 and multiplied by the scale in fp32 (exact:
+//    <= 6 significant bits), then packed to bf16 (exact).
+//    v_mfma_f32_16x16x32_bf16 sums exact products in fp32.
+//  - A wavefront runs U unit blocks (and, for gate/up, both matrices) against
+//    the same A registers, so one unit carries U times the weight bytes for
+//    the registers of one A fragment.
+//  - SPLITK wavefronts of a unit block split K; partials meet in LDS.  A
+//    wavefront's share of K is covered in K rounds of S steps.
 #include <math.h>
 
 #include "moe_common.hpp"
 
+#ifndef MOE_DEC_WGS_PER_CU
+#define MOE_DEC_WGS_PER_CU 2
+#endif
+// unit blocks per wavefront and steps per K round, per stage
+#ifndef MOE_DEC_U_GU
+#define MOE_DEC_U_GU 1
+#endif
+#ifndef MOE_DEC_MAXS_GU
+#define MOE_DEC_MAXS_GU 4
+#endif
+#ifndef MOE_DEC_U_DN
+#define MOE_DEC_U_DN 2
+#endif
+#ifndef MOE_DEC_MAXS_DN
+#define MOE_DEC_MAXS_DN 4
+#endif
+
 namespace moe {
 namespace {
 
-// Data that no kernel of this launch writes (tile descriptors, token tables,
-// the weight pool) is read through the constant address space: a load from it
-// at a wavefront-uniform address always becomes a scalar load, which is counted
-// apart from the vector loads in flight.
-template <typename T>
-using cptr = const __attribute__((address_space(4))) T*;
-using i32x4 = int __attribute__((ext_vector_type(4)));
-
-template <typename T>
-__device__ inline cptr<T> as_const(const T* p) {
-  return (cptr<T>)p;
-}
-
 #ifdef MOE_DEC_TIMING
-// Tuning builds only: per-wavefront wall-clock stamps (start, first item's
-// descriptor ready, first weights arrived, end of items 1..4, end).
+// Tuning builds only: per-wavefront wall-clock stamps (start, first unit's
+// descriptor ready, first weights arrived, end of units 1..4, end).
 __device__ unsigned long long g_dec_times[1 << 17][8];
 #define DEC_STAMP(i)                                                                              \
   do {                                                                                            \
@@ -55,152 +65,150 @@ __device__ unsigned long long g_dec_times[1 << 17][8];
   } while (0)
 #endif
 
-#ifndef MOE_DEC_CONTIG
-#define MOE_DEC_CONTIG 0
-#endif
-#ifndef MOE_DEC_ABUF
-#define MOE_DEC_ABUF 1
-#endif
+// Data that no kernel of this launch writes (tile descriptors, token tables,
+// the weight pool) is read through the constant address space: a load from it
+// at a wavefront-uniform address always becomes a scalar load, which is counted
+// apart from the vector loads in flight.
+template <typename T>
+using cptr = const __attribute__((address_space(4))) T*;
+using i32x4 = int __attribute__((ext_vector_type(4)));
 
+template <typename T>
+__device__ inline cptr<T> as_const(const T* p) {
+  return (cptr<T>)p;
+}
+
+// Blob offsets and the slot stride fit 32 bits (a blob is at most 27 * 16384^2
+// / 16 bytes); narrow fields keep the kernel's scalar registers free.
 struct DecArgs {
-  uint64_t slot_stride;
-  int64_t n_slots;
-  uint64_t off_codes[3];
-  uint64_t off_scales[3];
-  uint64_t off_globals;
+  uint32_t slot_stride;
+  int32_t n_slots;
+  uint32_t off_codes[3];
+  uint32_t off_scales[3];
+  uint32_t off_globals;
   int32_t H, I;
-  int32_t n_ug;     // unit-block groups (workgroup items) per tile
-  int32_t a_bytes;  // bytes of x (T * H * 2), the gate/up A buffer
+  int32_t n_ug;       // items (unit-block groups) per tile
+  int32_t n_kr;       // K rounds per item
+  int32_t max_tiles;  // entries of the tile list
+  int32_t a_bytes;    // bytes of x (T * H * 2), the gate/up A buffer
 };
 
-// One lane's loads for one 128-value K step.
-template <int NMAT>
+// One lane's loads for one 128-value K step of NS weight streams.
+template <int NS>
 struct Step {
-  uint4 w[NMAT];
-  uint32_t sc[NMAT];
+  uint4 w[NS];
+  uint32_t sc[NS];
 };
 
-// Per-wavefront view of one work item.
-template <int NMAT>
+// Per-wavefront view of one item.  Stream m is matrix m % NMAT of unit block
+// m / NMAT.
+template <int NS>
 struct Item {
-  const uint8_t* codes[NMAT];
-  const uint8_t* scales[NMAT];
-  int sodd[NMAT];
-  const uint16_t* arow;  // this lane's input row (padding rows repeat row 0)
-  __amdgpu_buffer_rsrc_t arsrc;  // A rows as a buffer: padding lanes read out of range (zeros, no traffic)
-  uint32_t aoff;                 // this lane's row start in arsrc (bytes)
-  float g0, g1;          // fp32 global scales (gate, up) or (down, -)
-  int p0, n, unit;
-  bool live;      // an item exists
-  bool resident;  // its slot is inside the pool
+  const uint8_t* codes[NS];
+  const uint8_t* scales[NS];
+  int sodd[NS];
+  __amdgpu_buffer_rsrc_t arsrc;  // A rows as a buffer
+  uint32_t aoff;                 // this lane's row start in arsrc (bytes; past the end for padding rows)
+  float g0, g1;                  // fp32 global scales (gate, up) or (down, -)
+  int p0, n, unit;               // first row, rows, this lane's unit in its first unit block
+  bool live;                     // the item exists
+  bool resident;                 // it exists and its slot is inside the pool
 };
 
-// Everything here is read-only for the kernel and reached through restrict
-// pointers at uniform addresses, so the compiler uses scalar loads: they are
-// counted apart from the vector loads of the weights in flight, and waiting on
-// them never drains the weight pipeline.
+// The raw descriptor of an item: its tile entry (the same 16 bytes in every
+// lane) and, for gate/up, this lane's token from the tile's token table.  Both
+// are vector loads issued two work units ahead of their use: the in-order wait
+// for them then only covers loads that are a whole unit old.  The tile index
+// is clamped, so the load does not wait for the item count; the item is masked
+// when it is derived.
+struct Desc {
+  int4 td;
+  int tok;
+  int item;
+};
+
 template <bool GATEUP>
-__device__ inline Item<GATEUP ? 2 : 1> make_item(const DecArgs& a, int item, int n_items, int ub, int c,
-                                                  const int4* __restrict__ tiles,
-                                                  const int32_t* __restrict__ tile_tok,
-                                                  const uint8_t* __restrict__ pool,
-                                                  const uint16_t* __restrict__ ain) {
-  constexpr int NMAT = GATEUP ? 2 : 1;
-  Item<NMAT> it;
+__device__ inline Desc load_desc(const DecArgs& a, int item, int c, const int4* __restrict__ tiles,
+                                 const int32_t* __restrict__ tile_tok) {
+  Desc d;
+  const int tile = min(item / a.n_ug, a.max_tiles - 1);
+  d.td = tiles[tile];
+  d.tok = GATEUP ? tile_tok[(int64_t)tile * 16 + c] : 0;
+  d.item = item;
+  return d;
+}
+
+template <bool GATEUP, int U>
+__device__ inline Item<(GATEUP ? 2 : 1) * U> make_item(const DecArgs& a, const Desc& d, int n_items, int wub, int c,
+                                                        const uint8_t* __restrict__ pool,
+                                                        const uint16_t* __restrict__ ain) {
+  constexpr int NMAT = GATEUP ? 2 : 1, NS = NMAT * U;
+  Item<NS> it;
   const int K = GATEUP ? a.H : a.I;
-  it.live = false;
-  it.resident = false;
-  it.arow = ain;
-  it.arsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(ain), (short)0, 0, 0x00020000);
-  it.aoff = 0x80000000u;
-  it.g0 = it.g1 = 0.f;
-  it.p0 = it.n = it.unit = 0;
-#pragma unroll
-  for (int m = 0; m < NMAT; m++) {
-    it.codes[m] = pool;
-    it.scales[m] = pool;
-    it.sodd[m] = 0;
-  }
-  if (item >= n_items) return it;
-  const int tile = item / a.n_ug, ug = item - tile * a.n_ug;
-  const i32x4 td = as_const(reinterpret_cast<const i32x4*>(tiles))[tile];
+  const int item = d.item;
+  const int tile_u = item / a.n_ug, ug = item - tile_u * a.n_ug;
+  // the tile entry is the same in every lane
+  const int p0 = __builtin_amdgcn_readfirstlane(d.td.y);
+  const int tn = __builtin_amdgcn_readfirstlane(d.td.z);
+  const int slot = __builtin_amdgcn_readfirstlane(d.td.w);
   const int ubw = (GATEUP ? a.I : a.H) / 16 / a.n_ug;  // unit blocks per item
-  it.live = true;
-  it.p0 = td.y;
-  it.n = td.z;
-  it.unit = (ug * ubw + ub) * 16 + c;
-  // this lane's input row; MFMA rows beyond n repeat row 0 (outputs discarded)
+  it.live = item < n_items;
+  it.p0 = p0;
+  it.n = it.live ? tn : 0;
+  it.unit = (ug * ubw + wub) * 16 + c;
   if (GATEUP) {
-    // one 64-byte scalar load of the tile's 16 tokens, then a per-lane pick
-    cptr<i32x4> tt = as_const(reinterpret_cast<const i32x4*>(tile_tok + (int64_t)tile * 16));
-    const i32x4 q0 = tt[0], q1 = tt[1], q2 = tt[2], q3 = tt[3];
-    const int tok[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
-                         q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
-    // the chain starts from a constant so that no select has two loads as
-    // operands (the code generator would fold that into a per-lane load)
-    int t = 0;
-#pragma unroll
-    for (int j = 0; j < 16; j++) t = (c == j) ? tok[j] : t;
-    it.arow = ain + (int64_t)t * a.H;
     it.arsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(ain), (short)0, a.a_bytes, 0x00020000);
-    it.aoff = c < it.n ? (uint32_t)t * (uint32_t)a.H * 2u : 0x80000000u;
+    it.aoff = c < it.n ? (uint32_t)d.tok * (uint32_t)a.H * 2u : 0x80000000u;
   } else {
-    it.arow = ain + (int64_t)(it.p0 + min(c, it.n - 1)) * a.I;
     // the buffer holds exactly the tile's rows, so lanes c >= n fall outside it
-    it.arsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(ain + (int64_t)it.p0 * a.I), (short)0,
-                                                 it.n * a.I * 2, 0x00020000);
+    it.arsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(ain + (it.live ? (int64_t)p0 * a.I : 0)),
+                                                 (short)0, it.n * a.I * 2, 0x00020000);
     it.aoff = (uint32_t)c * (uint32_t)a.I * 2u;
   }
-  it.resident = td.w >= 0 && td.w < a.n_slots;
-  if (!it.resident) return it;
-  const uint8_t* blob = pool + (uint64_t)td.w * a.slot_stride;
+  it.resident = it.live && slot >= 0 && slot < a.n_slots;
+  const uint8_t* blob = pool + (it.resident ? (uint64_t)slot * (uint64_t)a.slot_stride : 0);
 #pragma unroll
-  for (int m = 0; m < NMAT; m++) {
-    const int mi = GATEUP ? m : 2;
-    it.codes[m] = blob + a.off_codes[mi] + (int64_t)it.unit * (K / 2);
-    it.scales[m] = blob + a.off_scales[mi] + (int64_t)it.unit * (K / 16);
+  for (int m = 0; m < NS; m++) {
+    const int mi = GATEUP ? (m % NMAT) : 2;
+    const int unit = it.unit + (m / NMAT) * 16;
+    it.codes[m] = it.resident ? blob + a.off_codes[mi] + (int64_t)unit * (K / 2) : pool;
+    it.scales[m] = it.resident ? blob + a.off_scales[mi] + (int64_t)unit * (K / 16) : pool;
     it.sodd[m] = (int)((reinterpret_cast<uintptr_t>(it.scales[m]) >> 1) & 1);
   }
   cptr<float> glob = as_const(reinterpret_cast<const float*>(blob + a.off_globals));
-  it.g0 = glob[GATEUP ? 0 : 2];
-  it.g1 = GATEUP ? glob[1] : 0.f;
+  it.g0 = it.resident ? glob[GATEUP ? 0 : 2] : 0.f;
+  it.g1 = (GATEUP && it.resident) ? glob[1] : 0.f;
   return it;
 }
 
-// Unconditional, address-clamped weight loads (exact wait counts): see the
-// header of ffn.hip.  The scale dword is the aligned one holding the chunk's
-// two bytes.
-template <int NMAT>
-__device__ inline void load_step(Step<NMAT>& s, const Item<NMAT>& it, int ch) {
+// Unconditional, address-clamped weight loads (exact wait counts): invalid
+// chunks are zeroed through their scale.  The scale dword is the aligned one
+// holding the chunk's two bytes.
+template <int NS>
+__device__ inline void load_step(Step<NS>& s, const Item<NS>& it, int ch) {
 #pragma unroll
-  for (int m = 0; m < NMAT; m++) {
+  for (int m = 0; m < NS; m++) {
     s.w[m] = *reinterpret_cast<const uint4*>(it.codes[m] + (int64_t)ch * 16);
     const int64_t off = (int64_t)ch * 2 - 2 * ((it.sodd[m] + ch) & 1);
     s.sc[m] = *reinterpret_cast<const uint32_t*>(it.scales[m] + off);
   }
 }
 
-template <int NMAT>
-__device__ inline void load_a(uint4* xa, const Item<NMAT>& it, int ch) {
-#if MOE_DEC_ABUF
+template <int NS>
+__device__ inline void load_a(uint4* xa, const Item<NS>& it, int ch) {
   using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(it.arsrc, it.aoff + (uint32_t)ch * 64u + 16u * i, 0, 0);
     xa[i] = uint4{v.x, v.y, v.z, v.w};
   }
-#else
-  const uint4* p = reinterpret_cast<const uint4*>(it.arow + (int64_t)ch * 32);
-#pragma unroll
-  for (int i = 0; i < 4; i++) xa[i] = p[i];
-#endif
 }
 
-template <int NMAT>
-__device__ inline void mma_step(const Step<NMAT>& s, const uint4* xa, const Item<NMAT>& it, int ch, bool valid,
+template <int NS>
+__device__ inline void mma_step(const Step<NS>& s, const uint4* xa, const Item<NS>& it, int ch, bool valid,
                                 f32x4* acc) {
 #pragma unroll
-  for (int m = 0; m < NMAT; m++) {
+  for (int m = 0; m < NS; m++) {
     const uint32_t sw = valid ? (s.sc[m] >> (16 * ((it.sodd[m] + ch) & 1))) : 0u;
     const float s0 = e4m3_to_f32<0>(sw), s1 = e4m3_to_f32<1>(sw);
     acc[m] = mfma16x16x32(as_bf16x8(xa[0]), dequant8(s.w[m].x, s0), acc[m]);
@@ -210,122 +218,140 @@ __device__ inline void mma_step(const Step<NMAT>& s, const uint4* xa, const Item
   }
 }
 
-// S: 128-value steps per wavefront and item (<= 4).  UBW unit blocks per item;
-// SPLITK * UBW == 4 wavefronts.
-template <bool GATEUP, int SPLITK, int S>
+// S: 128-value steps per wavefront and K round; U unit blocks per wavefront;
+// SPLITK wavefronts per unit block (4 / SPLITK unit-block groups per item).
+template <bool GATEUP, int SPLITK, int S, int U>
 __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restrict__ tiles,
                                                  const int32_t* __restrict__ tile_tok,
                                                  const int32_t* __restrict__ n_tiles,
                                                  const uint8_t* __restrict__ pool, const uint16_t* __restrict__ ain,
                                                  uint16_t* __restrict__ out) {
-  constexpr int NMAT = GATEUP ? 2 : 1;
+  constexpr int NMAT = GATEUP ? 2 : 1, NS = NMAT * U;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int ub = wave / SPLITK, kpart = wave % SPLITK;
+  const int wub = (wave / SPLITK) * U, kpart = wave % SPLITK;  // first unit block of this wave in the item
   const int c = lane & 15, q = lane >> 4;
   const int K = GATEUP ? a.H : a.I;
   const int units = GATEUP ? a.I : a.H;
   const int n_items = *as_const(n_tiles) * a.n_ug;
+  const int nkr = a.n_kr;
   const int nc = K / 32;
   const int wc = (nc + SPLITK - 1) / SPLITK;
   const int c0 = min(kpart * wc, nc - 1), c1 = min(nc, kpart * wc + wc);  // this wave's chunks [c0, c1)
   const bool kempty = kpart * wc >= nc;
 
-  __shared__ f32x4 red[4][NMAT][64];
-  // chunk of step s for this lane
-#if MOE_DEC_CONTIG
-#define DEC_CH(s) (c0 + q * S + (s))
-#else
-#define DEC_CH(s) (c0 + 4 * (s) + q)
-#endif
+  __shared__ f32x4 red[SPLITK > 1 ? 4 : 1][NS][64];
+  // chunk of step s in K round r for this lane
+#define DEC_CH(r, s) (c0 + (r) * (4 * S) + 4 * (s) + q)
 
   DEC_STAMP(0);
-  int item = blockIdx.x;
-  Item<NMAT> cur = make_item<GATEUP>(a, item, n_items, ub, c, tiles, tile_tok, pool, ain);
+  // work units u = 0, 1, ...: item blockIdx.x + (u / nkr) * gridDim.x, K round u % nkr
+  const int G = gridDim.x;
+  int item = blockIdx.x, kr = 0;
+  Item<NS> cur = make_item<GATEUP, U>(a, load_desc<GATEUP>(a, item, c, tiles, tile_tok), n_items, wub, c, pool, ain);
   if (!cur.live) return;
+  // descriptor of unit 1
+  Desc dn = load_desc<GATEUP>(a, nkr > 1 ? item : item + G, c, tiles, tile_tok);
+  int kr2 = nkr > 2 ? 2 : (nkr == 2 ? 0 : 0);   // K round of unit 2
+  int item2 = nkr > 2 ? item : (nkr == 2 ? item + G : item + 2 * G);
   DEC_STAMP(1);
 #ifdef MOE_DEC_TIMING
   int n_done = 0;
 #endif
-  // A fragments of every step of the current item stay in registers.  Once
+  // A fragments of every step of the current unit stay in registers.  Once
   // step s is computed, its registers (weights and A) are refilled with the
-  // next item's step s, so both stream one item ahead and every wait is on
-  // loads issued a whole item earlier.
+  // next unit's step s, so both stream one unit ahead and every wait is on
+  // loads issued a whole unit earlier.
   uint4 xa[S][4];
 #pragma unroll
-  for (int s = 0; s < S; s++) load_a(xa[s], cur, min(DEC_CH(s), c1 - 1));
-  Step<NMAT> fb[S];
+  for (int s = 0; s < S; s++) load_a(xa[s], cur, min(DEC_CH(0, s), c1 - 1));
+  Step<NS> fb[S];
 #pragma unroll
-  for (int s = 0; s < S; s++) load_step<NMAT>(fb[s], cur, min(DEC_CH(s), c1 - 1));
+  for (int s = 0; s < S; s++) load_step<NS>(fb[s], cur, min(DEC_CH(0, s), c1 - 1));
+  f32x4 acc[NS];
 
   while (cur.live) {
-    const int nitem = item + gridDim.x;
-    const Item<NMAT> nxt = make_item<GATEUP>(a, nitem, n_items, ub, c, tiles, tile_tok, pool, ain);
-    f32x4 acc[NMAT];
+    const bool last_round = kr + 1 == nkr;
+    const int nkr_next = last_round ? 0 : kr + 1;
+    // the next unit (derived from the descriptor fetched a unit ago; the same
+    // item again when it is a further K round), then the descriptor of the
+    // unit after it
+    const Item<NS> nxt = make_item<GATEUP, U>(a, dn, n_items, wub, c, pool, ain);
+    __builtin_amdgcn_sched_barrier(0);
+    dn = load_desc<GATEUP>(a, item2, c, tiles, tile_tok);
+    kr2 = kr2 + 1 == nkr ? 0 : kr2 + 1;
+    item2 = kr2 == 0 ? item2 + G : item2;
+    __builtin_amdgcn_sched_barrier(0);
+    if (kr == 0) {
 #pragma unroll
-    for (int m = 0; m < NMAT; m++) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int m = 0; m < NS; m++) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int s = 0; s < S; s++) {
-      const int chr = DEC_CH(s);
+      const int chr = DEC_CH(kr, s);
       const int chc = min(chr, c1 - 1);
-      mma_step<NMAT>(fb[s], xa[s], cur, chc, !kempty && chr < c1 && cur.resident, acc);
+      mma_step<NS>(fb[s], xa[s], cur, chc, !kempty && chr < c1 && cur.resident, acc);
 #ifdef MOE_DEC_TIMING
       if (s == 0 && n_done == 0) {
         __builtin_amdgcn_sched_barrier(0);
         DEC_STAMP(2);
       }
 #endif
-      // this step's registers now carry the next item's step s
-      load_step<NMAT>(fb[s], nxt, min(DEC_CH(s), c1 - 1));
-      load_a(xa[s], nxt, min(DEC_CH(s), c1 - 1));
+      // this step's registers now carry the next unit's step s
+      const int chn = min(DEC_CH(nkr_next, s), c1 - 1);
+      load_step<NS>(fb[s], nxt, chn);
+      load_a(xa[s], nxt, chn);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // split-K partials meet in LDS; kpart 0 finishes the unit block
-    if (SPLITK > 1) {
+    if (last_round) {
+      // split-K partials meet in LDS; kpart 0 finishes the unit blocks
+      if (SPLITK > 1) {
 #pragma unroll
-      for (int m = 0; m < NMAT; m++) red[wave][m][lane] = acc[m];
-      __syncthreads();
-      if (kpart == 0) {
+        for (int m = 0; m < NS; m++) red[wave][m][lane] = acc[m];
+        __syncthreads();
+        if (kpart == 0) {
 #pragma unroll
-        for (int m = 0; m < NMAT; m++) {
-          f32x4 sum = red[wave][m][lane];
+          for (int m = 0; m < NS; m++) {
+            f32x4 sum = red[wave][m][lane];
 #pragma unroll
-          for (int w = 1; w < SPLITK; w++) sum += red[wave + w][m][lane];
-          acc[m] = sum;
-        }
-      }
-      __syncthreads();
-    }
-    if (kpart == 0) {
-      const float g0 = cur.g0, g1 = cur.g1;
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int m = 4 * q + r;  // D[m][c]
-        if (m >= cur.n) continue;
-        float v = 0.f;
-        if (cur.resident) {
-          if (GATEUP) {
-            const float gv = g0 * acc[0][r];
-            const float uv = g1 * acc[NMAT - 1][r];
-            v = gv / (1.0f + expf(-gv)) * uv;
-          } else {
-            v = g0 * acc[0][r];
+            for (int w = 1; w < SPLITK; w++) sum += red[wave + w][m][lane];
+            acc[m] = sum;
           }
         }
-        out[(int64_t)(cur.p0 + m) * units + cur.unit] = f32_to_bf16_rne(v);
+        __syncthreads();
       }
-    }
-    item = nitem;
-    cur = nxt;
+      if (kpart == 0) {
+        const float g0 = cur.g0, g1 = cur.g1;
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+#pragma unroll
+          for (int r = 0; r < 4; r++) {
+            const int m = 4 * q + r;  // D[m][c]
+            if (m >= cur.n) continue;
+            float v;
+            if (GATEUP) {
+              const float gv = g0 * acc[u * NMAT][r];
+              const float uv = g1 * acc[u * NMAT + NMAT - 1][r];
+              v = gv / (1.0f + expf(-gv)) * uv;
+            } else {
+              v = g0 * acc[u][r];
+            }
+            out[(int64_t)(cur.p0 + m) * units + cur.unit + 16 * u] = f32_to_bf16_rne(v);
+          }
+        }
+      }
 #ifdef MOE_DEC_TIMING
-    n_done++;
-    if (n_done <= 4) DEC_STAMP(2 + n_done);
+      n_done++;
+      if (n_done <= 4) DEC_STAMP(2 + n_done);
 #endif
+    }
+    item = last_round ? item + G : item;
+    kr = nkr_next;
+    cur = nxt;
   }
   DEC_STAMP(7);
+#undef DEC_CH
 }
 
-// steps per wave = ceil(K / 128 / SPLITK) <= 4 for K <= 2048 with SPLITK 4;
-// larger K uses more steps through the templated S.
 struct DecPtrs {
   const int4* tiles;
   const int32_t* tile_tok;
@@ -335,26 +361,27 @@ struct DecPtrs {
   uint16_t* out;
 };
 
-template <bool GATEUP, int SK>
-hipError_t launch_s(const DecArgs& a, const DecPtrs& p, int K, int grid, hipStream_t st) {
-  const int steps = ((K / 32 + SK - 1) / SK + 3) / 4;
-  const dim3 g(grid), b(256);
-#define MOE_DEC_LAUNCH(S_)                                                                                     \
-  hipLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S_>), g, b, 0, st, a, p.tiles, p.tile_tok, p.n_tiles, p.pool, p.ain, \
-                     p.out)
-  if (steps <= 1) MOE_DEC_LAUNCH(1);
-  else if (steps <= 2) MOE_DEC_LAUNCH(2);
-  else if (steps <= 4) MOE_DEC_LAUNCH(4);
-  else MOE_DEC_LAUNCH(8);
-#undef MOE_DEC_LAUNCH
+template <bool GATEUP, int SK, int S, int U>
+hipError_t launch_k(const DecArgs& a, const DecPtrs& p, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U>), dim3(grid), dim3(256), 0, st, a, p.tiles, p.tile_tok, p.n_tiles,
+                     p.pool, p.ain, p.out);
   return hipGetLastError();
 }
 
-}  // namespace
+template <bool GATEUP, int SK, int U>
+hipError_t launch_s(const DecArgs& a, const DecPtrs& p, int S, int grid, hipStream_t st) {
+  if (S <= 1) return launch_k<GATEUP, SK, 1, U>(a, p, grid, st);
+  if (S <= 2) return launch_k<GATEUP, SK, 2, U>(a, p, grid, st);
+  return launch_k<GATEUP, SK, (GATEUP ? MOE_DEC_MAXS_GU : MOE_DEC_MAXS_DN) >= 4 ? 4 : 2, U>(a, p, grid, st);
+}
 
-#ifndef MOE_DEC_WGS_PER_CU
-#define MOE_DEC_WGS_PER_CU 2
-#endif
+template <bool GATEUP>
+hipError_t launch_su(const DecArgs& a, const DecPtrs& p, int sk, int S, int U, int grid, hipStream_t st) {
+  if (sk == 4) return U == 2 ? launch_s<GATEUP, 4, 2>(a, p, S, grid, st) : launch_s<GATEUP, 4, 1>(a, p, S, grid, st);
+  return U == 2 ? launch_s<GATEUP, 1, 2>(a, p, S, grid, st) : launch_s<GATEUP, 1, 1>(a, p, S, grid, st);
+}
+
+}  // namespace
 
 // Decode-path FFN: both stages, persistent grids of (CUs x MOE_DEC_WGS_PER_CU)
 // workgroups (fewer when there is less work than that).
@@ -373,6 +400,7 @@ hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g
   a.off_globals = g.off_globals;
   a.H = d.H;
   a.I = d.I;
+  a.max_tiles = (int32_t)wl.max_tiles;
   a.a_bytes = (int32_t)((int64_t)d.T * d.H * 2);
   DecPtrs ptrs;
   ptrs.tiles = reinterpret_cast<const int4*>(base + wl.off_tiles);
@@ -383,24 +411,25 @@ hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g
   for (int stage = 0; stage < 2; stage++) {
     const bool gu = stage == 0;
     const int K = gu ? d.H : d.I, units = gu ? d.I : d.H;
+    const int ublocks = units / 16;
     const int steps = (K + 127) / 128;
     // split K four ways when a unit block has more than 4 steps, else give
-    // each wavefront its own unit block
-    const int sk = steps > 4 ? 4 : 1;
-    const int ubw = 4 / sk;
-    if ((units / 16) % ubw != 0) {  // unit blocks must fill whole items
-      a.n_ug = units / 16;           // one block per item, split K four ways
-    } else {
-      a.n_ug = units / 16 / ubw;
-    }
-    const int sk_used = ((units / 16) % ubw != 0) ? 4 : sk;
-    const int64_t items = wl.max_tiles * a.n_ug;
+    // each wavefront its own unit blocks; steps beyond MOE_DEC_MAXS per
+    // wavefront run as further K rounds
+    const int maxs = gu ? MOE_DEC_MAXS_GU : MOE_DEC_MAXS_DN;
+    int sk = steps > 4 ? 4 : 1;
+    int U = (gu ? MOE_DEC_U_GU : MOE_DEC_U_DN) > 1 ? 2 : 1;
+    if (ublocks % ((4 / sk) * U) != 0) U = 1;
+    if (ublocks % ((4 / sk) * U) != 0) sk = 4;  // one unit block per item, K split four ways
+    const int wsteps = (steps + sk - 1) / sk;
+    const int S = wsteps <= 1 ? 1 : (wsteps <= 2 || maxs <= 2) ? 2 : 4;
+    a.n_kr = (wsteps + S - 1) / S;
+    a.n_ug = ublocks / ((4 / sk) * U);
+    const int64_t items = (int64_t)wl.max_tiles * a.n_ug;
     const int grid = (int)(items < cap ? items : cap);
     ptrs.ain = gu ? x : h;
     ptrs.out = gu ? h : y_rows;
-    hipError_t e;
-    if (gu) e = sk_used == 4 ? launch_s<true, 4>(a, ptrs, K, grid, s) : launch_s<true, 1>(a, ptrs, K, grid, s);
-    else e = sk_used == 4 ? launch_s<false, 4>(a, ptrs, K, grid, s) : launch_s<false, 1>(a, ptrs, K, grid, s);
+    const hipError_t e = gu ? launch_su<true>(a, ptrs, sk, S, U, grid, s) : launch_su<false>(a, ptrs, sk, S, U, grid, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

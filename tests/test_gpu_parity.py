@@ -1,7 +1,8 @@
 """GPU parity at sizes the oracle finishes in seconds (every output compared).
 
 Covers the tiny workload, several FFN tiles with ragged tails, a reduction
-axis that is not a multiple of the 128-value step, degenerate shapes (T = 1,
+axis that is not a multiple of the 128-value step, reduction axes longer than
+4096 (several K rounds per wavefront), degenerate shapes (T = 1,
 E = k = 1, k = E, E = 1024), a non-resident slot, an out-of-range expert id,
 token-permutation invariance and run-to-run determinism."""
 import numpy as np
@@ -81,6 +82,9 @@ SMALL = {
     "k_equals_E": Config(34, "kE", T=5, H=128, I=64, E=6, k=6, L=1, router="zipf", zipf_s=0.5),
     "E1024_max": Config(35, "E1024", T=3, H=64, I=64, E=1024, k=8, L=1, router="zipf", zipf_s=1.0),
     "big_k_wide": Config(36, "bk", T=19, H=1024, I=512, E=64, k=16, L=1, router="matrix"),
+    # K beyond 4096 on both stages: each wavefront covers its share of K in
+    # several rounds, the last one ragged
+    "long_K_rounds": Config(37, "lk", T=6, H=4608, I=4352, E=4, k=2, L=1, router="matrix"),
 }
 
 
