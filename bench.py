@@ -9,16 +9,27 @@ every (layer, expert) resident in an HBM slot pool).  Inputs for every timed
 step are generated on the device before timing starts.
 
 Extra objects on the line:
-  roofline      the expert-FFN launch (dominant stage): algorithmic bytes (decode,
-                HBM-bound) or flops (prefill, MFMA-bound) per launch divided by
-                its mean duration from HIP events on its stream, against the
+  roofline      the dominant kernel, the expert FFN's gate/up stage (one
+                launch of moe_expert_ffn_stages with stages = 1 per layer):
+                algorithmic bytes (decode, HBM-bound: the gate and up codes,
+                scales and global scales of every distinct expert touched) or
+                flops (prefill, MFMA-bound: 4 H I per row) per launch, divided
+                by its mean duration from HIP events on its stream, against the
                 MI355X spec peak (HBM 8.0 TB/s; dense bf16 MFMA 2.5 PFLOP/s).
+                The down stage is reported beside it.  "traffic" is the HBM
+                bytes per launch measured with rocprofv3 counters and recorded
+                in profiles/ (null unless it was measured on this kernel source).
   cpu_baseline  the CPU oracle (oracle/, fp64 numpy, 1 thread) on a bounded
                 sample of the same workload, scaled to tokens/s.
+
+--copy-calibration BYTES runs only a plain device copy of BYTES bytes five
+times (the reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters).
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -48,7 +59,67 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch every call eagerly instead of HIP graphs")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_gateup_%s_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "moe_expert_ffn_top_amd", "csrc", "ffn_dec.hip")
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch already loaded (same
+    SONAME, so the same runtime instance), for kernel-bracketing launches."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = []
+
+    def new(self):
+        e = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(e))
+        assert rc == 0, "hipEventCreate failed (%d)" % rc
+        self.handles.append(e.value)
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        assert rc == 0, "hipEventElapsedTime failed (%d)" % rc
+        return float(ms.value)
+
+    def close(self):
+        for e in self.handles:
+            self.hip.hipEventDestroy(e)
+        self.handles = []
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per gate/up launch from the counter summary in profiles/, if it
+    was taken on the current kernel source; else None."""
+    path = TRAFFIC_FILE % workload
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 class Workload:
@@ -98,9 +169,11 @@ class Workload:
     def input_index(self, step):
         return step % self.n_inputs
 
-    def run_step(self, step, stream=None, ffn_events=None):
-        """Enqueue every layer of one step.  ffn_events: list to which
-        (start, end) event pairs around each expert-FFN launch are appended."""
+    def run_step(self, step, stream=None, ffn_events=None, hip_events=None):
+        """Enqueue every layer of one step.  With ffn_events (a list) the FFN
+        runs as its two stages, each launched with a pair of HIP events that
+        the device records at the kernel's own start and end; per layer
+        ((gate/up start, end, down start, end), offsets) is appended."""
         import torch
         from moe_expert_ffn_top_amd import binding as B
 
@@ -114,29 +187,37 @@ class Workload:
                 B.moe_route(d, x, None, self.logits[s, l], self.wsg[l], None, buf.ids, buf.w, buf.sigma, stream)
             B.moe_group(d, l, buf.ids, self.slot_table, self.n_slots, buf.offsets, buf.perm, buf.inv_perm,
                         buf.group_slot, buf.status, buf.ws, stream=stream)
-            if ffn_events is not None:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-            B.moe_expert_ffn(d, x, self.pool, self.pool_bytes, self.layout, buf.offsets, buf.perm, buf.group_slot,
-                             buf.h, buf.y_rows, buf.status, buf.ws, stream=stream)
-            if ffn_events is not None:
-                e1.record()
-                ffn_events.append((e0, e1, buf.offsets.clone()))
+            if ffn_events is None:
+                B.moe_expert_ffn(d, x, self.pool, self.pool_bytes, self.layout, buf.offsets, buf.perm,
+                                 buf.group_slot, buf.h, buf.y_rows, buf.status, buf.ws, stream=stream)
+            else:
+                ev = [hip_events.new() for _ in range(4)]
+                for st in (1, 2):
+                    B.moe_expert_ffn_stages(d, x, self.pool, self.pool_bytes, self.layout, buf.offsets, buf.perm,
+                                            buf.group_slot, buf.h, buf.y_rows, buf.status, buf.ws, st,
+                                            ev[2 * st - 2], ev[2 * st - 1], stream=stream)
+                ffn_events.append((ev, buf.offsets.clone()))
             B.moe_combine(d, buf.y_rows, buf.inv_perm, buf.w, buf.sigma, buf.y, stream)
 
 
-def expert_work(cfg, offsets_list, blob_bytes):
-    """Algorithmic work of the FFN launches: bytes of the distinct expert blobs
-    touched (routed groups with rows, plus the shared expert) and flops
-    (6 H I per row)."""
-    nbytes, flops = [], []
+def expert_work(cfg, offsets_list):
+    """Algorithmic work of each FFN stage per launch, from the group offsets:
+    bytes of the distinct experts touched (routed groups with rows, plus the
+    shared expert) and flops per row.
+      gate/up: codes 2 I H / 2, scales 2 I H / 16, two fp32 globals; 4 H I flops
+      down:    codes H I / 2,   scales H I / 16,   one fp32 global;  2 H I flops
+    Returns arrays (gu_bytes, dn_bytes, gu_flops, dn_flops)."""
+    H, I = cfg.H, cfg.I
+    gu_b, dn_b, gu_f, dn_f = [], [], [], []
     for off in offsets_list:
         o = off.cpu().numpy()
         active = int(np.count_nonzero(np.diff(o[:cfg.E + 1]))) + 1
         rows = int(o[cfg.E]) + cfg.T
-        nbytes.append(active * blob_bytes)
-        flops.append(6.0 * cfg.H * cfg.I * rows)
-    return np.array(nbytes, dtype=np.float64), np.array(flops, dtype=np.float64)
+        gu_b.append(active * (I * H + I * H // 8 + 8))
+        dn_b.append(active * (H * I // 2 + H * I // 16 + 4))
+        gu_f.append(4.0 * H * I * rows)
+        dn_f.append(2.0 * H * I * rows)
+    return tuple(np.array(v, dtype=np.float64) for v in (gu_b, dn_b, gu_f, dn_f))
 
 
 def cpu_baseline(cfg, seconds):
@@ -206,6 +287,16 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied %d bytes five times" % n)
+        return
     from moe_expert_ffn_top_amd import binding as B
     from synth import DevGen, config_by_name
 
@@ -250,27 +341,37 @@ def main():
     tokens_per_s = cfg.T / (ms_per_step / 1e3)
     log("%.4f ms/step, %.1f tokens/s" % (ms_per_step, tokens_per_s))
 
-    # roofline of the expert-FFN launch: events around each launch on its stream
+    # roofline of the dominant kernel (the FFN's gate/up stage) and of the down
+    # stage: HIP events around each stage's launch on its stream
     events = []
+    hev = HipEvents()
     for i in range(min(K, 8)):
-        wl.run_step(W + i, ffn_events=events)
+        wl.run_step(W + i, ffn_events=events, hip_events=hev)
     torch.cuda.synchronize()
-    dur_ms = np.array([a.elapsed_time(b) for a, b, _ in events])
-    nbytes, flops = expert_work(cfg, [o for _, _, o in events], wl.layout.blob_bytes)
+    gu_ms = np.array([hev.elapsed_ms(ev[0], ev[1]) for ev, _ in events])
+    dn_ms = np.array([hev.elapsed_ms(ev[2], ev[3]) for ev, _ in events])
+    hev.close()
+    gu_b, dn_b, gu_f, dn_f = expert_work(cfg, [o for _, o in events])
     decode = cfg.T <= 64
     if decode:
-        achieved = float(nbytes.mean() / (dur_ms.mean() * 1e-3) / 1e9)
+        achieved = float(gu_b.mean() / (gu_ms.mean() * 1e-3) / 1e9)
+        traffic = recorded_traffic(cfg.name)
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                "kernel": "moe_expert_ffn launch (gate/up + down)", "launch_us": float(dur_ms.mean() * 1e3),
-                "bytes_per_launch": float(nbytes.mean())}
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                "kernel": "k_ffn_dec gate/up (moe_expert_ffn_stages, stages=1)",
+                "launch_us": float(gu_ms.mean() * 1e3), "bytes_per_launch": float(gu_b.mean()),
+                "down": {"launch_us": float(dn_ms.mean() * 1e3), "bytes_per_launch": float(dn_b.mean()),
+                         "achieved": float(dn_b.mean() / (dn_ms.mean() * 1e-3) / 1e9)}}
     else:
-        achieved = float(flops.mean() / (dur_ms.mean() * 1e-3) / 1e12)
+        achieved = float(gu_f.mean() / (gu_ms.mean() * 1e-3) / 1e12)
         roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
-                "kernel": "moe_expert_ffn launch (gate/up + down)", "launch_us": float(dur_ms.mean() * 1e3),
-                "flops_per_launch": float(flops.mean())}
-    log("expert FFN launch: %.1f us, %s" % (dur_ms.mean() * 1e3, roof))
+                "kernel": "k_ffn_dec gate/up (moe_expert_ffn_stages, stages=1)",
+                "launch_us": float(gu_ms.mean() * 1e3), "flops_per_launch": float(gu_f.mean()),
+                "down": {"launch_us": float(dn_ms.mean() * 1e3), "flops_per_launch": float(dn_f.mean()),
+                         "achieved": float(dn_f.mean() / (dn_ms.mean() * 1e-3) / 1e12)}}
+    roof["kernel_source_sha256_16"] = kernel_source_hash()
+    log("roofline: %s" % roof)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -208,6 +208,26 @@ int moe_expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool,
                    int32_t* dev_status, void* ws, uint64_t ws_bytes,
                    moe_stream_t stream);
 
+/* The two stages of moe_expert_ffn (same definition as above), selectively:
+ * stages = 1 runs gate/up and the activation (writes h), 2 runs the down
+ * projection (reads h, writes y_rows), 3 runs both and is moe_expert_ffn.  A
+ * down stage reads the h written by a gate/up stage with the same inputs
+ * earlier on the same stream.  For callers that time the stages apart or put
+ * other work between them.
+ * ev_start, ev_stop: hipEvent_t handles created by the caller, or NULL.  When
+ * set, the device records ev_start when the first launched kernel starts and
+ * ev_stop when the last one ends (hipExtLaunchKernelGGL), so their elapsed
+ * time is the stages' own duration.  Leave both NULL under graph capture.
+ * MOE_ERR_ARG for stages outside 1..3; every other argument as for
+ * moe_expert_ffn. */
+int moe_expert_ffn_stages(const moe_dims* d, const uint16_t* x, const void* pool,
+                          uint64_t pool_bytes, const moe_blob_layout* layout,
+                          const int32_t* offsets, const int32_t* perm,
+                          const int32_t* group_slot, uint16_t* h, uint16_t* y_rows,
+                          int32_t* dev_status, void* ws, uint64_t ws_bytes,
+                          int32_t stages, void* ev_start, void* ev_stop,
+                          moe_stream_t stream);
+
 /* ---- S5: combine -------------------------------------------------------
  * [Strata] "路由以后，专家怎样分工？" (each expert output times its router weight,
  * summed, plus the gated shared-expert contribution) and "少算这些专家，会付出

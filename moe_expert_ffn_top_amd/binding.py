@@ -33,8 +33,8 @@ MOE_DEV_BAD_SLOT = 4
 
 #: every symbol include/moe.h declares
 EXPORTED = ("moe_status_string", "moe_last_error", "moe_version", "moe_blob_layout_init", "moe_workspace_bytes",
-            "moe_route", "moe_group", "moe_expert_ffn", "moe_combine", "moe_ring_create", "moe_stage_h2d",
-            "moe_ring_acquire", "moe_ring_release", "moe_ring_slot_ptr", "moe_ring_destroy")
+            "moe_route", "moe_group", "moe_expert_ffn", "moe_expert_ffn_stages", "moe_combine", "moe_ring_create",
+            "moe_stage_h2d", "moe_ring_acquire", "moe_ring_release", "moe_ring_slot_ptr", "moe_ring_destroy")
 
 
 class Dims(ctypes.Structure):
@@ -74,6 +74,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.moe_group.argtypes = [_DP, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _u64, _vp]
     lib.moe_expert_ffn.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _u64, _vp]
+    lib.moe_expert_ffn_stages.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _vp,
+                                          _vp, _vp, _u64, _i32, _vp, _vp, _vp]
     lib.moe_combine.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.moe_ring_create.argtypes = [_vp, _vp, _u64, _vp, ctypes.POINTER(_vp)]
     lib.moe_stage_h2d.argtypes = [_vp, _vp, _u64, ctypes.POINTER(_i32)]
@@ -159,6 +161,18 @@ def moe_expert_ffn(dims, x, pool, pool_bytes, layout: BlobLayout, offsets, perm,
     _check(_lib.moe_expert_ffn(ctypes.byref(dims), _p(x), _p(pool), pool_bytes, ctypes.byref(layout), _p(offsets),
                                _p(perm), _p(group_slot), _p(h), _p(y_rows), _p(dev_status), _p(ws), ws_bytes,
                                _s(stream)), "moe_expert_ffn")
+
+
+def moe_expert_ffn_stages(dims, x, pool, pool_bytes, layout: BlobLayout, offsets, perm, group_slot, h, y_rows,
+                          dev_status, ws, stages: int, ev_start: Optional[int] = None, ev_stop: Optional[int] = None,
+                          ws_bytes: Optional[int] = None, stream=None) -> None:
+    """ev_start / ev_stop: raw hipEvent_t handles (ints) or None."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.moe_expert_ffn_stages(ctypes.byref(dims), _p(x), _p(pool), pool_bytes, ctypes.byref(layout),
+                                      _p(offsets), _p(perm), _p(group_slot), _p(h), _p(y_rows), _p(dev_status),
+                                      _p(ws), ws_bytes, stages, ev_start, ev_stop, _s(stream)),
+           "moe_expert_ffn_stages")
 
 
 def moe_combine(dims, y_rows, inv_perm, topk_w, shared_sigma, y, stream=None) -> None:

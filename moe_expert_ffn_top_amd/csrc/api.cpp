@@ -181,6 +181,15 @@ int moe_expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool, uint6
                    const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm,
                    const int32_t* group_slot, uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws,
                    uint64_t ws_bytes, moe_stream_t stream) {
+  return moe_expert_ffn_stages(d, x, pool, pool_bytes, layout, offsets, perm, group_slot, h, y_rows, dev_status, ws,
+                               ws_bytes, 3, nullptr, nullptr, stream);
+}
+
+int moe_expert_ffn_stages(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
+                          const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm,
+                          const int32_t* group_slot, uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws,
+                          uint64_t ws_bytes, int32_t stages, void* ev_start, void* ev_stop, moe_stream_t stream) {
+  if (stages < 1 || stages > 3) return fail(MOE_ERR_ARG, "stages = %d: must be 1 (gate/up), 2 (down) or 3", stages);
   int r = check_dims(d);
   if (r) return r;
   if (!layout) return fail(MOE_ERR_ARG, "layout is NULL");
@@ -217,8 +226,10 @@ int moe_expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool, uint6
     g.off_scales[m] = layout->off_scales[m];
   }
   g.off_globals = layout->off_globals;
-  return hip_status(moe::launch_ffn_dec(*d, x, g, perm, h, y_rows, ws, n_cu, reinterpret_cast<hipStream_t>(stream)),
-                    "expert FFN launch");
+  return hip_status(
+      moe::launch_ffn_dec(*d, x, g, perm, h, y_rows, ws, n_cu, stages, static_cast<hipEvent_t>(ev_start),
+                          static_cast<hipEvent_t>(ev_stop), reinterpret_cast<hipStream_t>(stream)),
+      "expert FFN launch");
 }
 
 int moe_combine(const moe_dims* d, const uint16_t* y_rows, const int32_t* inv_perm, const float* topk_w,

@@ -24,6 +24,7 @@
 //    the registers of one A fragment.
 //  - SPLITK wavefronts of a unit block split K; partials meet in LDS.  A
 //    wavefront's share of K is covered in K rounds of S steps.
+#include <hip/hip_ext.h>
 #include <math.h>
 
 #include "moe_common.hpp"
@@ -361,24 +362,36 @@ struct DecPtrs {
   uint16_t* out;
 };
 
+// ev0 / ev1: when either is set, the launch goes through hipExtLaunchKernelGGL
+// and the device records them at the kernel's start and end.
+struct DecLaunch {
+  int grid;
+  hipStream_t st;
+  hipEvent_t ev0, ev1;
+};
+
 template <bool GATEUP, int SK, int S, int U>
-hipError_t launch_k(const DecArgs& a, const DecPtrs& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U>), dim3(grid), dim3(256), 0, st, a, p.tiles, p.tile_tok, p.n_tiles,
-                     p.pool, p.ain, p.out);
+hipError_t launch_k(const DecArgs& a, const DecPtrs& p, const DecLaunch& l) {
+  if (l.ev0 || l.ev1)
+    hipExtLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U>), dim3(l.grid), dim3(256), 0, l.st, l.ev0, l.ev1, 0, a,
+                          p.tiles, p.tile_tok, p.n_tiles, p.pool, p.ain, p.out);
+  else
+    hipLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U>), dim3(l.grid), dim3(256), 0, l.st, a, p.tiles, p.tile_tok,
+                       p.n_tiles, p.pool, p.ain, p.out);
   return hipGetLastError();
 }
 
 template <bool GATEUP, int SK, int U>
-hipError_t launch_s(const DecArgs& a, const DecPtrs& p, int S, int grid, hipStream_t st) {
-  if (S <= 1) return launch_k<GATEUP, SK, 1, U>(a, p, grid, st);
-  if (S <= 2) return launch_k<GATEUP, SK, 2, U>(a, p, grid, st);
-  return launch_k<GATEUP, SK, (GATEUP ? MOE_DEC_MAXS_GU : MOE_DEC_MAXS_DN) >= 4 ? 4 : 2, U>(a, p, grid, st);
+hipError_t launch_s(const DecArgs& a, const DecPtrs& p, int S, const DecLaunch& l) {
+  if (S <= 1) return launch_k<GATEUP, SK, 1, U>(a, p, l);
+  if (S <= 2) return launch_k<GATEUP, SK, 2, U>(a, p, l);
+  return launch_k<GATEUP, SK, (GATEUP ? MOE_DEC_MAXS_GU : MOE_DEC_MAXS_DN) >= 4 ? 4 : 2, U>(a, p, l);
 }
 
 template <bool GATEUP>
-hipError_t launch_su(const DecArgs& a, const DecPtrs& p, int sk, int S, int U, int grid, hipStream_t st) {
-  if (sk == 4) return U == 2 ? launch_s<GATEUP, 4, 2>(a, p, S, grid, st) : launch_s<GATEUP, 4, 1>(a, p, S, grid, st);
-  return U == 2 ? launch_s<GATEUP, 1, 2>(a, p, S, grid, st) : launch_s<GATEUP, 1, 1>(a, p, S, grid, st);
+hipError_t launch_su(const DecArgs& a, const DecPtrs& p, int sk, int S, int U, const DecLaunch& l) {
+  if (sk == 4) return U == 2 ? launch_s<GATEUP, 4, 2>(a, p, S, l) : launch_s<GATEUP, 4, 1>(a, p, S, l);
+  return U == 2 ? launch_s<GATEUP, 1, 2>(a, p, S, l) : launch_s<GATEUP, 1, 1>(a, p, S, l);
 }
 
 }  // namespace
@@ -386,7 +399,8 @@ hipError_t launch_su(const DecArgs& a, const DecPtrs& p, int sk, int S, int U, i
 // Decode-path FFN: both stages, persistent grids of (CUs x MOE_DEC_WGS_PER_CU)
 // workgroups (fewer when there is less work than that).
 hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
-                          uint16_t* y_rows, void* ws, int n_cu, hipStream_t s) {
+                          uint16_t* y_rows, void* ws, int n_cu, int stages, hipEvent_t ev_start, hipEvent_t ev_stop,
+                          hipStream_t s) {
   (void)perm;
   const WsLayout wl = ws_layout(d);
   uint8_t* base = static_cast<uint8_t*>(ws);
@@ -409,6 +423,7 @@ hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g
   ptrs.pool = g.pool;
   const int64_t cap = (int64_t)n_cu * MOE_DEC_WGS_PER_CU;
   for (int stage = 0; stage < 2; stage++) {
+    if (!((stages >> stage) & 1)) continue;
     const bool gu = stage == 0;
     const int K = gu ? d.H : d.I, units = gu ? d.I : d.H;
     const int ublocks = units / 16;
@@ -429,7 +444,10 @@ hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g
     const int grid = (int)(items < cap ? items : cap);
     ptrs.ain = gu ? x : h;
     ptrs.out = gu ? h : y_rows;
-    const hipError_t e = gu ? launch_su<true>(a, ptrs, sk, S, U, grid, s) : launch_su<false>(a, ptrs, sk, S, U, grid, s);
+    // the start event goes with the first stage launched, the stop event with the last
+    const bool first = gu || !(stages & 1), last = !gu || !(stages & 2);
+    const DecLaunch l{grid, s, first ? ev_start : nullptr, last ? ev_stop : nullptr};
+    const hipError_t e = gu ? launch_su<true>(a, ptrs, sk, S, U, l) : launch_su<false>(a, ptrs, sk, S, U, l);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

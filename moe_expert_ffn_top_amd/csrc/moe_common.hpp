@@ -135,8 +135,12 @@ hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, co
                         int32_t* dev_status, void* ws, hipStream_t s);
 hipError_t launch_ffn(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm,
                       uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws, hipStream_t s);
+// stages: bit 1 = gate/up (writes h), bit 2 = down (reads h, writes y_rows)
+// ev_start / ev_stop (may be null): recorded at the start of the first launched
+// kernel and the end of the last one
 hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm,
-                          uint16_t* h, uint16_t* y_rows, void* ws, int n_cu, hipStream_t s);
+                          uint16_t* h, uint16_t* y_rows, void* ws, int n_cu, int stages, hipEvent_t ev_start,
+                          hipEvent_t ev_stop, hipStream_t s);
 hipError_t launch_combine(const moe_dims& d, const uint16_t* y_rows, const int32_t* inv_perm, const float* w,
                           const float* sigma, uint16_t* y, hipStream_t s);
 

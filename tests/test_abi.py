@@ -126,6 +126,12 @@ def test_ffn_validation(B):
     unaligned_pool = list(ok_args)
     unaligned_pool[1] = fake + 8
     assert B.raw_status("moe_expert_ffn", d, *unaligned_pool) == B.MOE_ERR_ALIGN
+    # the staged form rejects a stage mask outside 1..3 before anything else,
+    # and validates the rest like moe_expert_ffn
+    for stages in (0, 4, -1):
+        assert B.raw_status("moe_expert_ffn_stages", d, *ok_args[:-1], stages, None, None, None) == B.MOE_ERR_ARG
+    assert B.raw_status("moe_expert_ffn_stages", d, *short_ws[:-1], 1, None, None, None) == B.MOE_ERR_WORKSPACE
+    assert B.raw_status("moe_expert_ffn_stages", d, *unaligned_pool[:-1], 2, None, None, None) == B.MOE_ERR_ALIGN
 
 
 def test_combine_and_ring_validation(B):

@@ -99,6 +99,24 @@ def test_layer_parity_small(B, hostgen, name):
     say("[gpu]   %s ok: %s" % (name, stats))
 
 
+def test_ffn_stages_split_matches_whole(B, hostgen):
+    """gate/up then down as two calls gives the bytes of the single call."""
+    cfg = SMALL["multitile_ragged"]
+    say("[gpu] FFN stages 1 + 2 vs 3")
+    case = Case(B, cfg, hostgen)
+    case.run(B)
+    b = case.buf
+    h_ref, y_ref = b.h.clone(), b.y_rows.clone()
+    b.h.zero_()
+    b.y_rows.zero_()
+    for st in (1, 2):
+        B.moe_expert_ffn_stages(case.dims, case.x, case.pool, case.pool_bytes, case.layout, b.offsets, b.perm,
+                                b.group_slot, b.h, b.y_rows, b.status, b.ws, st)
+    torch.cuda.synchronize()
+    assert torch.equal(b.h.view(torch.int16), h_ref.view(torch.int16))
+    assert torch.equal(b.y_rows.view(torch.int16), y_ref.view(torch.int16))
+
+
 def test_non_resident_slot_gives_zero_rows_and_status(B, hostgen):
     cfg = CONFIGS[1]
     say("[gpu] non-resident slot case")
