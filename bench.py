@@ -64,7 +64,16 @@ def parse():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_gateup_%s_traffic.txt")
-KERNEL_SRC = os.path.join(ROOT, "moe_expert_ffn_top_amd", "csrc", "ffn_dec.hip")
+CSRC = os.path.join(ROOT, "moe_expert_ffn_top_amd", "csrc")
+
+
+def ffn_kernel(cfg):
+    """(kernel name, source file) of the FFN path the library takes for these
+    shapes: the grouped GEMM when groups average >= 16 rows (T k >= 16 E),
+    else the weight-streaming kernel."""
+    if cfg.T * cfg.k >= 16 * cfg.E:
+        return "k_ffn_gemm", os.path.join(CSRC, "ffn_gemm.hip")
+    return "k_ffn_dec", os.path.join(CSRC, "ffn_dec.hip")
 
 
 class HipEvents:
@@ -97,15 +106,15 @@ class HipEvents:
         self.handles = []
 
 
-def kernel_source_hash():
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_source_hash(cfg):
+    with open(ffn_kernel(cfg)[1], "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def recorded_traffic(workload):
+def recorded_traffic(cfg):
     """HBM bytes per gate/up launch from the counter summary in profiles/, if it
     was taken on the current kernel source; else None."""
-    path = TRAFFIC_FILE % workload
+    path = TRAFFIC_FILE % cfg.name
     if not os.path.exists(path):
         return None
     kv = {}
@@ -114,7 +123,7 @@ def recorded_traffic(workload):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash(cfg):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -355,10 +364,10 @@ def main():
     decode = cfg.T <= 64
     if decode:
         achieved = float(gu_b.mean() / (gu_ms.mean() * 1e-3) / 1e9)
-        traffic = recorded_traffic(cfg.name)
+        traffic = recorded_traffic(cfg)
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                "kernel": "k_ffn_dec gate/up (moe_expert_ffn_stages, stages=1)",
+                "kernel": "%s gate/up (moe_expert_ffn_stages, stages=1)" % ffn_kernel(cfg)[0],
                 "launch_us": float(gu_ms.mean() * 1e3), "bytes_per_launch": float(gu_b.mean()),
                 "down": {"launch_us": float(dn_ms.mean() * 1e3), "bytes_per_launch": float(dn_b.mean()),
                          "achieved": float(dn_b.mean() / (dn_ms.mean() * 1e-3) / 1e9)}}
@@ -366,11 +375,11 @@ def main():
         achieved = float(gu_f.mean() / (gu_ms.mean() * 1e-3) / 1e12)
         roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
-                "kernel": "k_ffn_dec gate/up (moe_expert_ffn_stages, stages=1)",
+                "kernel": "%s gate/up (moe_expert_ffn_stages, stages=1)" % ffn_kernel(cfg)[0],
                 "launch_us": float(gu_ms.mean() * 1e3), "flops_per_launch": float(gu_f.mean()),
                 "down": {"launch_us": float(dn_ms.mean() * 1e3), "flops_per_launch": float(dn_f.mean()),
                          "achieved": float(dn_f.mean() / (dn_ms.mean() * 1e-3) / 1e12)}}
-    roof["kernel_source_sha256_16"] = kernel_source_hash()
+    roof["kernel_source_sha256_16"] = kernel_source_hash(cfg)
     log("roofline: %s" % roof)
 
     cpu = None

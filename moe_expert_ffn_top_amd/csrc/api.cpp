@@ -226,10 +226,15 @@ int moe_expert_ffn_stages(const moe_dims* d, const uint16_t* x, const void* pool
     g.off_scales[m] = layout->off_scales[m];
   }
   g.off_globals = layout->off_globals;
-  return hip_status(
-      moe::launch_ffn_dec(*d, x, g, perm, h, y_rows, ws, n_cu, stages, static_cast<hipEvent_t>(ev_start),
-                          static_cast<hipEvent_t>(ev_stop), reinterpret_cast<hipStream_t>(stream)),
-      "expert FFN launch");
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
+  // groups averaging >= kGemmMinRows rows: grouped GEMM over 256-row chunks;
+  // otherwise weight streaming over 16-row tiles (the grouping kernels wrote
+  // the matching work list)
+  if (moe::use_gemm(*d))
+    return hip_status(moe::launch_ffn_gemm(*d, x, g, perm, h, y_rows, ws, stages, e0, e1, st), "expert FFN launch");
+  return hip_status(moe::launch_ffn_dec(*d, x, g, perm, h, y_rows, ws, n_cu, stages, e0, e1, st),
+                    "expert FFN launch");
 }
 
 int moe_combine(const moe_dims* d, const uint16_t* y_rows, const int32_t* inv_perm, const float* topk_w,

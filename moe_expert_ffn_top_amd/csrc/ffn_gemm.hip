@@ -1,0 +1,262 @@
+// S4 for prefill-sized groups: grouped GEMM over chunks of <= 256 rows.
+//
+// [Strata] "路由以后，专家怎样分工？": the rows routed to one expert form one
+// group, so the expert's weights can be read once for all of them; with a few
+// hundred rows per group the FFN is a dense contraction and belongs on MFMA.
+//  - Work: (chunk of <= 256 rows of one group, tile of output columns).  The
+//    grouping kernels list the chunks; blocks map to (chunk, tile) so that all
+//    tiles of one chunk run on the same XCD and share the chunk's A rows in
+//    that XCD's L2.
+//  - Per 64-value K step a 512-thread workgroup stages into LDS (double
+//    buffered) the chunk's A rows (bf16 rows of x gathered through perm, or
+//    rows of h) and the B tile: 128 columns of weights (gate/up: 64 units of
+//    each matrix; down: 128 units) decoded from E2M1 codes times their E4M3
+//    scale in fp32 (exact: <= 6 significant bits) and packed to bf16 (exact).
+//    Global loads run two steps ahead in registers.
+//  - Eight wavefronts each own a 64 x 64 block of the 256 x 128 output and
+//    accumulate exact bf16 products in fp32 with v_mfma_f32_16x16x32_bf16; the
+//    global scales and the activation are applied in the epilogue.
+#include <hip/hip_ext.h>
+#include <math.h>
+
+#include "moe_common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int GM = kChunkRows;   // rows per workgroup
+constexpr int GC = 128;          // output columns per workgroup
+constexpr int GK = 64;           // K per step
+constexpr int LROW = GK + 8;     // bf16 per LDS row: a 16-byte pad keeps 16-byte lane reads conflict-free
+constexpr int GT = 512;          // threads per workgroup
+
+template <typename T>
+using cptr = const __attribute__((address_space(4))) T*;
+template <typename T>
+__device__ inline cptr<T> as_const(const T* p) {
+  return (cptr<T>)p;
+}
+
+struct GemmArgs {
+  uint32_t slot_stride;
+  int32_t n_slots;
+  uint32_t off_codes[3];
+  uint32_t off_scales[3];
+  uint32_t off_globals;
+  int32_t H, I, k, Tk;  // Tk = T * k: routed rows; rows from Tk on are the shared group's
+  int32_t n_ut;         // column tiles per chunk
+  int32_t nk;           // K steps
+};
+
+// One thread's global loads for one K step: 32 A values, and (threads < 256)
+// 32 weight codes with the aligned dword holding their two scales.
+struct Stage {
+  uint4 a[4];
+  uint4 c;
+  uint32_t sc;
+};
+
+template <bool GATEUP>
+__global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restrict__ chunks,
+                                                 const int32_t* __restrict__ meta, const int32_t* __restrict__ perm,
+                                                 const uint8_t* __restrict__ pool, const uint16_t* __restrict__ ain,
+                                                 uint16_t* __restrict__ out) {
+  constexpr int NMAT = GATEUP ? 2 : 1;
+  constexpr int UPW = GC / NMAT;  // units per workgroup
+  const int K = GATEUP ? a.H : a.I;
+  const int units = GATEUP ? a.I : a.H;
+  // blocks are dealt to the 8 XCDs round-robin: block b runs on XCD b % 8
+  const int b = blockIdx.x, xcd = b & 7, jb = b >> 3;
+  const int ut = jb % a.n_ut, chunk = (jb / a.n_ut) * 8 + xcd;
+  if (chunk >= *as_const(meta + 1)) return;
+  using i32x4 = int __attribute__((ext_vector_type(4)));
+  const i32x4 cd = as_const(reinterpret_cast<const i32x4*>(chunks))[chunk];
+  const int p0 = cd.y, n = cd.z, slot = cd.w;
+  const bool resident = slot >= 0 && slot < a.n_slots;
+  const uint8_t* blob = pool + (resident ? (uint64_t)slot * (uint64_t)a.slot_stride : 0);
+  const int u0 = ut * UPW;
+
+  __shared__ __align__(16) uint16_t As[2][GM * LROW];
+  __shared__ __align__(16) uint16_t Bs[2][GC * LROW];
+
+  const int tid = threadIdx.x;
+  // A staging: thread -> row ar, K half ah (32 values); rows beyond n repeat
+  // the last row (their outputs are not written)
+  const int ar = tid >> 1, ah = tid & 1;
+  const int p = p0 + min(ar, n - 1);
+  const int64_t arow = GATEUP ? (int64_t)(p < a.Tk ? perm[p] / a.k : p - a.Tk) : (int64_t)p;
+  const uint16_t* asrc = ain + arow * K;
+  // B staging (threads < 256, i.e. wavefronts 0..3): column bc, K half bh
+  const int bc = (tid >> 1) & (GC - 1), bh = tid & 1;
+  const int bmat = GATEUP ? bc / UPW : 2;
+  const int bunit = u0 + bc % UPW;
+  const bool bvalid = resident && bunit < units;
+  const int bunit_c = min(bunit, units - 1);
+  // a non-resident group reads the pool's first bytes (valid memory) and is
+  // zeroed through its scales
+  const uint8_t* crow = bvalid ? blob + a.off_codes[bmat] + (int64_t)bunit_c * (K / 2) : pool;
+  const uint8_t* srow = bvalid ? blob + a.off_scales[bmat] + (int64_t)bunit_c * (K / 16) : pool;
+  const bool loads_b = tid < 256;
+
+  // Every load stays inside its row: the K offset is clamped to the last
+  // 32 values, which only a half step beyond K (K % 64 == 32) needs; that
+  // half is zeroed when staged.
+  auto gload = [&](Stage& st, int s) {
+    const int sc_ = min(s, a.nk - 1);
+    const uint4* ap = reinterpret_cast<const uint4*>(asrc + min(sc_ * GK + ah * 32, K - 32));
+#pragma unroll
+    for (int i = 0; i < 4; i++) st.a[i] = ap[i];
+    if (loads_b) {
+      st.c = *reinterpret_cast<const uint4*>(crow + min(sc_ * (GK / 2) + bh * 16, K / 2 - 16));
+      // the two scale bytes of these 32 values, from the aligned dword holding them
+      const uint8_t* sp = srow + min(sc_ * (GK / 16) + bh * 2, K / 16 - 2);
+      const int odd = (int)(reinterpret_cast<uintptr_t>(sp) & 2);
+      st.sc = *reinterpret_cast<const uint32_t*>(sp - odd) >> (8 * odd);
+    }
+  };
+  auto stage = [&](const Stage& st, int buf, int s) {
+    const bool kval = s * GK + ah * 32 < K;
+    uint4* ad = reinterpret_cast<uint4*>(&As[buf][ar * LROW + ah * 32]);
+#pragma unroll
+    for (int i = 0; i < 4; i++) ad[i] = kval ? st.a[i] : make_uint4(0, 0, 0, 0);
+    if (loads_b) {
+      const uint32_t sw = (bvalid && s * GK + bh * 32 < K) ? st.sc : 0u;
+      const float s0 = e4m3_to_f32<0>(sw), s1 = e4m3_to_f32<1>(sw);
+      bf16x8* bd = reinterpret_cast<bf16x8*>(&Bs[buf][bc * LROW + bh * 32]);
+      bd[0] = dequant8(st.c.x, s0);
+      bd[1] = dequant8(st.c.y, s0);
+      bd[2] = dequant8(st.c.z, s1);
+      bd[3] = dequant8(st.c.w, s1);
+    }
+  };
+
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave & 3, wn = wave >> 2;
+  const int r = lane & 15, q = lane >> 4;
+  // this wavefront's four 16-column blocks in the B tile; gate/up pairs the
+  // gate block cb with the up block cb + 2 (same units)
+  int bcol[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; cb++) bcol[cb] = GATEUP ? (cb >> 1) * UPW + 32 * wn + 16 * (cb & 1) : 64 * wn + 16 * cb;
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) {
+      bf16x8 fa[4], fb[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; rb++)
+        fa[rb] = *reinterpret_cast<const bf16x8*>(&As[buf][(64 * wm + 16 * rb + r) * LROW + 32 * ks + 8 * q]);
+#pragma unroll
+      for (int cb = 0; cb < 4; cb++)
+        fb[cb] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(bcol[cb] + r) * LROW + 32 * ks + 8 * q]);
+#pragma unroll
+      for (int rb = 0; rb < 4; rb++)
+#pragma unroll
+        for (int cb = 0; cb < 4; cb++) acc[rb][cb] = mfma16x16x32(fa[rb], fb[cb], acc[rb][cb]);
+    }
+  };
+
+  // two register stages in flight ahead of the LDS buffer being computed
+  Stage st0, st1;
+  gload(st0, 0);
+  gload(st1, 1);
+  stage(st0, 0, 0);
+  __syncthreads();
+  for (int s = 0; s < a.nk; s += 2) {
+    gload(st0, s + 2);
+    compute(0);
+    stage(st1, 1, s + 1);
+    __syncthreads();
+    if (s + 1 >= a.nk) break;
+    gload(st1, s + 3);
+    compute(1);
+    stage(st0, 0, s + 2);
+    __syncthreads();
+  }
+
+  // epilogue: D[i][j] of block (rb, cb) is in lane j + 16 (i / 4), element i % 4
+  cptr<float> glob = as_const(reinterpret_cast<const float*>(blob + a.off_globals));
+  const float g0 = resident ? glob[GATEUP ? 0 : 2] : 0.f;
+  const float g1 = (GATEUP && resident) ? glob[1] : 0.f;
+#pragma unroll
+  for (int rb = 0; rb < 4; rb++) {
+#pragma unroll
+    for (int e4 = 0; e4 < 4; e4++) {
+      const int row = 64 * wm + 16 * rb + 4 * q + e4;
+      if (row >= n) continue;
+      uint16_t* orow = out + (int64_t)(p0 + row) * units;
+      if (GATEUP) {
+#pragma unroll
+        for (int cb = 0; cb < 2; cb++) {
+          const int unit = u0 + 32 * wn + 16 * cb + r;
+          if (unit >= units) continue;
+          const float gv = g0 * acc[rb][cb][e4];
+          const float uv = g1 * acc[rb][cb + 2][e4];
+          orow[unit] = f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv);
+        }
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < 4; cb++) {
+          const int unit = u0 + 64 * wn + 16 * cb + r;
+          if (unit >= units) continue;
+          orow[unit] = f32_to_bf16_rne(g0 * acc[rb][cb][e4]);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_ffn_gemm(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
+                           uint16_t* y_rows, void* ws, int stages, hipEvent_t ev_start, hipEvent_t ev_stop,
+                           hipStream_t s) {
+  const WsLayout wl = ws_layout(d);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  GemmArgs a;
+  a.slot_stride = (uint32_t)g.slot_stride;
+  a.n_slots = (int32_t)g.n_slots;
+  for (int m = 0; m < 3; m++) {
+    a.off_codes[m] = (uint32_t)g.off_codes[m];
+    a.off_scales[m] = (uint32_t)g.off_scales[m];
+  }
+  a.off_globals = (uint32_t)g.off_globals;
+  a.H = d.H;
+  a.I = d.I;
+  a.k = d.k;
+  a.Tk = d.T * d.k;
+  const int4* chunks = reinterpret_cast<const int4*>(base + wl.off_chunks);
+  const int32_t* meta = reinterpret_cast<const int32_t*>(base + wl.off_meta);
+  for (int stage = 0; stage < 2; stage++) {
+    if (!((stages >> stage) & 1)) continue;
+    const bool gu = stage == 0;
+    const int K = gu ? d.H : d.I, units = gu ? d.I : d.H;
+    const int upw = GC / (gu ? 2 : 1);
+    a.n_ut = (units + upw - 1) / upw;
+    a.nk = (K + GK - 1) / GK;
+    const int64_t groups8 = (wl.max_chunks + 7) / 8;
+    const dim3 grid((unsigned)(groups8 * 8 * a.n_ut)), block(GT);
+    const bool first = gu || !(stages & 1), last = !gu || !(stages & 2);
+    hipEvent_t e0 = first ? ev_start : nullptr, e1 = last ? ev_stop : nullptr;
+    const uint16_t* ain = gu ? x : h;
+    uint16_t* out = gu ? h : y_rows;
+    if (e0 || e1) {
+      if (gu) hipExtLaunchKernelGGL(k_ffn_gemm<true>, grid, block, 0, s, e0, e1, 0, a, chunks, meta, perm, g.pool, ain, out);
+      else hipExtLaunchKernelGGL(k_ffn_gemm<false>, grid, block, 0, s, e0, e1, 0, a, chunks, meta, perm, g.pool, ain, out);
+    } else {
+      if (gu) hipLaunchKernelGGL(k_ffn_gemm<true>, grid, block, 0, s, a, chunks, meta, perm, g.pool, ain, out);
+      else hipLaunchKernelGGL(k_ffn_gemm<false>, grid, block, 0, s, a, chunks, meta, perm, g.pool, ain, out);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace moe

@@ -74,11 +74,13 @@ __device__ int block_exclusive_scan(int v, int* lds16, int* total) {
 // residency status and the FFN tile list; returns this expert's first row.
 // `slot` is slot_table[layer][e] for thread e < E and `ss` the shared expert's
 // slot; the caller loads both at its start, so their latency overlaps its own.
+// `chunks` (or null): the grouped-GEMM work list, written when the FFN will
+// run as a GEMM.
 __device__ int scan_and_tiles(int count, int T, int k, int E, int slot, int ss, int32_t n_slots,
                               int32_t* __restrict__ offsets, int32_t* __restrict__ group_slot,
                               int32_t* __restrict__ status, int32_t* __restrict__ meta, int4* __restrict__ tiles,
-                              int32_t* __restrict__ tile_tok, int32_t* __restrict__ tile_base, int* lds17,
-                              int* tbase_out = nullptr) {
+                              int32_t* __restrict__ tile_tok, int32_t* __restrict__ tile_base, int4* __restrict__ chunks,
+                              int* lds17, int* tbase_out = nullptr) {
   const int e = threadIdx.x;
   int total = 0;
   const int off = block_exclusive_scan(count, lds17, &total);
@@ -115,6 +117,18 @@ __device__ int scan_and_tiles(int count, int T, int k, int E, int slot, int ss, 
     tile_tok[(int64_t)(nt_total + tl) * kTileRows + r] = tl * kTileRows + (r < n ? r : 0);
   }
   if (threadIdx.x == 0) meta[0] = nt_total + nts;
+  if (chunks) {  // uniform: every thread of the block takes this branch or none does
+    const int nck = (count + kChunkRows - 1) / kChunkRows;
+    int nck_total = 0;
+    const int cbase = block_exclusive_scan(nck, lds17, &nck_total);
+    for (int i = 0; i < nck; i++)
+      chunks[cbase + i] = make_int4(e, off + i * kChunkRows, min(kChunkRows, count - i * kChunkRows), slot);
+    const int ncs = (T + kChunkRows - 1) / kChunkRows;
+    for (int i = threadIdx.x; i < ncs; i += blockDim.x)
+      chunks[nck_total + i] =
+          make_int4(E, (int32_t)(Tk + (int64_t)i * kChunkRows), min(kChunkRows, T - i * kChunkRows), ss);
+    if (threadIdx.x == 0) meta[1] = nck_total + ncs;
+  }
   return off;
 }
 
@@ -123,7 +137,8 @@ __global__ __launch_bounds__(1024) void k_scan(int64_t nb, int T, int k, int E, 
                                                int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
                                                int32_t* __restrict__ group_slot, int32_t* __restrict__ status,
                                                int32_t* __restrict__ meta, int4* __restrict__ tiles,
-                                               int32_t* __restrict__ tile_tok, int32_t* __restrict__ tile_base) {
+                                               int32_t* __restrict__ tile_tok, int32_t* __restrict__ tile_base,
+                                               int4* __restrict__ chunks) {
   __shared__ int lds[17];
   const int e = threadIdx.x;
   const int slot = e < E ? slot_table[(int64_t)layer * (E + 1) + e] : -1;
@@ -137,7 +152,7 @@ __global__ __launch_bounds__(1024) void k_scan(int64_t nb, int T, int k, int E, 
     }
   }
   scan_and_tiles(count, T, k, E, slot, ss, n_slots, offsets, group_slot, status, meta, tiles, tile_tok, tile_base,
-                 lds);
+                 chunks, lds);
 }
 
 // Token of routed row p (flat index f) into its tile's row table; the first
@@ -167,7 +182,7 @@ __global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict_
                                                       int32_t* __restrict__ group_slot, int32_t* __restrict__ status,
                                                       int32_t* __restrict__ meta, int4* __restrict__ tiles,
                                                       int32_t* __restrict__ tile_tok,
-                                                      int32_t* __restrict__ tile_base) {
+                                                      int32_t* __restrict__ tile_base, int4* __restrict__ chunks) {
   __shared__ int32_t hist[1024];
   __shared__ int32_t cntl[1024];
   __shared__ int32_t tbl[1024];
@@ -196,7 +211,7 @@ __global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict_
   int tb = 0;
   STAGE_STAMP(1, 2);
   const int off = scan_and_tiles(count, T, k, E, slot, ss, n_slots, offsets, group_slot, status, meta, tiles,
-                                 tile_tok, tile_base, lds, &tb);
+                                 tile_tok, tile_base, chunks, lds, &tb);
   STAGE_STAMP(1, 3);
   if (tid < E) {
     hist[tid] = off;  // hist now holds each expert's first row
@@ -275,14 +290,16 @@ hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, co
   int4* tiles = reinterpret_cast<int4*>(base + wl.off_tiles);
   int32_t* tile_tok = reinterpret_cast<int32_t*>(base + wl.off_tile_tok);
   int32_t* tile_base = reinterpret_cast<int32_t*>(base + wl.off_tile_base);
+  int4* chunks = use_gemm(d) ? reinterpret_cast<int4*>(base + wl.off_chunks) : nullptr;
   if (F <= kSmallF) {
     hipLaunchKernelGGL(k_group_small, dim3(1), dim3(1024), 0, s, ids, (int)F, d.T, d.k, d.E, layer, slot_table,
-                       n_slots, offsets, perm, inv_perm, group_slot, dev_status, meta, tiles, tile_tok, tile_base);
+                       n_slots, offsets, perm, inv_perm, group_slot, dev_status, meta, tiles, tile_tok, tile_base,
+                       chunks);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_count, dim3((unsigned)wl.nb), dim3(256), 0, s, ids, F, d.E, cnt, dev_status);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, wl.nb, d.T, d.k, d.E, layer, slot_table, n_slots, cnt,
-                     offsets, group_slot, dev_status, meta, tiles, tile_tok, tile_base);
+                     offsets, group_slot, dev_status, meta, tiles, tile_tok, tile_base, chunks);
   hipLaunchKernelGGL(k_scatter, dim3((unsigned)wl.nb), dim3(64), 0, s, ids, F, d.E, d.k, cnt, offsets, perm, inv_perm,
                      tile_tok, tile_base);
   return hipGetLastError();

@@ -14,17 +14,26 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Rows per FFN tile: the M extent of one v_mfma_f32_16x16x32_bf16.
 constexpr int kTileRows = 16;
+// Rows per grouped-GEMM chunk (the M extent of one GEMM workgroup).
+constexpr int kChunkRows = 256;
+// The expert FFN runs as a grouped GEMM over chunks when the groups average at
+// least this many rows (T k >= kGemmMinRows E); below that, the weight-streaming
+// kernel over 16-row tiles.  A host-side choice from the shapes alone.
+constexpr int kGemmMinRows = 16;
+inline bool use_gemm(const moe_dims& d) { return (int64_t)d.T * d.k >= (int64_t)kGemmMinRows * d.E; }
 
 // ---- workspace layout (shared by moe_group and moe_expert_ffn) --------------
 // cnt       int32 [nb][E]       per-256-row-block expert counts, then block prefixes
-// meta      int32 [64]          meta[0] = number of FFN tiles
+// meta      int32 [64]          meta[0] = number of FFN tiles, meta[1] = number of GEMM chunks
 // tiles     int4  [max_tiles]   {group, first row p0, rows n (<= 16), slot}
 // tile_tok  int32 [max_tiles][16] token of each tile row (rows >= n repeat row 0)
 // tile_base int32 [E]           first tile of each routed group
+// chunks    int4  [max_chunks]  {group, first row p0, rows n (<= 256), slot} (GEMM path only)
 struct WsLayout {
-  int64_t nb;         // blocks of 256 flat (token, slot) entries
-  int64_t max_tiles;  // upper bound on FFN tiles
-  uint64_t off_cnt, off_meta, off_tiles, off_tile_tok, off_tile_base, total;
+  int64_t nb;          // blocks of 256 flat (token, slot) entries
+  int64_t max_tiles;   // upper bound on FFN tiles
+  int64_t max_chunks;  // upper bound on GEMM chunks
+  uint64_t off_cnt, off_meta, off_tiles, off_tile_tok, off_tile_base, off_chunks, total;
 };
 
 inline uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
@@ -40,7 +49,9 @@ inline WsLayout ws_layout(const moe_dims& d) {
   w.off_tiles = w.off_meta + 256;
   w.off_tile_tok = align256(w.off_tiles + (uint64_t)w.max_tiles * 16);
   w.off_tile_base = align256(w.off_tile_tok + (uint64_t)w.max_tiles * 64);
-  w.total = align256(w.off_tile_base + (uint64_t)d.E * 4);
+  w.max_chunks = (F + kChunkRows - 1) / kChunkRows + routed_groups + (d.T + kChunkRows - 1) / kChunkRows + 1;
+  w.off_chunks = align256(w.off_tile_base + (uint64_t)d.E * 4);
+  w.total = align256(w.off_chunks + (uint64_t)w.max_chunks * 16);
   return w;
 }
 
@@ -133,14 +144,17 @@ hipError_t launch_topk(const moe_dims& d, const float* logits, const uint16_t* x
 hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, const int32_t* slot_table,
                         int32_t n_slots, int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
                         int32_t* dev_status, void* ws, hipStream_t s);
-hipError_t launch_ffn(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm,
-                      uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws, hipStream_t s);
 // stages: bit 1 = gate/up (writes h), bit 2 = down (reads h, writes y_rows)
 // ev_start / ev_stop (may be null): recorded at the start of the first launched
 // kernel and the end of the last one
 hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm,
                           uint16_t* h, uint16_t* y_rows, void* ws, int n_cu, int stages, hipEvent_t ev_start,
                           hipEvent_t ev_stop, hipStream_t s);
+// Grouped-GEMM expert FFN over the chunk list (prefill-sized groups); same
+// stage mask and events as launch_ffn_dec.
+hipError_t launch_ffn_gemm(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
+                           uint16_t* y_rows, void* ws, int stages, hipEvent_t ev_start, hipEvent_t ev_stop,
+                           hipStream_t s);
 hipError_t launch_combine(const moe_dims& d, const uint16_t* y_rows, const int32_t* inv_perm, const float* w,
                           const float* sigma, uint16_t* y, hipStream_t s);
 

@@ -1,8 +1,11 @@
 """GPU parity at sizes the oracle finishes in seconds (every output compared).
 
+Covers both FFN kernels: the weight-streaming kernel over 16-row tiles (groups
+averaging fewer than 16 rows) and the grouped GEMM over 256-row chunks (more).
 Covers the tiny workload, several FFN tiles with ragged tails, a reduction
 axis that is not a multiple of the 128-value step, reduction axes longer than
-4096 (several K rounds per wavefront), degenerate shapes (T = 1,
+4096 (several K rounds per wavefront), GEMM chunks with ragged K steps, column
+tiles and row chunks (a group split over two chunks), degenerate shapes (T = 1,
 E = k = 1, k = E, E = 1024), a non-resident slot, an out-of-range expert id,
 token-permutation invariance and run-to-run determinism."""
 import numpy as np
@@ -76,8 +79,8 @@ class Case:
 
 SMALL = {
     "tiny": CONFIGS[1],
-    "multitile_ragged": Config(31, "mt", T=100, H=512, I=256, E=8, k=2, L=1, router="matrix"),
-    "ragged_K_zipf": Config(32, "rk", T=37, H=96, I=160, E=6, k=3, L=1, router="zipf", zipf_s=1.0),
+    "multitile_ragged": Config(31, "mt", T=100, H=512, I=256, E=16, k=2, L=1, router="matrix"),
+    "ragged_K_zipf": Config(32, "rk", T=37, H=96, I=160, E=10, k=3, L=1, router="zipf", zipf_s=1.0),
     "degenerate_T1_E1": Config(33, "deg", T=1, H=64, I=32, E=1, k=1, L=1, router="matrix"),
     "k_equals_E": Config(34, "kE", T=5, H=128, I=64, E=6, k=6, L=1, router="zipf", zipf_s=0.5),
     "E1024_max": Config(35, "E1024", T=3, H=64, I=64, E=1024, k=8, L=1, router="zipf", zipf_s=1.0),
@@ -85,6 +88,12 @@ SMALL = {
     # K beyond 4096 on both stages: each wavefront covers its share of K in
     # several rounds, the last one ragged
     "long_K_rounds": Config(37, "lk", T=6, H=4608, I=4352, E=4, k=2, L=1, router="matrix"),
+    # grouped-GEMM path: K steps of 64 with a half step at the end (544, 224),
+    # column tiles that overhang (224 of 64, 544 of 128), the shared group split
+    # over two 256-row chunks
+    "gemm_ragged": Config(38, "gr", T=300, H=544, I=224, E=4, k=2, L=1, router="matrix"),
+    # GEMM path under Zipf routing: one group above 256 rows, many small ones
+    "gemm_zipf_split": Config(39, "gz", T=256, H=256, I=128, E=16, k=4, L=1, router="zipf", zipf_s=1.2),
 }
 
 
@@ -117,9 +126,10 @@ def test_ffn_stages_split_matches_whole(B, hostgen):
     assert torch.equal(b.y_rows.view(torch.int16), y_ref.view(torch.int16))
 
 
-def test_non_resident_slot_gives_zero_rows_and_status(B, hostgen):
-    cfg = CONFIGS[1]
-    say("[gpu] non-resident slot case")
+@pytest.mark.parametrize("cname", ["tiny", "gemm_ragged"])
+def test_non_resident_slot_gives_zero_rows_and_status(B, hostgen, cname):
+    cfg = CONFIGS[1] if cname == "tiny" else SMALL[cname]
+    say("[gpu] non-resident slot case (%s)" % cname)
     probe = Case(B, cfg, hostgen)
     probe.run(B)
     ids = probe.buf.ids.cpu().numpy()
@@ -171,9 +181,10 @@ def test_bad_expert_id_is_dropped_and_flagged(B, hostgen):
     assert_close(bf16_to_f64(buf.y), y_ref, "y with a dropped id")
 
 
-def test_token_permutation_bit_exact_on_gpu(B, hostgen):
-    cfg = SMALL["multitile_ragged"]
-    say("[gpu] token permutation case")
+@pytest.mark.parametrize("cname", ["multitile_ragged", "gemm_ragged"])
+def test_token_permutation_bit_exact_on_gpu(B, hostgen, cname):
+    cfg = SMALL[cname]
+    say("[gpu] token permutation case (%s)" % cname)
     a = Case(B, cfg, hostgen)
     a.run(B)
     pi = np.random.default_rng(7).permutation(cfg.T)
@@ -186,9 +197,10 @@ def test_token_permutation_bit_exact_on_gpu(B, hostgen):
     assert torch.equal(b.buf.y.view(torch.int16), a.buf.y.view(torch.int16)[pi_t])
 
 
-def test_run_to_run_determinism(B, hostgen):
-    cfg = SMALL["multitile_ragged"]
-    say("[gpu] determinism case")
+@pytest.mark.parametrize("cname", ["multitile_ragged", "gemm_ragged"])
+def test_run_to_run_determinism(B, hostgen, cname):
+    cfg = SMALL[cname]
+    say("[gpu] determinism case (%s)" % cname)
     a = Case(B, cfg, hostgen)
     a.run(B)
     first = [t.clone() for t in (a.buf.ids, a.buf.perm, a.buf.h.view(torch.int16), a.buf.y.view(torch.int16))]
