@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="decode48",
-                    help="tiny | decode48 | decode43x64 | prefill8192 (default decode48)")
+                    help="tiny | decode48 | decode43x64 | prefill8192 | streamed4x4096 (default decode48)")
     ap.add_argument("--eager", action="store_true", help="launch every call eagerly instead of HIP graphs")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -267,7 +267,7 @@ def cpu_baseline(cfg, seconds):
             wsg = gen.w_shared_gate(cfg, l)
             wr = gen.w_router(cfg, l) if cfg.router == "matrix" else None
             lgz = None if wr is not None else zipf_logits(cfg, l, 0)
-            ntok = 16
+            ntok = 16 if cfg.H * cfg.I <= 2048 * 512 else 4
             blob_cache = {}
 
             def blob(e):
@@ -285,6 +285,112 @@ def cpu_baseline(cfg, seconds):
             sample = "layer 0, routing and grouping of all %d tokens plus expert FFN and combine of %d sampled " \
                      "tokens; oracle time %.1f s; rate = sampled tokens / time" % (cfg.T, ntok, t_oracle)
     return {"value": value, "unit": "tokens/s", "cores": 1, "kind": "oracle", "sample": sample}
+
+
+def run_staged(cfg, args, B, DevGen):
+    """The streamed workload: every layer's expert blobs sit in page-locked host
+    memory and go through the two-slot device ring (copy stream) while the
+    previous layer computes (compute stream).  A step is the whole L-layer
+    stack.  Reports tokens/s, the H2D rate and the overlap fraction
+    sum_l |compute_l n copy_(l+1)| / sum_l compute_l, beside the FFN roofline
+    measured on a staged slot."""
+    import torch
+    from moe_expert_ffn_top_amd.staged import StagedLayers
+
+    K, W = args.steps, args.warmup
+    wl = Workload(cfg, 1, B, DevGen)
+    log("copying %.2f GB of blobs to page-locked host memory" % (wl.pool_bytes / 1e9))
+    host = torch.empty(wl.pool_bytes, dtype=torch.uint8, pin_memory=True)
+    host.copy_(wl.pool)
+    torch.cuda.synchronize()
+    del wl.pool
+    torch.cuda.empty_cache()
+    copy_s, comp_s = torch.cuda.Stream(), torch.cuda.Stream()
+    st = StagedLayers(wl.dims, wl.layout, host, cfg.L, copy_s, comp_s)
+
+    def step(events=None):
+        with torch.cuda.stream(comp_s):
+            st.run(lambda l: wl.x[0, l], lambda l: wl.wsg[l], lambda l: wl.logits[0, l], layer_events=events)
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    assert int(st.buf.status.item()) == 0, "device status after warmup"
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / K
+    tokens_per_s = cfg.T / (ms_per_step / 1e3)
+    log("%.2f ms/step, %.1f tokens/s" % (ms_per_step, tokens_per_s))
+
+    # copy and compute intervals of one more step, on a common time base
+    ev = []
+    step(ev)
+    torch.cuda.synchronize()
+    ref = ev[0][0]
+    iv = [tuple(ref.elapsed_time(e) for e in quad) for quad in ev]   # (copy0, copy1, comp0, comp1) per layer
+    layer_gb = st.layer_bytes / 1e9
+    copy_ms = np.array([c1 - c0 for c0, c1, _, _ in iv])
+    comp_ms = np.array([k1 - k0 for _, _, k0, k1 in iv])
+    inter = sum(max(0.0, min(iv[l][3], iv[l + 1][1]) - max(iv[l][2], iv[l + 1][0])) for l in range(len(iv) - 1))
+    overlap = inter / max(1e-9, comp_ms[:-1].sum()) if len(iv) > 1 else 0.0
+    h2d = {"layer_bytes": st.layer_bytes, "gb_per_s": float(layer_gb / (copy_ms.mean() * 1e-3)),
+           "copy_ms_per_layer": float(copy_ms.mean()), "compute_ms_per_layer": float(comp_ms.mean()),
+           "overlap_fraction": float(overlap)}
+    log("h2d: %s" % h2d)
+
+    # FFN roofline on a staged slot: stage layer 0, group it, time the two stages
+    hev = HipEvents()
+    d, buf = wl.dims, st.buf
+    gu_ms, dn_ms, offs = [], [], []
+    with torch.cuda.stream(comp_s):
+        slot = B.moe_stage_h2d(st.ring, host.data_ptr(), st.layer_bytes)
+        B.moe_ring_acquire(st.ring, slot, comp_s)
+        pool = st.slots[slot]
+        x = wl.x[0, 0]
+        for rep in range(3):
+            B.moe_route(d, x, None, wl.logits[0, 0], wl.wsg[0], None, buf.ids, buf.w, buf.sigma, comp_s)
+            B.moe_group(d, 0, buf.ids, st.slot_table, cfg.E1, buf.offsets, buf.perm, buf.inv_perm, buf.group_slot,
+                        buf.status, buf.ws, stream=comp_s)
+            e = [hev.new() for _ in range(4)]
+            for stg in (1, 2):
+                B.moe_expert_ffn_stages(d, x, pool, st.layer_bytes, wl.layout, buf.offsets, buf.perm,
+                                        buf.group_slot, buf.h, buf.y_rows, buf.status, buf.ws, stg, e[2 * stg - 2],
+                                        e[2 * stg - 1], stream=comp_s)
+            offs.append(buf.offsets.clone())
+            comp_s.synchronize()
+            gu_ms.append(hev.elapsed_ms(e[0], e[1]))
+            dn_ms.append(hev.elapsed_ms(e[2], e[3]))
+        B.moe_ring_release(st.ring, slot, comp_s)
+    torch.cuda.synchronize()
+    hev.close()
+    st.close()
+    gu_ms, dn_ms = np.array(gu_ms), np.array(dn_ms)
+    gu_b, dn_b, gu_f, dn_f = expert_work(cfg, offs)
+    achieved = float(gu_f.mean() / (gu_ms.mean() * 1e-3) / 1e12)
+    roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+            "kernel": "%s gate/up (moe_expert_ffn_stages, stages=1) on a staged slot" % ffn_kernel(cfg)[0],
+            "launch_us": float(gu_ms.mean() * 1e3), "flops_per_launch": float(gu_f.mean()),
+            "down": {"launch_us": float(dn_ms.mean() * 1e3), "flops_per_launch": float(dn_f.mean()),
+                     "achieved": float(dn_f.mean() / (dn_ms.mean() * 1e-3) / 1e12)},
+            "kernel_source_sha256_16": kernel_source_hash(cfg)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(cfg, args.cpu_baseline_seconds)
+    line = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded; random block-FP4 weights, bf16 activations)",
+        "config": {"workload": cfg.name, "T": cfg.T, "layers": cfg.L, "H": cfg.H, "I": cfg.I, "E": cfg.E,
+                   "k": cfg.k, "shared_experts": 1, "routing": "zipf s=%g" % cfg.zipf_s,
+                   "staging": "pinned host blobs through a two-slot device ring", "graphs": False,
+                   "parallelism": "single GPU"},
+        "roofline": roof, "h2d": h2d, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def main():
@@ -311,8 +417,8 @@ def main():
 
     cfg = config_by_name(args.config)
     if cfg.staged:
-        print("workload %s (staged ring) is not wired into bench.py yet" % cfg.name, file=sys.stderr)
-        sys.exit(2)
+        run_staged(cfg, args, B, DevGen)
+        return
     K, W = args.steps, args.warmup
     wl = Workload(cfg, W + K, B, DevGen)
     stream = torch.cuda.current_stream()
