@@ -190,12 +190,12 @@ class Workload:
         d, buf = self.dims, self.buf
         for l in range(self.cfg.L):
             x = self.x[s, l]
-            if self.wr is not None:
-                B.moe_route(d, x, self.wr[l], None, self.wsg[l], buf.logits, buf.ids, buf.w, buf.sigma, stream)
-            else:
-                B.moe_route(d, x, None, self.logits[s, l], self.wsg[l], None, buf.ids, buf.w, buf.sigma, stream)
-            B.moe_group(d, l, buf.ids, self.slot_table, self.n_slots, buf.offsets, buf.perm, buf.inv_perm,
-                        buf.group_slot, buf.status, buf.ws, stream=stream)
+            wr = self.wr[l] if self.wr is not None else None
+            lg_in = None if self.wr is not None else self.logits[s, l]
+            lg_out = buf.logits if self.wr is not None else None
+            B.moe_route_group(d, l, x, wr, lg_in, self.wsg[l], lg_out, buf.ids, buf.w, buf.sigma, self.slot_table,
+                              self.n_slots, buf.offsets, buf.perm, buf.inv_perm, buf.group_slot, buf.status, buf.ws,
+                              stream=stream)
             if ffn_events is None:
                 B.moe_expert_ffn(d, x, self.pool, self.pool_bytes, self.layout, buf.offsets, buf.perm,
                                  buf.group_slot, buf.h, buf.y_rows, buf.status, buf.ws, stream=stream)

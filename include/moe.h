@@ -183,6 +183,22 @@ int moe_group(const moe_dims* d, int32_t layer, const int32_t* topk_ids,
               int32_t* dev_status, void* ws, uint64_t ws_bytes,
               moe_stream_t stream);
 
+/* ---- S1 + S2 + S3 together ---------------------------------------------
+ * moe_route followed by moe_group on the same stream, with exactly their
+ * arguments, validation and results (every output bit-identical).  For small
+ * windows (T <= 16, T*k <= 256) the top-k and the grouping run in one kernel
+ * (after the router GEMM when w_router is given), which saves a launch and the
+ * ids' round trip through memory; otherwise the two calls' kernels are
+ * launched in turn. */
+int moe_route_group(const moe_dims* d, int32_t layer, const uint16_t* x,
+                    const float* w_router, const float* logits_in,
+                    const float* w_shared_gate, float* logits_out,
+                    int32_t* topk_ids, float* topk_w, float* shared_sigma,
+                    const int32_t* slot_table, int32_t n_slots, int32_t* offsets,
+                    int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
+                    int32_t* dev_status, void* ws, uint64_t ws_bytes,
+                    moe_stream_t stream);
+
 /* ---- S4: expert FFNs ---------------------------------------------------
  * [Strata] "路由以后，专家怎样分工？" and "CPU 怎样把剩下的专家算完？" (gate/up,
  * activation, the intermediate re-encoded for the next kernel, down).

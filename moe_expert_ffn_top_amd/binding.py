@@ -33,8 +33,9 @@ MOE_DEV_BAD_SLOT = 4
 
 #: every symbol include/moe.h declares
 EXPORTED = ("moe_status_string", "moe_last_error", "moe_version", "moe_blob_layout_init", "moe_workspace_bytes",
-            "moe_route", "moe_group", "moe_expert_ffn", "moe_expert_ffn_stages", "moe_combine", "moe_ring_create",
-            "moe_stage_h2d", "moe_ring_acquire", "moe_ring_release", "moe_ring_slot_ptr", "moe_ring_destroy")
+            "moe_route", "moe_group", "moe_route_group", "moe_expert_ffn", "moe_expert_ffn_stages", "moe_combine",
+            "moe_ring_create", "moe_stage_h2d", "moe_ring_acquire", "moe_ring_release", "moe_ring_slot_ptr",
+            "moe_ring_destroy")
 
 
 class Dims(ctypes.Structure):
@@ -72,6 +73,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.moe_workspace_bytes.argtypes = [_DP, ctypes.POINTER(_u64)]
     lib.moe_route.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.moe_group.argtypes = [_DP, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _u64, _vp]
+    lib.moe_route_group.argtypes = [_DP, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
+                                    _vp, _vp, _u64, _vp]
     lib.moe_expert_ffn.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _u64, _vp]
     lib.moe_expert_ffn_stages.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _vp,
@@ -152,6 +155,17 @@ def moe_group(dims, layer, topk_ids, slot_table, n_slots, offsets, perm, inv_per
         ws_bytes = ws.numel() * ws.element_size()
     _check(_lib.moe_group(ctypes.byref(dims), layer, _p(topk_ids), _p(slot_table), n_slots, _p(offsets), _p(perm),
                           _p(inv_perm), _p(group_slot), _p(dev_status), _p(ws), ws_bytes, _s(stream)), "moe_group")
+
+
+def moe_route_group(dims, layer, x, w_router, logits_in, w_shared_gate, logits_out, topk_ids, topk_w, shared_sigma,
+                    slot_table, n_slots, offsets, perm, inv_perm, group_slot, dev_status, ws,
+                    ws_bytes: Optional[int] = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.moe_route_group(ctypes.byref(dims), layer, _p(x), _p(w_router), _p(logits_in), _p(w_shared_gate),
+                                _p(logits_out), _p(topk_ids), _p(topk_w), _p(shared_sigma), _p(slot_table), n_slots,
+                                _p(offsets), _p(perm), _p(inv_perm), _p(group_slot), _p(dev_status), _p(ws),
+                                ws_bytes, _s(stream)), "moe_route_group")
 
 
 def moe_expert_ffn(dims, x, pool, pool_bytes, layout: BlobLayout, offsets, perm, group_slot, h, y_rows, dev_status,

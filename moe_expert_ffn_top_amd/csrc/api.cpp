@@ -123,9 +123,11 @@ int moe_workspace_bytes(const moe_dims* d, uint64_t* out_bytes) {
   return ok();
 }
 
-int moe_route(const moe_dims* d, const uint16_t* x, const float* w_router, const float* logits_in,
-              const float* w_shared_gate, float* logits_out, int32_t* topk_ids, float* topk_w, float* shared_sigma,
-              moe_stream_t stream) {
+namespace {
+
+int validate_route(const moe_dims* d, const uint16_t* x, const float* w_router, const float* logits_in,
+                   const float* w_shared_gate, float* logits_out, int32_t* topk_ids, float* topk_w,
+                   float* shared_sigma) {
   int r = check_dims(d);
   if (r) return r;
   if ((w_router == nullptr) == (logits_in == nullptr))
@@ -139,23 +141,12 @@ int moe_route(const moe_dims* d, const uint16_t* x, const float* w_router, const
   if (w_router) REQUIRE(w_router, 16, "w_router");
   if (logits_in) REQUIRE(logits_in, 4, "logits_in");
   if (logits_out) REQUIRE(logits_out, 4, "logits_out");
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const float* lg = logits_in;
-  if (w_router) {
-    hipError_t e = moe::launch_router_matrix(*d, x, w_router, logits_out, s);
-    if (e != hipSuccess) return hip_status(e, "router logits launch");
-    lg = logits_out;
-  } else if (logits_out && logits_out != logits_in) {
-    hipError_t e = hipMemcpyAsync(logits_out, logits_in, (size_t)d->T * d->E * sizeof(float),
-                                  hipMemcpyDeviceToDevice, s);
-    if (e != hipSuccess) return hip_status(e, "logits copy");
-  }
-  return hip_status(moe::launch_topk(*d, lg, x, w_shared_gate, topk_ids, topk_w, shared_sigma, s), "top-k launch");
+  return MOE_OK;
 }
 
-int moe_group(const moe_dims* d, int32_t layer, const int32_t* topk_ids, const int32_t* slot_table, int32_t n_slots,
-              int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* group_slot, int32_t* dev_status, void* ws,
-              uint64_t ws_bytes, moe_stream_t stream) {
+int validate_group(const moe_dims* d, int32_t layer, const int32_t* topk_ids, const int32_t* slot_table,
+                   int32_t n_slots, int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
+                   int32_t* dev_status, void* ws, uint64_t ws_bytes) {
   int r = check_dims(d);
   if (r) return r;
   if (layer < 0 || layer >= d->L) return fail(MOE_ERR_ARG, "layer = %d outside [0, L = %d)", layer, d->L);
@@ -172,8 +163,71 @@ int moe_group(const moe_dims* d, int32_t layer, const int32_t* topk_ids, const i
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace %llu bytes < required %llu", (unsigned long long)ws_bytes,
                 (unsigned long long)need);
+  return MOE_OK;
+}
+
+// The logits copy (logits_in -> logits_out) and, with w_router, the logits GEMM.
+int route_logits(const moe_dims* d, const uint16_t* x, const float* w_router, const float* logits_in,
+                 float* logits_out, hipStream_t s, const float** lg) {
+  *lg = logits_in;
+  if (w_router) {
+    hipError_t e = moe::launch_router_matrix(*d, x, w_router, logits_out, s);
+    if (e != hipSuccess) return hip_status(e, "router logits launch");
+    *lg = logits_out;
+  } else if (logits_out && logits_out != logits_in) {
+    hipError_t e = hipMemcpyAsync(logits_out, logits_in, (size_t)d->T * d->E * sizeof(float),
+                                  hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_status(e, "logits copy");
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+int moe_route(const moe_dims* d, const uint16_t* x, const float* w_router, const float* logits_in,
+              const float* w_shared_gate, float* logits_out, int32_t* topk_ids, float* topk_w, float* shared_sigma,
+              moe_stream_t stream) {
+  int r = validate_route(d, x, w_router, logits_in, w_shared_gate, logits_out, topk_ids, topk_w, shared_sigma);
+  if (r) return r;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const float* lg = nullptr;
+  if ((r = route_logits(d, x, w_router, logits_in, logits_out, s, &lg))) return r;
+  return hip_status(moe::launch_topk(*d, lg, x, w_shared_gate, topk_ids, topk_w, shared_sigma, s), "top-k launch");
+}
+
+int moe_group(const moe_dims* d, int32_t layer, const int32_t* topk_ids, const int32_t* slot_table, int32_t n_slots,
+              int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* group_slot, int32_t* dev_status, void* ws,
+              uint64_t ws_bytes, moe_stream_t stream) {
+  int r = validate_group(d, layer, topk_ids, slot_table, n_slots, offsets, perm, inv_perm, group_slot, dev_status, ws,
+                         ws_bytes);
+  if (r) return r;
   return hip_status(moe::launch_group(*d, layer, topk_ids, slot_table, n_slots, offsets, perm, inv_perm, group_slot,
                                       dev_status, ws, reinterpret_cast<hipStream_t>(stream)),
+                    "group launch");
+}
+
+int moe_route_group(const moe_dims* d, int32_t layer, const uint16_t* x, const float* w_router,
+                    const float* logits_in, const float* w_shared_gate, float* logits_out, int32_t* topk_ids,
+                    float* topk_w, float* shared_sigma, const int32_t* slot_table, int32_t n_slots,
+                    int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* group_slot, int32_t* dev_status,
+                    void* ws, uint64_t ws_bytes, moe_stream_t stream) {
+  int r = validate_route(d, x, w_router, logits_in, w_shared_gate, logits_out, topk_ids, topk_w, shared_sigma);
+  if (r) return r;
+  if ((r = validate_group(d, layer, topk_ids, slot_table, n_slots, offsets, perm, inv_perm, group_slot, dev_status,
+                          ws, ws_bytes)))
+    return r;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const float* lg = nullptr;
+  if ((r = route_logits(d, x, w_router, logits_in, logits_out, s, &lg))) return r;
+  if (moe::route_group_fusable(*d))
+    return hip_status(moe::launch_route_group(*d, layer, lg, x, w_shared_gate, slot_table, n_slots, topk_ids, topk_w,
+                                              shared_sigma, offsets, perm, inv_perm, group_slot, dev_status, ws, s),
+                      "route + group launch");
+  if ((r = hip_status(moe::launch_topk(*d, lg, x, w_shared_gate, topk_ids, topk_w, shared_sigma, s),
+                      "top-k launch")))
+    return r;
+  return hip_status(moe::launch_group(*d, layer, topk_ids, slot_table, n_slots, offsets, perm, inv_perm, group_slot,
+                                      dev_status, ws, s),
                     "group launch");
 }
 

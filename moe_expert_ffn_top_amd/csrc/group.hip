@@ -17,6 +17,7 @@
 //           inside a chunk, ballots give each entry its rank among equal ids,
 //           so a row's position depends only on the ids (deterministic).
 #include "moe_common.hpp"
+#include "topk_wave.hpp"
 
 namespace moe {
 #ifdef MOE_STAGE_TIMING
@@ -175,35 +176,17 @@ __device__ inline void note_tile_row(int32_t* __restrict__ tile_tok, const int32
 // counted directly over the ids staged in LDS.
 constexpr int kSmallF = 256;
 
-__global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict__ ids, int F, int T, int k, int E,
-                                                      int layer, const int32_t* __restrict__ slot_table,
-                                                      int32_t n_slots, int32_t* __restrict__ offsets,
-                                                      int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
-                                                      int32_t* __restrict__ group_slot, int32_t* __restrict__ status,
-                                                      int32_t* __restrict__ meta, int4* __restrict__ tiles,
-                                                      int32_t* __restrict__ tile_tok,
-                                                      int32_t* __restrict__ tile_base, int4* __restrict__ chunks) {
-  __shared__ int32_t hist[1024];
-  __shared__ int32_t cntl[1024];
-  __shared__ int32_t tbl[1024];
-  __shared__ __align__(16) int32_t sid[kSmallF];
-  __shared__ int lds[17];
+// The grouping of F <= kSmallF entries by one 1024-thread block, once every
+// thread's entry e_mine (-1 for none) is staged in sid[] (LDS, entries F..255
+// hold -1) and hist[0..E) is zero: counts, offsets, tiles, ranks, perm.
+__device__ inline void group_small_tail(int e_mine, int F, int T, int k, int E, int slot, int ss, int32_t n_slots,
+                                        int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                                        int32_t* __restrict__ inv_perm, int32_t* __restrict__ group_slot,
+                                        int32_t* __restrict__ status, int32_t* __restrict__ meta,
+                                        int4* __restrict__ tiles, int32_t* __restrict__ tile_tok,
+                                        int32_t* __restrict__ tile_base, int4* __restrict__ chunks, int32_t* hist,
+                                        int32_t* cntl, int32_t* tbl, const int32_t* sid, int* lds) {
   const int tid = threadIdx.x;
-  STAGE_STAMP(1, 0);
-  const int slot = tid < E ? slot_table[(int64_t)layer * (E + 1) + tid] : -1;
-  const int ss = slot_table[(int64_t)layer * (E + 1) + E];
-  if (tid < E) hist[tid] = 0;
-  int e_mine = -1;
-  if (tid < F) {
-    e_mine = ids[tid];
-    if (e_mine < 0 || e_mine >= E) {
-      atomicOr(status, MOE_DEV_BAD_EXPERT_ID);
-      e_mine = -1;
-    }
-  }
-  if (tid < kSmallF) sid[tid] = e_mine;  // -1 beyond F and for bad ids
-  __syncthreads();
-  STAGE_STAMP(1, 1);
   if (e_mine >= 0) atomicAdd(&hist[e_mine], 1);
   __syncthreads();
   const int count = tid < E ? hist[tid] : 0;
@@ -241,6 +224,75 @@ __global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict_
     }
   }
   STAGE_STAMP(1, 5);
+}
+
+// Whole grouping in one 1024-thread block for F = T*k <= kSmallF entries: the
+// rank of an entry is the number of earlier entries with the same expert,
+// counted directly over the ids staged in LDS.
+__global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict__ ids, int F, int T, int k, int E,
+                                                      int layer, const int32_t* __restrict__ slot_table,
+                                                      int32_t n_slots, int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+                                                      int32_t* __restrict__ group_slot, int32_t* __restrict__ status,
+                                                      int32_t* __restrict__ meta, int4* __restrict__ tiles,
+                                                      int32_t* __restrict__ tile_tok,
+                                                      int32_t* __restrict__ tile_base, int4* __restrict__ chunks) {
+  __shared__ int32_t hist[1024];
+  __shared__ int32_t cntl[1024];
+  __shared__ int32_t tbl[1024];
+  __shared__ __align__(16) int32_t sid[kSmallF];
+  __shared__ int lds[17];
+  const int tid = threadIdx.x;
+  STAGE_STAMP(1, 0);
+  const int slot = tid < E ? slot_table[(int64_t)layer * (E + 1) + tid] : -1;
+  const int ss = slot_table[(int64_t)layer * (E + 1) + E];
+  if (tid < E) hist[tid] = 0;
+  int e_mine = -1;
+  if (tid < F) {
+    e_mine = ids[tid];
+    if (e_mine < 0 || e_mine >= E) {
+      atomicOr(status, MOE_DEV_BAD_EXPERT_ID);
+      e_mine = -1;
+    }
+  }
+  if (tid < kSmallF) sid[tid] = e_mine;  // -1 beyond F and for bad ids
+  __syncthreads();
+  STAGE_STAMP(1, 1);
+  group_small_tail(e_mine, F, T, k, E, slot, ss, n_slots, offsets, perm, inv_perm, group_slot, status, meta, tiles,
+                   tile_tok, tile_base, chunks, hist, cntl, tbl, sid, lds);
+}
+
+// Route and group fused for small windows (T <= 16 tokens, T*k <= kSmallF,
+// drawn logits): wavefront t < T selects token t's experts straight into the
+// LDS id table; after one barrier the block groups them.  Saves a launch and the
+// round trip of the ids through memory; the slot-table loads overlap the top-k.
+template <int NPL>
+__global__ __launch_bounds__(1024) void k_route_group_small(
+    const float* __restrict__ logits, const uint16_t* __restrict__ x, const float* __restrict__ w_sg, int T, int H,
+    int E, int k, int layer, const int32_t* __restrict__ slot_table, int32_t n_slots, int32_t* __restrict__ ids,
+    float* __restrict__ wout, float* __restrict__ sigma, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv_perm, int32_t* __restrict__ group_slot, int32_t* __restrict__ status,
+    int32_t* __restrict__ meta, int4* __restrict__ tiles, int32_t* __restrict__ tile_tok,
+    int32_t* __restrict__ tile_base, int4* __restrict__ chunks) {
+  __shared__ int32_t hist[1024];
+  __shared__ int32_t cntl[1024];
+  __shared__ int32_t tbl[1024];
+  __shared__ __align__(16) int32_t sid[kSmallF];
+  __shared__ uint32_t wink[kSmallF];
+  __shared__ int lds[17];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int F = T * k;
+  STAGE_STAMP(1, 0);
+  const int slot = tid < E ? slot_table[(int64_t)layer * (E + 1) + tid] : -1;
+  const int ss = slot_table[(int64_t)layer * (E + 1) + E];
+  if (tid < E) hist[tid] = 0;
+  if (tid >= F && tid < kSmallF) sid[tid] = -1;
+  if (wave < T) topk_wave<NPL>(logits, x, w_sg, wave, H, E, k, ids, wout, sigma, wink + wave * k, sid + wave * k);
+  __syncthreads();
+  STAGE_STAMP(1, 1);
+  const int e_mine = tid < F ? sid[tid] : -1;
+  group_small_tail(e_mine, F, T, k, E, slot, ss, n_slots, offsets, perm, inv_perm, group_slot, status, meta, tiles,
+                   tile_tok, tile_base, chunks, hist, cntl, tbl, sid, lds);
 }
 
 __global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ ids, int64_t F, int E, int k,
@@ -302,6 +354,34 @@ hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, co
                      offsets, group_slot, dev_status, meta, tiles, tile_tok, tile_base, chunks);
   hipLaunchKernelGGL(k_scatter, dim3((unsigned)wl.nb), dim3(64), 0, s, ids, F, d.E, d.k, cnt, offsets, perm, inv_perm,
                      tile_tok, tile_base);
+  return hipGetLastError();
+}
+
+bool route_group_fusable(const moe_dims& d) { return d.T <= 16 && (int64_t)d.T * d.k <= kSmallF; }
+
+hipError_t launch_route_group(const moe_dims& d, int32_t layer, const float* logits, const uint16_t* x,
+                              const float* w_sg, const int32_t* slot_table, int32_t n_slots, int32_t* ids, float* w,
+                              float* sigma, int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
+                              int32_t* dev_status, void* ws, hipStream_t s) {
+  const WsLayout wl = ws_layout(d);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  int32_t* meta = reinterpret_cast<int32_t*>(base + wl.off_meta);
+  int4* tiles = reinterpret_cast<int4*>(base + wl.off_tiles);
+  int32_t* tile_tok = reinterpret_cast<int32_t*>(base + wl.off_tile_tok);
+  int32_t* tile_base = reinterpret_cast<int32_t*>(base + wl.off_tile_base);
+  int4* chunks = use_gemm(d) ? reinterpret_cast<int4*>(base + wl.off_chunks) : nullptr;
+  const int npl = (d.E + 63) / 64;
+  const dim3 g(1), b(1024);
+#define MOE_RG_LAUNCH(N)                                                                                        \
+  hipLaunchKernelGGL(k_route_group_small<N>, g, b, 0, s, logits, x, w_sg, d.T, d.H, d.E, d.k, layer, slot_table, \
+                     n_slots, ids, w, sigma, offsets, perm, inv_perm, group_slot, dev_status, meta, tiles, tile_tok, \
+                     tile_base, chunks)
+  if (npl <= 1) MOE_RG_LAUNCH(1);
+  else if (npl <= 2) MOE_RG_LAUNCH(2);
+  else if (npl <= 4) MOE_RG_LAUNCH(4);
+  else if (npl <= 8) MOE_RG_LAUNCH(8);
+  else MOE_RG_LAUNCH(16);
+#undef MOE_RG_LAUNCH
   return hipGetLastError();
 }
 

@@ -144,6 +144,12 @@ hipError_t launch_topk(const moe_dims& d, const float* logits, const uint16_t* x
 hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, const int32_t* slot_table,
                         int32_t n_slots, int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
                         int32_t* dev_status, void* ws, hipStream_t s);
+// Route + group in one kernel (drawn logits, T <= 16, T*k <= 256).
+bool route_group_fusable(const moe_dims& d);
+hipError_t launch_route_group(const moe_dims& d, int32_t layer, const float* logits, const uint16_t* x,
+                              const float* w_sg, const int32_t* slot_table, int32_t n_slots, int32_t* ids, float* w,
+                              float* sigma, int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
+                              int32_t* dev_status, void* ws, hipStream_t s);
 // stages: bit 1 = gate/up (writes h), bit 2 = down (reads h, writes y_rows)
 // ev_start / ev_stop (may be null): recorded at the start of the first launched
 // kernel and the end of the last one

@@ -47,15 +47,22 @@ class LayerBuffers:
 
 def run_layer(buf: LayerBuffers, layer: int, x: torch.Tensor, pool, pool_bytes: int, layout: B.BlobLayout,
               slot_table: torch.Tensor, n_slots: int, w_shared_gate: torch.Tensor,
-              w_router: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Enqueue one layer on `stream` (default: torch's current stream)."""
+              w_router: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None, stream=None,
+              fused: bool = True) -> None:
+    """Enqueue one layer on `stream` (default: torch's current stream).
+    fused: route and group through moe_route_group (else moe_route then
+    moe_group; the results are bit-identical)."""
     d = buf.dims
-    if w_router is not None:
-        B.moe_route(d, x, w_router, None, w_shared_gate, buf.logits, buf.ids, buf.w, buf.sigma, stream)
+    lg_out = buf.logits if w_router is not None else None
+    lg_in = None if w_router is not None else logits
+    if fused:
+        B.moe_route_group(d, layer, x, w_router, lg_in, w_shared_gate, lg_out, buf.ids, buf.w, buf.sigma, slot_table,
+                          n_slots, buf.offsets, buf.perm, buf.inv_perm, buf.group_slot, buf.status, buf.ws,
+                          stream=stream)
     else:
-        B.moe_route(d, x, None, logits, w_shared_gate, None, buf.ids, buf.w, buf.sigma, stream)
-    B.moe_group(d, layer, buf.ids, slot_table, n_slots, buf.offsets, buf.perm, buf.inv_perm, buf.group_slot,
-                buf.status, buf.ws, stream=stream)
+        B.moe_route(d, x, w_router, lg_in, w_shared_gate, lg_out, buf.ids, buf.w, buf.sigma, stream)
+        B.moe_group(d, layer, buf.ids, slot_table, n_slots, buf.offsets, buf.perm, buf.inv_perm, buf.group_slot,
+                    buf.status, buf.ws, stream=stream)
     B.moe_expert_ffn(d, x, pool, pool_bytes, layout, buf.offsets, buf.perm, buf.group_slot, buf.h, buf.y_rows,
                      buf.status, buf.ws, stream=stream)
     B.moe_combine(d, buf.y_rows, buf.inv_perm, buf.w, buf.sigma, buf.y, stream)

@@ -108,6 +108,31 @@ def test_layer_parity_small(B, hostgen, name):
     say("[gpu]   %s ok: %s" % (name, stats))
 
 
+@pytest.mark.parametrize("cname", ["tiny", "k_equals_E", "E1024_max", "big_k_wide", "multitile_ragged",
+                                   "decode48_window"])
+def test_route_group_matches_separate_calls(B, hostgen, cname):
+    """moe_route_group (one fused kernel for T <= 16, T*k <= 256; separate
+    kernels otherwise) gives the bits of moe_route then moe_group."""
+    cfg = SMALL[cname] if cname in SMALL else Config(40, "dw", T=4, H=2048, I=64, E=512, k=10, L=1, router="zipf",
+                                                     zipf_s=1.0)
+    say("[gpu] route+group vs separate (%s)" % cname)
+    case = Case(B, cfg, hostgen)
+    from moe_expert_ffn_top_amd.layer import run_layer
+    outs = []
+    for fused in (False, True):
+        b = case.buf
+        for t in (b.ids, b.perm, b.inv_perm, b.offsets, b.group_slot):
+            t.fill_(-7)
+        b.ws.zero_()
+        run_layer(b, 0, case.x, case.pool, case.pool_bytes, case.layout, case.slot_table, cfg.E1, case.wsg_t,
+                  w_router=case.wr_t, logits=None if case.logits is None else case.logits_t, fused=fused)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (b.ids, b.w, b.sigma, b.offsets, b.perm, b.inv_perm, b.group_slot,
+                                         b.y.view(torch.int16))])
+    for u, v in zip(*outs):
+        assert torch.equal(u, v)
+
+
 def test_ffn_stages_split_matches_whole(B, hostgen):
     """gate/up then down as two calls gives the bytes of the single call."""
     cfg = SMALL["multitile_ragged"]
