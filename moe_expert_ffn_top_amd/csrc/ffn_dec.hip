@@ -29,8 +29,12 @@
 
 #include "moe_common.hpp"
 
-#ifndef MOE_DEC_WGS_PER_CU
-#define MOE_DEC_WGS_PER_CU 2
+// resident workgroups per CU for the persistent grid, per stage
+#ifndef MOE_DEC_WGS_GU
+#define MOE_DEC_WGS_GU 2
+#endif
+#ifndef MOE_DEC_WGS_DN
+#define MOE_DEC_WGS_DN 2
 #endif
 // unit blocks per wavefront and steps per K round, per stage
 #ifndef MOE_DEC_U_GU
@@ -396,8 +400,8 @@ hipError_t launch_su(const DecArgs& a, const DecPtrs& p, int sk, int S, int U, c
 
 }  // namespace
 
-// Decode-path FFN: both stages, persistent grids of (CUs x MOE_DEC_WGS_PER_CU)
-// workgroups (fewer when there is less work than that).
+// Decode-path FFN: both stages, persistent grids of (CUs x MOE_DEC_WGS_GU or
+// MOE_DEC_WGS_DN) workgroups (fewer when there is less work than that).
 hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
                           uint16_t* y_rows, void* ws, int n_cu, int stages, hipEvent_t ev_start, hipEvent_t ev_stop,
                           hipStream_t s) {
@@ -421,10 +425,10 @@ hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g
   ptrs.tile_tok = reinterpret_cast<const int32_t*>(base + wl.off_tile_tok);
   ptrs.n_tiles = reinterpret_cast<const int32_t*>(base + wl.off_meta);
   ptrs.pool = g.pool;
-  const int64_t cap = (int64_t)n_cu * MOE_DEC_WGS_PER_CU;
   for (int stage = 0; stage < 2; stage++) {
     if (!((stages >> stage) & 1)) continue;
     const bool gu = stage == 0;
+    const int64_t cap = (int64_t)n_cu * (gu ? MOE_DEC_WGS_GU : MOE_DEC_WGS_DN);
     const int K = gu ? d.H : d.I, units = gu ? d.I : d.H;
     const int ublocks = units / 16;
     const int steps = (K + 127) / 128;
