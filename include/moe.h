@@ -96,20 +96,29 @@ typedef struct moe_dims {
  *     m = 2  down  [H rows][I columns]
  * (rows are output units; columns are the reduction axis K).
  * Each matrix is stored NVFP4-style:
- *   codes  [rows][K/2] bytes, row-major.  Byte c of a row holds column 2c in
- *          its low nibble and column 2c+1 in its high nibble.  A nibble is an
- *          E2M1 code: bit 3 is the sign, bits 0..2 index the magnitudes
- *          {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
- *   scales [rows][K/16] bytes, row-major, OCP FP8 E4M3FN (bias 7, no infinity,
- *          0x7F/0xFF NaN).  Scale b of a row applies to columns 16b..16b+15.
+ *   codes  rows * K/2 bytes.  Logically a row is K/2 bytes: byte c holds
+ *          column 2c in its low nibble and column 2c+1 in its high nibble.  A
+ *          nibble is an E2M1 code: bit 3 is the sign, bits 0..2 index the
+ *          magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+ *   scales rows * K/16 bytes, OCP FP8 E4M3FN (bias 7, no infinity, 0x7F/0xFF
+ *          NaN).  Scale b of a row applies to columns 16b..16b+15.
  *   global one fp32 per matrix.
  * value(r, c) = e2m1(code(r, c)) * e4m3(scale(r, c/16)) * global.
+ * Placement (rows and K are multiples of 16 and 32): the rows are tiled in
+ * blocks of 16.  Row block n/16 owns 8K code bytes from 8K*(n/16): the
+ * 32-column chunk j of its row n%16 is the 16 bytes at 256j + 16(n%16), i.e.
+ * logical bytes 16j..16j+15 of the row.  It owns K scale bytes from K*(n/16):
+ * the chunks form groups of 16 (512 columns; the last group may hold fewer,
+ * c_g = min(16, K/32 - 16g)); group g starts at 512g and holds 2c_g bytes per
+ * row, row n%16's at 2c_g*(n%16), scale b at byte b - 32g of them.  One
+ * chunk of 16 rows is thus 256 contiguous code bytes, and a row's scales of
+ * one group are contiguous.
  * Section order inside a blob: gate codes, up codes, down codes, gate scales,
  * up scales, down scales, then the three fp32 globals (gate, up, down).
  * Every section starts on a 256-byte boundary.  Blobs sit in a pool at
  * pool + slot * slot_stride, slot_stride = blob_bytes rounded up to 4096.
- * Gate codes and up codes are adjacent, so rows 0..2I-1 of the gate codes
- * section read as one [2I][H/2] matrix (likewise the gate+up scales).
+ * Gate codes and up codes are adjacent, so the gate codes section followed by
+ * the up codes section reads as one matrix of 2I rows (likewise the scales).
  */
 typedef struct moe_blob_layout {
   uint64_t blob_bytes;    /* bytes up to the end of the globals */

@@ -14,8 +14,13 @@
 //    tile's n rows address past the end of the buffer and get zeros without
 //    any memory traffic.
 //  - B operand: lane (c = lane % 16, q = lane / 16) owns output unit c of each
-//    of its unit blocks and per 128-value K step loads 16 code bytes (32 E2M1
-//    values) and their two E4M3 scales; codes are decoded with
+//    of its unit blocks and, in a K round of S steps, the S consecutive
+//    32-value chunks S q .. S q + S - 1 of the wavefront's share.  The blob
+//    stores a chunk of a 16-row block as 256 contiguous bytes, so one step's
+//    16-byte code loads cover four such runs.  When the share is whole
+//    512-value groups (S = 4), a lane's 8 scale bytes of a round are adjacent
+//    in the blob and come in one load per unit; otherwise each step loads the
+//    dword holding its chunk's two scales.  Codes are decoded with
 //    v_cvt_scalef32_pk_f32_fp4 and multiplied by the scale in fp32 (exact:
 //    <= 6 significant bits), then packed to bf16 (exact).
 //    v_mfma_f32_16x16x32_bf16 sums exact products in fp32.
@@ -106,12 +111,12 @@ struct Step {
 };
 
 // Per-wavefront view of one item.  Stream m is matrix m % NMAT of unit block
-// m / NMAT.
+// m / NMAT.  codes[m]: this lane's row of chunk 0 of the unit block; scales[m]:
+// the block's scales (plus, with whole groups, this lane's 8 bytes of group 0).
 template <int NS>
 struct Item {
   const uint8_t* codes[NS];
   const uint8_t* scales[NS];
-  int sodd[NS];
   __amdgpu_buffer_rsrc_t arsrc;  // A rows as a buffer
   uint32_t aoff;                 // this lane's row start in arsrc (bytes; past the end for padding rows)
   float g0, g1;                  // fp32 global scales (gate, up) or (down, -)
@@ -143,7 +148,7 @@ __device__ inline Desc load_desc(const DecArgs& a, int item, int c, const int4* 
   return d;
 }
 
-template <bool GATEUP, int U>
+template <bool GATEUP, int U, bool FS>
 __device__ inline Item<(GATEUP ? 2 : 1) * U> make_item(const DecArgs& a, const Desc& d, int n_items, int wub, int c,
                                                         const uint8_t* __restrict__ pool,
                                                         const uint16_t* __restrict__ ain) {
@@ -157,6 +162,7 @@ __device__ inline Item<(GATEUP ? 2 : 1) * U> make_item(const DecArgs& a, const D
   const int tn = __builtin_amdgcn_readfirstlane(d.td.z);
   const int slot = __builtin_amdgcn_readfirstlane(d.td.w);
   const int ubw = (GATEUP ? a.I : a.H) / 16 / a.n_ug;  // unit blocks per item
+  const int q = (threadIdx.x & 63) >> 4;
   it.live = item < n_items;
   it.p0 = p0;
   it.n = it.live ? tn : 0;
@@ -176,9 +182,10 @@ __device__ inline Item<(GATEUP ? 2 : 1) * U> make_item(const DecArgs& a, const D
   for (int m = 0; m < NS; m++) {
     const int mi = GATEUP ? (m % NMAT) : 2;
     const int unit = it.unit + (m / NMAT) * 16;
-    it.codes[m] = it.resident ? blob + a.off_codes[mi] + (int64_t)unit * (K / 2) : pool;
-    it.scales[m] = it.resident ? blob + a.off_scales[mi] + (int64_t)unit * (K / 16) : pool;
-    it.sodd[m] = (int)((reinterpret_cast<uintptr_t>(it.scales[m]) >> 1) & 1);
+    // the lane's row in its 16-row block (blob tiling in moe_common.hpp)
+    const int64_t ub = unit >> 4;
+    it.codes[m] = it.resident ? blob + a.off_codes[mi] + ub * (8 * K) + c * 16 : pool;
+    it.scales[m] = it.resident ? blob + a.off_scales[mi] + ub * K + (FS ? c * 32 + q * 8 : 0) : pool;
   }
   cptr<float> glob = as_const(reinterpret_cast<const float*>(blob + a.off_globals));
   it.g0 = it.resident ? glob[GATEUP ? 0 : 2] : 0.f;
@@ -187,16 +194,22 @@ __device__ inline Item<(GATEUP ? 2 : 1) * U> make_item(const DecArgs& a, const D
 }
 
 // Unconditional, address-clamped weight loads (exact wait counts): invalid
-// chunks are zeroed through their scale.  The scale dword is the aligned one
-// holding the chunk's two bytes.
-template <int NS>
-__device__ inline void load_step(Step<NS>& s, const Item<NS>& it, int ch) {
+// chunks are zeroed through their scale.  Without whole groups (FS false) the
+// scale dword is the aligned one holding the chunk's two bytes.
+template <int NS, bool FS>
+__device__ inline void load_step(Step<NS>& s, const Item<NS>& it, int ch, int nc, int c) {
 #pragma unroll
   for (int m = 0; m < NS; m++) {
-    s.w[m] = *reinterpret_cast<const uint4*>(it.codes[m] + (int64_t)ch * 16);
-    const int64_t off = (int64_t)ch * 2 - 2 * ((it.sodd[m] + ch) & 1);
-    s.sc[m] = *reinterpret_cast<const uint32_t*>(it.scales[m] + off);
+    s.w[m] = *reinterpret_cast<const uint4*>(it.codes[m] + (int64_t)ch * 256);
+    if (!FS) s.sc[m] = *reinterpret_cast<const uint32_t*>(it.scales[m] + (blob_sc_off(ch, nc, c) & ~3));
   }
+}
+
+// With whole groups: this lane's 8 scale bytes (its 4 chunks) of group grp.
+template <int NS>
+__device__ inline void load_sc(uint2* sc, const Item<NS>& it, int grp) {
+#pragma unroll
+  for (int m = 0; m < NS; m++) sc[m] = *reinterpret_cast<const uint2*>(it.scales[m] + (int64_t)grp * 512);
 }
 
 template <int NS>
@@ -209,12 +222,12 @@ __device__ inline void load_a(uint4* xa, const Item<NS>& it, int ch) {
   }
 }
 
+// sc[m]: the step's two scales of stream m in the low 16 bits
 template <int NS>
-__device__ inline void mma_step(const Step<NS>& s, const uint4* xa, const Item<NS>& it, int ch, bool valid,
-                                f32x4* acc) {
+__device__ inline void mma_step(const Step<NS>& s, const uint4* xa, const uint32_t* sc, bool valid, f32x4* acc) {
 #pragma unroll
   for (int m = 0; m < NS; m++) {
-    const uint32_t sw = valid ? (s.sc[m] >> (16 * ((it.sodd[m] + ch) & 1))) : 0u;
+    const uint32_t sw = valid ? sc[m] : 0u;
     const float s0 = e4m3_to_f32<0>(sw), s1 = e4m3_to_f32<1>(sw);
     acc[m] = mfma16x16x32(as_bf16x8(xa[0]), dequant8(s.w[m].x, s0), acc[m]);
     acc[m] = mfma16x16x32(as_bf16x8(xa[1]), dequant8(s.w[m].y, s0), acc[m]);
@@ -224,8 +237,9 @@ __device__ inline void mma_step(const Step<NS>& s, const uint4* xa, const Item<N
 }
 
 // S: 128-value steps per wavefront and K round; U unit blocks per wavefront;
-// SPLITK wavefronts per unit block (4 / SPLITK unit-block groups per item).
-template <bool GATEUP, int SPLITK, int S, int U>
+// SPLITK wavefronts per unit block (4 / SPLITK unit-block groups per item);
+// FS: every K round of every wavefront is one whole 512-value group (S = 4).
+template <bool GATEUP, int SPLITK, int S, int U, bool FS>
 __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restrict__ tiles,
                                                  const int32_t* __restrict__ tile_tok,
                                                  const int32_t* __restrict__ n_tiles,
@@ -245,14 +259,16 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
   const bool kempty = kpart * wc >= nc;
 
   __shared__ f32x4 red[SPLITK > 1 ? 4 : 1][NS][64];
-  // chunk of step s in K round r for this lane
-#define DEC_CH(r, s) (c0 + (r) * (4 * S) + 4 * (s) + q)
+  // chunk of step s in K round r for this lane, and (FS) the round's group
+#define DEC_CH(r, s) (c0 + (r) * (4 * S) + S * q + (s))
+#define DEC_GRP(r) ((c0 + (r) * (4 * S)) >> 4)
 
   DEC_STAMP(0);
   // work units u = 0, 1, ...: item blockIdx.x + (u / nkr) * gridDim.x, K round u % nkr
   const int G = gridDim.x;
   int item = blockIdx.x, kr = 0;
-  Item<NS> cur = make_item<GATEUP, U>(a, load_desc<GATEUP>(a, item, c, tiles, tile_tok), n_items, wub, c, pool, ain);
+  Item<NS> cur =
+      make_item<GATEUP, U, FS>(a, load_desc<GATEUP>(a, item, c, tiles, tile_tok), n_items, wub, c, pool, ain);
   if (!cur.live) return;
   // descriptor of unit 1
   Desc dn = load_desc<GATEUP>(a, nkr > 1 ? item : item + G, c, tiles, tile_tok);
@@ -270,8 +286,10 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
 #pragma unroll
   for (int s = 0; s < S; s++) load_a(xa[s], cur, min(DEC_CH(0, s), c1 - 1));
   Step<NS> fb[S];
+  uint2 scn[NS];  // FS: the scales of the next unit to compute
+  if (FS) load_sc<NS>(scn, cur, DEC_GRP(0));
 #pragma unroll
-  for (int s = 0; s < S; s++) load_step<NS>(fb[s], cur, min(DEC_CH(0, s), c1 - 1));
+  for (int s = 0; s < S; s++) load_step<NS, FS>(fb[s], cur, min(DEC_CH(0, s), c1 - 1), nc, c);
   f32x4 acc[NS];
 
   while (cur.live) {
@@ -280,7 +298,7 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
     // the next unit (derived from the descriptor fetched a unit ago; the same
     // item again when it is a further K round), then the descriptor of the
     // unit after it
-    const Item<NS> nxt = make_item<GATEUP, U>(a, dn, n_items, wub, c, pool, ain);
+    const Item<NS> nxt = make_item<GATEUP, U, FS>(a, dn, n_items, wub, c, pool, ain);
     __builtin_amdgcn_sched_barrier(0);
     dn = load_desc<GATEUP>(a, item2, c, tiles, tile_tok);
     kr2 = kr2 + 1 == nkr ? 0 : kr2 + 1;
@@ -290,11 +308,20 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
 #pragma unroll
       for (int m = 0; m < NS; m++) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // (FS) this unit's scales; scn is refilled with the next unit's at step 0
+    uint2 scc[NS];
+#pragma unroll
+    for (int m = 0; m < NS; m++) scc[m] = scn[m];
 #pragma unroll
     for (int s = 0; s < S; s++) {
       const int chr = DEC_CH(kr, s);
       const int chc = min(chr, c1 - 1);
-      mma_step<NS>(fb[s], xa[s], cur, chc, !kempty && chr < c1 && cur.resident, acc);
+      uint32_t sw[NS];
+#pragma unroll
+      for (int m = 0; m < NS; m++)
+        sw[m] = FS ? ((s < 2 ? scc[m].x : scc[m].y) >> (16 * (s & 1)))
+                   : (fb[s].sc[m] >> (16 * ((blob_sc_off(chc, nc, c) >> 1) & 1)));
+      mma_step<NS>(fb[s], xa[s], sw, !kempty && chr < c1 && cur.resident, acc);
 #ifdef MOE_DEC_TIMING
       if (s == 0 && n_done == 0) {
         __builtin_amdgcn_sched_barrier(0);
@@ -303,7 +330,8 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
 #endif
       // this step's registers now carry the next unit's step s
       const int chn = min(DEC_CH(nkr_next, s), c1 - 1);
-      load_step<NS>(fb[s], nxt, chn);
+      load_step<NS, FS>(fb[s], nxt, chn, nc, c);
+      if (FS && s == 0) load_sc<NS>(scn, nxt, DEC_GRP(nkr_next));
       load_a(xa[s], nxt, chn);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -355,6 +383,7 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
   }
   DEC_STAMP(7);
 #undef DEC_CH
+#undef DEC_GRP
 }
 
 struct DecPtrs {
@@ -374,22 +403,27 @@ struct DecLaunch {
   hipEvent_t ev0, ev1;
 };
 
-template <bool GATEUP, int SK, int S, int U>
+template <bool GATEUP, int SK, int S, int U, bool FS>
 hipError_t launch_k(const DecArgs& a, const DecPtrs& p, const DecLaunch& l) {
   if (l.ev0 || l.ev1)
-    hipExtLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U>), dim3(l.grid), dim3(256), 0, l.st, l.ev0, l.ev1, 0, a,
+    hipExtLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U, FS>), dim3(l.grid), dim3(256), 0, l.st, l.ev0, l.ev1, 0, a,
                           p.tiles, p.tile_tok, p.n_tiles, p.pool, p.ain, p.out);
   else
-    hipLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U>), dim3(l.grid), dim3(256), 0, l.st, a, p.tiles, p.tile_tok,
+    hipLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U, FS>), dim3(l.grid), dim3(256), 0, l.st, a, p.tiles, p.tile_tok,
                        p.n_tiles, p.pool, p.ain, p.out);
   return hipGetLastError();
 }
 
+// S = 4 with every wavefront's share of K made of whole 512-value groups
+// (K a multiple of 512 SK) takes the per-unit scale loads
 template <bool GATEUP, int SK, int U>
 hipError_t launch_s(const DecArgs& a, const DecPtrs& p, int S, const DecLaunch& l) {
-  if (S <= 1) return launch_k<GATEUP, SK, 1, U>(a, p, l);
-  if (S <= 2) return launch_k<GATEUP, SK, 2, U>(a, p, l);
-  return launch_k<GATEUP, SK, (GATEUP ? MOE_DEC_MAXS_GU : MOE_DEC_MAXS_DN) >= 4 ? 4 : 2, U>(a, p, l);
+  if (S <= 1) return launch_k<GATEUP, SK, 1, U, false>(a, p, l);
+  if (S <= 2) return launch_k<GATEUP, SK, 2, U, false>(a, p, l);
+  constexpr int S4 = (GATEUP ? MOE_DEC_MAXS_GU : MOE_DEC_MAXS_DN) >= 4 ? 4 : 2;
+  const int K = GATEUP ? a.H : a.I;
+  if (S4 == 4 && K % (512 * SK) == 0) return launch_k<GATEUP, SK, S4, U, S4 == 4>(a, p, l);
+  return launch_k<GATEUP, SK, S4, U, false>(a, p, l);
 }
 
 template <bool GATEUP>

@@ -94,8 +94,11 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
   const int bunit_c = min(bunit, units - 1);
   // a non-resident group reads the pool's first bytes (valid memory) and is
   // zeroed through its scales
-  const uint8_t* crow = bvalid ? blob + a.off_codes[bmat] + (int64_t)bunit_c * (K / 2) : pool;
-  const uint8_t* srow = bvalid ? blob + a.off_scales[bmat] + (int64_t)bunit_c * (K / 16) : pool;
+  // (blob tiling in moe_common.hpp: chunk j of the column at crow + 256 j, its
+  // scales at sblk + blob_sc_off(j, nc, br))
+  const int nc = K / 32, br = bunit_c & 15;
+  const uint8_t* crow = bvalid ? blob + a.off_codes[bmat] + (int64_t)(bunit_c >> 4) * (8 * K) + br * 16 : pool;
+  const uint8_t* sblk = bvalid ? blob + a.off_scales[bmat] + (int64_t)(bunit_c >> 4) * K : pool;
   const bool loads_b = tid < 256;
 
   // Every load stays inside its row: the K offset is clamped to the last
@@ -107,11 +110,11 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
 #pragma unroll
     for (int i = 0; i < 4; i++) st.a[i] = ap[i];
     if (loads_b) {
-      st.c = *reinterpret_cast<const uint4*>(crow + min(sc_ * (GK / 2) + bh * 16, K / 2 - 16));
+      const int j = min(2 * sc_ + bh, nc - 1);
+      st.c = *reinterpret_cast<const uint4*>(crow + (int64_t)j * 256);
       // the two scale bytes of these 32 values, from the aligned dword holding them
-      const uint8_t* sp = srow + min(sc_ * (GK / 16) + bh * 2, K / 16 - 2);
-      const int odd = (int)(reinterpret_cast<uintptr_t>(sp) & 2);
-      st.sc = *reinterpret_cast<const uint32_t*>(sp - odd) >> (8 * odd);
+      const int so = blob_sc_off(j, nc, br);
+      st.sc = *reinterpret_cast<const uint32_t*>(sblk + (so & ~3)) >> (8 * (so & 2));
     }
   };
   auto stage = [&](const Stage& st, int buf, int s) {

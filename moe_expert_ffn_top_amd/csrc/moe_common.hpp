@@ -77,6 +77,19 @@ inline WsLayout ws_layout(const moe_dims& d) {
   } while (0)
 #endif
 
+// ---- blob tiling -------------------------------------------------------------
+// A matrix of R rows and K columns is stored in blocks of 16 rows.  Block b
+// holds 8 K code bytes at 8 K b: chunk j (columns 32 j .. 32 j + 31) of its row
+// r is the 16 bytes at 256 j + 16 r.  Its K scale bytes sit at K b: K is cut
+// into groups of 16 chunks, group g takes 512 bytes from 512 g (the last group
+// 32 bytes per chunk it has) and holds each row's scales of the group
+// adjacent, in column order.  blob_sc_off: the offset, inside a block's scales,
+// of row r's two scales of chunk j (nc = K / 32 chunks).
+__host__ __device__ inline int blob_sc_off(int j, int nc, int r) {
+  const int g = j >> 4, len = (nc - 16 * g) < 16 ? nc - 16 * g : 16;
+  return g * 512 + r * 2 * len + 2 * (j & 15);
+}
+
 // ---- small device helpers --------------------------------------------------
 __device__ inline float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 

@@ -90,9 +90,10 @@ def e4m3fn_decode(b) -> np.ndarray:
 class BlobLayout:
     """Byte layout of one (layer, expert) blob, as specified in include/moe.h.
 
-    Sections, each starting on a 256-byte boundary: gate codes [I][H/2], up codes
-    [I][H/2], down codes [H][I/2], gate scales [I][H/16], up scales [I][H/16],
-    down scales [H][I/16], then 3 fp32 globals (gate, up, down).
+    Sections, each starting on a 256-byte boundary: gate codes (I x H/2 bytes),
+    up codes, down codes (H x I/2), gate scales (I x H/16), up scales, down
+    scales (H x I/16), then 3 fp32 globals (gate, up, down).  Inside a section
+    the rows are tiled in blocks of 16 (see matrix_codes / matrix_scales).
     """
 
     H: int
@@ -134,14 +135,44 @@ def blob_layout(H: int, I: int) -> BlobLayout:
     return BlobLayout(H, I, tuple(oc), tuple(os_), og, blob, _align(blob, 4096))
 
 
+def _blob_bytes(blob) -> np.ndarray:
+    return np.frombuffer(blob, dtype=np.uint8) if not isinstance(blob, np.ndarray) else blob.view(np.uint8)
+
+
+def matrix_codes(blob, lay: BlobLayout, m: int) -> np.ndarray:
+    """Code bytes of matrix m in row order, uint8 [rows, K/2] (byte c of a row:
+    columns 2c, 2c+1).  Stored layout (include/moe.h): blocks of 16 rows, each
+    8K bytes; inside a block the 32-column chunks follow one another, and a
+    chunk holds the 16 rows' 16 bytes for it in row order."""
+    rows, K = lay.matrix_shape(m)
+    raw = _blob_bytes(blob)[lay.off_codes[m]: lay.off_codes[m] + matrix_bytes(rows, K)[0]]
+    t = raw.reshape(rows // 16, K // 32, 16, 16)          # [block][chunk][row in block][byte]
+    return t.transpose(0, 2, 1, 3).reshape(rows, K // 2)
+
+
+def matrix_scales(blob, lay: BlobLayout, m: int) -> np.ndarray:
+    """E4M3 scale bytes of matrix m in row order, uint8 [rows, K/16] (scale b:
+    columns 16b..16b+15).  Stored layout (include/moe.h): blocks of 16 rows,
+    each K bytes; inside a block the columns form groups of 512 (the last may
+    be shorter), and a group holds each row's scales for it, rows in order."""
+    rows, K = lay.matrix_shape(m)
+    raw = _blob_bytes(blob)[lay.off_scales[m]: lay.off_scales[m] + matrix_bytes(rows, K)[1]]
+    blocks = raw.reshape(rows // 16, K)
+    out = np.empty((rows, K // 16), dtype=np.uint8)
+    for g0 in range(0, K // 16, 32):                       # 32 scales per row per group
+        n = min(32, K // 16 - g0)
+        grp = blocks[:, 16 * g0: 16 * g0 + 16 * n].reshape(rows // 16, 16, n)
+        out[:, g0: g0 + n] = grp.reshape(rows, n)
+    return out
+
+
 def dequant(blob, lay: BlobLayout, m: int) -> np.ndarray:
     """Matrix m of a blob as exact fp64 [rows, K]:
     value(r, c) = e2m1(code(r, c)) * e4m3(scale(r, c // 16)) * global."""
-    buf = np.frombuffer(blob, dtype=np.uint8) if not isinstance(blob, np.ndarray) else blob.view(np.uint8)
+    buf = _blob_bytes(blob)
     rows, K = lay.matrix_shape(m)
-    ncode, nscale = matrix_bytes(rows, K)
-    codes = buf[lay.off_codes[m]: lay.off_codes[m] + ncode].reshape(rows, K // 2)
-    scales = buf[lay.off_scales[m]: lay.off_scales[m] + nscale].reshape(rows, K // 16)
+    codes = matrix_codes(blob, lay, m)
+    scales = matrix_scales(blob, lay, m)
     g = float(np.frombuffer(buf[lay.off_globals + 4 * m: lay.off_globals + 4 * m + 4].tobytes(), dtype="<f4")[0])
     q = np.empty((rows, K), dtype=np.float64)
     q[:, 0::2] = e2m1_decode(codes & 0xF)          # even column: low nibble

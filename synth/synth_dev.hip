@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "blob_pos.h"
+
 namespace {
 
 constexpr uint64_t kGolden = 0x9E3779B97F4A7C15ull;
@@ -114,7 +116,7 @@ __global__ void k_pool_layer(uint64_t seed, int cfg, int layer, const int32_t* _
     amax = fmaxf(amax, fabsf(w[j]));
   }
   const uint8_t sb = e4m3_encode(__fdiv_rn(amax, t6));
-  blob[g.off_scales[m] + n * nbr + b] = sb;
+  blob[g.off_scales[m] + synth_scale_pos(n, b, K)] = sb;
   uint32_t lo = 0, hi = 0;
   if (sb != 0) {
     const float d = __fmul_rn(e4m3_value(sb), G);
@@ -129,7 +131,7 @@ __global__ void k_pool_layer(uint64_t seed, int cfg, int layer, const int32_t* _
   uint2 v;
   v.x = lo;
   v.y = hi;
-  *reinterpret_cast<uint2*>(blob + g.off_codes[m] + n * (uint64_t)(K / 2) + 8 * b) = v;
+  *reinterpret_cast<uint2*>(blob + g.off_codes[m] + synth_code_pos(n, b, K)) = v;
 }
 
 __global__ void k_x(uint64_t key, int64_t n, uint16_t* __restrict__ out) {

@@ -10,6 +10,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include "blob_pos.h"
+
 #define GOLDEN 0x9E3779B97F4A7C15ull
 
 static inline uint64_t mix64(uint64_t z) {
@@ -85,7 +87,8 @@ float synth_global_scale(uint64_t seed, int cfg, int layer, int expert, int matr
   return base * f;
 }
 
-/* One matrix (rows x K) of expert (layer, expert): codes [rows][K/2], scales [rows][K/16]. */
+/* One matrix (rows x K) of expert (layer, expert), codes and scales placed as
+ * blob_pos.h states. */
 static void gen_matrix(uint64_t seed, int cfg, int layer, int expert, int m, int rows, int K,
                        uint8_t* codes, uint8_t* scales) {
   uint64_t key = synth_key(seed, 1, cfg, layer, expert, m);
@@ -106,8 +109,8 @@ static void gen_matrix(uint64_t seed, int cfg, int layer, int expert, int m, int
       }
       float sv = amax / t6;
       uint8_t sb = e4m3_encode(sv);
-      scales[(size_t)n * nb + b] = sb;
-      uint8_t* cp = codes + (size_t)n * (K / 2) + 8 * b;
+      scales[synth_scale_pos((uint64_t)n, b, K)] = sb;
+      uint8_t* cp = codes + synth_code_pos((uint64_t)n, b, K);
       if (sb == 0) { memset(cp, 0, 8); continue; }
       float d = e4m3_value(sb) * G;
       for (int j = 0; j < 8; j++) {

@@ -103,6 +103,58 @@ def test_dequant_hand_built_blob():
     assert np.count_nonzero(wg) == 6 and np.count_nonzero(wu) == 1 and np.count_nonzero(wd) == 1
 
 
+def _hand_tiled_blob():
+    """H = 544, I = 32 blob, bytes placed by hand from the tiling in include/moe.h.
+
+    gate and up are [32 rows][544 cols]: 2 row blocks of 8*544 = 4352 code bytes
+    and 544 scale bytes; 17 chunks, so scale group 0 holds 32 bytes per row and
+    group 1 (chunk 16 only) 2 bytes per row.  down is [544 rows][32 cols]: 34
+    row blocks of 256 code bytes and 32 scale bytes."""
+    lay = O.blob_layout(544, 32)
+    buf = bytearray(lay.slot_stride)
+    G = (0.5, 2.0, 0.25)
+    for m in range(3):
+        struct.pack_into("<f", buf, lay.off_globals + 4 * m, G[m])
+    cg, cu, cd = lay.off_codes
+    sg, su, sd = lay.off_scales
+    # gate row 0, col 1: block 0, chunk 0, row 0, byte 0, high nibble: code 9 (-0.5); scale 0 at byte 0
+    buf[cg + 0] = 0x9 << 4
+    buf[sg + 0] = 0x38
+    # gate row 17, col 40: block 1 (4352), chunk 1 (+256), row 1 (+16), byte 4, low nibble: code 7 (+6)
+    buf[cg + 4352 + 256 + 16 + 4] = 0x7
+    # its scale (b = 2): block 1 (544) + group 0 + row 1 * 32 + 2 -> 1.0
+    buf[sg + 544 + 32 + 2] = 0x38
+    # gate row 17, col 530: chunk 16 (+4096), row 1 (+16), byte 9, low nibble: code 3 (+1.5)
+    buf[cg + 4352 + 4096 + 16 + 9] = 0x3
+    # its scale (b = 33): block 1 (544) + group 1 (512) + row 1 * 2 + 1 -> 2.0 (0x40)
+    buf[sg + 544 + 512 + 2 + 1] = 0x40
+    # up row 31, col 543: the last code byte of the section, high nibble: code 5 (+3)
+    buf[cu + 4352 + 4096 + 15 * 16 + 15] = 0x5 << 4
+    # its scale (b = 33): 544 + 512 + row 15 * 2 + 1, the last scale byte -> 448 (0x7E)
+    buf[su + 544 + 512 + 30 + 1] = 0x7E
+    # down row 543, col 31: block 33 (33 * 256), chunk 0, row 15 (+240), byte 15, high nibble: code 0xC (-2)
+    buf[cd + 33 * 256 + 240 + 15] = 0xC << 4
+    # its scale (b = 1): block 33 (33 * 32) + row 15 * 2 + 1 -> 0.875 (0x36)
+    buf[sd + 33 * 32 + 30 + 1] = 0x36
+    return bytes(buf), lay, G
+
+
+def test_dequant_hand_built_tiled_blob():
+    blob, lay, G = _hand_tiled_blob()
+    assert lay.off_codes == (0, 8704, 17408) and lay.off_scales[0] == 26112
+    wg, wu, wd = (O.dequant(blob, lay, m) for m in range(3))
+    assert wg.shape == (32, 544) and wd.shape == (544, 32)
+    assert wg[0, 1] == -0.5 * G[0]
+    assert wg[17, 40] == 6 * 1.0 * G[0]
+    assert wg[17, 530] == 1.5 * 2.0 * G[0]
+    assert wu[31, 543] == 3 * 448.0 * G[1]
+    assert wd[543, 31] == -2 * 0.875 * G[2]
+    assert np.count_nonzero(wg) == 3 and np.count_nonzero(wu) == 1 and np.count_nonzero(wd) == 1
+    # the up and down entries are the last byte of their sections
+    assert blob[lay.off_codes[1] + 8703] == 0x50 and blob[lay.off_scales[1] + 1087] == 0x7E
+    assert blob[lay.off_codes[2] + 8703] == 0xC0 and blob[lay.off_scales[2] + 1087] == 0x36
+
+
 def test_bf16_round_vs_torch_fp32_inputs():
     rng = np.random.default_rng(1)
     v = np.concatenate([

@@ -36,9 +36,17 @@ def _indep_decode(blob, H, I):
     glob = b[off:off + 12].numpy().view(np.float32).astype(np.float64)
     mats = []
     for m, (r, K) in enumerate(shapes):
-        codes = b[oc[m]:oc[m] + r * K // 2].reshape(r, K // 2).to(torch.int64)
+        # byte positions from the 16-row block tiling, one index per element
+        n = torch.arange(r).view(r, 1)
+        c = torch.arange(K // 2).view(1, K // 2)
+        cpos = (n // 16) * 8 * K + 256 * (c // 16) + 16 * (n % 16) + c % 16
+        codes = b[oc[m] + cpos].to(torch.int64)
         vals = torch.stack([lut[codes & 15], lut[codes >> 4]], dim=-1).reshape(r, K)
-        sc = b[osc[m]:osc[m] + r * K // 16].reshape(r, K // 16).view(torch.float8_e4m3fn).to(torch.float64)
+        sb = torch.arange(K // 16).view(1, K // 16)
+        g = sb // 32
+        per_row = torch.clamp(K // 16 - 32 * g, max=32)
+        spos = (n // 16) * K + 512 * g + per_row * (n % 16) + sb - 32 * g
+        sc = b[osc[m] + spos].contiguous().view(torch.float8_e4m3fn).to(torch.float64)
         mats.append(vals * sc.repeat_interleave(16, dim=1) * glob[m])
     return mats
 

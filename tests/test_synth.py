@@ -29,7 +29,7 @@ def test_quantised_weights_track_gaussian_recipe(hostgen):
         assert np.abs(w).max() <= 0.12 * 1.07
         # every block has a code of magnitude >= 4 (block max maps near 6)
         rows, K = w.shape
-        s = np.frombuffer(blob.tobytes(), np.uint8)[lay.off_scales[m]: lay.off_scales[m] + rows * K // 16]
+        s = O.matrix_scales(blob, lay, m)
         G = np.frombuffer(blob[lay.off_globals + 4 * m: lay.off_globals + 4 * m + 4].tobytes(), np.float32)[0]
         blockmax = np.abs(w).reshape(rows, K // 16, 16).max(axis=2) / (O.e4m3fn_decode(s).reshape(rows, -1) * G)
         assert blockmax.min() >= 4.0 and blockmax.max() <= 6.0
