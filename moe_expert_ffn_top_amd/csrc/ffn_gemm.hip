@@ -13,11 +13,15 @@
 //    each matrix; down: 128 units) decoded from E2M1 codes times their E4M3
 //    scale in fp32 (exact: <= 6 significant bits) and packed to bf16 (exact).
 //    Global loads run two steps ahead in registers.
-//  - Eight wavefronts each own a 64 x 64 block of the 256 x 128 output and
-//    accumulate exact bf16 products in fp32 with v_mfma_f32_16x16x32_bf16; the
-//    global scales and the activation are applied in the epilogue.
+//  - Eight wavefronts each own four 16-row blocks (interleaved over the
+//    SIMDs) by 64 columns of the 256 x 128 output and accumulate exact bf16
+//    products in fp32 with v_mfma_f32_16x16x32_bf16; row blocks past the
+//    chunk's rows are skipped.  The global scales and the activation are
+//    applied in the epilogue.
 #include <hip/hip_ext.h>
 #include <math.h>
+
+#include <type_traits>
 
 #include "moe_common.hpp"
 
@@ -48,12 +52,16 @@ struct GemmArgs {
   int32_t nk;           // K steps
 };
 
+// An empty instruction that reads v: the value counts as used on this path.
+__device__ inline void touch(const uint4& v) { asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w)); }
+
 // One thread's global loads for one K step: 32 A values, and (threads < 256)
 // 32 weight codes with the aligned dword holding their two scales.
 struct Stage {
   uint4 a[4];
   uint4 c;
-  uint32_t sc;
+  uint32_t sc;   // the dword holding the two scales
+  uint32_t ssh;  // their bit offset in it (0 or 16)
 };
 
 template <bool GATEUP>
@@ -80,9 +88,11 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
   __shared__ __align__(16) uint16_t Bs[2][GC * LROW];
 
   const int tid = threadIdx.x;
-  // A staging: thread -> row ar, K half ah (32 values); rows beyond n repeat
-  // the last row (their outputs are not written)
+  // A staging: thread -> row ar, K half ah (32 values).  Rows beyond n load
+  // the last row (unbranched loads keep the wait counts exact) but are not
+  // written to LDS unless their 16-row block is live (their outputs are dropped)
   const int ar = tid >> 1, ah = tid & 1;
+  const bool arow_live = ar < ((n + 15) & ~15);
   const int p = p0 + min(ar, n - 1);
   const int64_t arow = GATEUP ? (int64_t)(p < a.Tk ? perm[p] / a.k : p - a.Tk) : (int64_t)p;
   const uint16_t* asrc = ain + arow * K;
@@ -97,6 +107,10 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
   // (blob tiling in moe_common.hpp: chunk j of the column at crow + 256 j, its
   // scales at sblk + blob_sc_off(j, nc, br))
   const int nc = K / 32, br = bunit_c & 15;
+  // this row's offset in a scale group: 32 bytes per row in whole groups,
+  // 2 (nc % 16) in the last one when it is shorter
+  const uint32_t sfull = (uint32_t)br * 32u, stail = (uint32_t)br * 2u * (uint32_t)(nc & 15);
+  const int nfull = nc >> 4;
   const uint8_t* crow = bvalid ? blob + a.off_codes[bmat] + (int64_t)(bunit_c >> 4) * (8 * K) + br * 16 : pool;
   const uint8_t* sblk = bvalid ? blob + a.off_scales[bmat] + (int64_t)(bunit_c >> 4) * K : pool;
   const bool loads_b = tid < 256;
@@ -109,21 +123,36 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
     const uint4* ap = reinterpret_cast<const uint4*>(asrc + min(sc_ * GK + ah * 32, K - 32));
 #pragma unroll
     for (int i = 0; i < 4; i++) st.a[i] = ap[i];
-    if (loads_b) {
+    {
+      // every thread loads (threads >= 256 repeat those of tid - 256, from L2):
+      // an unbranched load keeps the wait counts exact
       const int j = min(2 * sc_ + bh, nc - 1);
       st.c = *reinterpret_cast<const uint4*>(crow + (int64_t)j * 256);
-      // the two scale bytes of these 32 values, from the aligned dword holding them
-      const int so = blob_sc_off(j, nc, br);
-      st.sc = *reinterpret_cast<const uint32_t*>(sblk + (so & ~3)) >> (8 * (so & 2));
+      // the two scale bytes of these 32 values, from the aligned dword holding
+      // them; the shift waits for the stage, so no wait is forced here
+      // blob_sc_off(j, nc, br) without a multiply in the loop
+      const uint32_t so = (uint32_t)(j >> 4) * 512u + ((j >> 4) < nfull ? sfull : stail) + 2u * (uint32_t)(j & 15);
+      st.sc = *reinterpret_cast<const uint32_t*>(sblk + (so & ~3u));
+      st.ssh = 8u * (so & 2u);
     }
   };
   auto stage = [&](const Stage& st, int buf, int s) {
+    // every loaded register is read here on every path (the stores below are
+    // branched): a load whose value only some paths read leaves the compiler
+    // unsure it has landed, and it then waits for all loads before reusing the
+    // register
+#pragma unroll
+    for (int i = 0; i < 4; i++) touch(st.a[i]);
+    touch(st.c);
+    asm volatile("" ::"v"(st.sc));
     const bool kval = s * GK + ah * 32 < K;
     uint4* ad = reinterpret_cast<uint4*>(&As[buf][ar * LROW + ah * 32]);
+    if (arow_live) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) ad[i] = kval ? st.a[i] : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < 4; i++) ad[i] = kval ? st.a[i] : make_uint4(0, 0, 0, 0);
+    }
     if (loads_b) {
-      const uint32_t sw = (bvalid && s * GK + bh * 32 < K) ? st.sc : 0u;
+      const uint32_t sw = (bvalid && s * GK + bh * 32 < K) ? st.sc >> st.ssh : 0u;
       const float s0 = e4m3_to_f32<0>(sw), s1 = e4m3_to_f32<1>(sw);
       bf16x8* bd = reinterpret_cast<bf16x8*>(&Bs[buf][bc * LROW + bh * 32]);
       bd[0] = dequant8(st.c.x, s0);
@@ -148,20 +177,34 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
 #pragma unroll
     for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf) {
+  // Row block rb of this wavefront is rows 64 rb + 16 wm .. + 15: the four
+  // SIMDs take turns over 16-row blocks, so a chunk of n < 256 rows leaves them
+  // evenly loaded, and the blocks at or past n are skipped (nrb live blocks).
+  const int nrb = max(0, min(4, (n - 16 * wm + 63) >> 6));
+  auto compute_n = [&](auto nrb_c, int buf) {
+    constexpr int NRB = decltype(nrb_c)::value;
 #pragma unroll
     for (int ks = 0; ks < 2; ks++) {
-      bf16x8 fa[4], fb[4];
+      bf16x8 fa[NRB], fb[4];
 #pragma unroll
-      for (int rb = 0; rb < 4; rb++)
-        fa[rb] = *reinterpret_cast<const bf16x8*>(&As[buf][(64 * wm + 16 * rb + r) * LROW + 32 * ks + 8 * q]);
+      for (int rb = 0; rb < NRB; rb++)
+        fa[rb] = *reinterpret_cast<const bf16x8*>(&As[buf][(64 * rb + 16 * wm + r) * LROW + 32 * ks + 8 * q]);
 #pragma unroll
       for (int cb = 0; cb < 4; cb++)
         fb[cb] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(bcol[cb] + r) * LROW + 32 * ks + 8 * q]);
 #pragma unroll
-      for (int rb = 0; rb < 4; rb++)
+      for (int rb = 0; rb < NRB; rb++)
 #pragma unroll
         for (int cb = 0; cb < 4; cb++) acc[rb][cb] = mfma16x16x32(fa[rb], fb[cb], acc[rb][cb]);
+    }
+  };
+  auto compute = [&](int buf) {
+    switch (nrb) {
+      case 4: compute_n(std::integral_constant<int, 4>{}, buf); break;
+      case 3: compute_n(std::integral_constant<int, 3>{}, buf); break;
+      case 2: compute_n(std::integral_constant<int, 2>{}, buf); break;
+      case 1: compute_n(std::integral_constant<int, 1>{}, buf); break;
+      default: break;
     }
   };
 
@@ -171,13 +214,19 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
   gload(st1, 1);
   stage(st0, 0, 0);
   __syncthreads();
-  for (int s = 0; s < a.nk; s += 2) {
+  // (the scheduling barriers keep each step's loads ahead of its MFMAs, so
+  // they have a step and a half to land)
+  // (an odd step count runs one more step, of zeros: its K lies past the end,
+  // which staging zeroes; the loop then has no exit in its middle)
+  const int nke = (a.nk + 1) & ~1;
+  for (int s = 0; s < nke; s += 2) {
     gload(st0, s + 2);
+    __builtin_amdgcn_sched_barrier(0);
     compute(0);
     stage(st1, 1, s + 1);
     __syncthreads();
-    if (s + 1 >= a.nk) break;
     gload(st1, s + 3);
+    __builtin_amdgcn_sched_barrier(0);
     compute(1);
     stage(st0, 0, s + 2);
     __syncthreads();
@@ -191,7 +240,7 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
   for (int rb = 0; rb < 4; rb++) {
 #pragma unroll
     for (int e4 = 0; e4 < 4; e4++) {
-      const int row = 64 * wm + 16 * rb + 4 * q + e4;
+      const int row = 64 * rb + 16 * wm + 4 * q + e4;
       if (row >= n) continue;
       uint16_t* orow = out + (int64_t)(p0 + row) * units;
       if (GATEUP) {
