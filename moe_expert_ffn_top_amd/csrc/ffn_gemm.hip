@@ -31,7 +31,7 @@ namespace {
 constexpr int GM = kChunkRows;   // rows per workgroup
 constexpr int GC = 128;          // output columns per workgroup
 constexpr int GK = 64;           // K per step
-constexpr int LROW = GK + 8;     // bf16 per LDS row: a 16-byte pad keeps 16-byte lane reads conflict-free
+constexpr int LROW = GK + 16;    // bf16 per LDS row: 160-byte rows keep the 16-byte fragment reads of 16 rows conflict-free (144 does not)
 constexpr int GT = 512;          // threads per workgroup
 
 template <typename T>
