@@ -145,15 +145,44 @@ __global__ __launch_bounds__(1024) void k_scan(int64_t nb, int T, int k, int E, 
                                                int32_t* __restrict__ tile_tok, int32_t* __restrict__ tile_base,
                                                int4* __restrict__ chunks) {
   __shared__ int lds[17];
-  const int e = threadIdx.x;
-  const int slot = e < E ? slot_table[(int64_t)layer * (E + 1) + e] : -1;
+  __shared__ int32_t part_sum[1024];
+  // P threads per expert (E2 = E rounded up to a power of two, P = 1024 / E2):
+  // thread (e = tid % E2, part = tid / E2) owns blocks [part nbp, part nbp + nbp)
+  // of expert e's column of per-block counts
+  const int tid = threadIdx.x;
+  const int E2 = E <= 1 ? 1 : 1 << (32 - __builtin_clz(E - 1));
+  const int P = 1024 / E2;
+  const int ec = tid % E2, part = tid / E2;
+  const int64_t nbp = (nb + P - 1) / P;
+  const int64_t b0 = min<int64_t>(nb, part * nbp), b1 = min<int64_t>(nb, b0 + nbp);
+  const int slot = tid < E ? slot_table[(int64_t)layer * (E + 1) + tid] : -1;
   const int ss = slot_table[(int64_t)layer * (E + 1) + E];
+  int32_t mine = 0;
+  if (ec < E) {
+    int64_t b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      int32_t c[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) c[i] = cnt[(b + i) * E + ec];
+#pragma unroll
+      for (int i = 0; i < 8; i++) mine += c[i];
+    }
+    for (; b < b1; b++) mine += cnt[b * E + ec];
+  }
+  part_sum[tid] = mine;
+  __syncthreads();
+  // exclusive prefix of the earlier parts, and expert tid's total
+  int32_t run = 0;
+  for (int pp = 0; pp < part; pp++) run += part_sum[pp * E2 + ec];
   int count = 0;
-  if (e < E) {
-    for (int64_t b = 0; b < nb; b++) {
-      const int c = cnt[b * E + e];
-      cnt[b * E + e] = count;  // exclusive prefix of expert e over blocks
-      count += c;
+  if (tid < E)
+    for (int pp = 0; pp < P; pp++) count += part_sum[pp * E2 + tid];
+  // the counts become each block's exclusive prefix within expert e
+  if (ec < E) {
+    for (int64_t b = b0; b < b1; b++) {
+      const int32_t c = cnt[b * E + ec];
+      cnt[b * E + ec] = run;
+      run += c;
     }
   }
   scan_and_tiles(count, T, k, E, slot, ss, n_slots, offsets, group_slot, status, meta, tiles, tile_tok, tile_base,
@@ -299,38 +328,35 @@ __global__ __launch_bounds__(1024) void k_route_group_small(
                    tile_tok, tile_base, chunks, hist, cntl, tbl, sid, lds);
 }
 
-__global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ ids, int64_t F, int E, int k,
-                                                const int32_t* __restrict__ cnt, const int32_t* __restrict__ offsets,
-                                                int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
-                                                int32_t* __restrict__ tile_tok,
-                                                const int32_t* __restrict__ tile_base) {
-  __shared__ int32_t run[1024];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) run[e] = offsets[e] + cnt[(int64_t)blockIdx.x * E + e];
+// Stable placement of one block of kBlk entries: an entry's rank is the number
+// of earlier entries of the block with the same expert, counted over the ids
+// staged in LDS (4 per read); its row is offsets[e] + the block's exclusive
+// prefix for e (from k_scan) + rank.
+__global__ __launch_bounds__(kBlk) void k_scatter(const int32_t* __restrict__ ids, int64_t F, int E, int k,
+                                                  const int32_t* __restrict__ cnt, const int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+                                                  int32_t* __restrict__ tile_tok,
+                                                  const int32_t* __restrict__ tile_base) {
+  __shared__ __align__(16) int32_t sid[kBlk];
+  const int i = threadIdx.x;
+  const int64_t f = (int64_t)blockIdx.x * kBlk + i;
+  const bool in = f < F;
+  const int e = in ? ids[f] : -1;
+  const bool ok = in && e >= 0 && e < E;
+  sid[i] = ok ? e : -1;
   __syncthreads();
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  for (int c = 0; c < kBlk / 64; c++) {
-    const int64_t f = (int64_t)blockIdx.x * kBlk + c * 64 + lane;
-    const bool in = f < F;
-    const int e = in ? ids[f] : -1;
-    const bool ok = in && e >= 0 && e < E;
-    if (in && !ok) inv_perm[f] = -1;
-    unsigned long long todo = __ballot(ok);
-    while (todo) {
-      const int leader = __ffsll((long long)todo) - 1;
-      const int le = __shfl(e, leader);
-      const unsigned long long mask = __ballot(ok && e == le);
-      const int base = run[le];
-      if (ok && e == le) {
-        const int p = base + __popcll(mask & lt);
-        perm[p] = (int32_t)f;
-        inv_perm[f] = p;
-        note_tile_row(tile_tok, tile_base, offsets, e, p, (int)f, k, offsets[e + 1] - offsets[e]);
-      }
-      if (lane == leader) run[le] = base + __popcll(mask);
-      todo &= ~mask;
-    }
+  if (in && !ok) inv_perm[f] = -1;
+  if (!ok) return;
+  int rank = 0;
+  const int4* sid4 = reinterpret_cast<const int4*>(sid);
+  for (int j0 = 0; j0 < i; j0 += 4) {
+    const int4 v = sid4[j0 >> 2];
+    rank += (j0 + 0 < i && v.x == e) + (j0 + 1 < i && v.y == e) + (j0 + 2 < i && v.z == e) + (j0 + 3 < i && v.w == e);
   }
+  const int p = offsets[e] + cnt[(int64_t)blockIdx.x * E + e] + rank;
+  perm[p] = (int32_t)f;
+  inv_perm[f] = p;
+  note_tile_row(tile_tok, tile_base, offsets, e, p, (int)f, k, offsets[e + 1] - offsets[e]);
 }
 
 }  // namespace
@@ -356,7 +382,7 @@ hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, co
   hipLaunchKernelGGL(k_count, dim3((unsigned)wl.nb), dim3(256), 0, s, ids, F, d.E, cnt, dev_status);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, wl.nb, d.T, d.k, d.E, layer, slot_table, n_slots, cnt,
                      offsets, group_slot, dev_status, meta, tiles, tile_tok, tile_base, chunks);
-  hipLaunchKernelGGL(k_scatter, dim3((unsigned)wl.nb), dim3(64), 0, s, ids, F, d.E, d.k, cnt, offsets, perm, inv_perm,
+  hipLaunchKernelGGL(k_scatter, dim3((unsigned)wl.nb), dim3(kBlk), 0, s, ids, F, d.E, d.k, cnt, offsets, perm, inv_perm,
                      tile_tok, tile_base);
   return hipGetLastError();
 }
