@@ -142,7 +142,10 @@ int moe_workspace_bytes(const moe_dims* d, uint64_t* out_bytes);
  *
  * Logits: exactly one of w_router / logits_in is non-NULL.
  *   w_router  device fp32 [H][E] row-major: l[t,e] = sum_h x[t,h] * W[h,e],
- *             accumulated in fp32 (rounding point R0: fp32 logits).
+ *             accumulated in fp32 (rounding point R0: fp32 logits).  Each
+ *             W[h,e] is split exactly into three bf16 parts and the products
+ *             (exact in fp32) are summed by bf16 MFMAs, so the only rounding
+ *             is the fp32 accumulation.
  *   logits_in device fp32 [T][E]: used as given.
  * x            device bf16 bits [T][H] row-major (required: the shared gate reads it).
  * w_shared_gate device fp32 [H], 16-byte aligned:
