@@ -10,14 +10,18 @@
 //
 // Up to 256 (token, slot) entries (decode): one fused single-block kernel.
 // Otherwise a stable counting sort in three fixed-shape kernels:
-//   count   per 256-entry block, LDS histogram of expert ids (order-free atomics)
+//   count   per kCntBlk-entry block, LDS histogram of expert ids (order-free atomics)
 //   scan    one block: per-expert prefix over blocks, exclusive scan over experts,
-//           slot rewrite, and the FFN tile list
-//   scatter per block, one wavefront walks its 4 chunks of 64 entries in order;
-//           inside a chunk, ballots give each entry its rank among equal ids,
-//           so a row's position depends only on the ids (deterministic).
+//           slot rewrite, and the FFN work list
+//   scatter per 256-entry block: an entry's row is its group's first row, plus
+//           the entries of its expert in earlier counting blocks (the scan),
+//           in earlier 256-entry parts of its own counting block (an LDS
+//           histogram) and earlier in its own part (counted over the ids
+//           staged in LDS), so a row depends only on the ids (deterministic).
 #include "moe_common.hpp"
 #include "topk_wave.hpp"
+
+#include <type_traits>
 
 namespace moe {
 #ifdef MOE_STAGE_TIMING
@@ -27,16 +31,26 @@ namespace {
 
 constexpr int kBlk = 256;
 
-__global__ __launch_bounds__(256) void k_count(const int32_t* __restrict__ ids, int64_t F, int E,
-                                               int32_t* __restrict__ cnt, int32_t* __restrict__ status) {
+constexpr int kParts = kCntBlk / kBlk;  // 256-entry parts per counting block
+
+__global__ __launch_bounds__(kBlk) void k_count(const int32_t* __restrict__ ids, int64_t F, int E,
+                                                int32_t* __restrict__ cnt, int32_t* __restrict__ status) {
   __shared__ int32_t hist[1024];
+  int ev[kParts];
+#pragma unroll
+  for (int j = 0; j < kParts; j++) {
+    const int64_t f = (int64_t)blockIdx.x * kCntBlk + j * kBlk + threadIdx.x;
+    ev[j] = f < F ? ids[f] : 0;
+  }
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
-  const int64_t f = (int64_t)blockIdx.x * kBlk + threadIdx.x;
-  if (f < F) {
-    const int e = ids[f];
-    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
-    else atomicOr(status, MOE_DEV_BAD_EXPERT_ID);
+#pragma unroll
+  for (int j = 0; j < kParts; j++) {
+    const int64_t f = (int64_t)blockIdx.x * kCntBlk + j * kBlk + threadIdx.x;
+    if (f < F) {
+      if (ev[j] >= 0 && ev[j] < E) atomicAdd(&hist[ev[j]], 1);
+      else atomicOr(status, MOE_DEV_BAD_EXPERT_ID);
+    }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[(int64_t)blockIdx.x * E + e] = hist[e];
@@ -76,11 +90,12 @@ __device__ int block_exclusive_scan(int v, int* lds16, int* total) {
 }
 
 // Thread e (< E) holds count = rows of expert e.  Writes offsets, group_slot,
-// residency status and the FFN tile list; returns this expert's first row.
+// residency status and the FFN work list (the tile lists, or with `chunks`
+// the chunk list); returns this expert's first row.
 // `slot` is slot_table[layer][e] for thread e < E and `ss` the shared expert's
 // slot; the caller loads both at its start, so their latency overlaps its own.
-// `chunks` (or null): the grouped-GEMM work list, written when the FFN will
-// run as a GEMM.
+// `chunks` (or null): the grouped-GEMM work list, written in place of the
+// tile lists when the FFN will run as a GEMM; *tbase_out is then not set.
 __device__ int scan_and_tiles(int count, int T, int k, int E, int slot, int ss, int32_t n_slots,
                               int32_t* __restrict__ offsets, int32_t* __restrict__ group_slot,
                               int32_t* __restrict__ status, int32_t* __restrict__ meta, int4* __restrict__ tiles,
@@ -103,26 +118,29 @@ __device__ int scan_and_tiles(int count, int T, int k, int E, int slot, int ss, 
     if (ss < 0) atomicOr(status, MOE_DEV_NOT_RESIDENT);
     if (ss >= n_slots) atomicOr(status, MOE_DEV_BAD_SLOT);
   }
-  // FFN tiles of kTileRows rows: routed groups in expert order, then the shared group
-  const int nt = (count + kTileRows - 1) / kTileRows;
-  int nt_total = 0;
-  const int tbase = block_exclusive_scan(nt, lds17, &nt_total);
-  if (e < E) tile_base[e] = tbase;
-  if (tbase_out) *tbase_out = tbase;
-  for (int i = 0; i < nt; i++) {
-    const int n = min(kTileRows, count - i * kTileRows);
-    tiles[tbase + i] = make_int4(e, off + i * kTileRows, n, slot);
-  }
-  const int nts = (T + kTileRows - 1) / kTileRows;
-  for (int i = threadIdx.x; i < nts; i += blockDim.x)
-    tiles[nt_total + i] = make_int4(E, (int32_t)(Tk + (int64_t)i * kTileRows), min(kTileRows, T - i * kTileRows), ss);
-  for (int i = threadIdx.x; i < nts * kTileRows; i += blockDim.x) {  // shared rows: token = row - T*k
-    const int tl = i / kTileRows, r = i % kTileRows;
-    const int n = min(kTileRows, T - tl * kTileRows);
-    tile_tok[(int64_t)(nt_total + tl) * kTileRows + r] = tl * kTileRows + (r < n ? r : 0);
-  }
-  if (threadIdx.x == 0) meta[0] = nt_total + nts;
-  if (chunks) {  // uniform: every thread of the block takes this branch or none does
+  if (!chunks) {  // uniform: every thread of the block takes this branch or none does
+    // FFN tiles of kTileRows rows: routed groups in expert order, then the shared group
+    const int nt = (count + kTileRows - 1) / kTileRows;
+    int nt_total = 0;
+    const int tbase = block_exclusive_scan(nt, lds17, &nt_total);
+    if (e < E) tile_base[e] = tbase;
+    if (tbase_out) *tbase_out = tbase;
+    for (int i = 0; i < nt; i++) {
+      const int n = min(kTileRows, count - i * kTileRows);
+      tiles[tbase + i] = make_int4(e, off + i * kTileRows, n, slot);
+    }
+    const int nts = (T + kTileRows - 1) / kTileRows;
+    for (int i = threadIdx.x; i < nts; i += blockDim.x)
+      tiles[nt_total + i] =
+          make_int4(E, (int32_t)(Tk + (int64_t)i * kTileRows), min(kTileRows, T - i * kTileRows), ss);
+    for (int i = threadIdx.x; i < nts * kTileRows; i += blockDim.x) {  // shared rows: token = row - T*k
+      const int tl = i / kTileRows, r = i % kTileRows;
+      const int n = min(kTileRows, T - tl * kTileRows);
+      tile_tok[(int64_t)(nt_total + tl) * kTileRows + r] = tl * kTileRows + (r < n ? r : 0);
+    }
+    if (threadIdx.x == 0) meta[0] = nt_total + nts;
+  } else {
+    // grouped-GEMM chunks of kChunkRows rows, in the same order
     const int nck = (count + kChunkRows - 1) / kChunkRows;
     int nck_total = 0;
     const int cbase = block_exclusive_scan(nck, lds17, &nck_total);
@@ -137,52 +155,94 @@ __device__ int scan_and_tiles(int count, int T, int k, int E, int slot, int ss, 
   return off;
 }
 
-__global__ __launch_bounds__(1024) void k_scan(int64_t nb, int T, int k, int E, int layer,
+// One block over the ncb x E counts.  V adjacent experts per thread (V = 4
+// when E % 4 == 0: one int4 per row of counts), EV = E2 / V expert groups
+// (E2 = E rounded up to a power of two) and P = 1024 / EV parts: thread
+// (eq = tid % EV, part = tid / EV) owns rows [part nbp, part nbp + nbp) of
+// experts eq V .. eq V + V - 1.  Rows go in batches of kBatch loads; the first
+// batch stays in registers for the second pass, so a part of at most kBatch
+// rows is read once.
+template <int V>
+__global__ __launch_bounds__(1024) void k_scan(int64_t ncb, int T, int k, int E, int layer,
                                                const int32_t* __restrict__ slot_table, int32_t n_slots,
                                                int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
                                                int32_t* __restrict__ group_slot, int32_t* __restrict__ status,
                                                int32_t* __restrict__ meta, int4* __restrict__ tiles,
                                                int32_t* __restrict__ tile_tok, int32_t* __restrict__ tile_base,
                                                int4* __restrict__ chunks) {
+  using vec = typename std::conditional<V == 4, int4, int>::type;
+  constexpr int kBatch = 16;
   __shared__ int lds[17];
-  __shared__ int32_t part_sum[1024];
-  // P threads per expert (E2 = E rounded up to a power of two, P = 1024 / E2):
-  // thread (e = tid % E2, part = tid / E2) owns blocks [part nbp, part nbp + nbp)
-  // of expert e's column of per-block counts
+  __shared__ int32_t part_sum[1024 * V];  // [part][eq][V] = [part][expert]
   const int tid = threadIdx.x;
   const int E2 = E <= 1 ? 1 : 1 << (32 - __builtin_clz(E - 1));
-  const int P = 1024 / E2;
-  const int ec = tid % E2, part = tid / E2;
-  const int64_t nbp = (nb + P - 1) / P;
-  const int64_t b0 = min<int64_t>(nb, part * nbp), b1 = min<int64_t>(nb, b0 + nbp);
+  const int EV = E2 / V > 0 ? E2 / V : 1;
+  const int P = 1024 / EV;
+  const int eq = tid % EV, part = tid / EV;
+  const int64_t nbp = (ncb + P - 1) / P;
+  const int64_t b0 = min<int64_t>(ncb, part * nbp), b1 = min<int64_t>(ncb, b0 + nbp);
   const int slot = tid < E ? slot_table[(int64_t)layer * (E + 1) + tid] : -1;
   const int ss = slot_table[(int64_t)layer * (E + 1) + E];
-  int32_t mine = 0;
-  if (ec < E) {
-    int64_t b = b0;
-    for (; b + 8 <= b1; b += 8) {
-      int32_t c[8];
-#pragma unroll
-      for (int i = 0; i < 8; i++) c[i] = cnt[(b + i) * E + ec];
-#pragma unroll
-      for (int i = 0; i < 8; i++) mine += c[i];
+  // with V = 4, E % 4 == 0: a live group has all four experts
+  const int64_t nrow = eq * V < E ? b1 - b0 : 0;
+  vec* col = reinterpret_cast<vec*>(cnt) + (int64_t)b0 * (E / V) + eq;
+  const int64_t rs = E / V;  // row stride in vec
+  int32_t mine[V] = {};
+  auto add = [&](const vec& c) {
+    if constexpr (V == 4) {
+      mine[0] += c.x; mine[1] += c.y; mine[2] += c.z; mine[3] += c.w;
+    } else {
+      mine[0] += c;
     }
-    for (; b < b1; b++) mine += cnt[b * E + ec];
+  };
+  vec first[kBatch];
+#pragma unroll
+  for (int i = 0; i < kBatch; i++) first[i] = i < nrow ? col[i * rs] : vec{};
+#pragma unroll
+  for (int i = 0; i < kBatch; i++) add(first[i]);
+  for (int64_t b = kBatch; b < nrow; b += kBatch) {
+    vec c[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; i++) c[i] = b + i < nrow ? col[(b + i) * rs] : vec{};
+#pragma unroll
+    for (int i = 0; i < kBatch; i++) add(c[i]);
   }
-  part_sum[tid] = mine;
+#pragma unroll
+  for (int i = 0; i < V; i++) part_sum[tid * V + i] = mine[i];
   __syncthreads();
   // exclusive prefix of the earlier parts, and expert tid's total
-  int32_t run = 0;
-  for (int pp = 0; pp < part; pp++) run += part_sum[pp * E2 + ec];
+  int32_t run[V] = {};
+  for (int pp = 0; pp < part; pp++)
+#pragma unroll
+    for (int i = 0; i < V; i++) run[i] += part_sum[(pp * EV + eq) * V + i];
   int count = 0;
   if (tid < E)
-    for (int pp = 0; pp < P; pp++) count += part_sum[pp * E2 + tid];
-  // the counts become each block's exclusive prefix within expert e
-  if (ec < E) {
-    for (int64_t b = b0; b < b1; b++) {
-      const int32_t c = cnt[b * E + ec];
-      cnt[b * E + ec] = run;
-      run += c;
+    for (int pp = 0; pp < P; pp++) count += part_sum[pp * EV * V + tid];
+  // the counts become each row's exclusive prefix within its expert
+  auto step = [&](vec& c) {
+    if constexpr (V == 4) {
+      const int4 v = c;
+      c = make_int4(run[0], run[1], run[2], run[3]);
+      run[0] += v.x; run[1] += v.y; run[2] += v.z; run[3] += v.w;
+    } else {
+      const int v = c;
+      c = run[0];
+      run[0] += v;
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kBatch; i++) {
+    step(first[i]);
+    if (i < nrow) col[i * rs] = first[i];
+  }
+  for (int64_t b = kBatch; b < nrow; b += kBatch) {
+    vec c[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; i++) c[i] = b + i < nrow ? col[(b + i) * rs] : vec{};
+#pragma unroll
+    for (int i = 0; i < kBatch; i++) {
+      step(c[i]);
+      if (b + i < nrow) col[(b + i) * rs] = c[i];
     }
   }
   scan_and_tiles(count, T, k, E, slot, ss, n_slots, offsets, group_slot, status, meta, tiles, tile_tok, tile_base,
@@ -253,7 +313,7 @@ __device__ inline void group_small_tail(int e_mine, int F, int T, int k, int E, 
       const int p = hist[e_mine] + rank;
       perm[p] = tid;
       inv_perm[tid] = p;
-      note_tile_row(tile_tok, tbl, hist, e_mine, p, tid, k, cntl[e_mine]);
+      if (!chunks) note_tile_row(tile_tok, tbl, hist, e_mine, p, tid, k, cntl[e_mine]);
     }
   }
   STAGE_STAMP(1, 5);
@@ -338,25 +398,38 @@ __global__ __launch_bounds__(kBlk) void k_scatter(const int32_t* __restrict__ id
                                                   int32_t* __restrict__ tile_tok,
                                                   const int32_t* __restrict__ tile_base) {
   __shared__ __align__(16) int32_t sid[kBlk];
+  __shared__ int32_t hist[1024];  // entries per expert in the earlier parts of this counting block
   const int i = threadIdx.x;
   const int64_t f = (int64_t)blockIdx.x * kBlk + i;
+  const int part = blockIdx.x % kParts;  // block-uniform
+  const int64_t cb = blockIdx.x / kParts;
+  // the earlier parts are whole (only the last block can be partial)
+  int prev[kParts - 1];
+#pragma unroll
+  for (int j = 0; j < kParts - 1; j++) prev[j] = j < part ? ids[cb * kCntBlk + j * kBlk + i] : -1;
   const bool in = f < F;
   const int e = in ? ids[f] : -1;
   const bool ok = in && e >= 0 && e < E;
   sid[i] = ok ? e : -1;
+  if (part)
+    for (int x = i; x < E; x += kBlk) hist[x] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kParts - 1; j++)
+    if (prev[j] >= 0 && prev[j] < E) atomicAdd(&hist[prev[j]], 1);
   __syncthreads();
   if (in && !ok) inv_perm[f] = -1;
   if (!ok) return;
-  int rank = 0;
+  int rank = part ? hist[e] : 0;
   const int4* sid4 = reinterpret_cast<const int4*>(sid);
   for (int j0 = 0; j0 < i; j0 += 4) {
     const int4 v = sid4[j0 >> 2];
     rank += (j0 + 0 < i && v.x == e) + (j0 + 1 < i && v.y == e) + (j0 + 2 < i && v.z == e) + (j0 + 3 < i && v.w == e);
   }
-  const int p = offsets[e] + cnt[(int64_t)blockIdx.x * E + e] + rank;
+  const int p = offsets[e] + cnt[cb * E + e] + rank;
   perm[p] = (int32_t)f;
   inv_perm[f] = p;
-  note_tile_row(tile_tok, tile_base, offsets, e, p, (int)f, k, offsets[e + 1] - offsets[e]);
+  if (tile_tok) note_tile_row(tile_tok, tile_base, offsets, e, p, (int)f, k, offsets[e + 1] - offsets[e]);
 }
 
 }  // namespace
@@ -379,11 +452,12 @@ hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, co
                        chunks);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_count, dim3((unsigned)wl.nb), dim3(256), 0, s, ids, F, d.E, cnt, dev_status);
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, wl.nb, d.T, d.k, d.E, layer, slot_table, n_slots, cnt,
+  hipLaunchKernelGGL(k_count, dim3((unsigned)wl.ncb), dim3(kBlk), 0, s, ids, F, d.E, cnt, dev_status);
+  auto scan = d.E % 4 == 0 ? k_scan<4> : k_scan<1>;
+  hipLaunchKernelGGL(scan, dim3(1), dim3(1024), 0, s, wl.ncb, d.T, d.k, d.E, layer, slot_table, n_slots, cnt,
                      offsets, group_slot, dev_status, meta, tiles, tile_tok, tile_base, chunks);
   hipLaunchKernelGGL(k_scatter, dim3((unsigned)wl.nb), dim3(kBlk), 0, s, ids, F, d.E, d.k, cnt, offsets, perm, inv_perm,
-                     tile_tok, tile_base);
+                     chunks ? nullptr : tile_tok, tile_base);
   return hipGetLastError();
 }
 

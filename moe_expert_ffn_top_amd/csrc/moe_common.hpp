@@ -23,14 +23,19 @@ constexpr int kGemmMinRows = 16;
 inline bool use_gemm(const moe_dims& d) { return (int64_t)d.T * d.k >= (int64_t)kGemmMinRows * d.E; }
 
 // ---- workspace layout (shared by moe_group and moe_expert_ffn) --------------
-// cnt       int32 [nb][E]       per-256-row-block expert counts, then block prefixes
+// cnt       int32 [ncb][E]      per-kCntBlk-entry-block expert counts, then block prefixes
 // meta      int32 [64]          meta[0] = number of FFN tiles, meta[1] = number of GEMM chunks
 // tiles     int4  [max_tiles]   {group, first row p0, rows n (<= 16), slot}
 // tile_tok  int32 [max_tiles][16] token of each tile row (rows >= n repeat row 0)
 // tile_base int32 [E]           first tile of each routed group
-// chunks    int4  [max_chunks]  {group, first row p0, rows n (<= 256), slot} (GEMM path only)
+// chunks    int4  [max_chunks]  {group, first row p0, rows n (<= 256), slot}
+// The FFN reads either the tile lists (weight-streaming kernel) or the chunk
+// list (grouped GEMM), and the grouping writes only the one that use_gemm names.
+// Flat entries per counting block of the grouping (a multiple of 256).
+constexpr int kCntBlk = 1024;
 struct WsLayout {
   int64_t nb;          // blocks of 256 flat (token, slot) entries
+  int64_t ncb;         // blocks of kCntBlk flat entries
   int64_t max_tiles;   // upper bound on FFN tiles
   int64_t max_chunks;  // upper bound on GEMM chunks
   uint64_t off_cnt, off_meta, off_tiles, off_tile_tok, off_tile_base, off_chunks, total;
@@ -42,10 +47,11 @@ inline WsLayout ws_layout(const moe_dims& d) {
   WsLayout w;
   const int64_t F = (int64_t)d.T * d.k;
   w.nb = (F + 255) / 256;
+  w.ncb = (F + kCntBlk - 1) / kCntBlk;
   const int64_t routed_groups = F < d.E ? F : d.E;
   w.max_tiles = (F + kTileRows - 1) / kTileRows + routed_groups + (d.T + kTileRows - 1) / kTileRows + 1;
   w.off_cnt = 0;
-  w.off_meta = align256((uint64_t)w.nb * d.E * 4);
+  w.off_meta = align256((uint64_t)w.ncb * d.E * 4);
   w.off_tiles = w.off_meta + 256;
   w.off_tile_tok = align256(w.off_tiles + (uint64_t)w.max_tiles * 16);
   w.off_tile_base = align256(w.off_tile_tok + (uint64_t)w.max_tiles * 64);

@@ -234,3 +234,38 @@ def test_run_to_run_determinism(B, hostgen, cname):
         again = (a.buf.ids, a.buf.perm, a.buf.h.view(torch.int16), a.buf.y.view(torch.int16))
         for u, v in zip(first, again):
             assert torch.equal(u, v)
+
+
+def _drawn_ids(rng, T, k, E, zipf_s):
+    """k distinct experts per token: Gumbel top-k over log-weights
+    -zipf_s * log(rank) (zipf_s = 0: uniform)."""
+    logw = -zipf_s * np.log(np.arange(1, E + 1, dtype=np.float64))
+    keys = logw[None, :] + rng.gumbel(size=(T, E))
+    return np.argsort(-keys, axis=1, kind="stable")[:, :k].astype(np.int32)
+
+
+# (T, k, E, zipf_s): the prefill shapes (512 and 256 experts, one int4 of four
+# experts per count load), E = 1024, and E not a multiple of 4 (one expert per
+# load) with enough 256-entry blocks that every scan thread runs full batches
+@pytest.mark.parametrize("T,k,E,zs", [(8192, 10, 512, 0.0), (4096, 6, 256, 1.2), (600, 8, 1024, 1.0),
+                                      (100000, 3, 10, 0.5), (97, 3, 7, 0.0)])
+def test_group_matches_oracle_on_drawn_ids(B, T, k, E, zs):
+    """moe_group on drawn ids gives the oracle's offsets, perm and inv_perm bit
+    for bit, and the slot table's entries as group slots, whichever of its
+    kernel paths the size selects."""
+    from moe_expert_ffn_top_amd.layer import LayerBuffers
+    say("[gpu] grouping case T=%d k=%d E=%d zipf=%.1f" % (T, k, E, zs))
+    ids = _drawn_ids(np.random.default_rng(T * 31 + E), T, k, E, zs)
+    d = B.Dims(T, 64, 32, E, k, 1)
+    buf = LayerBuffers.allocate(d)
+    buf.ids.copy_(torch.from_numpy(ids))
+    st = torch.from_numpy((np.arange(E + 1, dtype=np.int32)[::-1] + 3)[None, :].copy()).cuda()
+    buf.status.zero_()
+    B.moe_group(d, 0, buf.ids, st, E + 4, buf.offsets, buf.perm, buf.inv_perm, buf.group_slot, buf.status, buf.ws)
+    torch.cuda.synchronize()
+    g = O.group(ids, E)
+    assert int(buf.status.item()) == 0
+    assert np.array_equal(buf.offsets.cpu().numpy(), g.offsets)
+    assert np.array_equal(buf.perm.cpu().numpy(), g.perm)
+    assert np.array_equal(buf.inv_perm.cpu().numpy(), g.inv_perm)
+    assert np.array_equal(buf.group_slot.cpu().numpy(), st.cpu().numpy()[0])
