@@ -7,17 +7,21 @@
 //    grouping kernels list the chunks; blocks map to (chunk, tile) so that all
 //    tiles of one chunk run on the same XCD and share the chunk's A rows in
 //    that XCD's L2.
-//  - Per 64-value K step a 512-thread workgroup stages into LDS (double
-//    buffered) the chunk's A rows (bf16 rows of x gathered through perm, or
-//    rows of h) and the B tile: 128 columns of weights (gate/up: 64 units of
-//    each matrix; down: 128 units) decoded from E2M1 codes times their E4M3
-//    scale in fp32 (exact: <= 6 significant bits) and packed to bf16 (exact).
-//    Global loads run two steps ahead in registers.
-//  - Eight wavefronts each own four 16-row blocks (interleaved over the
-//    SIMDs) by 64 columns of the 256 x 128 output and accumulate exact bf16
-//    products in fp32 with v_mfma_f32_16x16x32_bf16; row blocks past the
-//    chunk's rows are skipped.  The global scales and the activation are
-//    applied in the epilogue.
+//  - A 512-thread workgroup has two roles, one wavefront of each per SIMD:
+//    four producer wavefronts do all global loads and stage each 64-value K
+//    step into LDS (double buffered): the chunk's A rows (bf16 rows of x
+//    gathered through perm, or rows of h) and the B tile, 128 columns of
+//    weights (gate/up: 64 units of each matrix; down: 128 units) decoded from
+//    E2M1 codes times their E4M3 scale in fp32 (exact: <= 6 significant bits)
+//    and packed to bf16 (exact).  Their loads run three steps ahead in four
+//    register stages.  Four consumer wavefronts only read fragments and issue
+//    MFMAs.  Each barrier interval then costs the longer of the two roles, not
+//    their sum, and the producers' staging overlaps the MFMAs on each SIMD.
+//  - Each consumer owns four 16-row blocks (interleaved over the SIMDs) by all
+//    128 columns of the 256 x 128 output and accumulates exact bf16 products
+//    in fp32 with v_mfma_f32_16x16x32_bf16; row blocks past the chunk's rows
+//    are skipped.  The global scales and the activation are applied in the
+//    epilogue.
 #include <hip/hip_ext.h>
 #include <math.h>
 
@@ -32,7 +36,8 @@ constexpr int GM = kChunkRows;   // rows per workgroup
 constexpr int GC = 128;          // output columns per workgroup
 constexpr int GK = 64;           // K per step
 constexpr int LROW = GK + 16;    // bf16 per LDS row: 160-byte rows keep the 16-byte fragment reads of 16 rows conflict-free (144 does not)
-constexpr int GT = 512;          // threads per workgroup
+constexpr int GT = 512;          // threads per workgroup: 4 consumer + 4 producer wavefronts
+constexpr int NST = 4;           // producer register stages
 
 template <typename T>
 using cptr = const __attribute__((address_space(4))) T*;
@@ -55,10 +60,18 @@ struct GemmArgs {
 // An empty instruction that reads v: the value counts as used on this path.
 __device__ inline void touch(const uint4& v) { asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w)); }
 
-// One thread's global loads for one K step: 32 A values, and (threads < 256)
-// 32 weight codes with the aligned dword holding their two scales.
+// Two floats as a bf16 pair (round to nearest even), lo in the low half.
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// One producer thread's global loads for one K step: 32 A values of each of
+// two rows, and 32 weight codes with the aligned dword holding their two
+// scales.
 struct Stage {
-  uint4 a[4];
+  uint4 a[2][4];
   uint4 c;
   uint32_t sc;   // the dword holding the two scales
   uint32_t ssh;  // their bit offset in it (0 or 16)
@@ -87,71 +100,97 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
   __shared__ __align__(16) uint16_t As[2][GM * LROW];
   __shared__ __align__(16) uint16_t Bs[2][GC * LROW];
 
-  const int tid = threadIdx.x;
-  // A staging: thread -> row ar, K half ah (32 values).  Rows beyond n load
-  // the last row (unbranched loads keep the wait counts exact) but are not
-  // written to LDS unless their 16-row block is live (their outputs are dropped)
-  const int ar = tid >> 1, ah = tid & 1;
-  const bool arow_live = ar < ((n + 15) & ~15);
-  const int p = p0 + min(ar, n - 1);
-  const int64_t arow = GATEUP ? (int64_t)(p < a.Tk ? perm[p] / a.k : p - a.Tk) : (int64_t)p;
-  const uint16_t* asrc = ain + arow * K;
-  // B staging (threads < 256, i.e. wavefronts 0..3): column bc, K half bh
-  const int bc = (tid >> 1) & (GC - 1), bh = tid & 1;
-  const int bmat = GATEUP ? bc / UPW : 2;
-  const int bunit = u0 + bc % UPW;
-  const bool bvalid = resident && bunit < units;
-  const int bunit_c = min(bunit, units - 1);
-  // a non-resident group reads the pool's first bytes (valid memory) and is
-  // zeroed through its scales
-  // (blob tiling in moe_common.hpp: chunk j of the column at crow + 256 j, its
-  // scales at sblk + blob_sc_off(j, nc, br))
-  const int nc = K / 32, br = bunit_c & 15;
-  // this row's offset in a scale group: 32 bytes per row in whole groups,
-  // 2 (nc % 16) in the last one when it is shorter
-  const uint32_t sfull = (uint32_t)br * 32u, stail = (uint32_t)br * 2u * (uint32_t)(nc & 15);
-  const int nfull = nc >> 4;
-  const uint8_t* crow = bvalid ? blob + a.off_codes[bmat] + (int64_t)(bunit_c >> 4) * (8 * K) + br * 16 : pool;
-  const uint8_t* sblk = bvalid ? blob + a.off_scales[bmat] + (int64_t)(bunit_c >> 4) * K : pool;
-  const bool loads_b = tid < 256;
+  // the output tile, staged for the epilogue in the A buffers
+  constexpr int OC = GATEUP ? GC / 2 : GC;  // output columns of the tile
+  constexpr int OSTR = OC + 8;              // uint16 per row: 16-byte pad, rows stay 16-byte aligned
+  static_assert(GM * OSTR <= 2 * GM * LROW, "output tile fits the A buffers");
+  uint16_t* os = &As[0][0];
 
-  // Every load stays inside its row: the K offset is clamped to the last
-  // 32 values, which only a half step beyond K (K % 64 == 32) needs; that
-  // half is zeroed when staged.
-  auto gload = [&](Stage& st, int s) {
-    const int sc_ = min(s, a.nk - 1);
-    const uint4* ap = reinterpret_cast<const uint4*>(asrc + min(sc_ * GK + ah * 32, K - 32));
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  // the step loop runs a multiple of 4 steps (the producers' register ring);
+  // steps past the end stage zeros
+  const int nk4 = (a.nk + 3) & ~3;
+
+  if (wave >= 4) {
+    // ---------------- producer ----------------
+    const int t = tid - 256;
+    // A staging: rows ar and ar + 128, K half ah (32 values each).  Rows beyond
+    // n load the last row (unbranched loads keep the wait counts exact) but are
+    // not written to LDS unless their 16-row block is live (their outputs are
+    // dropped)
+    const int ah = t & 1;
+    const int arow16 = (n + 15) & ~15;
+    int ar[2];
+    bool alive[2];
+    const uint16_t* asrc[2];
 #pragma unroll
-    for (int i = 0; i < 4; i++) st.a[i] = ap[i];
-    {
-      // every thread loads (threads >= 256 repeat those of tid - 256, from L2):
-      // an unbranched load keeps the wait counts exact
+    for (int h = 0; h < 2; h++) {
+      ar[h] = (t >> 1) + 128 * h;
+      alive[h] = ar[h] < arow16;
+      const int p = p0 + min(ar[h], n - 1);
+      const int64_t arow = GATEUP ? (int64_t)(p < a.Tk ? perm[p] / a.k : p - a.Tk) : (int64_t)p;
+      asrc[h] = ain + arow * K;
+    }
+    // B staging: column bc, K half bh
+    const int bc = t >> 1, bh = t & 1;
+    const int bmat = GATEUP ? bc / UPW : 2;
+    const int bunit = u0 + bc % UPW;
+    const bool bvalid = resident && bunit < units;
+    const int bunit_c = min(bunit, units - 1);
+    // a non-resident group reads the pool's first bytes (valid memory) and is
+    // zeroed through its scales
+    // (blob tiling in moe_common.hpp: chunk j of the column at crow + 256 j, its
+    // scales at sblk + blob_sc_off(j, nc, br))
+    const int nc = K / 32, br = bunit_c & 15;
+    // this row's offset in a scale group: 32 bytes per row in whole groups,
+    // 2 (nc % 16) in the last one when it is shorter
+    const uint32_t sfull = (uint32_t)br * 32u, stail = (uint32_t)br * 2u * (uint32_t)(nc & 15);
+    const int nfull = nc >> 4;
+    const uint8_t* crow = bvalid ? blob + a.off_codes[bmat] + (int64_t)(bunit_c >> 4) * (8 * K) + br * 16 : pool;
+    const uint8_t* sblk = bvalid ? blob + a.off_scales[bmat] + (int64_t)(bunit_c >> 4) * K : pool;
+
+    // Every load stays inside its row: the K offset is clamped to the last
+    // 32 values, which only a half step beyond K (K % 64 == 32) needs; that
+    // half is zeroed when staged.
+    auto gload = [&](Stage& st, int s) {
+      const int sc_ = min(s, a.nk - 1);
+      const int ko = min(sc_ * GK + ah * 32, K - 32);
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const uint4* ap = reinterpret_cast<const uint4*>(asrc[h] + ko);
+#pragma unroll
+        for (int i = 0; i < 4; i++) st.a[h][i] = ap[i];
+      }
       const int j = min(2 * sc_ + bh, nc - 1);
       st.c = *reinterpret_cast<const uint4*>(crow + (int64_t)j * 256);
       // the two scale bytes of these 32 values, from the aligned dword holding
       // them; the shift waits for the stage, so no wait is forced here
-      // blob_sc_off(j, nc, br) without a multiply in the loop
+      // (blob_sc_off(j, nc, br) without a multiply in the loop)
       const uint32_t so = (uint32_t)(j >> 4) * 512u + ((j >> 4) < nfull ? sfull : stail) + 2u * (uint32_t)(j & 15);
       st.sc = *reinterpret_cast<const uint32_t*>(sblk + (so & ~3u));
       st.ssh = 8u * (so & 2u);
-    }
-  };
-  auto stage = [&](const Stage& st, int buf, int s) {
-    // every loaded register is read here on every path (the stores below are
-    // branched): a load whose value only some paths read leaves the compiler
-    // unsure it has landed, and it then waits for all loads before reusing the
-    // register
+    };
+    auto stage = [&](const Stage& st, int buf, int s) {
+      // every loaded register is read here on every path (the stores below are
+      // branched): a load whose value only some paths read leaves the compiler
+      // unsure it has landed, and it then waits for all loads before reusing
+      // the register
 #pragma unroll
-    for (int i = 0; i < 4; i++) touch(st.a[i]);
-    touch(st.c);
-    asm volatile("" ::"v"(st.sc));
-    const bool kval = s * GK + ah * 32 < K;
-    uint4* ad = reinterpret_cast<uint4*>(&As[buf][ar * LROW + ah * 32]);
-    if (arow_live) {
+      for (int h = 0; h < 2; h++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) ad[i] = kval ? st.a[i] : make_uint4(0, 0, 0, 0);
-    }
-    if (loads_b) {
+        for (int i = 0; i < 4; i++) touch(st.a[h][i]);
+      touch(st.c);
+      asm volatile("" ::"v"(st.sc));
+      const bool kval = s * GK + ah * 32 < K;
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        uint4* ad = reinterpret_cast<uint4*>(&As[buf][ar[h] * LROW + ah * 32]);
+        if (alive[h]) {
+#pragma unroll
+          for (int i = 0; i < 4; i++) ad[i] = kval ? st.a[h][i] : make_uint4(0, 0, 0, 0);
+        }
+      }
       const uint32_t sw = (bvalid && s * GK + bh * 32 < K) ? st.sc >> st.ssh : 0u;
       const float s0 = e4m3_to_f32<0>(sw), s1 = e4m3_to_f32<1>(sw);
       bf16x8* bd = reinterpret_cast<bf16x8*>(&Bs[buf][bc * LROW + bh * 32]);
@@ -159,108 +198,147 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
       bd[1] = dequant8(st.c.y, s0);
       bd[2] = dequant8(st.c.z, s1);
       bd[3] = dequant8(st.c.w, s1);
+    };
+
+    // half-step h loads step h + 3 into stage (h + 3) % 4 and stages step h + 1
+    // (loaded two half-steps earlier) into LDS buffer (h + 1) % 2, while the
+    // consumers compute step h from buffer h % 2
+    // (four named stages, NST of them: an array of them is not kept in registers)
+    Stage st0, st1, st2, st3;
+    gload(st0, 0);
+    gload(st1, 1);
+    gload(st2, 2);
+    stage(st0, 0, 0);
+    __syncthreads();
+    for (int s = 0; s < nk4; s += 4) {
+      gload(st3, s + 3);
+      stage(st1, 1, s + 1);
+      __syncthreads();
+      gload(st0, s + 4);
+      stage(st2, 0, s + 2);
+      __syncthreads();
+      gload(st1, s + 5);
+      stage(st3, 1, s + 3);
+      __syncthreads();
+      gload(st2, s + 6);
+      stage(st0, 0, s + 4);
+      __syncthreads();
     }
-  };
+  } else {
 
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave & 3, wn = wave >> 2;
+  // ---------------- consumer ----------------
+  // the global scales, fetched now as a vector load: it has the whole loop to
+  // land (a scalar load would share the LDS wait counter)
+  int zero_v;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero_v));
+  const float4 gsc = *reinterpret_cast<const float4*>(blob + a.off_globals + zero_v);
+  const int wm = wave;
   const int r = lane & 15, q = lane >> 4;
-  // this wavefront's four 16-column blocks in the B tile; gate/up pairs the
-  // gate block cb with the up block cb + 2 (same units)
-  int bcol[4];
-#pragma unroll
-  for (int cb = 0; cb < 4; cb++) bcol[cb] = GATEUP ? (cb >> 1) * UPW + 32 * wn + 16 * (cb & 1) : 64 * wn + 16 * cb;
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Row block rb of this wavefront is rows 64 rb + 16 wm .. + 15: the four
   // SIMDs take turns over 16-row blocks, so a chunk of n < 256 rows leaves them
-  // evenly loaded, and the blocks at or past n are skipped (nrb live blocks).
-  const int nrb = max(0, min(4, (n - 16 * wm + 63) >> 6));
-  auto compute_n = [&](auto nrb_c, int buf) {
+  // evenly loaded, and the blocks at or past n are skipped.  The consumer is
+  // instantiated per count of live blocks (NRB), each with its own
+  // accumulators, so no accumulator is merged across code paths.
+  // The wavefront's eight 16-column blocks of the B tile: gate/up pairs the
+  // gate block cb with the up block cb + 4 (same units).
+  auto consume = [&](auto nrb_c) __attribute__((always_inline)) {
     constexpr int NRB = decltype(nrb_c)::value;
+    f32x4 acc[NRB][8];
 #pragma unroll
-    for (int ks = 0; ks < 2; ks++) {
-      bf16x8 fa[NRB], fb[4];
+    for (int i = 0; i < NRB; i++)
 #pragma unroll
-      for (int rb = 0; rb < NRB; rb++)
-        fa[rb] = *reinterpret_cast<const bf16x8*>(&As[buf][(64 * rb + 16 * wm + r) * LROW + 32 * ks + 8 * q]);
+      for (int j = 0; j < 8; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-      for (int cb = 0; cb < 4; cb++)
-        fb[cb] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(bcol[cb] + r) * LROW + 32 * ks + 8 * q]);
+      for (int ks = 0; ks < 2; ks++) {
+        bf16x8 fa[NRB], fb[8];
 #pragma unroll
-      for (int rb = 0; rb < NRB; rb++)
+        for (int rb = 0; rb < NRB; rb++)
+          fa[rb] = *reinterpret_cast<const bf16x8*>(&As[buf][(64 * rb + 16 * wm + r) * LROW + 32 * ks + 8 * q]);
 #pragma unroll
-        for (int cb = 0; cb < 4; cb++) acc[rb][cb] = mfma16x16x32(fa[rb], fb[cb], acc[rb][cb]);
-    }
-  };
-  auto compute = [&](int buf) {
-    switch (nrb) {
-      case 4: compute_n(std::integral_constant<int, 4>{}, buf); break;
-      case 3: compute_n(std::integral_constant<int, 3>{}, buf); break;
-      case 2: compute_n(std::integral_constant<int, 2>{}, buf); break;
-      case 1: compute_n(std::integral_constant<int, 1>{}, buf); break;
-      default: break;
-    }
-  };
-
-  // two register stages in flight ahead of the LDS buffer being computed
-  Stage st0, st1;
-  gload(st0, 0);
-  gload(st1, 1);
-  stage(st0, 0, 0);
-  __syncthreads();
-  // (the scheduling barriers keep each step's loads ahead of its MFMAs, so
-  // they have a step and a half to land)
-  // (an odd step count runs one more step, of zeros: its K lies past the end,
-  // which staging zeroes; the loop then has no exit in its middle)
-  const int nke = (a.nk + 1) & ~1;
-  for (int s = 0; s < nke; s += 2) {
-    gload(st0, s + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(0);
-    stage(st1, 1, s + 1);
+        for (int cb = 0; cb < 8; cb++)
+          fb[cb] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(16 * cb + r) * LROW + 32 * ks + 8 * q]);
+#pragma unroll
+        for (int rb = 0; rb < NRB; rb++)
+#pragma unroll
+          for (int cb = 0; cb < 8; cb++) acc[rb][cb] = mfma16x16x32(fa[rb], fb[cb], acc[rb][cb]);
+      }
+    };
+    // one barrier per step, as the producers have
     __syncthreads();
-    gload(st1, s + 3);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(1);
-    stage(st0, 0, s + 2);
-    __syncthreads();
-  }
-
-  // epilogue: D[i][j] of block (rb, cb) is in lane j + 16 (i / 4), element i % 4
-  cptr<float> glob = as_const(reinterpret_cast<const float*>(blob + a.off_globals));
-  const float g0 = resident ? glob[GATEUP ? 0 : 2] : 0.f;
-  const float g1 = (GATEUP && resident) ? glob[1] : 0.f;
+    for (int s = 0; s < nk4; s += 2) {
+      compute(0);
+      __syncthreads();
+      compute(1);
+      __syncthreads();
+    }
+    // epilogue, part 1: D[i][j] of block (rb, cb) is in lane j + 16 (i / 4),
+    // element i % 4, so a lane holds rows 4q .. 4q + 3 of column r.  Adjacent
+    // lanes swap two of their four bf16 results (one DPP move): the even lane
+    // then holds rows 4q and 4q + 2, the odd lane rows 4q + 1 and 4q + 3, each
+    // as a pair of columns, written to the output tile in LDS (the A buffers,
+    // free after the last step's barrier).
+    const float g0 = resident ? (GATEUP ? gsc.x : gsc.z) : 0.f;
+    const float g1 = (GATEUP && resident) ? gsc.y : 0.f;
+    const bool odd = r & 1;
 #pragma unroll
-  for (int rb = 0; rb < 4; rb++) {
+    for (int rb = 0; rb < NRB; rb++) {
 #pragma unroll
-    for (int e4 = 0; e4 < 4; e4++) {
-      const int row = 64 * rb + 16 * wm + 4 * q + e4;
-      if (row >= n) continue;
-      uint16_t* orow = out + (int64_t)(p0 + row) * units;
-      if (GATEUP) {
+      for (int oc = 0; oc < OC / 16; oc++) {
+        float v[4];
 #pragma unroll
-        for (int cb = 0; cb < 2; cb++) {
-          const int unit = u0 + 32 * wn + 16 * cb + r;
-          if (unit >= units) continue;
-          const float gv = g0 * acc[rb][cb][e4];
-          const float uv = g1 * acc[rb][cb + 2][e4];
-          orow[unit] = f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv);
+        for (int e4 = 0; e4 < 4; e4++) {
+          if (GATEUP) {
+            // silu(g) u = g u / (1 + e^-g): v_exp_f32 and v_rcp_f32 (errors of
+            // a few fp32 ulp, far below the bf16 rounding of h)
+            const float gv = g0 * acc[rb][oc][e4];
+            const float uv = g1 * acc[rb][oc + 4][e4];
+            v[e4] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+          } else {
+            v[e4] = g0 * acc[rb][oc][e4];
+          }
         }
-      } else {
-#pragma unroll
-        for (int cb = 0; cb < 4; cb++) {
-          const int unit = u0 + 64 * wn + 16 * cb + r;
-          if (unit >= units) continue;
-          orow[unit] = f32_to_bf16_rne(g0 * acc[rb][cb][e4]);
-        }
+        // what the partner lane needs: rows 4q + 1, 4q + 3 (to the even lane)
+        // or rows 4q, 4q + 2 (to the odd lane) of this lane's column
+        const uint32_t send = odd ? pack_bf16(v[0], v[2]) : pack_bf16(v[1], v[3]);
+        const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+        const uint32_t mine = odd ? pack_bf16(v[1], v[3]) : pack_bf16(v[0], v[2]);
+        // row pair words: low half = even column
+        const uint32_t w0 = odd ? ((recv & 0xFFFFu) | (mine << 16)) : ((mine & 0xFFFFu) | (recv << 16));
+        const uint32_t w1 = odd ? ((recv >> 16) | (mine & 0xFFFF0000u)) : ((mine >> 16) | (recv & 0xFFFF0000u));
+        const int row = 64 * rb + 16 * wm + 4 * q + (odd ? 1 : 0);
+        const int col = 16 * oc + (r & ~1);
+        *reinterpret_cast<uint32_t*>(&os[row * OSTR + col]) = w0;
+        *reinterpret_cast<uint32_t*>(&os[(row + 2) * OSTR + col]) = w1;
       }
     }
+  };
+  switch (max(0, min(4, (n - 16 * wm + 63) >> 6))) {
+    case 4: consume(std::integral_constant<int, 4>{}); break;
+    case 3: consume(std::integral_constant<int, 3>{}); break;
+    case 2: consume(std::integral_constant<int, 2>{}); break;
+    case 1: consume(std::integral_constant<int, 1>{}); break;
+    default:  // no live rows: the barriers only
+      __syncthreads();
+      for (int s = 0; s < nk4; s += 2) {
+        __syncthreads();
+        __syncthreads();
+      }
+  }
+  }
+
+  // epilogue, part 2 (all eight wavefronts): the tile leaves in 16-byte row
+  // segments (units come in multiples of 16)
+  __syncthreads();
+  constexpr int SEGS = OC / 8;
+#pragma unroll 4
+  for (int i = tid; i < n * SEGS; i += GT) {
+    const int row = i / SEGS, sg = i % SEGS;
+    const int unit = u0 + 8 * sg;
+    if (unit < units)
+      *reinterpret_cast<uint4*>(out + (int64_t)(p0 + row) * units + unit) =
+          *reinterpret_cast<const uint4*>(&os[row * OSTR + 8 * sg]);
   }
 }
 
