@@ -282,6 +282,10 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
     const float g0 = resident ? (GATEUP ? gsc.x : gsc.z) : 0.f;
     const float g1 = (GATEUP && resident) ? gsc.y : 0.f;
     const bool odd = r & 1;
+    // byte selectors over {recv: bytes 4..7, mine: bytes 0..3}, low column
+    // first: the even lane's words are (mine, recv), the odd lane's (recv, mine)
+    const uint32_t sel0 = odd ? 0x01000504u : 0x05040100u;  // the low halves: rows 4q / 4q + 1
+    const uint32_t sel1 = odd ? 0x03020706u : 0x07060302u;  // the high halves: rows 4q + 2 / 4q + 3
 #pragma unroll
     for (int rb = 0; rb < NRB; rb++) {
 #pragma unroll
@@ -299,14 +303,15 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
             v[e4] = g0 * acc[rb][oc][e4];
           }
         }
-        // what the partner lane needs: rows 4q + 1, 4q + 3 (to the even lane)
-        // or rows 4q, 4q + 2 (to the odd lane) of this lane's column
-        const uint32_t send = odd ? pack_bf16(v[0], v[2]) : pack_bf16(v[1], v[3]);
+        // pa: rows 4q, 4q + 2 of this lane's column; pb: rows 4q + 1, 4q + 3.
+        // The lane sends its partner the pair the partner keeps (the even lane
+        // keeps pa), then merges the received halves with its own: one byte
+        // permute whose selector depends only on the lane's parity.
+        const uint32_t pa = pack_bf16(v[0], v[2]), pb = pack_bf16(v[1], v[3]);
+        const uint32_t send = odd ? pa : pb, mine = odd ? pb : pa;
         const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-        const uint32_t mine = odd ? pack_bf16(v[1], v[3]) : pack_bf16(v[0], v[2]);
-        // row pair words: low half = even column
-        const uint32_t w0 = odd ? ((recv & 0xFFFFu) | (mine << 16)) : ((mine & 0xFFFFu) | (recv << 16));
-        const uint32_t w1 = odd ? ((recv >> 16) | (mine & 0xFFFF0000u)) : ((mine >> 16) | (recv & 0xFFFF0000u));
+        const uint32_t w0 = __builtin_amdgcn_perm(recv, mine, sel0);
+        const uint32_t w1 = __builtin_amdgcn_perm(recv, mine, sel1);
         const int row = 64 * rb + 16 * wm + 4 * q + (odd ? 1 : 0);
         const int col = 16 * oc + (r & ~1);
         *reinterpret_cast<uint32_t*>(&os[row * OSTR + col]) = w0;
