@@ -269,3 +269,45 @@ def test_group_matches_oracle_on_drawn_ids(B, T, k, E, zs):
     assert np.array_equal(buf.perm.cpu().numpy(), g.perm)
     assert np.array_equal(buf.inv_perm.cpu().numpy(), g.inv_perm)
     assert np.array_equal(buf.group_slot.cpu().numpy(), st.cpu().numpy()[0])
+
+
+# (T, E, k): the radix select with 8, 2 and 16 keys per lane, k above 64 (two
+# entries per lane to rank), k above 128 (the one-winner-per-round path), and
+# the fused decode kernel (T <= 16, T k <= 256)
+@pytest.mark.parametrize("T,E,k", [(64, 512, 10), (40, 100, 70), (8, 512, 200), (4, 512, 10), (16, 256, 6),
+                                   (33, 1024, 8)])
+def test_topk_with_ties_matches_oracle(B, T, E, k):
+    """Drawn logits on a half-unit grid tie everywhere; the winners and their
+    slot order (logit descending, lower expert index first among equal
+    logits, -0 equal to +0) match the oracle's top-k exactly, and the weights
+    match its softmax."""
+    from moe_expert_ffn_top_amd.layer import LayerBuffers
+    say("[gpu] top-k ties case T=%d E=%d k=%d" % (T, E, k))
+    rng = np.random.default_rng(T * 7 + E + k)
+    lg = (np.round(rng.normal(size=(T, E)) * 2) / 2).astype(np.float32)
+    lg[0, :] = 0.25                       # one value everywhere
+    if T > 1:
+        lg[1, 0::2] = -0.0                # the two zeros tie
+        lg[1, 1::2] = 0.0
+    want_ids = O.topk(lg, k)
+    want_w = O.topk_weights(lg, want_ids)
+    d = B.Dims(T, 64, 32, E, k, 1)
+    x = torch.zeros((T, 64), dtype=torch.bfloat16, device="cuda")
+    wsg = torch.zeros(64, dtype=torch.float32, device="cuda")
+    lg_t = torch.from_numpy(lg).cuda()
+    buf = LayerBuffers.allocate(d)
+    B.moe_route(d, x, None, lg_t, wsg, None, buf.ids, buf.w, buf.sigma)
+    torch.cuda.synchronize()
+    assert np.array_equal(buf.ids.cpu().numpy(), want_ids)
+    assert np.max(np.abs(buf.w.cpu().numpy().astype(np.float64) - want_w)) <= 1e-6
+    if T <= 16 and T * k <= 256:
+        st = torch.arange(E + 1, dtype=torch.int32, device="cuda").view(1, E + 1).contiguous()
+        buf.ids.fill_(-7)
+        buf.status.zero_()
+        B.moe_route_group(d, 0, x, None, lg_t, wsg, None, buf.ids, buf.w, buf.sigma, st, E + 1, buf.offsets,
+                          buf.perm, buf.inv_perm, buf.group_slot, buf.status, buf.ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(buf.ids.cpu().numpy(), want_ids)
+        assert int(buf.status.item()) == 0
+        g = O.group(want_ids, E)
+        assert np.array_equal(buf.perm.cpu().numpy(), g.perm)
