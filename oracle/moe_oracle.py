@@ -42,6 +42,12 @@ What it computes, step by step, and where each step is defined:
   8. Combine — [Strata] "路由以后，专家怎样分工？" and "少算这些专家，会付出什么代价？":
      y_t = bf16( sum_j w_j Y[row(t, j)] + sigma_t Y_shared[t] ) (rounding point
      R2), with no renormalisation.
+  9. Route tail-skip (a variant) — [Strata] "少算这些专家，会付出什么代价？" and the
+     skip-condition passage just before it: with a rank threshold R (default 7,
+     ranks counted from zero), an expert that is not resident is skipped when
+     every token of the window that picked it ranks it R or later.  A skipped
+     expert's rows are zero and the kept weights are not renormalised, so the
+     output moves by exactly -sum of the skipped w_i E_i(x).
 
 bf16 rounding is round-to-nearest-even from the exact fp64 value (no detour
 through fp32).  Parity pins for every function live in tests/test_oracle_*.py.
@@ -320,6 +326,31 @@ def combine(y_routed: np.ndarray, w: np.ndarray, sigma: np.ndarray, y_shared: np
 
 
 # ---------------------------------------------------------------------------
+# 9. Route tail-skip (variant)
+# ---------------------------------------------------------------------------
+
+def tail_skip(ids: np.ndarray, resident: np.ndarray, skip_rank: int) -> np.ndarray:
+    """The experts one window skips (bool [E]).
+
+    ids: int [T, k] of the window's tokens (slot j = rank j, from zero);
+    resident: bool [E].  Expert e is skipped when it is not resident, some token
+    picked it, and every token that picked it ranks it at skip_rank or later.
+    A single token ranking it earlier keeps it; a resident expert is always
+    kept; skip_rank <= 0 skips nothing."""
+    ids = np.asarray(ids)
+    E = len(resident)
+    out = np.zeros(E, dtype=bool)
+    if skip_rank <= 0:
+        return out
+    for e in range(E):
+        if resident[e]:
+            continue
+        ranks = [j for t in range(ids.shape[0]) for j in range(ids.shape[1]) if ids[t, j] == e]
+        out[e] = len(ranks) > 0 and min(ranks) >= skip_rank
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Whole layer
 # ---------------------------------------------------------------------------
 
@@ -342,14 +373,17 @@ class LayerResult:
 def moe_layer(x_bits: np.ndarray, blob_of: Callable[[int], bytes], H: int, I: int, E: int, k: int,
               w_shared_gate: np.ndarray, w_router: Optional[np.ndarray] = None,
               logits: Optional[np.ndarray] = None, tokens: Optional[Sequence[int]] = None,
-              dense_weights: Optional[Dict[int, tuple]] = None) -> LayerResult:
+              dense_weights: Optional[Dict[int, tuple]] = None,
+              skip: Optional[np.ndarray] = None) -> LayerResult:
     """One MoE layer.
 
     x_bits: uint16 bf16 bits [T, H].  blob_of(e) returns the blob bytes of
     expert e (e == E is the shared expert).  Exactly one of w_router / logits.
     Routing and grouping cover every token; the FFN rows and the combine are
     computed for `tokens` (default: all), since a token's output depends only
-    on its own row, its routing and the expert bytes.
+    on its own row, its routing and the expert bytes.  skip (bool [E], see
+    tail_skip): the routed rows of a skipped expert are zero (h and Y), so its
+    terms drop out of the combine and the other weights stay as they are.
     """
     assert (w_router is None) != (logits is None)
     T = x_bits.shape[0]
@@ -380,6 +414,11 @@ def moe_layer(x_bits: np.ndarray, blob_of: Callable[[int], bytes], H: int, I: in
         need.setdefault(E, []).append((T * k + int(t), int(t)))
     for e in sorted(need):
         rows = need[e]
+        if skip is not None and e < E and skip[e]:
+            for p, _ in rows:
+                res.h_pre[p] = res.h[p] = np.zeros(I)
+                res.y_rows_pre[p] = res.y_rows[p] = np.zeros(H)
+            continue
         wg, wu, wd = weights(e)
         out = expert_ffn(x[[t for _, t in rows]], wg, wu, wd)
         for i, (p, _) in enumerate(rows):
