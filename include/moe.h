@@ -69,6 +69,7 @@ typedef struct ihipStream_t* moe_stream_t;
 #define MOE_DEV_BAD_EXPERT_ID 1   /* a topk id outside [0, E): its row is dropped */
 #define MOE_DEV_NOT_RESIDENT 2    /* a non-empty group's slot is -1: rows are zero */
 #define MOE_DEV_BAD_SLOT 4        /* a slot index >= n_slots: rows are zero */
+#define MOE_DEV_TAIL_SKIPPED 8    /* moe_group_tail_skip skipped a group (rows zero) */
 
 const char* moe_status_string(int status);
 /* Detail of the last error returned on the calling thread ("" if none). */
@@ -194,6 +195,28 @@ int moe_group(const moe_dims* d, int32_t layer, const int32_t* topk_ids,
               int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
               int32_t* dev_status, void* ws, uint64_t ws_bytes,
               moe_stream_t stream);
+
+/* ---- S3 with the route tail-skip (a variant) ---------------------------
+ * [Strata] "少算这些专家，会付出什么代价？" and the skip-condition passage before it
+ * (default threshold 7, ranks from zero; the kept experts' weights are not
+ * renormalised).
+ *
+ * moe_group with one more rule, over the T tokens of this call (the window):
+ * a routed expert that is not resident (slot -1) and that every token of the
+ * window that picked it ranks at skip_rank or later (slot j >= skip_rank) is
+ * skipped.  Its rows are zero as for any non-resident group and moe_combine
+ * adds nothing for them, so the output moves by exactly the skipped w_j E_j(x)
+ * terms; it sets MOE_DEV_TAIL_SKIPPED instead of MOE_DEV_NOT_RESIDENT.  A
+ * non-resident expert that some token ranks earlier still sets
+ * MOE_DEV_NOT_RESIDENT.  skip_rank <= 0 (or >= k) skips nothing.
+ * n_skipped  device int32 [1] or NULL: receives the number of skipped experts.
+ * Every other argument, the validation and the results are moe_group's.
+ */
+int moe_group_tail_skip(const moe_dims* d, int32_t layer, const int32_t* topk_ids,
+                        const int32_t* slot_table, int32_t n_slots, int32_t skip_rank,
+                        int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                        int32_t* group_slot, int32_t* dev_status, int32_t* n_skipped,
+                        void* ws, uint64_t ws_bytes, moe_stream_t stream);
 
 /* ---- S1 + S2 + S3 together ---------------------------------------------
  * moe_route followed by moe_group on the same stream, with exactly their

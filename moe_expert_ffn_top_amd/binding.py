@@ -30,10 +30,11 @@ MOE_ERR_STATE = -7
 MOE_DEV_BAD_EXPERT_ID = 1
 MOE_DEV_NOT_RESIDENT = 2
 MOE_DEV_BAD_SLOT = 4
+MOE_DEV_TAIL_SKIPPED = 8
 
 #: every symbol include/moe.h declares
 EXPORTED = ("moe_status_string", "moe_last_error", "moe_version", "moe_blob_layout_init", "moe_workspace_bytes",
-            "moe_route", "moe_group", "moe_route_group", "moe_expert_ffn", "moe_expert_ffn_stages", "moe_combine",
+            "moe_route", "moe_group", "moe_group_tail_skip", "moe_route_group", "moe_expert_ffn", "moe_expert_ffn_stages", "moe_combine",
             "moe_ring_create", "moe_stage_h2d", "moe_ring_acquire", "moe_ring_release", "moe_ring_slot_ptr",
             "moe_ring_destroy")
 
@@ -73,6 +74,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.moe_workspace_bytes.argtypes = [_DP, ctypes.POINTER(_u64)]
     lib.moe_route.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.moe_group.argtypes = [_DP, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _u64, _vp]
+    lib.moe_group_tail_skip.argtypes = [_DP, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _u64,
+                                        _vp]
     lib.moe_route_group.argtypes = [_DP, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _u64, _vp]
     lib.moe_expert_ffn.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _vp, _vp,
@@ -155,6 +158,15 @@ def moe_group(dims, layer, topk_ids, slot_table, n_slots, offsets, perm, inv_per
         ws_bytes = ws.numel() * ws.element_size()
     _check(_lib.moe_group(ctypes.byref(dims), layer, _p(topk_ids), _p(slot_table), n_slots, _p(offsets), _p(perm),
                           _p(inv_perm), _p(group_slot), _p(dev_status), _p(ws), ws_bytes, _s(stream)), "moe_group")
+
+
+def moe_group_tail_skip(dims, layer, topk_ids, slot_table, n_slots, skip_rank, offsets, perm, inv_perm, group_slot,
+                        dev_status, n_skipped, ws, ws_bytes: Optional[int] = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.moe_group_tail_skip(ctypes.byref(dims), layer, _p(topk_ids), _p(slot_table), n_slots, skip_rank,
+                                    _p(offsets), _p(perm), _p(inv_perm), _p(group_slot), _p(dev_status),
+                                    _p(n_skipped), _p(ws), ws_bytes, _s(stream)), "moe_group_tail_skip")
 
 
 def moe_route_group(dims, layer, x, w_router, logits_in, w_shared_gate, logits_out, topk_ids, topk_w, shared_sigma,

@@ -206,6 +206,19 @@ int moe_group(const moe_dims* d, int32_t layer, const int32_t* topk_ids, const i
                     "group launch");
 }
 
+int moe_group_tail_skip(const moe_dims* d, int32_t layer, const int32_t* topk_ids, const int32_t* slot_table,
+                        int32_t n_slots, int32_t skip_rank, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                        int32_t* group_slot, int32_t* dev_status, int32_t* n_skipped, void* ws, uint64_t ws_bytes,
+                        moe_stream_t stream) {
+  int r = validate_group(d, layer, topk_ids, slot_table, n_slots, offsets, perm, inv_perm, group_slot, dev_status, ws,
+                         ws_bytes);
+  if (r) return r;
+  if (n_skipped) REQUIRE(n_skipped, 4, "n_skipped");
+  return hip_status(moe::launch_group(*d, layer, topk_ids, slot_table, n_slots, offsets, perm, inv_perm, group_slot,
+                                      dev_status, ws, reinterpret_cast<hipStream_t>(stream), skip_rank, n_skipped),
+                    "group launch");
+}
+
 int moe_route_group(const moe_dims* d, int32_t layer, const uint16_t* x, const float* w_router,
                     const float* logits_in, const float* w_shared_gate, float* logits_out, int32_t* topk_ids,
                     float* topk_w, float* shared_sigma, const int32_t* slot_table, int32_t n_slots,

@@ -33,26 +33,39 @@ constexpr int kBlk = 256;
 
 constexpr int kParts = kCntBlk / kBlk;  // 256-entry parts per counting block
 
-__global__ __launch_bounds__(kBlk) void k_count(const int32_t* __restrict__ ids, int64_t F, int E,
-                                                int32_t* __restrict__ cnt, int32_t* __restrict__ status) {
+// With the tail-skip rule (skip_rank > 0) also each expert's lowest slot rank
+// in the block, into mrk [ncb][E] (k where the block has none).
+__global__ __launch_bounds__(kBlk) void k_count(const int32_t* __restrict__ ids, int64_t F, int E, int k,
+                                                int skip_rank, int32_t* __restrict__ cnt, int32_t* __restrict__ mrk,
+                                                int32_t* __restrict__ status) {
   __shared__ int32_t hist[1024];
+  __shared__ int32_t mr[1024];
   int ev[kParts];
 #pragma unroll
   for (int j = 0; j < kParts; j++) {
     const int64_t f = (int64_t)blockIdx.x * kCntBlk + j * kBlk + threadIdx.x;
     ev[j] = f < F ? ids[f] : 0;
   }
-  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    hist[e] = 0;
+    mr[e] = k;
+  }
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < kParts; j++) {
     const int64_t f = (int64_t)blockIdx.x * kCntBlk + j * kBlk + threadIdx.x;
     if (f < F) {
-      if (ev[j] >= 0 && ev[j] < E) atomicAdd(&hist[ev[j]], 1);
-      else atomicOr(status, MOE_DEV_BAD_EXPERT_ID);
+      if (ev[j] >= 0 && ev[j] < E) {
+        atomicAdd(&hist[ev[j]], 1);
+        if (skip_rank > 0) atomicMin(&mr[ev[j]], (int)(f % k));
+      } else {
+        atomicOr(status, MOE_DEV_BAD_EXPERT_ID);
+      }
     }
   }
   __syncthreads();
+  if (skip_rank > 0)
+    for (int e = threadIdx.x; e < E; e += blockDim.x) mrk[(int64_t)blockIdx.x * E + e] = mr[e];
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
@@ -96,20 +109,32 @@ __device__ int block_exclusive_scan(int v, int* lds16, int* total) {
 // slot; the caller loads both at its start, so their latency overlaps its own.
 // `chunks` (or null): the grouped-GEMM work list, written in place of the
 // tile lists when the FFN will run as a GEMM; *tbase_out is then not set.
+// Tail-skip (skip_rank > 0): thread e's expert, when it is not resident and
+// minrank (its lowest slot rank in the window) is skip_rank or more, is
+// skipped: its rows are zero like any non-resident group's, it sets
+// MOE_DEV_TAIL_SKIPPED instead of MOE_DEV_NOT_RESIDENT, and *n_skipped (if
+// set) receives the number of skipped experts.
 __device__ int scan_and_tiles(int count, int T, int k, int E, int slot, int ss, int32_t n_slots,
                               int32_t* __restrict__ offsets, int32_t* __restrict__ group_slot,
                               int32_t* __restrict__ status, int32_t* __restrict__ meta, int4* __restrict__ tiles,
                               int32_t* __restrict__ tile_tok, int32_t* __restrict__ tile_base, int4* __restrict__ chunks,
-                              int* lds17, int* tbase_out = nullptr) {
+                              int* lds17, int* tbase_out = nullptr, int minrank = 0, int skip_rank = 0,
+                              int32_t* __restrict__ n_skipped = nullptr) {
   const int e = threadIdx.x;
   int total = 0;
   const int off = block_exclusive_scan(count, lds17, &total);
   const int64_t Tk = (int64_t)T * k;
+  const bool skipped = skip_rank > 0 && e < E && count > 0 && slot < 0 && minrank >= skip_rank;
   if (e < E) {
     offsets[e] = off;
     group_slot[e] = slot;
-    if (count > 0 && slot < 0) atomicOr(status, MOE_DEV_NOT_RESIDENT);
+    if (count > 0 && slot < 0) atomicOr(status, skipped ? MOE_DEV_TAIL_SKIPPED : MOE_DEV_NOT_RESIDENT);
     if (count > 0 && slot >= n_slots) atomicOr(status, MOE_DEV_BAD_SLOT);
+  }
+  if (n_skipped) {  // uniform: every thread of the block takes this branch or none does
+    int ns = 0;
+    block_exclusive_scan(skipped ? 1 : 0, lds17, &ns);
+    if (threadIdx.x == 0) *n_skipped = ns;
   }
   if (e == 0) {
     offsets[E] = total;
@@ -169,7 +194,8 @@ __global__ __launch_bounds__(1024) void k_scan(int64_t ncb, int T, int k, int E,
                                                int32_t* __restrict__ group_slot, int32_t* __restrict__ status,
                                                int32_t* __restrict__ meta, int4* __restrict__ tiles,
                                                int32_t* __restrict__ tile_tok, int32_t* __restrict__ tile_base,
-                                               int4* __restrict__ chunks) {
+                                               int4* __restrict__ chunks, int skip_rank,
+                                               const int32_t* __restrict__ mrk, int32_t* __restrict__ n_skipped) {
   using vec = typename std::conditional<V == 4, int4, int>::type;
   constexpr int kBatch = 16;
   __shared__ int lds[17];
@@ -245,8 +271,12 @@ __global__ __launch_bounds__(1024) void k_scan(int64_t ncb, int T, int k, int E,
       if (b + i < nrow) col[(b + i) * rs] = c[i];
     }
   }
+  // tail-skip: expert tid's lowest slot rank over the counting blocks
+  int minrank = k;
+  if (skip_rank > 0 && tid < E)
+    for (int64_t b = 0; b < ncb; b++) minrank = min(minrank, mrk[b * E + tid]);
   scan_and_tiles(count, T, k, E, slot, ss, n_slots, offsets, group_slot, status, meta, tiles, tile_tok, tile_base,
-                 chunks, lds);
+                 chunks, lds, nullptr, minrank, skip_rank, n_skipped);
 }
 
 // Token of routed row p (flat index f) into its tile's row table; the first
@@ -278,16 +308,22 @@ __device__ inline void group_small_tail(int e_mine, int F, int T, int k, int E, 
                                         int32_t* __restrict__ status, int32_t* __restrict__ meta,
                                         int4* __restrict__ tiles, int32_t* __restrict__ tile_tok,
                                         int32_t* __restrict__ tile_base, int4* __restrict__ chunks, int32_t* hist,
-                                        int32_t* cntl, int32_t* tbl, const int32_t* sid, int* lds) {
+                                        int32_t* cntl, int32_t* tbl, const int32_t* sid, int* lds,
+                                        int32_t* minr = nullptr, int skip_rank = 0,
+                                        int32_t* __restrict__ n_skipped = nullptr) {
   const int tid = threadIdx.x;
-  if (e_mine >= 0) atomicAdd(&hist[e_mine], 1);
+  if (e_mine >= 0) {
+    atomicAdd(&hist[e_mine], 1);
+    if (skip_rank > 0) atomicMin(&minr[e_mine], tid % k);  // minr[e] = k beforehand
+  }
   __syncthreads();
   const int count = tid < E ? hist[tid] : 0;
+  const int minrank = (skip_rank > 0 && tid < E) ? minr[tid] : k;
   if (tid < E) cntl[tid] = count;
   int tb = 0;
   STAGE_STAMP(1, 2);
   const int off = scan_and_tiles(count, T, k, E, slot, ss, n_slots, offsets, group_slot, status, meta, tiles,
-                                 tile_tok, tile_base, chunks, lds, &tb);
+                                 tile_tok, tile_base, chunks, lds, &tb, minrank, skip_rank, n_skipped);
   STAGE_STAMP(1, 3);
   if (tid < E) {
     hist[tid] = off;  // hist now holds each expert's first row
@@ -329,17 +365,22 @@ __global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict_
                                                       int32_t* __restrict__ group_slot, int32_t* __restrict__ status,
                                                       int32_t* __restrict__ meta, int4* __restrict__ tiles,
                                                       int32_t* __restrict__ tile_tok,
-                                                      int32_t* __restrict__ tile_base, int4* __restrict__ chunks) {
+                                                      int32_t* __restrict__ tile_base, int4* __restrict__ chunks,
+                                                      int skip_rank, int32_t* __restrict__ n_skipped) {
   __shared__ int32_t hist[1024];
   __shared__ int32_t cntl[1024];
   __shared__ int32_t tbl[1024];
+  __shared__ int32_t minr[1024];
   __shared__ __align__(16) int32_t sid[kSmallF];
   __shared__ int lds[17];
   const int tid = threadIdx.x;
   STAGE_STAMP(1, 0);
   const int slot = tid < E ? slot_table[(int64_t)layer * (E + 1) + tid] : -1;
   const int ss = slot_table[(int64_t)layer * (E + 1) + E];
-  if (tid < E) hist[tid] = 0;
+  if (tid < E) {
+    hist[tid] = 0;
+    minr[tid] = k;
+  }
   int e_mine = -1;
   if (tid < F) {
     e_mine = ids[tid];
@@ -352,7 +393,7 @@ __global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict_
   __syncthreads();
   STAGE_STAMP(1, 1);
   group_small_tail(e_mine, F, T, k, E, slot, ss, n_slots, offsets, perm, inv_perm, group_slot, status, meta, tiles,
-                   tile_tok, tile_base, chunks, hist, cntl, tbl, sid, lds);
+                   tile_tok, tile_base, chunks, hist, cntl, tbl, sid, lds, minr, skip_rank, n_skipped);
 }
 
 // Route and group fused for small windows (T <= 16 tokens, T*k <= kSmallF,
@@ -436,7 +477,7 @@ __global__ __launch_bounds__(kBlk) void k_scatter(const int32_t* __restrict__ id
 
 hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, const int32_t* slot_table,
                         int32_t n_slots, int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
-                        int32_t* dev_status, void* ws, hipStream_t s) {
+                        int32_t* dev_status, void* ws, hipStream_t s, int32_t skip_rank, int32_t* n_skipped) {
   const WsLayout wl = ws_layout(d);
   const int64_t F = (int64_t)d.T * d.k;
   uint8_t* base = static_cast<uint8_t*>(ws);
@@ -449,13 +490,16 @@ hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, co
   if (F <= kSmallF) {
     hipLaunchKernelGGL(k_group_small, dim3(1), dim3(1024), 0, s, ids, (int)F, d.T, d.k, d.E, layer, slot_table,
                        n_slots, offsets, perm, inv_perm, group_slot, dev_status, meta, tiles, tile_tok, tile_base,
-                       chunks);
+                       chunks, skip_rank, n_skipped);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_count, dim3((unsigned)wl.ncb), dim3(kBlk), 0, s, ids, F, d.E, cnt, dev_status);
+  int32_t* mrk = reinterpret_cast<int32_t*>(base + wl.off_mrk);
+  hipLaunchKernelGGL(k_count, dim3((unsigned)wl.ncb), dim3(kBlk), 0, s, ids, F, d.E, d.k, skip_rank, cnt, mrk,
+                     dev_status);
   auto scan = d.E % 4 == 0 ? k_scan<4> : k_scan<1>;
   hipLaunchKernelGGL(scan, dim3(1), dim3(1024), 0, s, wl.ncb, d.T, d.k, d.E, layer, slot_table, n_slots, cnt,
-                     offsets, group_slot, dev_status, meta, tiles, tile_tok, tile_base, chunks);
+                     offsets, group_slot, dev_status, meta, tiles, tile_tok, tile_base, chunks, skip_rank, mrk,
+                     n_skipped);
   hipLaunchKernelGGL(k_scatter, dim3((unsigned)wl.nb), dim3(kBlk), 0, s, ids, F, d.E, d.k, cnt, offsets, perm, inv_perm,
                      chunks ? nullptr : tile_tok, tile_base);
   return hipGetLastError();

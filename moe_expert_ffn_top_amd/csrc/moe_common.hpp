@@ -29,6 +29,7 @@ inline bool use_gemm(const moe_dims& d) { return (int64_t)d.T * d.k >= (int64_t)
 // tile_tok  int32 [max_tiles][16] token of each tile row (rows >= n repeat row 0)
 // tile_base int32 [E]           first tile of each routed group
 // chunks    int4  [max_chunks]  {group, first row p0, rows n (<= 256), slot}
+// mrk       int32 [ncb][E]      per-block lowest slot rank per expert (tail-skip only)
 // The FFN reads either the tile lists (weight-streaming kernel) or the chunk
 // list (grouped GEMM), and the grouping writes only the one that use_gemm names.
 // Flat entries per counting block of the grouping (a multiple of 256).
@@ -38,7 +39,7 @@ struct WsLayout {
   int64_t ncb;         // blocks of kCntBlk flat entries
   int64_t max_tiles;   // upper bound on FFN tiles
   int64_t max_chunks;  // upper bound on GEMM chunks
-  uint64_t off_cnt, off_meta, off_tiles, off_tile_tok, off_tile_base, off_chunks, total;
+  uint64_t off_cnt, off_meta, off_tiles, off_tile_tok, off_tile_base, off_chunks, off_mrk, total;
 };
 
 inline uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
@@ -57,7 +58,8 @@ inline WsLayout ws_layout(const moe_dims& d) {
   w.off_tile_base = align256(w.off_tile_tok + (uint64_t)w.max_tiles * 64);
   w.max_chunks = (F + kChunkRows - 1) / kChunkRows + routed_groups + (d.T + kChunkRows - 1) / kChunkRows + 1;
   w.off_chunks = align256(w.off_tile_base + (uint64_t)d.E * 4);
-  w.total = align256(w.off_chunks + (uint64_t)w.max_chunks * 16);
+  w.off_mrk = align256(w.off_chunks + (uint64_t)w.max_chunks * 16);
+  w.total = align256(w.off_mrk + (uint64_t)w.ncb * d.E * 4);
   return w;
 }
 
@@ -162,7 +164,8 @@ hipError_t launch_topk(const moe_dims& d, const float* logits, const uint16_t* x
                        int32_t* ids, float* w, float* sigma, hipStream_t s);
 hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, const int32_t* slot_table,
                         int32_t n_slots, int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
-                        int32_t* dev_status, void* ws, hipStream_t s);
+                        int32_t* dev_status, void* ws, hipStream_t s,
+                        int32_t skip_rank = 0, int32_t* n_skipped = nullptr);
 // Route + group in one kernel (drawn logits, T <= 16, T*k <= 256).
 bool route_group_fusable(const moe_dims& d);
 hipError_t launch_route_group(const moe_dims& d, int32_t layer, const float* logits, const uint16_t* x,

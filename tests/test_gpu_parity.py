@@ -311,3 +311,75 @@ def test_topk_with_ties_matches_oracle(B, T, E, k):
         assert int(buf.status.item()) == 0
         g = O.group(want_ids, E)
         assert np.array_equal(buf.perm.cpu().numpy(), g.perm)
+
+
+def _late_logits(T, E, k, late, seed):
+    """Drawn logits in which each expert of `late` is picked, when at all, only
+    at the last slot k - 1 (every other token leaves it unpicked)."""
+    rng = np.random.default_rng(seed)
+    lg = rng.normal(size=(T, E)).astype(np.float32)
+    lg[:, late] = -20.0
+    for t in range(0, T, 2):
+        others = np.sort(np.delete(lg[t], late))[::-1]
+        lg[t, late[(t // 2) % len(late)]] = (others[k - 2] + others[k - 1]) / 2
+    return lg
+
+
+# one decode-sized window (single-kernel grouping) and one large window
+# (multi-kernel grouping, grouped-GEMM FFN)
+TAIL = {
+    "window12": Config(41, "ts", T=12, H=128, I=64, E=12, k=3, L=1, router="zipf", zipf_s=1.0),
+    "window300": Config(42, "tl", T=300, H=128, I=64, E=12, k=3, L=1, router="zipf", zipf_s=1.0),
+}
+
+
+@pytest.mark.parametrize("cname", list(TAIL))
+def test_tail_skip_matches_oracle(B, hostgen, cname):
+    """moe_group_tail_skip: non-resident experts that every token of the window
+    ranks at the threshold or later are skipped (zero rows, no renormalisation,
+    MOE_DEV_TAIL_SKIPPED, counted); a non-resident expert some token ranks
+    earlier still sets MOE_DEV_NOT_RESIDENT; threshold 0 skips nothing."""
+    cfg = TAIL[cname]
+    T, k, E = cfg.T, cfg.k, cfg.E
+    late = [9, 10, 11]
+    say("[gpu] tail-skip case %s T=%d E=%d k=%d" % (cname, T, E, k))
+    case = Case(B, cfg, hostgen, slot_override={e: -1 for e in late})
+    case.logits = _late_logits(T, E, k, late, cfg.cfg_id)
+    case.logits_t = torch.from_numpy(case.logits).cuda()
+    d, buf = case.dims, case.buf
+    ns = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+
+    def run(R, slot_table):
+        B.moe_route(d, case.x, None, case.logits_t, case.wsg_t, None, buf.ids, buf.w, buf.sigma)
+        buf.status.zero_()
+        B.moe_group_tail_skip(d, 0, buf.ids, slot_table, cfg.E1, R, buf.offsets, buf.perm, buf.inv_perm,
+                              buf.group_slot, buf.status, ns, buf.ws)
+        B.moe_expert_ffn(d, case.x, case.pool, case.pool_bytes, case.layout, buf.offsets, buf.perm, buf.group_slot,
+                         buf.h, buf.y_rows, buf.status, buf.ws)
+        B.moe_combine(d, buf.y_rows, buf.inv_perm, buf.w, buf.sigma, buf.y)
+        torch.cuda.synchronize()
+        return int(buf.status.item()), int(ns.item())
+
+    resident = np.ones(E, bool)
+    resident[late] = False
+    status, n = run(k - 1, case.slot_table)
+    ora_ids = O.topk(case.logits, k)
+    assert np.array_equal(buf.ids.cpu().numpy(), ora_ids)
+    mask = O.tail_skip(ora_ids, resident, k - 1)
+    assert list(np.nonzero(mask)[0]) == late
+    assert status == B.MOE_DEV_TAIL_SKIPPED and n == len(late)
+    ora = case.oracle(skip=mask)
+    inv = buf.inv_perm.cpu().numpy()
+    rows = [int(inv[t * k + j]) for t in range(T) for j in range(k) if mask[ora_ids[t, j]]]
+    assert rows and np.all(bf16_to_f64(buf.y_rows[rows]) == 0)
+    assert_close(bf16_to_f64(buf.y), ora.y_pre, "y with tail-skip")
+
+    # a non-resident expert that a token ranks first is not skippable
+    first = int(ora_ids[1, 0])
+    st2 = case.slot_table.clone()
+    st2[0, first] = -1
+    status, n = run(k - 1, st2)
+    assert status == B.MOE_DEV_TAIL_SKIPPED | B.MOE_DEV_NOT_RESIDENT and n == len(late)
+    # threshold 0: no skipping
+    status, n = run(0, case.slot_table)
+    assert status == B.MOE_DEV_NOT_RESIDENT and n == 0
