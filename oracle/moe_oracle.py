@@ -42,6 +42,15 @@ What it computes, step by step, and where each step is defined:
   8. Combine — [Strata] "路由以后，专家怎样分工？" and "少算这些专家，会付出什么代价？":
      y_t = bf16( sum_j w_j Y[row(t, j)] + sigma_t Y_shared[t] ) (rounding point
      R2), with no renormalisation.
+  10. Partial residency (a variant) — [FreeToken] 3.3: one LRU cache over
+     (layer, expert) shared by all layers; a hit refreshes the expert's last
+     use, a fill admits a newly chosen expert, eviction removes the least
+     recently used; and 4: per layer one step on the device dedups the routed
+     experts, classifies them against the residency table, picks the victims
+     (the least recently used slots, found in one pass) and rewrites the
+     table.  Readings: every miss is filled; the clock ticks once per layer
+     call; among slots of equal last use the lower slot index goes first;
+     empty slots count as never used; the shared expert is always needed.
   9. Route tail-skip (a variant) — [Strata] "少算这些专家，会付出什么代价？" and the
      skip-condition passage just before it: with a rank threshold R (default 7,
      ranks counted from zero), an expert that is not resident is skipped when
@@ -348,6 +357,55 @@ def tail_skip(ids: np.ndarray, resident: np.ndarray, skip_rank: int) -> np.ndarr
         ranks = [j for t in range(ids.shape[0]) for j in range(ids.shape[1]) if ids[t, j] == e]
         out[e] = len(ranks) > 0 and min(ranks) >= skip_rank
     return out
+
+
+# ---------------------------------------------------------------------------
+# 10. Partial residency (variant)
+# ---------------------------------------------------------------------------
+
+class LruCache:
+    """S device slots caching (layer, expert) blobs; key = layer * (E + 1) + e.
+
+    slot_table [L][E+1] (slot or -1), owner [S] (key or -1), last [S] (clock
+    of the last use, -1 for a slot never used) and the clock, as the device
+    keeps them."""
+
+    def __init__(self, L: int, E: int, S: int):
+        self.L, self.E, self.S = L, E, S
+        self.slot_table = np.full((L, E + 1), -1, np.int32)
+        self.owner = np.full(S, -1, np.int32)
+        self.last = np.full(S, -1, np.int32)
+        self.clock = 0
+
+    def step(self, layer: int, ids: np.ndarray):
+        """One layer call of the window `ids` [T, k].  Returns (fills, full):
+        fills lists (key, slot) in the order the misses were placed; full is
+        True when there were more misses than slots to evict (the misses past
+        the available slots stay non-resident)."""
+        E1 = self.E + 1
+        now = self.clock
+        self.clock += 1
+        needed = sorted({int(e) for e in np.asarray(ids).ravel() if 0 <= e < self.E} | {self.E})
+        for e in needed:                          # hits refresh their last use
+            s = int(self.slot_table[layer, e])
+            if s >= 0:
+                self.last[s] = now
+        misses = [e for e in needed if self.slot_table[layer, e] < 0]
+        # victims: the least recently used slots; this call's hits (last == now)
+        # are not candidates
+        cand = sorted((int(self.last[s]), s) for s in range(self.S) if self.last[s] != now)
+        full = len(misses) > len(cand)
+        fills = []
+        for e, (_, s) in zip(misses, cand):
+            old = int(self.owner[s])
+            if old >= 0:
+                self.slot_table[old // E1, old % E1] = -1
+            key = layer * E1 + e
+            self.owner[s] = key
+            self.last[s] = now
+            self.slot_table[layer, e] = s
+            fills.append((key, s))
+        return fills, full
 
 
 # ---------------------------------------------------------------------------
