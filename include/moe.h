@@ -70,6 +70,7 @@ typedef struct ihipStream_t* moe_stream_t;
 #define MOE_DEV_NOT_RESIDENT 2    /* a non-empty group's slot is -1: rows are zero */
 #define MOE_DEV_BAD_SLOT 4        /* a slot index >= n_slots: rows are zero */
 #define MOE_DEV_TAIL_SKIPPED 8    /* moe_group_tail_skip skipped a group (rows zero) */
+#define MOE_DEV_CACHE_FULL 16     /* moe_residency_update had more misses than slots to evict */
 
 const char* moe_status_string(int status);
 /* Detail of the last error returned on the calling thread ("" if none). */
@@ -195,6 +196,50 @@ int moe_group(const moe_dims* d, int32_t layer, const int32_t* topk_ids,
               int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
               int32_t* dev_status, void* ws, uint64_t ws_bytes,
               moe_stream_t stream);
+
+/* ---- Partial residency (a variant): an LRU cache of expert blobs --------
+ * [FreeToken] 3.3 (one LRU over (layer, expert) shared by all layers: a hit
+ * refreshes the expert's last use, a fill admits a newly chosen expert,
+ * eviction removes the least recently used) and 4 (per layer one device
+ * kernel classifies the routed experts against the residency table, picks the
+ * victims in one pass and rewrites the table; one fixed-shape transfer, masked
+ * by a device-side count, moves the blobs; no host decision).
+ *
+ * The cache is n_slots slots of the pool (slot s at pool + s * slot_stride).
+ * Its state lives on the device and belongs to the caller:
+ *   slot_table [L][E+1] int32: slot of (layer, expert), or -1;
+ *   slot_owner [n_slots] int32: key layer*(E+1)+e of the slot's blob, or -1;
+ *   last_use   [n_slots] int32: clock of the slot's last use, -1 if never used;
+ *   clock      [1] int32: ticks once per moe_residency_update.
+ * Start from slot_table, slot_owner and last_use all -1 and clock 0 (or any
+ * state these calls produced).
+ *
+ * moe_residency_update: for the window topk_ids [T][k] of `layer`, the needed
+ * experts are its routed ids in [0, E) and the shared expert.  Hits refresh
+ * their slot's last use.  Misses, in ascending expert order, take the least
+ * recently used slots this call does not hit (ties: lower slot; never used
+ * first); a victim's previous owner becomes -1 in slot_table.  fill_list
+ * [E+1][2] int32 receives (key, slot) per placed miss in that order and
+ * n_fill [1] their count.  More misses than evictable slots: the first ones
+ * are placed, the rest stay -1 and MOE_DEV_CACHE_FULL is set in dev_status.
+ * Requires E <= 1024 and n_slots <= 262144.
+ *
+ * moe_residency_fill: copies the blob of each (key, slot) of fill_list (first
+ * *n_fill entries) from host_blobs + key * slot_stride to pool + slot *
+ * slot_stride (layout->blob_bytes bytes each).  host_blobs is pinned host
+ * memory the device can read (all L*(E+1) blobs, 16-byte aligned), owned by
+ * the caller and unchanged until the copy is done.  Fixed grid; entries with
+ * a key or slot out of range are skipped.  Run it on the stream of the update
+ * and before the FFN that reads the slots: stream order publishes the blobs.
+ */
+int moe_residency_update(const moe_dims* d, int32_t layer, const int32_t* topk_ids,
+                         int32_t* slot_table, int32_t* slot_owner, int32_t* last_use,
+                         int32_t n_slots, int32_t* clock, int32_t* fill_list,
+                         int32_t* n_fill, int32_t* dev_status, moe_stream_t stream);
+int moe_residency_fill(const moe_dims* d, const moe_blob_layout* layout,
+                       const void* host_blobs, void* pool, uint64_t pool_bytes,
+                       int32_t n_slots, const int32_t* fill_list, const int32_t* n_fill,
+                       moe_stream_t stream);
 
 /* ---- S3 with the route tail-skip (a variant) ---------------------------
  * [Strata] "少算这些专家，会付出什么代价？" and the skip-condition passage before it

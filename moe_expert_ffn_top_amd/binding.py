@@ -31,10 +31,12 @@ MOE_DEV_BAD_EXPERT_ID = 1
 MOE_DEV_NOT_RESIDENT = 2
 MOE_DEV_BAD_SLOT = 4
 MOE_DEV_TAIL_SKIPPED = 8
+MOE_DEV_CACHE_FULL = 16
 
 #: every symbol include/moe.h declares
 EXPORTED = ("moe_status_string", "moe_last_error", "moe_version", "moe_blob_layout_init", "moe_workspace_bytes",
-            "moe_route", "moe_group", "moe_group_tail_skip", "moe_route_group", "moe_expert_ffn", "moe_expert_ffn_stages", "moe_combine",
+            "moe_route", "moe_group", "moe_group_tail_skip", "moe_residency_update", "moe_residency_fill",
+            "moe_route_group", "moe_expert_ffn", "moe_expert_ffn_stages", "moe_combine",
             "moe_ring_create", "moe_stage_h2d", "moe_ring_acquire", "moe_ring_release", "moe_ring_slot_ptr",
             "moe_ring_destroy")
 
@@ -74,6 +76,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.moe_workspace_bytes.argtypes = [_DP, ctypes.POINTER(_u64)]
     lib.moe_route.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.moe_group.argtypes = [_DP, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _u64, _vp]
+    lib.moe_residency_update.argtypes = [_DP, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
+    lib.moe_residency_fill.argtypes = [_DP, ctypes.POINTER(BlobLayout), _vp, _vp, _u64, _i32, _vp, _vp, _vp]
     lib.moe_group_tail_skip.argtypes = [_DP, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _u64,
                                         _vp]
     lib.moe_route_group.argtypes = [_DP, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
@@ -158,6 +162,19 @@ def moe_group(dims, layer, topk_ids, slot_table, n_slots, offsets, perm, inv_per
         ws_bytes = ws.numel() * ws.element_size()
     _check(_lib.moe_group(ctypes.byref(dims), layer, _p(topk_ids), _p(slot_table), n_slots, _p(offsets), _p(perm),
                           _p(inv_perm), _p(group_slot), _p(dev_status), _p(ws), ws_bytes, _s(stream)), "moe_group")
+
+
+def moe_residency_update(dims, layer, topk_ids, slot_table, slot_owner, last_use, n_slots, clock, fill_list, n_fill,
+                         dev_status, stream=None) -> None:
+    _check(_lib.moe_residency_update(ctypes.byref(dims), layer, _p(topk_ids), _p(slot_table), _p(slot_owner),
+                                     _p(last_use), n_slots, _p(clock), _p(fill_list), _p(n_fill), _p(dev_status),
+                                     _s(stream)), "moe_residency_update")
+
+
+def moe_residency_fill(dims, layout, host_blobs, pool, pool_bytes, n_slots, fill_list, n_fill, stream=None) -> None:
+    """host_blobs: a device-readable address of pinned host memory (an int)."""
+    _check(_lib.moe_residency_fill(ctypes.byref(dims), ctypes.byref(layout), _p(host_blobs), _p(pool), pool_bytes,
+                                   n_slots, _p(fill_list), _p(n_fill), _s(stream)), "moe_residency_fill")
 
 
 def moe_group_tail_skip(dims, layer, topk_ids, slot_table, n_slots, skip_rank, offsets, perm, inv_perm, group_slot,

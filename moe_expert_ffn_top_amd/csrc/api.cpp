@@ -219,6 +219,46 @@ int moe_group_tail_skip(const moe_dims* d, int32_t layer, const int32_t* topk_id
                     "group launch");
 }
 
+int moe_residency_update(const moe_dims* d, int32_t layer, const int32_t* topk_ids, int32_t* slot_table,
+                         int32_t* slot_owner, int32_t* last_use, int32_t n_slots, int32_t* clock, int32_t* fill_list,
+                         int32_t* n_fill, int32_t* dev_status, moe_stream_t stream) {
+  int r = check_dims(d);
+  if (r) return r;
+  if (layer < 0 || layer >= d->L) return fail(MOE_ERR_ARG, "layer = %d outside [0, L = %d)", layer, d->L);
+  if (n_slots < 1 || n_slots > moe::kMaxResidencySlots)
+    return fail(MOE_ERR_ARG, "n_slots = %d outside [1, %d]", n_slots, moe::kMaxResidencySlots);
+  REQUIRE(topk_ids, 4, "topk_ids");
+  REQUIRE(slot_table, 4, "slot_table");
+  REQUIRE(slot_owner, 4, "slot_owner");
+  REQUIRE(last_use, 4, "last_use");
+  REQUIRE(clock, 4, "clock");
+  REQUIRE(fill_list, 8, "fill_list");
+  REQUIRE(n_fill, 4, "n_fill");
+  REQUIRE(dev_status, 4, "dev_status");
+  return hip_status(moe::launch_residency(*d, layer, topk_ids, slot_table, slot_owner, last_use, n_slots, clock,
+                                          fill_list, n_fill, dev_status, reinterpret_cast<hipStream_t>(stream)),
+                    "residency launch");
+}
+
+int moe_residency_fill(const moe_dims* d, const moe_blob_layout* layout, const void* host_blobs, void* pool,
+                       uint64_t pool_bytes, int32_t n_slots, const int32_t* fill_list, const int32_t* n_fill,
+                       moe_stream_t stream) {
+  int r = check_dims(d);
+  if (r) return r;
+  if (!layout) return fail(MOE_ERR_ARG, "layout is NULL");
+  if (n_slots < 1) return fail(MOE_ERR_ARG, "n_slots = %d < 1", n_slots);
+  REQUIRE(host_blobs, 16, "host_blobs");
+  REQUIRE(pool, 16, "pool");
+  REQUIRE(fill_list, 8, "fill_list");
+  REQUIRE(n_fill, 4, "n_fill");
+  if (pool_bytes < (uint64_t)n_slots * layout->slot_stride)
+    return fail(MOE_ERR_ARG, "pool_bytes %llu < n_slots * slot_stride", (unsigned long long)pool_bytes);
+  return hip_status(moe::launch_fill(*d, static_cast<const uint8_t*>(host_blobs), layout->slot_stride,
+                                     layout->blob_bytes, static_cast<uint8_t*>(pool), n_slots, fill_list, n_fill,
+                                     reinterpret_cast<hipStream_t>(stream)),
+                    "residency fill launch");
+}
+
 int moe_route_group(const moe_dims* d, int32_t layer, const uint16_t* x, const float* w_router,
                     const float* logits_in, const float* w_shared_gate, float* logits_out, int32_t* topk_ids,
                     float* topk_w, float* shared_sigma, const int32_t* slot_table, int32_t n_slots,

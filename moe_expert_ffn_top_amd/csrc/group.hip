@@ -69,39 +69,6 @@ __global__ __launch_bounds__(kBlk) void k_count(const int32_t* __restrict__ ids,
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
-// Inclusive scan of one wavefront with DPP: shifts 1, 2, 4, 8 inside each row
-// of 16 lanes (lanes shifted in from outside the row add 0), then the row
-// broadcasts carry row totals into the rows above.
-__device__ inline int wave_inclusive_scan(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
-  return v;
-}
-
-// Block-wide exclusive scan for blockDim.x == 1024 (16 wavefronts): a DPP scan
-// per wavefront, the 16 wavefront totals through LDS (one barrier), and a
-// second barrier before lds16 can be reused.
-__device__ int block_exclusive_scan(int v, int* lds16, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int inc = wave_inclusive_scan(v);
-  if (lane == 63) lds16[wave] = inc;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < 16; w++) {
-    const int t = lds16[w];
-    before += (w < wave) ? t : 0;
-    all += t;
-  }
-  *total = all;
-  __syncthreads();
-  return before + inc - v;
-}
-
 // Thread e (< E) holds count = rows of expert e.  Writes offsets, group_slot,
 // residency status and the FFN work list (the tile lists, or with `chunks`
 // the chunk list); returns this expert's first row.

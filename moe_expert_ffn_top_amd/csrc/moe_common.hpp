@@ -34,6 +34,11 @@ inline bool use_gemm(const moe_dims& d) { return (int64_t)d.T * d.k >= (int64_t)
 // list (grouped GEMM), and the grouping writes only the one that use_gemm names.
 // Flat entries per counting block of the grouping (a multiple of 256).
 constexpr int kCntBlk = 1024;
+// Largest routed-expert count (moe_dims.E).
+constexpr int kMaxExperts = 1024;
+// Largest slot count of a residency cache (the residency kernel keeps one bit
+// per slot in LDS).
+constexpr int kMaxResidencySlots = 262144;
 struct WsLayout {
   int64_t nb;          // blocks of 256 flat (token, slot) entries
   int64_t ncb;         // blocks of kCntBlk flat entries
@@ -145,6 +150,39 @@ __device__ inline f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Inclusive scan of one wavefront with DPP: shifts 1, 2, 4, 8 inside each row
+// of 16 lanes (lanes shifted in from outside the row add 0), then the row
+// broadcasts carry row totals into the rows above.
+__device__ inline int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+// Block-wide exclusive scan for blockDim.x == 1024 (16 wavefronts): a DPP scan
+// per wavefront, the 16 wavefront totals through LDS (one barrier), and a
+// second barrier before lds16 can be reused.
+__device__ inline int block_exclusive_scan(int v, int* lds16, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int inc = wave_inclusive_scan(v);
+  if (lane == 63) lds16[wave] = inc;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 16; w++) {
+    const int t = lds16[w];
+    before += (w < wave) ? t : 0;
+    all += t;
+  }
+  *total = all;
+  __syncthreads();
+  return before + inc - v;
+}
+
 // Sets the calling thread's moe_last_error() text; returns code.
 int record_error(int code, const char* msg);
 
@@ -166,6 +204,11 @@ hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, co
                         int32_t n_slots, int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
                         int32_t* dev_status, void* ws, hipStream_t s,
                         int32_t skip_rank = 0, int32_t* n_skipped = nullptr);
+hipError_t launch_residency(const moe_dims& d, int32_t layer, const int32_t* ids, int32_t* slot_table, int32_t* owner,
+                            int32_t* last, int32_t n_slots, int32_t* clock, int32_t* fills, int32_t* n_fill,
+                            int32_t* dev_status, hipStream_t s);
+hipError_t launch_fill(const moe_dims& d, const uint8_t* host, uint64_t stride, uint64_t blob_bytes, uint8_t* pool,
+                       int32_t n_slots, const int32_t* fills, const int32_t* n_fill, hipStream_t s);
 // Route + group in one kernel (drawn logits, T <= 16, T*k <= 256).
 bool route_group_fusable(const moe_dims& d);
 hipError_t launch_route_group(const moe_dims& d, int32_t layer, const float* logits, const uint16_t* x,
