@@ -55,7 +55,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="decode48",
-                    help="tiny | decode48 | decode43x64 | prefill8192 | streamed4x4096 (default decode48)")
+                    help="tiny | decode48 | decode43x64 | prefill8192 | streamed4x4096 | cached48x64 "
+                         "(default decode48)")
     ap.add_argument("--eager", action="store_true", help="launch every call eagerly instead of HIP graphs")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -287,6 +288,142 @@ def cpu_baseline(cfg, seconds):
     return {"value": value, "unit": "tokens/s", "cores": 1, "kind": "oracle", "sample": sample}
 
 
+PCIE_GEN5_X16_GBS = 64.0   # the host link's published rate per direction
+
+
+def host_device_pointer(host_ptr):
+    """The device-readable address of page-locked host memory (hipHostGetDevicePointer)."""
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_uint]
+    out = ctypes.c_void_p()
+    rc = hip.hipHostGetDevicePointer(ctypes.byref(out), ctypes.c_void_p(host_ptr), 0)
+    assert rc == 0 and out.value, "hipHostGetDevicePointer failed (%d)" % rc
+    return out.value
+
+
+def run_cached(cfg, args, B, DevGen):
+    """Decode through a device cache of expert blobs (partial residency).  Every
+    (layer, expert) blob sits in page-locked host memory; the pool holds
+    cache_frac of them.  Per layer: route, the residency update (LRU over
+    (layer, expert)), the fill of the misses from host memory, group, FFN and
+    combine, all captured in the step graphs.  Reports tokens/s and, from one
+    more eager pass with HIP events, the hit rate, the blobs filled per step,
+    the fill kernel's rate over the host link and the residency kernel's time."""
+    import torch
+    from moe_expert_ffn_top_amd.layer import LayerBuffers
+
+    K, W = args.steps, args.warmup
+    n_meas = min(K, 4)
+    wl = Workload(cfg, W + K + n_meas, B, DevGen)   # the measured eager steps continue the sequence
+    log("copying %.2f GB of blobs to page-locked host memory" % (wl.pool_bytes / 1e9))
+    host = torch.empty(wl.pool_bytes, dtype=torch.uint8, pin_memory=True)
+    host.copy_(wl.pool)
+    torch.cuda.synchronize()
+    del wl.pool
+    torch.cuda.empty_cache()
+    hptr = host_device_pointer(host.data_ptr())
+    L, E1, d, lay = cfg.L, cfg.E1, wl.dims, wl.layout
+    S = max(1, int(round(cfg.cache_frac * wl.n_slots)))
+    pool = torch.zeros(S * lay.slot_stride, dtype=torch.uint8, device="cuda")
+    i32 = dict(dtype=torch.int32, device="cuda")
+    table = torch.full((L, E1), -1, **i32)
+    owner, last, clock = torch.full((S,), -1, **i32), torch.full((S,), -1, **i32), torch.zeros(1, **i32)
+    fills, n_fill = torch.zeros((L, E1, 2), **i32), torch.zeros(L, **i32)
+    buf = LayerBuffers.allocate(d)
+    log("cache of %d of %d blobs (%.2f GB)" % (S, wl.n_slots, pool.numel() / 1e9))
+
+    def run_step(step, ev=None):
+        s = wl.input_index(step)
+        for l in range(L):
+            x = wl.x[s, l]
+            B.moe_route(d, x, None, wl.logits[s, l], wl.wsg[l], None, buf.ids, buf.w, buf.sigma)
+            if ev is not None:
+                ev.append([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+                ev[-1][0].record()
+            B.moe_residency_update(d, l, buf.ids, table, owner, last, S, clock, fills[l], n_fill[l:l + 1],
+                                   buf.status)
+            if ev is not None:
+                ev[-1][1].record()
+            B.moe_residency_fill(d, lay, hptr, pool, pool.numel(), S, fills[l], n_fill[l:l + 1])
+            if ev is not None:
+                ev[-1][2].record()
+            B.moe_group(d, l, buf.ids, table, S, buf.offsets, buf.perm, buf.inv_perm, buf.group_slot, buf.status,
+                        buf.ws)
+            B.moe_expert_ffn(d, x, pool, pool.numel(), lay, buf.offsets, buf.perm, buf.group_slot, buf.h,
+                             buf.y_rows, buf.status, buf.ws)
+            B.moe_combine(d, buf.y_rows, buf.inv_perm, buf.w, buf.sigma, buf.y)
+
+    graphs = []
+    if not args.eager:
+        log("capturing %d step graphs" % wl.n_inputs)
+        for s in range(wl.n_inputs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_step(s)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        # capture ran nothing: the cache starts cold at the first warm-up step
+
+    def step(i):
+        if graphs:
+            graphs[wl.input_index(i)].replay()
+        else:
+            run_step(i)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    assert int(buf.status.item()) == 0, "device status %d after warmup" % int(buf.status.item())
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(K):
+        step(W + i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / K
+    tokens_per_s = cfg.T / (ms_per_step / 1e3)
+    log("%.3f ms/step, %.1f tokens/s" % (ms_per_step, tokens_per_s))
+
+    # eager steps with events: residency kernel time, fill time and bytes, hit rate
+    res_ms, fill_ms, n_filled, n_needed = [], [], 0, 0
+    for i in range(n_meas):
+        ev = []
+        run_step(W + K + i, ev)
+        torch.cuda.synchronize()
+        res_ms += [a.elapsed_time(b) for a, b, _ in ev]
+        fill_ms += [b.elapsed_time(c) for _, b, c in ev]
+        n_filled += int(n_fill.sum().item())
+        s = wl.input_index(W + K + i)
+        from synth import zipf_logits
+        for l in range(L):
+            ids = np.argsort(-zipf_logits(cfg, l, s), axis=1, kind="stable")[:, :cfg.k]
+            n_needed += len(np.unique(ids)) + 1
+    fill_bytes = n_filled * lay.blob_bytes
+    fill_s = sum(fill_ms) * 1e-3
+    fill_gbs = fill_bytes / fill_s / 1e9 if fill_s > 0 else 0.0
+    residency = {"cache_slots": S, "blobs": wl.n_slots, "hit_rate": 1.0 - n_filled / max(1, n_needed),
+                 "blobs_filled_per_step": n_filled / n_meas, "fill_gb_per_s": fill_gbs,
+                 "fill_us_per_layer": float(np.mean(fill_ms) * 1e3),
+                 "residency_update_us_per_layer": float(np.mean(res_ms) * 1e3)}
+    log("residency: %s" % residency)
+    roof = {"bound": "pcie", "achieved": fill_gbs, "peak": PCIE_GEN5_X16_GBS, "unit": "GB/s",
+            "frac": fill_gbs / PCIE_GEN5_X16_GBS, "traffic": None,
+            "kernel": "k_fill (moe_residency_fill), blob bytes filled / fill time",
+            "peak_note": "host link: PCIe 5.0 x16 published rate per direction"}
+    line = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded; random block-FP4 weights, bf16 activations)",
+        "config": {"workload": cfg.name, "T": cfg.T, "layers": cfg.L, "H": cfg.H, "I": cfg.I, "E": cfg.E,
+                   "k": cfg.k, "shared_experts": 1, "routing": "zipf s=%g, hot set moves every %d steps"
+                   % (cfg.zipf_s, cfg.epoch_len), "cache_frac": cfg.cache_frac, "graphs": not args.eager,
+                   "parallelism": "single GPU"},
+        "roofline": roof, "residency": residency, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def run_staged(cfg, args, B, DevGen):
     """The streamed workload: every layer's expert blobs sit in page-locked host
     memory and go through the two-slot device ring (copy stream) while the
@@ -418,6 +555,9 @@ def main():
     cfg = config_by_name(args.config)
     if cfg.staged:
         run_staged(cfg, args, B, DevGen)
+        return
+    if cfg.cache_frac > 0:
+        run_cached(cfg, args, B, DevGen)
         return
     K, W = args.steps, args.warmup
     wl = Workload(cfg, W + K, B, DevGen)

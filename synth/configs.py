@@ -26,6 +26,7 @@ class Config:
     zipf_s: float = 0.0
     epoch_len: int = 0  # steps per hot-set epoch (0: one epoch)
     staged: bool = False  # expert blobs start in pinned host memory (two-slot ring)
+    cache_frac: float = 0.0  # > 0: blobs in pinned host memory, a device LRU cache of this share of them
     seed: int = 0
 
     @property
@@ -47,6 +48,10 @@ CONFIGS = {
     4: Config(4, "prefill8192", T=8192, H=2048, I=512, E=512, k=10, L=1, router="matrix"),
     5: Config(5, "streamed4x4096", T=4096, H=4096, I=2048, E=256, k=6, L=4, router="zipf", zipf_s=1.2,
               staged=True),
+    # partial residency: decode48's shapes, a hot set that moves every 16 of 64
+    # steps, and a device cache of one eighth of the (layer, expert) blobs
+    6: Config(6, "cached48x64", T=4, H=2048, I=512, E=512, k=10, L=48, router="zipf", steps=64, zipf_s=1.0,
+              epoch_len=16, cache_frac=0.125),
 }
 
 
