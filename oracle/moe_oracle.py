@@ -51,6 +51,17 @@ What it computes, step by step, and where each step is defined:
      table.  Readings: every miss is filled; the clock ticks once per layer
      call; among slots of equal last use the lower slot index goes first;
      empty slots count as never used; the shared expert is always needed.
+  11. Hot/cold swaps (a variant) — [Strata] "哪些专家能长期留在显存？" (the
+     passages on heat and candidate pairs, and on swaps and publication): each
+     expert's heat accumulates its routing counts; per round, inside one layer
+     the hottest experts outside the cache pair with the coldest inside, a pair
+     whose heat gap reaches the threshold (default 1.5) is a swap candidate,
+     the candidates go by gap, at most 96 a round (default), and afterwards
+     every heat is multiplied by the decay 0.7.  Readings: pairs are formed in
+     order (i-th hottest outside with i-th coldest inside, ties to the lower
+     expert index) and stop at the first pair below the threshold; the shared
+     expert never swaps; equal gaps go by (layer, pair index); heats are fp32
+     as on the device, so every comparison is taken in fp32.
   9. Route tail-skip (a variant) — [Strata] "少算这些专家，会付出什么代价？" and the
      skip-condition passage just before it: with a rank threshold R (default 7,
      ranks counted from zero), an expert that is not resident is skipped when
@@ -406,6 +417,45 @@ class LruCache:
             self.slot_table[layer, e] = s
             fills.append((key, s))
         return fills, full
+
+
+# ---------------------------------------------------------------------------
+# 11. Hot/cold swaps (variant)
+# ---------------------------------------------------------------------------
+
+def heat_add(heat: np.ndarray, layer: int, ids: np.ndarray) -> None:
+    """heat [L][E] fp32 += routing counts of the window ids [T, k] (ids outside
+    [0, E) are not counted)."""
+    E = heat.shape[1]
+    counts = np.zeros(E, np.float32)
+    for e in np.asarray(ids).ravel():
+        if 0 <= e < E:
+            counts[e] += np.float32(1.0)
+    heat[layer] = (heat[layer] + counts).astype(np.float32)
+
+
+def heat_decay(heat: np.ndarray, decay: float = 0.7) -> None:
+    """Every heat times the decay, in fp32."""
+    heat[...] = (heat * np.float32(decay)).astype(np.float32)
+
+
+def swap_plan(heat: np.ndarray, slot_table: np.ndarray, threshold: float = 1.5, max_swaps: int = 96):
+    """The round's swaps: a list of (layer, hot expert, cold expert), largest
+    heat gap first.  heat [L][E] fp32; slot_table [L][E+1] (-1: not resident;
+    column E, the shared expert, never swaps)."""
+    L, E = heat.shape
+    thr = np.float32(threshold)
+    cands = []
+    for l in range(L):
+        out = sorted((e for e in range(E) if slot_table[l, e] < 0), key=lambda e: (-heat[l, e], e))
+        ins = sorted((e for e in range(E) if slot_table[l, e] >= 0), key=lambda e: (heat[l, e], e))
+        for i in range(min(len(out), len(ins))):
+            gap = np.float32(heat[l, out[i]] - heat[l, ins[i]])
+            if not gap >= thr:
+                break
+            cands.append((-gap, l, i, out[i], ins[i]))
+    cands.sort()
+    return [(l, hot, cold) for _, l, _, hot, cold in cands[:max_swaps]]
 
 
 # ---------------------------------------------------------------------------
