@@ -241,6 +241,45 @@ int moe_residency_fill(const moe_dims* d, const moe_blob_layout* layout,
                        int32_t n_slots, const int32_t* fill_list, const int32_t* n_fill,
                        moe_stream_t stream);
 
+/* ---- Hot/cold swaps (a variant) -----------------------------------------
+ * [Strata] "哪些专家能长期留在显存？" (the passages on heat and candidate pairs,
+ * and on swaps and publication): each expert's heat accumulates its routing
+ * counts and is multiplied by a decay (default 0.7) after every round; per
+ * round, inside one layer the hottest experts outside the cache pair with the
+ * coldest inside, a pair whose heat gap reaches the threshold (default 1.5)
+ * is a candidate, and the candidates go by gap, at most max_swaps (default
+ * 96).  A swap copies the hot expert's blob into the cold expert's slot; the
+ * table names the new owner only after the copy.
+ *
+ * moe_heat_update: heat [L][E] fp32 (device) += the row count of each routed
+ * group of this layer call, from offsets written by moe_group (ids outside
+ * [0, E) have no group and do not count).
+ * moe_heat_decay: every entry of heat [L][E] times decay.
+ * moe_swap_plan (host, pure): heat [L][E] and slot_table [L][E+1] are HOST
+ * copies; writes the round's swaps to plan [max_swaps][3] as (layer, hot
+ * expert, cold expert), largest heat gap first, and their number to *n_plan.
+ * Pairs form in heat order (ties to the lower expert index), a layer stops at
+ * its first pair below the threshold, equal gaps go by (layer, pair index),
+ * the shared expert never swaps; comparisons are taken in fp32.
+ * moe_swap_apply: plan [n_plan][3] device (from moe_swap_plan); for each entry
+ * whose hot expert is still out of the cache and whose cold expert is still
+ * in it, copies the hot blob from host_blobs (device-readable pinned memory,
+ * as for moe_residency_fill) into the cold expert's slot, then sets the hot
+ * expert's table entry to that slot and the cold one's to -1.  fill_scratch
+ * [n_plan][2] and n_scratch [1]: device scratch.  Everything runs on `stream`
+ * in that order; kernels that read the pool must be ordered after it.
+ */
+int moe_heat_update(const moe_dims* d, int32_t layer, const int32_t* offsets,
+                    float* heat, moe_stream_t stream);
+int moe_heat_decay(const moe_dims* d, float* heat, float decay, moe_stream_t stream);
+int moe_swap_plan(const moe_dims* d, const float* heat, const int32_t* slot_table,
+                  float threshold, int32_t max_swaps, int32_t* plan, int32_t* n_plan);
+int moe_swap_apply(const moe_dims* d, const moe_blob_layout* layout,
+                   const void* host_blobs, void* pool, uint64_t pool_bytes,
+                   int32_t n_slots, int32_t* slot_table, const int32_t* plan,
+                   int32_t n_plan, int32_t* fill_scratch, int32_t* n_scratch,
+                   moe_stream_t stream);
+
 /* ---- S3 with the route tail-skip (a variant) ---------------------------
  * [Strata] "少算这些专家，会付出什么代价？" and the skip-condition passage before it
  * (default threshold 7, ranks from zero; the kept experts' weights are not

@@ -36,6 +36,7 @@ MOE_DEV_CACHE_FULL = 16
 #: every symbol include/moe.h declares
 EXPORTED = ("moe_status_string", "moe_last_error", "moe_version", "moe_blob_layout_init", "moe_workspace_bytes",
             "moe_route", "moe_group", "moe_group_tail_skip", "moe_residency_update", "moe_residency_fill",
+            "moe_heat_update", "moe_heat_decay", "moe_swap_plan", "moe_swap_apply",
             "moe_route_group", "moe_expert_ffn", "moe_expert_ffn_stages", "moe_combine",
             "moe_ring_create", "moe_stage_h2d", "moe_ring_acquire", "moe_ring_release", "moe_ring_slot_ptr",
             "moe_ring_destroy")
@@ -76,6 +77,11 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.moe_workspace_bytes.argtypes = [_DP, ctypes.POINTER(_u64)]
     lib.moe_route.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.moe_group.argtypes = [_DP, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _u64, _vp]
+    lib.moe_heat_update.argtypes = [_DP, _i32, _vp, _vp, _vp]
+    lib.moe_heat_decay.argtypes = [_DP, _vp, ctypes.c_float, _vp]
+    lib.moe_swap_plan.argtypes = [_DP, _vp, _vp, ctypes.c_float, _i32, _vp, ctypes.POINTER(_i32)]
+    lib.moe_swap_apply.argtypes = [_DP, ctypes.POINTER(BlobLayout), _vp, _vp, _u64, _i32, _vp, _vp, _i32, _vp, _vp,
+                                   _vp]
     lib.moe_residency_update.argtypes = [_DP, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
     lib.moe_residency_fill.argtypes = [_DP, ctypes.POINTER(BlobLayout), _vp, _vp, _u64, _i32, _vp, _vp, _vp]
     lib.moe_group_tail_skip.argtypes = [_DP, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _u64,
@@ -175,6 +181,34 @@ def moe_residency_fill(dims, layout, host_blobs, pool, pool_bytes, n_slots, fill
     """host_blobs: a device-readable address of pinned host memory (an int)."""
     _check(_lib.moe_residency_fill(ctypes.byref(dims), ctypes.byref(layout), _p(host_blobs), _p(pool), pool_bytes,
                                    n_slots, _p(fill_list), _p(n_fill), _s(stream)), "moe_residency_fill")
+
+
+def moe_heat_update(dims, layer, offsets, heat, stream=None) -> None:
+    _check(_lib.moe_heat_update(ctypes.byref(dims), layer, _p(offsets), _p(heat), _s(stream)), "moe_heat_update")
+
+
+def moe_heat_decay(dims, heat, decay: float = 0.7, stream=None) -> None:
+    _check(_lib.moe_heat_decay(ctypes.byref(dims), _p(heat), decay, _s(stream)), "moe_heat_decay")
+
+
+def moe_swap_plan(dims, heat, slot_table, threshold: float = 1.5, max_swaps: int = 96):
+    """Host call on numpy arrays: heat float32 [L][E], slot_table int32 [L][E+1].
+    Returns an int32 array [n][3] of (layer, hot, cold)."""
+    import numpy as np
+    h = np.ascontiguousarray(heat, dtype=np.float32)
+    t = np.ascontiguousarray(slot_table, dtype=np.int32)
+    plan = np.zeros((max(max_swaps, 1), 3), np.int32)
+    n = _i32(0)
+    _check(_lib.moe_swap_plan(ctypes.byref(dims), h.ctypes.data, t.ctypes.data, threshold, max_swaps,
+                              plan.ctypes.data, ctypes.byref(n)), "moe_swap_plan")
+    return plan[:n.value].copy()
+
+
+def moe_swap_apply(dims, layout, host_blobs, pool, pool_bytes, n_slots, slot_table, plan, n_plan, fill_scratch,
+                   n_scratch, stream=None) -> None:
+    _check(_lib.moe_swap_apply(ctypes.byref(dims), ctypes.byref(layout), _p(host_blobs), _p(pool), pool_bytes,
+                               n_slots, _p(slot_table), _p(plan), n_plan, _p(fill_scratch), _p(n_scratch),
+                               _s(stream)), "moe_swap_apply")
 
 
 def moe_group_tail_skip(dims, layer, topk_ids, slot_table, n_slots, skip_rank, offsets, perm, inv_perm, group_slot,

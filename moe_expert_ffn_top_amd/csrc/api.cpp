@@ -259,6 +259,57 @@ int moe_residency_fill(const moe_dims* d, const moe_blob_layout* layout, const v
                     "residency fill launch");
 }
 
+int moe_heat_update(const moe_dims* d, int32_t layer, const int32_t* offsets, float* heat, moe_stream_t stream) {
+  int r = check_dims(d);
+  if (r) return r;
+  if (layer < 0 || layer >= d->L) return fail(MOE_ERR_ARG, "layer = %d outside [0, L = %d)", layer, d->L);
+  REQUIRE(offsets, 4, "offsets");
+  REQUIRE(heat, 4, "heat");
+  return hip_status(moe::launch_heat(*d, layer, offsets, heat, reinterpret_cast<hipStream_t>(stream)), "heat launch");
+}
+
+int moe_heat_decay(const moe_dims* d, float* heat, float decay, moe_stream_t stream) {
+  int r = check_dims(d);
+  if (r) return r;
+  REQUIRE(heat, 4, "heat");
+  return hip_status(moe::launch_heat_decay(*d, heat, decay, reinterpret_cast<hipStream_t>(stream)),
+                    "heat decay launch");
+}
+
+int moe_swap_plan(const moe_dims* d, const float* heat, const int32_t* slot_table, float threshold,
+                  int32_t max_swaps, int32_t* plan, int32_t* n_plan) {
+  int r = check_dims(d);
+  if (r) return r;
+  if (!heat || !slot_table || !n_plan || (!plan && max_swaps > 0)) return fail(MOE_ERR_ARG, "a pointer is NULL");
+  if (max_swaps < 0) return fail(MOE_ERR_ARG, "max_swaps = %d < 0", max_swaps);
+  *n_plan = moe::plan_swaps(*d, heat, slot_table, threshold, max_swaps, plan);
+  return ok();
+}
+
+int moe_swap_apply(const moe_dims* d, const moe_blob_layout* layout, const void* host_blobs, void* pool,
+                   uint64_t pool_bytes, int32_t n_slots, int32_t* slot_table, const int32_t* plan, int32_t n_plan,
+                   int32_t* fill_scratch, int32_t* n_scratch, moe_stream_t stream) {
+  int r = check_dims(d);
+  if (r) return r;
+  if (!layout) return fail(MOE_ERR_ARG, "layout is NULL");
+  if (n_slots < 1) return fail(MOE_ERR_ARG, "n_slots = %d < 1", n_slots);
+  if (n_plan < 0) return fail(MOE_ERR_ARG, "n_plan = %d < 0", n_plan);
+  if (n_plan == 0) return ok();
+  REQUIRE(host_blobs, 16, "host_blobs");
+  REQUIRE(pool, 16, "pool");
+  REQUIRE(slot_table, 4, "slot_table");
+  REQUIRE(plan, 4, "plan");
+  REQUIRE(fill_scratch, 8, "fill_scratch");
+  REQUIRE(n_scratch, 4, "n_scratch");
+  if (pool_bytes < (uint64_t)n_slots * layout->slot_stride)
+    return fail(MOE_ERR_ARG, "pool_bytes %llu < n_slots * slot_stride", (unsigned long long)pool_bytes);
+  return hip_status(moe::launch_swap_apply(*d, static_cast<const uint8_t*>(host_blobs), layout->slot_stride,
+                                           layout->blob_bytes, static_cast<uint8_t*>(pool), n_slots, slot_table,
+                                           plan, n_plan, fill_scratch, n_scratch,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                    "swap launch");
+}
+
 int moe_route_group(const moe_dims* d, int32_t layer, const uint16_t* x, const float* w_router,
                     const float* logits_in, const float* w_shared_gate, float* logits_out, int32_t* topk_ids,
                     float* topk_w, float* shared_sigma, const int32_t* slot_table, int32_t n_slots,

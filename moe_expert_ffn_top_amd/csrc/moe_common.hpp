@@ -209,6 +209,14 @@ hipError_t launch_residency(const moe_dims& d, int32_t layer, const int32_t* ids
                             int32_t* dev_status, hipStream_t s);
 hipError_t launch_fill(const moe_dims& d, const uint8_t* host, uint64_t stride, uint64_t blob_bytes, uint8_t* pool,
                        int32_t n_slots, const int32_t* fills, const int32_t* n_fill, hipStream_t s);
+hipError_t launch_heat(const moe_dims& d, int32_t layer, const int32_t* offsets, float* heat, hipStream_t s);
+hipError_t launch_heat_decay(const moe_dims& d, float* heat, float decay, hipStream_t s);
+hipError_t launch_swap_apply(const moe_dims& d, const uint8_t* host, uint64_t stride, uint64_t blob_bytes,
+                             uint8_t* pool, int32_t n_slots, int32_t* table, const int32_t* plan, int32_t n_plan,
+                             int32_t* fills, int32_t* n_fill, hipStream_t s);
+// host: the round's swaps into plan [max_swaps][3] (layer, hot, cold); returns their number
+int plan_swaps(const moe_dims& d, const float* heat, const int32_t* table, float threshold, int32_t max_swaps,
+               int32_t* plan);
 // Route + group in one kernel (drawn logits, T <= 16, T*k <= 256).
 bool route_group_fusable(const moe_dims& d);
 hipError_t launch_route_group(const moe_dims& d, int32_t layer, const float* logits, const uint16_t* x,

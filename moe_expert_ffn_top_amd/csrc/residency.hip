@@ -219,3 +219,80 @@ hipError_t launch_fill(const moe_dims& d, const uint8_t* host, uint64_t stride, 
 }
 
 }  // namespace moe
+
+// ---- hot/cold swaps -----------------------------------------------------------
+// [Strata] "哪些专家能长期留在显存？": each expert's heat accumulates its routing
+// counts and decays after every swap round; a swap moves a hot expert's blob
+// into a cold expert's slot, and the table names the new owner only once the
+// copy is done (stream order: list, fill, publish).
+namespace moe {
+namespace {
+
+// heat[layer][e] += rows of routed group e (offsets from moe_group)
+__global__ __launch_bounds__(256) void k_heat(const int32_t* __restrict__ offsets, int E, int layer,
+                                              float* __restrict__ heat) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e < E) heat[(int64_t)layer * E + e] += (float)(offsets[e + 1] - offsets[e]);
+}
+
+__global__ __launch_bounds__(256) void k_heat_decay(float* __restrict__ heat, int64_t n, float decay) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) heat[i] *= decay;
+}
+
+// plan entry i = (layer, hot, cold) -> fill (key of (layer, hot), slot of cold);
+// an entry that no longer fits the table (hot resident, cold not) gets key -1
+// and is skipped by the fill and the publication
+__global__ __launch_bounds__(256) void k_swap_list(const int3* __restrict__ plan, int n_plan, int L, int E,
+                                                   int n_slots, const int32_t* __restrict__ table,
+                                                   int2* __restrict__ fills, int32_t* __restrict__ n_fill) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i == 0) *n_fill = n_plan;
+  if (i >= n_plan) return;
+  const int3 p = plan[i];
+  const int E1 = E + 1;
+  const bool ok = p.x >= 0 && p.x < L && p.y >= 0 && p.y < E && p.z >= 0 && p.z < E && p.y != p.z;
+  const int hot_slot = ok ? table[p.x * E1 + p.y] : 0, cold_slot = ok ? table[p.x * E1 + p.z] : -1;
+  const bool fits = ok && hot_slot < 0 && cold_slot >= 0 && cold_slot < n_slots;
+  fills[i] = fits ? make_int2(p.x * E1 + p.y, cold_slot) : make_int2(-1, -1);
+}
+
+__global__ __launch_bounds__(256) void k_swap_publish(const int3* __restrict__ plan, int n_plan, int E,
+                                                      const int2* __restrict__ fills, int32_t* __restrict__ table) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_plan) return;
+  const int2 f = fills[i];
+  if (f.x < 0) return;
+  const int3 p = plan[i];
+  table[p.x * (E + 1) + p.y] = f.y;
+  table[p.x * (E + 1) + p.z] = -1;
+}
+
+}  // namespace
+
+hipError_t launch_heat(const moe_dims& d, int32_t layer, const int32_t* offsets, float* heat, hipStream_t s) {
+  hipLaunchKernelGGL(k_heat, dim3((d.E + 255) / 256), dim3(256), 0, s, offsets, d.E, layer, heat);
+  return hipGetLastError();
+}
+
+hipError_t launch_heat_decay(const moe_dims& d, float* heat, float decay, hipStream_t s) {
+  const int64_t n = (int64_t)d.L * d.E;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(k_heat_decay, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, s, heat, n, decay);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap_apply(const moe_dims& d, const uint8_t* host, uint64_t stride, uint64_t blob_bytes,
+                             uint8_t* pool, int32_t n_slots, int32_t* table, const int32_t* plan, int32_t n_plan,
+                             int32_t* fills, int32_t* n_fill, hipStream_t s) {
+  const dim3 g((unsigned)((n_plan + 255) / 256 > 0 ? (n_plan + 255) / 256 : 1));
+  hipLaunchKernelGGL(k_swap_list, g, dim3(256), 0, s, reinterpret_cast<const int3*>(plan), n_plan, d.L, d.E, n_slots,
+                     table, reinterpret_cast<int2*>(fills), n_fill);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = launch_fill(d, host, stride, blob_bytes, pool, n_slots, fills, n_fill, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_swap_publish, g, dim3(256), 0, s, reinterpret_cast<const int3*>(plan), n_plan, d.E,
+                     reinterpret_cast<const int2*>(fills), table);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -144,3 +144,21 @@ def test_combine_and_ring_validation(B):
     assert B.raw_status("moe_ring_create", fake, fake + 1, 4096, None, ctypes.byref(out)) == B.MOE_ERR_ALIGN
     assert B.raw_status("moe_ring_destroy", None) == B.MOE_ERR_ARG
     assert B.raw_status("moe_ring_acquire", None, 0, None) == B.MOE_ERR_ARG
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_swap_plan_matches_oracle(B, seed):
+    """moe_swap_plan (host-pure) against the oracle's hot/cold rule on random
+    heats (integers and decayed values, so equal heats and equal gaps occur)
+    and residency tables; threshold and cap vary."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    L, E = int(rng.integers(1, 6)), int(rng.integers(2, 40))
+    heat = rng.integers(0, 12, size=(L, E)).astype(np.float32)
+    if seed % 2:
+        heat *= np.float32(0.7)
+    table = np.where(rng.random((L, E + 1)) < 0.5, np.arange(L * (E + 1)).reshape(L, E + 1), -1).astype(np.int32)
+    thr, cap = float(rng.choice([0.0, 1.5, 2.0])), int(rng.choice([0, 3, 96]))
+    d = B.Dims(1, 64, 32, E, 1, L)
+    got = [tuple(r) for r in B.moe_swap_plan(d, heat, table, thr, cap)]
+    assert got == O.swap_plan(heat, table, thr, cap)
