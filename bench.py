@@ -58,6 +58,9 @@ def parse():
                     help="tiny | decode48 | decode43x64 | prefill8192 | streamed4x4096 | cached48x64 "
                          "(default decode48)")
     ap.add_argument("--eager", action="store_true", help="launch every call eagerly instead of HIP graphs")
+    ap.add_argument("--policy", default="lru", choices=("lru", "hotcold"),
+                    help="cached workloads: lru (fill every miss; the layer's outputs) or hotcold (measure the "
+                         "hot/cold swap policy over the routing)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
@@ -424,6 +427,103 @@ def run_cached(cfg, args, B, DevGen):
     print(json.dumps(line), flush=True)
 
 
+def run_hotcold(cfg, args, B, DevGen):
+    """The hot/cold swap policy over the cached workload's routing (it measures
+    the policy, not the layer: without a second place to compute misses, the
+    experts out of the cache are not computed).  The cache starts with each
+    layer's shared expert and its lowest-index experts.  Every step, each
+    layer routes, groups and adds its routing counts to the heat; after the
+    step one swap round runs (heat and table to the host, plan, plan to the
+    device, apply, decay 0.7).  Reports the share of routed (layer, expert)
+    uses whose expert was resident, swaps per round, the apply rate over the
+    host link and the host planning time."""
+    import torch
+    from moe_expert_ffn_top_amd.layer import LayerBuffers
+
+    K, W = args.steps, args.warmup
+    wl = Workload(cfg, W + K, B, DevGen)
+    log("copying %.2f GB of blobs to page-locked host memory" % (wl.pool_bytes / 1e9))
+    host = torch.empty(wl.pool_bytes, dtype=torch.uint8, pin_memory=True)
+    host.copy_(wl.pool)
+    torch.cuda.synchronize()
+    hptr = host_device_pointer(host.data_ptr())
+    L, E, E1, d, lay = cfg.L, cfg.E, cfg.E1, wl.dims, wl.layout
+    stride = lay.slot_stride
+    S = max(L, int(round(cfg.cache_frac * wl.n_slots)))
+    per = S // L
+    table = np.full((L, E1), -1, np.int32)
+    n = 0
+    for l in range(L):
+        for e in [E] + list(range(per - 1)):
+            table[l, e] = n
+            n += 1
+    pool = torch.zeros(S * stride, dtype=torch.uint8, device="cuda")
+    src = wl.pool.view(wl.n_slots, stride)
+    for l in range(L):
+        keys = [l * E1 + e for e in range(E1) if table[l, e] >= 0]
+        slots = [int(table[l, e]) for e in range(E1) if table[l, e] >= 0]
+        pool.view(S, stride)[torch.tensor(slots, device="cuda")] = src[torch.tensor(keys, device="cuda")]
+    torch.cuda.synchronize()
+    del wl.pool, src
+    torch.cuda.empty_cache()
+    t_dev = torch.from_numpy(table).cuda()
+    heat = torch.zeros((L, E), dtype=torch.float32, device="cuda")
+    buf = LayerBuffers.allocate(d)
+    scratch = torch.zeros((96, 2), dtype=torch.int32, device="cuda")
+    nsc = torch.zeros(1, dtype=torch.int32, device="cuda")
+    log("cache of %d of %d blobs (%.2f GB), %d per layer at start" % (S, wl.n_slots, pool.numel() / 1e9, per))
+    uses = hits = 0
+    swaps, plan_ms, apply_ms = [], [], []
+    for step in range(W + K):
+        s = wl.input_index(step)
+        for l in range(L):
+            B.moe_route(d, wl.x[s, l], None, wl.logits[s, l], wl.wsg[l], None, buf.ids, buf.w, buf.sigma)
+            B.moe_group(d, l, buf.ids, t_dev, S, buf.offsets, buf.perm, buf.inv_perm, buf.group_slot, buf.status,
+                        buf.ws)
+            B.moe_heat_update(d, l, buf.offsets, heat)
+            if step >= W:
+                ids = buf.ids.cpu().numpy()
+                uses += ids.size
+                hits += int((t_dev[l].cpu().numpy()[ids] >= 0).sum())
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        plan = B.moe_swap_plan(d, heat.cpu().numpy(), t_dev.cpu().numpy())
+        t1 = time.perf_counter()
+        if len(plan):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            p_dev = torch.from_numpy(plan).cuda()
+            a.record()
+            B.moe_swap_apply(d, lay, hptr, pool, pool.numel(), S, t_dev, p_dev, len(plan), scratch, nsc)
+            b.record()
+            torch.cuda.synchronize()
+            if step >= W:
+                apply_ms.append(a.elapsed_time(b))
+        B.moe_heat_decay(d, heat, 0.7)
+        if step >= W:
+            swaps.append(len(plan))
+            plan_ms.append((t1 - t0) * 1e3)
+    moved = sum(swaps) * lay.blob_bytes
+    apply_gbs = moved / (sum(apply_ms) * 1e-3) / 1e9 if apply_ms else 0.0
+    pol = {"cache_slots": S, "blobs": wl.n_slots, "resident_share_of_routed_uses": hits / max(1, uses),
+           "swaps_per_round": float(np.mean(swaps)), "apply_gb_per_s": apply_gbs,
+           "apply_ms_per_round": float(np.mean(apply_ms)) if apply_ms else 0.0,
+           "plan_ms_per_round": float(np.mean(plan_ms)), "round": "one per decode step, after all layers",
+           "threshold": 1.5, "max_swaps": 96, "decay": 0.7}
+    log("hot/cold: %s" % pol)
+    line = {
+        "metric": "hot/cold swap policy: share of routed (layer, expert) uses resident", "value": pol[
+            "resident_share_of_routed_uses"], "unit": "fraction", "n_gpus": 1, "steps": K, "warmup": W,
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic (seeded; Zipf routing with a moving hot set)",
+        "config": {"workload": cfg.name, "policy": "hotcold", "T": cfg.T, "layers": cfg.L, "E": cfg.E, "k": cfg.k,
+                   "cache_frac": cfg.cache_frac, "parallelism": "single GPU"},
+        "roofline": {"bound": "pcie", "achieved": apply_gbs, "peak": PCIE_GEN5_X16_GBS, "unit": "GB/s",
+                     "frac": apply_gbs / PCIE_GEN5_X16_GBS, "traffic": None,
+                     "kernel": "moe_swap_apply (k_fill of the round's swaps)"},
+        "hotcold": pol,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def run_staged(cfg, args, B, DevGen):
     """The streamed workload: every layer's expert blobs sit in page-locked host
     memory and go through the two-slot device ring (copy stream) while the
@@ -557,7 +657,7 @@ def main():
         run_staged(cfg, args, B, DevGen)
         return
     if cfg.cache_frac > 0:
-        run_cached(cfg, args, B, DevGen)
+        (run_hotcold if args.policy == "hotcold" else run_cached)(cfg, args, B, DevGen)
         return
     K, W = args.steps, args.warmup
     wl = Workload(cfg, W + K, B, DevGen)
