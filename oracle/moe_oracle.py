@@ -62,6 +62,17 @@ What it computes, step by step, and where each step is defined:
      expert index) and stop at the first pair below the threshold; the shared
      expert never swaps; equal gaps go by (layer, pair index); heats are fp32
      as on the device, so every comparison is taken in fp32.
+  12. MX formats (a variant) — [FreeToken] notes that the DeepSeek-V4-Flash
+     experts are natively MXFP4; the pages do not define the format, so the
+     OCP Microscaling (MX) definitions are the reading adopted: 32 values along
+     K share one E8M0 scale 2^(b - 127) (b = 255 is NaN); MXFP4 elements are
+     E2M1 (no global scale); activations meet the scaled MFMA as MXFP8
+     (elements E4M3FN), a new rounding point RA: per 32 values the shared
+     exponent is floor(log2 amax) - 8 (clamped to [-127, 127]; a zero block
+     takes -127) and each element is v / 2^shared rounded to the nearest
+     E4M3FN value (ties to the even code), saturating at +-448.  The MX expert
+     FFN quantises x at RA, rounds h to bf16 (R1) and quantises that at RA
+     for the down projection.
   9. Route tail-skip (a variant) — [Strata] "少算这些专家，会付出什么代价？" and the
      skip-condition passage just before it: with a rank threshold R (default 7,
      ranks counted from zero), an expert that is not resident is skipped when
@@ -459,6 +470,119 @@ def swap_plan(heat: np.ndarray, slot_table: np.ndarray, threshold: float = 1.5, 
 
 
 # ---------------------------------------------------------------------------
+# 12. MX formats (variant)
+# ---------------------------------------------------------------------------
+
+def e8m0_decode(b) -> np.ndarray:
+    """E8M0 scale bytes -> 2^(b - 127); 255 is NaN."""
+    b = np.asarray(b, dtype=np.int64)
+    return np.where(b == 255, np.nan, np.exp2(b.astype(np.float64) - 127.0))
+
+
+def _e4m3_table():
+    codes = np.array([c for c in range(128) if c != 0x7F], dtype=np.int64)   # non-negative finite codes
+    vals = e4m3fn_decode(codes)
+    order = np.argsort(vals, kind="stable")
+    return vals[order], codes[order]
+
+
+_E4M3_VALS, _E4M3_CODES = _e4m3_table()
+
+
+def e4m3fn_encode(v) -> np.ndarray:
+    """fp64 -> OCP E4M3FN bytes: the nearest representable value, ties to the
+    even code (even mantissa), saturating at +-448; -0 encodes as 0x80."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), 448.0)
+    i = np.clip(np.searchsorted(_E4M3_VALS, a), 1, len(_E4M3_VALS) - 1)
+    lo, hi = _E4M3_VALS[i - 1], _E4M3_VALS[i]
+    clo, chi = _E4M3_CODES[i - 1], _E4M3_CODES[i]
+    pick_hi = (hi - a < a - lo) | ((hi - a == a - lo) & ((chi & 1) == 0))
+    code = np.where(a >= hi, chi, np.where(pick_hi, chi, clo))
+    code = np.where(a <= 0.0, 0, code)
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def mxfp8_quantize(v: np.ndarray):
+    """Rows of v [n, K] (K % 32 == 0) at rounding point RA.  Returns (E4M3
+    codes uint8 [n, K], E8M0 scale bytes uint8 [n, K/32], fp64 values)."""
+    v = np.asarray(v, dtype=np.float64)
+    n, K = v.shape
+    blocks = v.reshape(n, K // 32, 32)
+    amax = np.abs(blocks).max(axis=2)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))       # amax = m 2^ex, 0.5 <= m < 1
+    shared = np.where(amax > 0, np.clip(ex - 1 - 8, -127, 127), -127)
+    X = np.exp2(shared.astype(np.float64))[:, :, None]
+    codes = e4m3fn_encode(blocks / X)
+    vals = e4m3fn_decode(codes) * X
+    return codes.reshape(n, K), (shared + 127).astype(np.uint8), vals.reshape(n, K)
+
+
+@dataclass
+class MxBlobLayout:
+    blob_bytes: int
+    slot_stride: int
+    off_codes: tuple
+    off_scales: tuple
+
+
+def mx_blob_layout(H: int, I: int) -> MxBlobLayout:
+    """MXFP4 blob: gate, up, down codes (the NVFP4 blob's placement), then their
+    E8M0 scales; no global scales.  Scale placement: per 16-row block, K/2
+    bytes; inside it group g of four 32-value blocks takes 64 bytes, row r's
+    four bytes at 4 r (so the scale byte of (row n, block b) sits at
+    (n // 16) * (K / 2) + (b // 4) * 64 + (n % 16) * 4 + b % 4).  Needs K % 128
+    == 0 and rows % 16 == 0."""
+    assert H % 128 == 0 and I % 128 == 0
+    rows = (I, I, H)
+    ks = (H, H, I)
+    off = 0
+    oc, osc = [], []
+    for r, K in zip(rows, ks):
+        oc.append(off)
+        off = _align(off + r * K // 2, 256)
+    for r, K in zip(rows, ks):
+        osc.append(off)
+        off = _align(off + r * K // 32, 256)
+    return MxBlobLayout(off, _align(off, 4096), tuple(oc), tuple(osc))
+
+
+def mx_matrix_scales(blob, lay: MxBlobLayout, m: int, H: int, I: int) -> np.ndarray:
+    """E8M0 scale bytes of matrix m as [rows][K/32]."""
+    rows, K = ((I, H), (I, H), (H, I))[m]
+    b = _blob_bytes(blob)
+    raw = b[lay.off_scales[m]:lay.off_scales[m] + rows * K // 32]
+    # [row block][group][row in block][block in group]
+    t = raw.reshape(rows // 16, K // 128, 16, 4)
+    return t.transpose(0, 2, 1, 3).reshape(rows, K // 32)
+
+
+def mx_dequant(blob, lay: MxBlobLayout, m: int, H: int, I: int) -> np.ndarray:
+    """Matrix m as fp64 [rows][K]: e2m1(code) * 2^(scale - 127).  Exact."""
+    rows, K = ((I, H), (I, H), (H, I))[m]
+    nv = BlobLayout(H, I, lay.off_codes, lay.off_scales, 0, lay.blob_bytes, lay.slot_stride)
+    codes = matrix_codes(blob, nv, m)
+    q = np.empty((rows, K), dtype=np.float64)
+    q[:, 0::2] = e2m1_decode(codes & 0xF)          # even column: low nibble
+    q[:, 1::2] = e2m1_decode(codes >> 4)
+    sc = e8m0_decode(mx_matrix_scales(blob, lay, m, H, I))
+    return q * np.repeat(sc, 32, axis=1)
+
+
+def expert_ffn_mx(x_rows: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> FfnRows:
+    """The MX expert FFN: x at RA, gate/up, h = bf16(silu(g) u) (R1), h at RA,
+    down, Y = bf16(o) (R3).  Weights are the exact MX dequantisation."""
+    xq = mxfp8_quantize(x_rows)[2]
+    g = xq @ wg.T
+    u = xq @ wu.T
+    h_pre = silu(g) * u
+    h = bf16_round(h_pre)
+    hq = mxfp8_quantize(h)[2]
+    y_pre = hq @ wd.T
+    return FfnRows(h_pre, h, y_pre, bf16_round(y_pre))
+
+
+# ---------------------------------------------------------------------------
 # Whole layer
 # ---------------------------------------------------------------------------
 
@@ -482,7 +606,7 @@ def moe_layer(x_bits: np.ndarray, blob_of: Callable[[int], bytes], H: int, I: in
               w_shared_gate: np.ndarray, w_router: Optional[np.ndarray] = None,
               logits: Optional[np.ndarray] = None, tokens: Optional[Sequence[int]] = None,
               dense_weights: Optional[Dict[int, tuple]] = None,
-              skip: Optional[np.ndarray] = None) -> LayerResult:
+              skip: Optional[np.ndarray] = None, fmt: str = "nvfp4") -> LayerResult:
     """One MoE layer.
 
     x_bits: uint16 bf16 bits [T, H].  blob_of(e) returns the blob bytes of
@@ -492,6 +616,8 @@ def moe_layer(x_bits: np.ndarray, blob_of: Callable[[int], bytes], H: int, I: in
     on its own row, its routing and the expert bytes.  skip (bool [E], see
     tail_skip): the routed rows of a skipped expert are zero (h and Y), so its
     terms drop out of the combine and the other weights stay as they are.
+    fmt "mx": the blobs are MXFP4 (mx_blob_layout) and each expert runs
+    expert_ffn_mx.
     """
     assert (w_router is None) != (logits is None)
     T = x_bits.shape[0]
@@ -504,13 +630,16 @@ def moe_layer(x_bits: np.ndarray, blob_of: Callable[[int], bytes], H: int, I: in
     tok = np.arange(T) if tokens is None else np.asarray(sorted(set(int(t) for t in tokens)), np.int64)
     res = LayerResult(lg, ids, w, sigma, groups, tok)
 
-    lay = blob_layout(H, I)
+    assert fmt in ("nvfp4", "mx")
+    lay = blob_layout(H, I) if fmt == "nvfp4" else mx_blob_layout(H, I)
     cache = {} if dense_weights is None else dense_weights
+    ffn = expert_ffn if fmt == "nvfp4" else expert_ffn_mx
 
     def weights(e):
         if e not in cache:
             b = blob_of(e)
-            cache[e] = tuple(dequant(b, lay, m) for m in range(3))
+            cache[e] = tuple(dequant(b, lay, m) if fmt == "nvfp4" else mx_dequant(b, lay, m, H, I)
+                             for m in range(3))
         return cache[e]
 
     # rows needed, grouped by expert: (expert, row p, token t)
@@ -528,7 +657,7 @@ def moe_layer(x_bits: np.ndarray, blob_of: Callable[[int], bytes], H: int, I: in
                 res.y_rows_pre[p] = res.y_rows[p] = np.zeros(H)
             continue
         wg, wu, wd = weights(e)
-        out = expert_ffn(x[[t for _, t in rows]], wg, wu, wd)
+        out = ffn(x[[t for _, t in rows]], wg, wu, wd)
         for i, (p, _) in enumerate(rows):
             res.h_pre[p], res.h[p] = out.h_pre[i], out.h[i]
             res.y_rows_pre[p], res.y_rows[p] = out.y_pre[i], out.y[i]
