@@ -577,9 +577,16 @@ def expert_ffn_mx(x_rows: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.nda
     u = xq @ wu.T
     h_pre = silu(g) * u
     h = bf16_round(h_pre)
+    y_pre, y = down_mx(h, wd)
+    return FfnRows(h_pre, h, y_pre, y)
+
+
+def down_mx(h: np.ndarray, wd: np.ndarray):
+    """The MX FFN from bf16 rows h on: h at RA, the down projection, Y = bf16(o)
+    (R3).  Returns (Y before R3, Y)."""
     hq = mxfp8_quantize(h)[2]
     y_pre = hq @ wd.T
-    return FfnRows(h_pre, h, y_pre, bf16_round(y_pre))
+    return y_pre, bf16_round(y_pre)
 
 
 # ---------------------------------------------------------------------------
