@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s; decode expert-weight GB/s & prefill TFLOP/s vs peak"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0   # dense fp8 MFMA: the rate of the scaled FP8 x FP4 instruction
 
 
 def log(msg):
@@ -55,7 +56,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="decode48",
-                    help="tiny | decode48 | decode43x64 | prefill8192 | streamed4x4096 | cached48x64 "
+                    help="tiny | decode48 | decode43x64 | prefill8192 | streamed4x4096 | cached48x64 | prefill8192_mx "
                          "(default decode48)")
     ap.add_argument("--eager", action="store_true", help="launch every call eagerly instead of HIP graphs")
     ap.add_argument("--policy", default="lru", choices=("lru", "hotcold"),
@@ -75,6 +76,8 @@ def ffn_kernel(cfg):
     """(kernel name, source file) of the FFN path the library takes for these
     shapes: the grouped GEMM when groups average >= 16 rows (T k >= 16 E),
     else the weight-streaming kernel."""
+    if cfg.fmt == "mx":
+        return "k_ffn_mx", os.path.join(CSRC, "ffn_mx.hip")
     if cfg.T * cfg.k >= 16 * cfg.E:
         return "k_ffn_gemm", os.path.join(CSRC, "ffn_gemm.hip")
     return "k_ffn_dec", os.path.join(CSRC, "ffn_dec.hip")
@@ -145,7 +148,8 @@ class Workload:
 
         self.cfg = cfg
         self.dims = B.Dims(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.L)
-        self.layout = B.moe_blob_layout_init(cfg.H, cfg.I)
+        self.mx = cfg.fmt == "mx"
+        self.layout = B.moe_blob_layout_init_mx(cfg.H, cfg.I) if self.mx else B.moe_blob_layout_init(cfg.H, cfg.I)
         dev = DevGen()
         E1, L = cfg.E1, cfg.L
         self.n_slots = L * E1
@@ -155,7 +159,8 @@ class Workload:
                                                                  self.layout.slot_stride))
         self.pool = torch.zeros(self.pool_bytes, dtype=torch.uint8, device="cuda")
         t0 = time.time()
-        dev.pool(cfg, 0, L, self.slot_table.data_ptr(), self.n_slots, self.layout, self.pool.data_ptr())
+        (dev.pool_mx if self.mx else dev.pool)(cfg, 0, L, self.slot_table.data_ptr(), self.n_slots, self.layout,
+                                               self.pool.data_ptr())
         torch.cuda.synchronize()
         log("pool generated on device in %.1f s" % (time.time() - t0))
         # per-step inputs: steps cycle through the workload's own steps
@@ -177,7 +182,20 @@ class Workload:
             lg = np.stack([np.stack([zipf_logits(cfg, l, s) for l in range(L)]) for s in range(self.n_inputs)])
             self.logits = torch.from_numpy(lg).cuda()
         torch.cuda.synchronize()
-        self.buf = LayerBuffers.allocate(self.dims)
+        self.buf = LayerBuffers.allocate(self.dims, mx=self.mx)
+
+    def ffn(self, x, stages=3, ev_start=None, ev_stop=None, stream=None):
+        """The expert FFN of the current layer (the blob format's entry point)."""
+        from moe_expert_ffn_top_amd import binding as B
+        d, buf = self.dims, self.buf
+        if self.mx:
+            B.moe_expert_ffn_mx(d, x, self.pool, self.pool_bytes, self.layout, buf.offsets, buf.perm,
+                                buf.group_slot, buf.h, buf.y_rows, buf.status, buf.ws, buf.mx_ws, stages,
+                                ev_start, ev_stop, stream=stream)
+        else:
+            B.moe_expert_ffn_stages(d, x, self.pool, self.pool_bytes, self.layout, buf.offsets, buf.perm,
+                                    buf.group_slot, buf.h, buf.y_rows, buf.status, buf.ws, stages, ev_start,
+                                    ev_stop, stream=stream)
 
     def input_index(self, step):
         return step % self.n_inputs
@@ -201,14 +219,11 @@ class Workload:
                               self.n_slots, buf.offsets, buf.perm, buf.inv_perm, buf.group_slot, buf.status, buf.ws,
                               stream=stream)
             if ffn_events is None:
-                B.moe_expert_ffn(d, x, self.pool, self.pool_bytes, self.layout, buf.offsets, buf.perm,
-                                 buf.group_slot, buf.h, buf.y_rows, buf.status, buf.ws, stream=stream)
+                self.ffn(x, stream=stream)
             else:
                 ev = [hip_events.new() for _ in range(4)]
                 for st in (1, 2):
-                    B.moe_expert_ffn_stages(d, x, self.pool, self.pool_bytes, self.layout, buf.offsets, buf.perm,
-                                            buf.group_slot, buf.h, buf.y_rows, buf.status, buf.ws, st,
-                                            ev[2 * st - 2], ev[2 * st - 1], stream=stream)
+                    self.ffn(x, st, ev[2 * st - 2], ev[2 * st - 1], stream=stream)
                 ffn_events.append((ev, buf.offsets.clone()))
             B.moe_combine(d, buf.y_rows, buf.inv_perm, buf.w, buf.sigma, buf.y, stream)
 
@@ -243,7 +258,9 @@ def cpu_baseline(cfg, seconds):
     from synth import HostGen, zipf_logits
 
     gen = HostGen()
-    olay = O.blob_layout(cfg.H, cfg.I)
+    mx = cfg.fmt == "mx"
+    olay = O.mx_blob_layout(cfg.H, cfg.I) if mx else O.blob_layout(cfg.H, cfg.I)
+    make_blob = gen.expert_blob_mx if mx else gen.expert_blob
     done_layers, t_oracle = 0, 0.0
     sample = ""
     with threadpool_limits(limits=1):
@@ -255,9 +272,9 @@ def cpu_baseline(cfg, seconds):
                     logits=zipf_logits(cfg, l, 0))
                 lg = O.router_logits(O.bf16_bits_to_f64(x), kw["w_router"]) if "w_router" in kw else kw["logits"]
                 need = set(O.topk(lg, cfg.k).reshape(-1).tolist()) | {cfg.E}
-                blobs = {e: gen.expert_blob(cfg, l, e, olay) for e in need}   # generation is not timed
+                blobs = {e: make_blob(cfg, l, e, olay) for e in need}   # generation is not timed
                 t0 = time.perf_counter()
-                O.moe_layer(x, lambda e: blobs[e], cfg.H, cfg.I, cfg.E, cfg.k, wsg, **kw)
+                O.moe_layer(x, lambda e: blobs[e], cfg.H, cfg.I, cfg.E, cfg.k, wsg, fmt=cfg.fmt, **kw)
                 t_oracle += time.perf_counter() - t0
                 done_layers += 1
                 if t_oracle >= seconds:
@@ -276,14 +293,14 @@ def cpu_baseline(cfg, seconds):
 
             def blob(e):
                 if e not in blob_cache:
-                    blob_cache[e] = gen.expert_blob(cfg, l, e, olay)
+                    blob_cache[e] = make_blob(cfg, l, e, olay)
                 return blob_cache[e]
             lg = O.router_logits(O.bf16_bits_to_f64(x), wr) if wr is not None else lgz
             toks = list(range(ntok))
             for e in set(O.topk(lg[toks], cfg.k).reshape(-1).tolist()) | {cfg.E}:
                 blob(e)
             t0 = time.perf_counter()
-            O.moe_layer(x, blob, cfg.H, cfg.I, cfg.E, cfg.k, wsg, w_router=wr, logits=lgz, tokens=toks)
+            O.moe_layer(x, blob, cfg.H, cfg.I, cfg.E, cfg.k, wsg, w_router=wr, logits=lgz, tokens=toks, fmt=cfg.fmt)
             t_oracle = time.perf_counter() - t0
             value = ntok / t_oracle
             sample = "layer 0, routing and grouping of all %d tokens plus expert FFN and combine of %d sampled " \
@@ -719,9 +736,11 @@ def main():
                          "achieved": float(dn_b.mean() / (dn_ms.mean() * 1e-3) / 1e9)}}
     else:
         achieved = float(gu_f.mean() / (gu_ms.mean() * 1e-3) / 1e12)
-        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
-                "kernel": "%s gate/up (moe_expert_ffn_stages, stages=1)" % ffn_kernel(cfg)[0],
+        peak = FP8_PEAK_TFLOPS if cfg.fmt == "mx" else BF16_PEAK_TFLOPS
+        entry = "moe_expert_ffn_mx" if cfg.fmt == "mx" else "moe_expert_ffn_stages"
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": None,
+                "kernel": "%s gate/up (%s, stages=1)" % (ffn_kernel(cfg)[0], entry),
                 "launch_us": float(gu_ms.mean() * 1e3), "flops_per_launch": float(gu_f.mean()),
                 "down": {"launch_us": float(dn_ms.mean() * 1e3), "flops_per_launch": float(dn_f.mean()),
                          "achieved": float(dn_f.mean() / (dn_ms.mean() * 1e-3) / 1e12)}}
@@ -736,7 +755,9 @@ def main():
     line = {
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic (seeded; random block-FP4 weights, bf16 activations)",
+        "dtype": "mxfp8 x mxfp4" if cfg.fmt == "mx" else "bf16",
+        "data": "synthetic (seeded; random MXFP4 weights, bf16 activations quantised to MXFP8)" if cfg.fmt == "mx"
+        else "synthetic (seeded; random block-FP4 weights, bf16 activations)",
         "config": {"workload": cfg.name, "T": cfg.T, "layers": cfg.L, "H": cfg.H, "I": cfg.I, "E": cfg.E,
                    "k": cfg.k, "shared_experts": 1,
                    "routing": ("zipf s=%g" % cfg.zipf_s) if cfg.router == "zipf" else "router matrix",

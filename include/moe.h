@@ -363,6 +363,65 @@ int moe_expert_ffn_stages(const moe_dims* d, const uint16_t* x, const void* pool
                           int32_t stages, void* ev_start, void* ev_stop,
                           moe_stream_t stream);
 
+/* ---- S4, MX variant: MXFP4 experts on the scaled MFMA ---------------------
+ * [FreeToken] notes that the DeepSeek-V4-Flash experts are natively MXFP4; the
+ * pages do not define the format, which is read as OCP Microscaling (MX):
+ *   E8M0   a scale byte b is 2^(b - 127); 255 is NaN.
+ *   MXFP4  32 values along K share one E8M0 scale; elements are E2M1 codes
+ *          (nibbles as in the NVFP4 blob); there is no global scale.
+ *   MXFP8  32 values share an E8M0 scale X = 2^(floor(log2 amax) - 8), the
+ *          exponent clamped to [-127, 127] (a zero block takes -127); each
+ *          element is v / X rounded to the nearest E4M3FN value (ties to the
+ *          even code), saturating at +-448.
+ *
+ * MX blob (moe_blob_layout_init_mx): the three matrices' codes exactly as in the
+ * NVFP4 blob (same tiling and section order), then their E8M0 scales, rows*K/32
+ * bytes per matrix, every section on a 256-byte boundary.  No globals:
+ * off_globals == blob_bytes.  Scale placement: each 16-row block owns K/2
+ * bytes from (K/2)*(n/16); inside, group g of four 32-value blocks (128
+ * columns, one step of the scaled MFMA) takes the 64 bytes from 64g, row
+ * n%16's four bytes at 4(n%16), block b at byte b%4 of them.  So the scale of
+ * (row n, block b) sits at (K/2)(n/16) + 64(b/4) + 4(n%16) + b%4.
+ * Requires H and I multiples of 128 in [128, 16384] (MOE_ERR_SHAPE otherwise).
+ */
+int moe_blob_layout_init_mx(int32_t H, int32_t I, moe_blob_layout* out);
+
+/* Host, pure.  Bytes of the MX activation workspace that moe_expert_ffn_mx
+ * needs for d.  Layout (each section from a 256-byte boundary, in order):
+ *   xq [T][H] E4M3 codes of x, xs [T][H/32] their E8M0 scales,
+ *   hq [T*k+T][I] E4M3 codes of h, hs [T*k+T][I/32] their E8M0 scales.
+ * After a gate/up stage, hq/hs hold MXFP8(h) for the rows that stage wrote. */
+int moe_mx_workspace_bytes(const moe_dims* d, uint64_t* out_bytes);
+
+/* MXFP8 quantisation (definition above) of bf16 rows x [rows][K] (device,
+ * 16-byte aligned; K a positive multiple of 32) into codes [rows][K] (device,
+ * 8-byte aligned) and scales [rows][K/32] (device), on stream.  The gate/up
+ * stage of moe_expert_ffn_mx applies it to x. */
+int moe_quantize_mxfp8(const uint16_t* x, int64_t rows, int32_t K, uint8_t* codes,
+                       uint8_t* scales, moe_stream_t stream);
+
+/* The expert FFN of S4 on MX blobs:
+ *   x^ = MXFP8(x[t])                                               (rounding point RA)
+ *   g = sum_c x^[c] Wg[i,c],  u = sum_c x^[c] Wu[i,c]   (Wg, Wu, Wd: MXFP4 values)
+ *   h[p,i] = bf16_rne( g / (1 + exp(-g)) * u )                     (R1)
+ *   h^ = MXFP8(h[p])                                               (RA)
+ *   Y[p,n] = bf16_rne( sum_i h^[i] Wd[n,i] )                       (R3)
+ * Products of codes and scales are exact; sums are fp32.  The MX workspace
+ * mx_ws (device, 256-byte aligned, at least moe_mx_workspace_bytes; contents
+ * as documented there) carries x^ and h^ between the stages.  It runs as the
+ * grouped GEMM only: MOE_ERR_SHAPE unless T*k >= 16 E (the group sizes for
+ * which moe_group writes the GEMM's chunk list).  layout must equal
+ * moe_blob_layout_init_mx(H, I).  stages, ev_start and ev_stop as for
+ * moe_expert_ffn_stages; the gate/up stage also quantises x.  Every other
+ * argument and the handling of missing slots as for moe_expert_ffn. */
+int moe_expert_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool,
+                      uint64_t pool_bytes, const moe_blob_layout* layout,
+                      const int32_t* offsets, const int32_t* perm,
+                      const int32_t* group_slot, uint16_t* h, uint16_t* y_rows,
+                      int32_t* dev_status, void* ws, uint64_t ws_bytes, void* mx_ws,
+                      uint64_t mx_ws_bytes, int32_t stages, void* ev_start, void* ev_stop,
+                      moe_stream_t stream);
+
 /* ---- S5: combine -------------------------------------------------------
  * [Strata] "路由以后，专家怎样分工？" (each expert output times its router weight,
  * summed, plus the gated shared-expert contribution) and "少算这些专家，会付出

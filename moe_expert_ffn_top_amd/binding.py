@@ -37,7 +37,8 @@ MOE_DEV_CACHE_FULL = 16
 EXPORTED = ("moe_status_string", "moe_last_error", "moe_version", "moe_blob_layout_init", "moe_workspace_bytes",
             "moe_route", "moe_group", "moe_group_tail_skip", "moe_residency_update", "moe_residency_fill",
             "moe_heat_update", "moe_heat_decay", "moe_swap_plan", "moe_swap_apply",
-            "moe_route_group", "moe_expert_ffn", "moe_expert_ffn_stages", "moe_combine",
+            "moe_route_group", "moe_expert_ffn", "moe_expert_ffn_stages", "moe_blob_layout_init_mx",
+            "moe_mx_workspace_bytes", "moe_quantize_mxfp8", "moe_expert_ffn_mx", "moe_combine",
             "moe_ring_create", "moe_stage_h2d", "moe_ring_acquire", "moe_ring_release", "moe_ring_slot_ptr",
             "moe_ring_destroy")
 
@@ -92,6 +93,11 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
                                    _vp, _u64, _vp]
     lib.moe_expert_ffn_stages.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _vp,
                                           _vp, _vp, _u64, _i32, _vp, _vp, _vp]
+    lib.moe_blob_layout_init_mx.argtypes = [_i32, _i32, ctypes.POINTER(BlobLayout)]
+    lib.moe_mx_workspace_bytes.argtypes = [_DP, ctypes.POINTER(_u64)]
+    lib.moe_quantize_mxfp8.argtypes = [_vp, ctypes.c_int64, _i32, _vp, _vp, _vp]
+    lib.moe_expert_ffn_mx.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _u64, _vp, _u64, _i32, _vp, _vp, _vp]
     lib.moe_combine.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.moe_ring_create.argtypes = [_vp, _vp, _u64, _vp, ctypes.POINTER(_vp)]
     lib.moe_stage_h2d.argtypes = [_vp, _vp, _u64, ctypes.POINTER(_i32)]
@@ -250,6 +256,51 @@ def moe_expert_ffn_stages(dims, x, pool, pool_bytes, layout: BlobLayout, offsets
                                       _p(offsets), _p(perm), _p(group_slot), _p(h), _p(y_rows), _p(dev_status),
                                       _p(ws), ws_bytes, stages, ev_start, ev_stop, _s(stream)),
            "moe_expert_ffn_stages")
+
+
+def moe_blob_layout_init_mx(H: int, I: int) -> BlobLayout:
+    out = BlobLayout()
+    _check(_lib.moe_blob_layout_init_mx(H, I, ctypes.byref(out)), "moe_blob_layout_init_mx")
+    return out
+
+
+class MxWorkspace:
+    """Section offsets of the MX activation workspace (include/moe.h)."""
+
+    def __init__(self, dims: Dims):
+        def a256(v):
+            return (v + 255) // 256 * 256
+        T, H, I, k = dims.T, dims.H, dims.I, dims.k
+        rows_h = T * k + T
+        self.off_xq = 0
+        self.off_xs = a256(T * H)
+        self.off_hq = a256(self.off_xs + T * H // 32)
+        self.off_hs = a256(self.off_hq + rows_h * I)
+        self.total = a256(self.off_hs + rows_h * I // 32)
+
+
+def moe_mx_workspace_bytes(dims: Dims) -> int:
+    out = _u64()
+    _check(_lib.moe_mx_workspace_bytes(ctypes.byref(dims), ctypes.byref(out)), "moe_mx_workspace_bytes")
+    return out.value
+
+
+def moe_quantize_mxfp8(x, rows: int, K: int, codes, scales, stream=None) -> None:
+    _check(_lib.moe_quantize_mxfp8(_p(x), rows, K, _p(codes), _p(scales), _s(stream)), "moe_quantize_mxfp8")
+
+
+def moe_expert_ffn_mx(dims, x, pool, pool_bytes, layout: BlobLayout, offsets, perm, group_slot, h, y_rows,
+                      dev_status, ws, mx_ws, stages: int = 3, ev_start: Optional[int] = None,
+                      ev_stop: Optional[int] = None, ws_bytes: Optional[int] = None,
+                      mx_ws_bytes: Optional[int] = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    if mx_ws_bytes is None:
+        mx_ws_bytes = mx_ws.numel() * mx_ws.element_size()
+    _check(_lib.moe_expert_ffn_mx(ctypes.byref(dims), _p(x), _p(pool), pool_bytes, ctypes.byref(layout),
+                                  _p(offsets), _p(perm), _p(group_slot), _p(h), _p(y_rows), _p(dev_status), _p(ws),
+                                  ws_bytes, _p(mx_ws), mx_ws_bytes, stages, ev_start, ev_stop, _s(stream)),
+           "moe_expert_ffn_mx")
 
 
 def moe_combine(dims, y_rows, inv_perm, topk_w, shared_sigma, y, stream=None) -> None:

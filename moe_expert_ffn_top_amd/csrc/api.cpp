@@ -395,6 +395,98 @@ int moe_expert_ffn_stages(const moe_dims* d, const uint16_t* x, const void* pool
                     "expert FFN launch");
 }
 
+int moe_blob_layout_init_mx(int32_t H, int32_t I, moe_blob_layout* out) {
+  if (!out) return fail(MOE_ERR_ARG, "out is NULL");
+  if (H < 128 || H > 16384 || H % 128 != 0) return fail(MOE_ERR_SHAPE, "H = %d: must be a multiple of 128 in [128, 16384]", H);
+  if (I < 128 || I > 16384 || I % 128 != 0) return fail(MOE_ERR_SHAPE, "I = %d: must be a multiple of 128 in [128, 16384]", I);
+  const uint64_t rows[3] = {(uint64_t)I, (uint64_t)I, (uint64_t)H};
+  const uint64_t kk[3] = {(uint64_t)H, (uint64_t)H, (uint64_t)I};
+  uint64_t off = 0;
+  for (int m = 0; m < 3; m++) {
+    out->off_codes[m] = off;
+    off = moe::align256(off + rows[m] * kk[m] / 2);
+  }
+  for (int m = 0; m < 3; m++) {
+    out->off_scales[m] = off;
+    off = moe::align256(off + rows[m] * kk[m] / 32);
+  }
+  out->off_globals = off;  // no globals: the blob ends here
+  out->blob_bytes = off;
+  out->slot_stride = (off + 4095) & ~uint64_t(4095);
+  return ok();
+}
+
+int moe_mx_workspace_bytes(const moe_dims* d, uint64_t* out_bytes) {
+  int r = check_dims(d);
+  if (r) return r;
+  if (!out_bytes) return fail(MOE_ERR_ARG, "out_bytes is NULL");
+  *out_bytes = moe::mx_ws_layout(*d).total;
+  return ok();
+}
+
+int moe_quantize_mxfp8(const uint16_t* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                       moe_stream_t stream) {
+  if (rows < 0) return fail(MOE_ERR_SHAPE, "rows = %lld: must be >= 0", (long long)rows);
+  if (K < 32 || K % 32 != 0) return fail(MOE_ERR_SHAPE, "K = %d: must be a positive multiple of 32", K);
+  if (rows * (int64_t)K / 8 > INT32_MAX * 64LL) return fail(MOE_ERR_SHAPE, "rows * K too large");
+  REQUIRE(x, 16, "x");
+  REQUIRE(codes, 8, "codes");
+  REQUIRE(scales, 1, "scales");
+  return hip_status(moe::launch_quant_mx(x, rows, K, codes, scales, nullptr, reinterpret_cast<hipStream_t>(stream)),
+                    "MXFP8 quantisation launch");
+}
+
+int moe_expert_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
+                      const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm,
+                      const int32_t* group_slot, uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws,
+                      uint64_t ws_bytes, void* mx_ws, uint64_t mx_ws_bytes, int32_t stages, void* ev_start,
+                      void* ev_stop, moe_stream_t stream) {
+  if (stages < 1 || stages > 3) return fail(MOE_ERR_ARG, "stages = %d: must be 1 (gate/up), 2 (down) or 3", stages);
+  int r = check_dims(d);
+  if (r) return r;
+  if (!layout) return fail(MOE_ERR_ARG, "layout is NULL");
+  moe_blob_layout want;
+  if ((r = moe_blob_layout_init_mx(d->H, d->I, &want))) return r;
+  if (memcmp(&want, layout, sizeof want) != 0)
+    return fail(MOE_ERR_ARG, "layout does not match moe_blob_layout_init_mx(H = %d, I = %d)", d->H, d->I);
+  if (!moe::use_gemm(*d))
+    return fail(MOE_ERR_SHAPE, "T * k = %lld < %d E: the MX FFN runs as the grouped GEMM only",
+                (long long)d->T * d->k, moe::kGemmMinRows);
+  REQUIRE(x, 16, "x");
+  REQUIRE(pool, 16, "pool");
+  REQUIRE(offsets, 4, "offsets");
+  REQUIRE(perm, 4, "perm");
+  REQUIRE(group_slot, 4, "group_slot");
+  REQUIRE(h, 16, "h");
+  REQUIRE(y_rows, 16, "y_rows");
+  REQUIRE(dev_status, 4, "dev_status");
+  REQUIRE(ws, 16, "ws");
+  REQUIRE(mx_ws, 256, "mx_ws");
+  const uint64_t need = moe::ws_layout(*d).total;
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace %llu bytes < required %llu", (unsigned long long)ws_bytes,
+                (unsigned long long)need);
+  const uint64_t need_mx = moe::mx_ws_layout(*d).total;
+  if (mx_ws_bytes < need_mx)
+    return fail(MOE_ERR_WORKSPACE, "MX workspace %llu bytes < required %llu", (unsigned long long)mx_ws_bytes,
+                (unsigned long long)need_mx);
+  if (pool_bytes < layout->slot_stride)
+    return fail(MOE_ERR_ARG, "pool_bytes %llu is smaller than one slot (%llu)", (unsigned long long)pool_bytes,
+                (unsigned long long)layout->slot_stride);
+  moe::FfnGeom g;
+  g.pool = static_cast<const uint8_t*>(pool);
+  g.slot_stride = layout->slot_stride;
+  g.n_slots = (int64_t)(pool_bytes / layout->slot_stride);
+  for (int m = 0; m < 3; m++) {
+    g.off_codes[m] = layout->off_codes[m];
+    g.off_scales[m] = layout->off_scales[m];
+  }
+  g.off_globals = layout->off_globals;
+  return hip_status(moe::launch_ffn_mx(*d, x, g, perm, h, y_rows, ws, mx_ws, stages, static_cast<hipEvent_t>(ev_start),
+                                       static_cast<hipEvent_t>(ev_stop), reinterpret_cast<hipStream_t>(stream)),
+                    "MX expert FFN launch");
+}
+
 int moe_combine(const moe_dims* d, const uint16_t* y_rows, const int32_t* inv_perm, const float* topk_w,
                 const float* shared_sigma, uint16_t* y, moe_stream_t stream) {
   int r = check_dims(d);

@@ -186,6 +186,25 @@ __device__ inline int block_exclusive_scan(int v, int* lds16, int* total) {
 // Sets the calling thread's moe_last_error() text; returns code.
 int record_error(int code, const char* msg);
 
+// ---- MX activation workspace (moe_expert_ffn_mx) ----------------------------
+// xq  uint8 [T][H]          E4M3 codes of x
+// xs  uint8 [T][H/32]       their E8M0 scales
+// hq  uint8 [T*k + T][I]    E4M3 codes of h (rows in group order, then the shared rows)
+// hs  uint8 [T*k + T][I/32] their E8M0 scales
+struct MxWsLayout {
+  uint64_t off_xq, off_xs, off_hq, off_hs, total;
+};
+inline MxWsLayout mx_ws_layout(const moe_dims& d) {
+  MxWsLayout w;
+  const uint64_t rows_h = (uint64_t)d.T * d.k + (uint64_t)d.T;
+  w.off_xq = 0;
+  w.off_xs = align256((uint64_t)d.T * d.H);
+  w.off_hq = align256(w.off_xs + (uint64_t)d.T * d.H / 32);
+  w.off_hs = align256(w.off_hq + rows_h * d.I);
+  w.total = align256(w.off_hs + rows_h * d.I / 32);
+  return w;
+}
+
 // ---- launchers (return hipSuccess or the launch error) ---------------------
 struct FfnGeom {
   const uint8_t* pool;
@@ -234,6 +253,16 @@ hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g
 hipError_t launch_ffn_gemm(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
                            uint16_t* y_rows, void* ws, int stages, hipEvent_t ev_start, hipEvent_t ev_stop,
                            hipStream_t s);
+// bf16 rows [rows][K] (K % 32 == 0) -> E4M3 codes [rows][K] and E8M0 scales
+// [rows][K/32] (MXFP8); ev_start (may be null) is recorded at its start.
+hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                           hipEvent_t ev_start, hipStream_t s);
+// Grouped-GEMM expert FFN on MX blobs (scaled MFMA) over the chunk list; the
+// MX workspace mx_ws (mx_ws_layout) carries the quantised activations.  Same
+// stage mask and events as launch_ffn_gemm.
+hipError_t launch_ffn_mx(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
+                         uint16_t* y_rows, void* ws, void* mx_ws, int stages, hipEvent_t ev_start, hipEvent_t ev_stop,
+                         hipStream_t s);
 hipError_t launch_combine(const moe_dims& d, const uint16_t* y_rows, const int32_t* inv_perm, const float* w,
                           const float* sigma, uint16_t* y, hipStream_t s);
 

@@ -27,9 +27,10 @@ class LayerBuffers:
     h: torch.Tensor           # bf16 [T*k+T, I]
     y_rows: torch.Tensor      # bf16 [T*k+T, H]
     y: torch.Tensor           # bf16 [T, H]
+    mx_ws: Optional[torch.Tensor] = None  # uint8 [moe_mx_workspace_bytes]: MX blobs (moe_expert_ffn_mx)
 
     @staticmethod
-    def allocate(dims: B.Dims, device="cuda") -> "LayerBuffers":
+    def allocate(dims: B.Dims, device="cuda", mx: bool = False) -> "LayerBuffers":
         T, H, I, E, k = dims.T, dims.H, dims.I, dims.E, dims.k
         i32 = dict(dtype=torch.int32, device=device)
         f32 = dict(dtype=torch.float32, device=device)
@@ -42,7 +43,8 @@ class LayerBuffers:
             status=torch.zeros(1, **i32),
             ws=torch.empty(B.moe_workspace_bytes(dims), dtype=torch.uint8, device=device),
             h=torch.empty((T * k + T, I), **bf), y_rows=torch.empty((T * k + T, H), **bf),
-            y=torch.empty((T, H), **bf))
+            y=torch.empty((T, H), **bf),
+            mx_ws=torch.empty(B.moe_mx_workspace_bytes(dims), dtype=torch.uint8, device=device) if mx else None)
 
 
 def run_layer(buf: LayerBuffers, layer: int, x: torch.Tensor, pool, pool_bytes: int, layout: B.BlobLayout,
@@ -63,6 +65,10 @@ def run_layer(buf: LayerBuffers, layer: int, x: torch.Tensor, pool, pool_bytes: 
         B.moe_route(d, x, w_router, lg_in, w_shared_gate, lg_out, buf.ids, buf.w, buf.sigma, stream)
         B.moe_group(d, layer, buf.ids, slot_table, n_slots, buf.offsets, buf.perm, buf.inv_perm, buf.group_slot,
                     buf.status, buf.ws, stream=stream)
-    B.moe_expert_ffn(d, x, pool, pool_bytes, layout, buf.offsets, buf.perm, buf.group_slot, buf.h, buf.y_rows,
-                     buf.status, buf.ws, stream=stream)
+    if buf.mx_ws is not None:   # MX blobs: layout from moe_blob_layout_init_mx
+        B.moe_expert_ffn_mx(d, x, pool, pool_bytes, layout, buf.offsets, buf.perm, buf.group_slot, buf.h, buf.y_rows,
+                            buf.status, buf.ws, buf.mx_ws, stream=stream)
+    else:
+        B.moe_expert_ffn(d, x, pool, pool_bytes, layout, buf.offsets, buf.perm, buf.group_slot, buf.h, buf.y_rows,
+                         buf.status, buf.ws, stream=stream)
     B.moe_combine(d, buf.y_rows, buf.inv_perm, buf.w, buf.sigma, buf.y, stream)

@@ -21,6 +21,12 @@ static inline SYNTH_HD uint64_t synth_code_pos(uint64_t n, int b, int K) {
   return (n >> 4) * 8ull * (uint64_t)K + 256ull * (uint64_t)(b >> 1) + 16ull * (n & 15) + 8ull * (uint64_t)(b & 1);
 }
 
+/* MX blobs: the E8M0 scale of row n, 32-value block B sits at
+ * (n / 16)(K / 2) + 64 (B / 4) + 4 (n % 16) + B % 4; codes as above. */
+static inline SYNTH_HD uint64_t synth_mx_scale_pos(uint64_t n, int B, int K) {
+  return (n >> 4) * (uint64_t)(K / 2) + 64ull * (uint64_t)(B >> 2) + 4ull * (n & 15) + (uint64_t)(B & 3);
+}
+
 static inline SYNTH_HD uint64_t synth_scale_pos(uint64_t n, int b, int K) {
   const int g = b >> 5, nc = K / 32;
   const int len = 2 * ((nc - 16 * g) < 16 ? nc - 16 * g : 16);

@@ -27,6 +27,7 @@ class Config:
     epoch_len: int = 0  # steps per hot-set epoch (0: one epoch)
     staged: bool = False  # expert blobs start in pinned host memory (two-slot ring)
     cache_frac: float = 0.0  # > 0: blobs in pinned host memory, a device LRU cache of this share of them
+    fmt: str = "nvfp4"  # expert blob format: "nvfp4" (E4M3 scale per 16, fp32 global) or "mx" (MXFP4)
     seed: int = 0
 
     @property
@@ -52,6 +53,9 @@ CONFIGS = {
     # steps, and a device cache of one eighth of the (layer, expert) blobs
     6: Config(6, "cached48x64", T=4, H=2048, I=512, E=512, k=10, L=48, router="zipf", steps=64, zipf_s=1.0,
               epoch_len=16, cache_frac=0.125),
+    # prefill8192's shapes with natively MXFP4 experts ([FreeToken] 2.1): the
+    # scaled-MFMA path (MXFP8 activations)
+    7: Config(7, "prefill8192_mx", T=8192, H=2048, I=512, E=512, k=10, L=1, router="matrix", fmt="mx"),
 }
 
 

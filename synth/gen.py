@@ -52,6 +52,8 @@ class HostGen:
         lib.synth_expert_blob.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
                                           ctypes.c_void_p]
+        lib.synth_expert_blob_mx.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         lib.synth_x.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_void_p]
         lib.synth_w_router.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -68,6 +70,13 @@ class HostGen:
         self.lib.synth_expert_blob(cfg.seed, cfg.cfg_id, layer, expert, cfg.H, cfg.I,
                                    _u64p(layout.off_codes), _u64p(layout.off_scales), int(layout.off_globals),
                                    out.ctypes.data)
+        return out
+
+    def expert_blob_mx(self, cfg: Config, layer: int, expert: int, layout) -> np.ndarray:
+        """uint8 [slot_stride]: the MX blob of (layer, expert); layout gives the offsets."""
+        out = np.zeros(int(layout.slot_stride), dtype=np.uint8)
+        self.lib.synth_expert_blob_mx(cfg.seed, cfg.cfg_id, layer, expert, cfg.H, cfg.I,
+                                      _u64p(layout.off_codes), _u64p(layout.off_scales), out.ctypes.data)
         return out
 
     def x(self, cfg: Config, layer: int, step: int = 0, T: Optional[int] = None) -> np.ndarray:
@@ -98,6 +107,7 @@ class DevGen:
         lib = ctypes.CDLL(path)
         vp, i32, i64, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64
         lib.synth_dev_pool.argtypes = [u64, i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, u64, u64, vp, vp]
+        lib.synth_dev_pool_mx.argtypes = [u64, i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, u64, vp, vp]
         lib.synth_dev_x.argtypes = [u64, i32, i32, i32, i32, i32, vp, vp]
         lib.synth_dev_w_router.argtypes = [u64, i32, i32, i32, i32, vp, vp]
         lib.synth_dev_w_shared_gate.argtypes = [u64, i32, i32, i32, vp, vp]
@@ -114,6 +124,12 @@ class DevGen:
                                             slot_table_ptr, n_slots, _u64p(layout.off_codes),
                                             _u64p(layout.off_scales), int(layout.off_globals),
                                             int(layout.slot_stride), pool_ptr, stream))
+
+    def pool_mx(self, cfg: Config, layer0: int, n_layers: int, slot_table_ptr: int, n_slots: int, layout,
+                pool_ptr: int, stream: int = 0) -> None:
+        self._check(self.lib.synth_dev_pool_mx(cfg.seed, cfg.cfg_id, layer0, n_layers, cfg.E1, cfg.H, cfg.I,
+                                               slot_table_ptr, n_slots, _u64p(layout.off_codes),
+                                               _u64p(layout.off_scales), int(layout.slot_stride), pool_ptr, stream))
 
     def x(self, cfg: Config, layer: int, step: int, out_ptr: int, stream: int = 0, T: Optional[int] = None) -> None:
         self._check(self.lib.synth_dev_x(cfg.seed, cfg.cfg_id, layer, step, cfg.T if T is None else T, cfg.H,

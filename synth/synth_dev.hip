@@ -134,6 +134,52 @@ __global__ void k_pool_layer(uint64_t seed, int cfg, int layer, const int32_t* _
   *reinterpret_cast<uint2*>(blob + g.off_codes[m] + synth_code_pos(n, b, K)) = v;
 }
 
+// MX recipe (synth_recipe.md): one thread per 32-value block.
+__global__ void k_pool_layer_mx(uint64_t seed, int cfg, int layer, const int32_t* __restrict__ slot_row,
+                                int64_t n_slots, BlobGeom g, uint8_t* __restrict__ pool) {
+  const int expert = blockIdx.y;
+  const int32_t slot = slot_row[expert];
+  if (slot < 0 || slot >= n_slots) return;
+  uint8_t* blob = pool + (uint64_t)slot * g.slot_stride;
+  const uint64_t nb_gu = (uint64_t)g.I * (g.H / 32);
+  const uint64_t gb = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gb >= 3 * nb_gu) return;
+  const int m = (int)(gb / nb_gu);
+  const uint64_t lb = gb - (uint64_t)m * nb_gu;
+  const int K = m < 2 ? g.H : g.I;
+  const int nbr = K / 32;
+  const uint64_t n = lb / nbr;
+  const int b = (int)(lb % nbr);
+  const uint64_t key = make_key(seed, 1, cfg, layer, expert, m);
+  float w[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 32; j++) {
+    const uint64_t i = n * (uint64_t)K + (uint64_t)(32 * b + j);
+    w[j] = __fmul_rn(0.02f, normal_dev(key, i));
+    amax = fmaxf(amax, fabsf(w[j]));
+  }
+  const uint32_t ef = (__float_as_uint(amax) >> 23) & 0xFFu;
+  const uint8_t sb = ef >= 2 ? (uint8_t)(ef - 2) : 0;
+  blob[g.off_scales[m] + synth_mx_scale_pos(n, b, K)] = sb;
+  const float inv = __uint_as_float((uint32_t)(254 - sb) << 23);
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const uint32_t c = (uint32_t)e2m1_encode(__fmul_rn(w[16 * h + 2 * j], inv)) |
+                         ((uint32_t)e2m1_encode(__fmul_rn(w[16 * h + 2 * j + 1], inv)) << 4);
+      if (j < 4) lo |= c << (8 * j);
+      else hi |= c << (8 * (j - 4));
+    }
+    uint2 v;
+    v.x = lo;
+    v.y = hi;
+    *reinterpret_cast<uint2*>(blob + g.off_codes[m] + synth_code_pos(n, 2 * b + h, K)) = v;
+  }
+}
+
 __global__ void k_x(uint64_t key, int64_t n, uint16_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
@@ -172,6 +218,30 @@ int synth_dev_pool(uint64_t seed, int cfg, int layer0, int n_layers, int E1, int
   dim3 grid((unsigned)((nb_all + 255) / 256), (unsigned)E1);
   for (int l = layer0; l < layer0 + n_layers; l++) {
     hipLaunchKernelGGL(k_pool_layer, grid, dim3(256), 0, stream, seed, cfg, l, slot_table_dev + (int64_t)l * E1,
+                       n_slots, g, static_cast<uint8_t*>(pool));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
+  return 0;
+}
+
+// As synth_dev_pool, with MX blobs (no globals).
+int synth_dev_pool_mx(uint64_t seed, int cfg, int layer0, int n_layers, int E1, int H, int I,
+                      const int32_t* slot_table_dev, int64_t n_slots, const uint64_t* off_codes,
+                      const uint64_t* off_scales, uint64_t slot_stride, void* pool, hipStream_t stream) {
+  BlobGeom g;
+  for (int m = 0; m < 3; m++) {
+    g.off_codes[m] = off_codes[m];
+    g.off_scales[m] = off_scales[m];
+  }
+  g.off_globals = 0;
+  g.slot_stride = slot_stride;
+  g.H = H;
+  g.I = I;
+  const uint64_t nb_all = 3ull * (uint64_t)I * (uint64_t)(H / 32);
+  dim3 grid((unsigned)((nb_all + 255) / 256), (unsigned)E1);
+  for (int l = layer0; l < layer0 + n_layers; l++) {
+    hipLaunchKernelGGL(k_pool_layer_mx, grid, dim3(256), 0, stream, seed, cfg, l, slot_table_dev + (int64_t)l * E1,
                        n_slots, g, static_cast<uint8_t*>(pool));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;

@@ -134,6 +134,50 @@ void synth_expert_blob(uint64_t seed, int cfg, int layer, int expert, int H, int
   }
 }
 
+/* MX recipe: the same weights w as gen_matrix (stream kind 1); per 32-value
+ * block, E8M0 byte sb = (fp32 exponent field of amax) - 2 (0 if that is
+ * negative), codes e2m1_encode(w * 2^(127 - sb)), the factor an exact power of
+ * two. */
+static void gen_matrix_mx(uint64_t seed, int cfg, int layer, int expert, int m, int rows, int K,
+                          uint8_t* codes, uint8_t* scales) {
+  uint64_t key = synth_key(seed, 1, cfg, layer, expert, m);
+  int nb = K / 32;
+#pragma omp parallel for schedule(static)
+  for (int n = 0; n < rows; n++) {
+    for (int b = 0; b < nb; b++) {
+      float w[32];
+      float amax = 0.0f;
+      for (int j = 0; j < 32; j++) {
+        uint64_t i = (uint64_t)n * (uint64_t)K + (uint64_t)(32 * b + j);
+        w[j] = 0.02f * normal_dev(key, i);
+        float a = fabsf(w[j]);
+        if (a > amax) amax = a;
+      }
+      uint32_t ef = (f2u(amax) >> 23) & 0xFFu;
+      uint8_t sb = ef >= 2 ? (uint8_t)(ef - 2) : 0;
+      scales[synth_mx_scale_pos((uint64_t)n, b, K)] = sb;
+      float inv = u2f((uint32_t)(254 - sb) << 23);
+      for (int h = 0; h < 2; h++) {
+        uint8_t* cp = codes + synth_code_pos((uint64_t)n, 2 * b + h, K);
+        for (int j = 0; j < 8; j++) {
+          uint8_t lo = e2m1_encode(w[16 * h + 2 * j] * inv);
+          uint8_t hi = e2m1_encode(w[16 * h + 2 * j + 1] * inv);
+          cp[j] = (uint8_t)(lo | (hi << 4));
+        }
+      }
+    }
+  }
+}
+
+/* Fill one MX blob (caller zeroes `out`). */
+void synth_expert_blob_mx(uint64_t seed, int cfg, int layer, int expert, int H, int I,
+                          const uint64_t* off_codes, const uint64_t* off_scales, uint8_t* out) {
+  for (int m = 0; m < 3; m++) {
+    int rows = m < 2 ? I : H, K = m < 2 ? H : I;
+    gen_matrix_mx(seed, cfg, layer, expert, m, rows, K, out + off_codes[m], out + off_scales[m]);
+  }
+}
+
 void synth_x(uint64_t seed, int cfg, int layer, int step, int T, int H, uint16_t* out) {
   uint64_t key = synth_key(seed, 3, cfg, layer, step, 0);
   int64_t n = (int64_t)T * H;

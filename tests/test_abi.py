@@ -134,6 +134,54 @@ def test_ffn_validation(B):
     assert B.raw_status("moe_expert_ffn_stages", d, *unaligned_pool[:-1], 2, None, None, None) == B.MOE_ERR_ALIGN
 
 
+@pytest.mark.parametrize("H,I", [(128, 128), (256, 128), (2048, 512), (4096, 2048), (384, 640), (16384, 128)])
+def test_mx_blob_layout_matches_oracle(B, H, I):
+    lay = B.moe_blob_layout_init_mx(H, I)
+    ref = O.mx_blob_layout(H, I)
+    assert tuple(lay.off_codes) == ref.off_codes and tuple(lay.off_scales) == ref.off_scales
+    assert lay.blob_bytes == ref.blob_bytes == lay.off_globals and lay.slot_stride == ref.slot_stride
+    # the codes sit where the NVFP4 blob puts them
+    assert tuple(lay.off_codes) == tuple(B.moe_blob_layout_init(H, I).off_codes)
+
+
+@pytest.mark.parametrize("H,I", [(96, 128), (128, 160), (64, 64), (16512, 128)])
+def test_mx_blob_layout_rejects_widths_off_128(B, H, I):
+    with pytest.raises(B.MoeError) as e:
+        B.moe_blob_layout_init_mx(H, I)
+    assert e.value.status == B.MOE_ERR_SHAPE
+
+
+def test_mx_workspace_matches_documented_layout(B):
+    for dims in [B.Dims(64, 256, 128, 8, 2), B.Dims(8192, 2048, 512, 512, 10), B.Dims(3, 384, 640, 4, 4)]:
+        assert B.moe_mx_workspace_bytes(dims) == B.MxWorkspace(dims).total
+
+
+def test_mx_ffn_validation(B):
+    """Rejected before any device work: decode-sized groups (the MX FFN is the
+    grouped GEMM only), an NVFP4 layout, a short MX workspace, a bad stage mask."""
+    fake = 1 << 20
+    dims = B.Dims(64, 256, 128, 8, 2)               # T k = 128 = 16 E: the GEMM path
+    d = ctypes.byref(dims)
+    lay = B.moe_blob_layout_init_mx(256, 128)
+    need = B.moe_workspace_bytes(dims)
+    need_mx = B.moe_mx_workspace_bytes(dims)
+    ok = [fake, fake, 1 << 30, ctypes.byref(lay), fake, fake, fake, fake, fake, fake, fake, need, fake, need_mx, 3,
+          None, None, None]
+
+    def st(args, dd=d):
+        return B.raw_status("moe_expert_ffn_mx", dd, *args)
+    small = B.Dims(4, 256, 128, 64, 4)              # T k = 16 < 16 E
+    assert st(ok, ctypes.byref(small)) == B.MOE_ERR_SHAPE
+    nv = B.moe_blob_layout_init(256, 128)
+    assert st(ok[:3] + [ctypes.byref(nv)] + ok[4:]) == B.MOE_ERR_ARG
+    assert st(ok[:13] + [need_mx - 256] + ok[14:]) == B.MOE_ERR_WORKSPACE
+    assert st(ok[:12] + [fake + 16] + ok[13:]) == B.MOE_ERR_ALIGN     # mx_ws must be 256-byte aligned
+    for stages in (0, 4):
+        assert st(ok[:14] + [stages] + ok[15:]) == B.MOE_ERR_ARG
+    assert B.raw_status("moe_quantize_mxfp8", fake, 4, 48, fake, fake, None) == B.MOE_ERR_SHAPE
+    assert B.raw_status("moe_quantize_mxfp8", fake + 8, 4, 64, fake, fake, None) == B.MOE_ERR_ALIGN
+
+
 def test_combine_and_ring_validation(B):
     d = ctypes.byref(_d(B))
     fake = 1 << 20

@@ -35,6 +35,26 @@ def test_quantised_weights_track_gaussian_recipe(hostgen):
         assert blockmax.min() >= 4.0 and blockmax.max() <= 6.0
 
 
+def test_mx_blob_recipe(hostgen):
+    """MX blobs hold the NVFP4 blobs' weights (same stream), re-quantised per 32
+    values: every block's largest code magnitude is 4 or 6 (amax / 2^shared in
+    [4, 8), 6 saturating), and the two decodings agree to within their
+    quantisation steps."""
+    c = Config(cfg_id=1, name="q", T=1, H=512, I=256, E=1, k=1, L=1, router="matrix")
+    lay, mlay = O.blob_layout(c.H, c.I), O.mx_blob_layout(c.H, c.I)
+    nv = hostgen.expert_blob(c, 0, 0, lay)
+    mx = hostgen.expert_blob_mx(c, 0, 0, mlay)
+    assert not mx[mlay.blob_bytes:].any()
+    for m in range(3):
+        w = O.mx_dequant(mx, mlay, m, c.H, c.I)
+        sc = O.e8m0_decode(O.mx_matrix_scales(mx, mlay, m, c.H, c.I))
+        top = np.abs(w).reshape(w.shape[0], -1, 32).max(axis=2) / sc
+        assert set(np.unique(top)) <= {4.0, 6.0}
+        w_nv = O.dequant(nv, lay, m)
+        assert np.linalg.norm(w - w_nv) / np.linalg.norm(w_nv) < 0.25
+        assert abs(w.std() / 0.02 - 1) < 0.06
+
+
 def test_activation_statistics(hostgen):
     x = O.bf16_bits_to_f64(hostgen.x(CONFIGS[4], 0, 0, T=256))
     assert abs(x.std() - 1) < 0.01 and abs(x.mean()) < 0.01 and np.abs(x).max() <= 6
