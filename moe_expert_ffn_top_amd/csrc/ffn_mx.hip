@@ -96,19 +96,17 @@ __device__ inline void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// fp32 -> OCP E4M3FN byte: the nearest value, ties to the even code, |v| >= 448
-// saturating to 448.  Below 2^-6 the codes are subnormal multiples of 2^-9
-// (a * 512 is exact, rint rounds half to even); above, the fp32 mantissa is
-// rounded to 3 bits (a carry moves into the exponent).  v is finite.
-__device__ inline uint32_t e4m3_encode(float v) {
-  const uint32_t b = __float_as_uint(v);
-  const uint32_t ab = b & 0x7FFFFFFFu;
-  const float a = __uint_as_float(ab);
-  const uint32_t rb = ab + 0x7FFFFu + ((ab >> 20) & 1u);
-  uint32_t code = (((rb >> 23) - 120u) << 3) | ((rb >> 20) & 7u);
-  code = a < 0.015625f ? (uint32_t)__builtin_rintf(a * 512.f) : code;
-  code = a >= 448.f ? 0x7Eu : code;
-  return code | ((b >> 24) & 0x80u);
+// Two fp32 values of a block with E8M0 byte sb as OCP E4M3FN bytes (lo in
+// byte 0, hi in byte 1): v / 2^(sb - 127) is exact (ldexp), clamped to
+// +-448 (the saturation), then v_cvt_scalef32_pk_fp8_f32 with scale 1 rounds
+// to the nearest E4M3 value, ties to even, subnormals included (it returns
+// NaN above the range instead of saturating, hence the clamp).
+__device__ inline uint32_t e4m3_pair(float lo, float hi, int sb) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  const float a = __builtin_amdgcn_fmed3f(ldexpf(lo, 127 - sb), -448.f, 448.f);
+  const float b = __builtin_amdgcn_fmed3f(ldexpf(hi, 127 - sb), -448.f, 448.f);
+  const s16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, a, b, 1.0f, false);
+  return (uint32_t)(uint16_t)r[0];
 }
 
 // The E8M0 byte of a block with largest magnitude m (m >= 0, fp32): the shared
@@ -154,11 +152,8 @@ __global__ __launch_bounds__(256) void k_quant_mx(const uint16_t* __restrict__ x
   m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
   m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
   const int sb = e8m0_of_amax(m);
-  uint32_t c[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) c[i] = e4m3_encode(ldexpf(f[i], 127 - sb));
-  const uint2 out = make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                               c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+  const uint2 out = make_uint2(e4m3_pair(f[0], f[1], sb) | (e4m3_pair(f[2], f[3], sb) << 16),
+                               e4m3_pair(f[4], f[5], sb) | (e4m3_pair(f[6], f[7], sb) << 16));
   reinterpret_cast<uint2*>(q)[t] = out;
   if ((t & 3) == 0) sc[t >> 2] = (uint8_t)sb;
 }
@@ -361,8 +356,9 @@ __global__ __launch_bounds__(XT) void k_ffn_mx(MxArgs a, const int4* __restrict_
               const float m = row16_max(fmaxf(fabsf(v[2 * p][e4]), fabsf(v[2 * p + 1][e4])));
               const int sb = e8m0_of_amax(m);
               const int row = row0 + e4;
-              qs[row * QSTR + 32 * p + r] = (uint8_t)e4m3_encode(ldexpf(v[2 * p][e4], 127 - sb));
-              qs[row * QSTR + 32 * p + 16 + r] = (uint8_t)e4m3_encode(ldexpf(v[2 * p + 1][e4], 127 - sb));
+              const uint32_t c2 = e4m3_pair(v[2 * p][e4], v[2 * p + 1][e4], sb);
+              qs[row * QSTR + 32 * p + r] = (uint8_t)c2;
+              qs[row * QSTR + 32 * p + 16 + r] = (uint8_t)(c2 >> 8);
               if (r == 0) ss[row * 2 + p] = (uint8_t)sb;
             }
         }
