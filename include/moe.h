@@ -388,9 +388,11 @@ int moe_blob_layout_init_mx(int32_t H, int32_t I, moe_blob_layout* out);
 
 /* Host, pure.  Bytes of the MX activation workspace that moe_expert_ffn_mx
  * needs for d.  Layout (each section from a 256-byte boundary, in order):
- *   xq [T][H] E4M3 codes of x, xs [T][H/32] their E8M0 scales,
- *   hq [T*k+T][I] E4M3 codes of h, hs [T*k+T][I/32] their E8M0 scales.
- * After a gate/up stage, hq/hs hold MXFP8(h) for the rows that stage wrote. */
+ *   xq [T][H] E4M3 codes of x, xs [T][SX] their E8M0 scales,
+ *   hq [T*k+T][I] E4M3 codes of h, hs [T*k+T][SI] their E8M0 scales,
+ * where a scale row holds H/32 (I/32) bytes and is padded to SX = H/32 (SI =
+ * I/32) rounded up to a multiple of 16 (padding bytes undefined).  After a
+ * gate/up stage, hq/hs hold MXFP8(h) for the rows that stage wrote. */
 int moe_mx_workspace_bytes(const moe_dims* d, uint64_t* out_bytes);
 
 /* MXFP8 quantisation (definition above) of bf16 rows x [rows][K] (device,

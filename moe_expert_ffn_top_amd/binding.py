@@ -272,11 +272,13 @@ class MxWorkspace:
             return (v + 255) // 256 * 256
         T, H, I, k = dims.T, dims.H, dims.I, dims.k
         rows_h = T * k + T
+        self.xs_stride = (H // 32 + 15) // 16 * 16
+        self.hs_stride = (I // 32 + 15) // 16 * 16
         self.off_xq = 0
         self.off_xs = a256(T * H)
-        self.off_hq = a256(self.off_xs + T * H // 32)
+        self.off_hq = a256(self.off_xs + T * self.xs_stride)
         self.off_hs = a256(self.off_hq + rows_h * I)
-        self.total = a256(self.off_hs + rows_h * I // 32)
+        self.total = a256(self.off_hs + rows_h * self.hs_stride)
 
 
 def moe_mx_workspace_bytes(dims: Dims) -> int:

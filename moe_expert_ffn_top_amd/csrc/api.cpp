@@ -432,7 +432,8 @@ int moe_quantize_mxfp8(const uint16_t* x, int64_t rows, int32_t K, uint8_t* code
   REQUIRE(x, 16, "x");
   REQUIRE(codes, 8, "codes");
   REQUIRE(scales, 1, "scales");
-  return hip_status(moe::launch_quant_mx(x, rows, K, codes, scales, nullptr, reinterpret_cast<hipStream_t>(stream)),
+  return hip_status(moe::launch_quant_mx(x, rows, K, codes, scales, K / 32, nullptr,
+                                         reinterpret_cast<hipStream_t>(stream)),
                     "MXFP8 quantisation launch");
 }
 

@@ -25,8 +25,11 @@
 //        A   two 1 KB halves per 16-row block.  Lane r + 16 q of half hf holds
 //            row r, K 64 hf + 16 q .. + 15: the two 16-byte pieces of the FP8
 //            operand.
-//        scales  one dword per row (column) holding the step's four E8M0
-//            bytes; lane (r, q) shifts byte q down (the MFMA reads byte 0).
+//        scales  per step one dword per B column holding the step's four E8M0
+//            bytes; the A rows' scales come every four steps, 16 bytes per
+//            row, into a two-slot ring (one gathered 16-byte load per row
+//            instead of four 4-byte ones).  Lane (r, q) shifts byte q of its
+//            dword down (the MFMA reads byte 0).
 //    - Four consumer wavefronts read fragments (64 lanes x 16 contiguous bytes,
 //      conflict-free) and issue one scaled MFMA per (16-row block, 16-column
 //      block) per step.
@@ -53,10 +56,12 @@ constexpr int NBUF = 3;
 // one LDS buffer
 constexpr int A_OFF = 0;                       // FP8 A, operand order: 16 row blocks x 2 KB
 constexpr int B_OFF = A_OFF + XM * XK;         // FP4 B, operand order: 8 column blocks x 1 KB
-constexpr int AS_OFF = B_OFF + XC * XK / 2;    // A scales: a dword per row
-constexpr int BS_OFF = AS_OFF + XM * 4;        // B scales: a dword per column
-constexpr int BUF_BYTES = BS_OFF + XC * 4;     // 42496
-constexpr int LDS_BYTES = NBUF * BUF_BYTES;    // 127488
+constexpr int BS_OFF = B_OFF + XC * XK / 2;    // B scales: a dword per column
+constexpr int BUF_BYTES = BS_OFF + XC * 4;     // 41472
+// A scales of four steps: [row][4 dwords], two slots
+constexpr int ASG_OFF = NBUF * BUF_BYTES;
+constexpr int ASG_SLOT = XM * 16;
+constexpr int LDS_BYTES = ASG_OFF + 2 * ASG_SLOT;  // 132608
 // epilogue tiles (in the buffers, free after the last step)
 constexpr int QSTR = 80;  // bytes per row of the code tile: rows 4 apart land 16 banks apart
 
@@ -74,6 +79,8 @@ struct MxArgs {
   int32_t H, I, k, Tk;  // Tk = T * k: routed rows; rows from Tk on are the shared group's
   int32_t n_ut;         // column tiles per chunk
   int32_t nk;           // K steps
+  int32_t as_stride;    // bytes per row of the A scales (a multiple of 16)
+  int32_t hs_stride;    // bytes per row of the h scales written by gate/up
 };
 
 // One LDS DMA instruction: lane l's 16 (4) bytes at src land at LDS byte
@@ -132,10 +139,12 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
 
 __device__ inline float bf16_round(float v) { return (float)(__bf16)v; }
 
-// x [rows][K] bf16 -> codes [rows][K] E4M3 and scales [rows][K/32] E8M0.
-// Thread t takes 8 consecutive values; the four threads of a 32-value block
-// are one DPP quad (K % 32 == 0, so quads never straddle rows).
-__global__ __launch_bounds__(256) void k_quant_mx(const uint16_t* __restrict__ x, int64_t n8, uint8_t* __restrict__ q,
+// x [rows][K] bf16 -> codes [rows][K] E4M3 and scales [rows][stride] E8M0
+// (K/32 of them per row).  Thread t takes 8 consecutive values (tpr = K/8
+// threads per row); the four threads of a 32-value block are one DPP quad
+// (K % 32 == 0, so quads never straddle rows).
+__global__ __launch_bounds__(256) void k_quant_mx(const uint16_t* __restrict__ x, int64_t n8, int32_t tpr,
+                                                  int32_t stride, uint8_t* __restrict__ q,
                                                   uint8_t* __restrict__ sc) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= n8) return;  // whole quads leave together (n8 % 4 == 0)
@@ -155,7 +164,7 @@ __global__ __launch_bounds__(256) void k_quant_mx(const uint16_t* __restrict__ x
   const uint2 out = make_uint2(e4m3_pair(f[0], f[1], sb) | (e4m3_pair(f[2], f[3], sb) << 16),
                                e4m3_pair(f[4], f[5], sb) | (e4m3_pair(f[6], f[7], sb) << 16));
   reinterpret_cast<uint2*>(q)[t] = out;
-  if ((t & 3) == 0) sc[t >> 2] = (uint8_t)sb;
+  if ((t & 3) == 0) sc[(t / tpr) * stride + (t % tpr) / 4] = (uint8_t)sb;
 }
 
 template <bool GATEUP>
@@ -190,7 +199,6 @@ __global__ __launch_bounds__(XT) void k_ffn_mx(MxArgs a, const int4* __restrict_
   if (wave >= 4) {
     // ---------------- producer ----------------
     const int pw = wave - 4;
-    const int kb = K / 32;  // scale bytes per A row
     // A rows past n load row n - 1 (their outputs are dropped)
     auto arow = [&](int row) -> int64_t {
       const int p = p0 + min(row, n - 1);
@@ -199,7 +207,7 @@ __global__ __launch_bounds__(XT) void k_ffn_mx(MxArgs a, const int4* __restrict_
     const uint8_t* asrc[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) asrc[i] = aq + arow(16 * (pw + 4 * i) + r) * K + 16 * q;
-    const uint8_t* ssrc = as + arow(64 * pw + lane) * kb;
+    const uint8_t* ssrc = as + arow(64 * pw + lane) * a.as_stride;
     // B: column blocks 2 pw and 2 pw + 1 (gate/up: blocks 0..3 gate, 4..7 up,
     // the same units)
     auto bunit = [&](int cb) { return u0 + 16 * (GATEUP ? (cb & 3) : cb); };
@@ -217,7 +225,7 @@ __global__ __launch_bounds__(XT) void k_ffn_mx(MxArgs a, const int4* __restrict_
 
     auto run = [&](auto na_c) __attribute__((always_inline)) {
       constexpr int NA = decltype(na_c)::value;  // live A blocks of this wavefront: pw + 4 i, i < NA
-      constexpr int N = 2 * NA + 3;              // DMA instructions per step (+1 on wavefronts 0 and 1)
+      constexpr int N = 2 * NA + 2;  // DMA instructions per step (+1 on wavefronts 0 and 1, +1 every fourth step)
       auto issue = [&](int s, int bi) __attribute__((always_inline)) {
         const uint32_t buf = lds0 + (uint32_t)(bi * BUF_BYTES);
 #pragma unroll
@@ -229,18 +237,27 @@ __global__ __launch_bounds__(XT) void k_ffn_mx(MxArgs a, const int4* __restrict_
 #pragma unroll
         for (int j = 0; j < 2; j++)
           dma16(bsrc[j] + 1024 * s, __builtin_amdgcn_readfirstlane(buf + B_OFF + (uint32_t)(2 * pw + j) * 1024u));
-        dma4(ssrc + 4 * s, __builtin_amdgcn_readfirstlane(buf + AS_OFF + 256u * (uint32_t)pw));
         if (pw < 2) dma4(bssrc + 64 * s, __builtin_amdgcn_readfirstlane(buf + BS_OFF + 256u * (uint32_t)pw));
+        if ((s & 3) == 0)  // the A scales of steps s .. s + 3 (the row's 16 bytes from 4 s)
+          dma16(ssrc + 4 * s, __builtin_amdgcn_readfirstlane(lds0 + ASG_OFF + (uint32_t)(((s >> 2) & 1) * ASG_SLOT) +
+                                                            1024u * (uint32_t)pw));
       };
-      // step s + 1 has landed once at most one step's instructions are in flight
-      auto wait_next = [&]() __attribute__((always_inline)) {
-        if (pw < 2) wait_vm<N + 1>();
-        else wait_vm<N>();
+      // the step before step s has landed once at most step s's instructions
+      // are in flight
+      auto wait_next = [&](int s) __attribute__((always_inline)) {
+        const bool g = (s & 3) == 0;
+        if (pw < 2) {
+          if (g) wait_vm<N + 2>();
+          else wait_vm<N + 1>();
+        } else {
+          if (g) wait_vm<N + 1>();
+          else wait_vm<N>();
+        }
       };
       issue(0, 0);
       if (a.nk > 1) {
         issue(1, 1);
-        wait_next();
+        wait_next(1);
       } else {
         wait_vm<0>();
       }
@@ -248,11 +265,12 @@ __global__ __launch_bounds__(XT) void k_ffn_mx(MxArgs a, const int4* __restrict_
       int bi = 2;  // buffer of step s + 2
       for (int s = 0; s < a.nk; s++) {
         // buffer (s + 2) % 3 was last read in step s - 1, which every consumer
-        // finished before the barrier just passed
+        // finished before the barrier just passed; so was the A-scale slot of
+        // step s + 2 (last read in step s - 6)
         if (s + 2 < a.nk) {
           issue(s + 2, bi);
           bi = bi == 2 ? 0 : bi + 1;
-          wait_next();
+          wait_next(s + 2);
         } else {
           wait_vm<0>();
         }
@@ -297,7 +315,8 @@ __global__ __launch_bounds__(XT) void k_ffn_mx(MxArgs a, const int4* __restrict_
           const i32x4 lo = *reinterpret_cast<const i32x4*>(bb + A_OFF + rbk * 2048 + 16 * lane);
           const i32x4 hi = *reinterpret_cast<const i32x4*>(bb + A_OFF + rbk * 2048 + 1024 + 16 * lane);
           fa[rb] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          sa[rb] = (int)(*reinterpret_cast<const uint32_t*>(bb + AS_OFF + (16 * rbk + r) * 4) >> (8 * q));
+          sa[rb] = (int)(*reinterpret_cast<const uint32_t*>(smem + ASG_OFF + ((s >> 2) & 1) * ASG_SLOT +
+                                                            (16 * rbk + r) * 16 + 4 * (s & 3)) >> (8 * q));
         }
 #pragma unroll
         for (int cb = 0; cb < 8; cb++) {
@@ -398,7 +417,7 @@ __global__ __launch_bounds__(XT) void k_ffn_mx(MxArgs a, const int4* __restrict_
             *reinterpret_cast<const uint4*>(&qs[row * QSTR + 16 * sg]);
       }
       for (int row = tid; row < n; row += XT)
-        *reinterpret_cast<uint16_t*>(hs + (int64_t)(p0 + row) * (units / 32) + u0 / 32) =
+        *reinterpret_cast<uint16_t*>(hs + (int64_t)(p0 + row) * a.hs_stride + u0 / 32) =
             *reinterpret_cast<const uint16_t*>(&ss[row * 2]);
     }
   }
@@ -407,14 +426,15 @@ __global__ __launch_bounds__(XT) void k_ffn_mx(MxArgs a, const int4* __restrict_
 }  // namespace
 
 hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
-                           hipEvent_t ev_start, hipStream_t s) {
+                           int32_t scale_stride, hipEvent_t ev_start, hipStream_t s) {
   const int64_t n8 = rows * (K / 8);
   if (n8 == 0) return hipSuccess;
   const dim3 grid((unsigned)((n8 + 255) / 256)), block(256);
+  const int32_t tpr = K / 8;
   if (ev_start)
-    hipExtLaunchKernelGGL(k_quant_mx, grid, block, 0, s, ev_start, nullptr, 0, x, n8, codes, scales);
+    hipExtLaunchKernelGGL(k_quant_mx, grid, block, 0, s, ev_start, nullptr, 0, x, n8, tpr, scale_stride, codes, scales);
   else
-    hipLaunchKernelGGL(k_quant_mx, grid, block, 0, s, x, n8, codes, scales);
+    hipLaunchKernelGGL(k_quant_mx, grid, block, 0, s, x, n8, tpr, scale_stride, codes, scales);
   return hipGetLastError();
 }
 
@@ -445,13 +465,15 @@ hipError_t launch_ffn_mx(const moe_dims& d, const uint16_t* x, const FfnGeom& g,
     const bool first = gu || !(stages & 1), last = !gu || !(stages & 2);
     hipEvent_t e0 = first ? ev_start : nullptr, e1 = last ? ev_stop : nullptr;
     if (gu) {
-      const hipError_t e = launch_quant_mx(x, d.T, d.H, xq, xs, e0, s);
+      const hipError_t e = launch_quant_mx(x, d.T, d.H, xq, xs, ml.xs_stride, e0, s);
       if (e != hipSuccess) return e;
       e0 = nullptr;
     }
     const int K = gu ? d.H : d.I, units = gu ? d.I : d.H;
     a.n_ut = units / (gu ? XC / 2 : XC);
     a.nk = K / XK;
+    a.as_stride = gu ? ml.xs_stride : ml.hs_stride;
+    a.hs_stride = ml.hs_stride;
     const int64_t groups8 = (wl.max_chunks + 7) / 8;
     const dim3 grid((unsigned)(groups8 * 8 * a.n_ut)), block(XT);
     const uint8_t* aq = gu ? xq : hq;

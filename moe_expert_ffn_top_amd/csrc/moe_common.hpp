@@ -188,20 +188,23 @@ int record_error(int code, const char* msg);
 
 // ---- MX activation workspace (moe_expert_ffn_mx) ----------------------------
 // xq  uint8 [T][H]          E4M3 codes of x
-// xs  uint8 [T][H/32]       their E8M0 scales
+// xs  uint8 [T][xs_stride]  their E8M0 scales (H/32 per row, rows padded to 16 bytes)
 // hq  uint8 [T*k + T][I]    E4M3 codes of h (rows in group order, then the shared rows)
-// hs  uint8 [T*k + T][I/32] their E8M0 scales
+// hs  uint8 [T*k + T][hs_stride] their E8M0 scales (I/32 per row, padded likewise)
 struct MxWsLayout {
   uint64_t off_xq, off_xs, off_hq, off_hs, total;
+  int32_t xs_stride, hs_stride;
 };
 inline MxWsLayout mx_ws_layout(const moe_dims& d) {
   MxWsLayout w;
   const uint64_t rows_h = (uint64_t)d.T * d.k + (uint64_t)d.T;
+  w.xs_stride = (d.H / 32 + 15) & ~15;
+  w.hs_stride = (d.I / 32 + 15) & ~15;
   w.off_xq = 0;
   w.off_xs = align256((uint64_t)d.T * d.H);
-  w.off_hq = align256(w.off_xs + (uint64_t)d.T * d.H / 32);
+  w.off_hq = align256(w.off_xs + (uint64_t)d.T * w.xs_stride);
   w.off_hs = align256(w.off_hq + rows_h * d.I);
-  w.total = align256(w.off_hs + rows_h * d.I / 32);
+  w.total = align256(w.off_hs + rows_h * w.hs_stride);
   return w;
 }
 
@@ -256,7 +259,7 @@ hipError_t launch_ffn_gemm(const moe_dims& d, const uint16_t* x, const FfnGeom& 
 // bf16 rows [rows][K] (K % 32 == 0) -> E4M3 codes [rows][K] and E8M0 scales
 // [rows][K/32] (MXFP8); ev_start (may be null) is recorded at its start.
 hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
-                           hipEvent_t ev_start, hipStream_t s);
+                           int32_t scale_stride, hipEvent_t ev_start, hipStream_t s);
 // Grouped-GEMM expert FFN on MX blobs (scaled MFMA) over the chunk list; the
 // MX workspace mx_ws (mx_ws_layout) carries the quantised activations.  Same
 // stage mask and events as launch_ffn_gemm.

@@ -145,12 +145,13 @@ class MxCase:
         c, m = self.cfg, self.mws
         xc, xs, _ = O.mxfp8_quantize(O.bf16_bits_to_f64(self.x_bits))
         assert np.array_equal(self.ws_section(m.off_xq, c.T * c.H).reshape(c.T, c.H), xc), "x codes"
-        assert np.array_equal(self.ws_section(m.off_xs, c.T * c.H // 32).reshape(c.T, c.H // 32), xs), "x scales"
+        gxs = self.ws_section(m.off_xs, c.T * m.xs_stride).reshape(c.T, m.xs_stride)[:, :c.H // 32]
+        assert np.array_equal(gxs, xs), "x scales"
         nr = c.T * c.k + c.T
         h = bf16_to_f64(self.buf.h)
         hc, hs, _ = O.mxfp8_quantize(h)
         gq = self.ws_section(m.off_hq, nr * c.I).reshape(nr, c.I)
-        gs = self.ws_section(m.off_hs, nr * c.I // 32).reshape(nr, c.I // 32)
+        gs = self.ws_section(m.off_hs, nr * m.hs_stride).reshape(nr, m.hs_stride)[:, :c.I // 32]
         rows = np.arange(nr) if rows is None else np.asarray(rows)
         bad = np.nonzero(np.any(gq[rows] != hc[rows], axis=1) | np.any(gs[rows] != hs[rows], axis=1))[0]
         assert bad.size == 0, "h codes/scales differ on %d rows, first %s" % (bad.size, rows[bad[:5]])
@@ -292,7 +293,8 @@ def test_prefill8192_mx_full_size(B, hostgen):
     h = bf16_to_f64(buf.h.index_select(0, rt))
     hc, hs, _ = O.mxfp8_quantize(h)
     gq = buf.mx_ws[m.off_hq:m.off_hq + (cfg.T * cfg.k + cfg.T) * cfg.I].view(-1, cfg.I).index_select(0, rt)
-    gs = buf.mx_ws[m.off_hs:m.off_hs + (cfg.T * cfg.k + cfg.T) * cfg.I // 32].view(-1, cfg.I // 32).index_select(0, rt)
+    gs = buf.mx_ws[m.off_hs:m.off_hs + (cfg.T * cfg.k + cfg.T) * m.hs_stride].view(-1, m.hs_stride)[:, :cfg.I // 32]
+    gs = gs.index_select(0, rt)
     assert np.array_equal(gq.cpu().numpy(), hc) and np.array_equal(gs.cpu().numpy(), hs)
     del wl
     torch.cuda.empty_cache()
