@@ -414,7 +414,8 @@ int moe_quantize_mxfp8(const uint16_t* x, int64_t rows, int32_t K, uint8_t* code
  * grouped GEMM only: MOE_ERR_SHAPE unless T*k >= 16 E (the group sizes for
  * which moe_group writes the GEMM's chunk list).  layout must equal
  * moe_blob_layout_init_mx(H, I).  stages, ev_start and ev_stop as for
- * moe_expert_ffn_stages; the gate/up stage also quantises x.  Every other
+ * moe_expert_ffn_stages, except that the events bracket the GEMM kernels
+ * only; the gate/up stage first quantises x (a kernel before them).  Every other
  * argument and the handling of missing slots as for moe_expert_ffn. */
 int moe_expert_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool,
                       uint64_t pool_bytes, const moe_blob_layout* layout,

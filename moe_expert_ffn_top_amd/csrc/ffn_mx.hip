@@ -464,10 +464,9 @@ hipError_t launch_ffn_mx(const moe_dims& d, const uint16_t* x, const FfnGeom& g,
     const bool gu = stage == 0;
     const bool first = gu || !(stages & 1), last = !gu || !(stages & 2);
     hipEvent_t e0 = first ? ev_start : nullptr, e1 = last ? ev_stop : nullptr;
-    if (gu) {
-      const hipError_t e = launch_quant_mx(x, d.T, d.H, xq, xs, ml.xs_stride, e0, s);
+    if (gu) {  // the events bracket the GEMMs alone
+      const hipError_t e = launch_quant_mx(x, d.T, d.H, xq, xs, ml.xs_stride, nullptr, s);
       if (e != hipSuccess) return e;
-      e0 = nullptr;
     }
     const int K = gu ? d.H : d.I, units = gu ? d.I : d.H;
     a.n_ut = units / (gu ? XC / 2 : XC);
