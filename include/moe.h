@@ -392,7 +392,11 @@ int moe_blob_layout_init_mx(int32_t H, int32_t I, moe_blob_layout* out);
  *   hq [T*k+T][I] E4M3 codes of h, hs [T*k+T][SI] their E8M0 scales,
  * where a scale row holds H/32 (I/32) bytes and is padded to SX = H/32 (SI =
  * I/32) rounded up to a multiple of 16 (padding bytes undefined).  After a
- * gate/up stage, hq/hs hold MXFP8(h) for the rows that stage wrote. */
+ * gate/up stage, hq/hs hold MXFP8(h) for the rows that stage wrote.  That is
+ * the layout when T*k >= 16 E (the grouped GEMM).  Below, the FFN streams the
+ * weights through bf16 MFMAs instead, and the workspace holds
+ *   xb [T][H] bf16, the values of MXFP8(x); hb [T*k+T][I] bf16, those of
+ *   MXFP8(h) (written by the down stage before it reads them). */
 int moe_mx_workspace_bytes(const moe_dims* d, uint64_t* out_bytes);
 
 /* MXFP8 quantisation (definition above) of bf16 rows x [rows][K] (device,
@@ -410,9 +414,11 @@ int moe_quantize_mxfp8(const uint16_t* x, int64_t rows, int32_t K, uint8_t* code
  *   Y[p,n] = bf16_rne( sum_i h^[i] Wd[n,i] )                       (R3)
  * Products of codes and scales are exact; sums are fp32.  The MX workspace
  * mx_ws (device, 256-byte aligned, at least moe_mx_workspace_bytes; contents
- * as documented there) carries x^ and h^ between the stages.  It runs as the
- * grouped GEMM only: MOE_ERR_SHAPE unless T*k >= 16 E (the group sizes for
- * which moe_group writes the GEMM's chunk list).  layout must equal
+ * as documented there) carries x^ and h^ between the stages.  As for
+ * moe_expert_ffn, groups averaging >= 16 rows (T*k >= 16 E) run as a grouped
+ * GEMM on the scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, FP8 x FP4 with
+ * their E8M0 scales); smaller ones stream the weights through bf16 MFMAs on
+ * the bf16 values of x^ and h^ (exact).  layout must equal
  * moe_blob_layout_init_mx(H, I).  stages, ev_start and ev_stop as for
  * moe_expert_ffn_stages, except that the events bracket the GEMM kernels
  * only; the gate/up stage first quantises x (a kernel before them).  Every other

@@ -274,11 +274,19 @@ class MxWorkspace:
         rows_h = T * k + T
         self.xs_stride = (H // 32 + 15) // 16 * 16
         self.hs_stride = (I // 32 + 15) // 16 * 16
-        self.off_xq = 0
-        self.off_xs = a256(T * H)
-        self.off_hq = a256(self.off_xs + T * self.xs_stride)
-        self.off_hs = a256(self.off_hq + rows_h * I)
-        self.total = a256(self.off_hs + rows_h * self.hs_stride)
+        self.gemm = T * k >= 16 * dims.E   # the grouped-GEMM layout; else the bf16 one
+        if self.gemm:
+            self.off_xq = 0
+            self.off_xs = a256(T * H)
+            self.off_hq = a256(self.off_xs + T * self.xs_stride)
+            self.off_hs = a256(self.off_hq + rows_h * I)
+            self.total = a256(self.off_hs + rows_h * self.hs_stride)
+            self.off_xb = self.off_hb = self.total
+        else:
+            self.off_xb = 0
+            self.off_hb = a256(T * H * 2)
+            self.total = a256(self.off_hb + rows_h * I * 2)
+            self.off_xq = self.off_xs = self.off_hq = self.off_hs = self.total
 
 
 def moe_mx_workspace_bytes(dims: Dims) -> int:

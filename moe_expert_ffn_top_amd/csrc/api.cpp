@@ -450,9 +450,6 @@ int moe_expert_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool, ui
   if ((r = moe_blob_layout_init_mx(d->H, d->I, &want))) return r;
   if (memcmp(&want, layout, sizeof want) != 0)
     return fail(MOE_ERR_ARG, "layout does not match moe_blob_layout_init_mx(H = %d, I = %d)", d->H, d->I);
-  if (!moe::use_gemm(*d))
-    return fail(MOE_ERR_SHAPE, "T * k = %lld < %d E: the MX FFN runs as the grouped GEMM only",
-                (long long)d->T * d->k, moe::kGemmMinRows);
   REQUIRE(x, 16, "x");
   REQUIRE(pool, 16, "pool");
   REQUIRE(offsets, 4, "offsets");
@@ -483,8 +480,16 @@ int moe_expert_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool, ui
     g.off_scales[m] = layout->off_scales[m];
   }
   g.off_globals = layout->off_globals;
-  return hip_status(moe::launch_ffn_mx(*d, x, g, perm, h, y_rows, ws, mx_ws, stages, static_cast<hipEvent_t>(ev_start),
-                                       static_cast<hipEvent_t>(ev_stop), reinterpret_cast<hipStream_t>(stream)),
+  const hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (moe::use_gemm(*d))
+    return hip_status(moe::launch_ffn_mx(*d, x, g, perm, h, y_rows, ws, mx_ws, stages, e0, e1, st),
+                      "MX expert FFN launch");
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || n_cu <= 0)
+    return fail(MOE_ERR_HIP, "cannot query the device's compute-unit count");
+  return hip_status(moe::launch_ffn_dec_mx(*d, x, g, perm, h, y_rows, ws, mx_ws, n_cu, stages, e0, e1, st),
                     "MX expert FFN launch");
 }
 

@@ -29,6 +29,11 @@
 //    the registers of one A fragment.
 //  - SPLITK wavefronts of a unit block split K; partials meet in LDS.  A
 //    wavefront's share of K is covered in K rounds of S steps.
+//  - MX blobs ([FreeToken] 2.1: natively MXFP4 experts, read as OCP MX): one
+//    E8M0 scale 2^(b - 127) per 32-value chunk, the four of a 128-value group
+//    in one dword per row, and no global scales.  The A rows are then the
+//    bf16 values of MXFP8(x) and MXFP8(h) (exact in bf16), so the products
+//    stay exact and the sums fp32, as on the NVFP4 path.
 #include <hip/hip_ext.h>
 #include <math.h>
 
@@ -148,7 +153,7 @@ __device__ inline Desc load_desc(const DecArgs& a, int item, int c, const int4* 
   return d;
 }
 
-template <bool GATEUP, int U, bool FS>
+template <bool GATEUP, int U, bool FS, bool MX>
 __device__ inline Item<(GATEUP ? 2 : 1) * U> make_item(const DecArgs& a, const Desc& d, int n_items, int wub, int c,
                                                         const uint8_t* __restrict__ pool,
                                                         const uint16_t* __restrict__ ain) {
@@ -185,23 +190,32 @@ __device__ inline Item<(GATEUP ? 2 : 1) * U> make_item(const DecArgs& a, const D
     // the lane's row in its 16-row block (blob tiling in moe_common.hpp)
     const int64_t ub = unit >> 4;
     it.codes[m] = it.resident ? blob + a.off_codes[mi] + ub * (8 * K) + c * 16 : pool;
-    it.scales[m] = it.resident ? blob + a.off_scales[mi] + ub * K + (FS ? c * 32 + q * 8 : 0) : pool;
+    if (MX)  // the row's dword of group g at 64 g + 4 c of its block's K/2 bytes
+      it.scales[m] = it.resident ? blob + a.off_scales[mi] + ub * (K / 2) + c * 4 : pool;
+    else
+      it.scales[m] = it.resident ? blob + a.off_scales[mi] + ub * K + (FS ? c * 32 + q * 8 : 0) : pool;
   }
-  cptr<float> glob = as_const(reinterpret_cast<const float*>(blob + a.off_globals));
-  it.g0 = it.resident ? glob[GATEUP ? 0 : 2] : 0.f;
-  it.g1 = (GATEUP && it.resident) ? glob[1] : 0.f;
+  if (MX) {  // no globals (off_globals is the end of the blob)
+    it.g0 = it.resident ? 1.f : 0.f;
+    it.g1 = (GATEUP && it.resident) ? 1.f : 0.f;
+  } else {
+    cptr<float> glob = as_const(reinterpret_cast<const float*>(blob + a.off_globals));
+    it.g0 = it.resident ? glob[GATEUP ? 0 : 2] : 0.f;
+    it.g1 = (GATEUP && it.resident) ? glob[1] : 0.f;
+  }
   return it;
 }
 
 // Unconditional, address-clamped weight loads (exact wait counts): invalid
 // chunks are zeroed through their scale.  Without whole groups (FS false) the
 // scale dword is the aligned one holding the chunk's two bytes.
-template <int NS, bool FS>
+template <int NS, bool FS, bool MX>
 __device__ inline void load_step(Step<NS>& s, const Item<NS>& it, int ch, int nc, int c) {
 #pragma unroll
   for (int m = 0; m < NS; m++) {
     s.w[m] = *reinterpret_cast<const uint4*>(it.codes[m] + (int64_t)ch * 256);
-    if (!FS) s.sc[m] = *reinterpret_cast<const uint32_t*>(it.scales[m] + (blob_sc_off(ch, nc, c) & ~3));
+    if (MX) s.sc[m] = *reinterpret_cast<const uint32_t*>(it.scales[m] + 64 * (ch >> 2));
+    else if (!FS) s.sc[m] = *reinterpret_cast<const uint32_t*>(it.scales[m] + (blob_sc_off(ch, nc, c) & ~3));
   }
 }
 
@@ -222,13 +236,22 @@ __device__ inline void load_a(uint4* xa, const Item<NS>& it, int ch) {
   }
 }
 
-// sc[m]: the step's two scales of stream m in the low 16 bits
-template <int NS>
+// sc[m]: the step's two E4M3 scales of stream m in the low 16 bits, or (MX)
+// its E8M0 byte in the low 8
+template <int NS, bool MX>
 __device__ inline void mma_step(const Step<NS>& s, const uint4* xa, const uint32_t* sc, bool valid, f32x4* acc) {
 #pragma unroll
   for (int m = 0; m < NS; m++) {
     const uint32_t sw = valid ? sc[m] : 0u;
-    const float s0 = e4m3_to_f32<0>(sw), s1 = e4m3_to_f32<1>(sw);
+    float s0, s1;
+    if (MX) {
+      // 2^(b - 127); b = 0 is the subnormal 2^-127
+      const uint32_t b = sw & 0xFFu;
+      s0 = s1 = valid ? __uint_as_float(b ? b << 23 : 0x00400000u) : 0.f;
+    } else {
+      s0 = e4m3_to_f32<0>(sw);
+      s1 = e4m3_to_f32<1>(sw);
+    }
     acc[m] = mfma16x16x32(as_bf16x8(xa[0]), dequant8(s.w[m].x, s0), acc[m]);
     acc[m] = mfma16x16x32(as_bf16x8(xa[1]), dequant8(s.w[m].y, s0), acc[m]);
     acc[m] = mfma16x16x32(as_bf16x8(xa[2]), dequant8(s.w[m].z, s1), acc[m]);
@@ -239,7 +262,7 @@ __device__ inline void mma_step(const Step<NS>& s, const uint4* xa, const uint32
 // S: 128-value steps per wavefront and K round; U unit blocks per wavefront;
 // SPLITK wavefronts per unit block (4 / SPLITK unit-block groups per item);
 // FS: every K round of every wavefront is one whole 512-value group (S = 4).
-template <bool GATEUP, int SPLITK, int S, int U, bool FS>
+template <bool GATEUP, int SPLITK, int S, int U, bool FS, bool MX>
 __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restrict__ tiles,
                                                  const int32_t* __restrict__ tile_tok,
                                                  const int32_t* __restrict__ n_tiles,
@@ -268,7 +291,7 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
   const int G = gridDim.x;
   int item = blockIdx.x, kr = 0;
   Item<NS> cur =
-      make_item<GATEUP, U, FS>(a, load_desc<GATEUP>(a, item, c, tiles, tile_tok), n_items, wub, c, pool, ain);
+      make_item<GATEUP, U, FS, MX>(a, load_desc<GATEUP>(a, item, c, tiles, tile_tok), n_items, wub, c, pool, ain);
   if (!cur.live) return;
   // descriptor of unit 1
   Desc dn = load_desc<GATEUP>(a, nkr > 1 ? item : item + G, c, tiles, tile_tok);
@@ -289,7 +312,7 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
   uint2 scn[NS];  // FS: the scales of the next unit to compute
   if (FS) load_sc<NS>(scn, cur, DEC_GRP(0));
 #pragma unroll
-  for (int s = 0; s < S; s++) load_step<NS, FS>(fb[s], cur, min(DEC_CH(0, s), c1 - 1), nc, c);
+  for (int s = 0; s < S; s++) load_step<NS, FS, MX>(fb[s], cur, min(DEC_CH(0, s), c1 - 1), nc, c);
   f32x4 acc[NS];
 
   while (cur.live) {
@@ -298,7 +321,7 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
     // the next unit (derived from the descriptor fetched a unit ago; the same
     // item again when it is a further K round), then the descriptor of the
     // unit after it
-    const Item<NS> nxt = make_item<GATEUP, U, FS>(a, dn, n_items, wub, c, pool, ain);
+    const Item<NS> nxt = make_item<GATEUP, U, FS, MX>(a, dn, n_items, wub, c, pool, ain);
     __builtin_amdgcn_sched_barrier(0);
     dn = load_desc<GATEUP>(a, item2, c, tiles, tile_tok);
     kr2 = kr2 + 1 == nkr ? 0 : kr2 + 1;
@@ -319,9 +342,10 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
       uint32_t sw[NS];
 #pragma unroll
       for (int m = 0; m < NS; m++)
-        sw[m] = FS ? ((s < 2 ? scc[m].x : scc[m].y) >> (16 * (s & 1)))
-                   : (fb[s].sc[m] >> (16 * ((blob_sc_off(chc, nc, c) >> 1) & 1)));
-      mma_step<NS>(fb[s], xa[s], sw, !kempty && chr < c1 && cur.resident, acc);
+        sw[m] = MX   ? (fb[s].sc[m] >> (8 * (chc & 3)))
+                : FS ? ((s < 2 ? scc[m].x : scc[m].y) >> (16 * (s & 1)))
+                     : (fb[s].sc[m] >> (16 * ((blob_sc_off(chc, nc, c) >> 1) & 1)));
+      mma_step<NS, MX>(fb[s], xa[s], sw, !kempty && chr < c1 && cur.resident, acc);
 #ifdef MOE_DEC_TIMING
       if (s == 0 && n_done == 0) {
         __builtin_amdgcn_sched_barrier(0);
@@ -330,7 +354,7 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
 #endif
       // this step's registers now carry the next unit's step s
       const int chn = min(DEC_CH(nkr_next, s), c1 - 1);
-      load_step<NS, FS>(fb[s], nxt, chn, nc, c);
+      load_step<NS, FS, MX>(fb[s], nxt, chn, nc, c);
       if (FS && s == 0) load_sc<NS>(scn, nxt, DEC_GRP(nkr_next));
       load_a(xa[s], nxt, chn);
       __builtin_amdgcn_sched_barrier(0);
@@ -403,33 +427,33 @@ struct DecLaunch {
   hipEvent_t ev0, ev1;
 };
 
-template <bool GATEUP, int SK, int S, int U, bool FS>
+template <bool GATEUP, int SK, int S, int U, bool FS, bool MX>
 hipError_t launch_k(const DecArgs& a, const DecPtrs& p, const DecLaunch& l) {
   if (l.ev0 || l.ev1)
-    hipExtLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U, FS>), dim3(l.grid), dim3(256), 0, l.st, l.ev0, l.ev1, 0, a,
-                          p.tiles, p.tile_tok, p.n_tiles, p.pool, p.ain, p.out);
+    hipExtLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U, FS, MX>), dim3(l.grid), dim3(256), 0, l.st, l.ev0, l.ev1, 0,
+                          a, p.tiles, p.tile_tok, p.n_tiles, p.pool, p.ain, p.out);
   else
-    hipLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U, FS>), dim3(l.grid), dim3(256), 0, l.st, a, p.tiles, p.tile_tok,
-                       p.n_tiles, p.pool, p.ain, p.out);
+    hipLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U, FS, MX>), dim3(l.grid), dim3(256), 0, l.st, a, p.tiles,
+                       p.tile_tok, p.n_tiles, p.pool, p.ain, p.out);
   return hipGetLastError();
 }
 
 // S = 4 with every wavefront's share of K made of whole 512-value groups
 // (K a multiple of 512 SK) takes the per-unit scale loads
-template <bool GATEUP, int SK, int U>
+template <bool GATEUP, int SK, int U, bool MX>
 hipError_t launch_s(const DecArgs& a, const DecPtrs& p, int S, const DecLaunch& l) {
-  if (S <= 1) return launch_k<GATEUP, SK, 1, U, false>(a, p, l);
-  if (S <= 2) return launch_k<GATEUP, SK, 2, U, false>(a, p, l);
+  if (S <= 1) return launch_k<GATEUP, SK, 1, U, false, MX>(a, p, l);
+  if (S <= 2) return launch_k<GATEUP, SK, 2, U, false, MX>(a, p, l);
   constexpr int S4 = (GATEUP ? MOE_DEC_MAXS_GU : MOE_DEC_MAXS_DN) >= 4 ? 4 : 2;
   const int K = GATEUP ? a.H : a.I;
-  if (S4 == 4 && K % (512 * SK) == 0) return launch_k<GATEUP, SK, S4, U, S4 == 4>(a, p, l);
-  return launch_k<GATEUP, SK, S4, U, false>(a, p, l);
+  if (!MX && S4 == 4 && K % (512 * SK) == 0) return launch_k<GATEUP, SK, S4, U, S4 == 4, MX>(a, p, l);
+  return launch_k<GATEUP, SK, S4, U, false, MX>(a, p, l);
 }
 
-template <bool GATEUP>
+template <bool GATEUP, bool MX>
 hipError_t launch_su(const DecArgs& a, const DecPtrs& p, int sk, int S, int U, const DecLaunch& l) {
-  if (sk == 4) return U == 2 ? launch_s<GATEUP, 4, 2>(a, p, S, l) : launch_s<GATEUP, 4, 1>(a, p, S, l);
-  return U == 2 ? launch_s<GATEUP, 1, 2>(a, p, S, l) : launch_s<GATEUP, 1, 1>(a, p, S, l);
+  if (sk == 4) return U == 2 ? launch_s<GATEUP, 4, 2, MX>(a, p, S, l) : launch_s<GATEUP, 4, 1, MX>(a, p, S, l);
+  return U == 2 ? launch_s<GATEUP, 1, 2, MX>(a, p, S, l) : launch_s<GATEUP, 1, 1, MX>(a, p, S, l);
 }
 
 }  // namespace
@@ -438,7 +462,7 @@ hipError_t launch_su(const DecArgs& a, const DecPtrs& p, int sk, int S, int U, c
 // MOE_DEC_WGS_DN) workgroups (fewer when there is less work than that).
 hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
                           uint16_t* y_rows, void* ws, int n_cu, int stages, hipEvent_t ev_start, hipEvent_t ev_stop,
-                          hipStream_t s) {
+                          hipStream_t s, bool mx, const uint16_t* down_in) {
   (void)perm;
   const WsLayout wl = ws_layout(d);
   uint8_t* base = static_cast<uint8_t*>(ws);
@@ -480,12 +504,14 @@ hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g
     a.n_ug = ublocks / ((4 / sk) * U);
     const int64_t items = (int64_t)wl.max_tiles * a.n_ug;
     const int grid = (int)(items < cap ? items : cap);
-    ptrs.ain = gu ? x : h;
+    ptrs.ain = gu ? x : (down_in ? down_in : h);
     ptrs.out = gu ? h : y_rows;
     // the start event goes with the first stage launched, the stop event with the last
     const bool first = gu || !(stages & 1), last = !gu || !(stages & 2);
     const DecLaunch l{grid, s, first ? ev_start : nullptr, last ? ev_stop : nullptr};
-    const hipError_t e = gu ? launch_su<true>(a, ptrs, sk, S, U, l) : launch_su<false>(a, ptrs, sk, S, U, l);
+    const hipError_t e = mx ? (gu ? launch_su<true, true>(a, ptrs, sk, S, U, l) : launch_su<false, true>(a, ptrs, sk, S, U, l))
+                            : (gu ? launch_su<true, false>(a, ptrs, sk, S, U, l)
+                                  : launch_su<false, false>(a, ptrs, sk, S, U, l));
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

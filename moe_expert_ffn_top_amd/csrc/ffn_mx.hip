@@ -167,6 +167,37 @@ __global__ __launch_bounds__(256) void k_quant_mx(const uint16_t* __restrict__ x
   if ((t & 3) == 0) sc[(t / tpr) * stride + (t % tpr) / 4] = (uint8_t)sb;
 }
 
+// The same quantisation, written back as the bf16 values it stands for:
+// e4m3(code) * 2^(sb - 127), exact in bf16 (both have at most 4 significant
+// bits; values below 2^-133 would round, far below any activation here).
+__global__ __launch_bounds__(256) void k_quant_mx_bf16(const uint16_t* __restrict__ x, int64_t n8,
+                                                       uint16_t* __restrict__ y) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n8) return;  // whole quads leave together (n8 % 4 == 0)
+  const uint4 w = reinterpret_cast<const uint4*>(x)[t];
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+  float f[8];
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    f[2 * i] = __uint_as_float(ww[i] << 16);
+    f[2 * i + 1] = __uint_as_float(ww[i] & 0xFFFF0000u);
+    m = fmaxf(m, fmaxf(fabsf(f[2 * i]), fabsf(f[2 * i + 1])));
+  }
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+  const int sb = e8m0_of_amax(m);
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t c2 = e4m3_pair(f[2 * i], f[2 * i + 1], sb);
+    const float v0 = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)c2, 0), sb - 127);
+    const float v1 = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)c2, 1), sb - 127);
+    o[i] = (__float_as_uint(v0) >> 16) | (__float_as_uint(v1) & 0xFFFF0000u);  // exact: the low halves are zero
+  }
+  reinterpret_cast<uint4*>(y)[t] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 template <bool GATEUP>
 __global__ __launch_bounds__(XT) void k_ffn_mx(MxArgs a, const int4* __restrict__ chunks,
                                                const int32_t* __restrict__ meta, const int32_t* __restrict__ perm,
@@ -436,6 +467,31 @@ hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int32_t K, uint8_t* 
   else
     hipLaunchKernelGGL(k_quant_mx, grid, block, 0, s, x, n8, tpr, scale_stride, codes, scales);
   return hipGetLastError();
+}
+
+hipError_t launch_ffn_dec_mx(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
+                             uint16_t* y_rows, void* ws, void* mx_ws, int n_cu, int stages, hipEvent_t ev_start,
+                             hipEvent_t ev_stop, hipStream_t s) {
+  const MxWsLayout ml = mx_ws_layout(d);
+  uint16_t* xb = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(mx_ws) + ml.off_xb);
+  uint16_t* hb = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(mx_ws) + ml.off_hb);
+  for (int stage = 0; stage < 2; stage++) {
+    if (!((stages >> stage) & 1)) continue;
+    const bool gu = stage == 0;
+    const bool first = gu || !(stages & 1), last = !gu || !(stages & 2);
+    // the quantisation first, then the FFN kernel, which the events bracket
+    const int64_t rows = gu ? d.T : (int64_t)d.T * d.k + d.T;
+    const int64_t n8 = rows * ((gu ? d.H : d.I) / 8);
+    if (n8 > 0)
+      hipLaunchKernelGGL(k_quant_mx_bf16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, gu ? x : h, n8,
+                         gu ? xb : hb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_ffn_dec(d, xb, g, perm, h, y_rows, ws, n_cu, gu ? 1 : 2, first ? ev_start : nullptr,
+                       last ? ev_stop : nullptr, s, true, hb);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_ffn_mx(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,

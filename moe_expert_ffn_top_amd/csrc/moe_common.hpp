@@ -191,8 +191,11 @@ int record_error(int code, const char* msg);
 // xs  uint8 [T][xs_stride]  their E8M0 scales (H/32 per row, rows padded to 16 bytes)
 // hq  uint8 [T*k + T][I]    E4M3 codes of h (rows in group order, then the shared rows)
 // hs  uint8 [T*k + T][hs_stride] their E8M0 scales (I/32 per row, padded likewise)
+// For decode-sized groups (!use_gemm) it holds instead
+// xb  bf16 [T][H]           the values of MXFP8(x)
+// hb  bf16 [T*k + T][I]     the values of MXFP8(h)
 struct MxWsLayout {
-  uint64_t off_xq, off_xs, off_hq, off_hs, total;
+  uint64_t off_xq, off_xs, off_hq, off_hs, off_xb, off_hb, total;
   int32_t xs_stride, hs_stride;
 };
 inline MxWsLayout mx_ws_layout(const moe_dims& d) {
@@ -200,11 +203,19 @@ inline MxWsLayout mx_ws_layout(const moe_dims& d) {
   const uint64_t rows_h = (uint64_t)d.T * d.k + (uint64_t)d.T;
   w.xs_stride = (d.H / 32 + 15) & ~15;
   w.hs_stride = (d.I / 32 + 15) & ~15;
-  w.off_xq = 0;
-  w.off_xs = align256((uint64_t)d.T * d.H);
-  w.off_hq = align256(w.off_xs + (uint64_t)d.T * w.xs_stride);
-  w.off_hs = align256(w.off_hq + rows_h * d.I);
-  w.total = align256(w.off_hs + rows_h * w.hs_stride);
+  if (use_gemm(d)) {
+    w.off_xq = 0;
+    w.off_xs = align256((uint64_t)d.T * d.H);
+    w.off_hq = align256(w.off_xs + (uint64_t)d.T * w.xs_stride);
+    w.off_hs = align256(w.off_hq + rows_h * d.I);
+    w.total = align256(w.off_hs + rows_h * w.hs_stride);
+    w.off_xb = w.off_hb = w.total;
+  } else {
+    w.off_xb = 0;
+    w.off_hb = align256((uint64_t)d.T * d.H * 2);
+    w.total = align256(w.off_hb + rows_h * d.I * 2);
+    w.off_xq = w.off_xs = w.off_hq = w.off_hs = w.total;
+  }
   return w;
 }
 
@@ -248,9 +259,11 @@ hipError_t launch_route_group(const moe_dims& d, int32_t layer, const float* log
 // stages: bit 1 = gate/up (writes h), bit 2 = down (reads h, writes y_rows)
 // ev_start / ev_stop (may be null): recorded at the start of the first launched
 // kernel and the end of the last one
+// mx: MX blobs (E8M0 scale per 32 values, no globals); down_in (may be null:
+// h) is the down stage's A rows.
 hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm,
                           uint16_t* h, uint16_t* y_rows, void* ws, int n_cu, int stages, hipEvent_t ev_start,
-                          hipEvent_t ev_stop, hipStream_t s);
+                          hipEvent_t ev_stop, hipStream_t s, bool mx = false, const uint16_t* down_in = nullptr);
 // Grouped-GEMM expert FFN over the chunk list (prefill-sized groups); same
 // stage mask and events as launch_ffn_dec.
 hipError_t launch_ffn_gemm(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
@@ -266,6 +279,11 @@ hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int32_t K, uint8_t* 
 hipError_t launch_ffn_mx(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
                          uint16_t* y_rows, void* ws, void* mx_ws, int stages, hipEvent_t ev_start, hipEvent_t ev_stop,
                          hipStream_t s);
+// The same for decode-sized groups: the weight-streaming kernel on MX blobs,
+// its A rows the bf16 values of MXFP8(x) and MXFP8(h) (kept in mx_ws).
+hipError_t launch_ffn_dec_mx(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
+                             uint16_t* y_rows, void* ws, void* mx_ws, int n_cu, int stages, hipEvent_t ev_start,
+                             hipEvent_t ev_stop, hipStream_t s);
 hipError_t launch_combine(const moe_dims& d, const uint16_t* y_rows, const int32_t* inv_perm, const float* w,
                           const float* sigma, uint16_t* y, hipStream_t s);
 

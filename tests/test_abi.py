@@ -157,8 +157,8 @@ def test_mx_workspace_matches_documented_layout(B):
 
 
 def test_mx_ffn_validation(B):
-    """Rejected before any device work: decode-sized groups (the MX FFN is the
-    grouped GEMM only), an NVFP4 layout, a short MX workspace, a bad stage mask."""
+    """Rejected before any device work: an NVFP4 layout, a short MX workspace
+    (for the GEMM and for the decode layout), an unaligned one, a bad stage mask."""
     fake = 1 << 20
     dims = B.Dims(64, 256, 128, 8, 2)               # T k = 128 = 16 E: the GEMM path
     d = ctypes.byref(dims)
@@ -170,8 +170,12 @@ def test_mx_ffn_validation(B):
 
     def st(args, dd=d):
         return B.raw_status("moe_expert_ffn_mx", dd, *args)
-    small = B.Dims(4, 256, 128, 64, 4)              # T k = 16 < 16 E
-    assert st(ok, ctypes.byref(small)) == B.MOE_ERR_SHAPE
+    small = B.Dims(4, 256, 128, 64, 4)              # T k = 16 < 16 E: the decode layout
+    small_ok = list(ok)
+    small_ok[11] = B.moe_workspace_bytes(small)
+    small_ok[13] = B.moe_mx_workspace_bytes(small) - 256
+    assert st(small_ok, ctypes.byref(small)) == B.MOE_ERR_WORKSPACE
+    assert B.MxWorkspace(small).total == B.moe_mx_workspace_bytes(small) and not B.MxWorkspace(small).gemm
     nv = B.moe_blob_layout_init(256, 128)
     assert st(ok[:3] + [ctypes.byref(nv)] + ok[4:]) == B.MOE_ERR_ARG
     assert st(ok[:13] + [need_mx - 256] + ok[14:]) == B.MOE_ERR_WORKSPACE

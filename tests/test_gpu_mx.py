@@ -15,6 +15,9 @@
   - a non-resident group;
   - stages split;
   - the device pool generator against the host one.
+- Decode-sized groups (T k < 16 E): the weight-streaming kernel on MX blobs,
+  its A rows the bf16 values of MXFP8(x) and MXFP8(h), both bit for bit
+  against the oracle's quantisation; a K split into several rounds (H = 4608).
 - Full size: prefill8192_mx on 17 sampled tokens."""
 import numpy as np
 import pytest
@@ -141,8 +144,20 @@ class MxCase:
         return self.buf.mx_ws[off:off + n].cpu().numpy()
 
     def check_quantised_workspace(self, rows=None):
-        """xq/xs and hq/hs against the oracle's MXFP8 of x and of the kernel's h."""
+        """xq/xs and hq/hs (or, for decode shapes, the bf16 values xb/hb) against
+        the oracle's MXFP8 of x and of the kernel's h."""
         c, m = self.cfg, self.mws
+        if not m.gemm:
+            nr = c.T * c.k + c.T
+            xb = self.buf.mx_ws[m.off_xb:m.off_xb + c.T * c.H * 2].view(torch.bfloat16).view(c.T, c.H)
+            assert np.array_equal(bf16_to_f64(xb), O.mxfp8_quantize(O.bf16_bits_to_f64(self.x_bits))[2]), "x values"
+            hb = self.buf.mx_ws[m.off_hb:m.off_hb + nr * c.I * 2].view(torch.bfloat16).view(nr, c.I)
+            # rows of groups that exist (rows past offsets[E] of dropped entries are not written)
+            off = self.buf.offsets.cpu().numpy()
+            live = np.r_[np.arange(int(off[c.E])), np.arange(c.T * c.k, nr)]
+            want = O.mxfp8_quantize(bf16_to_f64(self.buf.h)[live])[2]
+            assert np.array_equal(bf16_to_f64(hb)[live], want), "h values"
+            return
         xc, xs, _ = O.mxfp8_quantize(O.bf16_bits_to_f64(self.x_bits))
         assert np.array_equal(self.ws_section(m.off_xq, c.T * c.H).reshape(c.T, c.H), xc), "x codes"
         gxs = self.ws_section(m.off_xs, c.T * m.xs_stride).reshape(c.T, m.xs_stride)[:, :c.H // 32]
@@ -165,6 +180,46 @@ MX_SMALL = {
     # Zipf routing: one group above 256 rows and many small ones; H = 384 (3 K steps)
     "mx_zipf": Config(53, "mxz", T=256, H=384, I=128, E=16, k=4, L=1, router="zipf", zipf_s=1.2, fmt="mx"),
 }
+
+
+MX_DEC = {
+    # a decode window under Zipf routing
+    "mxd_small": Config(61, "mxd", T=4, H=256, I=128, E=32, k=4, L=1, router="zipf", zipf_s=1.0, fmt="mx"),
+    # 16 tokens through the router matrix; several unit blocks per item
+    "mxd_multi": Config(62, "mxdm", T=16, H=512, I=256, E=64, k=6, L=1, router="matrix", fmt="mx"),
+    # K split over wavefronts and covered in several rounds, the last ragged
+    "mxd_longK": Config(63, "mxdl", T=6, H=4608, I=1152, E=8, k=2, L=1, router="matrix", fmt="mx"),
+}
+
+
+@pytest.mark.parametrize("name", list(MX_DEC))
+def test_mx_decode_layer_parity(B, hostgen, name):
+    cfg = MX_DEC[name]
+    assert cfg.T * cfg.k < 16 * cfg.E
+    say("[gpu] mx decode-path parity %s (T=%d H=%d I=%d E=%d k=%d)" % (name, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k))
+    c = MxCase(B, cfg, hostgen)
+    assert not c.mws.gemm
+    c.run(B)
+    assert int(c.buf.status.item()) == 0
+    stats = c.compare(c.oracle())
+    c.check_quantised_workspace()
+    say("[gpu]   %s: %s" % (name, stats))
+
+
+def test_mx_decode_non_resident_group(B, hostgen):
+    cfg = MX_DEC["mxd_multi"]
+    say("[gpu] mx decode non-resident group")
+    c = MxCase(B, cfg, hostgen)
+    c.run(B)
+    off = c.buf.offsets.cpu().numpy()
+    e = int(np.argmax(np.diff(off[:cfg.E + 1])))   # an expert with rows
+    d = MxCase(B, cfg, hostgen, slot_override={e: -1})
+    d.run(B)
+    assert int(d.buf.status.item()) & B.MOE_DEV_NOT_RESIDENT
+    assert torch.count_nonzero(d.buf.y_rows[off[e]:off[e + 1]].float()) == 0
+    keep = torch.ones(cfg.T * cfg.k + cfg.T, dtype=torch.bool, device="cuda")
+    keep[off[e]:off[e + 1]] = False
+    assert torch.equal(d.buf.y_rows[keep].view(torch.int16), c.buf.y_rows[keep].view(torch.int16))
 
 
 def test_quantize_mxfp8_bit_exact(B):
