@@ -56,7 +56,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="decode48",
-                    help="tiny | decode48 | decode43x64 | prefill8192 | streamed4x4096 | cached48x64 | prefill8192_mx "
+                    help="tiny | decode48 | decode43x64 | prefill8192 | streamed4x4096 | cached48x64 | prefill8192_mx | "
+                         "decode48_mx "
                          "(default decode48)")
     ap.add_argument("--eager", action="store_true", help="launch every call eagerly instead of HIP graphs")
     ap.add_argument("--policy", default="lru", choices=("lru", "hotcold"),
@@ -76,7 +77,7 @@ def ffn_kernel(cfg):
     """(kernel name, source file) of the FFN path the library takes for these
     shapes: the grouped GEMM when groups average >= 16 rows (T k >= 16 E),
     else the weight-streaming kernel."""
-    if cfg.fmt == "mx":
+    if cfg.fmt == "mx" and cfg.T * cfg.k >= 16 * cfg.E:
         return "k_ffn_mx", os.path.join(CSRC, "ffn_mx.hip")
     if cfg.T * cfg.k >= 16 * cfg.E:
         return "k_ffn_gemm", os.path.join(CSRC, "ffn_gemm.hip")
@@ -234,6 +235,7 @@ def expert_work(cfg, offsets_list):
     shared expert) and flops per row.
       gate/up: codes 2 I H / 2, scales 2 I H / 16, two fp32 globals; 4 H I flops
       down:    codes H I / 2,   scales H I / 16,   one fp32 global;  2 H I flops
+    MX blobs: scales per 32 values (2 I H / 32, H I / 32), no globals.
     Returns arrays (gu_bytes, dn_bytes, gu_flops, dn_flops)."""
     H, I = cfg.H, cfg.I
     gu_b, dn_b, gu_f, dn_f = [], [], [], []
@@ -241,8 +243,12 @@ def expert_work(cfg, offsets_list):
         o = off.cpu().numpy()
         active = int(np.count_nonzero(np.diff(o[:cfg.E + 1]))) + 1
         rows = int(o[cfg.E]) + cfg.T
-        gu_b.append(active * (I * H + I * H // 8 + 8))
-        dn_b.append(active * (H * I // 2 + H * I // 16 + 4))
+        if cfg.fmt == "mx":
+            gu_b.append(active * (I * H + I * H // 16))
+            dn_b.append(active * (H * I // 2 + H * I // 32))
+        else:
+            gu_b.append(active * (I * H + I * H // 8 + 8))
+            dn_b.append(active * (H * I // 2 + H * I // 16 + 4))
         gu_f.append(4.0 * H * I * rows)
         dn_f.append(2.0 * H * I * rows)
     return tuple(np.array(v, dtype=np.float64) for v in (gu_b, dn_b, gu_f, dn_f))
@@ -730,7 +736,8 @@ def main():
         traffic = recorded_traffic(cfg)
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                "kernel": "%s gate/up (moe_expert_ffn_stages, stages=1)" % ffn_kernel(cfg)[0],
+                "kernel": "%s gate/up (%s, stages=1)" % (
+                    ffn_kernel(cfg)[0], "moe_expert_ffn_mx" if cfg.fmt == "mx" else "moe_expert_ffn_stages"),
                 "launch_us": float(gu_ms.mean() * 1e3), "bytes_per_launch": float(gu_b.mean()),
                 "down": {"launch_us": float(dn_ms.mean() * 1e3), "bytes_per_launch": float(dn_b.mean()),
                          "achieved": float(dn_b.mean() / (dn_ms.mean() * 1e-3) / 1e9)}}
@@ -755,7 +762,8 @@ def main():
     line = {
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "mxfp8 x mxfp4" if cfg.fmt == "mx" else "bf16",
+        "dtype": ("mxfp8 x mxfp4" if cfg.T * cfg.k >= 16 * cfg.E else "bf16 (mxfp8 x mxfp4 values)")
+        if cfg.fmt == "mx" else "bf16",
         "data": "synthetic (seeded; random MXFP4 weights, bf16 activations quantised to MXFP8)" if cfg.fmt == "mx"
         else "synthetic (seeded; random block-FP4 weights, bf16 activations)",
         "config": {"workload": cfg.name, "T": cfg.T, "layers": cfg.L, "H": cfg.H, "I": cfg.I, "E": cfg.E,

@@ -56,6 +56,8 @@ CONFIGS = {
     # prefill8192's shapes with natively MXFP4 experts ([FreeToken] 2.1): the
     # scaled-MFMA path (MXFP8 activations)
     7: Config(7, "prefill8192_mx", T=8192, H=2048, I=512, E=512, k=10, L=1, router="matrix", fmt="mx"),
+    # decode48 with MXFP4 experts: the weight-streaming kernel on MX blobs
+    8: Config(8, "decode48_mx", T=4, H=2048, I=512, E=512, k=10, L=48, router="zipf", zipf_s=1.0, fmt="mx"),
 }
 
 

@@ -311,6 +311,38 @@ def test_device_mx_pool_matches_host(B, hostgen):
         assert np.array_equal(got[e], hostgen.expert_blob_mx(cfg, 0, e, olay)), "expert %d" % e
 
 
+@pytest.mark.timeout(600)
+def test_decode48_mx_full_size(B, hostgen):
+    """A whole 48-layer decode step on MX blobs; the buffers then hold layer 47,
+    checked against the oracle on all four tokens."""
+    from bench import Workload
+    cfg = CONFIGS[8]
+    say("[gpu] full-size %s: building workload" % cfg.name)
+    wl = Workload(cfg, 1, B, DevGen)
+    wl.run_step(0)
+    torch.cuda.synchronize()
+    buf, l = wl.buf, cfg.L - 1
+    assert int(buf.status.item()) == 0
+    olay = O.mx_blob_layout(cfg.H, cfg.I)
+    x = hostgen.x(cfg, l, 0)
+    lg = zipf_logits(cfg, l, 0)
+    need = set(O.topk(lg, cfg.k).reshape(-1).tolist()) | {cfg.E}
+    blobs = {e: hostgen.expert_blob_mx(cfg, l, e, olay) for e in need}
+    stride = wl.layout.slot_stride
+    s0 = l * cfg.E1 + cfg.E
+    assert np.array_equal(wl.pool[s0 * stride:s0 * stride + olay.blob_bytes].cpu().numpy(),
+                          blobs[cfg.E][:olay.blob_bytes]), "device pool bytes"
+    say("[gpu]   %s: oracle for layer %d" % (cfg.name, l))
+    ora = O.moe_layer(x, lambda e: blobs[e], cfg.H, cfg.I, cfg.E, cfg.k, hostgen.w_shared_gate(cfg, l), logits=lg,
+                      fmt="mx")
+    staged = downstream_from_kernel_h(buf, ora, cfg, lambda e: blobs[e])
+    stats = compare_layer(buf, staged, cfg.T, cfg.k, cfg.E, drawn_logits=True)
+    stats["y_end_to_end"] = end_to_end_y(buf, ora)
+    say("[gpu]   %s ok: %s" % (cfg.name, stats))
+    del wl
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.timeout(900)
 def test_prefill8192_mx_full_size(B, hostgen):
     from bench import Workload
