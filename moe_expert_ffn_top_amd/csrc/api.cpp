@@ -482,13 +482,13 @@ int moe_expert_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool, ui
   g.off_globals = layout->off_globals;
   const hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (moe::use_gemm(*d))
-    return hip_status(moe::launch_ffn_mx(*d, x, g, perm, h, y_rows, ws, mx_ws, stages, e0, e1, st),
-                      "MX expert FFN launch");
   int dev = 0, n_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) !=
                                               hipSuccess || n_cu <= 0)
     return fail(MOE_ERR_HIP, "cannot query the device's compute-unit count");
+  if (moe::use_gemm(*d))
+    return hip_status(moe::launch_ffn_mx(*d, x, g, perm, h, y_rows, ws, mx_ws, n_cu, stages, e0, e1, st),
+                      "MX expert FFN launch");
   return hip_status(moe::launch_ffn_dec_mx(*d, x, g, perm, h, y_rows, ws, mx_ws, n_cu, stages, e0, e1, st),
                     "MX expert FFN launch");
 }

@@ -204,252 +204,312 @@ __global__ __launch_bounds__(XT) void k_ffn_mx(MxArgs a, const int4* __restrict_
                                                const uint8_t* __restrict__ pool, const uint8_t* __restrict__ aq,
                                                const uint8_t* __restrict__ as, uint16_t* __restrict__ out,
                                                uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
-  constexpr int UPW = GATEUP ? XC / 2 : XC;  // units per workgroup
+  constexpr int UPW = GATEUP ? XC / 2 : XC;  // units per work item
+  constexpr int OC = GATEUP ? XC / 2 : XC;   // output columns of the tile
+  constexpr int OSTR = OC + 8;               // uint16 per row of the h / Y tile
+  // the epilogue's tiles sit in buffers 1 and 2, so that the next item's
+  // first step can land in buffer 0 meanwhile
+  static_assert(XM * OSTR * 2 + (GATEUP ? XM * QSTR + XM * 2 : 0) <= 2 * BUF_BYTES, "epilogue tiles fit");
   const int K = GATEUP ? a.H : a.I;
   const int units = GATEUP ? a.I : a.H;
-  // blocks are dealt to the 8 XCDs round-robin: block b runs on XCD b % 8
-  const int bid = blockIdx.x, xcd = bid & 7, jb = bid >> 3;
-  const int ut = jb % a.n_ut, chunk = (jb / a.n_ut) * 8 + xcd;
-  if (chunk >= *(cptr<int32_t>)(meta + 1)) return;
-  const i32x4 cd = ((cptr<i32x4>)chunks)[chunk];
-  const int p0 = cd.y, n = cd.z, slot = cd.w;
-  const bool resident = slot >= 0 && slot < a.n_slots;
-  // a non-resident group reads the pool's first bytes (valid memory); its
-  // outputs are zero (selected, so no scale byte read there matters)
-  const uint8_t* blob = pool + (resident ? (uint64_t)slot * (uint64_t)a.slot_stride : 0);
-  const int u0 = ut * UPW;
 
   __shared__ __align__(16) uint8_t smem[LDS_BYTES];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  uint16_t* os = reinterpret_cast<uint16_t*>(smem + BUF_BYTES);
+  uint8_t* qs = smem + BUF_BYTES + XM * OSTR * 2;  // gate/up: code tile [XM][QSTR]
+  uint8_t* ss = qs + XM * QSTR;                    // gate/up: scale tile [XM][2]
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = lane & 15, q = lane >> 4;
-  const int nb = (n + 15) >> 4;  // live 16-row blocks; block rbk belongs to wavefront pair rbk % 4
+
+  // Persistent: workgroup w takes work items w, w + P, w + 2 P, ... (P, the
+  // grid, a multiple of 8).  Item i is column tile (i >> 3) % n_ut of chunk
+  // ((i >> 3) / n_ut) * 8 + i % 8: workgroups are dealt to the XCDs round-
+  // robin, so item i runs on XCD i % 8 and the tiles of one chunk run at once
+  // on one XCD, sharing its A rows in that XCD's L2.  Chunks grow with i, so a
+  // workgroup's first inactive item ends its walk.
+  const int n_chunks = *(cptr<int32_t>)(meta + 1);
+  const int P = gridDim.x;
+  auto item_chunk = [&](int i) { return ((i >> 3) / a.n_ut) * 8 + (i & 7); };
+  struct ItemInfo {
+    int p0, n, u0;
+    bool resident;
+    const uint8_t* blob;
+  };
+  // a non-resident group reads the pool's first bytes (valid memory); its
+  // outputs are zero (selected, so no scale byte read there matters)
+  auto info = [&](int i) __attribute__((always_inline)) {
+    const i32x4 cd = ((cptr<i32x4>)chunks)[item_chunk(i)];
+    ItemInfo it;
+    it.p0 = cd.y;
+    it.n = cd.z;
+    it.resident = cd.w >= 0 && cd.w < a.n_slots;
+    it.blob = pool + (it.resident ? (uint64_t)cd.w * (uint64_t)a.slot_stride : 0);
+    it.u0 = ((i >> 3) % a.n_ut) * UPW;
+    return it;
+  };
+  // epilogue, part 2 (all eight wavefronts): the tiles leave in 16-byte row
+  // segments
+  auto copy_out = [&](const ItemInfo& it) __attribute__((always_inline)) {
+    constexpr int SEGS = OC / 8;
+#pragma unroll 4
+    for (int i = tid; i < it.n * SEGS; i += XT) {
+      const int row = i / SEGS, sg = i % SEGS;
+      *reinterpret_cast<uint4*>(out + (int64_t)(it.p0 + row) * units + it.u0 + 8 * sg) =
+          *reinterpret_cast<const uint4*>(&os[row * OSTR + 8 * sg]);
+    }
+    if (GATEUP) {
+      for (int i = tid; i < it.n * 4; i += XT) {
+        const int row = i >> 2, sg = i & 3;
+        *reinterpret_cast<uint4*>(hq + (int64_t)(it.p0 + row) * units + it.u0 + 16 * sg) =
+            *reinterpret_cast<const uint4*>(&qs[row * QSTR + 16 * sg]);
+      }
+      for (int row = tid; row < it.n; row += XT)
+        *reinterpret_cast<uint16_t*>(hs + (int64_t)(it.p0 + row) * a.hs_stride + it.u0 / 32) =
+            *reinterpret_cast<const uint16_t*>(&ss[row * 2]);
+    }
+  };
+
+  int item = blockIdx.x;
+  if (item_chunk(item) >= n_chunks) return;
 
   if (wave >= 4) {
     // ---------------- producer ----------------
     const int pw = wave - 4;
-    // A rows past n load row n - 1 (their outputs are dropped)
-    auto arow = [&](int row) -> int64_t {
-      const int p = p0 + min(row, n - 1);
-      return GATEUP ? (int64_t)(p < a.Tk ? perm[p] / a.k : p - a.Tk) : (int64_t)p;
+    // this wavefront's source addresses for one item; A rows past n load row
+    // n - 1 (their outputs are dropped)
+    struct PAddr {
+      const uint8_t* asrc[4];
+      const uint8_t* ssrc;
+      const uint8_t* bsrc[2];
+      const uint8_t* bssrc;
+      int na;  // live A blocks of this wavefront: pw + 4 i, i < na
     };
-    const uint8_t* asrc[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) asrc[i] = aq + arow(16 * (pw + 4 * i) + r) * K + 16 * q;
-    const uint8_t* ssrc = as + arow(64 * pw + lane) * a.as_stride;
-    // B: column blocks 2 pw and 2 pw + 1 (gate/up: blocks 0..3 gate, 4..7 up,
-    // the same units)
-    auto bunit = [&](int cb) { return u0 + 16 * (GATEUP ? (cb & 3) : cb); };
-    auto bmat = [&](int cb) { return GATEUP ? (cb >> 2) : 2; };
-    const uint8_t* bsrc[2];
-#pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int cb = 2 * pw + j;
-      bsrc[j] = (resident ? blob + a.off_codes[bmat(cb)] + (int64_t)(bunit(cb) >> 4) * (8 * K) : pool) + 16 * lane;
-    }
-    // B scales (wavefronts 0 and 1): column 64 pw + lane
-    const int scol = (64 * pw + lane) & (XC - 1), scb = scol >> 4;
-    const uint8_t* bssrc =
-        (resident ? blob + a.off_scales[bmat(scb)] + (int64_t)(bunit(scb) >> 4) * (K / 2) : pool) + 4 * (scol & 15);
-
-    auto run = [&](auto na_c) __attribute__((always_inline)) {
-      constexpr int NA = decltype(na_c)::value;  // live A blocks of this wavefront: pw + 4 i, i < NA
-      constexpr int N = 2 * NA + 2;  // DMA instructions per step (+1 on wavefronts 0 and 1, +1 every fourth step)
-      auto issue = [&](int s, int bi) __attribute__((always_inline)) {
-        const uint32_t buf = lds0 + (uint32_t)(bi * BUF_BYTES);
-#pragma unroll
-        for (int i = 0; i < NA; i++) {
-          const uint32_t d = buf + A_OFF + (uint32_t)(pw + 4 * i) * 2048u;
-          dma16(asrc[i] + XK * s, __builtin_amdgcn_readfirstlane(d));
-          dma16(asrc[i] + XK * s + 64, __builtin_amdgcn_readfirstlane(d + 1024u));
-        }
-#pragma unroll
-        for (int j = 0; j < 2; j++)
-          dma16(bsrc[j] + 1024 * s, __builtin_amdgcn_readfirstlane(buf + B_OFF + (uint32_t)(2 * pw + j) * 1024u));
-        if (pw < 2) dma4(bssrc + 64 * s, __builtin_amdgcn_readfirstlane(buf + BS_OFF + 256u * (uint32_t)pw));
-        if ((s & 3) == 0)  // the A scales of steps s .. s + 3 (the row's 16 bytes from 4 s)
-          dma16(ssrc + 4 * s, __builtin_amdgcn_readfirstlane(lds0 + ASG_OFF + (uint32_t)(((s >> 2) & 1) * ASG_SLOT) +
-                                                            1024u * (uint32_t)pw));
+    auto paddr = [&](const ItemInfo& it) __attribute__((always_inline)) {
+      PAddr pa;
+      auto arow = [&](int row) -> int64_t {
+        const int p = it.p0 + min(row, it.n - 1);
+        return GATEUP ? (int64_t)(p < a.Tk ? perm[p] / a.k : p - a.Tk) : (int64_t)p;
       };
-      // the step before step s has landed once at most step s's instructions
-      // are in flight
-      auto wait_next = [&](int s) __attribute__((always_inline)) {
-        const bool g = (s & 3) == 0;
-        if (pw < 2) {
-          if (g) wait_vm<N + 2>();
-          else wait_vm<N + 1>();
-        } else {
-          if (g) wait_vm<N + 1>();
-          else wait_vm<N>();
-        }
-      };
-      issue(0, 0);
-      if (a.nk > 1) {
-        issue(1, 1);
-        wait_next(1);
-      } else {
-        wait_vm<0>();
+#pragma unroll
+      for (int i = 0; i < 4; i++) pa.asrc[i] = aq + arow(16 * (pw + 4 * i) + r) * K + 16 * q;
+      pa.ssrc = as + arow(64 * pw + lane) * a.as_stride;
+      // B: column blocks 2 pw and 2 pw + 1 (gate/up: blocks 0..3 gate, 4..7
+      // up, the same units)
+      auto bunit = [&](int cb) { return it.u0 + 16 * (GATEUP ? (cb & 3) : cb); };
+      auto bmat = [&](int cb) { return GATEUP ? (cb >> 2) : 2; };
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const int cb = 2 * pw + j;
+        pa.bsrc[j] =
+            (it.resident ? it.blob + a.off_codes[bmat(cb)] + (int64_t)(bunit(cb) >> 4) * (8 * K) : pool) + 16 * lane;
       }
-      __syncthreads();
-      int bi = 2;  // buffer of step s + 2
-      for (int s = 0; s < a.nk; s++) {
-        // buffer (s + 2) % 3 was last read in step s - 1, which every consumer
-        // finished before the barrier just passed; so was the A-scale slot of
-        // step s + 2 (last read in step s - 6)
-        if (s + 2 < a.nk) {
-          issue(s + 2, bi);
-          bi = bi == 2 ? 0 : bi + 1;
-          wait_next(s + 2);
+      // B scales (wavefronts 0 and 1): column 64 pw + lane
+      const int scol = (64 * pw + lane) & (XC - 1), scb = scol >> 4;
+      pa.bssrc = (it.resident ? it.blob + a.off_scales[bmat(scb)] + (int64_t)(bunit(scb) >> 4) * (K / 2) : pool) +
+                 4 * (scol & 15);
+      pa.na = max(0, min(4, (((it.n + 15) >> 4) - pw + 3) >> 2));
+      return pa;
+    };
+    // the DMA instructions of step s into buffer bi: 2 na (A) + 2 (B) + 1
+    // (B scales, wavefronts 0 and 1) + 1 every fourth step (A scales)
+    auto issue = [&](const PAddr& pa, int s, int bi) __attribute__((always_inline)) {
+      const uint32_t buf = lds0 + (uint32_t)(bi * BUF_BYTES);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        if (i < pa.na) {
+          const uint32_t d = buf + A_OFF + (uint32_t)(pw + 4 * i) * 2048u;
+          dma16(pa.asrc[i] + XK * s, __builtin_amdgcn_readfirstlane(d));
+          dma16(pa.asrc[i] + XK * s + 64, __builtin_amdgcn_readfirstlane(d + 1024u));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+        dma16(pa.bsrc[j] + 1024 * s, __builtin_amdgcn_readfirstlane(buf + B_OFF + (uint32_t)(2 * pw + j) * 1024u));
+      if (pw < 2) dma4(pa.bssrc + 64 * s, __builtin_amdgcn_readfirstlane(buf + BS_OFF + 256u * (uint32_t)pw));
+      if ((s & 3) == 0)  // the A scales of steps s .. s + 3 (the row's 16 bytes from 4 s)
+        dma16(pa.ssrc + 4 * s, __builtin_amdgcn_readfirstlane(lds0 + ASG_OFF + (uint32_t)(((s >> 2) & 1) * ASG_SLOT) +
+                                                             1024u * (uint32_t)pw));
+    };
+
+    ItemInfo cur = info(item);
+    PAddr pa = paddr(cur);
+    bool pre0 = false;  // step 0 of the current item already issued
+    for (;;) {
+      auto run = [&](auto na_c) __attribute__((always_inline)) {
+        constexpr int NA = decltype(na_c)::value;
+        constexpr int N = 2 * NA + 2;
+        // the step before step s has landed once at most step s's
+        // instructions (and none older) are in flight
+        auto wait_next = [&](int s) __attribute__((always_inline)) {
+          const bool g = (s & 3) == 0;
+          if (pw < 2) {
+            if (g) wait_vm<N + 2>();
+            else wait_vm<N + 1>();
+          } else {
+            if (g) wait_vm<N + 1>();
+            else wait_vm<N>();
+          }
+        };
+        if (!pre0) issue(pa, 0, 0);
+        if (a.nk > 1) {
+          issue(pa, 1, 1);
+          wait_next(1);
         } else {
           wait_vm<0>();
         }
         __syncthreads();
+        int bi = 2;  // buffer of step s + 2
+        for (int s = 0; s < a.nk; s++) {
+          // buffer (s + 2) % 3 was last read in step s - 1, which every
+          // consumer finished before the barrier just passed; so was the
+          // A-scale slot of step s + 2 (last read in step s - 6)
+          if (s + 2 < a.nk) {
+            issue(pa, s + 2, bi);
+            bi = bi == 2 ? 0 : bi + 1;
+            wait_next(s + 2);
+          } else {
+            wait_vm<0>();
+          }
+          __syncthreads();
+        }
+      };
+      switch (pa.na) {
+        case 4: run(std::integral_constant<int, 4>{}); break;
+        case 3: run(std::integral_constant<int, 3>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        default: run(std::integral_constant<int, 0>{}); break;
       }
-    };
-    switch (max(0, min(4, (nb - pw + 3) >> 2))) {
-      case 4: run(std::integral_constant<int, 4>{}); break;
-      case 3: run(std::integral_constant<int, 3>{}); break;
-      case 2: run(std::integral_constant<int, 2>{}); break;
-      case 1: run(std::integral_constant<int, 1>{}); break;
-      default: run(std::integral_constant<int, 0>{}); break;
+      // every consumer is past the last step: buffer 0 and both A-scale slots
+      // are free, so the next item's first step goes out now, while the
+      // consumers run the epilogue in buffers 1 and 2
+      const int nxt = item + P;
+      const bool more = item_chunk(nxt) < n_chunks;
+      const ItemInfo done = cur;
+      if (more) {
+        cur = info(nxt);
+        pa = paddr(cur);
+        issue(pa, 0, 0);
+        pre0 = true;
+      }
+      __syncthreads();
+      copy_out(done);
+      __syncthreads();
+      if (!more) break;
+      item = nxt;
     }
   } else {
     // ---------------- consumer ----------------
     const int wm = wave;
-    constexpr int OC = GATEUP ? XC / 2 : XC;  // output columns of the tile
-    constexpr int OSTR = OC + 8;              // uint16 per row of the h / Y tile
-    static_assert(XM * OSTR * 2 + (GATEUP ? XM * QSTR + XM * 2 : 0) <= LDS_BYTES, "epilogue tiles fit");
-    uint16_t* os = reinterpret_cast<uint16_t*>(smem);
-    uint8_t* qs = smem + XM * OSTR * 2;  // gate/up: code tile [XM][QSTR]
-    uint8_t* ss = qs + XM * QSTR;        // gate/up: scale tile [XM][2]
+    for (;;) {
+      const ItemInfo it = info(item);
+      const int nb = (it.n + 15) >> 4;  // live 16-row blocks; block rbk belongs to wavefront pair rbk % 4
 
-    // Row block rb of this wavefront is block 4 rb + wm (rows 64 rb + 16 wm ..
-    // + 15); the consumer is instantiated per count of live blocks (NRB).
-    auto consume = [&](auto nrb_c) __attribute__((always_inline)) {
-      constexpr int NRB = decltype(nrb_c)::value;
-      f32x4 acc[NRB][8];
+      // Row block rb of this wavefront is block 4 rb + wm (rows 64 rb + 16 wm
+      // .. + 15); the consumer is instantiated per count of live blocks (NRB).
+      auto consume = [&](auto nrb_c) __attribute__((always_inline)) {
+        constexpr int NRB = decltype(nrb_c)::value;
+        f32x4 acc[NRB][8];
 #pragma unroll
-      for (int i = 0; i < NRB; i++)
+        for (int i = 0; i < NRB; i++)
 #pragma unroll
-        for (int j = 0; j < 8; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      __syncthreads();
-      int bi = 0;
-      for (int s = 0; s < a.nk; s++) {
-        const uint8_t* bb = smem + bi * BUF_BYTES;
-        i32x8 fa[NRB];
-        int sa[NRB];
-#pragma unroll
-        for (int rb = 0; rb < NRB; rb++) {
-          const int rbk = 4 * rb + wm;
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(bb + A_OFF + rbk * 2048 + 16 * lane);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(bb + A_OFF + rbk * 2048 + 1024 + 16 * lane);
-          fa[rb] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          sa[rb] = (int)(*reinterpret_cast<const uint32_t*>(smem + ASG_OFF + ((s >> 2) & 1) * ASG_SLOT +
-                                                            (16 * rbk + r) * 16 + 4 * (s & 3)) >> (8 * q));
-        }
-#pragma unroll
-        for (int cb = 0; cb < 8; cb++) {
-          const i32x4 f = *reinterpret_cast<const i32x4*>(bb + B_OFF + cb * 1024 + 16 * lane);
-          const i32x8 fb = i32x8{f.x, f.y, f.z, f.w, 0, 0, 0, 0};
-          const int sb = (int)(*reinterpret_cast<const uint32_t*>(bb + BS_OFF + (16 * cb + r) * 4) >> (8 * q));
-#pragma unroll
-          for (int rb = 0; rb < NRB; rb++)
-            acc[rb][cb] =
-                __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[rb], fb, acc[rb][cb], 0, 4, 0, sa[rb], 0, sb);
-        }
-        bi = bi == 2 ? 0 : bi + 1;
+          for (int j = 0; j < 8; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
         __syncthreads();
-      }
-      // epilogue, part 1: D[i][j] of block (rb, cb) is in lane j + 16 (i / 4),
-      // element i % 4: a lane holds rows 4q .. 4q + 3 of column r.  The bf16
-      // results leave through the tile in LDS as in the bf16 GEMM: adjacent
-      // lanes swap half their pairs (one DPP move) and write column pairs.
-      const bool odd = r & 1;
-      const uint32_t sel0 = odd ? 0x01000504u : 0x05040100u;
-      const uint32_t sel1 = odd ? 0x03020706u : 0x07060302u;
+        int bi = 0;
+        for (int s = 0; s < a.nk; s++) {
+          const uint8_t* bb = smem + bi * BUF_BYTES;
+          i32x8 fa[NRB];
+          int sa[NRB];
 #pragma unroll
-      for (int rb = 0; rb < NRB; rb++) {
-        const int row0 = 16 * (4 * rb + wm) + 4 * q;
-        float v[OC / 16][4];
-#pragma unroll
-        for (int oc = 0; oc < OC / 16; oc++)
-#pragma unroll
-          for (int e4 = 0; e4 < 4; e4++) {
-            float t;
-            if (GATEUP) {
-              const float gv = acc[rb][oc][e4], uv = acc[rb][oc + 4][e4];
-              t = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-            } else {
-              t = acc[rb][oc][e4];
-            }
-            v[oc][e4] = bf16_round(resident ? t : 0.f);
+          for (int rb = 0; rb < NRB; rb++) {
+            const int rbk = 4 * rb + wm;
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(bb + A_OFF + rbk * 2048 + 16 * lane);
+            const i32x4 hi = *reinterpret_cast<const i32x4*>(bb + A_OFF + rbk * 2048 + 1024 + 16 * lane);
+            fa[rb] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            sa[rb] = (int)(*reinterpret_cast<const uint32_t*>(smem + ASG_OFF + ((s >> 2) & 1) * ASG_SLOT +
+                                                              (16 * rbk + r) * 16 + 4 * (s & 3)) >> (8 * q));
           }
 #pragma unroll
-        for (int oc = 0; oc < OC / 16; oc++) {
-          const uint32_t pa = pack_bf16(v[oc][0], v[oc][2]), pb = pack_bf16(v[oc][1], v[oc][3]);
-          const uint32_t send = odd ? pa : pb, mine = odd ? pb : pa;
-          const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0xB1, 0xF, 0xF, false);
-          const int row = row0 + (odd ? 1 : 0);
-          const int col = 16 * oc + (r & ~1);
-          *reinterpret_cast<uint32_t*>(&os[row * OSTR + col]) = __builtin_amdgcn_perm(recv, mine, sel0);
-          *reinterpret_cast<uint32_t*>(&os[(row + 2) * OSTR + col]) = __builtin_amdgcn_perm(recv, mine, sel1);
+          for (int cb = 0; cb < 8; cb++) {
+            const i32x4 f = *reinterpret_cast<const i32x4*>(bb + B_OFF + cb * 1024 + 16 * lane);
+            const i32x8 fb = i32x8{f.x, f.y, f.z, f.w, 0, 0, 0, 0};
+            const int sb = (int)(*reinterpret_cast<const uint32_t*>(bb + BS_OFF + (16 * cb + r) * 4) >> (8 * q));
+#pragma unroll
+            for (int rb = 0; rb < NRB; rb++)
+              acc[rb][cb] =
+                  __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[rb], fb, acc[rb][cb], 0, 4, 0, sa[rb], 0, sb);
+          }
+          bi = bi == 2 ? 0 : bi + 1;
+          __syncthreads();
         }
-        if (GATEUP) {
-          // h at the MXFP8 rounding point: the 32-unit block p of row row0 + e4
-          // is column blocks 2p, 2p + 1 of the 16 lanes of this lane row
+        // epilogue, part 1: D[i][j] of block (rb, cb) is in lane j + 16 (i / 4),
+        // element i % 4: a lane holds rows 4q .. 4q + 3 of column r.  The bf16
+        // results leave through the tile in LDS as in the bf16 GEMM: adjacent
+        // lanes swap half their pairs (one DPP move) and write column pairs.
+        const bool odd = r & 1;
+        const uint32_t sel0 = odd ? 0x01000504u : 0x05040100u;
+        const uint32_t sel1 = odd ? 0x03020706u : 0x07060302u;
 #pragma unroll
-          for (int e4 = 0; e4 < 4; e4++)
+        for (int rb = 0; rb < NRB; rb++) {
+          const int row0 = 16 * (4 * rb + wm) + 4 * q;
+          float v[OC / 16][4];
 #pragma unroll
-            for (int p = 0; p < 2; p++) {
-              const float m = row16_max(fmaxf(fabsf(v[2 * p][e4]), fabsf(v[2 * p + 1][e4])));
-              const int sb = e8m0_of_amax(m);
-              const int row = row0 + e4;
-              const uint32_t c2 = e4m3_pair(v[2 * p][e4], v[2 * p + 1][e4], sb);
-              qs[row * QSTR + 32 * p + r] = (uint8_t)c2;
-              qs[row * QSTR + 32 * p + 16 + r] = (uint8_t)(c2 >> 8);
-              if (r == 0) ss[row * 2 + p] = (uint8_t)sb;
+          for (int oc = 0; oc < OC / 16; oc++)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; e4++) {
+              float t;
+              if (GATEUP) {
+                const float gv = acc[rb][oc][e4], uv = acc[rb][oc + 4][e4];
+                t = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+              } else {
+                t = acc[rb][oc][e4];
+              }
+              v[oc][e4] = bf16_round(it.resident ? t : 0.f);
             }
+#pragma unroll
+          for (int oc = 0; oc < OC / 16; oc++) {
+            const uint32_t pa = pack_bf16(v[oc][0], v[oc][2]), pb = pack_bf16(v[oc][1], v[oc][3]);
+            const uint32_t send = odd ? pa : pb, mine = odd ? pb : pa;
+            const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0xB1, 0xF, 0xF, false);
+            const int row = row0 + (odd ? 1 : 0);
+            const int col = 16 * oc + (r & ~1);
+            *reinterpret_cast<uint32_t*>(&os[row * OSTR + col]) = __builtin_amdgcn_perm(recv, mine, sel0);
+            *reinterpret_cast<uint32_t*>(&os[(row + 2) * OSTR + col]) = __builtin_amdgcn_perm(recv, mine, sel1);
+          }
+          if (GATEUP) {
+            // h at the MXFP8 rounding point: the 32-unit block p of row row0 +
+            // e4 is column blocks 2p, 2p + 1 of the 16 lanes of this lane row
+#pragma unroll
+            for (int e4 = 0; e4 < 4; e4++)
+#pragma unroll
+              for (int p = 0; p < 2; p++) {
+                const float m = row16_max(fmaxf(fabsf(v[2 * p][e4]), fabsf(v[2 * p + 1][e4])));
+                const int sb = e8m0_of_amax(m);
+                const int row = row0 + e4;
+                const uint32_t c2 = e4m3_pair(v[2 * p][e4], v[2 * p + 1][e4], sb);
+                qs[row * QSTR + 32 * p + r] = (uint8_t)c2;
+                qs[row * QSTR + 32 * p + 16 + r] = (uint8_t)(c2 >> 8);
+                if (r == 0) ss[row * 2 + p] = (uint8_t)sb;
+              }
+          }
         }
+      };
+      switch (max(0, min(4, (nb - wm + 3) >> 2))) {
+        case 4: consume(std::integral_constant<int, 4>{}); break;
+        case 3: consume(std::integral_constant<int, 3>{}); break;
+        case 2: consume(std::integral_constant<int, 2>{}); break;
+        case 1: consume(std::integral_constant<int, 1>{}); break;
+        default:  // no live rows: the barriers only
+          __syncthreads();
+          for (int s = 0; s < a.nk; s++) __syncthreads();
       }
-    };
-    switch (max(0, min(4, (nb - wm + 3) >> 2))) {
-      case 4: consume(std::integral_constant<int, 4>{}); break;
-      case 3: consume(std::integral_constant<int, 3>{}); break;
-      case 2: consume(std::integral_constant<int, 2>{}); break;
-      case 1: consume(std::integral_constant<int, 1>{}); break;
-      default:  // no live rows: the barriers only
-        __syncthreads();
-        for (int s = 0; s < a.nk; s++) __syncthreads();
-    }
-  }
-
-  // epilogue, part 2 (all eight wavefronts): the tiles leave in 16-byte row
-  // segments
-  __syncthreads();
-  {
-    constexpr int OC = GATEUP ? XC / 2 : XC;
-    constexpr int OSTR = OC + 8;
-    constexpr int SEGS = OC / 8;
-    const uint16_t* os = reinterpret_cast<const uint16_t*>(smem);
-#pragma unroll 4
-    for (int i = tid; i < n * SEGS; i += XT) {
-      const int row = i / SEGS, sg = i % SEGS;
-      *reinterpret_cast<uint4*>(out + (int64_t)(p0 + row) * units + u0 + 8 * sg) =
-          *reinterpret_cast<const uint4*>(&os[row * OSTR + 8 * sg]);
-    }
-    if (GATEUP) {
-      const uint8_t* qs = smem + XM * OSTR * 2;
-      const uint8_t* ss = qs + XM * QSTR;
-      for (int i = tid; i < n * 4; i += XT) {
-        const int row = i >> 2, sg = i & 3;
-        *reinterpret_cast<uint4*>(hq + (int64_t)(p0 + row) * units + u0 + 16 * sg) =
-            *reinterpret_cast<const uint4*>(&qs[row * QSTR + 16 * sg]);
-      }
-      for (int row = tid; row < n; row += XT)
-        *reinterpret_cast<uint16_t*>(hs + (int64_t)(p0 + row) * a.hs_stride + u0 / 32) =
-            *reinterpret_cast<const uint16_t*>(&ss[row * 2]);
+      __syncthreads();
+      copy_out(it);
+      __syncthreads();
+      item += P;
+      if (item_chunk(item) >= n_chunks) break;
     }
   }
 }
@@ -495,8 +555,8 @@ hipError_t launch_ffn_dec_mx(const moe_dims& d, const uint16_t* x, const FfnGeom
 }
 
 hipError_t launch_ffn_mx(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
-                         uint16_t* y_rows, void* ws, void* mx_ws, int stages, hipEvent_t ev_start, hipEvent_t ev_stop,
-                         hipStream_t s) {
+                         uint16_t* y_rows, void* ws, void* mx_ws, int n_cu, int stages, hipEvent_t ev_start,
+                         hipEvent_t ev_stop, hipStream_t s) {
   const WsLayout wl = ws_layout(d);
   const MxWsLayout ml = mx_ws_layout(d);
   uint8_t* base = static_cast<uint8_t*>(ws);
@@ -529,8 +589,10 @@ hipError_t launch_ffn_mx(const moe_dims& d, const uint16_t* x, const FfnGeom& g,
     a.nk = K / XK;
     a.as_stride = gu ? ml.xs_stride : ml.hs_stride;
     a.hs_stride = ml.hs_stride;
-    const int64_t groups8 = (wl.max_chunks + 7) / 8;
-    const dim3 grid((unsigned)(groups8 * 8 * a.n_ut)), block(XT);
+    // persistent grid: one workgroup per CU (a multiple of 8), at most one per item
+    const int64_t items = (wl.max_chunks + 7) / 8 * 8 * a.n_ut;
+    const int64_t cap = ((int64_t)n_cu + 7) / 8 * 8;
+    const dim3 grid((unsigned)(items < cap ? items : cap)), block(XT);
     const uint8_t* aq = gu ? xq : hq;
     const uint8_t* as = gu ? xs : hs;
     uint16_t* out = gu ? h : y_rows;

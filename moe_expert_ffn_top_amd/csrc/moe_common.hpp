@@ -277,8 +277,8 @@ hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int32_t K, uint8_t* 
 // MX workspace mx_ws (mx_ws_layout) carries the quantised activations.  Same
 // stage mask and events as launch_ffn_gemm.
 hipError_t launch_ffn_mx(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
-                         uint16_t* y_rows, void* ws, void* mx_ws, int stages, hipEvent_t ev_start, hipEvent_t ev_stop,
-                         hipStream_t s);
+                         uint16_t* y_rows, void* ws, void* mx_ws, int n_cu, int stages, hipEvent_t ev_start,
+                         hipEvent_t ev_stop, hipStream_t s);
 // The same for decode-sized groups: the weight-streaming kernel on MX blobs,
 // its A rows the bf16 values of MXFP8(x) and MXFP8(h) (kept in mx_ws).
 hipError_t launch_ffn_dec_mx(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
