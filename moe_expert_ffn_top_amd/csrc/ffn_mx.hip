@@ -22,9 +22,11 @@
 //        B   the 128 K values of a 16-column block are 1 KB of contiguous blob
 //            bytes (four 32-column chunks of its 16 rows).  Lane c + 16 q holds
 //            column c, K 32q .. 32q + 31: the scaled MFMA's FP4 operand.
-//        A   two 1 KB halves per 16-row block.  Lane r + 16 q of half hf holds
-//            row r, K 64 hf + 16 q .. + 15: the two 16-byte pieces of the FP8
-//            operand.
+//        A   16-row blocks of 2 KB, row r's 128 bytes at 128 r, its 16-byte
+//            chunk c at slot c ^ (r & 7) (a swizzle that keeps the fragment
+//            reads of 16 rows conflict-free).  One DMA instruction moves 8
+//            whole rows (8 lanes each, one 128-byte line per row).  The FP8
+//            operand of lane (r, q) is chunks q and 4 + q of row r.
 //        scales  per step one dword per B column holding the step's four E8M0
 //            bytes; the A rows' scales come every four steps, 16 bytes per
 //            row, into a two-slot ring (one gathered 16-byte load per row
@@ -281,6 +283,7 @@ __global__ __launch_bounds__(XT) void k_ffn_mx(MxArgs a, const int4* __restrict_
     // n - 1 (their outputs are dropped)
     struct PAddr {
       const uint8_t* asrc[4];
+      const uint8_t* asrc2[4];
       const uint8_t* ssrc;
       const uint8_t* bsrc[2];
       const uint8_t* bssrc;
@@ -292,8 +295,15 @@ __global__ __launch_bounds__(XT) void k_ffn_mx(MxArgs a, const int4* __restrict_
         const int p = it.p0 + min(row, it.n - 1);
         return GATEUP ? (int64_t)(p < a.Tk ? perm[p] / a.k : p - a.Tk) : (int64_t)p;
       };
+      // lane l of the block's half hf moves row 8 hf + l / 8, slot l % 8
+      // (chunk (l % 8) ^ (row & 7)); asrc[i] is the lane's row of half 0,
+      // asrc2[i] of half 1
+      const int sl = lane & 7, rr = lane >> 3;
 #pragma unroll
-      for (int i = 0; i < 4; i++) pa.asrc[i] = aq + arow(16 * (pw + 4 * i) + r) * K + 16 * q;
+      for (int i = 0; i < 4; i++) {
+        pa.asrc[i] = aq + arow(16 * (pw + 4 * i) + rr) * K + 16 * (sl ^ rr);
+        pa.asrc2[i] = aq + arow(16 * (pw + 4 * i) + 8 + rr) * K + 16 * (sl ^ rr);  // (8 + rr) & 7 == rr
+      }
       pa.ssrc = as + arow(64 * pw + lane) * a.as_stride;
       // B: column blocks 2 pw and 2 pw + 1 (gate/up: blocks 0..3 gate, 4..7
       // up, the same units)
@@ -321,7 +331,7 @@ __global__ __launch_bounds__(XT) void k_ffn_mx(MxArgs a, const int4* __restrict_
         if (i < pa.na) {
           const uint32_t d = buf + A_OFF + (uint32_t)(pw + 4 * i) * 2048u;
           dma16(pa.asrc[i] + XK * s, __builtin_amdgcn_readfirstlane(d));
-          dma16(pa.asrc[i] + XK * s + 64, __builtin_amdgcn_readfirstlane(d + 1024u));
+          dma16(pa.asrc2[i] + XK * s, __builtin_amdgcn_readfirstlane(d + 1024u));
         }
       }
 #pragma unroll
@@ -425,8 +435,9 @@ __global__ __launch_bounds__(XT) void k_ffn_mx(MxArgs a, const int4* __restrict_
 #pragma unroll
           for (int rb = 0; rb < NRB; rb++) {
             const int rbk = 4 * rb + wm;
-            const i32x4 lo = *reinterpret_cast<const i32x4*>(bb + A_OFF + rbk * 2048 + 16 * lane);
-            const i32x4 hi = *reinterpret_cast<const i32x4*>(bb + A_OFF + rbk * 2048 + 1024 + 16 * lane);
+            const uint8_t* rowp = bb + A_OFF + rbk * 2048 + 128 * r;
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(rowp + 16 * (q ^ (r & 7)));
+            const i32x4 hi = *reinterpret_cast<const i32x4*>(rowp + 16 * ((4 + q) ^ (r & 7)));
             fa[rb] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
             sa[rb] = (int)(*reinterpret_cast<const uint32_t*>(smem + ASG_OFF + ((s >> 2) & 1) * ASG_SLOT +
                                                               (16 * rbk + r) * 16 + 4 * (s & 3)) >> (8 * q));
