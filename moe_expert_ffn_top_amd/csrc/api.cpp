@@ -390,7 +390,7 @@ int moe_expert_ffn_stages(const moe_dims* d, const uint16_t* x, const void* pool
   // otherwise weight streaming over 16-row tiles (the grouping kernels wrote
   // the matching work list)
   if (moe::use_gemm(*d))
-    return hip_status(moe::launch_ffn_gemm(*d, x, g, perm, h, y_rows, ws, stages, e0, e1, st), "expert FFN launch");
+    return hip_status(moe::launch_ffn_gemm(*d, x, g, perm, h, y_rows, ws, n_cu, stages, e0, e1, st), "expert FFN launch");
   return hip_status(moe::launch_ffn_dec(*d, x, g, perm, h, y_rows, ws, n_cu, stages, e0, e1, st),
                     "expert FFN launch");
 }

@@ -25,6 +25,7 @@
 #include <hip/hip_ext.h>
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "moe_common.hpp"
@@ -86,16 +87,19 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
   constexpr int UPW = GC / NMAT;  // units per workgroup
   const int K = GATEUP ? a.H : a.I;
   const int units = GATEUP ? a.I : a.H;
-  // blocks are dealt to the 8 XCDs round-robin: block b runs on XCD b % 8
-  const int b = blockIdx.x, xcd = b & 7, jb = b >> 3;
-  const int ut = jb % a.n_ut, chunk = (jb / a.n_ut) * 8 + xcd;
-  if (chunk >= *as_const(meta + 1)) return;
+  // Work items are (chunk, column tile) pairs: item i is tile (i / 8) % n_ut
+  // of chunk ((i / 8) / n_ut) * 8 + i % 8.  Blocks are dealt to the 8 XCDs
+  // round-robin and the grid is a multiple of 8, so the items block b walks
+  // (b, b + gridDim.x, ...) all run on XCD b % 8, where the tiles of their
+  // chunks share its L2.  Their chunks grow along the walk: the first one
+  // past the chunk count ends it.
+  const int n_chunks = *as_const(meta + 1);
   using i32x4 = int __attribute__((ext_vector_type(4)));
-  const i32x4 cd = as_const(reinterpret_cast<const i32x4*>(chunks))[chunk];
-  const int p0 = cd.y, n = cd.z, slot = cd.w;
-  const bool resident = slot >= 0 && slot < a.n_slots;
-  const uint8_t* blob = pool + (resident ? (uint64_t)slot * (uint64_t)a.slot_stride : 0);
-  const int u0 = ut * UPW;
+  auto item_chunk = [&](int i) { return ((i >> 3) / a.n_ut) * 8 + (i & 7); };
+  auto item_desc = [&](int i) { return as_const(reinterpret_cast<const i32x4*>(chunks))[item_chunk(i)]; };
+  auto item_u0 = [&](int i) { return ((i >> 3) % a.n_ut) * UPW; };
+  int item = blockIdx.x;
+  if (item_chunk(item) >= n_chunks) return;
 
   __shared__ __align__(16) uint16_t As[2][GM * LROW];
   __shared__ __align__(16) uint16_t Bs[2][GC * LROW];
@@ -112,6 +116,23 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
   // steps past the end stage zeros
   const int nk4 = (a.nk + 3) & ~3;
 
+  // epilogue, part 2 (all eight wavefronts, once the consumers have written
+  // the tile): it leaves in 16-byte row segments (units come in multiples of
+  // 16); the second barrier frees the A buffers for the next item
+  constexpr int SEGS = OC / 8;
+  auto copy_out = [&](int p0, int n, int u0) __attribute__((always_inline)) {
+    __syncthreads();
+#pragma unroll 4
+    for (int i = tid; i < n * SEGS; i += GT) {
+      const int row = i / SEGS, sg = i % SEGS;
+      const int unit = u0 + 8 * sg;
+      if (unit < units)
+        *reinterpret_cast<uint4*>(out + (int64_t)(p0 + row) * units + unit) =
+            *reinterpret_cast<const uint4*>(&os[row * OSTR + 8 * sg]);
+    }
+    __syncthreads();
+  };
+
   if (wave >= 4) {
     // ---------------- producer ----------------
     const int t = tid - 256;
@@ -120,35 +141,48 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
     // not written to LDS unless their 16-row block is live (their outputs are
     // dropped)
     const int ah = t & 1;
-    const int arow16 = (n + 15) & ~15;
     int ar[2];
-    bool alive[2];
-    const uint16_t* asrc[2];
 #pragma unroll
-    for (int h = 0; h < 2; h++) {
-      ar[h] = (t >> 1) + 128 * h;
-      alive[h] = ar[h] < arow16;
-      const int p = p0 + min(ar[h], n - 1);
-      const int64_t arow = GATEUP ? (int64_t)(p < a.Tk ? perm[p] / a.k : p - a.Tk) : (int64_t)p;
-      asrc[h] = ain + arow * K;
-    }
+    for (int h = 0; h < 2; h++) ar[h] = (t >> 1) + 128 * h;
     // B staging: column bc, K half bh
     const int bc = t >> 1, bh = t & 1;
     const int bmat = GATEUP ? bc / UPW : 2;
-    const int bunit = u0 + bc % UPW;
-    const bool bvalid = resident && bunit < units;
-    const int bunit_c = min(bunit, units - 1);
-    // a non-resident group reads the pool's first bytes (valid memory) and is
-    // zeroed through its scales
-    // (blob tiling in moe_common.hpp: chunk j of the column at crow + 256 j, its
-    // scales at sblk + blob_sc_off(j, nc, br))
-    const int nc = K / 32, br = bunit_c & 15;
-    // this row's offset in a scale group: 32 bytes per row in whole groups,
-    // 2 (nc % 16) in the last one when it is shorter
-    const uint32_t sfull = (uint32_t)br * 32u, stail = (uint32_t)br * 2u * (uint32_t)(nc & 15);
-    const int nfull = nc >> 4;
-    const uint8_t* crow = bvalid ? blob + a.off_codes[bmat] + (int64_t)(bunit_c >> 4) * (8 * K) + br * 16 : pool;
-    const uint8_t* sblk = bvalid ? blob + a.off_scales[bmat] + (int64_t)(bunit_c >> 4) * K : pool;
+    const int nc = K / 32, nfull = nc >> 4;
+    // the item's sources, set by setup()
+    bool alive[2];
+    const uint16_t* asrc[2];
+    bool bvalid;
+    uint32_t sfull, stail;
+    const uint8_t* crow;
+    const uint8_t* sblk;
+    auto setup = [&](int it) __attribute__((always_inline)) {
+      const i32x4 cd = item_desc(it);
+      const int p0 = cd.y, n = cd.z, slot = cd.w;
+      const bool resident = slot >= 0 && slot < a.n_slots;
+      const uint8_t* blob = pool + (resident ? (uint64_t)slot * (uint64_t)a.slot_stride : 0);
+      const int arow16 = (n + 15) & ~15;
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        alive[h] = ar[h] < arow16;
+        const int p = p0 + min(ar[h], n - 1);
+        const int64_t arow = GATEUP ? (int64_t)(p < a.Tk ? perm[p] / a.k : p - a.Tk) : (int64_t)p;
+        asrc[h] = ain + arow * K;
+      }
+      const int bunit = item_u0(it) + bc % UPW;
+      bvalid = resident && bunit < units;
+      const int bunit_c = min(bunit, units - 1);
+      // a non-resident group reads the pool's first bytes (valid memory) and
+      // is zeroed through its scales
+      // (blob tiling in moe_common.hpp: chunk j of the column at crow + 256 j,
+      // its scales at sblk + blob_sc_off(j, nc, br))
+      const int br = bunit_c & 15;
+      // this row's offset in a scale group: 32 bytes per row in whole groups,
+      // 2 (nc % 16) in the last one when it is shorter
+      sfull = (uint32_t)br * 32u;
+      stail = (uint32_t)br * 2u * (uint32_t)(nc & 15);
+      crow = bvalid ? blob + a.off_codes[bmat] + (int64_t)(bunit_c >> 4) * (8 * K) + br * 16 : pool;
+      sblk = bvalid ? blob + a.off_scales[bmat] + (int64_t)(bunit_c >> 4) * K : pool;
+    };
 
     // Every load stays inside its row: the K offset is clamped to the last
     // 32 values, which only a half step beyond K (K % 64 == 32) needs; that
@@ -205,28 +239,48 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
     // consumers compute step h from buffer h % 2
     // (four named stages, NST of them: an array of them is not kept in registers)
     Stage st0, st1, st2, st3;
+    setup(item);
     gload(st0, 0);
     gload(st1, 1);
     gload(st2, 2);
-    stage(st0, 0, 0);
-    __syncthreads();
-    for (int s = 0; s < nk4; s += 4) {
-      gload(st3, s + 3);
-      stage(st1, 1, s + 1);
+    for (;;) {
+      const i32x4 cd = item_desc(item);
+      stage(st0, 0, 0);
       __syncthreads();
-      gload(st0, s + 4);
-      stage(st2, 0, s + 2);
-      __syncthreads();
-      gload(st1, s + 5);
-      stage(st3, 1, s + 3);
-      __syncthreads();
-      gload(st2, s + 6);
-      stage(st0, 0, s + 4);
-      __syncthreads();
+      for (int s = 0; s < nk4; s += 4) {
+        gload(st3, s + 3);
+        stage(st1, 1, s + 1);
+        __syncthreads();
+        gload(st0, s + 4);
+        stage(st2, 0, s + 2);
+        __syncthreads();
+        gload(st1, s + 5);
+        stage(st3, 1, s + 3);
+        __syncthreads();
+        gload(st2, s + 6);
+        stage(st0, 0, s + 4);
+        __syncthreads();
+      }
+      // the next item's first three steps load while the consumers finish this
+      // one (after the last item they reload its own, harmlessly)
+      const int nxt = item + (int)gridDim.x;
+      const bool more = item_chunk(nxt) < n_chunks;
+      if (more) setup(nxt);
+      gload(st0, 0);
+      gload(st1, 1);
+      gload(st2, 2);
+      copy_out(cd.y, cd.z, item_u0(item));
+      if (!more) break;
+      item = nxt;
     }
   } else {
 
   // ---------------- consumer ----------------
+  for (;;) {
+  const i32x4 cd = item_desc(item);
+  const int p0 = cd.y, n = cd.z, slot = cd.w;
+  const bool resident = slot >= 0 && slot < a.n_slots;
+  const uint8_t* blob = pool + (resident ? (uint64_t)slot * (uint64_t)a.slot_stride : 0);
   // the global scales, fetched now as a vector load: it has the whole loop to
   // land (a scalar load would share the LDS wait counter)
   int zero_v;
@@ -331,26 +385,17 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
         __syncthreads();
       }
   }
+  copy_out(p0, n, item_u0(item));
+  item += (int)gridDim.x;
+  if (item_chunk(item) >= n_chunks) break;
   }
-
-  // epilogue, part 2 (all eight wavefronts): the tile leaves in 16-byte row
-  // segments (units come in multiples of 16)
-  __syncthreads();
-  constexpr int SEGS = OC / 8;
-#pragma unroll 4
-  for (int i = tid; i < n * SEGS; i += GT) {
-    const int row = i / SEGS, sg = i % SEGS;
-    const int unit = u0 + 8 * sg;
-    if (unit < units)
-      *reinterpret_cast<uint4*>(out + (int64_t)(p0 + row) * units + unit) =
-          *reinterpret_cast<const uint4*>(&os[row * OSTR + 8 * sg]);
   }
 }
 
 }  // namespace
 
 hipError_t launch_ffn_gemm(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
-                           uint16_t* y_rows, void* ws, int stages, hipEvent_t ev_start, hipEvent_t ev_stop,
+                           uint16_t* y_rows, void* ws, int n_cu, int stages, hipEvent_t ev_start, hipEvent_t ev_stop,
                            hipStream_t s) {
   const WsLayout wl = ws_layout(d);
   uint8_t* base = static_cast<uint8_t*>(ws);
@@ -375,8 +420,9 @@ hipError_t launch_ffn_gemm(const moe_dims& d, const uint16_t* x, const FfnGeom& 
     const int upw = GC / (gu ? 2 : 1);
     a.n_ut = (units + upw - 1) / upw;
     a.nk = (K + GK - 1) / GK;
-    const int64_t groups8 = (wl.max_chunks + 7) / 8;
-    const dim3 grid((unsigned)(groups8 * 8 * a.n_ut)), block(GT);
+    // persistent: one workgroup per CU (the LDS holds one), a multiple of 8
+    const int64_t items = (wl.max_chunks + 7) / 8 * 8 * a.n_ut;
+    const dim3 grid((unsigned)std::min<int64_t>(items, (int64_t)(n_cu + 7) / 8 * 8)), block(GT);
     const bool first = gu || !(stages & 1), last = !gu || !(stages & 2);
     hipEvent_t e0 = first ? ev_start : nullptr, e1 = last ? ev_stop : nullptr;
     const uint16_t* ain = gu ? x : h;

@@ -265,9 +265,9 @@ hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g
                           uint16_t* h, uint16_t* y_rows, void* ws, int n_cu, int stages, hipEvent_t ev_start,
                           hipEvent_t ev_stop, hipStream_t s, bool mx = false, const uint16_t* down_in = nullptr);
 // Grouped-GEMM expert FFN over the chunk list (prefill-sized groups); same
-// stage mask and events as launch_ffn_dec.
+// stage mask and events as launch_ffn_dec; n_cu sizes the persistent grid.
 hipError_t launch_ffn_gemm(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
-                           uint16_t* y_rows, void* ws, int stages, hipEvent_t ev_start, hipEvent_t ev_stop,
+                           uint16_t* y_rows, void* ws, int n_cu, int stages, hipEvent_t ev_start, hipEvent_t ev_stop,
                            hipStream_t s);
 // bf16 rows [rows][K] (K % 32 == 0) -> E4M3 codes [rows][K] and E8M0 scales
 // [rows][K/32] (MXFP8); ev_start (may be null) is recorded at its start.
