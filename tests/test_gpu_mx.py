@@ -179,6 +179,9 @@ MX_SMALL = {
     "mx_multichunk": Config(52, "mxm", T=700, H=512, I=256, E=4, k=2, L=1, router="matrix", fmt="mx"),
     # Zipf routing: one group above 256 rows and many small ones; H = 384 (3 K steps)
     "mx_zipf": Config(53, "mxz", T=256, H=384, I=128, E=16, k=4, L=1, router="zipf", zipf_s=1.2, fmt="mx"),
+    # more (chunk, column tile) items than CUs (100 chunks: 800 gate/up and
+    # 400 down items), so each persistent workgroup walks several
+    "mx_many_items": Config(54, "mxi", T=2048, H=512, I=512, E=64, k=8, L=1, router="matrix", fmt="mx"),
 }
 
 

@@ -94,6 +94,10 @@ SMALL = {
     "gemm_ragged": Config(38, "gr", T=300, H=544, I=224, E=4, k=2, L=1, router="matrix"),
     # GEMM path under Zipf routing: one group above 256 rows, many small ones
     "gemm_zipf_split": Config(39, "gz", T=256, H=256, I=128, E=16, k=4, L=1, router="zipf", zipf_s=1.2),
+    # GEMM path with more (chunk, column tile) items than any GPU has CUs: 100
+    # chunks give 800 gate/up and 400 down items, so each persistent workgroup
+    # walks several, loading the next while finishing the last
+    "gemm_many_items": Config(44, "mi", T=2048, H=512, I=512, E=64, k=8, L=1, router="matrix"),
 }
 
 
