@@ -265,9 +265,16 @@ int moe_residency_fill(const moe_dims* d, const moe_blob_layout* layout,
  * whose hot expert is still out of the cache and whose cold expert is still
  * in it, copies the hot blob from host_blobs (device-readable pinned memory,
  * as for moe_residency_fill) into the cold expert's slot, then sets the hot
- * expert's table entry to that slot and the cold one's to -1.  fill_scratch
- * [n_plan][2] and n_scratch [1]: device scratch.  Everything runs on `stream`
- * in that order; kernels that read the pool must be ordered after it.
+ * expert's table entry to that slot and the cold one's to -1.  An entry that
+ * names, in its layer, an expert that an earlier entry of the plan already
+ * names (as hot or cold) is skipped.  fill_scratch [n_plan][2] and n_scratch
+ * [1]: device scratch.  Everything runs on `stream` in that order; kernels
+ * that read the pool must be ordered after it.
+ * The swaps rewrite slot_table only.  A table whose slots are also managed by
+ * moe_residency_update (slot_owner, last_use) must not be passed here: the
+ * LRU state would still name the cold expert as the slot's owner, and a later
+ * eviction of that slot would leave the hot expert's entry pointing at another
+ * expert's bytes.  Use one of the two policies per table.
  */
 int moe_heat_update(const moe_dims* d, int32_t layer, const int32_t* offsets,
                     float* heat, moe_stream_t stream);

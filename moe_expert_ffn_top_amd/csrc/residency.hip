@@ -241,7 +241,10 @@ __global__ __launch_bounds__(256) void k_heat_decay(float* __restrict__ heat, in
 
 // plan entry i = (layer, hot, cold) -> fill (key of (layer, hot), slot of cold);
 // an entry that no longer fits the table (hot resident, cold not) gets key -1
-// and is skipped by the fill and the publication
+// and is skipped by the fill and the publication.  So does an entry that
+// names, in its layer, an expert an earlier entry already names (as hot or as
+// cold): two fills into one slot, or one expert moved twice, would leave the
+// table pointing at bytes that are not its expert's.
 __global__ __launch_bounds__(256) void k_swap_list(const int3* __restrict__ plan, int n_plan, int L, int E,
                                                    int n_slots, const int32_t* __restrict__ table,
                                                    int2* __restrict__ fills, int32_t* __restrict__ n_fill) {
@@ -250,7 +253,11 @@ __global__ __launch_bounds__(256) void k_swap_list(const int3* __restrict__ plan
   if (i >= n_plan) return;
   const int3 p = plan[i];
   const int E1 = E + 1;
-  const bool ok = p.x >= 0 && p.x < L && p.y >= 0 && p.y < E && p.z >= 0 && p.z < E && p.y != p.z;
+  bool ok = p.x >= 0 && p.x < L && p.y >= 0 && p.y < E && p.z >= 0 && p.z < E && p.y != p.z;
+  for (int j = 0; ok && j < i; j++) {
+    const int3 q = plan[j];
+    if (q.x == p.x && (q.y == p.y || q.y == p.z || q.z == p.y || q.z == p.z)) ok = false;
+  }
   const int hot_slot = ok ? table[p.x * E1 + p.y] : 0, cold_slot = ok ? table[p.x * E1 + p.z] : -1;
   const bool fits = ok && hot_slot < 0 && cold_slot >= 0 && cold_slot < n_slots;
   fills[i] = fits ? make_int2(p.x * E1 + p.y, cold_slot) : make_int2(-1, -1);

@@ -108,3 +108,51 @@ def test_swap_apply_moves_blobs_and_publishes(B):
         exp_pool[s, :lay.blob_bytes] = blobs[l * E1 + hot, :lay.blob_bytes]
     assert np.array_equal(t_dev.cpu().numpy(), exp_table)
     assert np.array_equal(pool.view(S, stride).cpu().numpy(), exp_pool)
+
+
+def test_swap_apply_skips_entries_naming_an_expert_twice(B):
+    """A plan that names one expert in two entries of a layer (as hot or as
+    cold) applies only the first of them: two fills into one slot, or one
+    expert moved twice, would leave the table naming bytes of another expert."""
+    L, E, H, I = 1, 8, 64, 32
+    E1 = E + 1
+    say("[gpu] swap apply: repeated experts in a plan")
+    lay = B.moe_blob_layout_init(H, I)
+    stride = lay.slot_stride
+    rng = np.random.default_rng(9)
+    blobs = rng.integers(0, 256, size=(L * E1, stride), dtype=np.uint8)
+    host = torch.empty(blobs.size, dtype=torch.uint8, pin_memory=True)
+    host.numpy()[:] = blobs.reshape(-1)
+    dptr = _device_pointer(host.data_ptr())
+    if dptr is None:
+        pytest.skip("pinned host memory has no device address here")
+    table = np.full((L, E1), -1, np.int32)
+    for s, e in enumerate(list(range(4, E)) + [E]):   # experts 4..7 and the shared one resident
+        table[0, e] = s
+    S = 5
+    pool_np = np.zeros((S, stride), np.uint8)
+    for e in range(E1):
+        if table[0, e] >= 0:
+            pool_np[table[0, e]] = blobs[e]
+    pool = torch.from_numpy(pool_np.reshape(-1).copy()).cuda()
+    d = B.Dims(1, H, I, E, 1, L)
+    plan = np.array([[0, 0, 6],    # applied
+                     [0, 1, 6],    # cold 6 again: skipped
+                     [0, 0, 4],    # hot 0 again: skipped
+                     [0, 2, 4],    # applied
+                     [0, 6, 5]],   # names 6, already a cold of entry 0: skipped
+                    np.int32)
+    t_dev = torch.from_numpy(table.copy()).cuda()
+    scratch = torch.zeros((len(plan), 2), dtype=torch.int32, device="cuda")
+    nsc = torch.zeros(1, dtype=torch.int32, device="cuda")
+    B.moe_swap_apply(d, lay, dptr, pool, pool.numel(), S, t_dev, torch.from_numpy(plan).cuda(), len(plan),
+                     scratch, nsc)
+    torch.cuda.synchronize()
+    exp_table, exp_pool = table.copy(), pool_np.copy()
+    for hot, cold in ((0, 6), (2, 4)):
+        s = table[0, cold]
+        exp_table[0, hot], exp_table[0, cold] = s, -1
+        exp_pool[s, :lay.blob_bytes] = blobs[hot, :lay.blob_bytes]
+    assert np.array_equal(t_dev.cpu().numpy(), exp_table)
+    assert np.array_equal(pool.view(S, stride).cpu().numpy(), exp_pool)
+    assert np.array_equal(scratch.cpu().numpy()[[1, 2, 4], 0], [-1, -1, -1])
