@@ -136,10 +136,12 @@ def test_swap_apply_skips_entries_naming_an_expert_twice(B):
             pool_np[table[0, e]] = blobs[e]
     pool = torch.from_numpy(pool_np.reshape(-1).copy()).cuda()
     d = B.Dims(1, H, I, E, 1, L)
+    # an entry is checked against every earlier entry, applied or skipped
     plan = np.array([[0, 0, 6],    # applied
                      [0, 1, 6],    # cold 6 again: skipped
                      [0, 0, 4],    # hot 0 again: skipped
-                     [0, 2, 4],    # applied
+                     [0, 2, 4],    # cold 4 named by the (skipped) entry before: skipped
+                     [0, 2, 7],    # applied
                      [0, 6, 5]],   # names 6, already a cold of entry 0: skipped
                     np.int32)
     t_dev = torch.from_numpy(table.copy()).cuda()
@@ -149,10 +151,10 @@ def test_swap_apply_skips_entries_naming_an_expert_twice(B):
                      scratch, nsc)
     torch.cuda.synchronize()
     exp_table, exp_pool = table.copy(), pool_np.copy()
-    for hot, cold in ((0, 6), (2, 4)):
+    for hot, cold in ((0, 6), (2, 7)):
         s = table[0, cold]
         exp_table[0, hot], exp_table[0, cold] = s, -1
         exp_pool[s, :lay.blob_bytes] = blobs[hot, :lay.blob_bytes]
     assert np.array_equal(t_dev.cpu().numpy(), exp_table)
     assert np.array_equal(pool.view(S, stride).cpu().numpy(), exp_pool)
-    assert np.array_equal(scratch.cpu().numpy()[[1, 2, 4], 0], [-1, -1, -1])
+    assert np.array_equal(scratch.cpu().numpy()[[1, 2, 3, 5], 0], [-1, -1, -1, -1])
