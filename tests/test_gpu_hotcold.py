@@ -141,7 +141,7 @@ def test_swap_apply_skips_entries_naming_an_expert_twice(B):
                      [0, 1, 6],    # cold 6 again: skipped
                      [0, 0, 4],    # hot 0 again: skipped
                      [0, 2, 4],    # cold 4 named by the (skipped) entry before: skipped
-                     [0, 2, 7],    # applied
+                     [0, 3, 7],    # applied (experts named by no earlier entry)
                      [0, 6, 5]],   # names 6, already a cold of entry 0: skipped
                     np.int32)
     t_dev = torch.from_numpy(table.copy()).cuda()
@@ -151,7 +151,7 @@ def test_swap_apply_skips_entries_naming_an_expert_twice(B):
                      scratch, nsc)
     torch.cuda.synchronize()
     exp_table, exp_pool = table.copy(), pool_np.copy()
-    for hot, cold in ((0, 6), (2, 7)):
+    for hot, cold in ((0, 6), (3, 7)):
         s = table[0, cold]
         exp_table[0, hot], exp_table[0, cold] = s, -1
         exp_pool[s, :lay.blob_bytes] = blobs[hot, :lay.blob_bytes]
