@@ -438,6 +438,31 @@ int moe_expert_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool,
                       uint64_t mx_ws_bytes, int32_t stages, void* ev_start, void* ev_stop,
                       moe_stream_t stream);
 
+/* moe_expert_ffn_mx for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, hosts that forbid
+ * hipMalloc.  Same computation, arguments and results as moe_expert_ffn_mx
+ * with stages as there, except that the MX workspace (mx_ws) is not an
+ * argument: it is a static device array inside the library, 32 MiB (33554432
+ * bytes) per GPU, held from the first call on that GPU until the process
+ * ends.  No timing events.
+ * Limit: dims whose moe_mx_workspace_bytes exceeds 32 MiB are refused with
+ * MOE_ERR_WORKSPACE, having enqueued nothing (e.g. T = 4096 at H = 2048,
+ * I = 512, k = 10 fits; T = 8192 does not).
+ * Set-up: the first call on a device looks up that device's address of the
+ * array (hipGetSymbolAddress, with the device current); make it outside any
+ * graph capture.  The call allocates nothing: no hipMalloc, no hipFree.
+ * Sharing: every call on one GPU uses that GPU's one array, which keeps the
+ * last call's contents.  Calls that overlap on one GPU (two streams, two
+ * threads, two captured graphs replayed concurrently) race on it and must be
+ * ordered by the caller; a gate/up stage and the down stage that reads its
+ * quantised h must not have another call's gate/up stage between them. */
+int moe_expert_ffn_mx_noalloc(const moe_dims* d, const uint16_t* x, const void* pool,
+                              uint64_t pool_bytes, const moe_blob_layout* layout,
+                              const int32_t* offsets, const int32_t* perm,
+                              const int32_t* group_slot, uint16_t* h, uint16_t* y_rows,
+                              int32_t* dev_status, void* ws, uint64_t ws_bytes, int32_t stages,
+                              moe_stream_t stream);
+
 /* ---- S5: combine -------------------------------------------------------
  * [Strata] "路由以后，专家怎样分工？" (each expert output times its router weight,
  * summed, plus the gated shared-expert contribution) and "少算这些专家，会付出

@@ -38,7 +38,8 @@ EXPORTED = ("moe_status_string", "moe_last_error", "moe_version", "moe_blob_layo
             "moe_route", "moe_group", "moe_group_tail_skip", "moe_residency_update", "moe_residency_fill",
             "moe_heat_update", "moe_heat_decay", "moe_swap_plan", "moe_swap_apply",
             "moe_route_group", "moe_expert_ffn", "moe_expert_ffn_stages", "moe_blob_layout_init_mx",
-            "moe_mx_workspace_bytes", "moe_quantize_mxfp8", "moe_expert_ffn_mx", "moe_combine",
+            "moe_mx_workspace_bytes", "moe_quantize_mxfp8", "moe_expert_ffn_mx", "moe_expert_ffn_mx_noalloc",
+            "moe_combine",
             "moe_ring_create", "moe_stage_h2d", "moe_ring_acquire", "moe_ring_release", "moe_ring_slot_ptr",
             "moe_ring_destroy")
 
@@ -98,6 +99,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.moe_quantize_mxfp8.argtypes = [_vp, ctypes.c_int64, _i32, _vp, _vp, _vp]
     lib.moe_expert_ffn_mx.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _u64, _vp, _u64, _i32, _vp, _vp, _vp]
+    lib.moe_expert_ffn_mx_noalloc.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp,
+                                              _vp, _vp, _vp, _u64, _i32, _vp]
     lib.moe_combine.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.moe_ring_create.argtypes = [_vp, _vp, _u64, _vp, ctypes.POINTER(_vp)]
     lib.moe_stage_h2d.argtypes = [_vp, _vp, _u64, ctypes.POINTER(_i32)]
@@ -311,6 +314,15 @@ def moe_expert_ffn_mx(dims, x, pool, pool_bytes, layout: BlobLayout, offsets, pe
                                   _p(offsets), _p(perm), _p(group_slot), _p(h), _p(y_rows), _p(dev_status), _p(ws),
                                   ws_bytes, _p(mx_ws), mx_ws_bytes, stages, ev_start, ev_stop, _s(stream)),
            "moe_expert_ffn_mx")
+
+
+def moe_expert_ffn_mx_noalloc(dims, x, pool, pool_bytes, layout: BlobLayout, offsets, perm, group_slot, h, y_rows,
+                              dev_status, ws, stages: int = 3, ws_bytes: Optional[int] = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.moe_expert_ffn_mx_noalloc(ctypes.byref(dims), _p(x), _p(pool), pool_bytes, ctypes.byref(layout),
+                                          _p(offsets), _p(perm), _p(group_slot), _p(h), _p(y_rows), _p(dev_status),
+                                          _p(ws), ws_bytes, stages, _s(stream)), "moe_expert_ffn_mx_noalloc")
 
 
 def moe_combine(dims, y_rows, inv_perm, topk_w, shared_sigma, y, stream=None) -> None:

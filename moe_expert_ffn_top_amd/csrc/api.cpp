@@ -437,11 +437,18 @@ int moe_quantize_mxfp8(const uint16_t* x, int64_t rows, int32_t K, uint8_t* code
                     "MXFP8 quantisation launch");
 }
 
-int moe_expert_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
-                      const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm,
-                      const int32_t* group_slot, uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws,
-                      uint64_t ws_bytes, void* mx_ws, uint64_t mx_ws_bytes, int32_t stages, void* ev_start,
-                      void* ev_stop, moe_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_expert_ffn_mx; with mx_ws NULL (moe_expert_ffn_mx_noalloc) the MX
+// workspace is the library's static scratch, and a size beyond it is refused
+// before any HIP call.
+int expert_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
+                  const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm,
+                  const int32_t* group_slot, uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws,
+                  uint64_t ws_bytes, void* mx_ws, uint64_t mx_ws_bytes, int32_t stages, void* ev_start,
+                  void* ev_stop, moe_stream_t stream, bool static_scratch) {
   if (stages < 1 || stages > 3) return fail(MOE_ERR_ARG, "stages = %d: must be 1 (gate/up), 2 (down) or 3", stages);
   int r = check_dims(d);
   if (r) return r;
@@ -459,13 +466,18 @@ int moe_expert_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool, ui
   REQUIRE(y_rows, 16, "y_rows");
   REQUIRE(dev_status, 4, "dev_status");
   REQUIRE(ws, 16, "ws");
-  REQUIRE(mx_ws, 256, "mx_ws");
+  if (!static_scratch) REQUIRE(mx_ws, 256, "mx_ws");
   const uint64_t need = moe::ws_layout(*d).total;
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace %llu bytes < required %llu", (unsigned long long)ws_bytes,
                 (unsigned long long)need);
   const uint64_t need_mx = moe::mx_ws_layout(*d).total;
-  if (mx_ws_bytes < need_mx)
+  if (static_scratch && need_mx > moe::kNoAllocScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "these dims need %llu bytes of MX workspace, more than the %llu bytes of the library's static "
+                "scratch; use moe_expert_ffn_mx with a caller workspace",
+                (unsigned long long)need_mx, (unsigned long long)moe::kNoAllocScratchBytes);
+  if (!static_scratch && mx_ws_bytes < need_mx)
     return fail(MOE_ERR_WORKSPACE, "MX workspace %llu bytes < required %llu", (unsigned long long)mx_ws_bytes,
                 (unsigned long long)need_mx);
   if (pool_bytes < layout->slot_stride)
@@ -486,11 +498,36 @@ int moe_expert_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool, ui
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) !=
                                               hipSuccess || n_cu <= 0)
     return fail(MOE_ERR_HIP, "cannot query the device's compute-unit count");
+  if (static_scratch) {
+    const hipError_t e = moe::noalloc_scratch(&mx_ws);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "static scratch address: %s", hipGetErrorString(e));
+  }
   if (moe::use_gemm(*d))
     return hip_status(moe::launch_ffn_mx(*d, x, g, perm, h, y_rows, ws, mx_ws, n_cu, stages, e0, e1, st),
                       "MX expert FFN launch");
   return hip_status(moe::launch_ffn_dec_mx(*d, x, g, perm, h, y_rows, ws, mx_ws, n_cu, stages, e0, e1, st),
                     "MX expert FFN launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_expert_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
+                      const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm,
+                      const int32_t* group_slot, uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws,
+                      uint64_t ws_bytes, void* mx_ws, uint64_t mx_ws_bytes, int32_t stages, void* ev_start,
+                      void* ev_stop, moe_stream_t stream) {
+  return expert_ffn_mx(d, x, pool, pool_bytes, layout, offsets, perm, group_slot, h, y_rows, dev_status, ws,
+                       ws_bytes, mx_ws, mx_ws_bytes, stages, ev_start, ev_stop, stream, false);
+}
+
+int moe_expert_ffn_mx_noalloc(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
+                              const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm,
+                              const int32_t* group_slot, uint16_t* h, uint16_t* y_rows, int32_t* dev_status,
+                              void* ws, uint64_t ws_bytes, int32_t stages, moe_stream_t stream) {
+  return expert_ffn_mx(d, x, pool, pool_bytes, layout, offsets, perm, group_slot, h, y_rows, dev_status, ws,
+                       ws_bytes, nullptr, 0, stages, nullptr, nullptr, stream, true);
 }
 
 int moe_combine(const moe_dims* d, const uint16_t* y_rows, const int32_t* inv_perm, const float* topk_w,

@@ -219,6 +219,14 @@ inline MxWsLayout mx_ws_layout(const moe_dims& d) {
   return w;
 }
 
+// ---- library-owned scratch (moe_expert_ffn_mx_noalloc) ----------------------
+// Bytes of the static device array that stands in for the MX workspace; a
+// call whose mx_ws_layout(d).total exceeds it is refused.
+constexpr uint64_t kNoAllocScratchBytes = 32ull << 20;
+// The calling thread's current device's address of that array (looked up
+// once per device through hipGetSymbolAddress, then cached).
+hipError_t noalloc_scratch(void** out);
+
 // ---- launchers (return hipSuccess or the launch error) ---------------------
 struct FfnGeom {
   const uint8_t* pool;

@@ -214,3 +214,18 @@ def test_swap_plan_matches_oracle(B, seed):
     d = B.Dims(1, 64, 32, E, 1, L)
     got = [tuple(r) for r in B.moe_swap_plan(d, heat, table, thr, cap)]
     assert got == O.swap_plan(heat, table, thr, cap)
+
+
+def test_noalloc_refuses_dims_beyond_its_static_scratch(B):
+    """moe_expert_ffn_mx_noalloc refuses, before any HIP call, dims whose MX
+    workspace exceeds the library's 32 MiB static scratch."""
+    big = B.Dims(8192, 2048, 512, 512, 10, 1)
+    assert B.moe_mx_workspace_bytes(big) > 32 << 20
+    assert B.moe_mx_workspace_bytes(B.Dims(4096, 2048, 512, 512, 10, 1)) <= 32 << 20
+    lay = B.moe_blob_layout_init_mx(2048, 512)
+    ws_bytes = B.moe_workspace_bytes(big)
+    p = 1 << 20   # aligned stand-in addresses: validation fails before any of them is used
+    rc = B.raw_status("moe_expert_ffn_mx_noalloc", ctypes.byref(big), p, p, lay.slot_stride * 8, ctypes.byref(lay),
+                      p, p, p, p, p, p, p, ws_bytes, 3, None)
+    assert rc == B.MOE_ERR_WORKSPACE
+    assert b"static" in B._lib.moe_last_error()
