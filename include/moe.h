@@ -71,6 +71,8 @@ typedef struct ihipStream_t* moe_stream_t;
 #define MOE_DEV_BAD_SLOT 4        /* a slot index >= n_slots: rows are zero */
 #define MOE_DEV_TAIL_SKIPPED 8    /* moe_group_tail_skip skipped a group (rows zero) */
 #define MOE_DEV_CACHE_FULL 16     /* moe_residency_update had more misses than slots to evict */
+#define MOE_DEV_SYNC_TIMEOUT 32   /* a one-launch FFN's wait for another workgroup's rows timed out:
+                                     that call's h / y_rows / y are undefined */
 
 const char* moe_status_string(int status);
 /* Detail of the last error returned on the calling thread ("" if none). */
@@ -342,6 +344,13 @@ int moe_route_group(const moe_dims* d, int32_t layer, const uint16_t* x,
  * Rows of a group whose slot is -1 or >= pool_bytes/slot_stride are written
  * as zeros and flagged in dev_status.
  * offsets/perm/group_slot/ws: exactly as written by moe_group on the same stream.
+ * For decode-sized groups ([FreeToken] 3.5: a step's control flow stays on
+ * the device) both stages may run as one launch: the down projection of a
+ * tile waits, inside the launch, for the workgroups that write its h rows.
+ * The wait is bounded; should it time out (only if the device cannot keep
+ * the launch's workgroups resident together, e.g. other work holds its
+ * compute units for a long time), MOE_DEV_SYNC_TIMEOUT is set and h, y_rows
+ * are undefined.  The results are the same bits either way.
  */
 int moe_expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool,
                    uint64_t pool_bytes, const moe_blob_layout* layout,
@@ -369,6 +378,24 @@ int moe_expert_ffn_stages(const moe_dims* d, const uint16_t* x, const void* pool
                           int32_t* dev_status, void* ws, uint64_t ws_bytes,
                           int32_t stages, void* ev_start, void* ev_stop,
                           moe_stream_t stream);
+
+/* ---- S4 + S5 together ----------------------------------------------------
+ * moe_expert_ffn followed by moe_combine on the same stream, with exactly
+ * their arguments, validation and results (h, y_rows and y bit-identical).
+ * For decode windows (T <= 64 on the weight-streaming path, shapes with a
+ * one-launch instantiation) the combine runs inside the FFN's launch: the
+ * wavefront that completes the last down item of a block of output columns
+ * combines that block for every token ([Strata] "路由以后，专家怎样分工？": each
+ * token's expert outputs are weighted and summed once all have arrived).
+ * ev_start, ev_stop as for moe_expert_ffn_stages (they bracket the FFN
+ * launch, and the combine when it is part of it). */
+int moe_expert_ffn_combine(const moe_dims* d, const uint16_t* x, const void* pool,
+                           uint64_t pool_bytes, const moe_blob_layout* layout,
+                           const int32_t* offsets, const int32_t* perm,
+                           const int32_t* group_slot, const int32_t* inv_perm,
+                           const float* topk_w, const float* shared_sigma, uint16_t* h,
+                           uint16_t* y_rows, uint16_t* y, int32_t* dev_status, void* ws,
+                           uint64_t ws_bytes, void* ev_start, void* ev_stop, moe_stream_t stream);
 
 /* ---- S4, MX variant: MXFP4 experts on the scaled MFMA ---------------------
  * [FreeToken] notes that the DeepSeek-V4-Flash experts are natively MXFP4; the

@@ -32,12 +32,14 @@ MOE_DEV_NOT_RESIDENT = 2
 MOE_DEV_BAD_SLOT = 4
 MOE_DEV_TAIL_SKIPPED = 8
 MOE_DEV_CACHE_FULL = 16
+MOE_DEV_SYNC_TIMEOUT = 32
 
 #: every symbol include/moe.h declares
 EXPORTED = ("moe_status_string", "moe_last_error", "moe_version", "moe_blob_layout_init", "moe_workspace_bytes",
             "moe_route", "moe_group", "moe_group_tail_skip", "moe_residency_update", "moe_residency_fill",
             "moe_heat_update", "moe_heat_decay", "moe_swap_plan", "moe_swap_apply",
-            "moe_route_group", "moe_expert_ffn", "moe_expert_ffn_stages", "moe_blob_layout_init_mx",
+            "moe_route_group", "moe_expert_ffn", "moe_expert_ffn_stages", "moe_expert_ffn_combine",
+            "moe_blob_layout_init_mx",
             "moe_mx_workspace_bytes", "moe_quantize_mxfp8", "moe_expert_ffn_mx", "moe_expert_ffn_mx_noalloc",
             "moe_combine",
             "moe_ring_create", "moe_stage_h2d", "moe_ring_acquire", "moe_ring_release", "moe_ring_slot_ptr",
@@ -94,6 +96,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
                                    _vp, _u64, _vp]
     lib.moe_expert_ffn_stages.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _vp,
                                           _vp, _vp, _u64, _i32, _vp, _vp, _vp]
+    lib.moe_expert_ffn_combine.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _vp,
+                                           _vp, _vp, _vp, _vp, _vp, _vp, _u64, _vp, _vp, _vp]
     lib.moe_blob_layout_init_mx.argtypes = [_i32, _i32, ctypes.POINTER(BlobLayout)]
     lib.moe_mx_workspace_bytes.argtypes = [_DP, ctypes.POINTER(_u64)]
     lib.moe_quantize_mxfp8.argtypes = [_vp, ctypes.c_int64, _i32, _vp, _vp, _vp]
@@ -259,6 +263,17 @@ def moe_expert_ffn_stages(dims, x, pool, pool_bytes, layout: BlobLayout, offsets
                                       _p(offsets), _p(perm), _p(group_slot), _p(h), _p(y_rows), _p(dev_status),
                                       _p(ws), ws_bytes, stages, ev_start, ev_stop, _s(stream)),
            "moe_expert_ffn_stages")
+
+
+def moe_expert_ffn_combine(dims, x, pool, pool_bytes, layout: BlobLayout, offsets, perm, group_slot, inv_perm,
+                           topk_w, shared_sigma, h, y_rows, y, dev_status, ws, ev_start: Optional[int] = None,
+                           ev_stop: Optional[int] = None, ws_bytes: Optional[int] = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.moe_expert_ffn_combine(ctypes.byref(dims), _p(x), _p(pool), pool_bytes, ctypes.byref(layout),
+                                       _p(offsets), _p(perm), _p(group_slot), _p(inv_perm), _p(topk_w),
+                                       _p(shared_sigma), _p(h), _p(y_rows), _p(y), _p(dev_status), _p(ws), ws_bytes,
+                                       ev_start, ev_stop, _s(stream)), "moe_expert_ffn_combine")
 
 
 def moe_blob_layout_init_mx(H: int, I: int) -> BlobLayout:

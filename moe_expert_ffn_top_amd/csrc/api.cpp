@@ -343,10 +343,19 @@ int moe_expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool, uint6
                                ws_bytes, 3, nullptr, nullptr, stream);
 }
 
-int moe_expert_ffn_stages(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
-                          const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm,
-                          const int32_t* group_slot, uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws,
-                          uint64_t ws_bytes, int32_t stages, void* ev_start, void* ev_stop, moe_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// S4 (stages: 1 gate/up, 2 down, 3 both) and, with inv_perm set, S5 after it.
+// Both stages together on the weight-streaming path run as one launch when
+// the shapes have a fused instantiation (and so does the combine for small
+// windows); otherwise one launch per stage, then the combine's own.
+int expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
+               const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm, const int32_t* group_slot,
+               uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws, uint64_t ws_bytes, int32_t stages,
+               void* ev_start, void* ev_stop, moe_stream_t stream, const int32_t* inv_perm, const float* topk_w,
+               const float* shared_sigma, uint16_t* y) {
   if (stages < 1 || stages > 3) return fail(MOE_ERR_ARG, "stages = %d: must be 1 (gate/up), 2 (down) or 3", stages);
   int r = check_dims(d);
   if (r) return r;
@@ -364,6 +373,13 @@ int moe_expert_ffn_stages(const moe_dims* d, const uint16_t* x, const void* pool
   REQUIRE(y_rows, 16, "y_rows");
   REQUIRE(dev_status, 4, "dev_status");
   REQUIRE(ws, 16, "ws");
+  const bool comb = y != nullptr;
+  if (comb) {
+    REQUIRE(inv_perm, 4, "inv_perm");
+    REQUIRE(topk_w, 4, "topk_w");
+    REQUIRE(shared_sigma, 4, "shared_sigma");
+    REQUIRE(y, 16, "y");
+  }
   const uint64_t need = moe::ws_layout(*d).total;
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace %llu bytes < required %llu", (unsigned long long)ws_bytes,
@@ -389,10 +405,50 @@ int moe_expert_ffn_stages(const moe_dims* d, const uint16_t* x, const void* pool
   // groups averaging >= kGemmMinRows rows: grouped GEMM over 256-row chunks;
   // otherwise weight streaming over 16-row tiles (the grouping kernels wrote
   // the matching work list)
+  if (stages == 3 && !moe::use_gemm(*d)) {
+    if (comb && moe::ffn_dec_fusable(*d, true))
+      return hip_status(moe::launch_ffn_dec_fused(*d, x, g, h, y_rows, dev_status, ws, n_cu, e0, e1, st, inv_perm,
+                                                  topk_w, shared_sigma, y),
+                        "expert FFN + combine launch");
+    if (moe::ffn_dec_fusable(*d, false)) {
+      if ((r = hip_status(moe::launch_ffn_dec_fused(*d, x, g, h, y_rows, dev_status, ws, n_cu, e0, e1, st, nullptr,
+                                                    nullptr, nullptr, nullptr),
+                          "expert FFN launch")))
+        return r;
+      return comb ? hip_status(moe::launch_combine(*d, y_rows, inv_perm, topk_w, shared_sigma, y, st),
+                               "combine launch")
+                  : ok();
+    }
+  }
   if (moe::use_gemm(*d))
-    return hip_status(moe::launch_ffn_gemm(*d, x, g, perm, h, y_rows, ws, n_cu, stages, e0, e1, st), "expert FFN launch");
-  return hip_status(moe::launch_ffn_dec(*d, x, g, perm, h, y_rows, ws, n_cu, stages, e0, e1, st),
-                    "expert FFN launch");
+    r = hip_status(moe::launch_ffn_gemm(*d, x, g, perm, h, y_rows, ws, n_cu, stages, e0, e1, st), "expert FFN launch");
+  else
+    r = hip_status(moe::launch_ffn_dec(*d, x, g, perm, h, y_rows, ws, n_cu, stages, e0, e1, st), "expert FFN launch");
+  if (r || !comb) return r;
+  return hip_status(moe::launch_combine(*d, y_rows, inv_perm, topk_w, shared_sigma, y, st), "combine launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_expert_ffn_stages(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
+                          const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm,
+                          const int32_t* group_slot, uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws,
+                          uint64_t ws_bytes, int32_t stages, void* ev_start, void* ev_stop, moe_stream_t stream) {
+  return expert_ffn(d, x, pool, pool_bytes, layout, offsets, perm, group_slot, h, y_rows, dev_status, ws, ws_bytes,
+                    stages, ev_start, ev_stop, stream, nullptr, nullptr, nullptr, nullptr);
+}
+
+int moe_expert_ffn_combine(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
+                           const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm,
+                           const int32_t* group_slot, const int32_t* inv_perm, const float* topk_w,
+                           const float* shared_sigma, uint16_t* h, uint16_t* y_rows, uint16_t* y,
+                           int32_t* dev_status, void* ws, uint64_t ws_bytes, void* ev_start, void* ev_stop,
+                           moe_stream_t stream) {
+  if (!y) return fail(MOE_ERR_ARG, "y is NULL");
+  return expert_ffn(d, x, pool, pool_bytes, layout, offsets, perm, group_slot, h, y_rows, dev_status, ws, ws_bytes, 3,
+                    ev_start, ev_stop, stream, inv_perm, topk_w, shared_sigma, y);
 }
 
 int moe_blob_layout_init_mx(int32_t H, int32_t I, moe_blob_layout* out) {

@@ -34,8 +34,28 @@
 //    in one dword per row, and no global scales.  The A rows are then the
 //    bf16 values of MXFP8(x) and MXFP8(h) (exact in bf16), so the products
 //    stay exact and the sums fp32, as on the NVFP4 path.
+//
+// Both stages in one launch (k_ffn_dec_fused; [FreeToken] 3.5: one step's
+// control flow stays on the device).  The down projection of a tile needs the
+// whole of its h rows, which the tile's gate/up items (other workgroups,
+// possibly on other XCDs) write.  Each workgroup first issues the weight
+// loads of its first down unit, which do not depend on h, then walks its
+// gate/up items; at the end of that walk every wavefront that stored h rows
+// waits for its stores to complete and adds one to each of its items' tile
+// counters.  A down unit waits (bounded; one polling wavefront per
+// workgroup) until its tile's counter is full, then reads h.  Each counter
+// has a 256-byte line of its own.  Stores and loads of h go
+// through the device-coherent path (sc1: written through to memory, read
+// past the XCD-private caches), so no cache-wide write-back or invalidation
+// is needed.  Optionally the same launch also combines (S5): the wavefront
+// that completes the last down item of a column block marks it, and its
+// workgroup combines that block for every token of the window once its own
+// down items are done.
 #include <hip/hip_ext.h>
 #include <math.h>
+
+#include <atomic>
+#include <mutex>
 
 #include "moe_common.hpp"
 
@@ -45,6 +65,10 @@
 #endif
 #ifndef MOE_DEC_WGS_DN
 #define MOE_DEC_WGS_DN 2
+#endif
+// and for the fused launch
+#ifndef MOE_DEC_WGS_FUSED
+#define MOE_DEC_WGS_FUSED 2
 #endif
 // unit blocks per wavefront and steps per K round, per stage
 #ifndef MOE_DEC_U_GU
@@ -59,26 +83,18 @@
 #ifndef MOE_DEC_MAXS_DN
 #define MOE_DEC_MAXS_DN 4
 #endif
+// polls of a tile counter before a fused launch gives up on it (each poll is
+// a device-coherent load plus a short sleep: about 0.1-0.2 s in all)
+#ifndef MOE_DEC_SPIN_LIMIT
+#define MOE_DEC_SPIN_LIMIT (1 << 18)
+#endif
 
 namespace moe {
 namespace {
 
-#ifdef MOE_DEC_TIMING
-// Tuning builds only: per-wavefront wall-clock stamps (start, first unit's
-// descriptor ready, first weights arrived, end of units 1..4, end).
-__device__ unsigned long long g_dec_times[1 << 17][8];
-#define DEC_STAMP(i)                                                                              \
-  do {                                                                                            \
-    if ((threadIdx.x & 63) == 0) {                                                                \
-      const unsigned w = (((blockIdx.x * 4u + (threadIdx.x >> 6)) & ((1u << 16) - 1)) | (GATEUP ? 0u : (1u << 16))); \
-      g_dec_times[w][i] = wall_clock64();                                                         \
-    }                                                                                             \
-  } while (0)
-#else
-#define DEC_STAMP(i) \
-  do {               \
-  } while (0)
-#endif
+// cache policy of buffer loads and stores: sc1 = coherent at device scope
+constexpr int kAuxPlain = 0;
+constexpr int kAuxDevice = 16;
 
 // Data that no kernel of this launch writes (tile descriptors, token tables,
 // the weight pool) is read through the constant address space: a load from it
@@ -126,6 +142,7 @@ struct Item {
   uint32_t aoff;                 // this lane's row start in arsrc (bytes; past the end for padding rows)
   float g0, g1;                  // fp32 global scales (gate, up) or (down, -)
   int p0, n, unit;               // first row, rows, this lane's unit in its first unit block
+  int tile, ug;                  // tile and unit-block group of the item
   bool live;                     // the item exists
   bool resident;                 // it exists and its slot is inside the pool
 };
@@ -172,6 +189,8 @@ __device__ inline Item<(GATEUP ? 2 : 1) * U> make_item(const DecArgs& a, const D
   it.p0 = p0;
   it.n = it.live ? tn : 0;
   it.unit = (ug * ubw + wub) * 16 + c;
+  it.tile = tile_u;
+  it.ug = ug;
   if (GATEUP) {
     it.arsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(ain), (short)0, a.a_bytes, 0x00020000);
     it.aoff = c < it.n ? (uint32_t)d.tok * (uint32_t)a.H * 2u : 0x80000000u;
@@ -226,12 +245,13 @@ __device__ inline void load_sc(uint2* sc, const Item<NS>& it, int grp) {
   for (int m = 0; m < NS; m++) sc[m] = *reinterpret_cast<const uint2*>(it.scales[m] + (int64_t)grp * 512);
 }
 
-template <int NS>
+// AUX: the cache policy (sc1 for A rows that other workgroups of the launch wrote)
+template <int NS, int AUX>
 __device__ inline void load_a(uint4* xa, const Item<NS>& it, int ch) {
   using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(it.arsrc, it.aoff + (uint32_t)ch * 64u + 16u * i, 0, 0);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(it.arsrc, it.aoff + (uint32_t)ch * 64u + 16u * i, 0, AUX);
     xa[i] = uint4{v.x, v.y, v.z, v.w};
   }
 }
@@ -259,60 +279,241 @@ __device__ inline void mma_step(const Step<NS>& s, const uint4* xa, const uint32
   }
 }
 
-// S: 128-value steps per wavefront and K round; U unit blocks per wavefront;
-// SPLITK wavefronts per unit block (4 / SPLITK unit-block groups per item);
-// FS: every K round of every wavefront is one whole 512-value group (S = 4).
-template <bool GATEUP, int SPLITK, int S, int U, bool FS, bool MX>
-__global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restrict__ tiles,
-                                                 const int32_t* __restrict__ tile_tok,
-                                                 const int32_t* __restrict__ n_tiles,
-                                                 const uint8_t* __restrict__ pool, const uint16_t* __restrict__ ain,
-                                                 uint16_t* __restrict__ out) {
-  constexpr int NMAT = GATEUP ? 2 : 1, NS = NMAT * U;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wub = (wave / SPLITK) * U, kpart = wave % SPLITK;  // first unit block of this wave in the item
-  const int c = lane & 15, q = lane >> 4;
-  const int K = GATEUP ? a.H : a.I;
-  const int units = GATEUP ? a.I : a.H;
-  const int n_items = *as_const(n_tiles) * a.n_ug;
-  const int nkr = a.n_kr;
-  const int nc = K / 32;
-  const int wc = (nc + SPLITK - 1) / SPLITK;
-  const int c0 = min(kpart * wc, nc - 1), c1 = min(nc, kpart * wc + wc);  // this wave's chunks [c0, c1)
-  const bool kempty = kpart * wc >= nc;
+// ---- synchronisation of the fused launch ------------------------------------
+// The counters live in the workspace (ws_layout: sync), kSyncStride words
+// apart, zeroed by every grouping kernel and by the last workgroup of every
+// fused launch.  Counter i is the word sync[i * kSyncStride]:
+//   0                    workgroups of the launch that have finished
+//   1 + t                wavefront stores of tile t's h rows done
+//   1 + max_tiles + b    wavefront stores of column block b's Y rows done
+struct FusedCtx {
+  int32_t* sync;
+  int32_t* status;
+  int32_t max_tiles;
+  int32_t gu_target;  // h-row publications that complete a tile
+  int32_t dn_target;  // Y-row publications that complete a column block (x n_tiles)
+  int32_t spin_limit;
+  // combine (S5) arguments; inv_perm null: no combine in this launch
+  const int32_t* inv_perm;
+  const float* w;
+  const float* sigma;
+  uint16_t* y;
+  int32_t T, k, H, cols;  // cols: output columns per down item
+};
 
-  __shared__ f32x4 red[SPLITK > 1 ? 4 : 1][NS][64];
+__device__ inline int32_t* counter(const FusedCtx& fc, int i) { return fc.sync + (int64_t)i * kSyncStride; }
+
+// The calling wavefront's h or Y stores have completed (written through to
+// the device-coherent level); then one lane counts them.
+__device__ inline int publish(int32_t* ctr) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  int old = 0;
+  if ((threadIdx.x & 63) == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_amdgcn_readfirstlane(old);
+}
+
+// Wait (bounded) until *ctr >= target: wavefront 0 polls, the workgroup
+// meets it at a barrier (every wavefront of the workgroup calls this).  On
+// time-out MOE_DEV_SYNC_TIMEOUT is set and the workgroup goes on: its results
+// are then undefined, but every wave still ends.
+__device__ inline void wait_count(const int32_t* ctr, int target, const FusedCtx& fc) {
+  if ((threadIdx.x >> 6) == 0) {
+    int spins = 0;
+    while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) <
+           target) {
+      if (++spins > fc.spin_limit) {
+        if ((threadIdx.x & 63) == 0) atomicOr(fc.status, MOE_DEV_SYNC_TIMEOUT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(4);
+    }
+  }
+  __syncthreads();
+  asm volatile("" ::: "memory");
+}
+
+// bf16 store of element idx of rows (a wavefront-uniform base holding
+// `bytes` bytes) with a cache policy
+template <int AUX>
+__device__ inline void store_bf16(uint16_t* rows, int bytes, int idx, uint16_t v) {
+  if (AUX == kAuxPlain) {
+    rows[idx] = v;
+  } else {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(rows, (short)0, bytes, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, 2 * idx, 0, AUX);
+  }
+}
+
+// S5 for the column blocks marked in mask (bit b: columns [b cols, b cols +
+// cols)), for every token, by the whole workgroup, in exactly k_combine's
+// arithmetic: y = bf16(sum_j w_j Y[inv(t, j)] + sigma Y_sh), fp32 fused
+// multiply-adds in slot order, then the shared row.  inv_perm, w and sigma
+// (written before the launch) are staged in LDS once; the Y rows (written by
+// other workgroups of this launch) are read with device-coherent loads, all
+// of a column pair's at once.  Requires T k <= kFusedCombineMaxT *
+// kFusedCombineMaxK.
+__device__ inline void combine_blocks(const uint16_t* __restrict__ yr, const FusedCtx& fc, const uint32_t* mask,
+                                      int2* pw, float* sg) {
+  const int nb = fc.H / fc.cols, nw = (nb + 31) / 32;
+  bool any = false;
+  for (int i = 0; i < nw; i++) any |= mask[i] != 0;
+  if (!any) return;
+  const int Tk = fc.T * fc.k;
+  for (int i = threadIdx.x; i < Tk; i += blockDim.x)
+    pw[i] = make_int2(fc.inv_perm[i], __float_as_int(fc.w[i]));
+  for (int i = threadIdx.x; i < fc.T; i += blockDim.x) sg[i] = fc.sigma[i];
+  __syncthreads();
+  const int pairs = fc.cols / 2;
+  for (int wi = 0; wi < nw; wi++) {
+    uint32_t m = mask[wi];
+    while (m) {
+      const int b = 32 * wi + __builtin_ctz(m);
+      m &= m - 1;
+      for (int o = threadIdx.x; o < fc.T * pairs; o += blockDim.x) {
+        const int t = o / pairs, col = b * fc.cols + 2 * (o - t * pairs);
+        int p[kFusedCombineMaxK];
+        float wj[kFusedCombineMaxK];
+        uint32_t v[kFusedCombineMaxK];
+#pragma unroll
+        for (int j = 0; j < kFusedCombineMaxK; j++) {
+          const int2 e = pw[t * fc.k + min(j, fc.k - 1)];
+          p[j] = j < fc.k ? e.x : -1;
+          wj[j] = __int_as_float(e.y);
+        }
+#pragma unroll
+        for (int j = 0; j < kFusedCombineMaxK; j++)
+          v[j] = __hip_atomic_load(reinterpret_cast<const uint32_t*>(yr + (int64_t)max(p[j], 0) * fc.H + col),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t vs =
+            __hip_atomic_load(reinterpret_cast<const uint32_t*>(yr + ((int64_t)Tk + t) * fc.H + col),
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < kFusedCombineMaxK; j++) {
+          if (p[j] < 0) continue;
+          a0 = fmaf(wj[j], bf16_bits_to_f32(v[j] & 0xFFFFu), a0);
+          a1 = fmaf(wj[j], bf16_bits_to_f32(v[j] >> 16), a1);
+        }
+        const float st = sg[t];
+        const float b0 = fmaf(st, bf16_bits_to_f32(vs & 0xFFFFu), a0);
+        const float b1 = fmaf(st, bf16_bits_to_f32(vs >> 16), a1);
+        *reinterpret_cast<uint32_t*>(fc.y + (int64_t)t * fc.H + col) =
+            (uint32_t)f32_to_bf16_rne(b0) | ((uint32_t)f32_to_bf16_rne(b1) << 16);
+      }
+    }
+  }
+}
+
+// ---- one stage's walk over its work units -----------------------------------
+// Geometry of the calling wavefront in a stage.
+template <bool GATEUP, int SPLITK, int S, int U>
+struct Geo {
+  int wave, lane, wub, kpart, c, q, K, units, nc, wc, c0, c1;
+  bool kempty;
+  __device__ inline Geo(const DecArgs& a) {
+    wave = threadIdx.x >> 6;
+    lane = threadIdx.x & 63;
+    wub = (wave / SPLITK) * U;  // first unit block of this wave in the item
+    kpart = wave % SPLITK;
+    c = lane & 15;
+    q = lane >> 4;
+    K = GATEUP ? a.H : a.I;
+    units = GATEUP ? a.I : a.H;
+    nc = K / 32;
+    wc = (nc + SPLITK - 1) / SPLITK;
+    c0 = min(kpart * wc, nc - 1);  // this wave's chunks [c0, c1)
+    c1 = min(nc, kpart * wc + wc);
+    kempty = kpart * wc >= nc;
+  }
   // chunk of step s in K round r for this lane, and (FS) the round's group
-#define DEC_CH(r, s) (c0 + (r) * (4 * S) + S * q + (s))
-#define DEC_GRP(r) ((c0 + (r) * (4 * S)) >> 4)
+  __device__ inline int ch(int r, int s) const { return c0 + r * (4 * S) + S * q + s; }
+  __device__ inline int grp(int r) const { return (c0 + r * (4 * S)) >> 4; }
+};
 
-  DEC_STAMP(0);
-  // work units u = 0, 1, ...: item blockIdx.x + (u / nkr) * gridDim.x, K round u % nkr
-  const int G = gridDim.x;
-  int item = blockIdx.x, kr = 0;
-  Item<NS> cur =
-      make_item<GATEUP, U, FS, MX>(a, load_desc<GATEUP>(a, item, c, tiles, tile_tok), n_items, wub, c, pool, ain);
+// The first unit of a stage, with its weight loads issued: a caller can issue
+// them long before the stage runs (the fused launch issues its first down
+// unit's before its gate/up items).
+// Loads are counted in issue order (vmcnt), so a caller that starts two
+// stages issues both first descriptors before either start: a start then
+// waits only on loads issued before its own.
+template <bool GATEUP, int SPLITK, int S, int U, bool FS, bool MX>
+struct Start {
+  static constexpr int NS = (GATEUP ? 2 : 1) * U;
+  Item<NS> cur;
+  Step<NS> fb[S];
+  uint2 scn[NS];
+  uint4 xa[S][4];  // A rows of the first unit (when they are loaded at the start)
+  Desc dn;         // descriptor of the second unit
+};
+
+// The first unit (descriptor d0): its weights, its A rows when LOAD_A, then
+// the second unit's descriptor.  stride: item step of the walk.
+template <bool GATEUP, int SPLITK, int S, int U, bool FS, bool MX, bool LOAD_A>
+__device__ inline void stage_start(Start<GATEUP, SPLITK, S, U, FS, MX>& st, const DecArgs& a, const Desc& d0,
+                                   int n_items, int stride, const int4* __restrict__ tiles,
+                                   const int32_t* __restrict__ tile_tok, const uint8_t* __restrict__ pool,
+                                   const uint16_t* __restrict__ ain) {
+  constexpr int NS = (GATEUP ? 2 : 1) * U;
+  const Geo<GATEUP, SPLITK, S, U> g(a);
+  st.cur = make_item<GATEUP, U, FS, MX>(a, d0, n_items, g.wub, g.c, pool, ain);
+  if (FS) load_sc<NS>(st.scn, st.cur, g.grp(0));
+#pragma unroll
+  for (int s = 0; s < S; s++) load_step<NS, FS, MX>(st.fb[s], st.cur, min(g.ch(0, s), g.c1 - 1), g.nc, g.c);
+  if (LOAD_A) {
+#pragma unroll
+    for (int s = 0; s < S; s++) load_a<NS, kAuxPlain>(st.xa[s], st.cur, min(g.ch(0, s), g.c1 - 1));
+  }
+  st.dn = load_desc<GATEUP>(a, a.n_kr > 1 ? d0.item : d0.item + stride, g.c, tiles, tile_tok);
+}
+
+// Policy of a stage's walk:
+//   AAUX    cache policy of the A-row loads
+//   OAUX    cache policy of the output stores
+//   WAIT    before a unit's A rows are read, wait for its tile's h (fused down)
+//   PUB     (down) after an item's stores, publish them to the column
+//           block's counter; the wavefront that completes a column block
+//           marks it in comb_mask (LDS) for its workgroup to combine
+template <int AAUX, int OAUX, bool WAIT, bool PUB>
+struct Policy {
+  static constexpr int kAAux = AAUX, kOAux = OAUX;
+  static constexpr bool kWait = WAIT, kPub = PUB;
+};
+using PlainStage = Policy<kAuxPlain, kAuxPlain, false, false>;
+
+// Walks work units u = 0, 1, ...: item first_item + (u / nkr) * stride, K round
+// u % nkr, starting from st (its weight loads already issued).
+template <bool GATEUP, int SPLITK, int S, int U, bool FS, bool MX, class P>
+__device__ inline void stage_walk(Start<GATEUP, SPLITK, S, U, FS, MX>& st, const DecArgs& a, int stride,
+                                  int n_items, const int4* __restrict__ tiles, const int32_t* __restrict__ tile_tok,
+                                  const uint8_t* __restrict__ pool, const uint16_t* __restrict__ ain,
+                                  uint16_t* __restrict__ out, const FusedCtx* fc, f32x4 (*red)[(GATEUP ? 2 : 1) * U][64],
+                                  uint32_t* comb_mask = nullptr) {
+  constexpr int NMAT = GATEUP ? 2 : 1, NS = NMAT * U;
+  const Geo<GATEUP, SPLITK, S, U> g(a);
+  const int c = g.c, q = g.q, nc = g.nc, c1 = g.c1;
+  const int nkr = a.n_kr;
+  Item<NS> cur = st.cur;
   if (!cur.live) return;
-  // descriptor of unit 1
-  Desc dn = load_desc<GATEUP>(a, nkr > 1 ? item : item + G, c, tiles, tile_tok);
-  int kr2 = nkr > 2 ? 2 : (nkr == 2 ? 0 : 0);   // K round of unit 2
-  int item2 = nkr > 2 ? item : (nkr == 2 ? item + G : item + 2 * G);
-  DEC_STAMP(1);
-#ifdef MOE_DEC_TIMING
-  int n_done = 0;
-#endif
+  int item = cur.tile * a.n_ug + cur.ug, kr = 0;
+  Desc dn = st.dn;  // descriptor of unit 1
+  int kr2 = nkr > 2 ? 2 : 0;  // K round of unit 2
+  int item2 = nkr > 2 ? item : (nkr == 2 ? item + stride : item + 2 * stride);
   // A fragments of every step of the current unit stay in registers.  Once
   // step s is computed, its registers (weights and A) are refilled with the
   // next unit's step s, so both stream one unit ahead and every wait is on
-  // loads issued a whole unit earlier.
-  uint4 xa[S][4];
+  // loads issued a whole unit earlier.  With WAIT the A rows of a unit are
+  // requested only once its tile is complete: the first unit's here, every
+  // next unit's at the end of the unit before it.
+  uint4 (*xa)[4] = st.xa;
+  if (P::kWait) {
+    wait_count(counter(*fc, 1 + cur.tile), fc->gu_target, *fc);
 #pragma unroll
-  for (int s = 0; s < S; s++) load_a(xa[s], cur, min(DEC_CH(0, s), c1 - 1));
-  Step<NS> fb[S];
+    for (int s = 0; s < S; s++) load_a<NS, P::kAAux>(xa[s], cur, min(g.ch(0, s), c1 - 1));
+  }
+  Step<NS>* fb = st.fb;
   uint2 scn[NS];  // FS: the scales of the next unit to compute
-  if (FS) load_sc<NS>(scn, cur, DEC_GRP(0));
 #pragma unroll
-  for (int s = 0; s < S; s++) load_step<NS, FS, MX>(fb[s], cur, min(DEC_CH(0, s), c1 - 1), nc, c);
+  for (int m = 0; m < NS; m++) scn[m] = st.scn[m];
   f32x4 acc[NS];
 
   while (cur.live) {
@@ -321,11 +522,11 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
     // the next unit (derived from the descriptor fetched a unit ago; the same
     // item again when it is a further K round), then the descriptor of the
     // unit after it
-    const Item<NS> nxt = make_item<GATEUP, U, FS, MX>(a, dn, n_items, wub, c, pool, ain);
+    const Item<NS> nxt = make_item<GATEUP, U, FS, MX>(a, dn, n_items, g.wub, c, pool, ain);
     __builtin_amdgcn_sched_barrier(0);
     dn = load_desc<GATEUP>(a, item2, c, tiles, tile_tok);
     kr2 = kr2 + 1 == nkr ? 0 : kr2 + 1;
-    item2 = kr2 == 0 ? item2 + G : item2;
+    item2 = kr2 == 0 ? item2 + stride : item2;
     __builtin_amdgcn_sched_barrier(0);
     if (kr == 0) {
 #pragma unroll
@@ -337,7 +538,7 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
     for (int m = 0; m < NS; m++) scc[m] = scn[m];
 #pragma unroll
     for (int s = 0; s < S; s++) {
-      const int chr = DEC_CH(kr, s);
+      const int chr = g.ch(kr, s);
       const int chc = min(chr, c1 - 1);
       uint32_t sw[NS];
 #pragma unroll
@@ -345,39 +546,35 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
         sw[m] = MX   ? (fb[s].sc[m] >> (8 * (chc & 3)))
                 : FS ? ((s < 2 ? scc[m].x : scc[m].y) >> (16 * (s & 1)))
                      : (fb[s].sc[m] >> (16 * ((blob_sc_off(chc, nc, c) >> 1) & 1)));
-      mma_step<NS, MX>(fb[s], xa[s], sw, !kempty && chr < c1 && cur.resident, acc);
-#ifdef MOE_DEC_TIMING
-      if (s == 0 && n_done == 0) {
-        __builtin_amdgcn_sched_barrier(0);
-        DEC_STAMP(2);
-      }
-#endif
+      mma_step<NS, MX>(fb[s], xa[s], sw, !g.kempty && chr < c1 && cur.resident, acc);
       // this step's registers now carry the next unit's step s
-      const int chn = min(DEC_CH(nkr_next, s), c1 - 1);
+      const int chn = min(g.ch(nkr_next, s), c1 - 1);
       load_step<NS, FS, MX>(fb[s], nxt, chn, nc, c);
-      if (FS && s == 0) load_sc<NS>(scn, nxt, DEC_GRP(nkr_next));
-      load_a(xa[s], nxt, chn);
+      if (FS && s == 0) load_sc<NS>(scn, nxt, g.grp(nkr_next));
+      if (!P::kWait) load_a<NS, P::kAAux>(xa[s], nxt, chn);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (last_round) {
       // split-K partials meet in LDS; kpart 0 finishes the unit blocks
       if (SPLITK > 1) {
 #pragma unroll
-        for (int m = 0; m < NS; m++) red[wave][m][lane] = acc[m];
+        for (int m = 0; m < NS; m++) red[g.wave][m][g.lane] = acc[m];
         __syncthreads();
-        if (kpart == 0) {
+        if (g.kpart == 0) {
 #pragma unroll
           for (int m = 0; m < NS; m++) {
-            f32x4 sum = red[wave][m][lane];
+            f32x4 sum = red[g.wave][m][g.lane];
 #pragma unroll
-            for (int w = 1; w < SPLITK; w++) sum += red[wave + w][m][lane];
+            for (int w = 1; w < SPLITK; w++) sum += red[g.wave + w][m][g.lane];
             acc[m] = sum;
           }
         }
         __syncthreads();
       }
-      if (kpart == 0) {
+      if (g.kpart == 0) {
         const float g0 = cur.g0, g1 = cur.g1;
+        uint16_t* orows = out + (int64_t)cur.p0 * g.units;  // the tile's rows
+        const int obytes = cur.n * g.units * 2;
 #pragma unroll
         for (int u = 0; u < U; u++) {
 #pragma unroll
@@ -392,22 +589,129 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
             } else {
               v = g0 * acc[u][r];
             }
-            out[(int64_t)(cur.p0 + m) * units + cur.unit + 16 * u] = f32_to_bf16_rne(v);
+            store_bf16<P::kOAux>(orows, obytes, m * g.units + cur.unit + 16 * u, f32_to_bf16_rne(v));
           }
         }
+        if (P::kPub) {
+          // the wavefront that completes the column block combines it
+          const int old = publish(counter(*fc, 1 + fc->max_tiles + cur.ug));
+          const int n_tiles = n_items / a.n_ug;
+          if (old == fc->dn_target * n_tiles - 1 && g.lane == 0)
+            atomicOr(&comb_mask[cur.ug >> 5], 1u << (cur.ug & 31));
+        }
       }
-#ifdef MOE_DEC_TIMING
-      n_done++;
-      if (n_done <= 4) DEC_STAMP(2 + n_done);
-#endif
     }
-    item = last_round ? item + G : item;
+    if (P::kWait && nxt.live) {
+      // the next unit's A rows, once its tile is complete
+      if (nxt.tile != cur.tile || last_round) wait_count(counter(*fc, 1 + nxt.tile), fc->gu_target, *fc);
+#pragma unroll
+      for (int s = 0; s < S; s++) load_a<NS, P::kAAux>(xa[s], nxt, min(g.ch(nkr_next, s), c1 - 1));
+    }
+    item = last_round ? item + stride : item;
     kr = nkr_next;
     cur = nxt;
   }
-  DEC_STAMP(7);
-#undef DEC_CH
-#undef DEC_GRP
+}
+
+// One stage as its own launch (stages split, and the MX path).
+template <bool GATEUP, int SPLITK, int S, int U, bool FS, bool MX>
+__global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restrict__ tiles,
+                                                 const int32_t* __restrict__ tile_tok,
+                                                 const int32_t* __restrict__ n_tiles,
+                                                 const uint8_t* __restrict__ pool, const uint16_t* __restrict__ ain,
+                                                 uint16_t* __restrict__ out) {
+  constexpr int NS = (GATEUP ? 2 : 1) * U;
+  __shared__ f32x4 red[SPLITK > 1 ? 4 : 1][NS][64];
+  const int n_items = *as_const(n_tiles) * a.n_ug;
+  Start<GATEUP, SPLITK, S, U, FS, MX> st;
+  const Desc d0 = load_desc<GATEUP>(a, blockIdx.x, threadIdx.x & 15, tiles, tile_tok);
+  stage_start<GATEUP, SPLITK, S, U, FS, MX, true>(st, a, d0, n_items, gridDim.x, tiles, tile_tok, pool, ain);
+  stage_walk<GATEUP, SPLITK, S, U, FS, MX, PlainStage>(st, a, gridDim.x, n_items, tiles, tile_tok, pool, ain, out,
+                                                       nullptr, red);
+}
+
+// Gate/up items of the fused launch: with R = ceil(n / G) rounds, the first
+// nf = n - (R - 1) G workgroups take R items each, the others R - 1.  The R-item
+// workgroups take the last R nf items (strided by nf, so each round covers
+// consecutive items), so only the tiles of those items finish a round late;
+// the others take items [0, n - R nf), strided by G - nf.
+struct GuWalk {
+  int first, stride, limit;
+};
+__device__ inline GuWalk gu_walk(int n, int G, int b) {
+  const int R = (n + G - 1) / G;
+  const int nf = n - (R - 1) * G;
+  if (R == 0) return GuWalk{0, 1, 0};
+  if (b < nf) return GuWalk{n - R * nf + b, nf, n};
+  return GuWalk{b - nf, G - nf, n - R * nf};
+}
+
+// Both stages in one launch.  Gate/up items as gu_walk gives them; down items
+// to G - 1 - b, G - 1 - b + G, ... (the workgroups that take the late tiles'
+// gate/up items take the late tiles' first down items, so these wait on no
+// other late work).  The grid must be resident as a whole (the launcher sizes
+// it by the occupancy), so a down item's wait only ever waits on gate/up
+// work of running workgroups.
+template <int GSK, int GS, int GU, bool GFS, int DSK, int DS, int DU, bool DFS, bool COMB>
+__global__ __launch_bounds__(256) void k_ffn_dec_fused(DecArgs ag, DecArgs ad, const int4* __restrict__ tiles,
+                                                       const int32_t* __restrict__ tile_tok,
+                                                       const int32_t* __restrict__ n_tiles_p,
+                                                       const uint8_t* __restrict__ pool,
+                                                       const uint16_t* __restrict__ x, uint16_t* __restrict__ h,
+                                                       uint16_t* __restrict__ y_rows, FusedCtx fc) {
+  constexpr int GNS = 2 * GU, DNS = DU;
+  constexpr int RW = (GSK > 1 || DSK > 1) ? 4 : 1, RNS = GNS > DNS ? GNS : DNS;
+  __shared__ f32x4 red[RW][RNS][64];
+  __shared__ int last_wg;
+  // column blocks this workgroup combines, and the staged combine inputs
+  __shared__ uint32_t comb_mask[COMB ? kMaxExperts / 32 : 1];
+  __shared__ int2 comb_pw[COMB ? kFusedCombineMaxT * kFusedCombineMaxK : 1];
+  __shared__ float comb_sg[COMB ? kFusedCombineMaxT : 1];
+  if (COMB)
+    for (int i = threadIdx.x; i < kMaxExperts / 32; i += blockDim.x) comb_mask[i] = 0;
+  const int n_tiles = *as_const(n_tiles_p);
+  const int n_gu = n_tiles * ag.n_ug, n_dn = n_tiles * ad.n_ug;
+  const int G = gridDim.x, b = blockIdx.x;
+  // both first descriptors; gate/up's first unit (weights, A rows, next
+  // descriptor); then the first down unit's weights (they do not depend on h)
+  const int c = threadIdx.x & 15;
+  const GuWalk gw = gu_walk(n_gu, G, b);
+  const Desc gd0 = load_desc<true>(ag, gw.first, c, tiles, tile_tok);
+  const Desc dd0 = load_desc<false>(ad, G - 1 - b, c, tiles, tile_tok);
+  Start<true, GSK, GS, GU, GFS, false> sg;
+  stage_start<true, GSK, GS, GU, GFS, false, true>(sg, ag, gd0, gw.limit, gw.stride, tiles, tile_tok, pool, x);
+  Start<false, DSK, DS, DU, DFS, false> sd;
+  stage_start<false, DSK, DS, DU, DFS, false, false>(sd, ad, dd0, n_dn, G, tiles, tile_tok, pool, h);
+  stage_walk<true, GSK, GS, GU, GFS, false, Policy<kAuxPlain, kAuxDevice, false, false>>(
+      sg, ag, gw.stride, gw.limit, tiles, tile_tok, pool, x, h, &fc, reinterpret_cast<f32x4(*)[GNS][64]>(red));
+  // every wavefront that stored h rows: once its stores are complete, one
+  // count for each of its gate/up items' tiles.  Published together at the
+  // end of the gate/up walk: one wait for the stores instead of one per item
+  // (no down item of this workgroup could start earlier anyway).
+  if ((threadIdx.x >> 6) % GSK == 0 && gw.first < gw.limit) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if ((threadIdx.x & 63) == 0)
+      for (int it = gw.first; it < gw.limit; it += gw.stride)
+        __hip_atomic_fetch_add(counter(fc, 1 + it / ag.n_ug), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  stage_walk<false, DSK, DS, DU, DFS, false,
+             Policy<kAuxDevice, COMB ? kAuxDevice : kAuxPlain, true, COMB>>(
+      sd, ad, G, n_dn, tiles, tile_tok, pool, h, y_rows, &fc, reinterpret_cast<f32x4(*)[DNS][64]>(red), comb_mask);
+  if (COMB) {
+    __syncthreads();
+    combine_blocks(y_rows, fc, comb_mask, comb_pw, comb_sg);
+  }
+  // the last workgroup to finish zeroes the counters for the next launch
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last_wg = __hip_atomic_fetch_add(counter(fc, 0), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == G - 1;
+  __syncthreads();
+  if (last_wg) {
+    const int nb = COMB ? fc.H / fc.cols : 0;
+    for (int i = threadIdx.x; i < n_tiles; i += blockDim.x) *counter(fc, 1 + i) = 0;
+    for (int i = threadIdx.x; i < nb; i += blockDim.x) *counter(fc, 1 + fc.max_tiles + i) = 0;
+    if (threadIdx.x == 0) *counter(fc, 0) = 0;
+  }
 }
 
 struct DecPtrs {
@@ -456,16 +760,34 @@ hipError_t launch_su(const DecArgs& a, const DecPtrs& p, int sk, int S, int U, c
   return U == 2 ? launch_s<GATEUP, 1, 2, MX>(a, p, S, l) : launch_s<GATEUP, 1, 1, MX>(a, p, S, l);
 }
 
-}  // namespace
+// A stage's split: K four ways when a unit block has more than 4 steps, else
+// each wavefront its own unit blocks; steps beyond MOE_DEC_MAXS per wavefront
+// run as further K rounds.  FS: every wavefront's share is whole 512-value
+// groups with S = 4.
+struct Split {
+  int sk, U, S, n_kr, n_ug;
+  bool fs;
+};
 
-// Decode-path FFN: both stages, persistent grids of (CUs x MOE_DEC_WGS_GU or
-// MOE_DEC_WGS_DN) workgroups (fewer when there is less work than that).
-hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
-                          uint16_t* y_rows, void* ws, int n_cu, int stages, hipEvent_t ev_start, hipEvent_t ev_stop,
-                          hipStream_t s, bool mx, const uint16_t* down_in) {
-  (void)perm;
-  const WsLayout wl = ws_layout(d);
-  uint8_t* base = static_cast<uint8_t*>(ws);
+Split stage_split(const moe_dims& d, bool gu, bool mx) {
+  Split sp;
+  const int K = gu ? d.H : d.I, units = gu ? d.I : d.H;
+  const int ublocks = units / 16;
+  const int steps = (K + 127) / 128;
+  const int maxs = gu ? MOE_DEC_MAXS_GU : MOE_DEC_MAXS_DN;
+  sp.sk = steps > 4 ? 4 : 1;
+  sp.U = (gu ? MOE_DEC_U_GU : MOE_DEC_U_DN) > 1 ? 2 : 1;
+  if (ublocks % ((4 / sp.sk) * sp.U) != 0) sp.U = 1;
+  if (ublocks % ((4 / sp.sk) * sp.U) != 0) sp.sk = 4;  // one unit block per item, K split four ways
+  const int wsteps = (steps + sp.sk - 1) / sp.sk;
+  sp.S = wsteps <= 1 ? 1 : (wsteps <= 2 || maxs <= 2) ? 2 : 4;
+  sp.n_kr = (wsteps + sp.S - 1) / sp.S;
+  sp.n_ug = ublocks / ((4 / sp.sk) * sp.U);
+  sp.fs = !mx && sp.S == 4 && maxs >= 4 && K % (512 * sp.sk) == 0;
+  return sp;
+}
+
+DecArgs dec_args(const moe_dims& d, const FfnGeom& g, const WsLayout& wl, const Split& sp) {
   DecArgs a;
   a.slot_stride = g.slot_stride;
   a.n_slots = g.n_slots;
@@ -478,6 +800,82 @@ hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g
   a.I = d.I;
   a.max_tiles = (int32_t)wl.max_tiles;
   a.a_bytes = (int32_t)((int64_t)d.T * d.H * 2);
+  a.n_kr = sp.n_kr;
+  a.n_ug = sp.n_ug;
+  return a;
+}
+
+// ---- the fused launch: the splits it is built for ---------------------------
+// (gate/up split, down split) pairs with an instantiation; other shapes run
+// the two stages as two launches.
+struct FusedKey {
+  int gsk, gs, gu, gfs, dsk, ds, du, dfs;
+};
+constexpr FusedKey kFused[] = {
+    {4, 4, 1, 1, 1, 4, 2, 1},  // H 2048, I 512 (the 48-layer 512-expert decode)
+    {4, 4, 1, 1, 4, 4, 2, 1},  // H 4096, I 2048 (the 43-layer 256-expert decode)
+    {1, 4, 1, 1, 1, 2, 2, 0},  // H 512, I 256
+};
+
+using FusedFn = void (*)(DecArgs, DecArgs, const int4*, const int32_t*, const int32_t*, const uint8_t*,
+                         const uint16_t*, uint16_t*, uint16_t*, FusedCtx);
+
+template <int I>
+FusedFn fused_fn(bool comb) {
+  constexpr FusedKey f = kFused[I];
+  return comb ? k_ffn_dec_fused<f.gsk, f.gs, f.gu, (bool)f.gfs, f.dsk, f.ds, f.du, (bool)f.dfs, true>
+              : k_ffn_dec_fused<f.gsk, f.gs, f.gu, (bool)f.gfs, f.dsk, f.ds, f.du, (bool)f.dfs, false>;
+}
+
+FusedFn find_fused(const Split& g, const Split& dn, bool comb) {
+  auto match = [&](const FusedKey& f) {
+    return f.gsk == g.sk && f.gs == g.S && f.gu == g.U && f.gfs == (int)g.fs && f.dsk == dn.sk && f.ds == dn.S &&
+           f.du == dn.U && f.dfs == (int)dn.fs;
+  };
+  if (match(kFused[0])) return fused_fn<0>(comb);
+  if (match(kFused[1])) return fused_fn<1>(comb);
+  if (match(kFused[2])) return fused_fn<2>(comb);
+  return nullptr;
+}
+
+// The fused launch's wait parameters: the poll limit, and a count added to
+// every tile's target.  Tests set them (moe_debug_set_fused_wait) to force a
+// wait to time out while every wavefront still ends: with an added count the
+// target is never reached and each wait gives up after the poll limit.
+std::atomic<int> g_spin_limit{MOE_DEC_SPIN_LIMIT};
+std::atomic<int> g_extra_target{0};
+
+// workgroups of fn resident per CU (queried once per kernel)
+int fused_occupancy(FusedFn fn) {
+  static std::mutex mu;
+  static FusedFn keys[8];
+  static int vals[8];
+  static int n = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < n; i++)
+    if (keys[i] == fn) return vals[i];
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), 256, 0) !=
+      hipSuccess)
+    per_cu = 0;
+  if (n < 8) {
+    keys[n] = fn;
+    vals[n] = per_cu;
+    n++;
+  }
+  return per_cu;
+}
+
+}  // namespace
+
+// Decode-path FFN: both stages, persistent grids of (CUs x MOE_DEC_WGS_GU or
+// MOE_DEC_WGS_DN) workgroups (fewer when there is less work than that).
+hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
+                          uint16_t* y_rows, void* ws, int n_cu, int stages, hipEvent_t ev_start, hipEvent_t ev_stop,
+                          hipStream_t s, bool mx, const uint16_t* down_in) {
+  (void)perm;
+  const WsLayout wl = ws_layout(d);
+  uint8_t* base = static_cast<uint8_t*>(ws);
   DecPtrs ptrs;
   ptrs.tiles = reinterpret_cast<const int4*>(base + wl.off_tiles);
   ptrs.tile_tok = reinterpret_cast<const int32_t*>(base + wl.off_tile_tok);
@@ -487,21 +885,8 @@ hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g
     if (!((stages >> stage) & 1)) continue;
     const bool gu = stage == 0;
     const int64_t cap = (int64_t)n_cu * (gu ? MOE_DEC_WGS_GU : MOE_DEC_WGS_DN);
-    const int K = gu ? d.H : d.I, units = gu ? d.I : d.H;
-    const int ublocks = units / 16;
-    const int steps = (K + 127) / 128;
-    // split K four ways when a unit block has more than 4 steps, else give
-    // each wavefront its own unit blocks; steps beyond MOE_DEC_MAXS per
-    // wavefront run as further K rounds
-    const int maxs = gu ? MOE_DEC_MAXS_GU : MOE_DEC_MAXS_DN;
-    int sk = steps > 4 ? 4 : 1;
-    int U = (gu ? MOE_DEC_U_GU : MOE_DEC_U_DN) > 1 ? 2 : 1;
-    if (ublocks % ((4 / sk) * U) != 0) U = 1;
-    if (ublocks % ((4 / sk) * U) != 0) sk = 4;  // one unit block per item, K split four ways
-    const int wsteps = (steps + sk - 1) / sk;
-    const int S = wsteps <= 1 ? 1 : (wsteps <= 2 || maxs <= 2) ? 2 : 4;
-    a.n_kr = (wsteps + S - 1) / S;
-    a.n_ug = ublocks / ((4 / sk) * U);
+    const Split sp = stage_split(d, gu, mx);
+    const DecArgs a = dec_args(d, g, wl, sp);
     const int64_t items = (int64_t)wl.max_tiles * a.n_ug;
     const int grid = (int)(items < cap ? items : cap);
     ptrs.ain = gu ? x : (down_in ? down_in : h);
@@ -509,20 +894,71 @@ hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g
     // the start event goes with the first stage launched, the stop event with the last
     const bool first = gu || !(stages & 1), last = !gu || !(stages & 2);
     const DecLaunch l{grid, s, first ? ev_start : nullptr, last ? ev_stop : nullptr};
-    const hipError_t e = mx ? (gu ? launch_su<true, true>(a, ptrs, sk, S, U, l) : launch_su<false, true>(a, ptrs, sk, S, U, l))
-                            : (gu ? launch_su<true, false>(a, ptrs, sk, S, U, l)
-                                  : launch_su<false, false>(a, ptrs, sk, S, U, l));
+    const hipError_t e = mx ? (gu ? launch_su<true, true>(a, ptrs, sp.sk, sp.S, sp.U, l)
+                                  : launch_su<false, true>(a, ptrs, sp.sk, sp.S, sp.U, l))
+                            : (gu ? launch_su<true, false>(a, ptrs, sp.sk, sp.S, sp.U, l)
+                                  : launch_su<false, false>(a, ptrs, sp.sk, sp.S, sp.U, l));
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
-#ifdef MOE_DEC_TIMING
-extern "C" void* moe_debug_dec_times(void) {
-  void* p = nullptr;
-  if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_dec_times)) != hipSuccess) return nullptr;
-  return p;
+bool ffn_dec_fusable(const moe_dims& d, bool combine) {
+  if (use_gemm(d)) return false;
+  if (combine && (d.T > kFusedCombineMaxT || d.k > kFusedCombineMaxK)) return false;
+  return find_fused(stage_split(d, true, false), stage_split(d, false, false), combine) != nullptr;
 }
-#endif
+
+hipError_t launch_ffn_dec_fused(const moe_dims& d, const uint16_t* x, const FfnGeom& g, uint16_t* h,
+                                uint16_t* y_rows, int32_t* dev_status, void* ws, int n_cu, hipEvent_t ev_start,
+                                hipEvent_t ev_stop, hipStream_t s, const int32_t* inv_perm, const float* w,
+                                const float* sigma, uint16_t* y) {
+  const WsLayout wl = ws_layout(d);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  const Split sg = stage_split(d, true, false), sdn = stage_split(d, false, false);
+  const bool comb = inv_perm != nullptr;
+  const FusedFn fn = find_fused(sg, sdn, comb);
+  if (!fn) return hipErrorInvalidConfiguration;
+  const DecArgs ag = dec_args(d, g, wl, sg), ad = dec_args(d, g, wl, sdn);
+  const int per_cu = fused_occupancy(fn);
+  if (per_cu <= 0) return hipErrorInvalidConfiguration;
+  const int64_t cap = (int64_t)n_cu * (per_cu < MOE_DEC_WGS_FUSED ? per_cu : MOE_DEC_WGS_FUSED);
+  const int64_t items = (int64_t)wl.max_tiles * (ag.n_ug > ad.n_ug ? ag.n_ug : ad.n_ug);
+  const int grid = (int)(items < cap ? items : cap);
+  FusedCtx fc;
+  fc.sync = reinterpret_cast<int32_t*>(base + wl.off_sync);
+  fc.status = dev_status;
+  fc.max_tiles = (int32_t)wl.max_tiles;
+  // every storing wavefront of every gate/up item of a tile
+  fc.gu_target = ag.n_ug * (4 / sg.sk) + g_extra_target.load(std::memory_order_relaxed);
+  fc.dn_target = 4 / sdn.sk;  // storing wavefronts of a down item
+  fc.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  fc.inv_perm = inv_perm;
+  fc.w = w;
+  fc.sigma = sigma;
+  fc.y = y;
+  fc.T = d.T;
+  fc.k = d.k;
+  fc.H = d.H;
+  fc.cols = d.H / ad.n_ug;
+  const int4* tiles = reinterpret_cast<const int4*>(base + wl.off_tiles);
+  const int32_t* tile_tok = reinterpret_cast<const int32_t*>(base + wl.off_tile_tok);
+  const int32_t* n_tiles = reinterpret_cast<const int32_t*>(base + wl.off_meta);
+  const uint8_t* pool = g.pool;
+  void* args[] = {(void*)&ag, (void*)&ad, (void*)&tiles, (void*)&tile_tok, (void*)&n_tiles, (void*)&pool,
+                  (void*)&x, (void*)&h, (void*)&y_rows, (void*)&fc};
+  if (ev_start || ev_stop)
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(256), args, 0, s, ev_start, ev_stop,
+                              0);
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(256), args, 0, s);
+}
 
 }  // namespace moe
+
+// Test hook (not part of the documented interface): the fused FFN launch's
+// poll limit and a count added to its tile targets; (-1, 0) restores the
+// defaults.  Affects launches enqueued afterwards, from every thread.
+extern "C" void moe_debug_set_fused_wait(int spin_limit, int extra_target) {
+  moe::g_spin_limit.store(spin_limit < 0 ? MOE_DEC_SPIN_LIMIT : spin_limit);
+  moe::g_extra_target.store(extra_target < 0 ? 0 : extra_target);
+}

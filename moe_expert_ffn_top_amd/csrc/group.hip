@@ -162,8 +162,10 @@ __global__ __launch_bounds__(1024) void k_scan(int64_t ncb, int T, int k, int E,
                                                int32_t* __restrict__ meta, int4* __restrict__ tiles,
                                                int32_t* __restrict__ tile_tok, int32_t* __restrict__ tile_base,
                                                int4* __restrict__ chunks, int skip_rank,
-                                               const int32_t* __restrict__ mrk, int32_t* __restrict__ n_skipped) {
+                                               const int32_t* __restrict__ mrk, int32_t* __restrict__ n_skipped,
+                                               int32_t* __restrict__ sync, int64_t n_sync) {
   using vec = typename std::conditional<V == 4, int4, int>::type;
+  zero_sync(sync, n_sync);
   constexpr int kBatch = 16;
   __shared__ int lds[17];
   __shared__ int32_t part_sum[1024 * V];  // [part][eq][V] = [part][expert]
@@ -333,7 +335,8 @@ __global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict_
                                                       int32_t* __restrict__ meta, int4* __restrict__ tiles,
                                                       int32_t* __restrict__ tile_tok,
                                                       int32_t* __restrict__ tile_base, int4* __restrict__ chunks,
-                                                      int skip_rank, int32_t* __restrict__ n_skipped) {
+                                                      int skip_rank, int32_t* __restrict__ n_skipped,
+                                                      int32_t* __restrict__ sync, int64_t n_sync) {
   __shared__ int32_t hist[1024];
   __shared__ int32_t cntl[1024];
   __shared__ int32_t tbl[1024];
@@ -344,6 +347,7 @@ __global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict_
   STAGE_STAMP(1, 0);
   const int slot = tid < E ? slot_table[(int64_t)layer * (E + 1) + tid] : -1;
   const int ss = slot_table[(int64_t)layer * (E + 1) + E];
+  zero_sync(sync, n_sync);
   if (tid < E) {
     hist[tid] = 0;
     minr[tid] = k;
@@ -374,7 +378,7 @@ __global__ __launch_bounds__(1024) void k_route_group_small(
     float* __restrict__ wout, float* __restrict__ sigma, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv_perm, int32_t* __restrict__ group_slot, int32_t* __restrict__ status,
     int32_t* __restrict__ meta, int4* __restrict__ tiles, int32_t* __restrict__ tile_tok,
-    int32_t* __restrict__ tile_base, int4* __restrict__ chunks) {
+    int32_t* __restrict__ tile_base, int4* __restrict__ chunks, int32_t* __restrict__ sync, int64_t n_sync) {
   __shared__ int32_t hist[1024];
   __shared__ int32_t cntl[1024];
   __shared__ int32_t tbl[1024];
@@ -386,6 +390,7 @@ __global__ __launch_bounds__(1024) void k_route_group_small(
   STAGE_STAMP(1, 0);
   const int slot = tid < E ? slot_table[(int64_t)layer * (E + 1) + tid] : -1;
   const int ss = slot_table[(int64_t)layer * (E + 1) + E];
+  zero_sync(sync, n_sync);
   if (tid < E) hist[tid] = 0;
   if (tid >= F && tid < kSmallF) sid[tid] = -1;
   if (wave < T) topk_wave<NPL>(logits, x, w_sg, wave, H, E, k, ids, wout, sigma, wink + wave * k, sid + wave * k);
@@ -454,10 +459,11 @@ hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, co
   int32_t* tile_tok = reinterpret_cast<int32_t*>(base + wl.off_tile_tok);
   int32_t* tile_base = reinterpret_cast<int32_t*>(base + wl.off_tile_base);
   int4* chunks = use_gemm(d) ? reinterpret_cast<int4*>(base + wl.off_chunks) : nullptr;
+  int32_t* sync = reinterpret_cast<int32_t*>(base + wl.off_sync);
   if (F <= kSmallF) {
     hipLaunchKernelGGL(k_group_small, dim3(1), dim3(1024), 0, s, ids, (int)F, d.T, d.k, d.E, layer, slot_table,
                        n_slots, offsets, perm, inv_perm, group_slot, dev_status, meta, tiles, tile_tok, tile_base,
-                       chunks, skip_rank, n_skipped);
+                       chunks, skip_rank, n_skipped, sync, wl.n_sync);
     return hipGetLastError();
   }
   int32_t* mrk = reinterpret_cast<int32_t*>(base + wl.off_mrk);
@@ -466,7 +472,7 @@ hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, co
   auto scan = d.E % 4 == 0 ? k_scan<4> : k_scan<1>;
   hipLaunchKernelGGL(scan, dim3(1), dim3(1024), 0, s, wl.ncb, d.T, d.k, d.E, layer, slot_table, n_slots, cnt,
                      offsets, group_slot, dev_status, meta, tiles, tile_tok, tile_base, chunks, skip_rank, mrk,
-                     n_skipped);
+                     n_skipped, sync, wl.n_sync);
   hipLaunchKernelGGL(k_scatter, dim3((unsigned)wl.nb), dim3(kBlk), 0, s, ids, F, d.E, d.k, cnt, offsets, perm, inv_perm,
                      chunks ? nullptr : tile_tok, tile_base);
   return hipGetLastError();
@@ -485,12 +491,13 @@ hipError_t launch_route_group(const moe_dims& d, int32_t layer, const float* log
   int32_t* tile_tok = reinterpret_cast<int32_t*>(base + wl.off_tile_tok);
   int32_t* tile_base = reinterpret_cast<int32_t*>(base + wl.off_tile_base);
   int4* chunks = use_gemm(d) ? reinterpret_cast<int4*>(base + wl.off_chunks) : nullptr;
+  int32_t* sync = reinterpret_cast<int32_t*>(base + wl.off_sync);
   const int npl = (d.E + 63) / 64;
   const dim3 g(1), b(1024);
 #define MOE_RG_LAUNCH(N)                                                                                        \
   hipLaunchKernelGGL(k_route_group_small<N>, g, b, 0, s, logits, x, w_sg, d.T, d.H, d.E, d.k, layer, slot_table, \
                      n_slots, ids, w, sigma, offsets, perm, inv_perm, group_slot, dev_status, meta, tiles, tile_tok, \
-                     tile_base, chunks)
+                     tile_base, chunks, sync, wl.n_sync)
   if (npl <= 1) MOE_RG_LAUNCH(1);
   else if (npl <= 2) MOE_RG_LAUNCH(2);
   else if (npl <= 4) MOE_RG_LAUNCH(4);

@@ -30,6 +30,8 @@ inline bool use_gemm(const moe_dims& d) { return (int64_t)d.T * d.k >= (int64_t)
 // tile_base int32 [E]           first tile of each routed group
 // chunks    int4  [max_chunks]  {group, first row p0, rows n (<= 256), slot}
 // mrk       int32 [ncb][E]      per-block lowest slot rank per expert (tail-skip only)
+// sync      int32 [n_sync]      counters of the fused decode FFN launch (ffn_dec.hip); every
+//                               grouping kernel zeroes them, and so does the launch's last workgroup
 // The FFN reads either the tile lists (weight-streaming kernel) or the chunk
 // list (grouped GEMM), and the grouping writes only the one that use_gemm names.
 // Flat entries per counting block of the grouping (a multiple of 256).
@@ -39,12 +41,16 @@ constexpr int kMaxExperts = 1024;
 // Largest slot count of a residency cache (the residency kernel keeps one bit
 // per slot in LDS).
 constexpr int kMaxResidencySlots = 262144;
+// Words between two counters of the fused FFN (each on its own 256-byte
+// line, so that polls and increments of different counters do not meet).
+constexpr int kSyncStride = 64;
 struct WsLayout {
   int64_t nb;          // blocks of 256 flat (token, slot) entries
   int64_t ncb;         // blocks of kCntBlk flat entries
   int64_t max_tiles;   // upper bound on FFN tiles
   int64_t max_chunks;  // upper bound on GEMM chunks
-  uint64_t off_cnt, off_meta, off_tiles, off_tile_tok, off_tile_base, off_chunks, off_mrk, total;
+  int64_t n_sync;      // counters of the fused FFN: 1 + max_tiles + H / 16, kSyncStride words apart
+  uint64_t off_cnt, off_meta, off_tiles, off_tile_tok, off_tile_base, off_chunks, off_mrk, off_sync, total;
 };
 
 inline uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
@@ -64,7 +70,9 @@ inline WsLayout ws_layout(const moe_dims& d) {
   w.max_chunks = (F + kChunkRows - 1) / kChunkRows + routed_groups + (d.T + kChunkRows - 1) / kChunkRows + 1;
   w.off_chunks = align256(w.off_tile_base + (uint64_t)d.E * 4);
   w.off_mrk = align256(w.off_chunks + (uint64_t)w.max_chunks * 16);
-  w.total = align256(w.off_mrk + (uint64_t)w.ncb * d.E * 4);
+  w.n_sync = 1 + w.max_tiles + d.H / 16;
+  w.off_sync = align256(w.off_mrk + (uint64_t)w.ncb * d.E * 4);
+  w.total = align256(w.off_sync + (uint64_t)w.n_sync * kSyncStride * 4);
   return w;
 }
 
@@ -294,5 +302,22 @@ hipError_t launch_ffn_dec_mx(const moe_dims& d, const uint16_t* x, const FfnGeom
                              hipEvent_t ev_stop, hipStream_t s);
 hipError_t launch_combine(const moe_dims& d, const uint16_t* y_rows, const int32_t* inv_perm, const float* w,
                           const float* sigma, uint16_t* y, hipStream_t s);
+// Decode-path FFN with both stages (and optionally the combine) in one launch
+// (ffn_dec.hip).  ffn_dec_fusable: the weight-streaming path is taken for d
+// and its two stage splits have a fused instantiation (and, with combine,
+// T <= kFusedCombineMaxT and k <= kFusedCombineMaxK).  inv_perm null: no
+// combine.
+constexpr int kFusedCombineMaxT = 64;
+constexpr int kFusedCombineMaxK = 16;
+bool ffn_dec_fusable(const moe_dims& d, bool combine);
+hipError_t launch_ffn_dec_fused(const moe_dims& d, const uint16_t* x, const FfnGeom& g, uint16_t* h,
+                                uint16_t* y_rows, int32_t* dev_status, void* ws, int n_cu, hipEvent_t ev_start,
+                                hipEvent_t ev_stop, hipStream_t s, const int32_t* inv_perm, const float* w,
+                                const float* sigma, uint16_t* y);
+// Zero the fused FFN's counters in the workspace: every thread of a
+// one-block grouping kernel calls it.
+__device__ inline void zero_sync(int32_t* sync, int64_t n) {
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) sync[i * kSyncStride] = 0;
+}
 
 }  // namespace moe
