@@ -19,8 +19,17 @@ Extra objects on the line:
                 The down stage is reported beside it.  "traffic" is the HBM
                 bytes per launch measured with rocprofv3 counters and recorded
                 in profiles/ (null unless it was measured on this kernel source).
-  cpu_baseline  the CPU oracle (oracle/, fp64 numpy, 1 thread) on a bounded
-                sample of the same workload, scaled to tokens/s.
+                With --ffn one-launch the dominant kernel is the one launch of
+                moe_expert_ffn_combine (both stages and the combine), against
+                both stages' expert bytes.
+  prefill8192,  (default workload only) the 8192-token prefill layer and the
+  decode43x64   43-layer decode over 64 steps, measured in the same run:
+                tokens/s and their own roofline; for decode43x64 also the p50
+                and p90 of the 64 step times and the expert-weight GB/s of a
+                step.  --no-extra skips them.
+  cpu_baseline  the CPU oracle (oracle/, fp64 numpy) on a bounded sample of
+                the same workload, scaled to tokens/s: on every host core this
+                process may use (cores), and on one thread (one_thread).
 
 --copy-calibration BYTES runs only a plain device copy of BYTES bytes five
 times (the reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters).
@@ -60,10 +69,16 @@ def parse():
                          "decode48_mx "
                          "(default decode48)")
     ap.add_argument("--eager", action="store_true", help="launch every call eagerly instead of HIP graphs")
+    ap.add_argument("--ffn", default="split", choices=("one-launch", "split"),
+                    help="decode windows: FFN and combine in one launch (moe_expert_ffn_combine) or one launch per "
+                         "FFN stage plus the combine's (moe_expert_ffn_stages 1, 2; moe_combine)")
     ap.add_argument("--policy", default="lru", choices=("lru", "hotcold"),
                     help="cached workloads: lru (fill every miss; the layer's outputs) or hotcold (measure the "
                          "hot/cold swap policy over the routing)")
-    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0,
+                    help="oracle seconds per timing (it is timed twice: all host cores, then one thread)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="decode48: skip the prefill8192 and decode43x64 measurements added to its line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     return ap.parse_args()
@@ -142,12 +157,13 @@ def recorded_traffic(cfg):
 class Workload:
     """Device-resident inputs of every step to be run, plus one set of layer buffers."""
 
-    def __init__(self, cfg, n_steps, B, DevGen):
+    def __init__(self, cfg, n_steps, B, DevGen, ffn="split"):
         import torch
         from moe_expert_ffn_top_amd.layer import LayerBuffers
         from synth import zipf_logits
 
         self.cfg = cfg
+        self.ffn_mode = ffn
         self.dims = B.Dims(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.L)
         self.mx = cfg.fmt == "mx"
         self.layout = B.moe_blob_layout_init_mx(cfg.H, cfg.I) if self.mx else B.moe_blob_layout_init(cfg.H, cfg.I)
@@ -205,7 +221,7 @@ class Workload:
     def one_launch(self):
         """NVFP4 decode windows: the FFN and the combine run through
         moe_expert_ffn_combine, one launch per layer."""
-        return not self.mx and self.cfg.T * self.cfg.k < 16 * self.cfg.E
+        return not self.mx and self.cfg.T * self.cfg.k < 16 * self.cfg.E and self.ffn_mode == "one-launch"
 
     def ffn_combine(self, x, ev_start=None, ev_stop=None, stream=None):
         from moe_expert_ffn_top_amd import binding as B
@@ -239,7 +255,11 @@ class Workload:
                     ffn_events.append((ev, buf.offsets.clone()))
                 continue
             if ffn_events is None:
-                self.ffn(x, stream=stream)
+                if self.ffn_mode == "split" and not self.mx:
+                    for st in (1, 2):
+                        self.ffn(x, st, stream=stream)
+                else:
+                    self.ffn(x, stream=stream)
             else:
                 ev = [hip_events.new() for _ in range(4)]
                 for st in (1, 2):
@@ -273,10 +293,10 @@ def expert_work(cfg, offsets_list):
     return tuple(np.array(v, dtype=np.float64) for v in (gu_b, dn_b, gu_f, dn_f))
 
 
-def cpu_baseline(cfg, seconds):
-    """Time the oracle (fp64 numpy, one thread) on a bounded sample of the
-    workload: whole layers of step 0 for decode (all T tokens), a token sample
-    for prefill; scaled to tokens/s of the full step."""
+def cpu_baseline(cfg, seconds, threads=1):
+    """Time the oracle (fp64 numpy, BLAS on `threads` threads) on a bounded
+    sample of the workload: whole layers of step 0 for decode (all T tokens),
+    a token sample for prefill; scaled to tokens/s of the full step."""
     from threadpoolctl import threadpool_limits
 
     from oracle import moe_oracle as O
@@ -288,7 +308,7 @@ def cpu_baseline(cfg, seconds):
     make_blob = gen.expert_blob_mx if mx else gen.expert_blob
     done_layers, t_oracle = 0, 0.0
     sample = ""
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         if cfg.T <= 64:
             for l in range(cfg.L):
                 x = gen.x(cfg, l, 0)
@@ -330,7 +350,18 @@ def cpu_baseline(cfg, seconds):
             value = ntok / t_oracle
             sample = "layer 0, routing and grouping of all %d tokens plus expert FFN and combine of %d sampled " \
                      "tokens; oracle time %.1f s; rate = sampled tokens / time" % (cfg.T, ntok, t_oracle)
-    return {"value": value, "unit": "tokens/s", "cores": 1, "kind": "oracle", "sample": sample}
+    return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle", "sample": sample}
+
+
+def cpu_baselines(cfg, seconds):
+    """The oracle timed on every host core this process may use, then on one
+    thread; both core counts are stated."""
+    cores = len(os.sched_getaffinity(0))
+    log("timing the CPU oracle on a bounded sample (%d threads, then 1)" % cores)
+    cpu = cpu_baseline(cfg, seconds, cores)
+    one = cpu_baseline(cfg, seconds, 1)
+    cpu["one_thread"] = {"value": one["value"], "cores": 1, "sample": one["sample"]}
+    return cpu
 
 
 PCIE_GEN5_X16_GBS = 64.0   # the host link's published rate per direction
@@ -657,8 +688,7 @@ def run_staged(cfg, args, B, DevGen):
             "kernel_source_sha256_16": kernel_source_hash(cfg)}
     cpu = None
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(cfg, args.cpu_baseline_seconds)
+        cpu = cpu_baselines(cfg, args.cpu_baseline_seconds)
     line = {
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -702,12 +732,69 @@ def main():
         (run_hotcold if args.policy == "hotcold" else run_cached)(cfg, args, B, DevGen)
         return
     K, W = args.steps, args.warmup
-    wl = Workload(cfg, W + K, B, DevGen)
-    stream = torch.cuda.current_stream()
+    res = measure_workload(cfg, args, B, DevGen, K, W, ffn=args.ffn)
+    extra = {}
+    if cfg.name == "decode48" and not args.no_extra:
+        # the other headline configurations, measured in the same run
+        torch.cuda.empty_cache()
+        pf = measure_workload(config_by_name("prefill8192"), args, B, DevGen, 10, 3, ffn=args.ffn)
+        extra["prefill8192"] = summarize(pf)
+        torch.cuda.empty_cache()
+        dc = measure_workload(config_by_name("decode43x64"), args, B, DevGen, 64, 3, ffn=args.ffn, per_step=True)
+        extra["decode43x64"] = summarize(dc)
+        torch.cuda.empty_cache()
 
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baselines(cfg, args.cpu_baseline_seconds)
+
+    line = {
+        "metric": METRIC, "value": res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": ("mxfp8 x mxfp4" if cfg.T * cfg.k >= 16 * cfg.E else "bf16 (mxfp8 x mxfp4 values)")
+        if cfg.fmt == "mx" else "bf16",
+        "data": "synthetic (seeded; random MXFP4 weights, bf16 activations quantised to MXFP8)" if cfg.fmt == "mx"
+        else "synthetic (seeded; random block-FP4 weights, bf16 activations)",
+        "config": res["config"],
+        "roofline": res["roof"], "cpu_baseline": cpu,
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+def workload_config(cfg, args, ffn):
+    return {"workload": cfg.name, "T": cfg.T, "layers": cfg.L, "H": cfg.H, "I": cfg.I, "E": cfg.E,
+            "k": cfg.k, "shared_experts": 1,
+            "routing": ("zipf s=%g" % cfg.zipf_s) if cfg.router == "zipf" else "router matrix",
+            "graphs": not args.eager, "ffn": ffn if cfg.T * cfg.k < 16 * cfg.E else "grouped GEMM",
+            "parallelism": "single GPU"}
+
+
+def summarize(res):
+    """The sub-object of an extra configuration on the bench line."""
+    out = {"tokens_per_s": res["tokens_per_s"], "ms_per_step": res["ms_per_step"], "steps": res["steps"],
+           "config": res["config"], "roofline": res["roof"]}
+    if "step_ms" in res:
+        v = np.array(res["step_ms"])
+        out["step_ms_p50"] = float(np.percentile(v, 50))
+        out["step_ms_p90"] = float(np.percentile(v, 90))
+        out["expert_gb_per_step"] = res["expert_bytes_per_step"] / 1e9
+        out["expert_gb_per_s"] = res["expert_bytes_per_step"] / (out["step_ms_p50"] * 1e-3) / 1e9
+        out["expert_frac_of_hbm_peak"] = out["expert_gb_per_s"] / HBM_PEAK_GBS
+    return out
+
+
+def measure_workload(cfg, args, B, DevGen, K, W, ffn="split", per_step=False):
+    """Time K steps of a workload (after W warm-up steps) with every step's
+    inputs resident in HBM, each step one captured HIP graph (unless --eager);
+    then the roofline of its dominant kernel from HIP events around its
+    launches on their stream.  per_step: also each step's own time (HIP events
+    around each replay) and the expert-weight bytes a step reads."""
+    import torch
+    wl = Workload(cfg, W + K, B, DevGen, ffn=ffn)
     graphs = []
     if not args.eager:
-        log("capturing %d step graphs" % min(W + K, wl.n_inputs))
+        log("%s: capturing %d step graphs" % (cfg.name, min(W + K, wl.n_inputs)))
         for s in range(min(W + K, wl.n_inputs)):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
@@ -726,20 +813,31 @@ def main():
     torch.cuda.synchronize()
     status = int(wl.buf.status.item())
     assert status == 0, "device status %d after warmup" % status
+    res = {"steps": K, "config": workload_config(cfg, args, ffn)}
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t0.record()
-    for i in range(K):
-        step(W + i)
-    t1.record()
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / K
-    tokens_per_s = cfg.T / (ms_per_step / 1e3)
-    log("%.4f ms/step, %.1f tokens/s" % (ms_per_step, tokens_per_s))
+    if per_step:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        t0.record()
+        for i in range(K):
+            ev[i][0].record()
+            step(W + i)
+            ev[i][1].record()
+        t1.record()
+        torch.cuda.synchronize()
+        res["step_ms"] = [a.elapsed_time(b) for a, b in ev]
+    else:
+        t0.record()
+        for i in range(K):
+            step(W + i)
+        t1.record()
+        torch.cuda.synchronize()
+    res["ms_per_step"] = t0.elapsed_time(t1) / K
+    res["tokens_per_s"] = cfg.T / (res["ms_per_step"] / 1e3)
+    log("%s: %.4f ms/step, %.1f tokens/s" % (cfg.name, res["ms_per_step"], res["tokens_per_s"]))
 
-    # roofline of the dominant kernel (the FFN's gate/up stage) and of the down
-    # stage: HIP events around each stage's launch on its stream
+    # roofline of the dominant kernel: HIP events around its launches on their stream
     events = []
     hev = HipEvents()
     for i in range(min(K, 8)):
@@ -752,7 +850,19 @@ def main():
         dn_ms = np.array([hev.elapsed_ms(ev[2], ev[3]) for ev, _ in events])
     hev.close()
     gu_b, dn_b, gu_f, dn_f = expert_work(cfg, [o for _, o in events])
-    decode = cfg.T <= 64
+    decode = cfg.T * cfg.k < 16 * cfg.E
+    if per_step:
+        # expert-weight bytes of a whole step: every layer's distinct experts
+        offs = []
+        for i in range(min(K, 4)):
+            lay_ev = []
+            hev2 = HipEvents()
+            wl.run_step(W + i, ffn_events=lay_ev, hip_events=hev2)
+            torch.cuda.synchronize()
+            hev2.close()
+            g2, d2, _, _ = expert_work(cfg, [o for _, o in lay_ev])
+            offs.append(float(g2.sum() + d2.sum()))
+        res["expert_bytes_per_step"] = float(np.mean(offs))
     if wl.one_launch:
         # the dominant kernel: gate/up, down and combine in one launch; its
         # algorithmic bytes are the expert weights it streams (both stages)
@@ -766,9 +876,8 @@ def main():
                     gu_b.mean(), dn_b.mean())}
     elif decode:
         achieved = float(gu_b.mean() / (gu_ms.mean() * 1e-3) / 1e9)
-        traffic = recorded_traffic(cfg)
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(cfg),
                 "kernel": "%s gate/up (%s, stages=1)" % (
                     ffn_kernel(cfg)[0], "moe_expert_ffn_mx" if cfg.fmt == "mx" else "moe_expert_ffn_stages"),
                 "launch_us": float(gu_ms.mean() * 1e3), "bytes_per_launch": float(gu_b.mean()),
@@ -785,27 +894,10 @@ def main():
                 "down": {"launch_us": float(dn_ms.mean() * 1e3), "flops_per_launch": float(dn_f.mean()),
                          "achieved": float(dn_f.mean() / (dn_ms.mean() * 1e-3) / 1e12)}}
     roof["kernel_source_sha256_16"] = kernel_source_hash(cfg)
-    log("roofline: %s" % roof)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(cfg, args.cpu_baseline_seconds)
-
-    line = {
-        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
-        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": ("mxfp8 x mxfp4" if cfg.T * cfg.k >= 16 * cfg.E else "bf16 (mxfp8 x mxfp4 values)")
-        if cfg.fmt == "mx" else "bf16",
-        "data": "synthetic (seeded; random MXFP4 weights, bf16 activations quantised to MXFP8)" if cfg.fmt == "mx"
-        else "synthetic (seeded; random block-FP4 weights, bf16 activations)",
-        "config": {"workload": cfg.name, "T": cfg.T, "layers": cfg.L, "H": cfg.H, "I": cfg.I, "E": cfg.E,
-                   "k": cfg.k, "shared_experts": 1,
-                   "routing": ("zipf s=%g" % cfg.zipf_s) if cfg.router == "zipf" else "router matrix",
-                   "graphs": not args.eager, "parallelism": "single GPU"},
-        "roofline": roof, "cpu_baseline": cpu,
-    }
-    print(json.dumps(line), flush=True)
+    log("%s roofline: %s" % (cfg.name, roof))
+    res["roof"] = roof
+    del graphs, wl
+    return res
 
 
 if __name__ == "__main__":

@@ -344,13 +344,6 @@ int moe_route_group(const moe_dims* d, int32_t layer, const uint16_t* x,
  * Rows of a group whose slot is -1 or >= pool_bytes/slot_stride are written
  * as zeros and flagged in dev_status.
  * offsets/perm/group_slot/ws: exactly as written by moe_group on the same stream.
- * For decode-sized groups ([FreeToken] 3.5: a step's control flow stays on
- * the device) both stages may run as one launch: the down projection of a
- * tile waits, inside the launch, for the workgroups that write its h rows.
- * The wait is bounded; should it time out (only if the device cannot keep
- * the launch's workgroups resident together, e.g. other work holds its
- * compute units for a long time), MOE_DEV_SYNC_TIMEOUT is set and h, y_rows
- * are undefined.  The results are the same bits either way.
  */
 int moe_expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool,
                    uint64_t pool_bytes, const moe_blob_layout* layout,
@@ -382,11 +375,20 @@ int moe_expert_ffn_stages(const moe_dims* d, const uint16_t* x, const void* pool
 /* ---- S4 + S5 together ----------------------------------------------------
  * moe_expert_ffn followed by moe_combine on the same stream, with exactly
  * their arguments, validation and results (h, y_rows and y bit-identical).
- * For decode windows (T <= 64 on the weight-streaming path, shapes with a
- * one-launch instantiation) the combine runs inside the FFN's launch: the
- * wavefront that completes the last down item of a block of output columns
- * combines that block for every token ([Strata] "路由以后，专家怎样分工？": each
+ * For decode windows (T <= 64 and k <= 16 on the weight-streaming path, and
+ * (H, I) of (2048, 512), (4096, 2048) or (512, 256)) both FFN stages and the
+ * combine run as one launch ([FreeToken] 3.5: a step's control flow stays on
+ * the device): the down projection of a tile waits, inside the launch, for
+ * the workgroups that write its h rows, and the wavefront that completes the
+ * last down item of a block of output columns marks that block for its
+ * workgroup to combine for every token ([Strata] "路由以后，专家怎样分工？": each
  * token's expert outputs are weighted and summed once all have arrived).
+ * The waits are bounded; should one time out (only if the device cannot keep
+ * the launch's workgroups resident together, e.g. other work holds its
+ * compute units for a long time), MOE_DEV_SYNC_TIMEOUT is set and h, y_rows
+ * and y are undefined.  One launch saves two launches' host cost; inside a
+ * HIP graph the separate launches overlap their start-up and were measured
+ * slightly faster on MI355X.
  * ev_start, ev_stop as for moe_expert_ffn_stages (they bracket the FFN
  * launch, and the combine when it is part of it). */
 int moe_expert_ffn_combine(const moe_dims* d, const uint16_t* x, const void* pool,

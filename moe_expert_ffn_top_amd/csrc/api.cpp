@@ -347,10 +347,10 @@ int moe_expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool, uint6
 
 namespace {
 
-// S4 (stages: 1 gate/up, 2 down, 3 both) and, with inv_perm set, S5 after it.
-// Both stages together on the weight-streaming path run as one launch when
-// the shapes have a fused instantiation (and so does the combine for small
-// windows); otherwise one launch per stage, then the combine's own.
+// S4 (stages: 1 gate/up, 2 down, 3 both) and, with y set, S5 after it.  With
+// the combine, decode windows whose shapes have an instantiation run the two
+// stages and the combine as one launch; otherwise one launch per stage, then
+// the combine's own.
 int expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
                const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm, const int32_t* group_slot,
                uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws, uint64_t ws_bytes, int32_t stages,
@@ -405,21 +405,12 @@ int expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t 
   // groups averaging >= kGemmMinRows rows: grouped GEMM over 256-row chunks;
   // otherwise weight streaming over 16-row tiles (the grouping kernels wrote
   // the matching work list)
-  if (stages == 3 && !moe::use_gemm(*d)) {
-    if (comb && moe::ffn_dec_fusable(*d, true))
-      return hip_status(moe::launch_ffn_dec_fused(*d, x, g, h, y_rows, dev_status, ws, n_cu, e0, e1, st, inv_perm,
-                                                  topk_w, shared_sigma, y),
-                        "expert FFN + combine launch");
-    if (moe::ffn_dec_fusable(*d, false)) {
-      if ((r = hip_status(moe::launch_ffn_dec_fused(*d, x, g, h, y_rows, dev_status, ws, n_cu, e0, e1, st, nullptr,
-                                                    nullptr, nullptr, nullptr),
-                          "expert FFN launch")))
-        return r;
-      return comb ? hip_status(moe::launch_combine(*d, y_rows, inv_perm, topk_w, shared_sigma, y, st),
-                               "combine launch")
-                  : ok();
-    }
-  }
+  // moe_expert_ffn_combine on decode windows: the FFN's two stages and the
+  // combine in one launch where the shapes have an instantiation
+  if (comb && stages == 3 && !moe::use_gemm(*d) && moe::ffn_dec_fusable(*d, true))
+    return hip_status(moe::launch_ffn_dec_fused(*d, x, g, h, y_rows, dev_status, ws, n_cu, e0, e1, st, inv_perm,
+                                                topk_w, shared_sigma, y),
+                      "expert FFN + combine launch");
   if (moe::use_gemm(*d))
     r = hip_status(moe::launch_ffn_gemm(*d, x, g, perm, h, y_rows, ws, n_cu, stages, e0, e1, st), "expert FFN launch");
   else

@@ -347,22 +347,17 @@ __device__ inline void store_bf16(uint16_t* rows, int bytes, int idx, uint16_t v
 // S5 for the column blocks marked in mask (bit b: columns [b cols, b cols +
 // cols)), for every token, by the whole workgroup, in exactly k_combine's
 // arithmetic: y = bf16(sum_j w_j Y[inv(t, j)] + sigma Y_sh), fp32 fused
-// multiply-adds in slot order, then the shared row.  inv_perm, w and sigma
-// (written before the launch) are staged in LDS once; the Y rows (written by
-// other workgroups of this launch) are read with device-coherent loads, all
-// of a column pair's at once.  Requires T k <= kFusedCombineMaxT *
-// kFusedCombineMaxK.
+// multiply-adds in slot order, then the shared row.  pw / sg: inv_perm, w
+// and sigma (written before the launch), staged in LDS at the launch's
+// start; the Y rows (written by other workgroups of this launch) are read
+// with device-coherent loads, all of a column pair's at once.
 __device__ inline void combine_blocks(const uint16_t* __restrict__ yr, const FusedCtx& fc, const uint32_t* mask,
-                                      int2* pw, float* sg) {
+                                      const int2* pw, const float* sg) {
   const int nb = fc.H / fc.cols, nw = (nb + 31) / 32;
   bool any = false;
   for (int i = 0; i < nw; i++) any |= mask[i] != 0;
   if (!any) return;
   const int Tk = fc.T * fc.k;
-  for (int i = threadIdx.x; i < Tk; i += blockDim.x)
-    pw[i] = make_int2(fc.inv_perm[i], __float_as_int(fc.w[i]));
-  for (int i = threadIdx.x; i < fc.T; i += blockDim.x) sg[i] = fc.sigma[i];
-  __syncthreads();
   const int pairs = fc.cols / 2;
   for (int wi = 0; wi < nw; wi++) {
     uint32_t m = mask[wi];
@@ -678,10 +673,30 @@ __global__ __launch_bounds__(256) void k_ffn_dec_fused(DecArgs ag, DecArgs ad, c
   const GuWalk gw = gu_walk(n_gu, G, b);
   const Desc gd0 = load_desc<true>(ag, gw.first, c, tiles, tile_tok);
   const Desc dd0 = load_desc<false>(ad, G - 1 - b, c, tiles, tile_tok);
+  // (combine) this thread's share of inv_perm, w and sigma, staged in LDS
+  // after the starts: off the launch's critical tail
+  constexpr int kPwPer = kFusedCombineMaxT * kFusedCombineMaxK / 256;
+  int2 cpw[COMB ? kPwPer : 1];
+  float csg = 0.f;
+  const int Tk = fc.T * fc.k;
+  if (COMB) {
+#pragma unroll
+    for (int r = 0; r < kPwPer; r++) {
+      const int i = min((int)threadIdx.x + 256 * r, Tk - 1);
+      cpw[r] = make_int2(fc.inv_perm[i], __float_as_int(fc.w[i]));
+    }
+    csg = fc.sigma[min((int)threadIdx.x, fc.T - 1)];
+  }
   Start<true, GSK, GS, GU, GFS, false> sg;
   stage_start<true, GSK, GS, GU, GFS, false, true>(sg, ag, gd0, gw.limit, gw.stride, tiles, tile_tok, pool, x);
   Start<false, DSK, DS, DU, DFS, false> sd;
   stage_start<false, DSK, DS, DU, DFS, false, false>(sd, ad, dd0, n_dn, G, tiles, tile_tok, pool, h);
+  if (COMB) {
+#pragma unroll
+    for (int r = 0; r < kPwPer; r++)
+      if ((int)threadIdx.x + 256 * r < Tk) comb_pw[threadIdx.x + 256 * r] = cpw[r];
+    if ((int)threadIdx.x < fc.T) comb_sg[threadIdx.x] = csg;
+  }
   stage_walk<true, GSK, GS, GU, GFS, false, Policy<kAuxPlain, kAuxDevice, false, false>>(
       sg, ag, gw.stride, gw.limit, tiles, tile_tok, pool, x, h, &fc, reinterpret_cast<f32x4(*)[GNS][64]>(red));
   // every wavefront that stored h rows: once its stores are complete, one

@@ -104,6 +104,31 @@ def _run_one_layer(B, wl, s, l):
     B.moe_combine(d, buf.y_rows, buf.inv_perm, buf.w, buf.sigma, buf.y)
 
 
+def _one_launch_matches(B, wl, s, l, snap):
+    """The same layer through moe_route_group + moe_expert_ffn_combine (gate/up,
+    down and combine in one launch) gives the split path's h, Y rows and y bit
+    for bit."""
+    d, buf = wl.dims, wl.buf
+    x = wl.x[wl.input_index(s), l]
+    wr = wl.wr[l] if wl.wr is not None else None
+    lg = None if wl.wr is not None else wl.logits[wl.input_index(s), l]
+    for t in (buf.h, buf.y_rows, buf.y):
+        t.fill_(3.0)
+    B.moe_route_group(d, l, x, wr, lg, wl.wsg[l], buf.logits if wr is not None else None, buf.ids, buf.w, buf.sigma,
+                      wl.slot_table, wl.n_slots, buf.offsets, buf.perm, buf.inv_perm, buf.group_slot, buf.status,
+                      buf.ws)
+    wl.ffn_combine(x)
+    torch.cuda.synchronize()
+    assert int(buf.status.item()) == 0
+    off_e = int(buf.offsets[wl.cfg.E].item())
+    Tk = wl.cfg.T * wl.cfg.k
+    live = torch.cat([torch.arange(off_e), torch.arange(Tk, Tk + wl.cfg.T)]).cuda()
+    for name in ("h", "y_rows"):
+        a, b = getattr(buf, name), getattr(snap, name)
+        assert torch.equal(a.view(torch.int16)[live], b.view(torch.int16)[live]), "one launch: %s differs" % name
+    assert torch.equal(buf.y.view(torch.int16), snap.y.view(torch.int16)), "one launch: y differs"
+
+
 def _graph_replays_match_eager(wl, step):
     """Capture one step, replay it 3 times with eager work in between, and check
     each replay's last-layer output against the eager run bit for bit."""
@@ -126,9 +151,13 @@ def _graph_replays_match_eager(wl, step):
 @pytest.mark.timeout(600)
 def test_decode48_full_size(B, hostgen):
     cfg = CONFIGS[2]
-    wl, _ = _run_and_compare(B, cfg, 2, [(0, 0), (0, 23), (0, 47)], list(range(cfg.T)), hostgen)
-    say("[gpu]   decode48: graph replay vs eager")
-    _graph_replays_match_eager(wl, 0)
+    wl, snaps = _run_and_compare(B, cfg, 2, [(0, 0), (0, 23), (0, 47)], list(range(cfg.T)), hostgen)
+    say("[gpu]   decode48: one launch (FFN + combine) vs the split path")
+    _one_launch_matches(B, wl, 0, 47, snaps[(0, 47)])
+    for mode in ("split", "one-launch"):
+        say("[gpu]   decode48: graph replay vs eager (%s)" % mode)
+        wl.ffn_mode = mode
+        _graph_replays_match_eager(wl, 0)
     del wl
     torch.cuda.empty_cache()
 
@@ -136,7 +165,9 @@ def test_decode48_full_size(B, hostgen):
 @pytest.mark.timeout(900)
 def test_decode43x64_full_size(B, hostgen):
     cfg = CONFIGS[3]
-    wl, _ = _run_and_compare(B, cfg, 64, [(0, 0), (17, 21), (63, 42)], [0, 7, 15], hostgen)
+    wl, snaps = _run_and_compare(B, cfg, 64, [(0, 0), (17, 21), (63, 42)], [0, 7, 15], hostgen)
+    say("[gpu]   decode43x64: one launch (FFN + combine) vs the split path")
+    _one_launch_matches(B, wl, 63, 42, snaps[(63, 42)])
     del wl
     torch.cuda.empty_cache()
 

@@ -1,12 +1,11 @@
-"""GPU tests of the one-launch decode FFN (both stages, optionally the combine,
-in one persistent launch whose down items wait inside the launch for the
-gate/up items that write their h rows; [FreeToken] 3.5, one step's control
-flow on the device).
+"""GPU tests of the one-launch decode FFN (moe_expert_ffn_combine: both stages
+and the combine in one persistent launch whose down items wait inside the
+launch for the gate/up items that write their h rows; [FreeToken] 3.5, one
+step's control flow on the device).
 
-- moe_expert_ffn (one launch) against its two stages launched apart
-  (moe_expert_ffn_stages 1 then 2): h and Y rows bit for bit;
-- moe_expert_ffn_combine against moe_expert_ffn + moe_combine: h, Y and y bit
-  for bit, and y against the oracle;
+- moe_expert_ffn_combine against the two stages launched apart
+  (moe_expert_ffn_stages 1 then 2) and moe_combine: h, Y and y bit for bit,
+  and y against the oracle;
 - a second call with the same grouping (the launch resets its counters);
 - many more items than workgroups (each walks several, and several down
   items wait);
@@ -151,7 +150,7 @@ def test_one_launch_matches_split_stages_and_combine(B, hostgen, name):
         c.ffn(B)
         c.combine(B)
         torch.cuda.synchronize()
-        _same(c.outputs(), want, "moe_expert_ffn, call %d" % rep)
+        _same(c.outputs(), want, "moe_expert_ffn + moe_combine, call %d" % rep)
         c.scramble()
         c.ffn(B, combine=True)
         torch.cuda.synchronize()
@@ -232,14 +231,14 @@ def test_one_launch_wait_timeout_is_flagged_and_recovers(B, hostgen):
     try:
         lib.moe_debug_set_fused_wait(8, 1)   # the tile targets are never reached; 8 polls each
         c.buf.status.zero_()
-        c.ffn(B)
+        c.ffn(B, combine=True)
         torch.cuda.synchronize()
         assert int(c.buf.status.item()) & B.MOE_DEV_SYNC_TIMEOUT
     finally:
         lib.moe_debug_set_fused_wait(-1, 0)
     c.buf.status.zero_()
     c.scramble()
-    c.ffn(B)
+    c.ffn(B, combine=True)
     torch.cuda.synchronize()
     assert int(c.buf.status.item()) == 0
     got = c.outputs()[:2]

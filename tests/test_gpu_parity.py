@@ -278,8 +278,11 @@ def test_group_matches_oracle_on_drawn_ids(B, T, k, E, zs):
 # (T, E, k): the radix select with 8, 2 and 16 keys per lane, k above 64 (two
 # entries per lane to rank), k above 128 (the one-winner-per-round path), and
 # the fused decode kernel (T <= 16, T k <= 256)
+# (4, 512, 10), (3, 1024, 8), (2, 300, 16) and (8, 128, 4) run moe_route_group's
+# top-k over several wavefronts per token (merged by rank; 300 experts split in
+# parts of 75, 16 x 4 candidates filling one wavefront)
 @pytest.mark.parametrize("T,E,k", [(64, 512, 10), (40, 100, 70), (8, 512, 200), (4, 512, 10), (16, 256, 6),
-                                   (33, 1024, 8)])
+                                   (33, 1024, 8), (3, 1024, 8), (2, 300, 16), (8, 128, 4)])
 def test_topk_with_ties_matches_oracle(B, T, E, k):
     """Drawn logits on a half-unit grid tie everywhere; the winners and their
     slot order (logit descending, lower expert index first among equal
@@ -312,9 +315,12 @@ def test_topk_with_ties_matches_oracle(B, T, E, k):
                           buf.perm, buf.inv_perm, buf.group_slot, buf.status, buf.ws)
         torch.cuda.synchronize()
         assert np.array_equal(buf.ids.cpu().numpy(), want_ids)
+        assert np.max(np.abs(buf.w.cpu().numpy().astype(np.float64) - want_w)) <= 1e-6
         assert int(buf.status.item()) == 0
         g = O.group(want_ids, E)
         assert np.array_equal(buf.perm.cpu().numpy(), g.perm)
+        assert np.array_equal(buf.inv_perm.cpu().numpy(), g.inv_perm)
+        assert np.array_equal(buf.offsets.cpu().numpy(), g.offsets)
 
 
 def _late_logits(T, E, k, late, seed):
