@@ -27,11 +27,18 @@ Extra objects on the line:
                 tokens/s and their own roofline; for decode43x64 also the p50
                 and p90 of the 64 step times and the expert-weight GB/s of a
                 step.  --no-extra skips them.
+  probes        (default workload only) measured peaks beside the spec ones:
+                the stream-read probe's best HBM read rate and the dense MFMA
+                rate of back-to-back bf16, fp8 x fp4 and fp8 MFMAs.
   cpu_baseline  the CPU oracle (oracle/, fp64 numpy) on a bounded sample of
                 the same workload, scaled to tokens/s: on every host core this
                 process may use (cores), and on one thread (one_thread).
 
---copy-calibration BYTES runs only a plain device copy of BYTES bytes five
+The streamed workload adds "h2d" (the copy rate and the overlap fraction of
+copy and compute) and "serial" (the same layers with one slot, each copy then
+its compute on one stream: the reference without the second buffer).
+
+--probes runs only the probes.  --copy-calibration BYTES runs only a plain device copy of BYTES bytes five
 times (the reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters).
 """
 from __future__ import annotations
@@ -81,6 +88,8 @@ def parse():
                     help="decode48: skip the prefill8192 and decode43x64 measurements added to its line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--probes", action="store_true",
+                    help="run only the HBM-read and MFMA-loop probes and print their line")
     return ap.parse_args()
 
 
@@ -634,6 +643,23 @@ def run_staged(cfg, args, B, DevGen):
     tokens_per_s = cfg.T / (ms_per_step / 1e3)
     log("%.2f ms/step, %.1f tokens/s" % (ms_per_step, tokens_per_s))
 
+    # the serial reference: one slot, copy then compute on one stream
+    def serial_step():
+        with torch.cuda.stream(comp_s):
+            st.run_serial(lambda l: wl.x[0, l], lambda l: wl.wsg[l], lambda l: wl.logits[0, l])
+
+    serial_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        serial_step()
+    torch.cuda.synchronize()
+    serial_ms = (time.perf_counter() - t0) * 1e3 / K
+    serial = {"ms_per_step": serial_ms, "tokens_per_s": cfg.T / (serial_ms / 1e3),
+              "ring_speedup": serial_ms / ms_per_step,
+              "loss_without_second_buffer": ms_per_step / serial_ms - 1.0}
+    log("serial (no ring): %s" % serial)
+
     # copy and compute intervals of one more step, on a common time base
     ev = []
     step(ev)
@@ -697,9 +723,51 @@ def run_staged(cfg, args, B, DevGen):
                    "k": cfg.k, "shared_experts": 1, "routing": "zipf s=%g" % cfg.zipf_s,
                    "staging": "pinned host blobs through a two-slot device ring", "graphs": False,
                    "parallelism": "single GPU"},
-        "roofline": roof, "h2d": h2d, "cpu_baseline": cpu,
+        "roofline": roof, "h2d": h2d, "serial": serial, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def measure_probes(B):
+    """Measured peaks beside the spec ones: the best HBM read rate of the
+    stream-read probe over launch shapes, and the dense MFMA rate of
+    back-to-back bf16, fp8 x fp4 and fp8 MFMAs (moe_probe_*)."""
+    import torch
+    n = 8 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1 << 20, dtype=torch.float32, device="cuda")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    read = {}
+    for grid in (1024, 2048, 4096, 8192):
+        ms = timed(lambda: B.moe_probe_hbm_read(buf, n, grid, sink), 5)
+        read[grid] = n / (ms * 1e-3) / 1e9
+    best = max(read, key=read.get)
+    out = {"hbm_read_gb_s": read[best], "hbm_read_grid": best, "hbm_read_bytes": n,
+           "hbm_read_frac_of_spec": read[best] / HBM_PEAK_GBS}
+    del buf
+    iters = 4000
+    for kind, name, flop, spec in ((0, "mfma_bf16", 32768, BF16_PEAK_TFLOPS), (1, "mfma_f8f4", 65536, FP8_PEAK_TFLOPS),
+                                   (2, "mfma_f8", 65536, FP8_PEAK_TFLOPS)):
+        best_t = 0.0
+        for grid in (1024, 2048):
+            ms = timed(lambda: B.moe_probe_mfma(kind, grid, iters, sink), 3)
+            best_t = max(best_t, grid * 4 * iters * 4 * flop / (ms * 1e-3) / 1e12)
+        out[name + "_tflops"] = best_t
+        out[name + "_frac_of_spec"] = best_t / spec
+    with open(os.path.join(CSRC, "probes.hip"), "rb") as f:
+        out["kernel_source_sha256_16"] = hashlib.sha256(f.read()).hexdigest()[:16]
+    log("probes: %s" % out)
+    return out
 
 
 def main():
@@ -724,6 +792,9 @@ def main():
     from moe_expert_ffn_top_amd import binding as B
     from synth import DevGen, config_by_name
 
+    if args.probes:
+        print(json.dumps({"probes": measure_probes(B)}), flush=True)
+        return
     cfg = config_by_name(args.config)
     if cfg.staged:
         run_staged(cfg, args, B, DevGen)
@@ -742,6 +813,8 @@ def main():
         torch.cuda.empty_cache()
         dc = measure_workload(config_by_name("decode43x64"), args, B, DevGen, 64, 3, ffn=args.ffn, per_step=True)
         extra["decode43x64"] = summarize(dc)
+        torch.cuda.empty_cache()
+        extra["probes"] = measure_probes(B)
         torch.cuda.empty_cache()
 
     cpu = None

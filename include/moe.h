@@ -529,6 +529,30 @@ int moe_ring_release(moe_ring* ring, int32_t slot, moe_stream_t compute);
 int moe_ring_slot_ptr(moe_ring* ring, int32_t slot, void** out);
 int moe_ring_destroy(moe_ring* ring);
 
+/* ---- measurement probes ------------------------------------------------------
+ * Not part of the layer.  Two kernels that measure what this GPU reaches, so a
+ * roofline fraction against a published peak can be read beside the measured
+ * one ([Strata] "PCIe 搬运怎样与计算重叠？": a claimed rate needs a trace on
+ * the device).  Both only enqueue on `stream`; time them with events on it.
+ *
+ * moe_probe_hbm_read: reads bytes of buf once, 1 KiB per wavefront
+ *   instruction, 8 KiB per wavefront per loop trip, over `grid` workgroups of
+ *   256 threads.  buf: device, 16-byte aligned, bytes a positive multiple of
+ *   8192.  sink: one device uint32 that is written only if the folded words
+ *   equal a constant (a guard against the loads being dropped), so its content
+ *   is unchanged for ordinary data.  MOE_ERR_ARG / MOE_ERR_ALIGN on bad input.
+ * moe_probe_mfma: `grid` workgroups of 4 wavefronts, each wavefront issuing
+ *   `iters` x 4 back-to-back MFMAs on register operands.  kind 0:
+ *   v_mfma_f32_32x32x16_bf16 (32768 flop each); kind 1: the scaled
+ *   16x16x128 MFMA with E4M3 A and E2M1 B (65536 flop each); kind 2: the same
+ *   with E4M3 on both sides.  sink: device float[grid * 256], each lane's sum
+ *   of its four accumulators.  grid in [1, 2^16], iters in [1, 2^20].
+ */
+int moe_probe_hbm_read(const void* buf, uint64_t bytes, int32_t grid,
+                       uint32_t* sink, moe_stream_t stream);
+int moe_probe_mfma(int32_t kind, int32_t grid, int32_t iters, float* sink,
+                   moe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

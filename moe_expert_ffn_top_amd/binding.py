@@ -43,7 +43,7 @@ EXPORTED = ("moe_status_string", "moe_last_error", "moe_version", "moe_blob_layo
             "moe_mx_workspace_bytes", "moe_quantize_mxfp8", "moe_expert_ffn_mx", "moe_expert_ffn_mx_noalloc",
             "moe_combine",
             "moe_ring_create", "moe_stage_h2d", "moe_ring_acquire", "moe_ring_release", "moe_ring_slot_ptr",
-            "moe_ring_destroy")
+            "moe_ring_destroy", "moe_probe_hbm_read", "moe_probe_mfma")
 
 
 class Dims(ctypes.Structure):
@@ -112,6 +112,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.moe_ring_release.argtypes = [_vp, _i32, _vp]
     lib.moe_ring_slot_ptr.argtypes = [_vp, _i32, ctypes.POINTER(_vp)]
     lib.moe_ring_destroy.argtypes = [_vp]
+    lib.moe_probe_hbm_read.argtypes = [_vp, _u64, _i32, _vp, _vp]
+    lib.moe_probe_mfma.argtypes = [_i32, _i32, _i32, _vp, _vp]
     return lib
 
 
@@ -374,6 +376,14 @@ def moe_ring_slot_ptr(ring: int, slot: int) -> int:
 
 def moe_ring_destroy(ring: int) -> None:
     _check(_lib.moe_ring_destroy(ring), "moe_ring_destroy")
+
+
+def moe_probe_hbm_read(buf, nbytes: int, grid: int, sink, stream=None) -> None:
+    _check(_lib.moe_probe_hbm_read(_p(buf), nbytes, grid, _p(sink), _s(stream)), "moe_probe_hbm_read")
+
+
+def moe_probe_mfma(kind: int, grid: int, iters: int, sink, stream=None) -> None:
+    _check(_lib.moe_probe_mfma(kind, grid, iters, _p(sink), _s(stream)), "moe_probe_mfma")
 
 
 def raw_status(fn_name: str, *args) -> int:

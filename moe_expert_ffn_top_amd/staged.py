@@ -89,3 +89,24 @@ class StagedLayers:
                 after_layer(l)
             if l + 2 < self.L:
                 stage(l + 2)
+
+    def run_serial(self, x_of: Callable[[int], torch.Tensor], wsg_of: Callable[[int], torch.Tensor],
+                   logits_of: Callable[[int], Optional[torch.Tensor]]) -> None:
+        """The reference without the second buffer: one slot, and on the
+        compute stream each layer's copy, then its compute, so no copy overlaps
+        any compute ([FreeToken] 5.3 measures what the second buffer buys).
+        The ring is not used."""
+        d, buf = self.dims, self.buf
+        cs = self.compute_stream
+        pool = self.slots[0]
+        for l in range(self.L):
+            src = self.host[l * self.layer_bytes:(l + 1) * self.layer_bytes]
+            with torch.cuda.stream(cs):
+                pool.copy_(src, non_blocking=True)
+            x = x_of(l)
+            B.moe_route(d, x, None, logits_of(l), wsg_of(l), None, buf.ids, buf.w, buf.sigma, cs)
+            B.moe_group(d, l, buf.ids, self.slot_table, d.E + 1, buf.offsets, buf.perm, buf.inv_perm,
+                        buf.group_slot, buf.status, buf.ws, stream=cs)
+            B.moe_expert_ffn(d, x, pool, self.layer_bytes, self.layout, buf.offsets, buf.perm, buf.group_slot,
+                             buf.h, buf.y_rows, buf.status, buf.ws, stream=cs)
+            B.moe_combine(d, buf.y_rows, buf.inv_perm, buf.w, buf.sigma, buf.y, cs)

@@ -229,3 +229,17 @@ def test_noalloc_refuses_dims_beyond_its_static_scratch(B):
                       p, p, p, p, p, p, p, ws_bytes, 3, None)
     assert rc == B.MOE_ERR_WORKSPACE
     assert b"static" in B._lib.moe_last_error()
+
+
+def test_probe_validation(B):
+    """The measurement probes refuse bad arguments before enqueueing anything."""
+    fake = 1 << 20
+    assert B.raw_status("moe_probe_hbm_read", None, 8192, 64, fake, None) == B.MOE_ERR_ARG
+    assert B.raw_status("moe_probe_hbm_read", fake, 8192 + 1024, 64, fake, None) == B.MOE_ERR_ARG
+    assert B.raw_status("moe_probe_hbm_read", fake, 0, 64, fake, None) == B.MOE_ERR_ARG
+    assert B.raw_status("moe_probe_hbm_read", fake + 4, 8192, 64, fake, None) == B.MOE_ERR_ALIGN
+    assert B.raw_status("moe_probe_hbm_read", fake, 8192, 0, fake, None) == B.MOE_ERR_ARG
+    assert B.raw_status("moe_probe_mfma", 3, 1, 1, fake, None) == B.MOE_ERR_ARG
+    assert B.raw_status("moe_probe_mfma", 0, 0, 1, fake, None) == B.MOE_ERR_ARG
+    assert B.raw_status("moe_probe_mfma", 0, 1, 0, fake, None) == B.MOE_ERR_ARG
+    assert B.raw_status("moe_probe_mfma", 1, 1, 1, None, None) == B.MOE_ERR_ARG
