@@ -529,6 +529,16 @@ int moe_ring_release(moe_ring* ring, int32_t slot, moe_stream_t compute);
 int moe_ring_slot_ptr(moe_ring* ring, int32_t slot, void** out);
 int moe_ring_destroy(moe_ring* ring);
 
+/* ---- test hook ----------------------------------------------------------------
+ * For the tests of moe_expert_ffn_combine's bounded wait only: sets the poll
+ * limit of that launch's in-kernel waits and a count added to every tile
+ * target (a target that is never reached makes each wait give up after the
+ * limit, set MOE_DEV_SYNC_TIMEOUT, and let every wavefront end).  (-1, 0)
+ * restores the defaults.  Applies to launches enqueued afterwards, from every
+ * thread of the process; not for production use.
+ */
+void moe_debug_set_fused_wait(int spin_limit, int extra_target);
+
 /* ---- measurement probes ------------------------------------------------------
  * Not part of the layer.  Two kernels that measure what this GPU reaches, so a
  * roofline fraction against a published peak can be read beside the measured

@@ -43,7 +43,7 @@ EXPORTED = ("moe_status_string", "moe_last_error", "moe_version", "moe_blob_layo
             "moe_mx_workspace_bytes", "moe_quantize_mxfp8", "moe_expert_ffn_mx", "moe_expert_ffn_mx_noalloc",
             "moe_combine",
             "moe_ring_create", "moe_stage_h2d", "moe_ring_acquire", "moe_ring_release", "moe_ring_slot_ptr",
-            "moe_ring_destroy", "moe_probe_hbm_read", "moe_probe_mfma")
+            "moe_ring_destroy", "moe_probe_hbm_read", "moe_probe_mfma", "moe_debug_set_fused_wait")
 
 
 class Dims(ctypes.Structure):
@@ -114,6 +114,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.moe_ring_destroy.argtypes = [_vp]
     lib.moe_probe_hbm_read.argtypes = [_vp, _u64, _i32, _vp, _vp]
     lib.moe_probe_mfma.argtypes = [_i32, _i32, _i32, _vp, _vp]
+    lib.moe_debug_set_fused_wait.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.moe_debug_set_fused_wait.restype = None
     return lib
 
 

@@ -970,7 +970,7 @@ hipError_t launch_ffn_dec_fused(const moe_dims& d, const uint16_t* x, const FfnG
 
 }  // namespace moe
 
-// Test hook (not part of the documented interface): the fused FFN launch's
+// Test hook (declared in include/moe.h for the tests only): the fused FFN launch's
 // poll limit and a count added to its tile targets; (-1, 0) restores the
 // defaults.  Affects launches enqueued afterwards, from every thread.
 extern "C" void moe_debug_set_fused_wait(int spin_limit, int extra_target) {
