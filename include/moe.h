@@ -540,10 +540,10 @@ int moe_ring_destroy(moe_ring* ring);
 void moe_debug_set_fused_wait(int spin_limit, int extra_target);
 
 /* ---- measurement probes ------------------------------------------------------
- * Not part of the layer.  Two kernels that measure what this GPU reaches, so a
+ * Not part of the layer.  Kernels that measure what this GPU reaches, so a
  * roofline fraction against a published peak can be read beside the measured
  * one ([Strata] "PCIe 搬运怎样与计算重叠？": a claimed rate needs a trace on
- * the device).  Both only enqueue on `stream`; time them with events on it.
+ * the device).  Each only enqueues on `stream`; time them with events on it.
  *
  * moe_probe_hbm_read: reads bytes of buf once, 1 KiB per wavefront
  *   instruction, 8 KiB per wavefront per loop trip, over `grid` workgroups of
@@ -557,11 +557,27 @@ void moe_debug_set_fused_wait(int spin_limit, int extra_target);
  *   16x16x128 MFMA with E4M3 A and E2M1 B (65536 flop each); kind 2: the same
  *   with E4M3 on both sides.  sink: device float[grid * 256], each lane's sum
  *   of its four accumulators.  grid in [1, 2^16], iters in [1, 2^20].
+ * moe_probe_scaled_mfma: the arithmetic of the MX grouped GEMM's instruction
+ *   ([FreeToken] "FreeToken 阅读笔记" §2.1: the experts are MXFP4), one
+ *   v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 A, E2M1 B, C = 0) per wavefront,
+ *   n wavefronts; split = 1 issues the gate/up pair instead (A cut into its
+ *   codes of magnitude >= 2 and the rest, two MFMAs into one accumulator).
+ *   Operands lane by lane, all device int32 arrays, lane l of wavefront w at
+ *   index 64 w + l: a [n*64][8] (the lane's 32 E4M3 bytes, little-endian),
+ *   b [n*64][4] (32 E2M1 nibbles, low nibble first), sa, sb [n*64] (E8M0 scale
+ *   in the low byte).  Lane (i, j) = l % 16, l / 16 holds A row i, K 16 j ..
+ *   16 j + 15 and 64 + 16 j .. 64 + 16 j + 15; B column i, K 32 j .. 32 j +
+ *   31; the scales of row / column i, K block j (32 j .. 32 j + 31).
+ *   d [n*64][4]: D[4 (l / 16) + e][l % 16] at lane l, element e.  n in
+ *   [1, 2^16]; split 0 or 1; MOE_ERR_ARG otherwise.
  */
 int moe_probe_hbm_read(const void* buf, uint64_t bytes, int32_t grid,
                        uint32_t* sink, moe_stream_t stream);
 int moe_probe_mfma(int32_t kind, int32_t grid, int32_t iters, float* sink,
                    moe_stream_t stream);
+int moe_probe_scaled_mfma(const int32_t* a, const int32_t* b,
+                          const int32_t* sa, const int32_t* sb, int32_t n,
+                          int32_t split, float* d, moe_stream_t stream);
 
 #ifdef __cplusplus
 }

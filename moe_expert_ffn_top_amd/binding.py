@@ -43,7 +43,8 @@ EXPORTED = ("moe_status_string", "moe_last_error", "moe_version", "moe_blob_layo
             "moe_mx_workspace_bytes", "moe_quantize_mxfp8", "moe_expert_ffn_mx", "moe_expert_ffn_mx_noalloc",
             "moe_combine",
             "moe_ring_create", "moe_stage_h2d", "moe_ring_acquire", "moe_ring_release", "moe_ring_slot_ptr",
-            "moe_ring_destroy", "moe_probe_hbm_read", "moe_probe_mfma", "moe_debug_set_fused_wait")
+            "moe_ring_destroy", "moe_probe_hbm_read", "moe_probe_mfma", "moe_probe_scaled_mfma",
+            "moe_debug_set_fused_wait")
 
 
 class Dims(ctypes.Structure):
@@ -114,6 +115,7 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.moe_ring_destroy.argtypes = [_vp]
     lib.moe_probe_hbm_read.argtypes = [_vp, _u64, _i32, _vp, _vp]
     lib.moe_probe_mfma.argtypes = [_i32, _i32, _i32, _vp, _vp]
+    lib.moe_probe_scaled_mfma.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp]
     lib.moe_debug_set_fused_wait.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.moe_debug_set_fused_wait.restype = None
     return lib
@@ -386,6 +388,11 @@ def moe_probe_hbm_read(buf, nbytes: int, grid: int, sink, stream=None) -> None:
 
 def moe_probe_mfma(kind: int, grid: int, iters: int, sink, stream=None) -> None:
     _check(_lib.moe_probe_mfma(kind, grid, iters, _p(sink), _s(stream)), "moe_probe_mfma")
+
+
+def moe_probe_scaled_mfma(a, b, sa, sb, n: int, split: int, d, stream=None) -> None:
+    _check(_lib.moe_probe_scaled_mfma(_p(a), _p(b), _p(sa), _p(sb), n, split, _p(d), _s(stream)),
+           "moe_probe_scaled_mfma")
 
 
 def raw_status(fn_name: str, *args) -> int:

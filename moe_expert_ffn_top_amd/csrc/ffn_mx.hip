@@ -33,8 +33,13 @@
 //            instead of four 4-byte ones).  Lane (r, q) shifts byte q of its
 //            dword down (the MFMA reads byte 0).
 //    - Four consumer wavefronts read fragments (64 lanes x 16 contiguous bytes,
-//      conflict-free) and issue one scaled MFMA per (16-row block, 16-column
-//      block) per step.
+//      conflict-free): a step's eight B fragments first, then row block by row
+//      block its A fragment, and issue two scaled MFMAs per (16-row block,
+//      16-column block) per step: the instruction truncates small products
+//      inside each run of 8 (split_e4m3), so the A codes are cut into those of
+//      magnitude >= 2 and the rest and each part is summed whole.  g, u and
+//      the down projection are then the exact sums up to fp32 addition, as the
+//      roundings that follow (h to bf16 and MXFP8, Y to bf16) require.
 //  - Gate/up epilogue: h = bf16(silu(g) u), as in the bf16 path, and h quantised
 //    to MXFP8.  A 32-unit block of one row lies in two 16-column blocks of one
 //    16-lane row, so its amax is an in-lane max plus four DPP max steps.  It
@@ -67,7 +72,6 @@ constexpr int LDS_BYTES = ASG_OFF + 2 * ASG_SLOT;  // 132608
 // epilogue tiles (in the buffers, free after the last step)
 constexpr int QSTR = 80;  // bytes per row of the code tile: rows 4 apart land 16 banks apart
 
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
@@ -430,27 +434,36 @@ __global__ __launch_bounds__(XT) void k_ffn_mx(MxArgs a, const int4* __restrict_
         int bi = 0;
         for (int s = 0; s < a.nk; s++) {
           const uint8_t* bb = smem + bi * BUF_BYTES;
-          i32x8 fa[NRB];
-          int sa[NRB];
+          i32x8 fb[8];
+          int sb[8];
+#pragma unroll
+          for (int cb = 0; cb < 8; cb++) {
+            const i32x4 f = *reinterpret_cast<const i32x4*>(bb + B_OFF + cb * 1024 + 16 * lane);
+            fb[cb] = i32x8{f.x, f.y, f.z, f.w, 0, 0, 0, 0};
+            sb[cb] = (int)(*reinterpret_cast<const uint32_t*>(bb + BS_OFF + (16 * cb + r) * 4) >> (8 * q));
+          }
 #pragma unroll
           for (int rb = 0; rb < NRB; rb++) {
             const int rbk = 4 * rb + wm;
             const uint8_t* rowp = bb + A_OFF + rbk * 2048 + 128 * r;
             const i32x4 lo = *reinterpret_cast<const i32x4*>(rowp + 16 * (q ^ (r & 7)));
             const i32x4 hi = *reinterpret_cast<const i32x4*>(rowp + 16 * ((4 + q) ^ (r & 7)));
-            fa[rb] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            sa[rb] = (int)(*reinterpret_cast<const uint32_t*>(smem + ASG_OFF + ((s >> 2) & 1) * ASG_SLOT +
-                                                              (16 * rbk + r) * 16 + 4 * (s & 3)) >> (8 * q));
-          }
+            const i32x8 fa = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            const int sa = (int)(*reinterpret_cast<const uint32_t*>(smem + ASG_OFF + ((s >> 2) & 1) * ASG_SLOT +
+                                                                   (16 * rbk + r) * 16 + 4 * (s & 3)) >> (8 * q));
+            // both products feed a rounding that the oracle takes on the exact
+            // sum (h: bf16 then MXFP8; Y: bf16), so each is summed whole: two
+            // MFMAs, the big and the small codes of A
+            i32x8 big, small;
+            split_e4m3(fa, big, small);
 #pragma unroll
-          for (int cb = 0; cb < 8; cb++) {
-            const i32x4 f = *reinterpret_cast<const i32x4*>(bb + B_OFF + cb * 1024 + 16 * lane);
-            const i32x8 fb = i32x8{f.x, f.y, f.z, f.w, 0, 0, 0, 0};
-            const int sb = (int)(*reinterpret_cast<const uint32_t*>(bb + BS_OFF + (16 * cb + r) * 4) >> (8 * q));
-#pragma unroll
-            for (int rb = 0; rb < NRB; rb++)
+            for (int cb = 0; cb < 8; cb++)
               acc[rb][cb] =
-                  __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[rb], fb, acc[rb][cb], 0, 4, 0, sa[rb], 0, sb);
+                  __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(big, fb[cb], acc[rb][cb], 0, 4, 0, sa, 0, sb[cb]);
+#pragma unroll
+            for (int cb = 0; cb < 8; cb++)
+              acc[rb][cb] =
+                  __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(small, fb[cb], acc[rb][cb], 0, 4, 0, sa, 0, sb[cb]);
           }
           bi = bi == 2 ? 0 : bi + 1;
           __syncthreads();

@@ -13,6 +13,12 @@
 // grouped GEMM), kind 1 = the scaled 16x16x128 MFMA with fp8 (E4M3) A and
 // fp4 (E2M1) B operands (what the MX grouped GEMM issues), kind 2 = the same
 // with fp8 on both sides.
+//
+// k_probe_scaled_mfma runs one v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 A,
+// E2M1 B, C = 0) per wavefront on operands given lane by lane, or, with split,
+// the pair the MX grouped GEMM issues for gate/up (split_e4m3: big codes, then
+// small codes into the same accumulator): the instruction's own arithmetic,
+// held against exact sums by the tests.
 #include <hip/hip_runtime.h>
 
 #include "moe_common.hpp"
@@ -21,7 +27,6 @@ namespace moe {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kReadChunk = 8192;   // bytes per wavefront per loop trip
 constexpr uint32_t kNever = 0x9e3779b9u;
@@ -85,6 +90,29 @@ __global__ __launch_bounds__(256) void k_probe_mfma(int iters, float* __restrict
   sink[static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x] = r;
 }
 
+template <bool SPLIT>
+__global__ __launch_bounds__(64) void k_probe_scaled_mfma(const int32_t* __restrict__ a, const int32_t* __restrict__ b,
+                                                          const int32_t* __restrict__ sa,
+                                                          const int32_t* __restrict__ sb, float* __restrict__ d) {
+  const uint64_t l = static_cast<uint64_t>(blockIdx.x) * 64 + threadIdx.x;
+  i32x8 av, bv = {};
+#pragma unroll
+  for (int i = 0; i < 8; i++) av[i] = a[8 * l + i];
+#pragma unroll
+  for (int i = 0; i < 4; i++) bv[i] = b[4 * l + i];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (SPLIT) {
+    i32x8 big, small;
+    split_e4m3(av, big, small);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(big, bv, acc, 0, 4, 0, sa[l], 0, sb[l]);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(small, bv, acc, 0, 4, 0, sa[l], 0, sb[l]);
+  } else {
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 4, 0, sa[l], 0, sb[l]);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; e++) d[4 * l + e] = acc[e];
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -112,6 +140,19 @@ int moe_probe_mfma(int32_t kind, int32_t grid, int32_t iters, float* sink, moe_s
   if (kind == 0) hipLaunchKernelGGL(moe::k_probe_mfma<0>, dim3(grid), dim3(256), 0, s, iters, sink);
   if (kind == 1) hipLaunchKernelGGL(moe::k_probe_mfma<1>, dim3(grid), dim3(256), 0, s, iters, sink);
   if (kind == 2) hipLaunchKernelGGL(moe::k_probe_mfma<2>, dim3(grid), dim3(256), 0, s, iters, sink);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return moe::record_error(MOE_ERR_HIP, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+int moe_probe_scaled_mfma(const int32_t* a, const int32_t* b, const int32_t* sa, const int32_t* sb, int32_t n,
+                          int32_t split, float* d, moe_stream_t stream) {
+  if (!a || !b || !sa || !sb || !d) return moe::record_error(MOE_ERR_ARG, "a, b, sa, sb and d are required");
+  if (n < 1 || n > (1 << 16)) return moe::record_error(MOE_ERR_ARG, "n must be in [1, 2^16]");
+  if (split != 0 && split != 1) return moe::record_error(MOE_ERR_ARG, "split must be 0 or 1");
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (split) hipLaunchKernelGGL(moe::k_probe_scaled_mfma<true>, dim3(n), dim3(64), 0, s, a, b, sa, sb, d);
+  else hipLaunchKernelGGL(moe::k_probe_scaled_mfma<false>, dim3(n), dim3(64), 0, s, a, b, sa, sb, d);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return moe::record_error(MOE_ERR_HIP, hipGetErrorString(e));
   return MOE_OK;

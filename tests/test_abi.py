@@ -243,3 +243,9 @@ def test_probe_validation(B):
     assert B.raw_status("moe_probe_mfma", 0, 0, 1, fake, None) == B.MOE_ERR_ARG
     assert B.raw_status("moe_probe_mfma", 0, 1, 0, fake, None) == B.MOE_ERR_ARG
     assert B.raw_status("moe_probe_mfma", 1, 1, 1, None, None) == B.MOE_ERR_ARG
+    f = fake
+    assert B.raw_status("moe_probe_scaled_mfma", None, f, f, f, 1, 0, f, None) == B.MOE_ERR_ARG
+    assert B.raw_status("moe_probe_scaled_mfma", f, f, f, f, 1, 0, None, None) == B.MOE_ERR_ARG
+    assert B.raw_status("moe_probe_scaled_mfma", f, f, f, f, 0, 0, f, None) == B.MOE_ERR_ARG
+    assert B.raw_status("moe_probe_scaled_mfma", f, f, f, f, (1 << 16) + 1, 0, f, None) == B.MOE_ERR_ARG
+    assert B.raw_status("moe_probe_scaled_mfma", f, f, f, f, 1, 2, f, None) == B.MOE_ERR_ARG
