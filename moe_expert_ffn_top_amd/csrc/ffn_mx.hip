@@ -465,6 +465,15 @@ __global__ __launch_bounds__(XT) void k_ffn_mx(MxArgs a, const int4* __restrict_
               acc[rb][cb] =
                   __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(small, fb[cb], acc[rb][cb], 0, 4, 0, sa, 0, sb[cb]);
           }
+          // a wavefront issues in order, so the split of row block rb + 1 would
+          // leave the matrix core idle if it ran as one block between the MFMAs
+          // of rb and rb + 1: interleave up to four VALU instructions after each
+          // MFMA instead
+#pragma unroll
+          for (int i = 0; i < NRB * 16; i++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to four VALU
+          }
           bi = bi == 2 ? 0 : bi + 1;
           __syncthreads();
         }
