@@ -76,9 +76,11 @@ def parse():
                          "decode48_mx "
                          "(default decode48)")
     ap.add_argument("--eager", action="store_true", help="launch every call eagerly instead of HIP graphs")
-    ap.add_argument("--ffn", default="split", choices=("one-launch", "split"),
-                    help="decode windows: FFN and combine in one launch (moe_expert_ffn_combine) or one launch per "
-                         "FFN stage plus the combine's (moe_expert_ffn_stages 1, 2; moe_combine)")
+    ap.add_argument("--ffn", default="routed", choices=("routed", "one-launch", "split"),
+                    help="decode windows: the routing inside the gate/up launch (moe_route_group_ffn, stages 1; then "
+                         "the down stage and moe_combine; where the window allows, else split), FFN and combine in "
+                         "one launch (moe_expert_ffn_combine) or one launch per FFN stage plus the combine's "
+                         "(moe_expert_ffn_stages 1, 2; moe_combine)")
     ap.add_argument("--policy", default="lru", choices=("lru", "hotcold"),
                     help="cached workloads: lru (fill every miss; the layer's outputs) or hotcold (measure the "
                          "hot/cold swap policy over the routing)")
@@ -232,6 +234,15 @@ class Workload:
         moe_expert_ffn_combine, one launch per layer."""
         return not self.mx and self.cfg.T * self.cfg.k < 16 * self.cfg.E and self.ffn_mode == "one-launch"
 
+    @property
+    def routed(self):
+        """NVFP4 decode windows with drawn logits that moe_route_group_ffn runs in
+        one launch (T <= 16, T k <= 64, E <= 1024): route, group and gate/up
+        together, then the down stage and the combine."""
+        c = self.cfg
+        return (not self.mx and self.wr is None and self.ffn_mode == "routed" and c.T * c.k < 16 * c.E
+                and c.T <= 16 and c.T * c.k <= 64 and c.E <= 1024)
+
     def ffn_combine(self, x, ev_start=None, ev_stop=None, stream=None):
         from moe_expert_ffn_top_amd import binding as B
         d, buf = self.dims, self.buf
@@ -254,6 +265,17 @@ class Workload:
             wr = self.wr[l] if self.wr is not None else None
             lg_in = None if self.wr is not None else self.logits[s, l]
             lg_out = buf.logits if self.wr is not None else None
+            if self.routed:
+                ev = [hip_events.new() for _ in range(4)] if ffn_events is not None else [None] * 4
+                B.moe_route_group_ffn(d, l, x, wr, lg_in, self.wsg[l], lg_out, buf.ids, buf.w, buf.sigma,
+                                      self.slot_table, self.n_slots, buf.offsets, buf.perm, buf.inv_perm,
+                                      buf.group_slot, self.pool, self.pool_bytes, self.layout, buf.h, buf.y_rows,
+                                      buf.status, buf.ws, 1, ev[0], ev[1], stream=stream)
+                self.ffn(x, 2, ev[2], ev[3], stream=stream)
+                if ffn_events is not None:
+                    ffn_events.append((ev, buf.offsets.clone()))
+                B.moe_combine(d, buf.y_rows, buf.inv_perm, buf.w, buf.sigma, buf.y, stream)
+                continue
             B.moe_route_group(d, l, x, wr, lg_in, self.wsg[l], lg_out, buf.ids, buf.w, buf.sigma, self.slot_table,
                               self.n_slots, buf.offsets, buf.perm, buf.inv_perm, buf.group_slot, buf.status, buf.ws,
                               stream=stream)
@@ -264,7 +286,7 @@ class Workload:
                     ffn_events.append((ev, buf.offsets.clone()))
                 continue
             if ffn_events is None:
-                if self.ffn_mode == "split" and not self.mx:
+                if self.ffn_mode in ("split", "routed") and not self.mx:
                     for st in (1, 2):
                         self.ffn(x, st, stream=stream)
                 else:
@@ -835,11 +857,21 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def ffn_label(cfg, ffn):
+    """The FFN path a workload runs (Workload's choice, from the shapes)."""
+    if cfg.T * cfg.k >= 16 * cfg.E:
+        return "grouped GEMM"
+    if ffn == "routed" and not (cfg.fmt != "mx" and cfg.router == "zipf" and cfg.T <= 16 and cfg.T * cfg.k <= 64
+                                and cfg.E <= 1024):
+        return "split"
+    return ffn
+
+
 def workload_config(cfg, args, ffn):
     return {"workload": cfg.name, "T": cfg.T, "layers": cfg.L, "H": cfg.H, "I": cfg.I, "E": cfg.E,
             "k": cfg.k, "shared_experts": 1,
             "routing": ("zipf s=%g" % cfg.zipf_s) if cfg.router == "zipf" else "router matrix",
-            "graphs": not args.eager, "ffn": ffn if cfg.T * cfg.k < 16 * cfg.E else "grouped GEMM",
+            "graphs": not args.eager, "ffn": ffn_label(cfg, ffn),
             "parallelism": "single GPU"}
 
 
@@ -949,10 +981,14 @@ def measure_workload(cfg, args, B, DevGen, K, W, ffn="split", per_step=False):
                     gu_b.mean(), dn_b.mean())}
     elif decode:
         achieved = float(gu_b.mean() / (gu_ms.mean() * 1e-3) / 1e9)
+        if wl.routed:
+            kname = "%s gate/up with the routing in its launch (moe_route_group_ffn, stages=1)" % ffn_kernel(cfg)[0]
+        else:
+            kname = "%s gate/up (%s, stages=1)" % (
+                ffn_kernel(cfg)[0], "moe_expert_ffn_mx" if cfg.fmt == "mx" else "moe_expert_ffn_stages")
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(cfg),
-                "kernel": "%s gate/up (%s, stages=1)" % (
-                    ffn_kernel(cfg)[0], "moe_expert_ffn_mx" if cfg.fmt == "mx" else "moe_expert_ffn_stages"),
+                "kernel": kname,
                 "launch_us": float(gu_ms.mean() * 1e3), "bytes_per_launch": float(gu_b.mean()),
                 "down": {"launch_us": float(dn_ms.mean() * 1e3), "bytes_per_launch": float(dn_b.mean()),
                          "achieved": float(dn_b.mean() / (dn_ms.mean() * 1e-3) / 1e9)}}

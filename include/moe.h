@@ -399,6 +399,31 @@ int moe_expert_ffn_combine(const moe_dims* d, const uint16_t* x, const void* poo
                            uint16_t* y_rows, uint16_t* y, int32_t* dev_status, void* ws,
                            uint64_t ws_bytes, void* ev_start, void* ev_stop, moe_stream_t stream);
 
+/* ---- S1 + S2 + S3 + S4 together ---------------------------------------
+ * moe_route_group followed by moe_expert_ffn_stages on the same stream, with
+ * exactly their arguments, validation and results (every output of both
+ * bit-identical); stages is 1 (gate/up) or 3 (gate/up and down).  For decode
+ * windows with drawn logits (logits_in, not w_router; T <= 16, T*k <= 64,
+ * E <= 1024, T*k < 16 E) the routing runs inside the gate/up launch
+ * ([FreeToken] 3.5: a step's control flow stays on the device): every
+ * workgroup selects the window's top-k and groups it into its own work list,
+ * so the weight stream starts without a routing kernel or a work-list round
+ * trip through memory before it, and one more workgroup stores the routing
+ * outputs (ids, weights, sigma, offsets, perm, inv_perm, group_slot, status,
+ * and the workspace's work list for the down stage).  Otherwise the two
+ * calls' kernels are launched in turn.  ev_start, ev_stop bracket the FFN
+ * launches, which then include the routing. */
+int moe_route_group_ffn(const moe_dims* d, int32_t layer, const uint16_t* x,
+                        const float* w_router, const float* logits_in,
+                        const float* w_shared_gate, float* logits_out,
+                        int32_t* topk_ids, float* topk_w, float* shared_sigma,
+                        const int32_t* slot_table, int32_t n_slots, int32_t* offsets,
+                        int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
+                        const void* pool, uint64_t pool_bytes, const moe_blob_layout* layout,
+                        uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws,
+                        uint64_t ws_bytes, int32_t stages, void* ev_start, void* ev_stop,
+                        moe_stream_t stream);
+
 /* ---- S4, MX variant: MXFP4 experts on the scaled MFMA ---------------------
  * [FreeToken] notes that the DeepSeek-V4-Flash experts are natively MXFP4; the
  * pages do not define the format, which is read as OCP Microscaling (MX):

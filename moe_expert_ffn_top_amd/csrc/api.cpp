@@ -351,11 +351,12 @@ namespace {
 // the combine, decode windows whose shapes have an instantiation run the two
 // stages and the combine as one launch; otherwise one launch per stage, then
 // the combine's own.
-int expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
-               const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm, const int32_t* group_slot,
-               uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws, uint64_t ws_bytes, int32_t stages,
-               void* ev_start, void* ev_stop, moe_stream_t stream, const int32_t* inv_perm, const float* topk_w,
-               const float* shared_sigma, uint16_t* y) {
+// The NVFP4 FFN's arguments (moe_expert_ffn_stages) checked, and its geometry:
+// the pool's slots and the device's compute-unit count.
+int validate_ffn(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
+                 const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm, const int32_t* group_slot,
+                 uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws, uint64_t ws_bytes, int32_t stages,
+                 moe::FfnGeom* g, int* n_cu) {
   if (stages < 1 || stages > 3) return fail(MOE_ERR_ARG, "stages = %d: must be 1 (gate/up), 2 (down) or 3", stages);
   int r = check_dims(d);
   if (r) return r;
@@ -373,13 +374,6 @@ int expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t 
   REQUIRE(y_rows, 16, "y_rows");
   REQUIRE(dev_status, 4, "dev_status");
   REQUIRE(ws, 16, "ws");
-  const bool comb = y != nullptr;
-  if (comb) {
-    REQUIRE(inv_perm, 4, "inv_perm");
-    REQUIRE(topk_w, 4, "topk_w");
-    REQUIRE(shared_sigma, 4, "shared_sigma");
-    REQUIRE(y, 16, "y");
-  }
   const uint64_t need = moe::ws_layout(*d).total;
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace %llu bytes < required %llu", (unsigned long long)ws_bytes,
@@ -387,19 +381,43 @@ int expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t 
   if (pool_bytes < layout->slot_stride)
     return fail(MOE_ERR_ARG, "pool_bytes %llu is smaller than one slot (%llu)", (unsigned long long)pool_bytes,
                 (unsigned long long)layout->slot_stride);
-  int dev = 0, n_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                              hipSuccess || n_cu <= 0)
+  int dev = 0;
+  *n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || *n_cu <= 0)
     return fail(MOE_ERR_HIP, "cannot query the device's compute-unit count");
-  moe::FfnGeom g;
-  g.pool = static_cast<const uint8_t*>(pool);
-  g.slot_stride = layout->slot_stride;
-  g.n_slots = (int64_t)(pool_bytes / layout->slot_stride);
+  g->pool = static_cast<const uint8_t*>(pool);
+  g->slot_stride = layout->slot_stride;
+  g->n_slots = (int64_t)(pool_bytes / layout->slot_stride);
   for (int m = 0; m < 3; m++) {
-    g.off_codes[m] = layout->off_codes[m];
-    g.off_scales[m] = layout->off_scales[m];
+    g->off_codes[m] = layout->off_codes[m];
+    g->off_scales[m] = layout->off_scales[m];
   }
-  g.off_globals = layout->off_globals;
+  g->off_globals = layout->off_globals;
+  return MOE_OK;
+}
+
+// S4 (stages: 1 gate/up, 2 down, 3 both) and, with y set, S5 after it.  With
+// the combine, decode windows whose shapes have an instantiation run the two
+// stages and the combine as one launch; otherwise one launch per stage, then
+// the combine's own.
+int expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
+               const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm, const int32_t* group_slot,
+               uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws, uint64_t ws_bytes, int32_t stages,
+               void* ev_start, void* ev_stop, moe_stream_t stream, const int32_t* inv_perm, const float* topk_w,
+               const float* shared_sigma, uint16_t* y) {
+  moe::FfnGeom g;
+  int n_cu = 0;
+  int r = validate_ffn(d, x, pool, pool_bytes, layout, offsets, perm, group_slot, h, y_rows, dev_status, ws,
+                       ws_bytes, stages, &g, &n_cu);
+  if (r) return r;
+  const bool comb = y != nullptr;
+  if (comb) {
+    REQUIRE(inv_perm, 4, "inv_perm");
+    REQUIRE(topk_w, 4, "topk_w");
+    REQUIRE(shared_sigma, 4, "shared_sigma");
+    REQUIRE(y, 16, "y");
+  }
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
   // groups averaging >= kGemmMinRows rows: grouped GEMM over 256-row chunks;
@@ -440,6 +458,43 @@ int moe_expert_ffn_combine(const moe_dims* d, const uint16_t* x, const void* poo
   if (!y) return fail(MOE_ERR_ARG, "y is NULL");
   return expert_ffn(d, x, pool, pool_bytes, layout, offsets, perm, group_slot, h, y_rows, dev_status, ws, ws_bytes, 3,
                     ev_start, ev_stop, stream, inv_perm, topk_w, shared_sigma, y);
+}
+
+int moe_route_group_ffn(const moe_dims* d, int32_t layer, const uint16_t* x, const float* w_router,
+                        const float* logits_in, const float* w_shared_gate, float* logits_out, int32_t* topk_ids,
+                        float* topk_w, float* shared_sigma, const int32_t* slot_table, int32_t n_slots,
+                        int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* group_slot, const void* pool,
+                        uint64_t pool_bytes, const moe_blob_layout* layout, uint16_t* h, uint16_t* y_rows,
+                        int32_t* dev_status, void* ws, uint64_t ws_bytes, int32_t stages, void* ev_start,
+                        void* ev_stop, moe_stream_t stream) {
+  if (stages != 1 && stages != 3) return fail(MOE_ERR_ARG, "stages = %d: must be 1 (gate/up) or 3 (both)", stages);
+  int r = validate_route(d, x, w_router, logits_in, w_shared_gate, logits_out, topk_ids, topk_w, shared_sigma);
+  if (r) return r;
+  if ((r = validate_group(d, layer, topk_ids, slot_table, n_slots, offsets, perm, inv_perm, group_slot, dev_status,
+                          ws, ws_bytes)))
+    return r;
+  moe::FfnGeom g;
+  int n_cu = 0;
+  if ((r = validate_ffn(d, x, pool, pool_bytes, layout, offsets, perm, group_slot, h, y_rows, dev_status, ws,
+                        ws_bytes, stages, &g, &n_cu)))
+    return r;
+  if (w_router || !moe::route_ffn_fusable(*d)) {
+    // the routing in kernels of its own: route + group, then the FFN
+    if ((r = moe_route_group(d, layer, x, w_router, logits_in, w_shared_gate, logits_out, topk_ids, topk_w,
+                             shared_sigma, slot_table, n_slots, offsets, perm, inv_perm, group_slot, dev_status, ws,
+                             ws_bytes, stream)))
+      return r;
+    return moe_expert_ffn_stages(d, x, pool, pool_bytes, layout, offsets, perm, group_slot, h, y_rows, dev_status, ws,
+                                 ws_bytes, stages, ev_start, ev_stop, stream);
+  }
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const float* lg = nullptr;
+  if ((r = route_logits(d, x, nullptr, logits_in, logits_out, st, &lg))) return r;
+  return hip_status(moe::launch_route_ffn_dec(*d, layer, lg, x, w_shared_gate, slot_table, n_slots, topk_ids, topk_w,
+                                              shared_sigma, offsets, perm, inv_perm, group_slot, dev_status, g, h,
+                                              y_rows, ws, n_cu, stages, static_cast<hipEvent_t>(ev_start),
+                                              static_cast<hipEvent_t>(ev_stop), st),
+                    "route + group + expert FFN launch");
 }
 
 int moe_blob_layout_init_mx(int32_t H, int32_t I, moe_blob_layout* out) {

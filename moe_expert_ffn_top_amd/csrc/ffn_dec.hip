@@ -55,9 +55,11 @@
 #include <math.h>
 
 #include <atomic>
+#include <type_traits>
 #include <mutex>
 
 #include "moe_common.hpp"
+#include "route_small.hpp"
 
 // resident workgroups per CU for the persistent grid, per stage
 #ifndef MOE_DEC_WGS_GU
@@ -124,6 +126,32 @@ struct DecArgs {
   int32_t a_bytes;    // bytes of x (T * H * 2), the gate/up A buffer
 };
 
+// Routing in the gate/up launch (moe_route_group_ffn): with logits set, every
+// workgroup routes and groups the window itself (route_small.hpp) into LDS and
+// walks that work list; workgroup 0 then stores every output of
+// moe_route_group (the down stage and the combine read them).
+struct RouteArgs {
+  const float* logits;      // [T][E]; null: the work list comes from memory
+  const float* w_sg;        // [H]
+  const int32_t* slot_row;  // the layer's row of the slot table, E + 1 entries
+  int32_t T, k, E;
+  int32_t n_slots;          // the slot table's bound (status bits), as for moe_route_group
+  int32_t* ids;
+  float* w;
+  float* sigma;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv_perm;
+  int32_t* group_slot;
+  int32_t* status;
+  int32_t* meta;
+  int4* tiles;
+  int32_t* tile_tok;
+  int32_t* sync;
+  int64_t n_sync;
+};
+constexpr int kRouteMaxTiles = kSortF + 1;   // routed groups, then the shared group's one tile (T <= 16)
+
 // One lane's loads for one 128-value K step of NS weight streams.
 template <int NS>
 struct Step {
@@ -159,12 +187,22 @@ struct Desc {
   int item;
 };
 
-template <bool GATEUP>
-__device__ inline Desc load_desc(const DecArgs& a, int item, int c, const int4* __restrict__ tiles,
-                                 const int32_t* __restrict__ tile_tok) {
+// TilesP / TokP: pointers into memory, or (the routing launch) into LDS, so
+// that the reads are LDS reads there and never flat ones (which the wait
+// counters would have to treat as both).
+using lds_int4_p = const __attribute__((address_space(3))) int4*;
+using lds_int_p = const __attribute__((address_space(3))) int*;
+__device__ inline int4 tile_at(const int4* __restrict__ tiles, int i) { return tiles[i]; }
+__device__ inline int4 tile_at(lds_int4_p tiles, int i) {
+  const lds_int_p q = (lds_int_p)(tiles + i);
+  return make_int4(q[0], q[1], q[2], q[3]);
+}
+
+template <bool GATEUP, class TilesP, class TokP>
+__device__ inline Desc load_desc(const DecArgs& a, int item, int c, TilesP tiles, TokP tile_tok) {
   Desc d;
   const int tile = min(item / a.n_ug, a.max_tiles - 1);
-  d.td = tiles[tile];
+  d.td = tile_at(tiles, tile);
   d.tok = GATEUP ? tile_tok[(int64_t)tile * 16 + c] : 0;
   d.item = item;
   return d;
@@ -443,10 +481,10 @@ struct Start {
 
 // The first unit (descriptor d0): its weights, its A rows when LOAD_A, then
 // the second unit's descriptor.  stride: item step of the walk.
-template <bool GATEUP, int SPLITK, int S, int U, bool FS, bool MX, bool LOAD_A>
+template <bool GATEUP, int SPLITK, int S, int U, bool FS, bool MX, bool LOAD_A, class TilesP, class TokP>
 __device__ inline void stage_start(Start<GATEUP, SPLITK, S, U, FS, MX>& st, const DecArgs& a, const Desc& d0,
-                                   int n_items, int stride, const int4* __restrict__ tiles,
-                                   const int32_t* __restrict__ tile_tok, const uint8_t* __restrict__ pool,
+                                   int n_items, int stride, TilesP tiles, TokP tile_tok,
+                                   const uint8_t* __restrict__ pool,
                                    const uint16_t* __restrict__ ain) {
   constexpr int NS = (GATEUP ? 2 : 1) * U;
   const Geo<GATEUP, SPLITK, S, U> g(a);
@@ -477,9 +515,9 @@ using PlainStage = Policy<kAuxPlain, kAuxPlain, false, false>;
 
 // Walks work units u = 0, 1, ...: item first_item + (u / nkr) * stride, K round
 // u % nkr, starting from st (its weight loads already issued).
-template <bool GATEUP, int SPLITK, int S, int U, bool FS, bool MX, class P>
+template <bool GATEUP, int SPLITK, int S, int U, bool FS, bool MX, class P, class TilesP, class TokP>
 __device__ inline void stage_walk(Start<GATEUP, SPLITK, S, U, FS, MX>& st, const DecArgs& a, int stride,
-                                  int n_items, const int4* __restrict__ tiles, const int32_t* __restrict__ tile_tok,
+                                  int n_items, TilesP tiles, TokP tile_tok,
                                   const uint8_t* __restrict__ pool, const uint16_t* __restrict__ ain,
                                   uint16_t* __restrict__ out, const FusedCtx* fc, f32x4 (*red)[(GATEUP ? 2 : 1) * U][64],
                                   uint32_t* comb_mask = nullptr) {
@@ -609,20 +647,68 @@ __device__ inline void stage_walk(Start<GATEUP, SPLITK, S, U, FS, MX>& st, const
 }
 
 // One stage as its own launch (stages split, and the MX path).
-template <bool GATEUP, int SPLITK, int S, int U, bool FS, bool MX>
+// ROUTE (gate/up on NVFP4 blobs, RouteArgs r): every workgroup first routes
+// and groups the window itself (T <= 16, T k <= 64, E <= 1024) into LDS, the
+// same in each.  Workgroup 0 then stores the routing outputs and ends;
+// workgroups 1 .. G walk the items with the work list from LDS (item i goes to
+// workgroup 1 + i mod (G - 1)), so no item waits on those stores and the walk
+// holds none of the output pointers.
+struct RouteLds {
+  SmallRouteLds<4> L;
+  int4 tiles[kRouteMaxTiles];
+  int32_t tok[kRouteMaxTiles * kTileRows];
+  int32_t n[2];
+};
+struct NoRouteLds {
+  int32_t unused;
+};
+
+template <bool GATEUP, int SPLITK, int S, int U, bool FS, bool MX, int RNPL>
 __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restrict__ tiles,
                                                  const int32_t* __restrict__ tile_tok,
                                                  const int32_t* __restrict__ n_tiles,
                                                  const uint8_t* __restrict__ pool, const uint16_t* __restrict__ ain,
-                                                 uint16_t* __restrict__ out) {
+                                                 uint16_t* __restrict__ out, RouteArgs r) {
+  constexpr bool ROUTE = RNPL > 0;   // RNPL: logits per lane of the routing (E <= 64 RNPL)
+  static_assert(!ROUTE || (GATEUP && !MX), "routing runs in the NVFP4 gate/up launch");
   constexpr int NS = (GATEUP ? 2 : 1) * U;
   __shared__ f32x4 red[SPLITK > 1 ? 4 : 1][NS][64];
-  const int n_items = *as_const(n_tiles) * a.n_ug;
-  Start<GATEUP, SPLITK, S, U, FS, MX> st;
-  const Desc d0 = load_desc<GATEUP>(a, blockIdx.x, threadIdx.x & 15, tiles, tile_tok);
-  stage_start<GATEUP, SPLITK, S, U, FS, MX, true>(st, a, d0, n_items, gridDim.x, tiles, tile_tok, pool, ain);
-  stage_walk<GATEUP, SPLITK, S, U, FS, MX, PlainStage>(st, a, gridDim.x, n_items, tiles, tile_tok, pool, ain, out,
-                                                       nullptr, red);
+  __shared__ std::conditional_t<ROUTE, RouteLds, NoRouteLds> rl;
+  int n_items, first = blockIdx.x, stride = gridDim.x;
+  if constexpr (ROUTE) {
+    const int wave = threadIdx.x >> 6;
+    small_route_topk<(RNPL > 0 ? RNPL : 1), 4>(rl.L, r.logits, ain, r.w_sg, r.T, a.H, r.E, r.k, r.slot_row,
+                                               false);
+    __syncthreads();
+    if (wave == 0) small_route_sort<4>(rl.L, r.T * r.k, r.E);
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      // the shared gates here, not beside the top-k: their registers would
+      // stay live through the other workgroups' walks otherwise
+      small_route_gate<4>(rl.L, ain, r.w_sg, r.T, a.H);
+      small_route_store<4>(rl.L, r.T, r.k, r.E, r.n_slots, r.ids, r.w, r.sigma, r.offsets, r.perm, r.inv_perm,
+                           r.group_slot, r.status, r.meta, r.tiles, r.tile_tok, nullptr, r.sync, r.n_sync);
+      return;
+    }
+    if (wave == 0) small_route_tiles<4>(rl.L, r.T, r.k, r.E, rl.tiles, rl.tok, rl.n, nullptr, nullptr);
+    __syncthreads();
+    n_items = rl.n[0] * a.n_ug;
+    first -= 1;
+    stride -= 1;
+  } else {
+    n_items = *as_const(n_tiles) * a.n_ug;
+  }
+  auto walk = [&](auto tl, auto tt) __attribute__((always_inline)) {
+    Start<GATEUP, SPLITK, S, U, FS, MX> st;
+    const Desc d0 = load_desc<GATEUP>(a, first, threadIdx.x & 15, tl, tt);
+    stage_start<GATEUP, SPLITK, S, U, FS, MX, true>(st, a, d0, n_items, stride, tl, tt, pool, ain);
+    stage_walk<GATEUP, SPLITK, S, U, FS, MX, PlainStage>(st, a, stride, n_items, tl, tt, pool, ain, out, nullptr,
+                                                         red);
+  };
+  if constexpr (ROUTE)
+    walk((lds_int4_p)rl.tiles, (lds_int_p)rl.tok);
+  else
+    walk(tiles, tile_tok);
 }
 
 // Gate/up items of the fused launch: with R = ceil(n / G) rounds, the first
@@ -736,6 +822,7 @@ struct DecPtrs {
   const uint8_t* pool;
   const uint16_t* ain;
   uint16_t* out;
+  RouteArgs route;  // gate/up only; logits null otherwise
 };
 
 // ev0 / ev1: when either is set, the launch goes through hipExtLaunchKernelGGL
@@ -746,15 +833,24 @@ struct DecLaunch {
   hipEvent_t ev0, ev1;
 };
 
+template <bool GATEUP, int SK, int S, int U, bool FS, bool MX, int RNPL>
+hipError_t launch_kr(const DecArgs& a, const DecPtrs& p, const DecLaunch& l) {
+  if (l.ev0 || l.ev1)
+    hipExtLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U, FS, MX, RNPL>), dim3(l.grid), dim3(256), 0, l.st, l.ev0,
+                          l.ev1, 0, a, p.tiles, p.tile_tok, p.n_tiles, p.pool, p.ain, p.out, p.route);
+  else
+    hipLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U, FS, MX, RNPL>), dim3(l.grid), dim3(256), 0, l.st, a, p.tiles,
+                       p.tile_tok, p.n_tiles, p.pool, p.ain, p.out, p.route);
+  return hipGetLastError();
+}
+
 template <bool GATEUP, int SK, int S, int U, bool FS, bool MX>
 hipError_t launch_k(const DecArgs& a, const DecPtrs& p, const DecLaunch& l) {
-  if (l.ev0 || l.ev1)
-    hipExtLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U, FS, MX>), dim3(l.grid), dim3(256), 0, l.st, l.ev0, l.ev1, 0,
-                          a, p.tiles, p.tile_tok, p.n_tiles, p.pool, p.ain, p.out);
-  else
-    hipLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U, FS, MX>), dim3(l.grid), dim3(256), 0, l.st, a, p.tiles,
-                       p.tile_tok, p.n_tiles, p.pool, p.ain, p.out);
-  return hipGetLastError();
+  if constexpr (GATEUP && !MX)
+    if (p.route.logits)
+      return p.route.E <= 512 ? launch_kr<GATEUP, SK, S, U, FS, MX, 8>(a, p, l)
+                              : launch_kr<GATEUP, SK, S, U, FS, MX, 16>(a, p, l);
+  return launch_kr<GATEUP, SK, S, U, FS, MX, 0>(a, p, l);
 }
 
 // S = 4 with every wavefront's share of K made of whole 512-value groups
@@ -883,12 +979,13 @@ int fused_occupancy(FusedFn fn) {
 
 }  // namespace
 
-// Decode-path FFN: both stages, persistent grids of (CUs x MOE_DEC_WGS_GU or
-// MOE_DEC_WGS_DN) workgroups (fewer when there is less work than that).
-hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
-                          uint16_t* y_rows, void* ws, int n_cu, int stages, hipEvent_t ev_start, hipEvent_t ev_stop,
-                          hipStream_t s, bool mx, const uint16_t* down_in) {
-  (void)perm;
+namespace {
+
+// The stages of the decode-path FFN, one launch each; route (gate/up only):
+// the window's routing in that launch.
+hipError_t launch_dec_stages(const moe_dims& d, const uint16_t* x, const FfnGeom& g, uint16_t* h, uint16_t* y_rows,
+                             void* ws, int n_cu, int stages, hipEvent_t ev_start, hipEvent_t ev_stop, hipStream_t s,
+                             bool mx, const uint16_t* down_in, const RouteArgs* route) {
   const WsLayout wl = ws_layout(d);
   uint8_t* base = static_cast<uint8_t*>(ws);
   DecPtrs ptrs;
@@ -903,9 +1000,15 @@ hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g
     const Split sp = stage_split(d, gu, mx);
     const DecArgs a = dec_args(d, g, wl, sp);
     const int64_t items = (int64_t)wl.max_tiles * a.n_ug;
-    const int grid = (int)(items < cap ? items : cap);
+    // a routing launch has one more workgroup, which only stores the routing;
+    // the grid stays within the resident cap (a workgroup beyond it would
+    // start only when another ends)
+    const int64_t want = items + ((gu && route) ? 1 : 0);
+    const int grid = (int)(want < cap ? want : cap);
     ptrs.ain = gu ? x : (down_in ? down_in : h);
     ptrs.out = gu ? h : y_rows;
+    ptrs.route = RouteArgs{};
+    if (gu && route) ptrs.route = *route;
     // the start event goes with the first stage launched, the stop event with the last
     const bool first = gu || !(stages & 1), last = !gu || !(stages & 2);
     const DecLaunch l{grid, s, first ? ev_start : nullptr, last ? ev_stop : nullptr};
@@ -916,6 +1019,53 @@ hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+// Decode-path FFN: both stages, persistent grids of (CUs x MOE_DEC_WGS_GU or
+// MOE_DEC_WGS_DN) workgroups (fewer when there is less work than that).
+hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
+                          uint16_t* y_rows, void* ws, int n_cu, int stages, hipEvent_t ev_start, hipEvent_t ev_stop,
+                          hipStream_t s, bool mx, const uint16_t* down_in) {
+  (void)perm;
+  return launch_dec_stages(d, x, g, h, y_rows, ws, n_cu, stages, ev_start, ev_stop, s, mx, down_in, nullptr);
+}
+
+bool route_ffn_fusable(const moe_dims& d) {
+  return !use_gemm(d) && d.T <= 16 && (int64_t)d.T * d.k <= kSortF && d.E <= kMaxExperts;
+}
+
+hipError_t launch_route_ffn_dec(const moe_dims& d, int32_t layer, const float* logits, const uint16_t* x,
+                                const float* w_sg, const int32_t* slot_table, int32_t n_slots, int32_t* ids,
+                                float* w, float* sigma, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                int32_t* group_slot, int32_t* dev_status, const FfnGeom& g, uint16_t* h,
+                                uint16_t* y_rows, void* ws, int n_cu, int stages, hipEvent_t ev_start,
+                                hipEvent_t ev_stop, hipStream_t s) {
+  const WsLayout wl = ws_layout(d);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  RouteArgs r;
+  r.logits = logits;
+  r.w_sg = w_sg;
+  r.slot_row = slot_table + (int64_t)layer * (d.E + 1);
+  r.T = d.T;
+  r.k = d.k;
+  r.E = d.E;
+  r.n_slots = n_slots;
+  r.ids = ids;
+  r.w = w;
+  r.sigma = sigma;
+  r.offsets = offsets;
+  r.perm = perm;
+  r.inv_perm = inv_perm;
+  r.group_slot = group_slot;
+  r.status = dev_status;
+  r.meta = reinterpret_cast<int32_t*>(base + wl.off_meta);
+  r.tiles = reinterpret_cast<int4*>(base + wl.off_tiles);
+  r.tile_tok = reinterpret_cast<int32_t*>(base + wl.off_tile_tok);
+  r.sync = reinterpret_cast<int32_t*>(base + wl.off_sync);
+  r.n_sync = wl.n_sync;
+  return launch_dec_stages(d, x, g, h, y_rows, ws, n_cu, stages | 1, ev_start, ev_stop, s, false, nullptr, &r);
 }
 
 bool ffn_dec_fusable(const moe_dims& d, bool combine) {

@@ -19,6 +19,7 @@
 //           histogram) and earlier in its own part (counted over the ids
 //           staged in LDS), so a row depends only on the ids (deterministic).
 #include "moe_common.hpp"
+#include "route_small.hpp"
 #include "topk_wave.hpp"
 
 #include <type_traits>
@@ -367,33 +368,34 @@ __global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict_
                    tile_tok, tile_base, chunks, hist, cntl, tbl, sid, lds, minr, skip_rank, n_skipped);
 }
 
-// Inclusive max-scan of one wavefront (values >= 0) with DPP, the pattern of
-// wave_inclusive_scan: lanes shifted in from outside a row give 0.
-__device__ inline int wave_inclusive_max(int v) {
-  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true));   // row_shr:1
-  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true));   // row_shr:2
-  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true));   // row_shr:4
-  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true));   // row_shr:8
-  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false));  // row_bcast:15
-  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false));  // row_bcast:31
-  return v;
+// Route and group fused for small windows (T <= 16 tokens, drawn logits), one
+// 1024-thread block.  T*k <= 64 entries: the sort path of route_small.hpp
+// (threshold top-k per token wavefront, one wavefront's bitonic sort).
+template <int NPL>
+__global__ __launch_bounds__(1024) void k_route_group_sort(
+    const float* __restrict__ logits, const uint16_t* __restrict__ x, const float* __restrict__ w_sg, int T, int H,
+    int E, int k, int layer, const int32_t* __restrict__ slot_table, int32_t n_slots, int32_t* __restrict__ ids,
+    float* __restrict__ wout, float* __restrict__ sigma, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv_perm, int32_t* __restrict__ group_slot, int32_t* __restrict__ status,
+    int32_t* __restrict__ meta, int4* __restrict__ tiles, int32_t* __restrict__ tile_tok, int4* __restrict__ chunks,
+    int32_t* __restrict__ sync, int64_t n_sync) {
+  __shared__ SmallRouteLds<16> L;
+  STAGE_STAMP(1, 0);
+  small_route_topk<NPL, 16>(L, logits, x, w_sg, T, H, E, k, slot_table + (int64_t)layer * (E + 1), true);
+  __syncthreads();
+  STAGE_STAMP(1, 1);
+  if ((threadIdx.x >> 6) == 0) small_route_sort<16>(L, T * k, E);
+  __syncthreads();
+  STAGE_STAMP(1, 2);
+  small_route_store<16>(L, T, k, E, n_slots, ids, wout, sigma, offsets, perm, inv_perm, group_slot, status, meta,
+                        tiles, tile_tok, chunks, sync, n_sync);
+  STAGE_STAMP(1, 3);
 }
 
-// Route and group fused for small windows (T <= 16 tokens, T*k <= kSmallF,
-// drawn logits), one 1024-thread block, every barrier before the kernel's
-// first global store (a barrier waits for the wavefront's outstanding memory
-// operations, stores included).
-// Top-k: one wavefront per token, by threshold (topk_threshold): the same
-// winners in the same slot order as the arg-max rounds.
-// Grouping of F <= 64 entries (SORT): wavefront 0 sorts the keys
-// (expert << 6 | entry) across its lanes (bitonic network), so lane p holds
-// row p of the grouped order (ascending expert, then entry, i.e. token).
-// Neighbour exchanges and two wavefront scans give each row its group's
-// first row, its rank in the group and the group's tile (one tile per group:
-// a group has at most T <= 16 rows).  The groups go to LDS; after one
-// barrier thread e finds expert e's first row by binary search over them.
-// F > 64: the block-scan grouping (group_small_tail).
-template <int NPL, bool SORT>
+// T*k in (64, kSmallF]: the threshold top-k per token wavefront, then the
+// block-scan grouping (group_small_tail), then the softmax, one 1024-thread
+// block; every barrier comes before the kernel's first global store.
+template <int NPL>
 __global__ __launch_bounds__(1024) void k_route_group_small(
     const float* __restrict__ logits, const uint16_t* __restrict__ x, const float* __restrict__ w_sg, int T, int H,
     int E, int k, int layer, const int32_t* __restrict__ slot_table, int32_t n_slots, int32_t* __restrict__ ids,
@@ -404,23 +406,17 @@ __global__ __launch_bounds__(1024) void k_route_group_small(
   __shared__ __align__(16) int32_t sid[kSmallF];  // the winners' experts, [T][k] (entry f = t k + j)
   __shared__ uint32_t wink[kSmallF];               // the winners' keys
   __shared__ uint2 cand[16 * 64];                  // top-k candidates, 64 per token
-  __shared__ int32_t slots[1024];                   // slot of each routed expert
-  __shared__ int32_t ge[SORT ? 64 : 1];             // SORT: expert of group g, ascending
-  __shared__ int32_t gp[SORT ? 64 : 1];             //       its first row
-  __shared__ int32_t gnv[2];                        //       groups, valid rows
-  __shared__ int4 rowi[SORT ? 64 : 1];               //       row p: (expert, entry, group, rank)
-  __shared__ int2 rowj[SORT ? 64 : 1];               //       row p: (group's first row, last row of its group)
-  __shared__ int32_t hist[SORT ? 1 : 1024];         // block-scan grouping
-  __shared__ int32_t cntl[SORT ? 1 : 1024];
-  __shared__ int32_t tbl[SORT ? 1 : 1024];
+  __shared__ int32_t hist[1024];
+  __shared__ int32_t cntl[1024];
+  __shared__ int32_t tbl[1024];
   __shared__ int lds[17];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = tid >> 6;
   const int F = T * k;
   STAGE_STAMP(1, 0);
   const int slot = tid < E ? slot_table[(int64_t)layer * (E + 1) + tid] : -1;
   const int ss = slot_table[(int64_t)layer * (E + 1) + E];
   if (tid >= F && tid < kSmallF) sid[tid] = -1;
-  if (!SORT && tid < E) hist[tid] = 0;
+  if (tid < E) hist[tid] = 0;
   const int t = wave;
   GateIn g;
   if (t < T) {
@@ -429,131 +425,11 @@ __global__ __launch_bounds__(1024) void k_route_group_small(
     gate_load(g, x, w_sg, t, H);
     topk_threshold<NPL>(key, k, wink + t * k, sid + t * k, cand + t * 64);
   }
-  if (tid < E) slots[tid] = slot;
   __syncthreads();
   STAGE_STAMP(1, 1);
-  if (!SORT) {
-    // the block-scan grouping, then the softmax
-    const int e_mine = tid < F ? sid[tid] : -1;
-    group_small_tail(e_mine, F, T, k, E, slot, ss, n_slots, offsets, perm, inv_perm, group_slot, status, meta, tiles,
-                     tile_tok, tile_base, chunks, hist, cntl, tbl, sid, lds);
-    if (t < T) topk_finish(wink + t * k, sid + t * k, t, k, gate_dot(g, x, w_sg, t, H), ids, wout, sigma);
-    zero_sync(sync, n_sync);
-    return;
-  }
-  // SORT: wavefront 0 orders the entries
-  uint32_t key = 0xFFFFFFFFu;
-  int e_r = 0, f_r = 0, rank = 0, grp = 0, start = 0;
-  bool valid = false, flag = false, last = false;
-  int nv = 0, nd = 0;
-  if (wave == 0) {
-    const int e0 = lane < F ? sid[lane] : -1;
-    const bool ok = lane < F && e0 >= 0 && e0 < E;
-    if (lane < F && !ok) inv_perm[lane] = -1;   // (top-k ids are always valid; kept for a bad id)
-    key = ok ? ((uint32_t)e0 << 6) | (uint32_t)lane : 0xFFFFFFFFu;
-#pragma unroll
-    for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        const uint32_t other = (uint32_t)__shfl_xor((int)key, stride);
-        const bool keep_min = ((lane & stride) == 0) == ((lane & size) == 0);
-        key = keep_min ? min(key, other) : max(key, other);
-      }
-    }
-    valid = key != 0xFFFFFFFFu;
-    e_r = (int)(key >> 6);
-    f_r = (int)(key & 63u);
-    nv = __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid));
-    const int e_prev = __shfl_up(e_r, 1);
-    flag = valid && (lane == 0 || e_prev != e_r);
-    const bool flag_next = __shfl_down((int)flag, 1) != 0;
-    last = valid && (lane == nv - 1 || flag_next);
-    grp = wave_inclusive_scan(flag ? 1 : 0) - 1;
-    start = wave_inclusive_max(flag ? lane : 0);
-    rank = lane - start;
-    nd = __builtin_popcountll(__builtin_amdgcn_ballot_w64(flag));
-    if (flag) {
-      ge[grp] = e_r;
-      gp[grp] = lane;
-    }
-    rowi[lane] = make_int4(valid ? e_r : -1, f_r, grp, rank);
-    rowj[lane] = make_int2(start, last ? 1 : 0);
-    if (lane == 0) {
-      gnv[0] = nd;
-      gnv[1] = nv;
-    }
-  }
-  __syncthreads();
-  STAGE_STAMP(1, 2);
-  // global stores only from here: expert e's first row (the first group at or
-  // above e), its slot and status
-  if (tid < E) {
-    const int ndg = gnv[0];
-    int lo = 0, hi = ndg;   // first g with ge[g] >= tid
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (ge[mid] < tid) lo = mid + 1;
-      else hi = mid;
-    }
-    offsets[tid] = lo < ndg ? gp[lo] : gnv[1];
-    group_slot[tid] = slot;
-    if (lo < ndg && ge[lo] == tid) {
-      if (slot < 0) atomicOr(status, MOE_DEV_NOT_RESIDENT);
-      if (slot >= n_slots) atomicOr(status, MOE_DEV_BAD_SLOT);
-    }
-  }
-  // the rows' stores by the block's last wavefront (wavefront 0 computed
-  // them; the expert threads and the token wavefronts store in parallel)
-  if (wave == 15) {
-    const int4 ri = rowi[lane];
-    const int2 rj = rowj[lane];
-    e_r = ri.x;
-    f_r = ri.y;
-    grp = ri.z;
-    rank = ri.w;
-    start = rj.x;
-    last = rj.y != 0;
-    valid = e_r >= 0;
-    nd = gnv[0];
-    nv = gnv[1];
-    if (lane == 0) {
-      offsets[E] = nv;
-      offsets[E + 1] = F + T;
-      group_slot[E] = ss;
-      if (ss < 0) atomicOr(status, MOE_DEV_NOT_RESIDENT);
-      if (ss >= n_slots) atomicOr(status, MOE_DEV_BAD_SLOT);
-      if (nv < F) atomicOr(status, MOE_DEV_BAD_EXPERT_ID);
-    }
-    const int f_first = rowi[start & 63].y;   // the group's first entry
-    if (valid) {
-      perm[lane] = f_r;
-      inv_perm[f_r] = lane;
-      if (!chunks) {
-        tile_tok[grp * kTileRows + rank] = f_r / k;
-        if (last) {
-          tiles[grp] = make_int4(e_r, start, rank + 1, slots[e_r]);
-          for (int r = rank + 1; r < kTileRows; r++) tile_tok[grp * kTileRows + r] = f_first / k;  // padding
-        }
-      } else if (last) {
-        chunks[grp] = make_int4(e_r, start, rank + 1, slots[e_r]);
-      }
-    }
-    // the shared group: tiles (chunks) after the routed ones, rows in token order
-    if (!chunks) {
-      const int nts = (T + kTileRows - 1) / kTileRows;
-      if (lane < nts) tiles[nd + lane] = make_int4(E, F + lane * kTileRows, min(kTileRows, T - lane * kTileRows), ss);
-      for (int i = lane; i < nts * kTileRows; i += 64) {
-        const int tl = i / kTileRows, r = i % kTileRows;
-        const int n = min(kTileRows, T - tl * kTileRows);
-        tile_tok[(nd + tl) * kTileRows + r] = tl * kTileRows + (r < n ? r : 0);
-      }
-      if (lane == 0) meta[0] = nd + nts;
-    } else if (lane == 0) {
-      chunks[nd] = make_int4(E, F, T, ss);   // T <= 16 <= kChunkRows
-      meta[1] = nd + 1;
-    }
-  }
-  // the softmax weights and the shared gate of each token
+  const int e_mine = tid < F ? sid[tid] : -1;
+  group_small_tail(e_mine, F, T, k, E, slot, ss, n_slots, offsets, perm, inv_perm, group_slot, status, meta, tiles,
+                   tile_tok, tile_base, chunks, hist, cntl, tbl, sid, lds);
   if (t < T) topk_finish(wink + t * k, sid + t * k, t, k, gate_dot(g, x, w_sg, t, H), ids, wout, sigma);
   zero_sync(sync, n_sync);
   STAGE_STAMP(1, 3);
@@ -651,25 +527,31 @@ hipError_t launch_route_group(const moe_dims& d, int32_t layer, const float* log
   int4* chunks = use_gemm(d) ? reinterpret_cast<int4*>(base + wl.off_chunks) : nullptr;
   int32_t* sync = reinterpret_cast<int32_t*>(base + wl.off_sync);
   const int npl = (d.E + 63) / 64;
-  const bool sort = d.T * d.k <= 64;
+  const bool sort = (int64_t)d.T * d.k <= kSortF;
   const dim3 g(1), b(1024);
-#define MOE_RG_LAUNCH(N, S)                                                                                       \
-  hipLaunchKernelGGL((k_route_group_small<N, S>), g, b, 0, s, logits, x, w_sg, d.T, d.H, d.E, d.k, layer,         \
-                     slot_table, n_slots, ids, w, sigma, offsets, perm, inv_perm, group_slot, dev_status, meta,      \
-                     tiles, tile_tok, tile_base, chunks, sync, wl.n_sync)
-#define MOE_RG_NPL(S)                      \
-  if (npl <= 1) MOE_RG_LAUNCH(1, S);       \
-  else if (npl <= 2) MOE_RG_LAUNCH(2, S);  \
-  else if (npl <= 4) MOE_RG_LAUNCH(4, S);  \
-  else if (npl <= 8) MOE_RG_LAUNCH(8, S);  \
-  else MOE_RG_LAUNCH(16, S);
+  const int32_t* st = slot_table;
+#define MOE_RG_SORT(N)                                                                                             \
+  hipLaunchKernelGGL((k_route_group_sort<N>), g, b, 0, s, logits, x, w_sg, d.T, d.H, d.E, d.k, layer, st, n_slots, \
+                     ids, w, sigma, offsets, perm, inv_perm, group_slot, dev_status, meta, tiles, tile_tok, chunks,   \
+                     sync, wl.n_sync)
+#define MOE_RG_SMALL(N)                                                                                             \
+  hipLaunchKernelGGL((k_route_group_small<N>), g, b, 0, s, logits, x, w_sg, d.T, d.H, d.E, d.k, layer, st, n_slots, \
+                     ids, w, sigma, offsets, perm, inv_perm, group_slot, dev_status, meta, tiles, tile_tok,          \
+                     tile_base, chunks, sync, wl.n_sync)
+#define MOE_RG_NPL(L)                 \
+  if (npl <= 1) L(1);                 \
+  else if (npl <= 2) L(2);            \
+  else if (npl <= 4) L(4);            \
+  else if (npl <= 8) L(8);            \
+  else L(16);
   if (sort) {
-    MOE_RG_NPL(true)
+    MOE_RG_NPL(MOE_RG_SORT)
   } else {
-    MOE_RG_NPL(false)
+    MOE_RG_NPL(MOE_RG_SMALL)
   }
 #undef MOE_RG_NPL
-#undef MOE_RG_LAUNCH
+#undef MOE_RG_SMALL
+#undef MOE_RG_SORT
   return hipGetLastError();
 }
 

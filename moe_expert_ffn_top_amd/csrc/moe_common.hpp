@@ -308,6 +308,17 @@ hipError_t launch_route_group(const moe_dims& d, int32_t layer, const float* log
 hipError_t launch_ffn_dec(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm,
                           uint16_t* h, uint16_t* y_rows, void* ws, int n_cu, int stages, hipEvent_t ev_start,
                           hipEvent_t ev_stop, hipStream_t s, bool mx = false, const uint16_t* down_in = nullptr);
+// Route + group of a small window (route_ffn_fusable: decode groups, T <= 16,
+// T k <= 64, E <= kMaxExperts, drawn logits) inside the gate/up launch, which
+// then writes every output of launch_route_group too; then (stages & 2) the
+// down stage.
+bool route_ffn_fusable(const moe_dims& d);
+hipError_t launch_route_ffn_dec(const moe_dims& d, int32_t layer, const float* logits, const uint16_t* x,
+                                const float* w_sg, const int32_t* slot_table, int32_t n_slots, int32_t* ids,
+                                float* w, float* sigma, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                int32_t* group_slot, int32_t* dev_status, const FfnGeom& g, uint16_t* h,
+                                uint16_t* y_rows, void* ws, int n_cu, int stages, hipEvent_t ev_start,
+                                hipEvent_t ev_stop, hipStream_t s);
 // Grouped-GEMM expert FFN over the chunk list (prefill-sized groups); same
 // stage mask and events as launch_ffn_dec; n_cu sizes the persistent grid.
 hipError_t launch_ffn_gemm(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,

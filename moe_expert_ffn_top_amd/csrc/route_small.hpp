@@ -1,0 +1,254 @@
+// Route (S1) and group (S3) of a small window by one workgroup: T <= 16
+// tokens, F = T k <= 64 (token, slot) entries, drawn logits.  The pieces are
+// shared by the route + group kernel (k_route_group_sort, one 1024-thread
+// workgroup) and by the gate/up kernel that routes in its own prologue
+// (k_ffn_dec with RouteArgs; every workgroup routes for itself, workgroup 0
+// stores the results).
+//
+// [Strata] "还有一条会改变输出的路径" and "路由以后，专家怎样分工？": a token's k
+// largest logits pick its experts (the lower index wins a tie, slot j holds
+// the j-th largest); the rows of one expert form one group, ascending token.
+//  - small_route_topk: the slot row into LDS; token t by wavefront t mod NW
+//    (threshold top-k, topk_threshold); optionally the shared gate's dot
+//    product.
+//  - small_route_sort: wavefront 0 sorts the keys (expert << 6 | entry) across
+//    its lanes (bitonic network), so lane p holds row p of the grouped order;
+//    neighbour exchanges and two wavefront scans give each row its group's
+//    first row, its rank in the group and the group's tile (one tile per
+//    group: a group has at most T <= 16 rows).
+//  - small_route_tiles: the FFN work list (tiles and their token tables, or
+//    the GEMM's chunks) through generic pointers, so into LDS or memory.
+//  - small_route_store: every other output.  No global store comes before the
+//    callers' last barrier (a barrier waits for the wavefront's outstanding
+//    memory operations, stores included).
+#pragma once
+
+#include "moe_common.hpp"
+#include "topk_wave.hpp"
+
+namespace moe {
+
+constexpr int kSortF = 64;  // entries of the sort path (one wavefront's lanes)
+
+template <int NW>
+struct SmallRouteLds {
+  int32_t sid[kSortF];              // the winners' experts [T][k] (entry f = t k + j), -1 beyond F
+  uint32_t wink[kSortF];            // the winners' keys
+  uint2 cand[NW * 64];              // top-k candidates, 64 per wavefront
+  int32_t slots[kMaxExperts + 1];   // slot of each expert, the shared one at E
+  float z[16];                      // the shared gate's dot product of each token
+  int32_t ge[kSortF];               // group g: its expert (ascending)
+  int32_t gp[kSortF];               //          its first row
+  int32_t gnv[2];                   // groups, valid rows
+  int4 rowi[kSortF];                // row p: (expert, entry, group, rank)
+  int2 rowj[kSortF];                // row p: (group's first row, last row of its group)
+};
+
+// Inclusive max-scan of one wavefront (values >= 0) with DPP, the pattern of
+// wave_inclusive_scan: lanes shifted in from outside a row give 0.
+__device__ inline int wave_inclusive_max(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true));   // row_shr:1
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true));   // row_shr:2
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true));   // row_shr:4
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true));   // row_shr:8
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return v;
+}
+
+// Every wavefront of the NW: the slot row slot_row[0..E] into LDS; tokens
+// t = wave, wave + NW, ... < T: the winners into sid / wink (slot order);
+// with gate, z[t] = x[t] . w_sg.  The caller then meets a barrier.
+template <int NPL, int NW>
+__device__ inline void small_route_topk(SmallRouteLds<NW>& L, const float* __restrict__ logits,
+                                        const uint16_t* __restrict__ x, const float* __restrict__ w_sg, int T, int H,
+                                        int E, int k, const int32_t* __restrict__ slot_row, bool gate) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int F = T * k;
+  // the slot row is loaded into registers first and stored after the top-k,
+  // so its round trip overlaps the logits' instead of preceding it
+  constexpr int SPT = (kMaxExperts + 1 + NW * 64 - 1) / (NW * 64);
+  int sl[SPT];
+#pragma unroll
+  for (int i = 0; i < SPT; i++) {
+    const int e = tid + i * NW * 64;
+    sl[i] = e <= E ? slot_row[e] : -1;
+  }
+  for (int f = F + tid; f < kSortF; f += NW * 64) L.sid[f] = -1;
+  for (int t = wave; t < T; t += NW) {
+    uint32_t key[NPL];
+    load_keys<NPL>(key, logits, t, E, 0, E);
+    GateIn g;
+    if (gate) gate_load(g, x, w_sg, t, H);
+    topk_threshold<NPL>(key, k, L.wink + t * k, L.sid + t * k, L.cand + wave * 64);
+    if (gate) {
+      const float z = gate_dot(g, x, w_sg, t, H);
+      if ((tid & 63) == 0) L.z[t] = z;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < SPT; i++) {
+    const int e = tid + i * NW * 64;
+    if (e <= E) L.slots[e] = sl[i];
+  }
+}
+
+// z[t] = x[t] . w_sg for tokens t = wave, wave + NW, ... < T (small_route_topk
+// without the gate; the same wavefront then finishes the token in
+// small_route_store, so no barrier is needed between).
+template <int NW>
+__device__ inline void small_route_gate(SmallRouteLds<NW>& L, const uint16_t* __restrict__ x,
+                                        const float* __restrict__ w_sg, int T, int H) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  for (int t = wave; t < T; t += NW) {
+    GateIn g;
+    gate_load(g, x, w_sg, t, H);
+    const float z = gate_dot(g, x, w_sg, t, H);
+    if ((tid & 63) == 0) L.z[t] = z;
+  }
+}
+
+// Wavefront 0, after the barrier that follows small_route_topk: the grouped
+// order of the F entries into rowi / rowj / ge / gp / gnv.  An entry whose
+// expert lies outside [0, E) (none, for top-k winners) sorts last and is not
+// valid.  The caller then meets a barrier.
+template <int NW>
+__device__ inline void small_route_sort(SmallRouteLds<NW>& L, int F, int E) {
+  const int lane = threadIdx.x & 63;
+  const int e0 = lane < F ? L.sid[lane] : -1;
+  const bool ok = lane < F && e0 >= 0 && e0 < E;
+  uint32_t key = ok ? ((uint32_t)e0 << 6) | (uint32_t)lane : 0xFFFFFFFFu;
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint32_t other = (uint32_t)__shfl_xor((int)key, stride);
+      const bool keep_min = ((lane & stride) == 0) == ((lane & size) == 0);
+      key = keep_min ? min(key, other) : max(key, other);
+    }
+  }
+  const bool valid = key != 0xFFFFFFFFu;
+  const int e_r = (int)(key >> 6);
+  const int f_r = (int)(key & 63u);
+  const int nv = __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid));
+  const int e_prev = __shfl_up(e_r, 1);
+  const bool flag = valid && (lane == 0 || e_prev != e_r);
+  const bool flag_next = __shfl_down((int)flag, 1) != 0;
+  const bool last = valid && (lane == nv - 1 || flag_next);
+  const int grp = wave_inclusive_scan(flag ? 1 : 0) - 1;
+  const int start = wave_inclusive_max(flag ? lane : 0);
+  const int rank = lane - start;
+  const int nd = __builtin_popcountll(__builtin_amdgcn_ballot_w64(flag));
+  if (flag) {
+    L.ge[grp] = e_r;
+    L.gp[grp] = lane;
+  }
+  L.rowi[lane] = make_int4(valid ? e_r : -1, f_r, grp, rank);
+  L.rowj[lane] = make_int2(start, last ? 1 : 0);
+  if (lane == 0) {
+    L.gnv[0] = nd;
+    L.gnv[1] = nv;
+  }
+}
+
+// One wavefront (lane = row): the FFN work list of the grouped rows.  Without
+// chunks: tile g of each routed group (expert, first row, rows, slot) and its
+// 16-entry token table (rows past n repeat the group's first token), then the
+// shared group's tiles, and n_tiles = their count.  With chunks (the grouped
+// GEMM's list): one chunk per routed group, then the shared group's, and
+// n_chunks = their count.  Generic pointers: LDS or memory.
+template <int NW>
+__device__ inline void small_route_tiles(const SmallRouteLds<NW>& L, int T, int k, int E, int4* tiles,
+                                         int32_t* tile_tok, int32_t* n_tiles, int4* chunks, int32_t* n_chunks) {
+  const int lane = threadIdx.x & 63;
+  const int F = T * k;
+  const int4 ri = L.rowi[lane];
+  const int2 rj = L.rowj[lane];
+  const int e_r = ri.x, f_r = ri.y, grp = ri.z, rank = ri.w, start = rj.x;
+  const bool valid = e_r >= 0, last = rj.y != 0;
+  const int nd = L.gnv[0];
+  const int ss = L.slots[E];
+  if (valid && last && chunks) chunks[grp] = make_int4(e_r, start, rank + 1, L.slots[e_r]);
+  if (!chunks) {
+    const int f_first = L.rowi[start & 63].y;   // the group's first entry
+    if (valid) {
+      tile_tok[grp * kTileRows + rank] = f_r / k;
+      if (last) {
+        tiles[grp] = make_int4(e_r, start, rank + 1, L.slots[e_r]);
+        for (int r = rank + 1; r < kTileRows; r++) tile_tok[grp * kTileRows + r] = f_first / k;  // padding
+      }
+    }
+    // the shared group: tiles after the routed ones, rows in token order
+    const int nts = (T + kTileRows - 1) / kTileRows;
+    if (lane < nts) tiles[nd + lane] = make_int4(E, F + lane * kTileRows, min(kTileRows, T - lane * kTileRows), ss);
+    for (int i = lane; i < nts * kTileRows; i += 64) {
+      const int tl = i / kTileRows, r = i % kTileRows;
+      const int n = min(kTileRows, T - tl * kTileRows);
+      tile_tok[(nd + tl) * kTileRows + r] = tl * kTileRows + (r < n ? r : 0);
+    }
+    if (lane == 0) *n_tiles = nd + nts;
+  } else if (lane == 0) {
+    chunks[nd] = make_int4(E, F, T, ss);   // T <= 16 <= kChunkRows
+    *n_chunks = nd + 1;
+  }
+}
+
+// The outputs, after the callers' last barrier, by a workgroup of NW
+// wavefronts: expert e's first row (the first group at or above e), its slot
+// and the status bits (threads e, e + 64 NW, ...); the rows' perm / inv_perm,
+// the groups' bounds and the work list (wavefront NW - 1); the tokens' ids,
+// weights and shared gates (wavefront t mod NW; needs z, small_route_topk with
+// gate); the fused launch's counters zeroed.
+template <int NW>
+__device__ inline void small_route_store(const SmallRouteLds<NW>& L, int T, int k, int E, int32_t n_slots,
+                                         int32_t* __restrict__ ids, float* __restrict__ wout,
+                                         float* __restrict__ sigma, int32_t* __restrict__ offsets,
+                                         int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+                                         int32_t* __restrict__ group_slot, int32_t* __restrict__ status,
+                                         int32_t* __restrict__ meta, int4* __restrict__ tiles,
+                                         int32_t* __restrict__ tile_tok, int4* __restrict__ chunks,
+                                         int32_t* __restrict__ sync, int64_t n_sync) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int F = T * k;
+  const int nd = L.gnv[0], nv = L.gnv[1];
+  for (int e = tid; e < E; e += NW * 64) {
+    int lo = 0, hi = nd;   // first g with ge[g] >= e
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (L.ge[mid] < e) lo = mid + 1;
+      else hi = mid;
+    }
+    const int slot = L.slots[e];
+    offsets[e] = lo < nd ? L.gp[lo] : nv;
+    group_slot[e] = slot;
+    if (lo < nd && L.ge[lo] == e) {
+      if (slot < 0) atomicOr(status, MOE_DEV_NOT_RESIDENT);
+      if (slot >= n_slots) atomicOr(status, MOE_DEV_BAD_SLOT);
+    }
+  }
+  if (wave == NW - 1) {
+    const int4 ri = L.rowi[lane];
+    if (ri.x >= 0) {
+      perm[lane] = ri.y;
+      inv_perm[ri.y] = lane;
+    }
+    if (lane < F) {
+      const int e0 = L.sid[lane];
+      if (e0 < 0 || e0 >= E) inv_perm[lane] = -1;   // (never for top-k winners)
+    }
+    if (lane == 0) {
+      const int ss = L.slots[E];
+      offsets[E] = nv;
+      offsets[E + 1] = F + T;
+      group_slot[E] = ss;
+      if (ss < 0) atomicOr(status, MOE_DEV_NOT_RESIDENT);
+      if (ss >= n_slots) atomicOr(status, MOE_DEV_BAD_SLOT);
+      if (nv < F) atomicOr(status, MOE_DEV_BAD_EXPERT_ID);
+    }
+    small_route_tiles<NW>(L, T, k, E, tiles, tile_tok, meta, chunks, meta + 1);
+  }
+  for (int t = wave; t < T; t += NW) topk_finish(L.wink + t * k, L.sid + t * k, t, k, L.z[t], ids, wout, sigma);
+  zero_sync(sync, n_sync);
+}
+
+}  // namespace moe

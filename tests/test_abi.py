@@ -134,6 +134,32 @@ def test_ffn_validation(B):
     assert B.raw_status("moe_expert_ffn_stages", d, *unaligned_pool[:-1], 2, None, None, None) == B.MOE_ERR_ALIGN
 
 
+def test_route_group_ffn_validation(B):
+    """moe_route_group_ffn validates like moe_route_group and
+    moe_expert_ffn_stages, and takes stages 1 or 3 only."""
+    dims = _d(B)
+    d = ctypes.byref(dims)
+    fake = 1 << 20
+    lay = B.moe_blob_layout_init(512, 256)
+    need = B.moe_workspace_bytes(dims)
+    ok = [0, fake, None, fake, fake, None, fake, fake, fake, fake, 4, fake, fake, fake, fake, fake, 1 << 30,
+          ctypes.byref(lay), fake, fake, fake, fake, need, 3, None, None, None]
+
+    def st(i, v):
+        a = list(ok)
+        a[i] = v
+        return B.raw_status("moe_route_group_ffn", d, *a)
+    for stages in (0, 2, 4, -1):
+        assert st(23, stages) == B.MOE_ERR_ARG
+    assert st(3, None) == B.MOE_ERR_ARG                         # neither router matrix nor logits
+    assert st(2, fake) == B.MOE_ERR_ARG                         # both
+    assert st(0, 1) == B.MOE_ERR_ARG                            # layer >= L
+    assert st(22, need - 256) == B.MOE_ERR_WORKSPACE
+    assert st(17, ctypes.byref(B.moe_blob_layout_init(512, 512))) == B.MOE_ERR_ARG
+    assert st(15, fake + 8) == B.MOE_ERR_ALIGN                  # pool
+    assert st(18, None) == B.MOE_ERR_ARG                        # h
+
+
 @pytest.mark.parametrize("H,I", [(128, 128), (256, 128), (2048, 512), (4096, 2048), (384, 640), (16384, 128)])
 def test_mx_blob_layout_matches_oracle(B, H, I):
     lay = B.moe_blob_layout_init_mx(H, I)
