@@ -680,7 +680,11 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
     small_route_topk<(RNPL > 0 ? RNPL : 1), 4>(rl.L, r.logits, ain, r.w_sg, r.T, a.H, r.E, r.k, r.slot_row,
                                                false);
     __syncthreads();
-    if (wave == 0) small_route_sort<4>(rl.L, r.T * r.k, r.E);
+    if (wave == 0) {
+      // the walkers' work list straight from the sorting wavefront's registers
+      const SortedRow row = small_route_sort<4>(rl.L, r.T * r.k, r.E);
+      if (blockIdx.x != 0) small_route_tiles<4>(rl.L, row, r.T, r.k, r.E, rl.tiles, rl.tok, rl.n, nullptr, nullptr);
+    }
     __syncthreads();
     if (blockIdx.x == 0) {
       // the shared gates here, not beside the top-k: their registers would
@@ -690,8 +694,6 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
                            r.group_slot, r.status, r.meta, r.tiles, r.tile_tok, nullptr, r.sync, r.n_sync);
       return;
     }
-    if (wave == 0) small_route_tiles<4>(rl.L, r.T, r.k, r.E, rl.tiles, rl.tok, rl.n, nullptr, nullptr);
-    __syncthreads();
     n_items = rl.n[0] * a.n_ug;
     first -= 1;
     stride -= 1;

@@ -11,13 +11,15 @@
 //  - small_route_topk: the slot row into LDS; token t by wavefront t mod NW
 //    (threshold top-k, topk_threshold); optionally the shared gate's dot
 //    product.
-//  - small_route_sort: wavefront 0 sorts the keys (expert << 6 | entry) across
-//    its lanes (bitonic network), so lane p holds row p of the grouped order;
-//    neighbour exchanges and two wavefront scans give each row its group's
-//    first row, its rank in the group and the group's tile (one tile per
-//    group: a group has at most T <= 16 rows).
+//  - small_route_sort: wavefront 0 ranks the distinct keys (expert << 6 |
+//    entry) by counting, for each lane, the smaller keys read lane by lane
+//    (readlane: no LDS round trip per step), and scatters them once through
+//    LDS, so lane p holds row p of the grouped order; its neighbours' keys and
+//    one wavefront scan give each row its group, its group's first row and its
+//    rank in the group (one tile per group: a group has at most T <= 16 rows).
 //  - small_route_tiles: the FFN work list (tiles and their token tables, or
-//    the GEMM's chunks) through generic pointers, so into LDS or memory.
+//    the GEMM's chunks) through generic pointers, so into LDS or memory, from
+//    the sorting wavefront's registers or from the rows the sort left in LDS.
 //  - small_route_store: every other output.  No global store comes before the
 //    callers' last barrier (a barrier waits for the wavefront's outstanding
 //    memory operations, stores included).
@@ -42,7 +44,22 @@ struct SmallRouteLds {
   int32_t gnv[2];                   // groups, valid rows
   int4 rowi[kSortF];                // row p: (expert, entry, group, rank)
   int2 rowj[kSortF];                // row p: (group's first row, last row of its group)
+  uint32_t skey[kSortF];            // the sort's scatter: row p's key
 };
+
+// Row p of the grouped order, held by lane p of the sorting wavefront.
+struct SortedRow {
+  int e;        // expert, -1 past the valid rows
+  int f;        // entry t k + j
+  int grp;      // group
+  int rank;     // rank in the group
+  int start;    // the group's first row
+  int f_first;  // the entry of that row
+  bool last;    // last row of the group
+  int nd, nv;   // groups, valid rows (the same in every lane)
+};
+
+constexpr uint32_t kNoRowKey = 1u << 30;   // above every valid key (expert < 2^10, entry < 2^6)
 
 // Inclusive max-scan of one wavefront (values >= 0) with DPP, the pattern of
 // wave_inclusive_scan: lanes shifted in from outside a row give 0.
@@ -109,46 +126,61 @@ __device__ inline void small_route_gate(SmallRouteLds<NW>& L, const uint16_t* __
 }
 
 // Wavefront 0, after the barrier that follows small_route_topk: the grouped
-// order of the F entries into rowi / rowj / ge / gp / gnv.  An entry whose
-// expert lies outside [0, E) (none, for top-k winners) sorts last and is not
-// valid.  The caller then meets a barrier.
+// order of the F entries, returned lane by lane and left in rowi / rowj / ge /
+// gp / gnv for small_route_store.  An entry whose expert lies outside [0, E)
+// (none, for top-k winners) sorts last and is not valid.  Keys are distinct, so
+// a valid key's rank (the count of smaller keys; only entries below F can be
+// smaller) is its row.
 template <int NW>
-__device__ inline void small_route_sort(SmallRouteLds<NW>& L, int F, int E) {
+__device__ inline SortedRow small_route_sort(SmallRouteLds<NW>& L, int F, int E) {
   const int lane = threadIdx.x & 63;
   const int e0 = lane < F ? L.sid[lane] : -1;
   const bool ok = lane < F && e0 >= 0 && e0 < E;
-  uint32_t key = ok ? ((uint32_t)e0 << 6) | (uint32_t)lane : 0xFFFFFFFFu;
+  const uint32_t key = ok ? ((uint32_t)e0 << 6) | (uint32_t)lane : kNoRowKey | (uint32_t)lane;
+  const int nv = __builtin_popcountll(__builtin_amdgcn_ballot_w64(ok));
+  int below = 0;
+  for (int j = 0; j < F; j += 4) {   // F <= 64; lanes from F on hold keys above every valid one
 #pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint32_t other = (uint32_t)__shfl_xor((int)key, stride);
-      const bool keep_min = ((lane & stride) == 0) == ((lane & size) == 0);
-      key = keep_min ? min(key, other) : max(key, other);
-    }
+    for (int u = 0; u < 4; u++) below += (uint32_t)__builtin_amdgcn_readlane((int)key, j + u) < key ? 1 : 0;
   }
-  const bool valid = key != 0xFFFFFFFFu;
-  const int e_r = (int)(key >> 6);
-  const int f_r = (int)(key & 63u);
-  const int nv = __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid));
-  const int e_prev = __shfl_up(e_r, 1);
-  const bool flag = valid && (lane == 0 || e_prev != e_r);
-  const bool flag_next = __shfl_down((int)flag, 1) != 0;
-  const bool last = valid && (lane == nv - 1 || flag_next);
+  if (ok) L.skey[below] = key;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const bool valid = lane < nv;
+  const uint32_t kp = valid ? L.skey[lane] : 0u;
+  const uint32_t kprev = valid && lane > 0 ? L.skey[lane - 1] : 0u;
+  const uint32_t knext = lane + 1 < nv ? L.skey[lane + 1] : 0u;
+  const int e_r = valid ? (int)(kp >> 6) : -1;
+  const int f_r = valid ? (int)(kp & 63u) : 63;
+  const bool flag = valid && (lane == 0 || (int)(kprev >> 6) != e_r);
+  const bool last = valid && (lane == nv - 1 || (int)(knext >> 6) != e_r);
   const int grp = wave_inclusive_scan(flag ? 1 : 0) - 1;
-  const int start = wave_inclusive_max(flag ? lane : 0);
-  const int rank = lane - start;
+  // the latest group start at or below this row, with its entry in the low bits
+  const int sf = wave_inclusive_max(flag ? (lane << 6) | f_r : 0);
+  const int start = sf >> 6;
   const int nd = __builtin_popcountll(__builtin_amdgcn_ballot_w64(flag));
   if (flag) {
     L.ge[grp] = e_r;
     L.gp[grp] = lane;
   }
-  L.rowi[lane] = make_int4(valid ? e_r : -1, f_r, grp, rank);
+  L.rowi[lane] = make_int4(e_r, f_r, grp, lane - start);
   L.rowj[lane] = make_int2(start, last ? 1 : 0);
   if (lane == 0) {
     L.gnv[0] = nd;
     L.gnv[1] = nv;
   }
+  return SortedRow{e_r, f_r, grp, lane - start, start, sf & 63, last, nd, nv};
+}
+
+// The sorted row of this lane from what small_route_sort left in LDS (after a
+// barrier, in a wavefront other than the sorting one).
+template <int NW>
+__device__ inline SortedRow sorted_row_from_lds(const SmallRouteLds<NW>& L) {
+  const int lane = threadIdx.x & 63;
+  const int4 ri = L.rowi[lane];
+  const int2 rj = L.rowj[lane];
+  return SortedRow{ri.x, ri.y, ri.z, ri.w, rj.x, L.rowi[rj.x & 63].y, rj.y != 0, L.gnv[0], L.gnv[1]};
 }
 
 // One wavefront (lane = row): the FFN work list of the grouped rows.  Without
@@ -158,23 +190,23 @@ __device__ inline void small_route_sort(SmallRouteLds<NW>& L, int F, int E) {
 // GEMM's list): one chunk per routed group, then the shared group's, and
 // n_chunks = their count.  Generic pointers: LDS or memory.
 template <int NW>
-__device__ inline void small_route_tiles(const SmallRouteLds<NW>& L, int T, int k, int E, int4* tiles,
-                                         int32_t* tile_tok, int32_t* n_tiles, int4* chunks, int32_t* n_chunks) {
+__device__ inline void small_route_tiles(const SmallRouteLds<NW>& L, const SortedRow& row, int T, int k, int E,
+                                         int4* tiles, int32_t* tile_tok, int32_t* n_tiles, int4* chunks,
+                                         int32_t* n_chunks) {
   const int lane = threadIdx.x & 63;
   const int F = T * k;
-  const int4 ri = L.rowi[lane];
-  const int2 rj = L.rowj[lane];
-  const int e_r = ri.x, f_r = ri.y, grp = ri.z, rank = ri.w, start = rj.x;
-  const bool valid = e_r >= 0, last = rj.y != 0;
-  const int nd = L.gnv[0];
+  const int e_r = row.e, f_r = row.f, grp = row.grp, rank = row.rank, start = row.start;
+  const bool valid = e_r >= 0, last = row.last;
+  const int nd = row.nd;
   const int ss = L.slots[E];
-  if (valid && last && chunks) chunks[grp] = make_int4(e_r, start, rank + 1, L.slots[e_r]);
+  const int se = valid ? L.slots[e_r] : -1;
+  if (valid && last && chunks) chunks[grp] = make_int4(e_r, start, rank + 1, se);
   if (!chunks) {
-    const int f_first = L.rowi[start & 63].y;   // the group's first entry
+    const int f_first = row.f_first;   // the group's first entry
     if (valid) {
       tile_tok[grp * kTileRows + rank] = f_r / k;
       if (last) {
-        tiles[grp] = make_int4(e_r, start, rank + 1, L.slots[e_r]);
+        tiles[grp] = make_int4(e_r, start, rank + 1, se);
         for (int r = rank + 1; r < kTileRows; r++) tile_tok[grp * kTileRows + r] = f_first / k;  // padding
       }
     }
@@ -245,7 +277,7 @@ __device__ inline void small_route_store(const SmallRouteLds<NW>& L, int T, int 
       if (ss >= n_slots) atomicOr(status, MOE_DEV_BAD_SLOT);
       if (nv < F) atomicOr(status, MOE_DEV_BAD_EXPERT_ID);
     }
-    small_route_tiles<NW>(L, T, k, E, tiles, tile_tok, meta, chunks, meta + 1);
+    small_route_tiles<NW>(L, sorted_row_from_lds(L), T, k, E, tiles, tile_tok, meta, chunks, meta + 1);
   }
   for (int t = wave; t < T; t += NW) topk_finish(L.wink + t * k, L.sid + t * k, t, k, L.z[t], ids, wout, sigma);
   zero_sync(sync, n_sync);

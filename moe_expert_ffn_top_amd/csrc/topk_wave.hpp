@@ -231,10 +231,15 @@ __device__ inline void topk_threshold(uint32_t* key, int k, uint32_t* win_k, int
   __builtin_amdgcn_wave_barrier();
   const uint2 me = lane < n ? cand[lane] : make_uint2(0u, 0u);
   int rank = 0;
-#pragma unroll 4
-  for (int j = 0; j < n; j++) {
-    const uint2 o = cand[j];
-    rank += (o.x > me.x || (o.x == me.x && o.y < me.y)) ? 1 : 0;
+  // the other candidates lane by lane, from registers; lanes from n on hold
+  // (0, 0), which never outranks a candidate (candidate keys are not 0)
+  for (int j = 0; j < n; j += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const uint32_t ox = (uint32_t)__builtin_amdgcn_readlane((int)me.x, j + u);
+      const uint32_t oy = (uint32_t)__builtin_amdgcn_readlane((int)me.y, j + u);
+      rank += (ox > me.x || (ox == me.x && oy < me.y)) ? 1 : 0;
+    }
   }
   if (lane < n && rank < k) {
     win_k[rank] = me.x;
