@@ -140,9 +140,32 @@ class HipEvents:
         self.handles = []
 
 
+def source_hash(path):
+    """sha256[:16] of a kernel source followed by the library headers it
+    includes (#include "x.hpp", recursively, each once), so a change to any
+    code compiled into the kernel changes the hash."""
+    h, seen = hashlib.sha256(), set()
+
+    def add(f):
+        if f in seen:
+            return
+        seen.add(f)
+        with open(f, "rb") as fh:
+            data = fh.read()
+        h.update(data)
+        for line in data.decode("utf-8", "replace").splitlines():
+            line = line.strip()
+            if line.startswith('#include "'):
+                inc = os.path.join(os.path.dirname(f), line.split('"')[1])
+                if os.path.exists(inc):
+                    add(inc)
+
+    add(path)
+    return h.hexdigest()[:16]
+
+
 def kernel_source_hash(cfg):
-    with open(ffn_kernel(cfg)[1], "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    return source_hash(ffn_kernel(cfg)[1])
 
 
 def recorded_traffic(cfg):
@@ -237,11 +260,9 @@ class Workload:
     @property
     def routed(self):
         """NVFP4 decode windows with drawn logits that moe_route_group_ffn runs in
-        one launch (T <= 16, T k <= 64, E <= 1024): route, group and gate/up
-        together, then the down stage and the combine."""
-        c = self.cfg
-        return (not self.mx and self.wr is None and self.ffn_mode == "routed" and c.T * c.k < 16 * c.E
-                and c.T <= 16 and c.T * c.k <= 64 and c.E <= 1024)
+        one launch: route, group and gate/up together, then the down stage and
+        the combine."""
+        return self.wr is None and self.ffn_mode == "routed" and routed_shape(self.cfg)
 
     def ffn_combine(self, x, ev_start=None, ev_stop=None, stream=None):
         from moe_expert_ffn_top_amd import binding as B
@@ -786,8 +807,7 @@ def measure_probes(B):
             best_t = max(best_t, grid * 4 * iters * 4 * flop / (ms * 1e-3) / 1e12)
         out[name + "_tflops"] = best_t
         out[name + "_frac_of_spec"] = best_t / spec
-    with open(os.path.join(CSRC, "probes.hip"), "rb") as f:
-        out["kernel_source_sha256_16"] = hashlib.sha256(f.read()).hexdigest()[:16]
+    out["kernel_source_sha256_16"] = source_hash(os.path.join(CSRC, "probes.hip"))
     log("probes: %s" % out)
     return out
 
@@ -857,12 +877,18 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def routed_shape(cfg):
+    """The shapes whose routing moe_route_group_ffn runs inside the gate/up
+    launch: NVFP4 weight streaming (T k < 16 E), T <= 16, T k <= 256, E <= 1024."""
+    return (cfg.fmt != "mx" and cfg.T * cfg.k < 16 * cfg.E and cfg.T <= 16 and cfg.T * cfg.k <= 256
+            and cfg.E <= 1024)
+
+
 def ffn_label(cfg, ffn):
     """The FFN path a workload runs (Workload's choice, from the shapes)."""
     if cfg.T * cfg.k >= 16 * cfg.E:
         return "grouped GEMM"
-    if ffn == "routed" and not (cfg.fmt != "mx" and cfg.router == "zipf" and cfg.T <= 16 and cfg.T * cfg.k <= 64
-                                and cfg.E <= 1024):
+    if ffn == "routed" and not (cfg.router == "zipf" and routed_shape(cfg)):
         return "split"
     return ffn
 

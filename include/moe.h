@@ -403,7 +403,7 @@ int moe_expert_ffn_combine(const moe_dims* d, const uint16_t* x, const void* poo
  * moe_route_group followed by moe_expert_ffn_stages on the same stream, with
  * exactly their arguments, validation and results (every output of both
  * bit-identical); stages is 1 (gate/up) or 3 (gate/up and down).  For decode
- * windows with drawn logits (logits_in, not w_router; T <= 16, T*k <= 64,
+ * windows with drawn logits (logits_in, not w_router; T <= 16, T*k <= 256,
  * E <= 1024, T*k < 16 E) the routing runs inside the gate/up launch
  * ([FreeToken] 3.5: a step's control flow stays on the device): every
  * workgroup selects the window's top-k and groups it into its own work list,

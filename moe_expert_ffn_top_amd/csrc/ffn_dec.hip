@@ -648,7 +648,7 @@ __device__ inline void stage_walk(Start<GATEUP, SPLITK, S, U, FS, MX>& st, const
 
 // One stage as its own launch (stages split, and the MX path).
 // ROUTE (gate/up on NVFP4 blobs, RouteArgs r): every workgroup first routes
-// and groups the window itself (T <= 16, T k <= 64, E <= 1024) into LDS, the
+// and groups the window itself (T <= 16, T k <= 256, E <= 1024) into LDS, the
 // same in each.  Workgroup 0 then stores the routing outputs and ends;
 // workgroups 1 .. G walk the items with the work list from LDS (item i goes to
 // workgroup 1 + i mod (G - 1)), so no item waits on those stores and the walk
@@ -677,14 +677,13 @@ __global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restri
   int n_items, first = blockIdx.x, stride = gridDim.x;
   if constexpr (ROUTE) {
     const int wave = threadIdx.x >> 6;
-    small_route_topk<(RNPL > 0 ? RNPL : 1), 4>(rl.L, r.logits, ain, r.w_sg, r.T, a.H, r.E, r.k, r.slot_row,
-                                               false);
+    const int F = r.T * r.k;
+    small_route_topk<(RNPL > 0 ? RNPL : 1), 4, false>(rl.L, r.logits, ain, r.w_sg, r.T, a.H, r.E, r.k, r.slot_row);
     __syncthreads();
-    if (wave == 0) {
-      // the walkers' work list straight from the sorting wavefront's registers
-      const SortedRow row = small_route_sort<4>(rl.L, r.T * r.k, r.E);
-      if (blockIdx.x != 0) small_route_tiles<4>(rl.L, row, r.T, r.k, r.E, rl.tiles, rl.tok, rl.n, nullptr, nullptr);
-    }
+    // the walkers' work list straight from the sorting wavefronts' registers
+    const SortedRow row = small_route_sort_rows<4>(rl.L, F, r.E);
+    if (blockIdx.x != 0 && wave < sort_waves(F))
+      small_route_tiles<4>(rl.L, row, r.T, r.k, r.E, rl.tiles, rl.tok, rl.n, nullptr, nullptr, wave == 0, false);
     __syncthreads();
     if (blockIdx.x == 0) {
       // the shared gates here, not beside the top-k: their registers would
@@ -1000,8 +999,10 @@ hipError_t launch_dec_stages(const moe_dims& d, const uint16_t* x, const FfnGeom
     const bool gu = stage == 0;
     const int64_t cap = (int64_t)n_cu * (gu ? MOE_DEC_WGS_GU : MOE_DEC_WGS_DN);
     const Split sp = stage_split(d, gu, mx);
-    const DecArgs a = dec_args(d, g, wl, sp);
-    const int64_t items = (int64_t)wl.max_tiles * a.n_ug;
+    DecArgs a = dec_args(d, g, wl, sp);
+    // a routing launch's work list is in LDS: at most kRouteMaxTiles entries
+    if (gu && route && a.max_tiles > kRouteMaxTiles) a.max_tiles = kRouteMaxTiles;
+    const int64_t items = (int64_t)a.max_tiles * a.n_ug;
     // a routing launch has one more workgroup, which only stores the routing;
     // the grid stays within the resident cap (a workgroup beyond it would
     // start only when another ends)

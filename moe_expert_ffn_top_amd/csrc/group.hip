@@ -368,9 +368,10 @@ __global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict_
                    tile_tok, tile_base, chunks, hist, cntl, tbl, sid, lds, minr, skip_rank, n_skipped);
 }
 
-// Route and group fused for small windows (T <= 16 tokens, drawn logits), one
-// 1024-thread block.  T*k <= 64 entries: the sort path of route_small.hpp
-// (threshold top-k per token wavefront, one wavefront's bitonic sort).
+// Route and group fused for small windows (T <= 16 tokens, T*k <= 256
+// entries, drawn logits), one 1024-thread block: the sort path of
+// route_small.hpp (threshold top-k per token wavefront, then the grouped order
+// by rank counting).
 template <int NPL>
 __global__ __launch_bounds__(1024) void k_route_group_sort(
     const float* __restrict__ logits, const uint16_t* __restrict__ x, const float* __restrict__ w_sg, int T, int H,
@@ -381,57 +382,14 @@ __global__ __launch_bounds__(1024) void k_route_group_sort(
     int32_t* __restrict__ sync, int64_t n_sync) {
   __shared__ SmallRouteLds<16> L;
   STAGE_STAMP(1, 0);
-  small_route_topk<NPL, 16>(L, logits, x, w_sg, T, H, E, k, slot_table + (int64_t)layer * (E + 1), true);
+  small_route_topk<NPL, 16, true>(L, logits, x, w_sg, T, H, E, k, slot_table + (int64_t)layer * (E + 1));
   __syncthreads();
   STAGE_STAMP(1, 1);
-  if ((threadIdx.x >> 6) == 0) small_route_sort<16>(L, T * k, E);
+  small_route_sort_rows<16>(L, T * k, E);
   __syncthreads();
   STAGE_STAMP(1, 2);
   small_route_store<16>(L, T, k, E, n_slots, ids, wout, sigma, offsets, perm, inv_perm, group_slot, status, meta,
                         tiles, tile_tok, chunks, sync, n_sync);
-  STAGE_STAMP(1, 3);
-}
-
-// T*k in (64, kSmallF]: the threshold top-k per token wavefront, then the
-// block-scan grouping (group_small_tail), then the softmax, one 1024-thread
-// block; every barrier comes before the kernel's first global store.
-template <int NPL>
-__global__ __launch_bounds__(1024) void k_route_group_small(
-    const float* __restrict__ logits, const uint16_t* __restrict__ x, const float* __restrict__ w_sg, int T, int H,
-    int E, int k, int layer, const int32_t* __restrict__ slot_table, int32_t n_slots, int32_t* __restrict__ ids,
-    float* __restrict__ wout, float* __restrict__ sigma, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv_perm, int32_t* __restrict__ group_slot, int32_t* __restrict__ status,
-    int32_t* __restrict__ meta, int4* __restrict__ tiles, int32_t* __restrict__ tile_tok,
-    int32_t* __restrict__ tile_base, int4* __restrict__ chunks, int32_t* __restrict__ sync, int64_t n_sync) {
-  __shared__ __align__(16) int32_t sid[kSmallF];  // the winners' experts, [T][k] (entry f = t k + j)
-  __shared__ uint32_t wink[kSmallF];               // the winners' keys
-  __shared__ uint2 cand[16 * 64];                  // top-k candidates, 64 per token
-  __shared__ int32_t hist[1024];
-  __shared__ int32_t cntl[1024];
-  __shared__ int32_t tbl[1024];
-  __shared__ int lds[17];
-  const int tid = threadIdx.x, wave = tid >> 6;
-  const int F = T * k;
-  STAGE_STAMP(1, 0);
-  const int slot = tid < E ? slot_table[(int64_t)layer * (E + 1) + tid] : -1;
-  const int ss = slot_table[(int64_t)layer * (E + 1) + E];
-  if (tid >= F && tid < kSmallF) sid[tid] = -1;
-  if (tid < E) hist[tid] = 0;
-  const int t = wave;
-  GateIn g;
-  if (t < T) {
-    uint32_t key[NPL];
-    load_keys<NPL>(key, logits, t, E, 0, E);
-    gate_load(g, x, w_sg, t, H);
-    topk_threshold<NPL>(key, k, wink + t * k, sid + t * k, cand + t * 64);
-  }
-  __syncthreads();
-  STAGE_STAMP(1, 1);
-  const int e_mine = tid < F ? sid[tid] : -1;
-  group_small_tail(e_mine, F, T, k, E, slot, ss, n_slots, offsets, perm, inv_perm, group_slot, status, meta, tiles,
-                   tile_tok, tile_base, chunks, hist, cntl, tbl, sid, lds);
-  if (t < T) topk_finish(wink + t * k, sid + t * k, t, k, gate_dot(g, x, w_sg, t, H), ids, wout, sigma);
-  zero_sync(sync, n_sync);
   STAGE_STAMP(1, 3);
 }
 
@@ -512,7 +470,7 @@ hipError_t launch_group(const moe_dims& d, int32_t layer, const int32_t* ids, co
   return hipGetLastError();
 }
 
-bool route_group_fusable(const moe_dims& d) { return d.T <= 16 && (int64_t)d.T * d.k <= kSmallF; }
+bool route_group_fusable(const moe_dims& d) { return d.T <= 16 && (int64_t)d.T * d.k <= kSortF; }
 
 hipError_t launch_route_group(const moe_dims& d, int32_t layer, const float* logits, const uint16_t* x,
                               const float* w_sg, const int32_t* slot_table, int32_t n_slots, int32_t* ids, float* w,
@@ -523,34 +481,23 @@ hipError_t launch_route_group(const moe_dims& d, int32_t layer, const float* log
   int32_t* meta = reinterpret_cast<int32_t*>(base + wl.off_meta);
   int4* tiles = reinterpret_cast<int4*>(base + wl.off_tiles);
   int32_t* tile_tok = reinterpret_cast<int32_t*>(base + wl.off_tile_tok);
-  int32_t* tile_base = reinterpret_cast<int32_t*>(base + wl.off_tile_base);
   int4* chunks = use_gemm(d) ? reinterpret_cast<int4*>(base + wl.off_chunks) : nullptr;
   int32_t* sync = reinterpret_cast<int32_t*>(base + wl.off_sync);
   const int npl = (d.E + 63) / 64;
-  const bool sort = (int64_t)d.T * d.k <= kSortF;
   const dim3 g(1), b(1024);
   const int32_t* st = slot_table;
 #define MOE_RG_SORT(N)                                                                                             \
   hipLaunchKernelGGL((k_route_group_sort<N>), g, b, 0, s, logits, x, w_sg, d.T, d.H, d.E, d.k, layer, st, n_slots, \
                      ids, w, sigma, offsets, perm, inv_perm, group_slot, dev_status, meta, tiles, tile_tok, chunks,   \
                      sync, wl.n_sync)
-#define MOE_RG_SMALL(N)                                                                                             \
-  hipLaunchKernelGGL((k_route_group_small<N>), g, b, 0, s, logits, x, w_sg, d.T, d.H, d.E, d.k, layer, st, n_slots, \
-                     ids, w, sigma, offsets, perm, inv_perm, group_slot, dev_status, meta, tiles, tile_tok,          \
-                     tile_base, chunks, sync, wl.n_sync)
 #define MOE_RG_NPL(L)                 \
   if (npl <= 1) L(1);                 \
   else if (npl <= 2) L(2);            \
   else if (npl <= 4) L(4);            \
   else if (npl <= 8) L(8);            \
   else L(16);
-  if (sort) {
-    MOE_RG_NPL(MOE_RG_SORT)
-  } else {
-    MOE_RG_NPL(MOE_RG_SMALL)
-  }
+  MOE_RG_NPL(MOE_RG_SORT)
 #undef MOE_RG_NPL
-#undef MOE_RG_SMALL
 #undef MOE_RG_SORT
   return hipGetLastError();
 }

@@ -14,25 +14,25 @@ namespace moe {
 
 // Order-preserving map of a finite fp32 to uint32 (a larger float gets a larger
 // key).  -0 is first made +0: the two zeros compare equal and must tie.
-__device__ inline uint32_t f32_key(float v) {
+__device__ __forceinline__ uint32_t f32_key(float v) {
   uint32_t u = __float_as_uint(v);
   u = (u == 0x80000000u) ? 0u : u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ inline float key_f32(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k); }
+__device__ __forceinline__ float key_f32(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k); }
 
 // DPP lane exchange (lanes a row mask leaves out keep their own value).
 template <int CTRL, int ROWMASK = 0xF>
-__device__ inline uint32_t dpp_u32(uint32_t v) {
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWMASK, 0xF, false);
 }
 template <int CTRL, int ROWMASK = 0xF>
-__device__ inline float dpp_f32(float v) {
+__device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWMASK, 0xF, false));
 }
 // Wave-wide max: within quads (xor 1, xor 2), half rows and rows, then the row
 // broadcasts fold rows 0..3 into lane 63, which every lane reads back.
-__device__ inline uint32_t wave_max_u32(uint32_t v) {
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
   v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
   v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));
@@ -42,7 +42,7 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 // fixed-order (deterministic) wave sum
-__device__ inline float wave_sum_f32(float v) {
+__device__ __forceinline__ float wave_sum_f32(float v) {
   v += dpp_f32<0xB1>(v);
   v += dpp_f32<0x4E>(v);
   v += dpp_f32<0x141>(v);
@@ -60,7 +60,7 @@ struct GateIn {
   float4 wv[4][2];
 };
 
-__device__ inline void gate_load(GateIn& g, const uint16_t* __restrict__ x, const float* __restrict__ w_sg, int t,
+__device__ __forceinline__ void gate_load(GateIn& g, const uint16_t* __restrict__ x, const float* __restrict__ w_sg, int t,
                                  int H) {
   const int lane = threadIdx.x & 63;
   const int nch = H / 8;
@@ -75,7 +75,7 @@ __device__ inline void gate_load(GateIn& g, const uint16_t* __restrict__ x, cons
 }
 
 // z = x[t] . w_sg: lane-strided chunks, then a fixed-order wave sum.
-__device__ inline float gate_dot(const GateIn& g, const uint16_t* __restrict__ x, const float* __restrict__ w_sg,
+__device__ __forceinline__ float gate_dot(const GateIn& g, const uint16_t* __restrict__ x, const float* __restrict__ w_sg,
                                  int t, int H) {
   const int lane = threadIdx.x & 63;
   const int nch = H / 8;
@@ -110,7 +110,7 @@ __device__ inline float gate_dot(const GateIn& g, const uint16_t* __restrict__ x
 
 // This lane's keys of experts e0 + lane + 64 i (i < NPL), 0 past e1.
 template <int NPL>
-__device__ inline void load_keys(uint32_t* key, const float* __restrict__ logits, int t, int E, int e0, int e1) {
+__device__ __forceinline__ void load_keys(uint32_t* key, const float* __restrict__ logits, int t, int E, int e0, int e1) {
   const int lane = threadIdx.x & 63;
   float v[NPL];
 #pragma unroll
@@ -124,7 +124,7 @@ __device__ inline void load_keys(uint32_t* key, const float* __restrict__ logits
 // lane 0 writes round j's key and expert to win_k[j], win_i[j].  kk must not
 // exceed the number of entries.
 template <int NPL>
-__device__ inline void topk_rounds(uint32_t* key, int e0, int kk, uint32_t* win_k, int* win_i) {
+__device__ __forceinline__ void topk_rounds(uint32_t* key, int e0, int kk, uint32_t* win_k, int* win_i) {
   const int lane = threadIdx.x & 63;
   for (int j = 0; j < kk; j++) {
     uint32_t kb = key[0];
@@ -151,7 +151,7 @@ __device__ inline void topk_rounds(uint32_t* key, int e0, int kk, uint32_t* win_
 // Renormalised softmax over the k winners (win_k / win_i in slot order, in
 // LDS, written by this wavefront or before a barrier); lane l takes slots l,
 // l + 64, ...; z is the shared gate's dot product.
-__device__ inline void topk_finish(const uint32_t* win_k, const int* win_i, int t, int k, float z,
+__device__ __forceinline__ void topk_finish(const uint32_t* win_k, const int* win_i, int t, int k, float z,
                                    int32_t* __restrict__ ids, float* __restrict__ wout, float* __restrict__ sigma) {
   const int lane = threadIdx.x & 63;
   __builtin_amdgcn_wave_barrier();
@@ -171,7 +171,7 @@ __device__ inline void topk_finish(const uint32_t* win_k, const int* win_i, int 
 // that receive the winners' keys and expert indices in slot order (lane 0
 // writes them); ids / wout / sigma receive the token's outputs.
 template <int NPL>
-__device__ inline void topk_wave(const float* __restrict__ logits, const uint16_t* __restrict__ x,
+__device__ __forceinline__ void topk_wave(const float* __restrict__ logits, const uint16_t* __restrict__ x,
                                  const float* __restrict__ w_sg, int t, int H, int E, int k,
                                  int32_t* __restrict__ ids, float* __restrict__ wout, float* __restrict__ sigma,
                                  uint32_t* win_k, int* win_i) {
@@ -195,7 +195,7 @@ __device__ inline void topk_wave(const float* __restrict__ logits, const uint16_
 // winners land in win_k / win_i in slot order.  More than 64 such keys, or
 // k > 64: the arg-max rounds instead.  Same winners, same order either way.
 template <int NPL>
-__device__ inline void topk_threshold(uint32_t* key, int k, uint32_t* win_k, int* win_i, uint2* cand) {
+__device__ __forceinline__ void topk_threshold(uint32_t* key, int k, uint32_t* win_k, int* win_i, uint2* cand) {
   const int lane = threadIdx.x & 63;
   if (k > 64) {
     topk_rounds<NPL>(key, 0, k, win_k, win_i);

@@ -98,6 +98,12 @@ SMALL = {
     # chunks give 800 gate/up and 400 down items, so each persistent workgroup
     # walks several, loading the next while finishing the last
     "gemm_many_items": Config(44, "mi", T=2048, H=512, I=512, E=64, k=8, L=1, router="matrix"),
+    # small-window routing with T*k above one wavefront's 64 lanes: the sort
+    # ranks over 2 (96 entries), 2 with one row in the second (65) and 4 (256)
+    # wavefronts
+    "sort_f96": Config(45, "s96", T=16, H=256, I=128, E=256, k=6, L=1, router="zipf", zipf_s=1.2),
+    "sort_f65": Config(46, "s65", T=13, H=128, I=96, E=40, k=5, L=1, router="zipf", zipf_s=0.7),
+    "sort_f256": Config(47, "s256", T=16, H=128, I=64, E=64, k=16, L=1, router="zipf", zipf_s=1.0),
 }
 
 
@@ -113,7 +119,7 @@ def test_layer_parity_small(B, hostgen, name):
 
 
 @pytest.mark.parametrize("cname", ["tiny", "k_equals_E", "E1024_max", "big_k_wide", "multitile_ragged",
-                                   "decode48_window"])
+                                   "decode48_window", "sort_f96", "sort_f65", "sort_f256"])
 def test_route_group_matches_separate_calls(B, hostgen, cname):
     """moe_route_group (one fused kernel for T <= 16, T*k <= 256; separate
     kernels otherwise) gives the bits of moe_route then moe_group."""

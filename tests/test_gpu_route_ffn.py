@@ -7,8 +7,11 @@ grouping the window for itself and one more storing the routing outputs.
   ids, weights, sigma, offsets, perm, inv_perm, group_slot, status, the live
   rows of h and Y, and y, all bit for bit; the decode48 shape also against the
   oracle.
-- Shapes: the 48-layer decode window (T = 4, k = 10, E = 512); T k = 64 (the
-  sort's limit); one token; E = 1000 (16 logits per lane, not a multiple of
+- Shapes: the 48-layer decode window (T = 4, k = 10, E = 512); T k = 64 (one
+  sorting wavefront's limit); the 43-layer decode window's routing (T = 16,
+  k = 6, E = 256: two sorting wavefronts); T k = 65 (a second wavefront with
+  one row); T k = 256 (four wavefronts, groups of up to 16 rows); T k = 200
+  with E = 1000; one token; E = 1000 (16 logits per lane, not a multiple of
   64); H = 512, I = 256.
 - A routed expert and the shared expert not resident: the status bits and zero
   rows, as on the separate path.
@@ -41,6 +44,10 @@ CASES = {
     "f64": Config(83, "r3", T=16, H=512, I=256, E=64, k=4, L=1, router="zipf", zipf_s=1.2),
     "one_token": Config(84, "r4", T=1, H=512, I=256, E=96, k=3, L=1, router="zipf", zipf_s=1.0),
     "e1000": Config(85, "r5", T=3, H=512, I=256, E=1000, k=7, L=1, router="zipf", zipf_s=1.1),
+    "f96_decode43_routing": Config(87, "r7", T=16, H=512, I=256, E=256, k=6, L=1, router="zipf", zipf_s=1.2),
+    "f65": Config(88, "r8", T=13, H=512, I=256, E=40, k=5, L=1, router="zipf", zipf_s=0.7),
+    "f256": Config(89, "r9", T=16, H=512, I=256, E=64, k=16, L=1, router="zipf", zipf_s=1.0),
+    "f200_e1000": Config(90, "r10", T=10, H=512, I=256, E=1000, k=20, L=1, router="zipf", zipf_s=1.1),
 }
 
 
