@@ -187,13 +187,18 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ logits, cons
 }
 
 // Top-k of one token by the calling wavefront through a threshold: tau = the
-// k-th largest of the 64 lane maxima (a 32-step radix select over one value
-// per lane, ballot and popcount).  The k largest keys are all >= tau: the k
-// lanes whose maxima reach tau hold k distinct keys >= tau.  The keys >= tau
-// (usually a little over k) are compacted into cand (LDS, 64 entries of this
-// wavefront) and ranked exactly under (key descending, expert ascending); the
-// winners land in win_k / win_i in slot order.  More than 64 such keys, or
-// k > 64: the arg-max rounds instead.  Same winners, same order either way.
+// k-th largest of the 64 lane maxima with its low 16 bits cleared (a radix
+// select over the top 16 bits of one value per lane, ballot and popcount).
+// The k largest keys are all >= tau: the k lanes whose maxima reach tau hold k
+// distinct keys >= tau.  A lower tau only admits more candidates, and the 16
+// bits kept (sign, exponent, 7 mantissa bits) already leave few keys of
+// continuous logits between tau and the k-th key.  The keys >= tau (usually a
+// little over k) are compacted into cand (LDS, 64 entries of this wavefront,
+// 16-byte aligned) and ranked exactly under (key descending, expert
+// ascending): each candidate counts those that outrank it, two per broadcast
+// LDS read, as 64-bit (key, ~expert) compares.  The winners land in win_k /
+// win_i in slot order.  More than 64 such keys, or k > 64: the arg-max rounds
+// instead.  Same winners, same order either way.
 template <int NPL>
 __device__ __forceinline__ void topk_threshold(uint32_t* key, int k, uint32_t* win_k, int* win_i, uint2* cand) {
   const int lane = threadIdx.x & 63;
@@ -205,7 +210,7 @@ __device__ __forceinline__ void topk_threshold(uint32_t* key, int k, uint32_t* w
 #pragma unroll
   for (int i = 1; i < NPL; i++) lm = max(lm, key[i]);
   uint32_t tau = 0;
-  for (int b = 31; b >= 0; b--) {
+  for (int b = 31; b >= 16; b--) {
     const uint32_t c = tau | (1u << b);
     if (__builtin_popcountll(__builtin_amdgcn_ballot_w64(lm >= c)) >= k) tau = c;
   }
@@ -230,16 +235,15 @@ __device__ __forceinline__ void topk_threshold(uint32_t* key, int k, uint32_t* w
   }
   __builtin_amdgcn_wave_barrier();
   const uint2 me = lane < n ? cand[lane] : make_uint2(0u, 0u);
+  // (key, ~expert) as one 64-bit value: larger means ranked earlier
+  const uint64_t pm = ((uint64_t)me.x << 32) | (uint32_t)~me.y;
+  const uint4* c4 = reinterpret_cast<const uint4*>(cand);
   int rank = 0;
-  // the other candidates lane by lane, from registers; lanes from n on hold
-  // (0, 0), which never outranks a candidate (candidate keys are not 0)
-  for (int j = 0; j < n; j += 4) {
-#pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const uint32_t ox = (uint32_t)__builtin_amdgcn_readlane((int)me.x, j + u);
-      const uint32_t oy = (uint32_t)__builtin_amdgcn_readlane((int)me.y, j + u);
-      rank += (ox > me.x || (ox == me.x && oy < me.y)) ? 1 : 0;
-    }
+#pragma unroll 4
+  for (int j = 0; j < n; j += 2) {   // two candidates per read; a last odd one masked
+    const uint4 v = c4[j >> 1];
+    rank += (((uint64_t)v.x << 32) | (uint32_t)~v.y) > pm ? 1 : 0;
+    rank += (j + 1 < n && (((uint64_t)v.z << 32) | (uint32_t)~v.w) > pm) ? 1 : 0;
   }
   if (lane < n && rank < k) {
     win_k[rank] = me.x;

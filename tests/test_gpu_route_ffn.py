@@ -17,7 +17,10 @@ grouping the window for itself and one more storing the routing outputs.
   rows, as on the separate path.
 - stages = 1, then the down stage on its own.
 - The step captured in a HIP graph, replayed with eager work between.
-- The router matrix (w_router): the separate kernels, the same results."""
+- The router matrix (w_router): the separate kernels, the same results.
+- Tied logits (a half-unit grid; one token with every logit equal, which
+  leaves more than 64 candidates at the threshold; -0 beside +0): the same
+  winners and slot order as the separate launches, and as the oracle's top-k."""
 import numpy as np
 import pytest
 import torch
@@ -180,3 +183,26 @@ def test_route_group_ffn_router_matrix_runs_separately(B, hostgen):
     c.combine(B)
     torch.cuda.synchronize()
     assert_same(snapshot(c), want, "router matrix")
+
+
+@pytest.mark.parametrize("T,E,k", [(4, 512, 10), (16, 256, 6), (13, 40, 5), (16, 64, 16)])
+def test_route_group_ffn_tied_logits(B, hostgen, T, E, k):
+    cfg = Config(91, "r11", T=T, H=512, I=256, E=E, k=k, L=1, router="zipf", zipf_s=1.0)
+    say("[gpu] route + group + FFN on tied logits (T=%d E=%d k=%d)" % (T, E, k))
+    c = FCase(B, cfg, hostgen)
+    rng = np.random.default_rng(T * 131 + E + k)
+    lg = (np.round(rng.normal(size=(T, E)) * 2) / 2).astype(np.float32)
+    lg[0, :] = 0.25
+    if T > 1:
+        lg[1, 0::2] = -0.0
+        lg[1, 1::2] = 0.0
+    c.lg = lg
+    c.lg_t = torch.from_numpy(lg).cuda()
+    want = separate(B, c)
+    assert np.array_equal(want["ids"].cpu().numpy(), O.topk(lg, k))
+    for rep in range(2):
+        scramble(c)
+        route_group_ffn(B, c)
+        c.combine(B)
+        torch.cuda.synchronize()
+        assert_same(snapshot(c), want, "tied logits, call %d" % rep)
