@@ -77,8 +77,9 @@ def parse():
                          "(default decode48)")
     ap.add_argument("--eager", action="store_true", help="launch every call eagerly instead of HIP graphs")
     ap.add_argument("--ffn", default="routed", choices=("routed", "one-launch", "split"),
-                    help="decode windows: the routing inside the gate/up launch (moe_route_group_ffn, stages 1; then "
-                         "the down stage and moe_combine; where the window allows, else split), FFN and combine in "
+                    help="decode windows: the routing in one launch with the FFN's first step (moe_route_group_ffn: "
+                         "inside the gate/up launch; moe_route_group_ffn_mx: with MXFP8(x); stages 1, then the down "
+                         "stage and moe_combine; where the window allows, else split), FFN and combine in "
                          "one launch (moe_expert_ffn_combine) or one launch per FFN stage plus the combine's "
                          "(moe_expert_ffn_stages 1, 2; moe_combine)")
     ap.add_argument("--policy", default="lru", choices=("lru", "hotcold"),
@@ -259,9 +260,10 @@ class Workload:
 
     @property
     def routed(self):
-        """NVFP4 decode windows with drawn logits that moe_route_group_ffn runs in
-        one launch: route, group and gate/up together, then the down stage and
-        the combine."""
+        """Decode windows with drawn logits whose routing runs in one launch with
+        the FFN's first step: moe_route_group_ffn (NVFP4: route, group and
+        gate/up together) or moe_route_group_ffn_mx (MX: route, group and
+        MXFP8(x) together), then the rest of the FFN and the combine."""
         return self.wr is None and self.ffn_mode == "routed" and routed_shape(self.cfg)
 
     def ffn_combine(self, x, ev_start=None, ev_stop=None, stream=None):
@@ -288,10 +290,17 @@ class Workload:
             lg_out = buf.logits if self.wr is not None else None
             if self.routed:
                 ev = [hip_events.new() for _ in range(4)] if ffn_events is not None else [None] * 4
-                B.moe_route_group_ffn(d, l, x, wr, lg_in, self.wsg[l], lg_out, buf.ids, buf.w, buf.sigma,
-                                      self.slot_table, self.n_slots, buf.offsets, buf.perm, buf.inv_perm,
-                                      buf.group_slot, self.pool, self.pool_bytes, self.layout, buf.h, buf.y_rows,
-                                      buf.status, buf.ws, 1, ev[0], ev[1], stream=stream)
+                if self.mx:
+                    B.moe_route_group_ffn_mx(d, l, x, wr, lg_in, self.wsg[l], lg_out, buf.ids, buf.w, buf.sigma,
+                                             self.slot_table, self.n_slots, buf.offsets, buf.perm, buf.inv_perm,
+                                             buf.group_slot, self.pool, self.pool_bytes, self.layout, buf.h,
+                                             buf.y_rows, buf.status, buf.ws, buf.mx_ws, 1, ev[0], ev[1],
+                                             stream=stream)
+                else:
+                    B.moe_route_group_ffn(d, l, x, wr, lg_in, self.wsg[l], lg_out, buf.ids, buf.w, buf.sigma,
+                                          self.slot_table, self.n_slots, buf.offsets, buf.perm, buf.inv_perm,
+                                          buf.group_slot, self.pool, self.pool_bytes, self.layout, buf.h,
+                                          buf.y_rows, buf.status, buf.ws, 1, ev[0], ev[1], stream=stream)
                 self.ffn(x, 2, ev[2], ev[3], stream=stream)
                 if ffn_events is not None:
                     ffn_events.append((ev, buf.offsets.clone()))
@@ -878,10 +887,10 @@ def main():
 
 
 def routed_shape(cfg):
-    """The shapes whose routing moe_route_group_ffn runs inside the gate/up
-    launch: NVFP4 weight streaming (T k < 16 E), T <= 16, T k <= 256, E <= 1024."""
-    return (cfg.fmt != "mx" and cfg.T * cfg.k < 16 * cfg.E and cfg.T <= 16 and cfg.T * cfg.k <= 256
-            and cfg.E <= 1024)
+    """The shapes whose routing moe_route_group_ffn(_mx) runs in one launch with
+    the FFN's first step: weight streaming (T k < 16 E), T <= 16, T k <= 256,
+    E <= 1024."""
+    return cfg.T * cfg.k < 16 * cfg.E and cfg.T <= 16 and cfg.T * cfg.k <= 256 and cfg.E <= 1024
 
 
 def ffn_label(cfg, ffn):
@@ -1007,7 +1016,10 @@ def measure_workload(cfg, args, B, DevGen, K, W, ffn="split", per_step=False):
                     gu_b.mean(), dn_b.mean())}
     elif decode:
         achieved = float(gu_b.mean() / (gu_ms.mean() * 1e-3) / 1e9)
-        if wl.routed:
+        if wl.routed and cfg.fmt == "mx":
+            kname = "%s gate/up (moe_route_group_ffn_mx, stages=1: x quantised in the route + group launch)" % (
+                ffn_kernel(cfg)[0])
+        elif wl.routed:
             kname = "%s gate/up with the routing in its launch (moe_route_group_ffn, stages=1)" % ffn_kernel(cfg)[0]
         else:
             kname = "%s gate/up (%s, stages=1)" % (

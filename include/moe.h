@@ -492,6 +492,28 @@ int moe_expert_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool,
                       uint64_t mx_ws_bytes, int32_t stages, void* ev_start, void* ev_stop,
                       moe_stream_t stream);
 
+/* ---- S1 + S2 + S3 + S4 together, MX experts --------------------------------
+ * moe_route_group followed by moe_expert_ffn_mx on the same stream, with
+ * exactly their arguments, validation and results (every output of both
+ * bit-identical); stages is 1 (gate/up) or 3 (gate/up and down).  For decode
+ * windows (T <= 16, T*k <= 256, T*k < 16 E) the one route + group kernel also
+ * writes the MX FFN's A rows into mx_ws (the bf16 values of MXFP8(x);
+ * [FreeToken] 2.1, the format read as OCP MX), so the FFN begins with its
+ * gate/up kernel: one launch fewer per layer ([FreeToken] 3.5: a step's
+ * control flow stays on the device).  Otherwise the two calls' kernels are
+ * launched in turn.  ev_start, ev_stop bracket the FFN launches. */
+int moe_route_group_ffn_mx(const moe_dims* d, int32_t layer, const uint16_t* x,
+                           const float* w_router, const float* logits_in,
+                           const float* w_shared_gate, float* logits_out,
+                           int32_t* topk_ids, float* topk_w, float* shared_sigma,
+                           const int32_t* slot_table, int32_t n_slots, int32_t* offsets,
+                           int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
+                           const void* pool, uint64_t pool_bytes,
+                           const moe_blob_layout* layout, uint16_t* h, uint16_t* y_rows,
+                           int32_t* dev_status, void* ws, uint64_t ws_bytes, void* mx_ws,
+                           uint64_t mx_ws_bytes, int32_t stages, void* ev_start,
+                           void* ev_stop, moe_stream_t stream);
+
 /* moe_expert_ffn_mx for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, hosts that forbid
  * hipMalloc.  Same computation, arguments and results as moe_expert_ffn_mx

@@ -42,6 +42,7 @@ EXPORTED = ("moe_status_string", "moe_last_error", "moe_version", "moe_blob_layo
             "moe_expert_ffn_combine",
             "moe_blob_layout_init_mx",
             "moe_mx_workspace_bytes", "moe_quantize_mxfp8", "moe_expert_ffn_mx", "moe_expert_ffn_mx_noalloc",
+            "moe_route_group_ffn_mx",
             "moe_combine",
             "moe_ring_create", "moe_stage_h2d", "moe_ring_acquire", "moe_ring_release", "moe_ring_slot_ptr",
             "moe_ring_destroy", "moe_probe_hbm_read", "moe_probe_mfma", "moe_probe_scaled_mfma",
@@ -97,6 +98,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.moe_route_group_ffn.argtypes = [_DP, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
                                         _vp, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _u64,
                                         _i32, _vp, _vp, _vp]
+    lib.moe_route_group_ffn_mx.argtypes = [_DP, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
+                                           _vp, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _u64,
+                                           _vp, _u64, _i32, _vp, _vp, _vp]
     lib.moe_expert_ffn.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _u64, _vp]
     lib.moe_expert_ffn_stages.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _vp,
@@ -267,6 +271,25 @@ def moe_route_group_ffn(dims, layer, x, w_router, logits_in, w_shared_gate, logi
                                     _p(slot_table), n_slots, _p(offsets), _p(perm), _p(inv_perm), _p(group_slot),
                                     _p(pool), pool_bytes, ctypes.byref(layout), _p(h), _p(y_rows), _p(dev_status),
                                     _p(ws), ws_bytes, stages, ev_start, ev_stop, _s(stream)), "moe_route_group_ffn")
+
+
+def moe_route_group_ffn_mx(dims, layer, x, w_router, logits_in, w_shared_gate, logits_out, topk_ids, topk_w,
+                           shared_sigma, slot_table, n_slots, offsets, perm, inv_perm, group_slot, pool, pool_bytes,
+                           layout: BlobLayout, h, y_rows, dev_status, ws, mx_ws, stages: int = 3,
+                           ev_start: Optional[int] = None, ev_stop: Optional[int] = None,
+                           ws_bytes: Optional[int] = None, mx_ws_bytes: Optional[int] = None, stream=None) -> None:
+    """moe_route_group, then moe_expert_ffn_mx(stages 1 or 3); ev_start / ev_stop:
+    raw hipEvent_t handles (ints) or None."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    if mx_ws_bytes is None:
+        mx_ws_bytes = mx_ws.numel() * mx_ws.element_size()
+    _check(_lib.moe_route_group_ffn_mx(ctypes.byref(dims), layer, _p(x), _p(w_router), _p(logits_in),
+                                       _p(w_shared_gate), _p(logits_out), _p(topk_ids), _p(topk_w),
+                                       _p(shared_sigma), _p(slot_table), n_slots, _p(offsets), _p(perm),
+                                       _p(inv_perm), _p(group_slot), _p(pool), pool_bytes, ctypes.byref(layout),
+                                       _p(h), _p(y_rows), _p(dev_status), _p(ws), ws_bytes, _p(mx_ws), mx_ws_bytes,
+                                       stages, ev_start, ev_stop, _s(stream)), "moe_route_group_ffn_mx")
 
 
 def moe_expert_ffn(dims, x, pool, pool_bytes, layout: BlobLayout, offsets, perm, group_slot, h, y_rows, dev_status,

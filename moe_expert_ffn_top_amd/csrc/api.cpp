@@ -546,11 +546,13 @@ namespace {
 // moe_expert_ffn_mx; with mx_ws NULL (moe_expert_ffn_mx_noalloc) the MX
 // workspace is the library's static scratch, and a size beyond it is refused
 // before any HIP call.
-int expert_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
-                  const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm,
-                  const int32_t* group_slot, uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws,
-                  uint64_t ws_bytes, void* mx_ws, uint64_t mx_ws_bytes, int32_t stages, void* ev_start,
-                  void* ev_stop, moe_stream_t stream, bool static_scratch) {
+// The MX FFN's argument checks (moe_expert_ffn_mx); fills the geometry, the
+// CU count and, with static_scratch, *mx_ws with the library's array.
+int validate_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
+                    const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm,
+                    const int32_t* group_slot, uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws,
+                    uint64_t ws_bytes, void** mx_ws, uint64_t mx_ws_bytes, int32_t stages, bool static_scratch,
+                    moe::FfnGeom* g_out, int* n_cu_out) {
   if (stages < 1 || stages > 3) return fail(MOE_ERR_ARG, "stages = %d: must be 1 (gate/up), 2 (down) or 3", stages);
   int r = check_dims(d);
   if (r) return r;
@@ -568,7 +570,7 @@ int expert_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool, uint64
   REQUIRE(y_rows, 16, "y_rows");
   REQUIRE(dev_status, 4, "dev_status");
   REQUIRE(ws, 16, "ws");
-  if (!static_scratch) REQUIRE(mx_ws, 256, "mx_ws");
+  if (!static_scratch) REQUIRE(*mx_ws, 256, "mx_ws");
   const uint64_t need = moe::ws_layout(*d).total;
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace %llu bytes < required %llu", (unsigned long long)ws_bytes,
@@ -585,7 +587,7 @@ int expert_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool, uint64
   if (pool_bytes < layout->slot_stride)
     return fail(MOE_ERR_ARG, "pool_bytes %llu is smaller than one slot (%llu)", (unsigned long long)pool_bytes,
                 (unsigned long long)layout->slot_stride);
-  moe::FfnGeom g;
+  moe::FfnGeom& g = *g_out;
   g.pool = static_cast<const uint8_t*>(pool);
   g.slot_stride = layout->slot_stride;
   g.n_slots = (int64_t)(pool_bytes / layout->slot_stride);
@@ -594,16 +596,30 @@ int expert_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool, uint64
     g.off_scales[m] = layout->off_scales[m];
   }
   g.off_globals = layout->off_globals;
-  const hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
-  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   int dev = 0, n_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) !=
                                               hipSuccess || n_cu <= 0)
     return fail(MOE_ERR_HIP, "cannot query the device's compute-unit count");
+  *n_cu_out = n_cu;
   if (static_scratch) {
-    const hipError_t e = moe::noalloc_scratch(&mx_ws);
+    const hipError_t e = moe::noalloc_scratch(mx_ws);
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "static scratch address: %s", hipGetErrorString(e));
   }
+  return ok();
+}
+
+int expert_ffn_mx(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
+                  const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm,
+                  const int32_t* group_slot, uint16_t* h, uint16_t* y_rows, int32_t* dev_status, void* ws,
+                  uint64_t ws_bytes, void* mx_ws, uint64_t mx_ws_bytes, int32_t stages, void* ev_start,
+                  void* ev_stop, moe_stream_t stream, bool static_scratch) {
+  moe::FfnGeom g;
+  int n_cu = 0;
+  const int r = validate_ffn_mx(d, x, pool, pool_bytes, layout, offsets, perm, group_slot, h, y_rows, dev_status, ws,
+                                ws_bytes, &mx_ws, mx_ws_bytes, stages, static_scratch, &g, &n_cu);
+  if (r) return r;
+  const hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (moe::use_gemm(*d))
     return hip_status(moe::launch_ffn_mx(*d, x, g, perm, h, y_rows, ws, mx_ws, n_cu, stages, e0, e1, st),
                       "MX expert FFN launch");
@@ -630,6 +646,48 @@ int moe_expert_ffn_mx_noalloc(const moe_dims* d, const uint16_t* x, const void* 
                               void* ws, uint64_t ws_bytes, int32_t stages, moe_stream_t stream) {
   return expert_ffn_mx(d, x, pool, pool_bytes, layout, offsets, perm, group_slot, h, y_rows, dev_status, ws,
                        ws_bytes, nullptr, 0, stages, nullptr, nullptr, stream, true);
+}
+
+int moe_route_group_ffn_mx(const moe_dims* d, int32_t layer, const uint16_t* x, const float* w_router,
+                           const float* logits_in, const float* w_shared_gate, float* logits_out, int32_t* topk_ids,
+                           float* topk_w, float* shared_sigma, const int32_t* slot_table, int32_t n_slots,
+                           int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* group_slot, const void* pool,
+                           uint64_t pool_bytes, const moe_blob_layout* layout, uint16_t* h, uint16_t* y_rows,
+                           int32_t* dev_status, void* ws, uint64_t ws_bytes, void* mx_ws, uint64_t mx_ws_bytes,
+                           int32_t stages, void* ev_start, void* ev_stop, moe_stream_t stream) {
+  if (stages != 1 && stages != 3) return fail(MOE_ERR_ARG, "stages = %d: must be 1 (gate/up) or 3 (both)", stages);
+  int r = validate_route(d, x, w_router, logits_in, w_shared_gate, logits_out, topk_ids, topk_w, shared_sigma);
+  if (r) return r;
+  if ((r = validate_group(d, layer, topk_ids, slot_table, n_slots, offsets, perm, inv_perm, group_slot, dev_status,
+                          ws, ws_bytes)))
+    return r;
+  moe::FfnGeom g;
+  int n_cu = 0;
+  if ((r = validate_ffn_mx(d, x, pool, pool_bytes, layout, offsets, perm, group_slot, h, y_rows, dev_status, ws,
+                           ws_bytes, &mx_ws, mx_ws_bytes, stages, false, &g, &n_cu)))
+    return r;
+  if (moe::use_gemm(*d) || !moe::route_group_fusable(*d)) {
+    // the two calls' kernels in turn
+    if ((r = moe_route_group(d, layer, x, w_router, logits_in, w_shared_gate, logits_out, topk_ids, topk_w,
+                             shared_sigma, slot_table, n_slots, offsets, perm, inv_perm, group_slot, dev_status, ws,
+                             ws_bytes, stream)))
+      return r;
+    return moe_expert_ffn_mx(d, x, pool, pool_bytes, layout, offsets, perm, group_slot, h, y_rows, dev_status, ws,
+                             ws_bytes, mx_ws, mx_ws_bytes, stages, ev_start, ev_stop, stream);
+  }
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const float* lg = nullptr;
+  if ((r = route_logits(d, x, w_router, logits_in, logits_out, st, &lg))) return r;
+  uint16_t* xb = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(mx_ws) + moe::mx_ws_layout(*d).off_xb);
+  if ((r = hip_status(moe::launch_route_group(*d, layer, lg, x, w_shared_gate, slot_table, n_slots, topk_ids, topk_w,
+                                              shared_sigma, offsets, perm, inv_perm, group_slot, dev_status, ws, st,
+                                              xb),
+                      "route + group + MXFP8(x) launch")))
+    return r;
+  return hip_status(moe::launch_ffn_dec_mx(*d, x, g, perm, h, y_rows, ws, mx_ws, n_cu, stages,
+                                           static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop), st,
+                                           true),
+                    "MX expert FFN launch");
 }
 
 int moe_combine(const moe_dims* d, const uint16_t* y_rows, const int32_t* inv_perm, const float* topk_w,

@@ -51,6 +51,7 @@
 #include <type_traits>
 
 #include "moe_common.hpp"
+#include "mx_quant.hpp"
 
 namespace moe {
 namespace {
@@ -109,24 +110,6 @@ __device__ inline void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Two fp32 values of a block with E8M0 byte sb as OCP E4M3FN bytes (lo in
-// byte 0, hi in byte 1): v / 2^(sb - 127) is exact (ldexp), clamped to
-// +-448 (the saturation), then v_cvt_scalef32_pk_fp8_f32 with scale 1 rounds
-// to the nearest E4M3 value, ties to even, subnormals included (it returns
-// NaN above the range instead of saturating, hence the clamp).
-__device__ inline uint32_t e4m3_pair(float lo, float hi, int sb) {
-  typedef short s16x2 __attribute__((ext_vector_type(2)));
-  const float a = __builtin_amdgcn_fmed3f(ldexpf(lo, 127 - sb), -448.f, 448.f);
-  const float b = __builtin_amdgcn_fmed3f(ldexpf(hi, 127 - sb), -448.f, 448.f);
-  const s16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, a, b, 1.0f, false);
-  return (uint32_t)(uint16_t)r[0];
-}
-
-// The E8M0 byte of a block with largest magnitude m (m >= 0, fp32): the shared
-// exponent floor(log2 m) - 8, clamped below at -127 (zero and tiny blocks), is
-// the biased fp32 exponent field minus 127 + 8.
-__device__ inline int e8m0_of_amax(float m) { return max((int)(__float_as_uint(m) >> 23) - 8, 0); }
-
 // max over the 16 lanes of a DPP row (lanes 16 q .. 16 q + 15)
 __device__ inline float row16_max(float m) {
   m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));   // quad [1,0,3,2]
@@ -173,35 +156,13 @@ __global__ __launch_bounds__(256) void k_quant_mx(const uint16_t* __restrict__ x
   if ((t & 3) == 0) sc[(t / tpr) * stride + (t % tpr) / 4] = (uint8_t)sb;
 }
 
-// The same quantisation, written back as the bf16 values it stands for:
-// e4m3(code) * 2^(sb - 127), exact in bf16 (both have at most 4 significant
-// bits; values below 2^-133 would round, far below any activation here).
+// The same quantisation, written back as the bf16 values it stands for
+// (mx_quant8_bf16).
 __global__ __launch_bounds__(256) void k_quant_mx_bf16(const uint16_t* __restrict__ x, int64_t n8,
                                                        uint16_t* __restrict__ y) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= n8) return;  // whole quads leave together (n8 % 4 == 0)
-  const uint4 w = reinterpret_cast<const uint4*>(x)[t];
-  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-  float f[8];
-  float m = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    f[2 * i] = __uint_as_float(ww[i] << 16);
-    f[2 * i + 1] = __uint_as_float(ww[i] & 0xFFFF0000u);
-    m = fmaxf(m, fmaxf(fabsf(f[2 * i]), fabsf(f[2 * i + 1])));
-  }
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
-  const int sb = e8m0_of_amax(m);
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const uint32_t c2 = e4m3_pair(f[2 * i], f[2 * i + 1], sb);
-    const float v0 = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)c2, 0), sb - 127);
-    const float v1 = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)c2, 1), sb - 127);
-    o[i] = (__float_as_uint(v0) >> 16) | (__float_as_uint(v1) & 0xFFFF0000u);  // exact: the low halves are zero
-  }
-  reinterpret_cast<uint4*>(y)[t] = make_uint4(o[0], o[1], o[2], o[3]);
+  reinterpret_cast<uint4*>(y)[t] = mx_quant8_bf16(reinterpret_cast<const uint4*>(x)[t]);
 }
 
 template <bool GATEUP>
@@ -564,7 +525,7 @@ hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int32_t K, uint8_t* 
 
 hipError_t launch_ffn_dec_mx(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
                              uint16_t* y_rows, void* ws, void* mx_ws, int n_cu, int stages, hipEvent_t ev_start,
-                             hipEvent_t ev_stop, hipStream_t s) {
+                             hipEvent_t ev_stop, hipStream_t s, bool x_ready) {
   const MxWsLayout ml = mx_ws_layout(d);
   uint16_t* xb = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(mx_ws) + ml.off_xb);
   uint16_t* hb = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(mx_ws) + ml.off_hb);
@@ -573,9 +534,10 @@ hipError_t launch_ffn_dec_mx(const moe_dims& d, const uint16_t* x, const FfnGeom
     const bool gu = stage == 0;
     const bool first = gu || !(stages & 1), last = !gu || !(stages & 2);
     // the quantisation first, then the FFN kernel, which the events bracket
+    // (x_ready: the route + group launch already wrote x's into the workspace)
     const int64_t rows = gu ? d.T : (int64_t)d.T * d.k + d.T;
     const int64_t n8 = rows * ((gu ? d.H : d.I) / 8);
-    if (n8 > 0)
+    if (n8 > 0 && !(gu && x_ready))
       hipLaunchKernelGGL(k_quant_mx_bf16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, gu ? x : h, n8,
                          gu ? xb : hb);
     hipError_t e = hipGetLastError();

@@ -19,6 +19,7 @@
 //           histogram) and earlier in its own part (counted over the ids
 //           staged in LDS), so a row depends only on the ids (deterministic).
 #include "moe_common.hpp"
+#include "mx_quant.hpp"
 #include "route_small.hpp"
 #include "topk_wave.hpp"
 
@@ -371,7 +372,9 @@ __global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict_
 // Route and group fused for small windows (T <= 16 tokens, T*k <= 256
 // entries, drawn logits), one 1024-thread block: the sort path of
 // route_small.hpp (threshold top-k per token wavefront, then the grouped order
-// by rank counting).
+// by rank counting).  With xq, the same launch also writes the MX FFN's A
+// rows, bf16(MXFP8(x)) (mx_quant8_bf16, eight values per thread; the first
+// pass's loads are issued before the top-k, so they land meanwhile).
 template <int NPL>
 __global__ __launch_bounds__(1024) void k_route_group_sort(
     const float* __restrict__ logits, const uint16_t* __restrict__ x, const float* __restrict__ w_sg, int T, int H,
@@ -379,9 +382,12 @@ __global__ __launch_bounds__(1024) void k_route_group_sort(
     float* __restrict__ wout, float* __restrict__ sigma, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv_perm, int32_t* __restrict__ group_slot, int32_t* __restrict__ status,
     int32_t* __restrict__ meta, int4* __restrict__ tiles, int32_t* __restrict__ tile_tok, int4* __restrict__ chunks,
-    int32_t* __restrict__ sync, int64_t n_sync) {
+    int32_t* __restrict__ sync, int64_t n_sync, uint16_t* __restrict__ xq) {
   __shared__ SmallRouteLds<16> L;
   STAGE_STAMP(1, 0);
+  const int64_t n8 = (int64_t)T * H / 8;  // x's 8-value groups (H % 32 == 0: whole quads)
+  uint4 xv0 = make_uint4(0u, 0u, 0u, 0u);
+  if (xq && threadIdx.x < n8) xv0 = reinterpret_cast<const uint4*>(x)[threadIdx.x];
   small_route_topk<NPL, 16, true>(L, logits, x, w_sg, T, H, E, k, slot_table + (int64_t)layer * (E + 1));
   __syncthreads();
   STAGE_STAMP(1, 1);
@@ -390,6 +396,10 @@ __global__ __launch_bounds__(1024) void k_route_group_sort(
   STAGE_STAMP(1, 2);
   small_route_store<16>(L, T, k, E, n_slots, ids, wout, sigma, offsets, perm, inv_perm, group_slot, status, meta,
                         tiles, tile_tok, chunks, sync, n_sync);
+  if (xq) {
+    for (int64_t g = threadIdx.x; g < n8; g += 1024)
+      reinterpret_cast<uint4*>(xq)[g] = mx_quant8_bf16(g < 1024 ? xv0 : reinterpret_cast<const uint4*>(x)[g]);
+  }
   STAGE_STAMP(1, 3);
 }
 
@@ -475,7 +485,7 @@ bool route_group_fusable(const moe_dims& d) { return d.T <= 16 && (int64_t)d.T *
 hipError_t launch_route_group(const moe_dims& d, int32_t layer, const float* logits, const uint16_t* x,
                               const float* w_sg, const int32_t* slot_table, int32_t n_slots, int32_t* ids, float* w,
                               float* sigma, int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
-                              int32_t* dev_status, void* ws, hipStream_t s) {
+                              int32_t* dev_status, void* ws, hipStream_t s, uint16_t* xq) {
   const WsLayout wl = ws_layout(d);
   uint8_t* base = static_cast<uint8_t*>(ws);
   int32_t* meta = reinterpret_cast<int32_t*>(base + wl.off_meta);
@@ -489,7 +499,7 @@ hipError_t launch_route_group(const moe_dims& d, int32_t layer, const float* log
 #define MOE_RG_SORT(N)                                                                                             \
   hipLaunchKernelGGL((k_route_group_sort<N>), g, b, 0, s, logits, x, w_sg, d.T, d.H, d.E, d.k, layer, st, n_slots, \
                      ids, w, sigma, offsets, perm, inv_perm, group_slot, dev_status, meta, tiles, tile_tok, chunks,   \
-                     sync, wl.n_sync)
+                     sync, wl.n_sync, xq)
 #define MOE_RG_NPL(L)                 \
   if (npl <= 1) L(1);                 \
   else if (npl <= 2) L(2);            \

@@ -299,7 +299,7 @@ bool route_group_fusable(const moe_dims& d);
 hipError_t launch_route_group(const moe_dims& d, int32_t layer, const float* logits, const uint16_t* x,
                               const float* w_sg, const int32_t* slot_table, int32_t n_slots, int32_t* ids, float* w,
                               float* sigma, int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
-                              int32_t* dev_status, void* ws, hipStream_t s);
+                              int32_t* dev_status, void* ws, hipStream_t s, uint16_t* xq = nullptr);
 // stages: bit 1 = gate/up (writes h), bit 2 = down (reads h, writes y_rows)
 // ev_start / ev_stop (may be null): recorded at the start of the first launched
 // kernel and the end of the last one
@@ -338,7 +338,7 @@ hipError_t launch_ffn_mx(const moe_dims& d, const uint16_t* x, const FfnGeom& g,
 // its A rows the bf16 values of MXFP8(x) and MXFP8(h) (kept in mx_ws).
 hipError_t launch_ffn_dec_mx(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,
                              uint16_t* y_rows, void* ws, void* mx_ws, int n_cu, int stages, hipEvent_t ev_start,
-                             hipEvent_t ev_stop, hipStream_t s);
+                             hipEvent_t ev_stop, hipStream_t s, bool x_ready = false);
 hipError_t launch_combine(const moe_dims& d, const uint16_t* y_rows, const int32_t* inv_perm, const float* w,
                           const float* sigma, uint16_t* y, hipStream_t s);
 // Decode-path FFN with both stages (and optionally the combine) in one launch

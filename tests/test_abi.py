@@ -160,6 +160,35 @@ def test_route_group_ffn_validation(B):
     assert st(18, None) == B.MOE_ERR_ARG                        # h
 
 
+def test_route_group_ffn_mx_validation(B):
+    """moe_route_group_ffn_mx validates like moe_route_group and
+    moe_expert_ffn_mx (the MX layout and workspace included), and takes
+    stages 1 or 3 only."""
+    dims = _d(B)
+    d = ctypes.byref(dims)
+    fake = 1 << 20
+    lay = B.moe_blob_layout_init_mx(512, 256)
+    need = B.moe_workspace_bytes(dims)
+    need_mx = B.moe_mx_workspace_bytes(dims)
+    ok = [0, fake, None, fake, fake, None, fake, fake, fake, fake, 4, fake, fake, fake, fake, fake, 1 << 30,
+          ctypes.byref(lay), fake, fake, fake, fake, need, fake, need_mx, 3, None, None, None]
+
+    def st(i, v):
+        a = list(ok)
+        a[i] = v
+        return B.raw_status("moe_route_group_ffn_mx", d, *a)
+    for stages in (0, 2, 4, -1):
+        assert st(25, stages) == B.MOE_ERR_ARG
+    assert st(3, None) == B.MOE_ERR_ARG                         # neither router matrix nor logits
+    assert st(0, 1) == B.MOE_ERR_ARG                            # layer >= L
+    assert st(22, need - 256) == B.MOE_ERR_WORKSPACE
+    assert st(24, need_mx - 256) == B.MOE_ERR_WORKSPACE         # MX workspace
+    assert st(17, ctypes.byref(B.moe_blob_layout_init(512, 256))) == B.MOE_ERR_ARG   # an NVFP4 layout
+    assert st(23, fake + 16) == B.MOE_ERR_ALIGN                 # mx_ws
+    assert st(23, None) == B.MOE_ERR_ARG
+    assert st(18, None) == B.MOE_ERR_ARG                        # h
+
+
 @pytest.mark.parametrize("H,I", [(128, 128), (256, 128), (2048, 512), (4096, 2048), (384, 640), (16384, 128)])
 def test_mx_blob_layout_matches_oracle(B, H, I):
     lay = B.moe_blob_layout_init_mx(H, I)

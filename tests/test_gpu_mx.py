@@ -27,7 +27,11 @@
   its A rows the bf16 values of MXFP8(x) and MXFP8(h), both bit for bit
   against the oracle's quantisation; a K split into several rounds (H = 4608).
 - Full size: decode48_mx on all four tokens of its last layer, prefill8192_mx
-  on 17 sampled tokens."""
+  on 17 sampled tokens.
+- moe_route_group_ffn_mx (route, group and MXFP8(x) in one launch for decode
+  windows) against moe_route_group then moe_expert_ffn_mx, every output bit
+  for bit, on the decode48 window, T k = 96 and 65, the router matrix, and a
+  prefill shape (separate kernels)."""
 import numpy as np
 import pytest
 import torch
@@ -472,3 +476,68 @@ def test_prefill8192_mx_full_size(B, hostgen):
         assert torch.equal(buf.y.view(torch.int16), want), "graph replay differs from eager"
     del wl
     torch.cuda.empty_cache()
+
+
+RGF_MX = {
+    "decode48_window": Config(101, "rm1", T=4, H=2048, I=512, E=512, k=10, L=1, router="zipf", zipf_s=1.0, fmt="mx"),
+    "t16_k6": Config(102, "rm2", T=16, H=512, I=256, E=256, k=6, L=1, router="zipf", zipf_s=1.2, fmt="mx"),
+    "t13_k5": Config(103, "rm3", T=13, H=256, I=128, E=40, k=5, L=1, router="zipf", zipf_s=0.7, fmt="mx"),
+    "router_matrix": Config(104, "rm4", T=8, H=512, I=256, E=32, k=4, L=1, router="matrix", fmt="mx"),
+    "prefill_gemm": Config(105, "rm5", T=256, H=256, I=128, E=8, k=2, L=1, router="zipf", zipf_s=1.0, fmt="mx"),
+}
+
+
+@pytest.mark.parametrize("name", list(RGF_MX))
+def test_route_group_ffn_mx_matches_separate_calls(B, hostgen, name):
+    """moe_route_group_ffn_mx (route + group + MXFP8(x) in one launch for
+    decode windows, separate kernels otherwise) gives every output of
+    moe_route_group then moe_expert_ffn_mx bit for bit: ids, weights, sigma,
+    offsets, perm, inv_perm, group_slot, status, the live rows of h and Y, and
+    y after the combine; twice in a row, and with stages 1 then the down stage
+    alone."""
+    cfg = RGF_MX[name]
+    say("[gpu] route + group + MX FFN %s (T=%d H=%d I=%d E=%d k=%d)" % (name, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k))
+    c = MxCase(B, cfg, hostgen)
+    b = c.buf
+    lg_in = None if c.wr_t is not None else c.logits_t
+    lg_out = b.logits if c.wr_t is not None else None
+
+    def call(mode):
+        for t in (b.ids, b.offsets, b.perm, b.inv_perm, b.group_slot):
+            t.fill_(-5)
+        for t in (b.w, b.sigma):
+            t.fill_(7.0)
+        for t in (b.h, b.y_rows, b.y):
+            t.fill_(3.0)
+        b.status.zero_()
+        b.mx_ws.fill_(0x5A)
+        if mode == "separate":
+            B.moe_route_group(c.dims, 0, c.x, c.wr_t, lg_in, c.wsg_t, lg_out, b.ids, b.w, b.sigma, c.slot_table,
+                              cfg.E1, b.offsets, b.perm, b.inv_perm, b.group_slot, b.status, b.ws)
+            B.moe_expert_ffn_mx(c.dims, c.x, c.pool, c.pool_bytes, c.layout, b.offsets, b.perm, b.group_slot, b.h,
+                                b.y_rows, b.status, b.ws, b.mx_ws)
+        else:
+            B.moe_route_group_ffn_mx(c.dims, 0, c.x, c.wr_t, lg_in, c.wsg_t, lg_out, b.ids, b.w, b.sigma,
+                                     c.slot_table, cfg.E1, b.offsets, b.perm, b.inv_perm, b.group_slot, c.pool,
+                                     c.pool_bytes, c.layout, b.h, b.y_rows, b.status, b.ws, b.mx_ws,
+                                     1 if mode == "fused_split" else 3)
+            if mode == "fused_split":
+                B.moe_expert_ffn_mx(c.dims, c.x, c.pool, c.pool_bytes, c.layout, b.offsets, b.perm, b.group_slot,
+                                    b.h, b.y_rows, b.status, b.ws, b.mx_ws, 2)
+        B.moe_combine(c.dims, b.y_rows, b.inv_perm, b.w, b.sigma, b.y)
+        torch.cuda.synchronize()
+        off = b.offsets.clone()
+        live = torch.cat([torch.arange(int(off[cfg.E].item())),
+                          torch.arange(cfg.T * cfg.k, cfg.T * cfg.k + cfg.T)]).cuda()
+        return dict(ids=b.ids.clone(), w=b.w.view(torch.int32).clone(), sigma=b.sigma.view(torch.int32).clone(),
+                    offsets=off, perm=b.perm.clone(), inv_perm=b.inv_perm.clone(),
+                    group_slot=b.group_slot.clone(), status=b.status.clone(),
+                    h=b.h.view(torch.int16)[live].clone(), y_rows=b.y_rows.view(torch.int16)[live].clone(),
+                    y=b.y.view(torch.int16).clone())
+
+    want = call("separate")
+    assert int(want["status"].item()) == 0
+    for mode in ("fused", "fused", "fused_split"):
+        got = call(mode)
+        for key in want:
+            assert torch.equal(got[key], want[key]), "%s: %s differs" % (mode, key)

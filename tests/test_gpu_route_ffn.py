@@ -11,8 +11,9 @@ grouping the window for itself and one more storing the routing outputs.
   sorting wavefront's limit); the 43-layer decode window's routing (T = 16,
   k = 6, E = 256: two sorting wavefronts); T k = 65 (a second wavefront with
   one row); T k = 256 (four wavefronts, groups of up to 16 rows); T k = 200
-  with E = 1000; one token; E = 1000 (16 logits per lane, not a multiple of
-  64); H = 512, I = 256.
+  with E = 1000; T k = 256 with E = 1024 (the largest window and pool); one
+  expert (E = 1, k = 1: one group of every token); one token; E = 1000 (16
+  logits per lane, not a multiple of 64); H = 512, I = 256.
 - A routed expert and the shared expert not resident: the status bits and zero
   rows, as on the separate path.
 - stages = 1, then the down stage on its own.
@@ -51,6 +52,8 @@ CASES = {
     "f65": Config(88, "r8", T=13, H=512, I=256, E=40, k=5, L=1, router="zipf", zipf_s=0.7),
     "f256": Config(89, "r9", T=16, H=512, I=256, E=64, k=16, L=1, router="zipf", zipf_s=1.0),
     "f200_e1000": Config(90, "r10", T=10, H=512, I=256, E=1000, k=20, L=1, router="zipf", zipf_s=1.1),
+    "one_expert": Config(92, "r12", T=5, H=512, I=256, E=1, k=1, L=1, router="zipf", zipf_s=1.0),
+    "e1024_f256": Config(93, "r13", T=16, H=256, I=128, E=1024, k=16, L=1, router="zipf", zipf_s=0.9),
 }
 
 
