@@ -76,7 +76,7 @@ def parse():
                          "decode48_mx "
                          "(default decode48)")
     ap.add_argument("--eager", action="store_true", help="launch every call eagerly instead of HIP graphs")
-    ap.add_argument("--ffn", default="routed", choices=("routed", "one-launch", "split"),
+    ap.add_argument("--ffn", default="routed", choices=("layer", "routed", "one-launch", "split"),
                     help="decode windows: the routing in one launch with the FFN's first step (moe_route_group_ffn: "
                          "inside the gate/up launch; moe_route_group_ffn_mx: with MXFP8(x); stages 1, then the down "
                          "stage and moe_combine; where the window allows, else split), FFN and combine in "
@@ -97,6 +97,7 @@ def parse():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_gateup_%s_traffic.txt")
+LAYER_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer_dec_%s_traffic.txt")
 CSRC = os.path.join(ROOT, "moe_expert_ffn_top_amd", "csrc")
 
 
@@ -169,10 +170,11 @@ def kernel_source_hash(cfg):
     return source_hash(ffn_kernel(cfg)[1])
 
 
-def recorded_traffic(cfg):
-    """HBM bytes per gate/up launch from the counter summary in profiles/, if it
+def recorded_traffic(cfg, layer=False):
+    """HBM bytes per launch of the dominant kernel (the gate/up launch, or with
+    layer the one-launch layer) from the counter summary in profiles/, if it
     was taken on the current kernel source; else None."""
-    path = TRAFFIC_FILE % cfg.name
+    path = (LAYER_TRAFFIC_FILE if layer else TRAFFIC_FILE) % cfg.name
     if not os.path.exists(path):
         return None
     kv = {}
@@ -259,12 +261,20 @@ class Workload:
         return not self.mx and self.cfg.T * self.cfg.k < 16 * self.cfg.E and self.ffn_mode == "one-launch"
 
     @property
+    def layer_launch(self):
+        """NVFP4 decode windows with drawn logits, --ffn layer: route, group,
+        both FFN stages and the combine through moe_route_group_ffn_combine,
+        one launch per layer."""
+        return (not self.mx and self.wr is None and self.ffn_mode == "layer" and routed_shape(self.cfg)
+                and self.cfg.k <= 16)
+
+    @property
     def routed(self):
         """Decode windows with drawn logits whose routing runs in one launch with
         the FFN's first step: moe_route_group_ffn (NVFP4: route, group and
         gate/up together) or moe_route_group_ffn_mx (MX: route, group and
         MXFP8(x) together), then the rest of the FFN and the combine."""
-        return self.wr is None and self.ffn_mode == "routed" and routed_shape(self.cfg)
+        return self.wr is None and self.ffn_mode in ("routed", "layer") and routed_shape(self.cfg)
 
     def ffn_combine(self, x, ev_start=None, ev_stop=None, stream=None):
         from moe_expert_ffn_top_amd import binding as B
@@ -288,6 +298,15 @@ class Workload:
             wr = self.wr[l] if self.wr is not None else None
             lg_in = None if self.wr is not None else self.logits[s, l]
             lg_out = buf.logits if self.wr is not None else None
+            if self.layer_launch:
+                ev = [hip_events.new() for _ in range(2)] if ffn_events is not None else [None, None]
+                B.moe_route_group_ffn_combine(d, l, x, None, lg_in, self.wsg[l], None, buf.ids, buf.w, buf.sigma,
+                                              self.slot_table, self.n_slots, buf.offsets, buf.perm, buf.inv_perm,
+                                              buf.group_slot, self.pool, self.pool_bytes, self.layout, buf.h,
+                                              buf.y_rows, buf.y, buf.status, buf.ws, ev[0], ev[1], stream=stream)
+                if ffn_events is not None:
+                    ffn_events.append((ev, buf.offsets.clone()))
+                continue
             if self.routed:
                 ev = [hip_events.new() for _ in range(4)] if ffn_events is not None else [None] * 4
                 if self.mx:
@@ -316,7 +335,7 @@ class Workload:
                     ffn_events.append((ev, buf.offsets.clone()))
                 continue
             if ffn_events is None:
-                if self.ffn_mode in ("split", "routed") and not self.mx:
+                if self.ffn_mode in ("split", "routed", "layer") and not self.mx:
                     for st in (1, 2):
                         self.ffn(x, st, stream=stream)
                 else:
@@ -897,8 +916,10 @@ def ffn_label(cfg, ffn):
     """The FFN path a workload runs (Workload's choice, from the shapes)."""
     if cfg.T * cfg.k >= 16 * cfg.E:
         return "grouped GEMM"
-    if ffn == "routed" and not (cfg.router == "zipf" and routed_shape(cfg)):
+    if ffn in ("routed", "layer") and not (cfg.router == "zipf" and routed_shape(cfg)):
         return "split"
+    if ffn == "layer" and (cfg.fmt == "mx" or cfg.k > 16):
+        return "routed"
     return ffn
 
 
@@ -983,7 +1004,7 @@ def measure_workload(cfg, args, B, DevGen, K, W, ffn="split", per_step=False):
     for i in range(min(K, 8)):
         wl.run_step(W + i, ffn_events=events, hip_events=hev)
     torch.cuda.synchronize()
-    if wl.one_launch:
+    if wl.one_launch or wl.layer_launch:
         fu_ms = np.array([hev.elapsed_ms(ev[0], ev[1]) for ev, _ in events])
     else:
         gu_ms = np.array([hev.elapsed_ms(ev[0], ev[1]) for ev, _ in events])
@@ -1003,14 +1024,18 @@ def measure_workload(cfg, args, B, DevGen, K, W, ffn="split", per_step=False):
             g2, d2, _, _ = expert_work(cfg, [o for _, o in lay_ev])
             offs.append(float(g2.sum() + d2.sum()))
         res["expert_bytes_per_step"] = float(np.mean(offs))
-    if wl.one_launch:
-        # the dominant kernel: gate/up, down and combine in one launch; its
-        # algorithmic bytes are the expert weights it streams (both stages)
+    if wl.one_launch or wl.layer_launch:
+        # the dominant kernel: gate/up, down and combine (and, for the layer
+        # launch, the routing) in one launch; its algorithmic bytes are the
+        # expert weights it streams (both stages)
         fu_b = gu_b + dn_b
         achieved = float(fu_b.mean() / (fu_ms.mean() * 1e-3) / 1e9)
+        kname = ("k_layer_dec (moe_route_group_ffn_combine: route, group, gate/up, down and combine in one launch)"
+                 if wl.layer_launch else
+                 "k_ffn_dec_fused (moe_expert_ffn_combine: gate/up, down and combine in one launch)")
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(cfg),
-                "kernel": "k_ffn_dec_fused (moe_expert_ffn_combine: gate/up, down and combine in one launch)",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(cfg, layer=wl.layer_launch),
+                "kernel": kname,
                 "launch_us": float(fu_ms.mean() * 1e3), "bytes_per_launch": float(fu_b.mean()),
                 "bytes": "expert-weight bytes of the distinct experts touched: gate/up %.0f + down %.0f" % (
                     gu_b.mean(), dn_b.mean())}

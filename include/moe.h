@@ -424,6 +424,44 @@ int moe_route_group_ffn(const moe_dims* d, int32_t layer, const uint16_t* x,
                         uint64_t ws_bytes, int32_t stages, void* ev_start, void* ev_stop,
                         moe_stream_t stream);
 
+/* ---- S1 + S2 + S3 + S4 + S5 together ---------------------------------
+ * moe_route_group_ffn (stages 3) followed by moe_combine on the same stream,
+ * with exactly their arguments, validation and results (every output of the
+ * three calls bit-identical, y included).  For decode windows with drawn
+ * logits (logits_in, not w_router; T <= 16, T*k <= 256, k <= 16, E <= 1024,
+ * T*k < 16 E, and (H, I) of (2048, 512), (4096, 2048) or (512, 256)) the
+ * whole layer runs as one launch ([FreeToken] 3.5: a decode step's control
+ * flow stays on the device; [Strata] "路由以后，专家怎样分工？": the expert
+ * outputs of a token are weighted and summed once all have arrived):
+ *  - every workgroup routes and groups the window into its own work list;
+ *  - one workgroup zeroes the launch's counters in ws, stores the routing
+ *    outputs and then sets a ready flag in ws; the others stream the gate/up
+ *    weights and count each tile's h rows once the flag is set;
+ *  - the down projection of a tile waits, inside the launch, for its h rows
+ *    (its weights were requested before the gate/up walk), and the wavefront
+ *    that completes a block of output columns combines that block for every
+ *    token.
+ * The waits are bounded; should one time out (only if the device cannot keep
+ * the launch's workgroups resident together), MOE_DEV_SYNC_TIMEOUT is set and
+ * h, y_rows and y are undefined.  ws needs no preparation: the counters are
+ * zeroed inside the launch before any is counted, and the flag is cleared
+ * again by the launch's last workgroup.  Calls that share one ws must not
+ * overlap in time.  Otherwise (other shapes, or w_router) the calls' own
+ * launches run in turn.  ev_start, ev_stop bracket the layer's launch (with
+ * the routing and the combine in it), or the FFN launches otherwise.
+ * MOE_ERR_ARG if y is NULL; every other argument as for moe_route_group_ffn
+ * and moe_combine. */
+int moe_route_group_ffn_combine(const moe_dims* d, int32_t layer, const uint16_t* x,
+                                const float* w_router, const float* logits_in,
+                                const float* w_shared_gate, float* logits_out,
+                                int32_t* topk_ids, float* topk_w, float* shared_sigma,
+                                const int32_t* slot_table, int32_t n_slots, int32_t* offsets,
+                                int32_t* perm, int32_t* inv_perm, int32_t* group_slot,
+                                const void* pool, uint64_t pool_bytes,
+                                const moe_blob_layout* layout, uint16_t* h, uint16_t* y_rows,
+                                uint16_t* y, int32_t* dev_status, void* ws, uint64_t ws_bytes,
+                                void* ev_start, void* ev_stop, moe_stream_t stream);
+
 /* ---- S4, MX variant: MXFP4 experts on the scaled MFMA ---------------------
  * [FreeToken] notes that the DeepSeek-V4-Flash experts are natively MXFP4; the
  * pages do not define the format, which is read as OCP Microscaling (MX):

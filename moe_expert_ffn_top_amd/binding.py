@@ -38,7 +38,8 @@ MOE_DEV_SYNC_TIMEOUT = 32
 EXPORTED = ("moe_status_string", "moe_last_error", "moe_version", "moe_blob_layout_init", "moe_workspace_bytes",
             "moe_route", "moe_group", "moe_group_tail_skip", "moe_residency_update", "moe_residency_fill",
             "moe_heat_update", "moe_heat_decay", "moe_swap_plan", "moe_swap_apply",
-            "moe_route_group", "moe_route_group_ffn", "moe_expert_ffn", "moe_expert_ffn_stages",
+            "moe_route_group", "moe_route_group_ffn", "moe_route_group_ffn_combine", "moe_expert_ffn",
+            "moe_expert_ffn_stages",
             "moe_expert_ffn_combine",
             "moe_blob_layout_init_mx",
             "moe_mx_workspace_bytes", "moe_quantize_mxfp8", "moe_expert_ffn_mx", "moe_expert_ffn_mx_noalloc",
@@ -98,6 +99,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.moe_route_group_ffn.argtypes = [_DP, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
                                         _vp, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _u64,
                                         _i32, _vp, _vp, _vp]
+    lib.moe_route_group_ffn_combine.argtypes = [_DP, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
+                                                _vp, _vp, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp,
+                                                _vp, _vp, _u64, _vp, _vp, _vp]
     lib.moe_route_group_ffn_mx.argtypes = [_DP, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
                                            _vp, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _u64,
                                            _vp, _u64, _i32, _vp, _vp, _vp]
@@ -271,6 +275,23 @@ def moe_route_group_ffn(dims, layer, x, w_router, logits_in, w_shared_gate, logi
                                     _p(slot_table), n_slots, _p(offsets), _p(perm), _p(inv_perm), _p(group_slot),
                                     _p(pool), pool_bytes, ctypes.byref(layout), _p(h), _p(y_rows), _p(dev_status),
                                     _p(ws), ws_bytes, stages, ev_start, ev_stop, _s(stream)), "moe_route_group_ffn")
+
+
+def moe_route_group_ffn_combine(dims, layer, x, w_router, logits_in, w_shared_gate, logits_out, topk_ids, topk_w,
+                                shared_sigma, slot_table, n_slots, offsets, perm, inv_perm, group_slot, pool,
+                                pool_bytes, layout: BlobLayout, h, y_rows, y, dev_status, ws,
+                                ev_start: Optional[int] = None, ev_stop: Optional[int] = None,
+                                ws_bytes: Optional[int] = None, stream=None) -> None:
+    """moe_route_group_ffn (stages 3), then moe_combine; ev_start / ev_stop:
+    raw hipEvent_t handles (ints) or None."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.moe_route_group_ffn_combine(ctypes.byref(dims), layer, _p(x), _p(w_router), _p(logits_in),
+                                            _p(w_shared_gate), _p(logits_out), _p(topk_ids), _p(topk_w),
+                                            _p(shared_sigma), _p(slot_table), n_slots, _p(offsets), _p(perm),
+                                            _p(inv_perm), _p(group_slot), _p(pool), pool_bytes, ctypes.byref(layout),
+                                            _p(h), _p(y_rows), _p(y), _p(dev_status), _p(ws), ws_bytes, ev_start,
+                                            ev_stop, _s(stream)), "moe_route_group_ffn_combine")
 
 
 def moe_route_group_ffn_mx(dims, layer, x, w_router, logits_in, w_shared_gate, logits_out, topk_ids, topk_w,

@@ -497,6 +497,46 @@ int moe_route_group_ffn(const moe_dims* d, int32_t layer, const uint16_t* x, con
                     "route + group + expert FFN launch");
 }
 
+int moe_route_group_ffn_combine(const moe_dims* d, int32_t layer, const uint16_t* x, const float* w_router,
+                                const float* logits_in, const float* w_shared_gate, float* logits_out,
+                                int32_t* topk_ids, float* topk_w, float* shared_sigma, const int32_t* slot_table,
+                                int32_t n_slots, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                int32_t* group_slot, const void* pool, uint64_t pool_bytes,
+                                const moe_blob_layout* layout, uint16_t* h, uint16_t* y_rows, uint16_t* y,
+                                int32_t* dev_status, void* ws, uint64_t ws_bytes, void* ev_start, void* ev_stop,
+                                moe_stream_t stream) {
+  if (!y) return fail(MOE_ERR_ARG, "y is NULL");
+  int r = validate_route(d, x, w_router, logits_in, w_shared_gate, logits_out, topk_ids, topk_w, shared_sigma);
+  if (r) return r;
+  if ((r = validate_group(d, layer, topk_ids, slot_table, n_slots, offsets, perm, inv_perm, group_slot, dev_status,
+                          ws, ws_bytes)))
+    return r;
+  moe::FfnGeom g;
+  int n_cu = 0;
+  if ((r = validate_ffn(d, x, pool, pool_bytes, layout, offsets, perm, group_slot, h, y_rows, dev_status, ws,
+                        ws_bytes, 3, &g, &n_cu)))
+    return r;
+  REQUIRE(y, 16, "y");
+  if (w_router || !moe::route_ffn_combine_fusable(*d)) {
+    // the calls' own launches, in turn
+    if ((r = moe_route_group_ffn(d, layer, x, w_router, logits_in, w_shared_gate, logits_out, topk_ids, topk_w,
+                                 shared_sigma, slot_table, n_slots, offsets, perm, inv_perm, group_slot, pool,
+                                 pool_bytes, layout, h, y_rows, dev_status, ws, ws_bytes, 3, ev_start, ev_stop,
+                                 stream)))
+      return r;
+    return moe_combine(d, y_rows, inv_perm, topk_w, shared_sigma, y, stream);
+  }
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const float* lg = nullptr;
+  if ((r = route_logits(d, x, nullptr, logits_in, logits_out, st, &lg))) return r;
+  return hip_status(moe::launch_route_ffn_combine_dec(*d, layer, lg, x, w_shared_gate, slot_table, n_slots, topk_ids,
+                                                      topk_w, shared_sigma, offsets, perm, inv_perm, group_slot,
+                                                      dev_status, g, h, y_rows, y, ws, n_cu,
+                                                      static_cast<hipEvent_t>(ev_start),
+                                                      static_cast<hipEvent_t>(ev_stop), st),
+                    "route + group + expert FFN + combine launch");
+}
+
 int moe_blob_layout_init_mx(int32_t H, int32_t I, moe_blob_layout* out) {
   if (!out) return fail(MOE_ERR_ARG, "out is NULL");
   if (H < 128 || H > 16384 || H % 128 != 0) return fail(MOE_ERR_SHAPE, "H = %d: must be a multiple of 128 in [128, 16384]", H);

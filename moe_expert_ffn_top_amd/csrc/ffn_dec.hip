@@ -331,6 +331,9 @@ struct FusedCtx {
   int32_t gu_target;  // h-row publications that complete a tile
   int32_t dn_target;  // Y-row publications that complete a column block (x n_tiles)
   int32_t spin_limit;
+  // (k_layer_dec) the ready flag and the counters workgroup 0 zeroes first
+  uint64_t* flag;
+  int32_t n_zero;
   // combine (S5) arguments; inv_perm null: no combine in this launch
   const int32_t* inv_perm;
   const float* w;
@@ -816,6 +819,124 @@ __global__ __launch_bounds__(256) void k_ffn_dec_fused(DecArgs ag, DecArgs ad, c
   }
 }
 
+// ---- route, group, both FFN stages and the combine in one launch ----------
+// (moe_route_group_ffn_combine; [FreeToken] 3.5: a decode step's control flow
+// stays on the device.)  Every workgroup first routes and groups the window
+// into its own LDS (as the routing gate/up launch does), so the weight stream
+// starts without a descriptor chain through memory.  Workgroup 0 then zeroes
+// this launch's counters, stores every routing output (the combine's inputs
+// device-coherently) and, once those stores have completed, sets the ready
+// flag to kLayerReady; it walks down items only.  Workgroups 1 .. G - 1 issue
+// their first down unit's weights, walk the gate/up items (gu_walk over G - 1
+// walkers, h stored device-coherently), and wait for the flag before their
+// first counter access, so every count of the launch lands on zeroed
+// counters even in a workspace fresh from the allocator (the flag holds the
+// value only between workgroup 0's stores and the launch's end).  From there
+// on the down stage and the combine run as in k_ffn_dec_fused, the combine's
+// inputs (inv_perm, weights, sigma) read back from memory into LDS.
+constexpr uint64_t kLayerReady = 0x4d6f454c61796572ull;
+
+template <int GSK, int GS, int GU, bool GFS, int DSK, int DS, int DU, bool DFS, int RNPL>
+__global__ __launch_bounds__(256) void k_layer_dec(DecArgs ag, DecArgs ad, const uint8_t* __restrict__ pool,
+                                                   const uint16_t* __restrict__ x, uint16_t* __restrict__ h,
+                                                   uint16_t* __restrict__ y_rows, FusedCtx fc, RouteArgs r) {
+  constexpr int GNS = 2 * GU, DNS = DU;
+  constexpr int RW = (GSK > 1 || DSK > 1) ? 4 : 1, RNS = GNS > DNS ? GNS : DNS;
+  __shared__ f32x4 red[RW][RNS][64];
+  __shared__ RouteLds rl;
+  __shared__ int last_wg;
+  __shared__ uint32_t comb_mask[kMaxExperts / 32];
+  __shared__ int2 comb_pw[kSortF];
+  __shared__ float comb_sg[16];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, c = tid & 15;
+  const int G = gridDim.x, b = blockIdx.x;
+  const int F = r.T * r.k;
+  for (int i = tid; i < kMaxExperts / 32; i += blockDim.x) comb_mask[i] = 0;
+  small_route_topk<RNPL, 4, false>(rl.L, r.logits, x, r.w_sg, r.T, ag.H, r.E, r.k, r.slot_row);
+  __syncthreads();
+  const SortedRow row = small_route_sort_rows<4>(rl.L, F, r.E);
+  if (wave < sort_waves(F))
+    small_route_tiles<4>(rl.L, row, r.T, r.k, r.E, rl.tiles, rl.tok, rl.n, nullptr, nullptr, wave == 0, false);
+  __syncthreads();
+  const lds_int4_p tiles = (lds_int4_p)rl.tiles;
+  const lds_int_p tok = (lds_int_p)rl.tok;
+  const int n_tiles = rl.n[0];
+  const int n_gu = n_tiles * ag.n_ug, n_dn = n_tiles * ad.n_ug;
+  const Desc dd0 = load_desc<false>(ad, G - 1 - b, c, tiles, tok);
+  Start<false, DSK, DS, DU, DFS, false> sd;
+  GuWalk gw{0, 1, 0};
+  if (b == 0) {
+    stage_start<false, DSK, DS, DU, DFS, false, false>(sd, ad, dd0, n_dn, G, tiles, tok, pool, h);
+    for (int i = tid; i < fc.n_zero; i += blockDim.x)
+      __hip_atomic_store(counter(fc, i), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    small_route_gate<4>(rl.L, x, r.w_sg, r.T, ag.H);
+    small_route_store<4, true>(rl.L, r.T, r.k, r.E, r.n_slots, r.ids, r.w, r.sigma, r.offsets, r.perm, r.inv_perm,
+                               r.group_slot, r.status, r.meta, r.tiles, r.tile_tok, nullptr, nullptr, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(fc.flag, kLayerReady, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    gw = gu_walk(n_gu, G - 1, b - 1);
+    const Desc gd0 = load_desc<true>(ag, gw.first, c, tiles, tok);
+    Start<true, GSK, GS, GU, GFS, false> sg;
+    stage_start<true, GSK, GS, GU, GFS, false, true>(sg, ag, gd0, gw.limit, gw.stride, tiles, tok, pool, x);
+    stage_start<false, DSK, DS, DU, DFS, false, false>(sd, ad, dd0, n_dn, G, tiles, tok, pool, h);
+    stage_walk<true, GSK, GS, GU, GFS, false, Policy<kAuxPlain, kAuxDevice, false, false>>(
+        sg, ag, gw.stride, gw.limit, tiles, tok, pool, x, h, &fc, reinterpret_cast<f32x4(*)[GNS][64]>(red));
+  }
+  // the ready flag (bounded wait by wavefront 0; its first poll is issued
+  // after this wavefront's h stores, so one wait covers both)
+  if (wave == 0) {
+    int spins = 0;
+    for (;;) {
+      const uint64_t v = __hip_atomic_load(fc.flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+      if ((((uint64_t)hi << 32) | lo) == kLayerReady) break;
+      if (++spins > fc.spin_limit) {
+        if (lane == 0) atomicOr(fc.status, MOE_DEV_SYNC_TIMEOUT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(4);
+    }
+  }
+  __syncthreads();
+  // every wavefront that stored h rows: one count for each of its gate/up
+  // items' tiles, once its stores have completed
+  if (b > 0 && wave % GSK == 0 && gw.first < gw.limit) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (lane == 0)
+      for (int it = gw.first; it < gw.limit; it += gw.stride)
+        __hip_atomic_fetch_add(counter(fc, 1 + it / ag.n_ug), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // the combine's inputs, written by workgroup 0 before the flag
+  if (wave > 0) {
+    for (int i = tid - 64; i < F; i += 192)
+      comb_pw[i] = make_int2(__hip_atomic_load(r.inv_perm + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                             __float_as_int(__hip_atomic_load(r.w + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+    if (tid - 64 < r.T)
+      comb_sg[tid - 64] = __hip_atomic_load(r.sigma + (tid - 64), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  stage_walk<false, DSK, DS, DU, DFS, false, Policy<kAuxDevice, kAuxDevice, true, true>>(
+      sd, ad, G, n_dn, tiles, tok, pool, h, y_rows, &fc, reinterpret_cast<f32x4(*)[DNS][64]>(red), comb_mask);
+  __syncthreads();
+  combine_blocks(y_rows, fc, comb_mask, comb_pw, comb_sg);
+  // the last workgroup to finish zeroes the counters and clears the flag
+  __syncthreads();
+  if (tid == 0)
+    last_wg = __hip_atomic_fetch_add(counter(fc, 0), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == G - 1;
+  __syncthreads();
+  if (last_wg) {
+    const int nb = fc.H / fc.cols;
+    for (int i = tid; i < n_tiles; i += blockDim.x) *counter(fc, 1 + i) = 0;
+    for (int i = tid; i < nb; i += blockDim.x) *counter(fc, 1 + fc.max_tiles + i) = 0;
+    if (tid == 0) {
+      *counter(fc, 0) = 0;
+      *fc.flag = 0;
+    }
+  }
+}
+
 struct DecPtrs {
   const int4* tiles;
   const int32_t* tile_tok;
@@ -957,17 +1078,40 @@ FusedFn find_fused(const Split& g, const Split& dn, bool comb) {
 std::atomic<int> g_spin_limit{MOE_DEC_SPIN_LIMIT};
 std::atomic<int> g_extra_target{0};
 
+// The routed one-launch layer (k_layer_dec) for the same splits; RNPL as for
+// the routing gate/up launch (8 logits per lane up to E = 512, 16 above).
+using LayerFn = void (*)(DecArgs, DecArgs, const uint8_t*, const uint16_t*, uint16_t*, uint16_t*, FusedCtx,
+                         RouteArgs);
+
+template <int I>
+LayerFn layer_fn(int E) {
+  constexpr FusedKey f = kFused[I];
+  return E <= 512 ? k_layer_dec<f.gsk, f.gs, f.gu, (bool)f.gfs, f.dsk, f.ds, f.du, (bool)f.dfs, 8>
+                  : k_layer_dec<f.gsk, f.gs, f.gu, (bool)f.gfs, f.dsk, f.ds, f.du, (bool)f.dfs, 16>;
+}
+
+LayerFn find_layer(const Split& g, const Split& dn, int E) {
+  auto match = [&](const FusedKey& f) {
+    return f.gsk == g.sk && f.gs == g.S && f.gu == g.U && f.gfs == (int)g.fs && f.dsk == dn.sk && f.ds == dn.S &&
+           f.du == dn.U && f.dfs == (int)dn.fs;
+  };
+  if (match(kFused[0])) return layer_fn<0>(E);
+  if (match(kFused[1])) return layer_fn<1>(E);
+  if (match(kFused[2])) return layer_fn<2>(E);
+  return nullptr;
+}
+
 // workgroups of fn resident per CU (queried once per kernel)
-int fused_occupancy(FusedFn fn) {
+int fused_occupancy(const void* fn) {
   static std::mutex mu;
-  static FusedFn keys[8];
+  static const void* keys[8];
   static int vals[8];
   static int n = 0;
   std::lock_guard<std::mutex> lock(mu);
   for (int i = 0; i < n; i++)
     if (keys[i] == fn) return vals[i];
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), 256, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) !=
       hipSuccess)
     per_cu = 0;
   if (n < 8) {
@@ -1088,7 +1232,7 @@ hipError_t launch_ffn_dec_fused(const moe_dims& d, const uint16_t* x, const FfnG
   const FusedFn fn = find_fused(sg, sdn, comb);
   if (!fn) return hipErrorInvalidConfiguration;
   const DecArgs ag = dec_args(d, g, wl, sg), ad = dec_args(d, g, wl, sdn);
-  const int per_cu = fused_occupancy(fn);
+  const int per_cu = fused_occupancy(reinterpret_cast<const void*>(fn));
   if (per_cu <= 0) return hipErrorInvalidConfiguration;
   const int64_t cap = (int64_t)n_cu * (per_cu < MOE_DEC_WGS_FUSED ? per_cu : MOE_DEC_WGS_FUSED);
   const int64_t items = (int64_t)wl.max_tiles * (ag.n_ug > ad.n_ug ? ag.n_ug : ad.n_ug);
@@ -1101,6 +1245,8 @@ hipError_t launch_ffn_dec_fused(const moe_dims& d, const uint16_t* x, const FfnG
   fc.gu_target = ag.n_ug * (4 / sg.sk) + g_extra_target.load(std::memory_order_relaxed);
   fc.dn_target = 4 / sdn.sk;  // storing wavefronts of a down item
   fc.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  fc.flag = nullptr;
+  fc.n_zero = 0;
   fc.inv_perm = inv_perm;
   fc.w = w;
   fc.sigma = sigma;
@@ -1115,6 +1261,81 @@ hipError_t launch_ffn_dec_fused(const moe_dims& d, const uint16_t* x, const FfnG
   const uint8_t* pool = g.pool;
   void* args[] = {(void*)&ag, (void*)&ad, (void*)&tiles, (void*)&tile_tok, (void*)&n_tiles, (void*)&pool,
                   (void*)&x, (void*)&h, (void*)&y_rows, (void*)&fc};
+  if (ev_start || ev_stop)
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(256), args, 0, s, ev_start, ev_stop,
+                              0);
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(256), args, 0, s);
+}
+
+bool route_ffn_combine_fusable(const moe_dims& d) {
+  return route_ffn_fusable(d) && d.T <= 16 && d.k <= kFusedCombineMaxK &&
+         find_layer(stage_split(d, true, false), stage_split(d, false, false), d.E) != nullptr;
+}
+
+hipError_t launch_route_ffn_combine_dec(const moe_dims& d, int32_t layer, const float* logits, const uint16_t* x,
+                                        const float* w_sg, const int32_t* slot_table, int32_t n_slots, int32_t* ids,
+                                        float* w, float* sigma, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                        int32_t* group_slot, int32_t* dev_status, const FfnGeom& g, uint16_t* h,
+                                        uint16_t* y_rows, uint16_t* y, void* ws, int n_cu, hipEvent_t ev_start,
+                                        hipEvent_t ev_stop, hipStream_t s) {
+  const WsLayout wl = ws_layout(d);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  const Split sg = stage_split(d, true, false), sdn = stage_split(d, false, false);
+  const LayerFn fn = find_layer(sg, sdn, d.E);
+  if (!fn) return hipErrorInvalidConfiguration;
+  DecArgs ag = dec_args(d, g, wl, sg), ad = dec_args(d, g, wl, sdn);
+  // the work list is in LDS: at most kRouteMaxTiles entries
+  if (ag.max_tiles > kRouteMaxTiles) ag.max_tiles = kRouteMaxTiles;
+  ad.max_tiles = ag.max_tiles;
+  const int per_cu = fused_occupancy(reinterpret_cast<const void*>(fn));
+  if (per_cu <= 0) return hipErrorInvalidConfiguration;
+  // the whole grid is resident (the waits only ever wait on running
+  // workgroups): workgroup 0 plus the walkers
+  const int64_t cap = (int64_t)n_cu * (per_cu < MOE_DEC_WGS_FUSED ? per_cu : MOE_DEC_WGS_FUSED);
+  const int64_t items = (int64_t)ag.max_tiles * (ag.n_ug > ad.n_ug ? ag.n_ug : ad.n_ug) + 1;
+  const int grid = (int)(items < cap ? items : cap);
+  if (grid < 2) return hipErrorInvalidConfiguration;
+  int32_t* sync = reinterpret_cast<int32_t*>(base + wl.off_sync);
+  FusedCtx fc;
+  fc.sync = sync;
+  fc.status = dev_status;
+  fc.max_tiles = (int32_t)wl.max_tiles;
+  fc.gu_target = ag.n_ug * (4 / sg.sk) + g_extra_target.load(std::memory_order_relaxed);
+  fc.dn_target = 4 / sdn.sk;
+  fc.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  fc.flag = reinterpret_cast<uint64_t*>(sync + (wl.n_sync - 1) * kSyncStride);
+  fc.n_zero = (int32_t)(wl.n_sync - 1);
+  fc.inv_perm = inv_perm;
+  fc.w = w;
+  fc.sigma = sigma;
+  fc.y = y;
+  fc.T = d.T;
+  fc.k = d.k;
+  fc.H = d.H;
+  fc.cols = d.H / ad.n_ug;
+  RouteArgs r;
+  r.logits = logits;
+  r.w_sg = w_sg;
+  r.slot_row = slot_table + (int64_t)layer * (d.E + 1);
+  r.T = d.T;
+  r.k = d.k;
+  r.E = d.E;
+  r.n_slots = n_slots;
+  r.ids = ids;
+  r.w = w;
+  r.sigma = sigma;
+  r.offsets = offsets;
+  r.perm = perm;
+  r.inv_perm = inv_perm;
+  r.group_slot = group_slot;
+  r.status = dev_status;
+  r.meta = reinterpret_cast<int32_t*>(base + wl.off_meta);
+  r.tiles = reinterpret_cast<int4*>(base + wl.off_tiles);
+  r.tile_tok = reinterpret_cast<int32_t*>(base + wl.off_tile_tok);
+  r.sync = nullptr;
+  r.n_sync = 0;
+  const uint8_t* pool = g.pool;
+  void* args[] = {(void*)&ag, (void*)&ad, (void*)&pool, (void*)&x, (void*)&h, (void*)&y_rows, (void*)&fc, (void*)&r};
   if (ev_start || ev_stop)
     return hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(256), args, 0, s, ev_start, ev_stop,
                               0);

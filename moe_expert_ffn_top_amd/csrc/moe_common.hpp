@@ -50,7 +50,8 @@ struct WsLayout {
   int64_t ncb;         // blocks of kCntBlk flat entries
   int64_t max_tiles;   // upper bound on FFN tiles
   int64_t max_chunks;  // upper bound on GEMM chunks
-  int64_t n_sync;      // counters of the fused FFN: 1 + max_tiles + H / 16, kSyncStride words apart
+  int64_t n_sync;      // counters of the fused FFN: 1 + max_tiles + H / 16, then the routed layer launch's
+                       // ready flag (64 bits), kSyncStride words apart
   uint64_t off_cnt, off_meta, off_tiles, off_tile_tok, off_tile_base, off_chunks, off_mrk, off_sync, total;
 };
 
@@ -71,7 +72,7 @@ inline WsLayout ws_layout(const moe_dims& d) {
   w.max_chunks = (F + kChunkRows - 1) / kChunkRows + routed_groups + (d.T + kChunkRows - 1) / kChunkRows + 1;
   w.off_chunks = align256(w.off_tile_base + (uint64_t)d.E * 4);
   w.off_mrk = align256(w.off_chunks + (uint64_t)w.max_chunks * 16);
-  w.n_sync = 1 + w.max_tiles + d.H / 16;
+  w.n_sync = 1 + w.max_tiles + d.H / 16 + 1;
   w.off_sync = align256(w.off_mrk + (uint64_t)w.ncb * d.E * 4);
   w.total = align256(w.off_sync + (uint64_t)w.n_sync * kSyncStride * 4);
   return w;
@@ -113,6 +114,16 @@ __host__ __device__ inline int blob_sc_off(int j, int nc, int r) {
 }
 
 // ---- small device helpers --------------------------------------------------
+// A store that is device-coherent when DEV (an agent-scope relaxed store:
+// written through past the XCD's L2), a plain one otherwise.
+template <bool DEV, typename T>
+__device__ inline void store_maybe_dev(T* p, T v) {
+  if constexpr (DEV)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
 __device__ inline float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
@@ -319,6 +330,17 @@ hipError_t launch_route_ffn_dec(const moe_dims& d, int32_t layer, const float* l
                                 int32_t* group_slot, int32_t* dev_status, const FfnGeom& g, uint16_t* h,
                                 uint16_t* y_rows, void* ws, int n_cu, int stages, hipEvent_t ev_start,
                                 hipEvent_t ev_stop, hipStream_t s);
+// Route + group, both FFN stages and the combine of a small window in one
+// launch (route_ffn_combine_fusable: route_ffn_fusable, T <= 16, k <=
+// kFusedCombineMaxK, and a fused instantiation of the two stage splits);
+// every output of launch_route_group, the FFN and launch_combine.
+bool route_ffn_combine_fusable(const moe_dims& d);
+hipError_t launch_route_ffn_combine_dec(const moe_dims& d, int32_t layer, const float* logits, const uint16_t* x,
+                                        const float* w_sg, const int32_t* slot_table, int32_t n_slots, int32_t* ids,
+                                        float* w, float* sigma, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                        int32_t* group_slot, int32_t* dev_status, const FfnGeom& g, uint16_t* h,
+                                        uint16_t* y_rows, uint16_t* y, void* ws, int n_cu, hipEvent_t ev_start,
+                                        hipEvent_t ev_stop, hipStream_t s);
 // Grouped-GEMM expert FFN over the chunk list (prefill-sized groups); same
 // stage mask and events as launch_ffn_dec; n_cu sizes the persistent grid.
 hipError_t launch_ffn_gemm(const moe_dims& d, const uint16_t* x, const FfnGeom& g, const int32_t* perm, uint16_t* h,

@@ -373,8 +373,10 @@ __device__ __forceinline__ void small_route_tiles(const SmallRouteLds<NW>& L, co
 // and the status bits (threads e, e + 64 NW, ...); the rows' perm / inv_perm,
 // the groups' bounds and the work list (wavefront NW - 1); the tokens' ids,
 // weights and shared gates (wavefront t mod NW; needs z, small_route_topk with
-// gate); the fused launch's counters zeroed.
-template <int NW>
+// gate); the fused launch's counters zeroed.  DEV: the weights, sigma and
+// inv_perm (the combine's inputs) are stored device-coherently, for the other
+// workgroups of a launch that combines.
+template <int NW, bool DEV = false>
 __device__ __forceinline__ void small_route_store(const SmallRouteLds<NW>& L, int T, int k, int E, int32_t n_slots,
                                          int32_t* __restrict__ ids, float* __restrict__ wout,
                                          float* __restrict__ sigma, int32_t* __restrict__ offsets,
@@ -407,11 +409,11 @@ __device__ __forceinline__ void small_route_store(const SmallRouteLds<NW>& L, in
       const int4 ri = L.rowi[p];
       if (ri.x >= 0) {
         perm[p] = ri.y;
-        inv_perm[ri.y] = p;
+        store_maybe_dev<DEV>(inv_perm + ri.y, p);
       }
       if (p < F) {
         const int e0 = L.sid[p];
-        if (e0 < 0 || e0 >= E) inv_perm[p] = -1;   // (never for top-k winners)
+        if (e0 < 0 || e0 >= E) store_maybe_dev<DEV>(inv_perm + p, -1);   // (never for top-k winners)
       }
       small_route_tiles<NW>(L, sorted_row_from_lds(L, p), T, k, E, tiles, tile_tok, meta, chunks, meta + 1, p0 == 0);
     }
@@ -425,7 +427,7 @@ __device__ __forceinline__ void small_route_store(const SmallRouteLds<NW>& L, in
       if (nv < F) atomicOr(status, MOE_DEV_BAD_EXPERT_ID);
     }
   }
-  for (int t = wave; t < T; t += NW) topk_finish(L.wink + t * k, L.sid + t * k, t, k, L.z[t], ids, wout, sigma);
+  for (int t = wave; t < T; t += NW) topk_finish<DEV>(L.wink + t * k, L.sid + t * k, t, k, L.z[t], ids, wout, sigma);
   zero_sync(sync, n_sync);
 }
 

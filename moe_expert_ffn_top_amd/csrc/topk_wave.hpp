@@ -151,6 +151,9 @@ __device__ __forceinline__ void topk_rounds(uint32_t* key, int e0, int kk, uint3
 // Renormalised softmax over the k winners (win_k / win_i in slot order, in
 // LDS, written by this wavefront or before a barrier); lane l takes slots l,
 // l + 64, ...; z is the shared gate's dot product.
+// DEV: the weights and sigma are stored device-coherently (written through to
+// memory), for workgroups on other XCDs of the same launch to read.
+template <bool DEV = false>
 __device__ __forceinline__ void topk_finish(const uint32_t* win_k, const int* win_i, int t, int k, float z,
                                    int32_t* __restrict__ ids, float* __restrict__ wout, float* __restrict__ sigma) {
   const int lane = threadIdx.x & 63;
@@ -161,9 +164,9 @@ __device__ __forceinline__ void topk_finish(const uint32_t* win_k, const int* wi
   const float den = wave_sum_f32(part);
   for (int j = lane; j < k; j += 64) {
     ids[(int64_t)t * k + j] = win_i[j];
-    wout[(int64_t)t * k + j] = expf(key_f32(win_k[j]) - l0) / den;
+    store_maybe_dev<DEV>(wout + (int64_t)t * k + j, expf(key_f32(win_k[j]) - l0) / den);
   }
-  if (lane == 0) sigma[t] = 1.0f / (1.0f + expf(-z));
+  if (lane == 0) store_maybe_dev<DEV>(sigma + t, 1.0f / (1.0f + expf(-z)));
 }
 
 // Token t by the calling wavefront.  NPL = logits per lane (E <= 64 * NPL);
