@@ -666,13 +666,27 @@ struct NoRouteLds {
   int32_t unused;
 };
 
+// The arguments that a workgroup's first loads depend on lead the list (the
+// routing's logits and slot row, the work list and its bounds): the library
+// is built to preload leading kernel arguments into scalar registers at
+// dispatch, so those loads do not wait for a load of the argument block.
 template <bool GATEUP, int SPLITK, int S, int U, bool FS, bool MX, int RNPL>
-__global__ __launch_bounds__(256) void k_ffn_dec(DecArgs a, const int4* __restrict__ tiles,
-                                                 const int32_t* __restrict__ tile_tok,
-                                                 const int32_t* __restrict__ n_tiles,
+__global__ __launch_bounds__(256) void k_ffn_dec(const float* __restrict__ r_logits,
+                                                 const int32_t* __restrict__ r_slot_row, int32_t r_T, int32_t r_E,
+                                                 int32_t r_k, const int4* __restrict__ tiles,
+                                                 const int32_t* __restrict__ n_tiles, int32_t n_ug, int32_t max_tiles,
+                                                 DecArgs a, const int32_t* __restrict__ tile_tok,
                                                  const uint8_t* __restrict__ pool, const uint16_t* __restrict__ ain,
                                                  uint16_t* __restrict__ out, RouteArgs r) {
   constexpr bool ROUTE = RNPL > 0;   // RNPL: logits per lane of the routing (E <= 64 RNPL)
+  // the leading copies of these fields (the same values)
+  a.n_ug = n_ug;
+  a.max_tiles = max_tiles;
+  r.logits = r_logits;
+  r.slot_row = r_slot_row;
+  r.T = r_T;
+  r.E = r_E;
+  r.k = r_k;
   static_assert(!ROUTE || (GATEUP && !MX), "routing runs in the NVFP4 gate/up launch");
   constexpr int NS = (GATEUP ? 2 : 1) * U;
   __shared__ f32x4 red[SPLITK > 1 ? 4 : 1][NS][64];
@@ -957,12 +971,15 @@ struct DecLaunch {
 
 template <bool GATEUP, int SK, int S, int U, bool FS, bool MX, int RNPL>
 hipError_t launch_kr(const DecArgs& a, const DecPtrs& p, const DecLaunch& l) {
+  const RouteArgs& r = p.route;
   if (l.ev0 || l.ev1)
     hipExtLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U, FS, MX, RNPL>), dim3(l.grid), dim3(256), 0, l.st, l.ev0,
-                          l.ev1, 0, a, p.tiles, p.tile_tok, p.n_tiles, p.pool, p.ain, p.out, p.route);
+                          l.ev1, 0, r.logits, r.slot_row, r.T, r.E, r.k, p.tiles, p.n_tiles, a.n_ug, a.max_tiles, a,
+                          p.tile_tok, p.pool, p.ain, p.out, r);
   else
-    hipLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U, FS, MX, RNPL>), dim3(l.grid), dim3(256), 0, l.st, a, p.tiles,
-                       p.tile_tok, p.n_tiles, p.pool, p.ain, p.out, p.route);
+    hipLaunchKernelGGL((k_ffn_dec<GATEUP, SK, S, U, FS, MX, RNPL>), dim3(l.grid), dim3(256), 0, l.st, r.logits,
+                       r.slot_row, r.T, r.E, r.k, p.tiles, p.n_tiles, a.n_ug, a.max_tiles, a, p.tile_tok, p.pool,
+                       p.ain, p.out, r);
   return hipGetLastError();
 }
 
