@@ -15,17 +15,23 @@ STAGE_TIMES_DEFINE(moe_debug_stage_times_combine)
 #endif
 namespace {
 
-// grid (T, ceil(H / 2048)); 256 threads x 8 consecutive columns.  Two dependent
-// rounds of loads: the slot indices, weights, sigma and the shared row first,
-// then every routed row of the token at once (kCombineSlots per pass).
+// grid (T, ceil(H / (8 kCombineThreads))); kCombineThreads threads x 8
+// consecutive columns.  Two dependent rounds of loads: the slot indices,
+// weights, sigma and the shared row first, then every routed row of the token
+// at once (kCombineSlots per pass).  Workgroups of one wavefront spread a
+// token's row loads over several CUs.
 constexpr int kCombineSlots = 16;
+#ifndef MOE_COMBINE_THREADS
+#define MOE_COMBINE_THREADS 64
+#endif
+constexpr int kCombineThreads = MOE_COMBINE_THREADS;
 
-__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ yr, const int32_t* __restrict__ inv,
+__global__ __launch_bounds__(kCombineThreads) void k_combine(const uint16_t* __restrict__ yr, const int32_t* __restrict__ inv,
                                                  const float* __restrict__ w, const float* __restrict__ sigma,
                                                  int T, int H, int k, uint16_t* __restrict__ y) {
   STAGE_STAMP(2, 0);
   const int t = blockIdx.x;
-  const int col = (blockIdx.y * 256 + threadIdx.x) * 8;
+  const int col = (blockIdx.y * kCombineThreads + threadIdx.x) * 8;
   if (col >= H) return;
   const float st = sigma[t];
   const uint4 vs = *reinterpret_cast<const uint4*>(yr + ((int64_t)T * k + t) * H + col);
@@ -71,8 +77,8 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ yr
 
 hipError_t launch_combine(const moe_dims& d, const uint16_t* y_rows, const int32_t* inv_perm, const float* w,
                           const float* sigma, uint16_t* y, hipStream_t s) {
-  dim3 grid((unsigned)d.T, (unsigned)((d.H + 2047) / 2048));
-  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, y_rows, inv_perm, w, sigma, d.T, d.H, d.k, y);
+  dim3 grid((unsigned)d.T, (unsigned)((d.H + 8 * kCombineThreads - 1) / (8 * kCombineThreads)));
+  hipLaunchKernelGGL(k_combine, grid, dim3(kCombineThreads), 0, s, y_rows, inv_perm, w, sigma, d.T, d.H, d.k, y);
   return hipGetLastError();
 }
 
