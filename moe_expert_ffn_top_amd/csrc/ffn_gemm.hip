@@ -7,21 +7,25 @@
 //    grouping kernels list the chunks; blocks map to (chunk, tile) so that all
 //    tiles of one chunk run on the same XCD and share the chunk's A rows in
 //    that XCD's L2.
-//  - A 512-thread workgroup has two roles, one wavefront of each per SIMD:
-//    four producer wavefronts do all global loads and stage each 64-value K
-//    step into LDS (double buffered): the chunk's A rows (bf16 rows of x
-//    gathered through perm, or rows of h) and the B tile, 128 columns of
-//    weights (gate/up: 64 units of each matrix; down: 128 units) decoded from
-//    E2M1 codes times their E4M3 scale in fp32 (exact: <= 6 significant bits)
-//    and packed to bf16 (exact).  Their loads run three steps ahead in four
-//    register stages.  Four consumer wavefronts only read fragments and issue
-//    MFMAs.  Each barrier interval then costs the longer of the two roles, not
-//    their sum, and the producers' staging overlaps the MFMAs on each SIMD.
-//  - Each consumer owns four 16-row blocks (interleaved over the SIMDs) by all
-//    128 columns of the 256 x 128 output and accumulates exact bf16 products
-//    in fp32 with v_mfma_f32_16x16x32_bf16; row blocks past the chunk's rows
-//    are skipped.  The global scales and the activation are applied in the
-//    epilogue.
+//  - A workgroup has two roles, ROLES wavefronts of each per SIMD (gate/up
+//    two: 1024 threads; down one: 512).  The producer wavefronts do all
+//    global loads and stage each 64-value K step into LDS (double buffered):
+//    the chunk's A rows (bf16 rows of x gathered through perm, or rows of h)
+//    and the B tile, 128 columns of weights (gate/up: 64 units of each
+//    matrix; down: 128 units) decoded from E2M1 codes times their E4M3 scale
+//    in fp32 (exact: <= 6 significant bits) and packed to bf16 (exact).  Their
+//    loads run three steps ahead in four register stages.  The consumer
+//    wavefronts only read fragments and issue MFMAs.  Each barrier interval
+//    then costs the longer of the two roles, not their sum, and the
+//    producers' staging overlaps the MFMAs on each SIMD; with two producers
+//    per SIMD each stages half as much per step (one A row half, a quarter
+//    of a B column), and their load, decode and store latencies overlap.
+//  - Consumer (row group wm, column part ch) owns four 16-row blocks
+//    (interleaved over the SIMDs) by 128 / ROLES columns of the 256 x 128
+//    output (gate/up: the gate and up blocks of the same units) and
+//    accumulates exact bf16 products in fp32 with v_mfma_f32_16x16x32_bf16;
+//    row blocks past the chunk's rows are skipped.  The global scales and the
+//    activation are applied in the epilogue.
 #include <hip/hip_ext.h>
 #include <math.h>
 
@@ -37,7 +41,22 @@ constexpr int GM = kChunkRows;   // rows per workgroup
 constexpr int GC = 128;          // output columns per workgroup
 constexpr int GK = 64;           // K per step
 constexpr int LROW = GK + 16;    // bf16 per LDS row: 160-byte rows keep the 16-byte fragment reads of 16 rows conflict-free (144 does not)
-constexpr int GT = 512;          // threads per workgroup: 4 consumer + 4 producer wavefronts
+// Wavefronts of each role per SIMD, per stage (1 or 2).  Gate/up (K = H,
+// long items) runs two of each; down (K = I, eight steps an item) one.
+#ifndef MOE_GEMM_ROLES_GU
+#define MOE_GEMM_ROLES_GU 2
+#endif
+#ifndef MOE_GEMM_ROLES_DN
+#define MOE_GEMM_ROLES_DN 1
+#endif
+template <int ROLES>
+struct Shape {
+  static constexpr int NCW = 4 * ROLES, NPW = NCW;    // consumer and producer wavefronts
+  static constexpr int GT = 64 * (NCW + NPW);         // threads per workgroup
+  static constexpr int AR = 2 * GM / (64 * NPW);      // A rows per producer thread (each its half of the step's 64 values)
+  static constexpr int BQ = 64 * NPW / GC;            // producer threads per B column and step (2: 32 values each; 4: 16)
+  static constexpr int NCB = 8 * 4 / NCW;             // 16-column blocks per consumer wavefront
+};
 constexpr int NST = 4;           // producer register stages
 
 template <typename T>
@@ -60,6 +79,22 @@ struct GemmArgs {
 
 // An empty instruction that reads v: the value counts as used on this path.
 __device__ inline void touch(const uint4& v) { asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w)); }
+__device__ inline void touch(const uint2& v) { asm volatile("" ::"v"(v.x), "v"(v.y)); }
+
+// A producer thread's B values of one step into LDS: 32 codes (two scale
+// blocks) or 16 codes (one), times their scales, as bf16
+__device__ inline void stage_b(bf16x8* bd, const uint4& c, uint32_t sw) {
+  const float s0 = e4m3_to_f32<0>(sw), s1 = e4m3_to_f32<1>(sw);
+  bd[0] = dequant8(c.x, s0);
+  bd[1] = dequant8(c.y, s0);
+  bd[2] = dequant8(c.z, s1);
+  bd[3] = dequant8(c.w, s1);
+}
+__device__ inline void stage_b(bf16x8* bd, const uint2& c, uint32_t sw) {
+  const float s0 = e4m3_to_f32<0>(sw);
+  bd[0] = dequant8(c.x, s0);
+  bd[1] = dequant8(c.y, s0);
+}
 
 // Two floats as a bf16 pair (round to nearest even), lo in the low half.
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
@@ -71,19 +106,33 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
 // One producer thread's global loads for one K step: 32 A values of each of
 // two rows, and 32 weight codes with the aligned dword holding their two
 // scales.
+template <int BQ>
+struct Codes;
+template <>
+struct Codes<2> {
+  using type = uint4;  // 32 codes
+};
+template <>
+struct Codes<4> {
+  using type = uint2;  // 16 codes
+};
+template <int AR, int BQ>
 struct Stage {
-  uint4 a[2][4];
-  uint4 c;
-  uint32_t sc;   // the dword holding the two scales
-  uint32_t ssh;  // their bit offset in it (0 or 16)
+  uint4 a[AR][4];
+  typename Codes<BQ>::type c;
+  uint32_t sc;   // the dword holding the scale byte(s)
+  uint32_t ssh;  // their bit offset in it
 };
 
-template <bool GATEUP>
-__global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restrict__ chunks,
+template <bool GATEUP, int ROLES>
+__global__ __launch_bounds__(Shape<ROLES>::GT) void k_ffn_gemm(GemmArgs a, const int4* __restrict__ chunks,
                                                  const int32_t* __restrict__ meta, const int32_t* __restrict__ perm,
                                                  const uint8_t* __restrict__ pool, const uint16_t* __restrict__ ain,
                                                  uint16_t* __restrict__ out) {
   constexpr int NMAT = GATEUP ? 2 : 1;
+  using S_ = Shape<ROLES>;
+  constexpr int NCW = S_::NCW, GT = S_::GT, AR = S_::AR, BQ = S_::BQ, NCB = S_::NCB;
+  using Stage = moe::Stage<AR, BQ>;
   constexpr int UPW = GC / NMAT;  // units per workgroup
   const int K = GATEUP ? a.H : a.I;
   const int units = GATEUP ? a.I : a.H;
@@ -133,24 +182,25 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
     __syncthreads();
   };
 
-  if (wave >= 4) {
+  if (wave >= NCW) {
     // ---------------- producer ----------------
-    const int t = tid - 256;
+    const int t = tid - 64 * NCW;
     // A staging: rows ar and ar + 128, K half ah (32 values each).  Rows beyond
     // n load the last row (unbranched loads keep the wait counts exact) but are
     // not written to LDS unless their 16-row block is live (their outputs are
     // dropped)
     const int ah = t & 1;
-    int ar[2];
+    int ar[AR];
 #pragma unroll
-    for (int h = 0; h < 2; h++) ar[h] = (t >> 1) + 128 * h;
-    // B staging: column bc, K half bh
-    const int bc = t >> 1, bh = t & 1;
+    for (int h = 0; h < AR; h++) ar[h] = (t >> 1) + (GM / AR) * h;
+    // B staging: column bc, K part bh of the step (a half of 32 values, or a
+    // quarter of 16)
+    const int bc = t / BQ, bh = t % BQ;
     const int bmat = GATEUP ? bc / UPW : 2;
     const int nc = K / 32, nfull = nc >> 4;
     // the item's sources, set by setup()
-    bool alive[2];
-    const uint16_t* asrc[2];
+    bool alive[AR];
+    const uint16_t* asrc[AR];
     bool bvalid;
     uint32_t sfull, stail;
     const uint8_t* crow;
@@ -162,7 +212,7 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
       const uint8_t* blob = pool + (resident ? (uint64_t)slot * (uint64_t)a.slot_stride : 0);
       const int arow16 = (n + 15) & ~15;
 #pragma unroll
-      for (int h = 0; h < 2; h++) {
+      for (int h = 0; h < AR; h++) {
         alive[h] = ar[h] < arow16;
         const int p = p0 + min(ar[h], n - 1);
         const int64_t arow = GATEUP ? (int64_t)(p < a.Tk ? perm[p] / a.k : p - a.Tk) : (int64_t)p;
@@ -191,19 +241,22 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
       const int sc_ = min(s, a.nk - 1);
       const int ko = min(sc_ * GK + ah * 32, K - 32);
 #pragma unroll
-      for (int h = 0; h < 2; h++) {
+      for (int h = 0; h < AR; h++) {
         const uint4* ap = reinterpret_cast<const uint4*>(asrc[h] + ko);
 #pragma unroll
         for (int i = 0; i < 4; i++) st.a[h][i] = ap[i];
       }
-      const int j = min(2 * sc_ + bh, nc - 1);
-      st.c = *reinterpret_cast<const uint4*>(crow + (int64_t)j * 256);
-      // the two scale bytes of these 32 values, from the aligned dword holding
+      // chunk j (32 values) of the column; a quarter thread takes half of it
+      const int j = min(2 * sc_ + bh / (BQ / 2), nc - 1);
+      const int hq = BQ == 4 ? (bh & 1) : 0;
+      st.c = *reinterpret_cast<const typename Codes<BQ>::type*>(crow + (int64_t)j * 256 + 8 * hq);
+      // the scale byte(s) of these values, from the aligned dword holding
       // them; the shift waits for the stage, so no wait is forced here
       // (blob_sc_off(j, nc, br) without a multiply in the loop)
-      const uint32_t so = (uint32_t)(j >> 4) * 512u + ((j >> 4) < nfull ? sfull : stail) + 2u * (uint32_t)(j & 15);
+      const uint32_t so =
+          (uint32_t)(j >> 4) * 512u + ((j >> 4) < nfull ? sfull : stail) + 2u * (uint32_t)(j & 15) + (uint32_t)hq;
       st.sc = *reinterpret_cast<const uint32_t*>(sblk + (so & ~3u));
-      st.ssh = 8u * (so & 2u);
+      st.ssh = 8u * (so & (BQ == 4 ? 3u : 2u));
     };
     auto stage = [&](const Stage& st, int buf, int s) {
       // every loaded register is read here on every path (the stores below are
@@ -211,27 +264,22 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
       // unsure it has landed, and it then waits for all loads before reusing
       // the register
 #pragma unroll
-      for (int h = 0; h < 2; h++)
+      for (int h = 0; h < AR; h++)
 #pragma unroll
         for (int i = 0; i < 4; i++) touch(st.a[h][i]);
       touch(st.c);
       asm volatile("" ::"v"(st.sc));
       const bool kval = s * GK + ah * 32 < K;
 #pragma unroll
-      for (int h = 0; h < 2; h++) {
+      for (int h = 0; h < AR; h++) {
         uint4* ad = reinterpret_cast<uint4*>(&As[buf][ar[h] * LROW + ah * 32]);
         if (alive[h]) {
 #pragma unroll
           for (int i = 0; i < 4; i++) ad[i] = kval ? st.a[h][i] : make_uint4(0, 0, 0, 0);
         }
       }
-      const uint32_t sw = (bvalid && s * GK + bh * 32 < K) ? st.sc >> st.ssh : 0u;
-      const float s0 = e4m3_to_f32<0>(sw), s1 = e4m3_to_f32<1>(sw);
-      bf16x8* bd = reinterpret_cast<bf16x8*>(&Bs[buf][bc * LROW + bh * 32]);
-      bd[0] = dequant8(st.c.x, s0);
-      bd[1] = dequant8(st.c.y, s0);
-      bd[2] = dequant8(st.c.z, s1);
-      bd[3] = dequant8(st.c.w, s1);
+      const uint32_t sw = (bvalid && s * GK + (bh / (BQ / 2)) * 32 < K) ? st.sc >> st.ssh : 0u;
+      stage_b(reinterpret_cast<bf16x8*>(&Bs[buf][bc * LROW + bh * (64 / BQ)]), st.c, sw);
     };
 
     // half-step h loads step h + 3 into stage (h + 3) % 4 and stages step h + 1
@@ -286,8 +334,14 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
   int zero_v;
   asm volatile("v_mov_b32 %0, 0" : "=v"(zero_v));
   const float4 gsc = *reinterpret_cast<const float4*>(blob + a.off_globals + zero_v);
-  const int wm = wave;
+  // row group wm (16-row blocks wm, wm + 4, ...) and column part ch: NCB of
+  // the tile's eight 16-column blocks (gate/up: the gate blocks and the up
+  // blocks of the same units)
+  const int wm = wave & 3, ch = wave >> 2;
   const int r = lane & 15, q = lane >> 4;
+  auto col_block = [&](int lc) {
+    return GATEUP ? (lc < NCB / 2 ? ch * (NCB / 2) + lc : 4 + ch * (NCB / 2) + lc - NCB / 2) : ch * NCB + lc;
+  };
 
   // Row block rb of this wavefront is rows 64 rb + 16 wm .. + 15: the four
   // SIMDs take turns over 16-row blocks, so a chunk of n < 256 rows leaves them
@@ -298,25 +352,25 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
   // gate block cb with the up block cb + 4 (same units).
   auto consume = [&](auto nrb_c) __attribute__((always_inline)) {
     constexpr int NRB = decltype(nrb_c)::value;
-    f32x4 acc[NRB][8];
+    f32x4 acc[NRB][NCB];
 #pragma unroll
     for (int i = 0; i < NRB; i++)
 #pragma unroll
-      for (int j = 0; j < 8; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NCB; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int ks = 0; ks < 2; ks++) {
-        bf16x8 fa[NRB], fb[8];
+        bf16x8 fa[NRB], fb[NCB];
 #pragma unroll
         for (int rb = 0; rb < NRB; rb++)
           fa[rb] = *reinterpret_cast<const bf16x8*>(&As[buf][(64 * rb + 16 * wm + r) * LROW + 32 * ks + 8 * q]);
 #pragma unroll
-        for (int cb = 0; cb < 8; cb++)
-          fb[cb] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(16 * cb + r) * LROW + 32 * ks + 8 * q]);
+        for (int cb = 0; cb < NCB; cb++)
+          fb[cb] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(16 * col_block(cb) + r) * LROW + 32 * ks + 8 * q]);
 #pragma unroll
         for (int rb = 0; rb < NRB; rb++)
 #pragma unroll
-          for (int cb = 0; cb < 8; cb++) acc[rb][cb] = mfma16x16x32(fa[rb], fb[cb], acc[rb][cb]);
+          for (int cb = 0; cb < NCB; cb++) acc[rb][cb] = mfma16x16x32(fa[rb], fb[cb], acc[rb][cb]);
       }
     };
     // one barrier per step, as the producers have
@@ -343,7 +397,7 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
 #pragma unroll
     for (int rb = 0; rb < NRB; rb++) {
 #pragma unroll
-      for (int oc = 0; oc < OC / 16; oc++) {
+      for (int oc = 0; oc < OC / 16 / (NCW / 4); oc++) {
         float v[4];
 #pragma unroll
         for (int e4 = 0; e4 < 4; e4++) {
@@ -351,7 +405,7 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
             // silu(g) u = g u / (1 + e^-g): v_exp_f32 and v_rcp_f32 (errors of
             // a few fp32 ulp, far below the bf16 rounding of h)
             const float gv = g0 * acc[rb][oc][e4];
-            const float uv = g1 * acc[rb][oc + 4][e4];
+            const float uv = g1 * acc[rb][oc + NCB / 2][e4];
             v[e4] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
           } else {
             v[e4] = g0 * acc[rb][oc][e4];
@@ -367,7 +421,7 @@ __global__ __launch_bounds__(GT) void k_ffn_gemm(GemmArgs a, const int4* __restr
         const uint32_t w0 = __builtin_amdgcn_perm(recv, mine, sel0);
         const uint32_t w1 = __builtin_amdgcn_perm(recv, mine, sel1);
         const int row = 64 * rb + 16 * wm + 4 * q + (odd ? 1 : 0);
-        const int col = 16 * oc + (r & ~1);
+        const int col = 16 * (ch * (OC / 16 / (NCW / 4)) + oc) + (r & ~1);
         *reinterpret_cast<uint32_t*>(&os[row * OSTR + col]) = w0;
         *reinterpret_cast<uint32_t*>(&os[(row + 2) * OSTR + col]) = w1;
       }
@@ -422,18 +476,17 @@ hipError_t launch_ffn_gemm(const moe_dims& d, const uint16_t* x, const FfnGeom& 
     a.nk = (K + GK - 1) / GK;
     // persistent: one workgroup per CU (the LDS holds one), a multiple of 8
     const int64_t items = (wl.max_chunks + 7) / 8 * 8 * a.n_ut;
-    const dim3 grid((unsigned)std::min<int64_t>(items, (int64_t)(n_cu + 7) / 8 * 8)), block(GT);
+    const dim3 grid((unsigned)std::min<int64_t>(items, (int64_t)(n_cu + 7) / 8 * 8));
+    const dim3 block(gu ? Shape<MOE_GEMM_ROLES_GU>::GT : Shape<MOE_GEMM_ROLES_DN>::GT);
     const bool first = gu || !(stages & 1), last = !gu || !(stages & 2);
     hipEvent_t e0 = first ? ev_start : nullptr, e1 = last ? ev_stop : nullptr;
     const uint16_t* ain = gu ? x : h;
     uint16_t* out = gu ? h : y_rows;
-    if (e0 || e1) {
-      if (gu) hipExtLaunchKernelGGL(k_ffn_gemm<true>, grid, block, 0, s, e0, e1, 0, a, chunks, meta, perm, g.pool, ain, out);
-      else hipExtLaunchKernelGGL(k_ffn_gemm<false>, grid, block, 0, s, e0, e1, 0, a, chunks, meta, perm, g.pool, ain, out);
-    } else {
-      if (gu) hipLaunchKernelGGL(k_ffn_gemm<true>, grid, block, 0, s, a, chunks, meta, perm, g.pool, ain, out);
-      else hipLaunchKernelGGL(k_ffn_gemm<false>, grid, block, 0, s, a, chunks, meta, perm, g.pool, ain, out);
-    }
+    auto* kern = gu ? k_ffn_gemm<true, MOE_GEMM_ROLES_GU> : k_ffn_gemm<false, MOE_GEMM_ROLES_DN>;
+    if (e0 || e1)
+      hipExtLaunchKernelGGL(kern, grid, block, 0, s, e0, e1, 0, a, chunks, meta, perm, g.pool, ain, out);
+    else
+      hipLaunchKernelGGL(kern, grid, block, 0, s, a, chunks, meta, perm, g.pool, ain, out);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
