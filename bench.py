@@ -76,10 +76,11 @@ def parse():
                          "decode48_mx "
                          "(default decode48)")
     ap.add_argument("--eager", action="store_true", help="launch every call eagerly instead of HIP graphs")
-    ap.add_argument("--ffn", default="routed", choices=("layer", "routed", "one-launch", "split"),
+    ap.add_argument("--ffn", default="routed-dc", choices=("layer", "routed", "routed-dc", "one-launch", "split"),
                     help="decode windows: the routing in one launch with the FFN's first step (moe_route_group_ffn: "
                          "inside the gate/up launch; moe_route_group_ffn_mx: with MXFP8(x); stages 1, then the down "
-                         "stage and moe_combine; where the window allows, else split), FFN and combine in "
+                         "stage and moe_combine (routed) or both in one call, moe_expert_ffn_down_combine "
+                         "(routed-dc, the default; MX keeps routed); where the window allows, else split), FFN and combine in "
                          "one launch (moe_expert_ffn_combine) or one launch per FFN stage plus the combine's "
                          "(moe_expert_ffn_stages 1, 2; moe_combine)")
     ap.add_argument("--policy", default="lru", choices=("lru", "hotcold"),
@@ -274,7 +275,12 @@ class Workload:
         the FFN's first step: moe_route_group_ffn (NVFP4: route, group and
         gate/up together) or moe_route_group_ffn_mx (MX: route, group and
         MXFP8(x) together), then the rest of the FFN and the combine."""
-        return self.wr is None and self.ffn_mode in ("routed", "layer") and routed_shape(self.cfg)
+        return self.wr is None and self.ffn_mode in ("routed", "routed-dc", "layer") and routed_shape(self.cfg)
+
+    @property
+    def down_combine(self):
+        """routed-dc: the down stage and the combine through moe_expert_ffn_down_combine."""
+        return not self.mx and self.ffn_mode == "routed-dc"
 
     def ffn_combine(self, x, ev_start=None, ev_stop=None, stream=None):
         from moe_expert_ffn_top_amd import binding as B
@@ -320,6 +326,15 @@ class Workload:
                                           self.slot_table, self.n_slots, buf.offsets, buf.perm, buf.inv_perm,
                                           buf.group_slot, self.pool, self.pool_bytes, self.layout, buf.h,
                                           buf.y_rows, buf.status, buf.ws, 1, ev[0], ev[1], stream=stream)
+                if self.down_combine:
+                    # the down stage and the combine in one call (one launch on decode windows)
+                    B.moe_expert_ffn_down_combine(d, x, self.pool, self.pool_bytes, self.layout, buf.offsets,
+                                                  buf.perm, buf.group_slot, buf.inv_perm, buf.w, buf.sigma, buf.h,
+                                                  buf.y_rows, buf.y, buf.status, buf.ws, ev[2], ev[3],
+                                                  stream=stream)
+                    if ffn_events is not None:
+                        ffn_events.append((ev, buf.offsets.clone()))
+                    continue
                 self.ffn(x, 2, ev[2], ev[3], stream=stream)
                 if ffn_events is not None:
                     ffn_events.append((ev, buf.offsets.clone()))
@@ -335,7 +350,7 @@ class Workload:
                     ffn_events.append((ev, buf.offsets.clone()))
                 continue
             if ffn_events is None:
-                if self.ffn_mode in ("split", "routed", "layer") and not self.mx:
+                if self.ffn_mode in ("split", "routed", "routed-dc", "layer") and not self.mx:
                     for st in (1, 2):
                         self.ffn(x, st, stream=stream)
                 else:
@@ -916,9 +931,11 @@ def ffn_label(cfg, ffn):
     """The FFN path a workload runs (Workload's choice, from the shapes)."""
     if cfg.T * cfg.k >= 16 * cfg.E:
         return "grouped GEMM"
-    if ffn in ("routed", "layer") and not (cfg.router == "zipf" and routed_shape(cfg)):
+    if ffn in ("routed", "routed-dc", "layer") and not (cfg.router == "zipf" and routed_shape(cfg)):
         return "split"
     if ffn == "layer" and (cfg.fmt == "mx" or cfg.k > 16):
+        return "routed"
+    if ffn == "routed-dc" and cfg.fmt == "mx":
         return "routed"
     return ffn
 
@@ -1055,6 +1072,9 @@ def measure_workload(cfg, args, B, DevGen, K, W, ffn="split", per_step=False):
                 "launch_us": float(gu_ms.mean() * 1e3), "bytes_per_launch": float(gu_b.mean()),
                 "down": {"launch_us": float(dn_ms.mean() * 1e3), "bytes_per_launch": float(dn_b.mean()),
                          "achieved": float(dn_b.mean() / (dn_ms.mean() * 1e-3) / 1e9)}}
+        if wl.down_combine:
+            roof["down"]["kernel"] = ("k_down_comb (moe_expert_ffn_down_combine: the down stage and the combine in "
+                                      "one launch; launch_us includes the combine)")
     else:
         achieved = float(gu_f.mean() / (gu_ms.mean() * 1e-3) / 1e12)
         peak = FP8_PEAK_TFLOPS if cfg.fmt == "mx" else BF16_PEAK_TFLOPS

@@ -399,6 +399,31 @@ int moe_expert_ffn_combine(const moe_dims* d, const uint16_t* x, const void* poo
                            uint16_t* y_rows, uint16_t* y, int32_t* dev_status, void* ws,
                            uint64_t ws_bytes, void* ev_start, void* ev_stop, moe_stream_t stream);
 
+/* ---- S4 down + S5 together ---------------------------------------------
+ * moe_expert_ffn_stages (stages 2) followed by moe_combine on the same stream,
+ * with exactly their arguments, validation and results (y_rows and y
+ * bit-identical).  x: as for moe_expert_ffn_stages (validated, not read); h:
+ * the rows a gate/up stage wrote earlier on the same stream, read only.  For
+ * decode windows on the weight-streaming path with I = 512, T <= 16 and
+ * k <= 16 the two run as one launch ([Strata] "路由以后，专家怎样分工？": a
+ * token's expert outputs are weighted and summed once all of them have
+ * arrived): two workgroups share each block of 16 output columns, each
+ * computing the Y rows of half the tiles for it, and the second of the two to
+ * finish combines the block for every token in moe_combine's arithmetic.
+ * Nothing in the launch waits.  Its two counters per block live in ws
+ * (zeroed by the grouping that wrote ws's work list and again after each use).
+ * Y rows are stored device-coherently (written through) so the combining
+ * workgroup reads them across XCDs.  Other shapes run the two launches.
+ * ev_start, ev_stop as for moe_expert_ffn_stages. */
+int moe_expert_ffn_down_combine(const moe_dims* d, const uint16_t* x, const void* pool,
+                                uint64_t pool_bytes, const moe_blob_layout* layout,
+                                const int32_t* offsets, const int32_t* perm,
+                                const int32_t* group_slot, const int32_t* inv_perm,
+                                const float* topk_w, const float* shared_sigma, const uint16_t* h,
+                                uint16_t* y_rows, uint16_t* y, int32_t* dev_status, void* ws,
+                                uint64_t ws_bytes, void* ev_start, void* ev_stop,
+                                moe_stream_t stream);
+
 /* ---- S1 + S2 + S3 + S4 together ---------------------------------------
  * moe_route_group followed by moe_expert_ffn_stages on the same stream, with
  * exactly their arguments, validation and results (every output of both

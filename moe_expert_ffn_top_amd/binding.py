@@ -41,6 +41,7 @@ EXPORTED = ("moe_status_string", "moe_last_error", "moe_version", "moe_blob_layo
             "moe_route_group", "moe_route_group_ffn", "moe_route_group_ffn_combine", "moe_expert_ffn",
             "moe_expert_ffn_stages",
             "moe_expert_ffn_combine",
+            "moe_expert_ffn_down_combine",
             "moe_blob_layout_init_mx",
             "moe_mx_workspace_bytes", "moe_quantize_mxfp8", "moe_expert_ffn_mx", "moe_expert_ffn_mx_noalloc",
             "moe_route_group_ffn_mx",
@@ -110,6 +111,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.moe_expert_ffn_stages.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _vp,
                                           _vp, _vp, _u64, _i32, _vp, _vp, _vp]
     lib.moe_expert_ffn_combine.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _vp,
+                                           _vp, _vp, _vp, _vp, _vp, _vp, _u64, _vp, _vp, _vp]
+    lib.moe_expert_ffn_down_combine.argtypes = [_DP, _vp, _vp, _u64, ctypes.POINTER(BlobLayout), _vp, _vp, _vp, _vp, _vp,
                                            _vp, _vp, _vp, _vp, _vp, _vp, _u64, _vp, _vp, _vp]
     lib.moe_blob_layout_init_mx.argtypes = [_i32, _i32, ctypes.POINTER(BlobLayout)]
     lib.moe_mx_workspace_bytes.argtypes = [_DP, ctypes.POINTER(_u64)]
@@ -343,6 +346,17 @@ def moe_expert_ffn_combine(dims, x, pool, pool_bytes, layout: BlobLayout, offset
                                        _p(offsets), _p(perm), _p(group_slot), _p(inv_perm), _p(topk_w),
                                        _p(shared_sigma), _p(h), _p(y_rows), _p(y), _p(dev_status), _p(ws), ws_bytes,
                                        ev_start, ev_stop, _s(stream)), "moe_expert_ffn_combine")
+
+
+def moe_expert_ffn_down_combine(dims, x, pool, pool_bytes, layout: BlobLayout, offsets, perm, group_slot, inv_perm,
+                                topk_w, shared_sigma, h, y_rows, y, dev_status, ws, ev_start: Optional[int] = None,
+                                ev_stop: Optional[int] = None, ws_bytes: Optional[int] = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.moe_expert_ffn_down_combine(ctypes.byref(dims), _p(x), _p(pool), pool_bytes, ctypes.byref(layout),
+                                            _p(offsets), _p(perm), _p(group_slot), _p(inv_perm), _p(topk_w),
+                                            _p(shared_sigma), _p(h), _p(y_rows), _p(y), _p(dev_status), _p(ws),
+                                            ws_bytes, ev_start, ev_stop, _s(stream)), "moe_expert_ffn_down_combine")
 
 
 def moe_blob_layout_init_mx(H: int, I: int) -> BlobLayout:

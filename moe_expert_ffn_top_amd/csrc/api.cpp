@@ -429,6 +429,11 @@ int expert_ffn(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t 
     return hip_status(moe::launch_ffn_dec_fused(*d, x, g, h, y_rows, dev_status, ws, n_cu, e0, e1, st, inv_perm,
                                                 topk_w, shared_sigma, y),
                       "expert FFN + combine launch");
+  // moe_expert_ffn_down_combine on decode windows: the down stage and the
+  // combine in one launch
+  if (comb && stages == 2 && moe::down_combine_fusable(*d))
+    return hip_status(moe::launch_down_combine(*d, g, h, y_rows, ws, e0, e1, st, inv_perm, topk_w, shared_sigma, y),
+                      "down + combine launch");
   if (moe::use_gemm(*d))
     r = hip_status(moe::launch_ffn_gemm(*d, x, g, perm, h, y_rows, ws, n_cu, stages, e0, e1, st), "expert FFN launch");
   else
@@ -458,6 +463,17 @@ int moe_expert_ffn_combine(const moe_dims* d, const uint16_t* x, const void* poo
   if (!y) return fail(MOE_ERR_ARG, "y is NULL");
   return expert_ffn(d, x, pool, pool_bytes, layout, offsets, perm, group_slot, h, y_rows, dev_status, ws, ws_bytes, 3,
                     ev_start, ev_stop, stream, inv_perm, topk_w, shared_sigma, y);
+}
+
+int moe_expert_ffn_down_combine(const moe_dims* d, const uint16_t* x, const void* pool, uint64_t pool_bytes,
+                                const moe_blob_layout* layout, const int32_t* offsets, const int32_t* perm,
+                                const int32_t* group_slot, const int32_t* inv_perm, const float* topk_w,
+                                const float* shared_sigma, const uint16_t* h, uint16_t* y_rows, uint16_t* y,
+                                int32_t* dev_status, void* ws, uint64_t ws_bytes, void* ev_start, void* ev_stop,
+                                moe_stream_t stream) {
+  if (!y) return fail(MOE_ERR_ARG, "y is NULL");
+  return expert_ffn(d, x, pool, pool_bytes, layout, offsets, perm, group_slot, const_cast<uint16_t*>(h), y_rows,
+                    dev_status, ws, ws_bytes, 2, ev_start, ev_stop, stream, inv_perm, topk_w, shared_sigma, y);
 }
 
 int moe_route_group_ffn(const moe_dims* d, int32_t layer, const uint16_t* x, const float* w_router,

@@ -729,6 +729,109 @@ __global__ __launch_bounds__(256) void k_ffn_dec(const float* __restrict__ r_log
     walk(tiles, tile_tok);
 }
 
+// The down projection and the combine in one launch, by column block (S4 down
+// + S5; [Strata] "路由以后，专家怎样分工？": a token's expert outputs are
+// weighted and summed once all have arrived).  Workgroup P b + e (P parts)
+// computes the Y rows of the tiles t = e, e + P, ... for the 16 output units
+// of column block b (K = I = 512: one round of four 32-value chunks per
+// lane); its wavefronts take those tiles in turn (t = e + P w + P W i), each
+// issuing a batch of tiles' weight loads at once and their h rows one tile
+// ahead.  Measured on the 48-layer decode window, one tile per wavefront and
+// batch, 16 wavefronts and two parts were fastest: many short independent
+// streams per CU.  The Y rows are stored device-coherently; the workgroup then
+// counts itself on the block's counter (zeroed by the grouping that wrote the
+// work list), and the last of the P combines the block for every token in
+// k_combine's arithmetic and zeroes the counter again.  Nothing waits, so the
+// grid need not be resident as a whole.
+#ifndef MOE_DC_TILES
+#define MOE_DC_TILES 1
+#endif
+#ifndef MOE_DC_PARTS
+#define MOE_DC_PARTS 2
+#endif
+#ifndef MOE_DC_WAVES
+#define MOE_DC_WAVES 16
+#endif
+constexpr int kDcTiles = MOE_DC_TILES;   // tiles per wavefront per batch
+constexpr int kDcWaves = MOE_DC_WAVES;   // wavefronts per workgroup
+constexpr int kDcParts = MOE_DC_PARTS;   // workgroups per column block
+constexpr int kDcMaxT = 16;       // tokens of a window
+constexpr int kDcMaskWords = 32;  // column blocks / 32 (H <= 16384)
+__global__ __launch_bounds__(64 * kDcWaves, kDcParts > 2 ? 2 : 1) void k_down_comb(const int4* __restrict__ tiles, const int32_t* __restrict__ n_tiles_p,
+                                                   DecArgs a, const uint8_t* __restrict__ pool,
+                                                   const uint16_t* __restrict__ h, uint16_t* __restrict__ y_rows,
+                                                   FusedCtx fc) {
+  __shared__ int2 pw[kSortF];         // (inv_perm, w) of each (token, slot) entry
+  __shared__ float sg[kDcMaxT];       // sigma of each token
+  __shared__ uint32_t mask[kDcMaskWords];
+  __shared__ int second;
+  const int cb = blockIdx.x / kDcParts, part = blockIdx.x % kDcParts;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
+  const int nt = *as_const(n_tiles_p);
+  const int n_items = nt * a.n_ug;
+  // wavefront w takes tiles part + P w + P W i (P parts, W wavefronts), kDcTiles at a time
+  for (int j0 = 0; part + kDcParts * wave + kDcParts * kDcWaves * kDcTiles * j0 < nt; j0++) {
+    Item<1> it[kDcTiles];
+    Step<1> fb[kDcTiles][4];
+    uint2 sc[kDcTiles];
+#pragma unroll
+    for (int m = 0; m < kDcTiles; m++) {
+      const int t = part + kDcParts * wave + kDcParts * kDcWaves * (kDcTiles * j0 + m);
+      Desc dd;
+      dd.td = tiles[min(t, a.max_tiles - 1)];
+      dd.tok = 0;
+      dd.item = t * a.n_ug + cb;
+      it[m] = make_item<false, 1, true, false>(a, dd, n_items, 0, c, pool, h);
+      load_sc<1>(&sc[m], it[m], 0);
+#pragma unroll
+      for (int st = 0; st < 4; st++) load_step<1, true, false>(fb[m][st], it[m], 4 * q + st, 16, c);
+    }
+    uint4 xa[2][4][4];
+#pragma unroll
+    for (int st = 0; st < 4; st++) load_a<1, kAuxPlain>(xa[0][st], it[0], 4 * q + st);
+#pragma unroll
+    for (int m = 0; m < kDcTiles; m++) {
+      if (m + 1 < kDcTiles) {
+#pragma unroll
+        for (int st = 0; st < 4; st++) load_a<1, kAuxPlain>(xa[(m + 1) & 1][st], it[m + 1], 4 * q + st);
+      }
+      f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int st = 0; st < 4; st++) {
+        const uint32_t sw = (st < 2 ? sc[m].x : sc[m].y) >> (16 * (st & 1));
+        mma_step<1, false>(fb[m][st], xa[m & 1][st], &sw, it[m].resident, acc);
+      }
+      if (it[m].live) {
+        uint16_t* orows = y_rows + (int64_t)it[m].p0 * a.H;
+        const int obytes = it[m].n * a.H * 2;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int row = 4 * q + r;  // D[row][c]
+          if (row < it[m].n)
+            store_bf16<kAuxDevice>(orows, obytes, row * a.H + it[m].unit, f32_to_bf16_rne(it[m].g0 * acc[0][r]));
+        }
+      }
+    }
+  }
+  // the routing's outputs for the combine (written before the launch)
+  const int F = fc.T * fc.k;
+  for (int i = threadIdx.x; i < F; i += blockDim.x) pw[i] = make_int2(fc.inv_perm[i], __float_as_int(fc.w[i]));
+  for (int i = threadIdx.x; i < fc.T; i += blockDim.x) sg[i] = fc.sigma[i];
+  for (int i = threadIdx.x; i < (fc.H / 16 + 31) / 32; i += blockDim.x) mask[i] = i == (cb >> 5) ? 1u << (cb & 31) : 0u;
+  // every Y store of this workgroup has completed (written through to the
+  // device-coherent level) before it is counted
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t* ctr = counter(fc, 1 + fc.max_tiles + cb);
+    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    second = old == kDcParts - 1;
+    if (old == kDcParts - 1) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (second) combine_blocks(y_rows, fc, mask, pw, sg);
+}
+
 // Gate/up items of the fused launch: with R = ceil(n / G) rounds, the first
 // nf = n - (R - 1) G workgroups take R items each, the others R - 1.  The R-item
 // workgroups take the last R nf items (strided by nf, so each round covers
@@ -1282,6 +1385,41 @@ hipError_t launch_ffn_dec_fused(const moe_dims& d, const uint16_t* x, const FfnG
     return hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(256), args, 0, s, ev_start, ev_stop,
                               0);
   return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(256), args, 0, s);
+}
+
+bool down_combine_fusable(const moe_dims& d) {
+  return !use_gemm(d) && d.I == 512 && d.T <= kDcMaxT && d.k <= kFusedCombineMaxK && (int64_t)d.T * d.k <= kSortF &&
+         d.H % 16 == 0 && d.H / 16 <= 32 * kDcMaskWords;
+}
+
+hipError_t launch_down_combine(const moe_dims& d, const FfnGeom& g, const uint16_t* h, uint16_t* y_rows, void* ws,
+                               hipEvent_t ev_start, hipEvent_t ev_stop, hipStream_t s, const int32_t* inv_perm,
+                               const float* w, const float* sigma, uint16_t* y) {
+  const WsLayout wl = ws_layout(d);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  DecArgs a = dec_args(d, g, wl, stage_split(d, false, false));
+  a.n_ug = d.H / 16;  // an item is one tile by one 16-unit column block
+  a.n_kr = 1;
+  FusedCtx fc = {};
+  fc.sync = reinterpret_cast<int32_t*>(base + wl.off_sync);
+  fc.max_tiles = (int32_t)wl.max_tiles;
+  fc.inv_perm = inv_perm;
+  fc.w = w;
+  fc.sigma = sigma;
+  fc.y = y;
+  fc.T = d.T;
+  fc.k = d.k;
+  fc.H = d.H;
+  fc.cols = 16;
+  const int4* tiles = reinterpret_cast<const int4*>(base + wl.off_tiles);
+  const int32_t* n_tiles = reinterpret_cast<const int32_t*>(base + wl.off_meta);
+  const dim3 grid((unsigned)(kDcParts * (d.H / 16))), block(64 * kDcWaves);
+  if (ev_start || ev_stop)
+    hipExtLaunchKernelGGL(k_down_comb, grid, block, 0, s, ev_start, ev_stop, 0, tiles, n_tiles, a, g.pool, h, y_rows,
+                          fc);
+  else
+    hipLaunchKernelGGL(k_down_comb, grid, block, 0, s, tiles, n_tiles, a, g.pool, h, y_rows, fc);
+  return hipGetLastError();
 }
 
 bool route_ffn_combine_fusable(const moe_dims& d) {

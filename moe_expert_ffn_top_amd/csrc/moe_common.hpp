@@ -371,6 +371,12 @@ hipError_t launch_combine(const moe_dims& d, const uint16_t* y_rows, const int32
 constexpr int kFusedCombineMaxT = 64;
 constexpr int kFusedCombineMaxK = 16;
 bool ffn_dec_fusable(const moe_dims& d, bool combine);
+// The down stage and the combine in one launch (ffn_dec.hip): decode windows
+// with I = 512, T <= 16, k <= 16.
+bool down_combine_fusable(const moe_dims& d);
+hipError_t launch_down_combine(const moe_dims& d, const FfnGeom& g, const uint16_t* h, uint16_t* y_rows, void* ws,
+                               hipEvent_t ev_start, hipEvent_t ev_stop, hipStream_t s, const int32_t* inv_perm,
+                               const float* w, const float* sigma, uint16_t* y);
 hipError_t launch_ffn_dec_fused(const moe_dims& d, const uint16_t* x, const FfnGeom& g, uint16_t* h,
                                 uint16_t* y_rows, int32_t* dev_status, void* ws, int n_cu, hipEvent_t ev_start,
                                 hipEvent_t ev_stop, hipStream_t s, const int32_t* inv_perm, const float* w,
