@@ -410,8 +410,8 @@ int moe_expert_ffn_combine(const moe_dims* d, const uint16_t* x, const void* poo
  * arrived): two workgroups share each block of 16 output columns, each
  * computing the Y rows of half the tiles for it, and the second of the two to
  * finish combines the block for every token in moe_combine's arithmetic.
- * Nothing in the launch waits.  Its two counters per block live in ws
- * (zeroed by the grouping that wrote ws's work list and again after each use).
+ * Nothing in the launch waits.  Each block's counter lives in ws (zeroed by
+ * the grouping that wrote ws's work list, and again after each use).
  * Y rows are stored device-coherently (written through) so the combining
  * workgroup reads them across XCDs.  Other shapes run the two launches.
  * ev_start, ev_stop as for moe_expert_ffn_stages. */
